@@ -1,0 +1,204 @@
+"""CPU oracle for block-shared top-k sparse KV attention (MAGE), fp64.
+
+TEST INFRASTRUCTURE ONLY: the tests, ``__graft_entry__.smoke()`` and the
+benchmark's ``cpu_baseline`` leg may use this package; the product path
+(``block_sparse_kv_amd``) never imports it and has no CPU fallback.
+
+The arithmetic lives in ``mage_oracle.cpp`` (plain C++17 + OpenMP, fp64,
+full sort for top-k, gather-then-dense for the sparse step); this module only
+marshals numpy/torch CPU arrays through ctypes and loops over sequences.
+Every function follows the MAGE page ("MAGE: All-[MASK] Block Already Knows
+Where to Look in Block Diffusion LLM", atlas.scime.ai summary): step-1 exact
+attention of the all-[MASK] block and its per-block top-k subset
+("Approach"), one subset shared by all block tokens ("Problem"), and reuse of
+that subset at the later steps ("Approach").
+
+Parity pins: every function here is pinned by tests/test_oracle_*.py against
+closed forms, library routines and brute force (see those tests); none is
+"parity unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+import torch
+
+_DIR = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_DIR, "mage_oracle.cpp")
+_LIB_PATH = os.path.join(_DIR, "liboracle.so")
+_lib = None
+
+_dp = ctypes.POINTER(ctypes.c_double)
+_u16p = ctypes.POINTER(ctypes.c_uint16)
+_i32p = ctypes.POINTER(ctypes.c_int32)
+
+
+def build(force: bool = True) -> str:
+    """Compile liboracle.so with g++ (no HIP headers, no shared sources)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        subprocess.run(["g++", "-O2", "-std=c++17", "-fopenmp", "-shared", "-fPIC",
+                        "-o", tmp, _SRC], check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build(force=False)
+        lib = ctypes.CDLL(_LIB_PATH)
+        lib.oracle_exact_seq.argtypes = [ctypes.c_int] * 4 + [ctypes.c_double, _u16p, _u16p, _u16p,
+                                                             ctypes.c_int, _dp, _dp, _dp]
+        lib.oracle_sparse_seq.argtypes = [ctypes.c_int] * 4 + [ctypes.c_double, _u16p, _u16p, _u16p,
+                                                              ctypes.c_int, _i32p, ctypes.c_int, _dp, _dp]
+        lib.oracle_topk.argtypes = [_dp, ctypes.c_int, ctypes.c_int, ctypes.c_int, _i32p]
+        lib.oracle_depage.argtypes = [_u16p, ctypes.c_int, ctypes.c_int, ctypes.c_int, _i32p,
+                                      ctypes.c_int, _u16p]
+        for f in (lib.oracle_exact_seq, lib.oracle_sparse_seq, lib.oracle_topk, lib.oracle_depage):
+            f.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _u16(t) -> np.ndarray:
+    """bf16 torch tensor (or uint16 array) -> contiguous uint16 numpy view."""
+    if isinstance(t, torch.Tensor):
+        assert t.dtype == torch.bfloat16 and t.device.type == "cpu"
+        return np.ascontiguousarray(t.contiguous().view(torch.int16).numpy().view(np.uint16))
+    return np.ascontiguousarray(t, dtype=np.uint16)
+
+
+def _ptr(a: np.ndarray, typ):
+    return a.ctypes.data_as(typ)
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise ValueError(f"oracle {what}: invalid arguments")
+
+
+def exact(q, k, v, scale: float, seq_lens=None):
+    """Exact attention + block-averaged score, contiguous cache.
+
+    q: bf16 [S][B][Hq][d]; k, v: bf16 [S][Hkv][N][d]. With ``seq_lens`` only
+    the first N_s rows of sequence s take part (ragged batch in a padded
+    array). Returns (O [S][B][Hq][d], lse [S][B][Hq], score list of
+    [Hkv][N_s]) as float64 numpy arrays.
+    """
+    lib = _load()
+    qn, kn, vn = _u16(q), _u16(k), _u16(v)
+    S, B, Hq, d = qn.shape
+    _, Hkv, N, _ = kn.shape
+    O = np.zeros((S, B, Hq, d))
+    lse = np.zeros((S, B, Hq))
+    scores = []
+    for s in range(S):
+        n = N if seq_lens is None else int(seq_lens[s])
+        ks = np.ascontiguousarray(kn[s, :, :n])
+        vs = np.ascontiguousarray(vn[s, :, :n])
+        qs = np.ascontiguousarray(qn[s])
+        Os = np.zeros((B, Hq, d))
+        ls = np.zeros((B, Hq))
+        sc = np.zeros((Hkv, n))
+        _check(lib.oracle_exact_seq(B, Hq, Hkv, d, float(scale), _ptr(qs, _u16p), _ptr(ks, _u16p),
+                                    _ptr(vs, _u16p), n, _ptr(Os, _dp), _ptr(ls, _dp),
+                                    _ptr(sc, _dp)), "exact")
+        O[s], lse[s] = Os, ls
+        scores.append(sc)
+    return O, lse, scores
+
+
+def topk(score_rows, k: int) -> np.ndarray:
+    """Top-k per row under (score desc, position asc); ascending output, -1 padded.
+
+    score_rows: [rows][N] array-like (fp32 inputs are widened exactly).
+    """
+    lib = _load()
+    a = np.ascontiguousarray(np.asarray(score_rows, dtype=np.float64))
+    if a.ndim == 1:
+        a = a[None]
+    rows, n = a.shape
+    idx = np.zeros((rows, k), dtype=np.int32)
+    _check(lib.oracle_topk(_ptr(a, _dp), rows, n, int(k), _ptr(idx, _i32p)), "topk")
+    return idx
+
+
+def select_exact(q, k, v, scale: float, topk_k: int, seq_lens=None):
+    """Step 1 of a block: exact O, lse, per-(seq, KV head) score, and top-k idx.
+
+    Returns (O, lse, scores, idx) with idx int32 [S][Hkv][topk_k].
+    """
+    O, lse, scores = exact(q, k, v, scale, seq_lens)
+    idx = np.stack([topk(sc, topk_k) for sc in scores])
+    return O, lse, scores, idx
+
+
+def sparse(q, k, v, idx, scale: float, seq_lens=None):
+    """Later-step attention over the gathered rows idx[s][h][:] (gather-then-dense)."""
+    lib = _load()
+    qn, kn, vn = _u16(q), _u16(k), _u16(v)
+    S, B, Hq, d = qn.shape
+    _, Hkv, N, _ = kn.shape
+    idn = np.ascontiguousarray(np.asarray(idx, dtype=np.int32))
+    kk = idn.shape[-1]
+    O = np.zeros((S, B, Hq, d))
+    lse = np.zeros((S, B, Hq))
+    for s in range(S):
+        n = N if seq_lens is None else int(seq_lens[s])
+        ks = np.ascontiguousarray(kn[s, :, :n])
+        vs = np.ascontiguousarray(vn[s, :, :n])
+        qs = np.ascontiguousarray(qn[s])
+        ids = np.ascontiguousarray(idn[s])
+        Os = np.zeros((B, Hq, d))
+        ls = np.zeros((B, Hq))
+        _check(lib.oracle_sparse_seq(B, Hq, Hkv, d, float(scale), _ptr(qs, _u16p), _ptr(ks, _u16p),
+                                     _ptr(vs, _u16p), n, _ptr(ids, _i32p), kk, _ptr(Os, _dp),
+                                     _ptr(ls, _dp)), "sparse")
+        O[s], lse[s] = Os, ls
+    return O, lse
+
+
+def depage(pool, page_table, seq_lens, num_kv_heads: int | None = None):
+    """Copy a page pool [P][Hkv][page][d] back to per-sequence [Hkv][N_s][d] uint16 arrays."""
+    lib = _load()
+    pn = _u16(pool)
+    P, Hkv, page, d = pn.shape
+    tab = np.ascontiguousarray(np.asarray(page_table, dtype=np.int32))
+    out = []
+    for s, n in enumerate(np.asarray(seq_lens).tolist()):
+        o = np.zeros((Hkv, int(n), d), dtype=np.uint16)
+        row = np.ascontiguousarray(tab[s])
+        _check(lib.oracle_depage(_ptr(pn, _u16p), Hkv, page, d, _ptr(row, _i32p), int(n),
+                                 _ptr(o, _u16p)), "depage")
+        out.append(o)
+    return out
+
+
+def _padded(seqs):
+    """Stack per-sequence [Hkv][N_s][d] arrays into [S][Hkv][maxN][d] (zero padded)."""
+    S = len(seqs)
+    Hkv, _, d = seqs[0].shape
+    n = max(a.shape[1] for a in seqs)
+    out = np.zeros((S, Hkv, n, d), dtype=np.uint16)
+    for s, a in enumerate(seqs):
+        out[s, :, :a.shape[1]] = a
+    return out
+
+
+def select_exact_paged(q, k_pool, v_pool, page_table, seq_lens, scale: float, topk_k: int):
+    """Paged step 1: de-page, then the contiguous definition per sequence."""
+    kc = _padded(depage(k_pool, page_table, seq_lens))
+    vc = _padded(depage(v_pool, page_table, seq_lens))
+    return select_exact(q, kc, vc, scale, topk_k, seq_lens=np.asarray(seq_lens))
+
+
+def sparse_paged(q, k_pool, v_pool, page_table, seq_lens, idx, scale: float):
+    """Paged later step: de-page, then gather-then-dense per sequence."""
+    kc = _padded(depage(k_pool, page_table, seq_lens))
+    vc = _padded(depage(v_pool, page_table, seq_lens))
+    return sparse(q, kc, vc, idx, scale, seq_lens=np.asarray(seq_lens))

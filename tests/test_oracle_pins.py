@@ -1,0 +1,269 @@
+"""Pins of the fp64 CPU oracle to things other than itself.
+
+Each check is independent of the oracle's code: torch's own attention routine
+(scaled_dot_product_attention) and logsumexp in float64, closed forms worked
+out from the definition, brute-force rank counting, and invariants. The
+definitions pinned are those of the MAGE page ("MAGE: All-[MASK] Block
+Already Knows Where to Look in Block Diffusion LLM", atlas.scime.ai summary):
+exact step-1 attention of the all-[MASK] block, the block-shared top-k subset
+("Problem", "Approach"), and reuse of that subset at later steps ("Approach").
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.filterwarnings("ignore")
+
+
+def bf16(a):
+    return torch.as_tensor(np.asarray(a, dtype=np.float32)).to(torch.bfloat16)
+
+
+def rand_case(S, B, Hq, Hkv, d, N, seed, kscale=1.0):
+    g = torch.Generator().manual_seed(seed)
+    q = (torch.randn(S, B, Hq, d, generator=g) / math.sqrt(d)).to(torch.bfloat16)
+    k = (kscale * torch.randn(S, Hkv, N, d, generator=g)).to(torch.bfloat16)
+    v = torch.randn(S, Hkv, N, d, generator=g).to(torch.bfloat16)
+    return q, k, v
+
+
+def sdpa_ref(q, k, v, scale, mask=None):
+    """torch's attention in float64; q [S][B][Hq][d], k/v [S][Hkv][N][d]."""
+    qq = q.double().permute(0, 2, 1, 3)          # [S][Hq][B][d]
+    o = F.scaled_dot_product_attention(qq, k.double(), v.double(), attn_mask=mask,
+                                       scale=scale, enable_gqa=True)
+    return o.permute(0, 2, 1, 3)                 # [S][B][Hq][d]
+
+
+def lse_ref(q, k, scale):
+    Hq, Hkv = q.shape[2], k.shape[1]
+    kk = k.double().repeat_interleave(Hq // Hkv, dim=1)     # [S][Hq][N][d]
+    x = torch.einsum("sbjd,sjnd->sbjn", q.double(), kk) * scale
+    return torch.logsumexp(x, dim=-1)
+
+
+def probs_ref(q, k, scale):
+    """Attention probabilities via torch's attention routine with V = identity."""
+    S, Hkv, N, d = k.shape
+    eye = torch.eye(N, dtype=torch.float64).expand(S, Hkv, N, N)
+    return sdpa_ref(q, k, eye, scale)            # [S][B][Hq][N]
+
+
+SHAPES = [  # (S, B, Hq, Hkv, d, N)
+    (1, 1, 1, 1, 64, 1), (1, 3, 1, 1, 64, 2), (1, 1, 4, 1, 64, 3), (2, 3, 4, 1, 128, 17),
+    (1, 16, 1, 1, 64, 64), (1, 3, 8, 2, 128, 64), (1, 2, 4, 4, 64, 1024),
+]
+
+
+@pytest.mark.parametrize("S,B,Hq,Hkv,d,N", SHAPES)
+def test_exact_matches_torch_attention(S, B, Hq, Hkv, d, N):
+    q, k, v = rand_case(S, B, Hq, Hkv, d, N, seed=N * 31 + d)
+    scale = 1.0 / math.sqrt(d) * 3.0
+    O, lse, scores = oracle.exact(q, k, v, scale)
+    np.testing.assert_allclose(O, sdpa_ref(q, k, v, scale).numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, lse_ref(q, k, scale).numpy(), rtol=0, atol=1e-12)
+    # score: mean over the B tokens and the G heads of the group of the probabilities
+    P = probs_ref(q, k, scale)                   # [S][B][Hq][N]
+    G = Hq // Hkv
+    for s in range(S):
+        for h in range(Hkv):
+            ref = P[s, :, h * G:(h + 1) * G].reshape(-1, N).mean(0).numpy()
+            np.testing.assert_allclose(scores[s][h], ref, rtol=0, atol=1e-14)
+
+
+def test_two_keys_logistic_closed_form():
+    # q = a e0, k0 = c0 e0, k1 = c1 e0: x_p = scale a c_p, P0 = 1/(1+exp(x1-x0))
+    d, scale = 64, 0.125
+    a, c0, c1 = 1.5, 2.0, -0.75
+    q = np.zeros((1, 1, 1, d)); q[..., 0] = a
+    k = np.zeros((1, 1, 2, d)); k[0, 0, 0, 0] = c0; k[0, 0, 1, 0] = c1
+    v = np.zeros((1, 1, 2, d)); v[0, 0, 0, :] = 1.0; v[0, 0, 1, :] = -2.0
+    O, lse, sc = oracle.exact(bf16(q), bf16(k), bf16(v), scale)
+    x0, x1 = scale * a * c0, scale * a * c1
+    p0 = 1.0 / (1.0 + math.exp(x1 - x0))
+    assert abs(sc[0][0, 0] - p0) < 1e-15 and abs(sc[0][0, 1] - (1 - p0)) < 1e-15
+    np.testing.assert_allclose(O[0, 0, 0], p0 * 1.0 + (1 - p0) * -2.0, atol=1e-15)
+    assert abs(lse[0, 0, 0] - (x0 + math.log1p(math.exp(x1 - x0)))) < 1e-14
+
+
+def test_zero_keys_give_mean_of_v():
+    q, _, v = rand_case(1, 3, 4, 2, 64, 37, seed=3)
+    k = torch.zeros(1, 2, 37, 64, dtype=torch.bfloat16)
+    O, lse, sc = oracle.exact(q, k, v, 0.3)
+    mean_v = v.double().mean(2)                                  # [S][Hkv][d]
+    for j in range(4):
+        np.testing.assert_allclose(O[0, :, j], mean_v[0, j // 2].expand(3, 64).numpy(), atol=1e-14)
+    np.testing.assert_allclose(lse, math.log(37), atol=1e-14)
+    np.testing.assert_allclose(np.stack(sc[0]), 1 / 37, atol=1e-16)
+
+
+def test_constant_v_and_single_key():
+    q, k, _ = rand_case(1, 4, 2, 1, 128, 50, seed=4, kscale=3.0)
+    v = torch.full((1, 1, 50, 128), -1.25, dtype=torch.bfloat16)
+    O, _, _ = oracle.exact(q, k, v, 1.0)
+    np.testing.assert_allclose(O, -1.25, atol=1e-14)
+    q, k, v = rand_case(1, 4, 2, 1, 64, 1, seed=5)
+    O, lse, sc = oracle.exact(q, k, v, 0.7)
+    np.testing.assert_allclose(O[0, :, :], v.double()[0, 0, 0].expand(4, 2, 64).numpy(), atol=0)
+    x = 0.7 * torch.einsum("bjd,d->bj", q.double()[0], k.double()[0, 0, 0])
+    np.testing.assert_allclose(lse[0], x.numpy(), atol=1e-14)
+    assert sc[0][0, 0] == 1.0
+
+
+def test_gqa_group_mapping():
+    # KV head h has constant V = h + 1, so query head j must read back j // G + 1.
+    Hq, Hkv = 8, 2
+    q, k, _ = rand_case(1, 3, Hq, Hkv, 64, 20, seed=6)
+    v = torch.stack([torch.full((20, 64), float(h + 1)) for h in range(Hkv)])[None].to(torch.bfloat16)
+    O, _, _ = oracle.exact(q, k, v, 0.5)
+    for j in range(Hq):
+        np.testing.assert_allclose(O[0, :, j], j // (Hq // Hkv) + 1, atol=1e-14)
+
+
+def test_probability_rows_and_scores_sum_to_one():
+    N, d = 64, 64
+    q, k, _ = rand_case(1, 5, 4, 2, d, N, seed=8, kscale=2.0)
+    eye = torch.eye(N).expand(1, 2, N, N).to(torch.bfloat16)   # V = I gives the P rows as O
+    O, _, sc = oracle.exact(q, k, eye, 0.4)
+    np.testing.assert_allclose(O.sum(-1), 1.0, atol=1e-13)
+    assert (O >= 0).all()
+    np.testing.assert_allclose(O, probs_ref(q, k, 0.4).numpy(), atol=1e-13)
+    for h in range(2):
+        assert abs(sc[0][h].sum() - 1.0) < 1e-12
+        assert (sc[0][h] >= 0).all() and (sc[0][h] <= 1).all()
+
+
+def test_dominant_key_selects_its_value_row():
+    q, k, v = rand_case(1, 4, 1, 1, 128, 300, seed=9)
+    m = q.double()[0, :, 0].mean(0)
+    kk = k.double()
+    kk[0, 0, 123] = 400.0 * m / m.norm()
+    k = kk.to(torch.bfloat16)
+    O, _, sc = oracle.exact(q, k, v, 1.0)
+    x = torch.einsum("bd,nd->bn", q.double()[0, :, 0], k.double()[0, 0])
+    gap = (x[:, 123:124] - torch.cat([x[:, :123], x[:, 124:]], 1)).min().item()
+    assert gap > 20
+    # O - v* = sum_p P_p (v_p - v*), and every P_p (p != 123) is below exp(-gap)
+    tol = 299 * math.exp(-gap) * 2 * v.double().abs().max().item()
+    np.testing.assert_allclose(O[0, :, 0], v.double()[0, 0, 123].expand(4, 128).numpy(),
+                               rtol=0, atol=tol + 1e-15)
+    assert int(np.argmax(sc[0][0])) == 123
+
+
+def rank_topk(score, k):
+    """O(N^2) brute force: rank(p) = #{q: s_q > s_p or (s_q == s_p and q < p)}."""
+    s = np.asarray(score, dtype=np.float64)
+    n = len(s)
+    ranks = np.array([np.sum((s > s[p]) | ((s == s[p]) & (np.arange(n) < p))) for p in range(n)])
+    sel = np.sort(np.nonzero(ranks < min(k, n))[0])
+    return np.concatenate([sel, -np.ones(k - len(sel), dtype=np.int64)])
+
+
+@pytest.mark.parametrize("ties", ["none", "many", "all", "zeros"])
+@pytest.mark.parametrize("n,k", [(1, 1), (5, 3), (64, 64), (300, 17), (1000, 100), (7, 20)])
+def test_topk_matches_rank_counting(ties, n, k):
+    sc = workloads.random_scores(3, n, seed=n + k, ties=ties).numpy()
+    idx = oracle.topk(sc, k)
+    for r in range(3):
+        np.testing.assert_array_equal(idx[r], rank_topk(sc[r], k))
+
+
+def test_topk_special_cases():
+    n = 100
+    assert oracle.topk(np.full(n, 0.01), 10)[0].tolist() == list(range(10))
+    assert oracle.topk(np.arange(n) * 1e-3, 200)[0].tolist() == list(range(n)) + [-1] * 100
+    # strictly decreasing scores: the first k positions
+    assert oracle.topk(1.0 - np.arange(n) * 1e-3, 5)[0].tolist() == [0, 1, 2, 3, 4]
+
+
+def test_single_row_topk_is_topk_of_logits():
+    # B * G = 1: the score is the softmax row, a monotone map of the raw logits,
+    # so its top-k equals the top-k of the logits (stable: lower position first).
+    q, k, v = rand_case(1, 1, 1, 1, 64, 500, seed=10, kscale=2.0)
+    _, _, sc, idx = oracle.select_exact(q, k, v, 0.125, 40)
+    x = (k.double()[0, 0] @ q.double()[0, 0, 0]).numpy()
+    order = np.argsort(-x, kind="stable")[:40]
+    np.testing.assert_array_equal(idx[0, 0], np.sort(order))
+
+
+def test_permuting_positions_permutes_selection():
+    q, k, v = rand_case(1, 4, 2, 1, 64, 256, seed=11, kscale=2.0)
+    _, _, sc, idx = oracle.select_exact(q, k, v, 0.25, 32)
+    perm = np.random.default_rng(0).permutation(256)
+    _, _, sc2, idx2 = oracle.select_exact(q, k[:, :, perm], v[:, :, perm], 0.25, 32)
+    # continuous random scores: no ties, so the selected set maps through perm
+    np.testing.assert_allclose(sc2[0][0], sc[0][0][perm], rtol=1e-12, atol=0)
+    assert set(perm[idx2[0, 0]].tolist()) == set(idx[0, 0].tolist())
+
+
+def test_sparse_with_all_positions_equals_exact():
+    q, k, v = rand_case(2, 3, 4, 2, 64, 77, seed=12, kscale=2.0)
+    O, lse, _ = oracle.exact(q, k, v, 0.3)
+    idx = np.broadcast_to(np.arange(77, dtype=np.int32), (2, 2, 77))
+    Os, lses = oracle.sparse(q, k, v, idx, 0.3)
+    np.testing.assert_allclose(Os, O, atol=1e-12)
+    np.testing.assert_allclose(lses, lse, atol=1e-12)
+
+
+def test_sparse_equals_masked_attention_and_ignores_order():
+    S, B, Hq, Hkv, d, N, kk = 1, 3, 4, 2, 128, 200, 23
+    q, k, v = rand_case(S, B, Hq, Hkv, d, N, seed=13, kscale=2.0)
+    rng = np.random.default_rng(1)
+    idx = np.stack([np.sort(rng.choice(N, kk, replace=False)) for _ in range(Hkv)])[None].astype(np.int32)
+    mask = torch.zeros(S, Hq, B, N, dtype=torch.bool)
+    for j in range(Hq):
+        mask[0, j, :, idx[0, j // 2]] = True
+    ref = sdpa_ref(q, k, v, 0.2, mask=mask).numpy()
+    Os, lses = oracle.sparse(q, k, v, idx, 0.2)
+    np.testing.assert_allclose(Os, ref, atol=1e-12)
+    scrambled = idx[:, :, rng.permutation(kk)]
+    Os2, lses2 = oracle.sparse(q, k, v, scrambled, 0.2)
+    np.testing.assert_allclose(Os2, Os, atol=1e-13)
+    np.testing.assert_allclose(lses2, lses, atol=1e-13)
+    # -1 padding and out-of-range entries are skipped
+    padded = np.concatenate([idx, np.full((1, Hkv, 5), -1, np.int32),
+                             np.full((1, Hkv, 2), N + 3, np.int32)], axis=-1)
+    Os3, _ = oracle.sparse(q, k, v, padded, 0.2)
+    np.testing.assert_allclose(Os3, Os, atol=1e-13)
+    Oe, le = oracle.sparse(q, k, v, np.full((1, Hkv, 4), -1, np.int32), 0.2)
+    assert (Oe == 0).all() and np.isneginf(le).all()
+
+
+def test_merge_of_disjoint_subsets_gives_union():
+    # O over I1 u I2 equals the lse-weighted merge of the parts.
+    q, k, v = rand_case(1, 2, 4, 1, 64, 90, seed=14, kscale=2.0)
+    i1 = np.arange(0, 90, 2, dtype=np.int32)[None, None]
+    i2 = np.arange(1, 90, 2, dtype=np.int32)[None, None]
+    O1, l1 = oracle.sparse(q, k, v, i1, 0.3)
+    O2, l2 = oracle.sparse(q, k, v, i2, 0.3)
+    O, lse, _ = oracle.exact(q, k, v, 0.3)
+    L = np.logaddexp(l1, l2)
+    np.testing.assert_allclose(L, lse, atol=1e-12)
+    merged = (np.exp(l1 - L)[..., None] * O1 + np.exp(l2 - L)[..., None] * O2)
+    np.testing.assert_allclose(merged, O, atol=1e-12)
+
+
+def test_paged_equals_contiguous_bit_exact():
+    q, k, v = rand_case(2, 4, 4, 2, 64, 53, seed=15, kscale=2.0)   # ragged tail page
+    kp, vp, table, lens = workloads.to_paged(k, v, 16, seed=3)
+    O, lse, sc, idx = oracle.select_exact(q, k, v, 0.3, 9)
+    Op, lsep, scp, idxp = oracle.select_exact_paged(q, kp, vp, table, lens, 0.3, 9)
+    assert np.array_equal(O, Op) and np.array_equal(lse, lsep) and np.array_equal(idx, idxp)
+    assert all(np.array_equal(a, b) for a, b in zip(sc, scp))
+    Os, ls = oracle.sparse(q, k, v, idx, 0.3)
+    Osp, lsp = oracle.sparse_paged(q, kp, vp, table, lens, idx, 0.3)
+    assert np.array_equal(Os, Osp) and np.array_equal(ls, lsp)
+
+
+def test_tiny_workload_plants_are_selected():
+    inp = workloads.make_inputs(0, with_steps=False)
+    w = inp.w
+    _, _, sc, idx = oracle.select_exact(inp.q1, inp.k, inp.v, w.scale, w.k)
+    assert set(inp.plants[(0, 0)].tolist()) <= set(idx[0, 0].tolist())
+    assert abs(sc[0][0].sum() - 1) < 1e-12
