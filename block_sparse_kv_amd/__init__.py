@@ -1,0 +1,296 @@
+"""Python binding of libmage.so: block-shared top-k sparse KV attention (MAGE) on MI355X.
+
+Argument marshalling only. Every step of the path runs in the HIP kernels of
+``libmage.so`` (C ABI in ``include/mage.h``); PyTorch provides device memory
+and streams. There is no CPU fallback: importing works without a GPU, but
+each call raises if the library or a GPU is missing.
+
+Entry points mirror the C ABI:
+
+* :func:`select_exact` / :func:`select_exact_paged` -- step 1 of a block:
+  exact O and lse on the caller's stream, the block-averaged scores and the
+  top-k index set on a second stream.
+* :func:`sparse_attn` / :func:`sparse_attn_paged` -- a later step over the
+  reused index set.
+* :func:`topk` -- the selection on its own, over caller-provided scores.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmage.so")
+
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE_TOO_SMALL, ERR_HIP = range(5)
+MAX_SEQS = 256
+MAX_ROWS = 128
+
+
+class MageError(RuntimeError):
+    def __init__(self, status: int, func: str, detail: str):
+        super().__init__(f"{func}: status {status} ({detail})")
+        self.status = status
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("num_seqs", ctypes.c_int32), ("block", ctypes.c_int32),
+                ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
+class PagedKv(ctypes.Structure):
+    _fields_ = [("k_pool", ctypes.c_void_p), ("v_pool", ctypes.c_void_p),
+                ("page_table", ctypes.c_void_p), ("max_pages", ctypes.c_int32),
+                ("page_size", ctypes.c_int32), ("seq_lens", ctypes.POINTER(ctypes.c_int32))]
+
+
+_lib = None
+_vp = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_sz = ctypes.c_size_t
+
+
+def lib():
+    """Load libmage.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: run `python -m block_sparse_kv_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.POINTER
+        L.mage_workspace_bytes.argtypes = [P(Dims), _i32, _i32]
+        L.mage_workspace_bytes.restype = _sz
+        L.mage_workspace_init.argtypes = [_vp, _sz, _vp]
+        L.mage_select_exact.argtypes = [P(Dims), _vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp,
+                                        _vp, _sz, _vp, _vp, _vp]
+        L.mage_select_exact_paged.argtypes = [P(Dims), _vp, P(PagedKv), _i32, _vp, _vp, _vp, _vp,
+                                              _vp, _sz, _vp, _vp, _vp]
+        L.mage_sparse_attn.argtypes = [P(Dims), _vp, _vp, _vp, _i32, _vp, _i32, _vp, _vp, _vp, _sz,
+                                       _vp]
+        L.mage_sparse_attn_paged.argtypes = [P(Dims), _vp, P(PagedKv), _vp, _i32, _vp, _vp, _vp,
+                                             _sz, _vp]
+        L.mage_topk.argtypes = [_i32, _vp, ctypes.c_int64, P(_i32), _i32, _i32, _vp, _vp, _sz, _vp]
+        for f in ("mage_workspace_init", "mage_select_exact", "mage_select_exact_paged",
+                  "mage_sparse_attn", "mage_sparse_attn_paged", "mage_topk"):
+            getattr(L, f).restype = ctypes.c_int
+        L.mage_status_string.argtypes = [ctypes.c_int]
+        L.mage_status_string.restype = ctypes.c_char_p
+        L.mage_last_error.argtypes = []
+        L.mage_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(status: int, func: str):
+    if status != OK:
+        raise MageError(status, func, lib().mage_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(s):
+    if s is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def make_dims(q: torch.Tensor, num_kv_heads: int, scale: float) -> Dims:
+    S, B, Hq, d = q.shape
+    return Dims(S, B, Hq, num_kv_heads, d, float(scale))
+
+
+def workspace_bytes(dims: Dims, max_seq_len: int, k: int) -> int:
+    return int(lib().mage_workspace_bytes(ctypes.byref(dims), int(max_seq_len), int(k)))
+
+
+class Workspace:
+    """A zero-filled device workspace; grows (re-zeroed) when a call needs more.
+
+    Calls through one Workspace are ordered: a call made after a step-1 call
+    whose selection ran on another stream first waits for that selection.
+    """
+
+    def __init__(self, device=None):
+        self.device = torch.device(device or "cuda")
+        self.buf = None
+        self.pending = None
+
+    def get(self, nbytes: int, stream=None) -> torch.Tensor:
+        st = stream if stream is not None else torch.cuda.current_stream(self.device)
+        if self.pending is not None:
+            st.wait_event(self.pending)
+            self.pending = None
+        if self.buf is None or self.buf.numel() < nbytes:
+            with torch.cuda.stream(st):
+                self.buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=self.device)
+        return self.buf
+
+    def mark(self, stream):
+        """Record that work using this workspace is still running on `stream`."""
+        ev = torch.cuda.Event()
+        ev.record(stream)
+        self.pending = ev
+
+
+_default_ws = {}
+
+
+def _ws_obj(workspace, device):
+    if workspace is None:
+        workspace = _default_ws.setdefault(str(device), Workspace(device))
+    return workspace
+
+
+def _bf16_ptr(t, name):
+    if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous bf16 CUDA tensor")
+    return _ptr(t)
+
+
+def _out(t, shape, dtype, device):
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous():
+        raise ValueError(f"output must be contiguous {dtype} of shape {tuple(shape)}")
+    return t
+
+
+def select_exact(q, k_cache, v_cache, k: int, scale: float, *, o=None, lse=None, idx=None,
+                 scores=None, want_scores=True, workspace=None, stream=None, select_stream=None,
+                 idx_ready=None):
+    """Step 1: exact attention + block-averaged scores + top-k, contiguous cache.
+
+    q bf16 [S][B][Hq][d]; k_cache, v_cache bf16 [S][Hkv][N][d].
+    Returns (o fp32 [S][B][Hq][d], lse fp32 [S][B][Hq], idx int32 [S][Hkv][k],
+    scores fp32 [S][Hkv][N] or None). idx/scores are ready on select_stream
+    (recorded into idx_ready, a torch.cuda.Event, if given).
+    """
+    S, B, Hq, d = q.shape
+    _, Hkv, N, _ = k_cache.shape
+    dims = make_dims(q, Hkv, scale)
+    dev = q.device
+    o = _out(o, (S, B, Hq, d), torch.float32, dev)
+    lse = _out(lse, (S, B, Hq), torch.float32, dev)
+    idx = _out(idx, (S, Hkv, k), torch.int32, dev)
+    if want_scores:
+        scores = _out(scores, (S, Hkv, N), torch.float32, dev)
+    wso = _ws_obj(workspace, dev)
+    ws = wso.get(workspace_bytes(dims, N, k), stream)
+    _check(lib().mage_select_exact(ctypes.byref(dims), _bf16_ptr(q, "q"),
+                                   _bf16_ptr(k_cache, "k_cache"), _bf16_ptr(v_cache, "v_cache"),
+                                   N, int(k), _ptr(o), _ptr(lse), _ptr(idx), _ptr(scores),
+                                   _ptr(ws), ws.numel(), _stream(stream),
+                                   None if select_stream is None else _stream(select_stream),
+                                   None), "mage_select_exact")
+    if select_stream is not None:
+        wso.mark(select_stream)
+    if idx_ready is not None:
+        idx_ready.record(select_stream if select_stream is not None else torch.cuda.current_stream())
+    return o, lse, idx, scores
+
+
+def _paged(k_pool, v_pool, page_table, seq_lens):
+    lens = [int(x) for x in (seq_lens.tolist() if torch.is_tensor(seq_lens) else seq_lens)]
+    arr = (ctypes.c_int32 * len(lens))(*lens)
+    if page_table.dtype != torch.int32 or not page_table.is_cuda or not page_table.is_contiguous():
+        raise ValueError("page_table must be a contiguous int32 CUDA tensor")
+    kv = PagedKv(_bf16_ptr(k_pool, "k_pool").value, _bf16_ptr(v_pool, "v_pool").value,
+                 page_table.data_ptr(), page_table.shape[1], k_pool.shape[2],
+                 ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32)))
+    return kv, arr, lens
+
+
+def select_exact_paged(q, k_pool, v_pool, page_table, seq_lens, k: int, scale: float, *, o=None,
+                       lse=None, idx=None, scores=None, want_scores=True, workspace=None,
+                       stream=None, select_stream=None, idx_ready=None):
+    """Step 1 over a paged cache (pools bf16 [P][Hkv][page][d], host seq_lens).
+
+    scores is fp32 [S][Hkv][max(seq_lens)]; entries past N_s are left untouched.
+    """
+    S, B, Hq, d = q.shape
+    Hkv = k_pool.shape[1]
+    dims = make_dims(q, Hkv, scale)
+    kv, keep, lens = _paged(k_pool, v_pool, page_table, seq_lens)
+    maxn = max(lens)
+    dev = q.device
+    o = _out(o, (S, B, Hq, d), torch.float32, dev)
+    lse = _out(lse, (S, B, Hq), torch.float32, dev)
+    idx = _out(idx, (S, Hkv, k), torch.int32, dev)
+    if want_scores:
+        scores = _out(scores, (S, Hkv, maxn), torch.float32, dev)
+    wso = _ws_obj(workspace, dev)
+    ws = wso.get(workspace_bytes(dims, maxn, k), stream)
+    _check(lib().mage_select_exact_paged(ctypes.byref(dims), _bf16_ptr(q, "q"), ctypes.byref(kv),
+                                         int(k), _ptr(o), _ptr(lse), _ptr(idx), _ptr(scores),
+                                         _ptr(ws), ws.numel(), _stream(stream),
+                                         None if select_stream is None else _stream(select_stream),
+                                         None), "mage_select_exact_paged")
+    if select_stream is not None:
+        wso.mark(select_stream)
+    if idx_ready is not None:
+        idx_ready.record(select_stream if select_stream is not None else torch.cuda.current_stream())
+    return o, lse, idx, scores
+
+
+def sparse_attn(q, k_cache, v_cache, idx, scale: float, *, o=None, lse=None, workspace=None,
+                stream=None):
+    """A later step: attention over k_cache/v_cache rows idx[s][h][:] (any order, -1 skipped)."""
+    S, B, Hq, d = q.shape
+    _, Hkv, N, _ = k_cache.shape
+    k = idx.shape[-1]
+    if idx.dtype != torch.int32 or not idx.is_contiguous() or tuple(idx.shape[:2]) != (S, Hkv):
+        raise ValueError("idx must be contiguous int32 [S][Hkv][k]")
+    dims = make_dims(q, Hkv, scale)
+    dev = q.device
+    o = _out(o, (S, B, Hq, d), torch.float32, dev)
+    lse = _out(lse, (S, B, Hq), torch.float32, dev)
+    ws = _ws_obj(workspace, dev).get(workspace_bytes(dims, N, k), stream)
+    _check(lib().mage_sparse_attn(ctypes.byref(dims), _bf16_ptr(q, "q"),
+                                  _bf16_ptr(k_cache, "k_cache"), _bf16_ptr(v_cache, "v_cache"), N,
+                                  _ptr(idx), int(k), _ptr(o), _ptr(lse), _ptr(ws), ws.numel(),
+                                  _stream(stream)), "mage_sparse_attn")
+    return o, lse
+
+
+def sparse_attn_paged(q, k_pool, v_pool, page_table, seq_lens, idx, scale: float, *, o=None,
+                      lse=None, workspace=None, stream=None):
+    """A later step over a paged cache; idx holds logical positions."""
+    S, B, Hq, d = q.shape
+    Hkv = k_pool.shape[1]
+    k = idx.shape[-1]
+    if idx.dtype != torch.int32 or not idx.is_contiguous() or tuple(idx.shape[:2]) != (S, Hkv):
+        raise ValueError("idx must be contiguous int32 [S][Hkv][k]")
+    dims = make_dims(q, Hkv, scale)
+    kv, keep, lens = _paged(k_pool, v_pool, page_table, seq_lens)
+    dev = q.device
+    o = _out(o, (S, B, Hq, d), torch.float32, dev)
+    lse = _out(lse, (S, B, Hq), torch.float32, dev)
+    ws = _ws_obj(workspace, dev).get(workspace_bytes(dims, max(lens), k), stream)
+    _check(lib().mage_sparse_attn_paged(ctypes.byref(dims), _bf16_ptr(q, "q"), ctypes.byref(kv),
+                                        _ptr(idx), int(k), _ptr(o), _ptr(lse), _ptr(ws),
+                                        ws.numel(), _stream(stream)), "mage_sparse_attn_paged")
+    return o, lse
+
+
+def topk(scores, k: int, lens=None, *, idx=None, workspace=None, stream=None):
+    """Top-k per row of non-negative fp32 scores [rows][n]; ties to the lower position."""
+    if scores.dtype != torch.float32 or not scores.is_cuda or scores.dim() != 2 or scores.stride(1) != 1:
+        raise ValueError("scores must be a 2-D fp32 CUDA tensor with unit column stride")
+    rows, n = scores.shape
+    idx = _out(idx, (rows, k), torch.int32, scores.device)
+    keep = None
+    lp = None
+    if lens is not None:
+        lens = [int(x) for x in (lens.tolist() if torch.is_tensor(lens) else lens)]
+        keep = (ctypes.c_int32 * rows)(*lens)
+        lp = ctypes.cast(keep, ctypes.POINTER(ctypes.c_int32))
+    dims = Dims(rows, 1, 1, 1, 64, 1.0)
+    ws = _ws_obj(workspace, scores.device).get(workspace_bytes(dims, n, k), stream)
+    _check(lib().mage_topk(rows, _ptr(scores), scores.stride(0), lp, n, int(k), _ptr(idx),
+                           _ptr(ws), ws.numel(), _stream(stream)), "mage_topk")
+    return idx

@@ -1,0 +1,515 @@
+// Host side of the C ABI declared in include/mage.h: argument checks, the
+// launch plan, the workspace layout, and the two-stream issue order of step 1.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+
+#include "../../include/mage.h"
+#include "attn_kernels.hpp"
+#include "select_kernels.hpp"
+
+namespace {
+
+using namespace mage;
+
+thread_local std::string g_last_error;
+
+mage_status fail(mage_status st, const char* what) {
+  g_last_error = what;
+  return st;
+}
+
+mage_status hip_fail(hipError_t e, const char* where) {
+  g_last_error = std::string(where) + ": " + hipGetErrorString(e);
+  return MAGE_ERR_HIP;
+}
+
+struct Dims {
+  int S, B, Hq, Hkv, G, R, D, nrb, units;
+  float scale;
+};
+
+mage_status check_dims(const mage_dims* d, Dims& o) {
+  if (!d) return fail(MAGE_ERR_INVALID_ARG, "dims is null");
+  if (d->num_seqs < 1 || d->block < 1 || d->num_q_heads < 1 || d->num_kv_heads < 1)
+    return fail(MAGE_ERR_INVALID_ARG, "num_seqs, block and head counts must be >= 1");
+  if (d->num_q_heads % d->num_kv_heads)
+    return fail(MAGE_ERR_INVALID_ARG, "num_q_heads must be a multiple of num_kv_heads");
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(MAGE_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (!(std::isfinite(d->scale) && d->scale > 0.f))
+    return fail(MAGE_ERR_INVALID_ARG, "scale must be finite and > 0");
+  o.S = d->num_seqs;
+  o.B = d->block;
+  o.Hq = d->num_q_heads;
+  o.Hkv = d->num_kv_heads;
+  o.G = o.Hq / o.Hkv;
+  if (static_cast<int64_t>(o.B) * o.G > MAGE_MAX_ROWS)
+    return fail(MAGE_ERR_UNSUPPORTED, "block * (num_q_heads / num_kv_heads) must be <= 128");
+  if (static_cast<int64_t>(o.S) * o.Hkv > 8192)
+    return fail(MAGE_ERR_UNSUPPORTED, "num_seqs * num_kv_heads must be <= 8192");
+  o.R = o.B * o.G;
+  o.D = d->head_dim;
+  o.nrb = (o.R + 31) / 32;
+  o.units = o.S * o.Hkv;
+  o.scale = d->scale;
+  return MAGE_OK;
+}
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int64_t round_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }
+
+int env_int(const char* name, int dflt) {
+#ifdef MAGE_TUNING
+  const char* v = std::getenv(name);
+  if (v && *v) return std::atoi(v);
+#else
+  (void)name;
+#endif
+  return dflt;
+}
+
+// ---- launch plan ----------------------------------------------------------
+// Exact pass: split each (seq, KV head) prefix into chunks of `chunk` keys so
+// that about kExactTargetWgs work-groups are busy; never below the floor that
+// bounds the partial-result workspace.
+constexpr int kExactTargetWgs = 512;
+constexpr int kExactMinChunk = 512;
+constexpr int kExactSlotBudget = 4096;
+
+int exact_chunk_floor(int64_t units, int64_t max_n) {
+  return static_cast<int>(std::max<int64_t>(kExactMinChunk,
+                                            round_up(cdiv(units * max_n, kExactSlotBudget), 64)));
+}
+
+int exact_chunk(int64_t units, int64_t max_n, int64_t total_keys) {
+  int64_t c = round_up(cdiv(total_keys, env_int("MAGE_EXACT_WGS", kExactTargetWgs)), 64);
+  c = std::max<int64_t>(c, exact_chunk_floor(units, max_n));
+  const int forced = env_int("MAGE_EXACT_CHUNK", 0);
+  if (forced > 0) c = std::max<int64_t>(round_up(forced, 64), exact_chunk_floor(units, max_n));
+  return static_cast<int>(c);
+}
+
+// Sparse step: at most kSparseMaxChunks chunks per (seq, KV head), aiming at
+// one work-group per CU.
+constexpr int kSparseMaxChunks = 8;
+constexpr int kCus = 256;
+
+int sparse_chunk(int64_t units, int k) {
+  const int forced = env_int("MAGE_SPARSE_CHUNK", 0);
+  if (forced > 0) {
+    const int c = static_cast<int>(round_up(forced, 64));
+    return std::max<int>(c, static_cast<int>(round_up(cdiv(k, kSparseMaxChunks), 64)));
+  }
+  const int64_t want = std::min<int64_t>(kSparseMaxChunks, std::max<int64_t>(1, cdiv(kCus, units)));
+  return static_cast<int>(round_up(cdiv(k, want), 64));
+}
+
+constexpr int kScoreChunk = 2048;
+constexpr int64_t kCounterBytes = 65536;
+
+// ---- workspace layout ------------------------------------------------------
+struct Layout {
+  size_t cnt_sparse, cnt_topk, rowstat, part_ml, part_o, cand_bits, cand_pos, scores, total;
+  int64_t slots, cand_stride;
+};
+
+Layout make_layout(const Dims& d, int64_t max_n, int64_t k) {
+  Layout L{};
+  const int64_t U = d.units;
+  const int64_t exact_slots = U * cdiv(max_n, exact_chunk_floor(U, max_n));
+  const int64_t sparse_slots = U * std::min<int64_t>(kSparseMaxChunks, cdiv(k, 64));
+  L.slots = std::max(exact_slots, sparse_slots);
+  const int64_t kc = std::min<int64_t>(k, kTopkChunk);
+  L.cand_stride = cdiv(max_n, kTopkChunk) * kc;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = round_up(off + bytes, 256);
+    return at;
+  };
+  // fixed-size counter region at the start, shared by every entry point and
+  // left zero by every completed call: unit u uses words 2u (sparse merge)
+  // and 2u + 1 (top-k merge)
+  L.cnt_sparse = take(kCounterBytes);
+  L.cnt_topk = L.cnt_sparse + 4;
+  L.rowstat = take(U * kMaxRows * 4);
+  L.part_ml = take(L.slots * kMaxRows * 2 * 4);
+  L.part_o = take(L.slots * 4 * (d.D / 32) * 4 * kWave * 16);
+  L.cand_bits = take(U * L.cand_stride * 4);
+  L.cand_pos = take(U * L.cand_stride * 4);
+  L.scores = take(U * max_n * 4);
+  L.total = off;
+  return L;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+template <class T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+hipEvent_t internal_event() {
+  // one per thread and device: orders the select stream after the merge
+  thread_local hipEvent_t ev[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  if (!ev[dev] && hipEventCreateWithFlags(&ev[dev], hipEventDisableTiming) != hipSuccess)
+    ev[dev] = nullptr;
+  return ev[dev];
+}
+
+// ---- common argument bundle of the attention paths -------------------------
+struct KvArgs {
+  KvSource src;
+  SeqLens lens;
+  int64_t max_n;
+  int64_t total_keys;  // sum over sequences of N_s, times Hkv
+};
+
+mage_status contiguous_kv(const Dims& d, const uint16_t* k, const uint16_t* v, int32_t n,
+                          KvArgs& a) {
+  if (!k || !v) return fail(MAGE_ERR_INVALID_ARG, "k_cache / v_cache is null");
+  if (!aligned(k, 16) || !aligned(v, 16))
+    return fail(MAGE_ERR_INVALID_ARG, "k_cache / v_cache must be 16-byte aligned");
+  if (n < 1) return fail(MAGE_ERR_INVALID_ARG, "seq_len must be >= 1");
+  a.src = KvSource{k, v, nullptr, 0, 0, n};
+  std::memset(&a.lens, 0, sizeof a.lens);
+  a.max_n = n;
+  a.total_keys = static_cast<int64_t>(n) * d.units;
+  return MAGE_OK;
+}
+
+mage_status paged_kv(const Dims& d, const mage_paged_kv* kv, KvArgs& a) {
+  if (!kv) return fail(MAGE_ERR_INVALID_ARG, "kv is null");
+  if (!kv->k_pool || !kv->v_pool || !kv->page_table || !kv->seq_lens)
+    return fail(MAGE_ERR_INVALID_ARG, "paged kv has a null pointer");
+  if (!aligned(kv->k_pool, 16) || !aligned(kv->v_pool, 16))
+    return fail(MAGE_ERR_INVALID_ARG, "k_pool / v_pool must be 16-byte aligned");
+  if (d.S > MAGE_MAX_SEQS) return fail(MAGE_ERR_UNSUPPORTED, "num_seqs > MAGE_MAX_SEQS for a paged call");
+  const int ps = kv->page_size;
+  if (ps < 1 || ps > 1024 || (ps & (ps - 1)))
+    return fail(MAGE_ERR_INVALID_ARG, "page_size must be a power of two in [1, 1024]");
+  if (kv->max_pages < 1) return fail(MAGE_ERR_INVALID_ARG, "max_pages must be >= 1");
+  int shift = 0;
+  while ((1 << shift) < ps) ++shift;
+  a.src = KvSource{kv->k_pool, kv->v_pool, kv->page_table, kv->max_pages, shift, -1};
+  std::memset(&a.lens, 0, sizeof a.lens);
+  a.max_n = 0;
+  a.total_keys = 0;
+  for (int s = 0; s < d.S; ++s) {
+    const int32_t n = kv->seq_lens[s];
+    if (n < 1 || static_cast<int64_t>(n) > static_cast<int64_t>(kv->max_pages) * ps)
+      return fail(MAGE_ERR_INVALID_ARG, "seq_lens[s] must be in [1, max_pages * page_size]");
+    a.lens.n[s] = n;
+    a.max_n = std::max<int64_t>(a.max_n, n);
+    a.total_keys += static_cast<int64_t>(n) * d.Hkv;
+  }
+  return MAGE_OK;
+}
+
+template <int D>
+mage_status launch_select(const Dims& d, const uint16_t* q, const KvArgs& kv, int32_t k, float* o,
+                          float* lse, int32_t* idx, float* scores, int64_t score_stride, void* ws,
+                          const Layout& L, hipStream_t attn, hipStream_t sel, hipEvent_t idx_ready) {
+  const int64_t U = d.units;
+  const int chunk = exact_chunk(U, kv.max_n, kv.total_keys);
+  const int nch = static_cast<int>(cdiv(kv.max_n, chunk));
+  const float scale_log2 = d.scale * kLog2e;
+
+  AttnParams ap{};
+  ap.q = q;
+  ap.kv = kv.src;
+  ap.idx = nullptr;
+  ap.idx_k = 0;
+  ap.o = o;
+  ap.lse = lse;
+  ap.part_o = at<float>(ws, L.part_o);
+  ap.part_ml = at<float>(ws, L.part_ml);
+  ap.counters = at<uint32_t>(ws, L.cnt_sparse);
+  ap.S = d.S; ap.B = d.B; ap.Hq = d.Hq; ap.Hkv = d.Hkv; ap.G = d.G; ap.R = d.R;
+  ap.chunk = chunk;
+  ap.nchunk = nch;
+  ap.xcd_group = 0;
+  ap.scale_log2 = scale_log2;
+  ap.lens = kv.lens;
+  hipLaunchKernelGGL((attn_chunk_kernel<D, false>), dim3(static_cast<unsigned>(U * nch)),
+                     dim3(kThreads), 0, attn, ap);
+  if (hipError_t e = hipGetLastError(); e != hipSuccess) return hip_fail(e, "exact pass launch");
+
+  MergeParams mp{};
+  mp.part_o = ap.part_o;
+  mp.part_ml = ap.part_ml;
+  mp.o = o;
+  mp.lse = lse;
+  mp.rowstat = at<float>(ws, L.rowstat);
+  mp.S = d.S; mp.B = d.B; mp.Hq = d.Hq; mp.Hkv = d.Hkv; mp.G = d.G; mp.R = d.R; mp.nrb = d.nrb;
+  mp.chunk = chunk;
+  mp.nchunk = nch;
+  mp.n_uniform = kv.src.page_table ? -1 : kv.src.n_uniform;
+  mp.lens = kv.lens;
+  hipLaunchKernelGGL((exact_merge_kernel<D>), dim3(static_cast<unsigned>(U * d.nrb * (D / 32))),
+                     dim3(kThreads), 0, attn, mp);
+  if (hipError_t e = hipGetLastError(); e != hipSuccess) return hip_fail(e, "merge launch");
+
+  if (sel && sel != attn) {
+    hipEvent_t ev = internal_event();
+    if (!ev) return fail(MAGE_ERR_HIP, "could not create the stream-ordering event");
+    if (hipError_t e = hipEventRecord(ev, attn); e != hipSuccess) return hip_fail(e, "hipEventRecord");
+    if (hipError_t e = hipStreamWaitEvent(sel, ev, 0); e != hipSuccess)
+      return hip_fail(e, "hipStreamWaitEvent");
+  } else {
+    sel = attn;
+  }
+
+  ScoreParams sp{};
+  sp.q = q;
+  sp.kv = kv.src;
+  sp.rowstat = mp.rowstat;
+  sp.scores = scores ? scores : at<float>(ws, L.scores);
+  sp.stride = scores ? score_stride : kv.max_n;
+  sp.S = d.S; sp.B = d.B; sp.Hq = d.Hq; sp.Hkv = d.Hkv; sp.G = d.G; sp.R = d.R;
+  sp.chunk = env_int("MAGE_SCORE_CHUNK", kScoreChunk);
+  sp.nchunk = static_cast<int>(cdiv(kv.max_n, sp.chunk));
+  sp.reverse = env_int("MAGE_SCORE_REVERSE", 1);
+  sp.scale_log2 = scale_log2;
+  sp.lens = kv.lens;
+  hipLaunchKernelGGL((score_kernel<D>), dim3(static_cast<unsigned>(U * sp.nchunk)), dim3(kThreads), 0,
+                     sel, sp);
+  if (hipError_t e = hipGetLastError(); e != hipSuccess) return hip_fail(e, "score launch");
+
+  TopkParams tp{};
+  tp.scores = sp.scores;
+  tp.stride = sp.stride;
+  tp.idx = idx;
+  tp.k = k;
+  tp.cand_bits = at<uint32_t>(ws, L.cand_bits);
+  tp.cand_pos = at<int32_t>(ws, L.cand_pos);
+  tp.cand_stride = L.cand_stride;
+  tp.counters = at<uint32_t>(ws, L.cnt_topk);
+  tp.rows = static_cast<int32_t>(U);
+  tp.rows_per_seq = d.Hkv;
+  tp.n_uniform = kv.src.page_table ? -1 : kv.src.n_uniform;
+  tp.nchunk = static_cast<int>(cdiv(kv.max_n, kTopkChunk));
+  tp.lens = kv.lens;
+  hipLaunchKernelGGL(topk_kernel, dim3(static_cast<unsigned>(U * tp.nchunk)), dim3(kTopkThreads), 0,
+                     sel, tp);
+  if (hipError_t e = hipGetLastError(); e != hipSuccess) return hip_fail(e, "top-k launch");
+  if (idx_ready) {
+    if (hipError_t e = hipEventRecord(idx_ready, sel); e != hipSuccess)
+      return hip_fail(e, "hipEventRecord(idx_ready)");
+  }
+  return MAGE_OK;
+}
+
+template <int D>
+mage_status launch_sparse(const Dims& d, const uint16_t* q, const KvArgs& kv, const int32_t* idx,
+                          int32_t k, float* o, float* lse, void* ws, const Layout& L,
+                          hipStream_t stream) {
+  const int64_t U = d.units;
+  const int chunk = sparse_chunk(U, k);
+  const int nch = static_cast<int>(cdiv(k, chunk));
+  AttnParams ap{};
+  ap.q = q;
+  ap.kv = kv.src;
+  ap.idx = idx;
+  ap.idx_k = k;
+  ap.o = o;
+  ap.lse = lse;
+  ap.part_o = at<float>(ws, L.part_o);
+  ap.part_ml = at<float>(ws, L.part_ml);
+  ap.counters = at<uint32_t>(ws, L.cnt_sparse);
+  ap.S = d.S; ap.B = d.B; ap.Hq = d.Hq; ap.Hkv = d.Hkv; ap.G = d.G; ap.R = d.R;
+  ap.chunk = chunk;
+  ap.nchunk = nch;
+  ap.xcd_group = env_int("MAGE_SPARSE_XCD", 1) && nch > 1;
+  ap.scale_log2 = d.scale * kLog2e;
+  ap.lens = kv.lens;
+  const int64_t grid = ap.xcd_group ? round_up(U, 8) * nch : U * nch;
+  hipLaunchKernelGGL((attn_chunk_kernel<D, true>), dim3(static_cast<unsigned>(grid)), dim3(kThreads),
+                     0, stream, ap);
+  if (hipError_t e = hipGetLastError(); e != hipSuccess) return hip_fail(e, "sparse launch");
+  return MAGE_OK;
+}
+
+mage_status check_ws(void* ws, size_t bytes, const Layout& L) {
+  if (!ws) return fail(MAGE_ERR_INVALID_ARG, "workspace is null");
+  if (!aligned(ws, 256)) return fail(MAGE_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  if (bytes < L.total) return fail(MAGE_ERR_WORKSPACE_TOO_SMALL, "workspace too small");
+  return MAGE_OK;
+}
+
+mage_status common_select_checks(const uint16_t* q, int32_t k, float* o, float* lse, int32_t* idx,
+                                 float* scores) {
+  if (!q || !o || !idx) return fail(MAGE_ERR_INVALID_ARG, "q, o and idx must not be null");
+  if (!aligned(q, 16) || !aligned(o, 16)) return fail(MAGE_ERR_INVALID_ARG, "q and o must be 16-byte aligned");
+  if (!aligned(idx, 4) || (lse && !aligned(lse, 4)) || (scores && !aligned(scores, 4)))
+    return fail(MAGE_ERR_INVALID_ARG, "idx, lse and scores must be 4-byte aligned");
+  if (k < 1) return fail(MAGE_ERR_INVALID_ARG, "k must be >= 1");
+  return MAGE_OK;
+}
+
+__global__ void fill_zero_kernel(uint32_t* p, size_t words) {
+  for (size_t i = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; i < words;
+       i += static_cast<size_t>(gridDim.x) * blockDim.x)
+    p[i] = 0u;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t mage_workspace_bytes(const mage_dims* dims, int32_t max_seq_len, int32_t k) {
+  Dims d;
+  if (check_dims(dims, d) != MAGE_OK || max_seq_len < 1 || k < 1) return 0;
+  return make_layout(d, max_seq_len, k).total;
+}
+
+mage_status mage_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!workspace || !aligned(workspace, 4) || workspace_bytes % 4)
+    return fail(MAGE_ERR_INVALID_ARG, "workspace must be non-null, 4-byte aligned, a multiple of 4 bytes");
+  const size_t words = workspace_bytes / 4;
+  if (words == 0) return MAGE_OK;
+  const unsigned blocks = static_cast<unsigned>(std::min<size_t>(4096, cdiv(words, 256)));
+  hipLaunchKernelGGL(fill_zero_kernel, dim3(blocks), dim3(256), 0, stream,
+                     static_cast<uint32_t*>(workspace), words);
+  if (hipError_t e = hipGetLastError(); e != hipSuccess) return hip_fail(e, "workspace init launch");
+  return MAGE_OK;
+}
+
+mage_status mage_select_exact(const mage_dims* dims, const uint16_t* q, const uint16_t* k_cache,
+                              const uint16_t* v_cache, int32_t seq_len, int32_t k, float* o,
+                              float* lse, int32_t* idx, float* scores, void* workspace,
+                              size_t workspace_bytes, hipStream_t attn_stream,
+                              hipStream_t select_stream, hipEvent_t idx_ready) {
+  Dims d;
+  if (mage_status st = check_dims(dims, d); st != MAGE_OK) return st;
+  if (mage_status st = common_select_checks(q, k, o, lse, idx, scores); st != MAGE_OK) return st;
+  KvArgs kv;
+  if (mage_status st = contiguous_kv(d, k_cache, v_cache, seq_len, kv); st != MAGE_OK) return st;
+  const Layout L = make_layout(d, kv.max_n, k);
+  if (mage_status st = check_ws(workspace, workspace_bytes, L); st != MAGE_OK) return st;
+  return d.D == 128 ? launch_select<128>(d, q, kv, k, o, lse, idx, scores, seq_len, workspace, L,
+                                         attn_stream, select_stream, idx_ready)
+                    : launch_select<64>(d, q, kv, k, o, lse, idx, scores, seq_len, workspace, L,
+                                        attn_stream, select_stream, idx_ready);
+}
+
+mage_status mage_select_exact_paged(const mage_dims* dims, const uint16_t* q, const mage_paged_kv* kvp,
+                                    int32_t k, float* o, float* lse, int32_t* idx, float* scores,
+                                    void* workspace, size_t workspace_bytes, hipStream_t attn_stream,
+                                    hipStream_t select_stream, hipEvent_t idx_ready) {
+  Dims d;
+  if (mage_status st = check_dims(dims, d); st != MAGE_OK) return st;
+  if (mage_status st = common_select_checks(q, k, o, lse, idx, scores); st != MAGE_OK) return st;
+  KvArgs kv;
+  if (mage_status st = paged_kv(d, kvp, kv); st != MAGE_OK) return st;
+  const Layout L = make_layout(d, kv.max_n, k);
+  if (mage_status st = check_ws(workspace, workspace_bytes, L); st != MAGE_OK) return st;
+  return d.D == 128 ? launch_select<128>(d, q, kv, k, o, lse, idx, scores, kv.max_n, workspace, L,
+                                         attn_stream, select_stream, idx_ready)
+                    : launch_select<64>(d, q, kv, k, o, lse, idx, scores, kv.max_n, workspace, L,
+                                        attn_stream, select_stream, idx_ready);
+}
+
+static mage_status sparse_common(const mage_dims* dims, const uint16_t* q, const int32_t* idx,
+                                 int32_t k, float* o, float* lse, Dims& d) {
+  if (mage_status st = check_dims(dims, d); st != MAGE_OK) return st;
+  if (!q || !o || !idx) return fail(MAGE_ERR_INVALID_ARG, "q, o and idx must not be null");
+  if (!aligned(q, 16) || !aligned(o, 16)) return fail(MAGE_ERR_INVALID_ARG, "q and o must be 16-byte aligned");
+  if (!aligned(idx, 4) || (lse && !aligned(lse, 4)))
+    return fail(MAGE_ERR_INVALID_ARG, "idx and lse must be 4-byte aligned");
+  if (k < 1) return fail(MAGE_ERR_INVALID_ARG, "k must be >= 1");
+  return MAGE_OK;
+}
+
+mage_status mage_sparse_attn(const mage_dims* dims, const uint16_t* q, const uint16_t* k_cache,
+                             const uint16_t* v_cache, int32_t seq_len, const int32_t* idx, int32_t k,
+                             float* o, float* lse, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
+  Dims d;
+  if (mage_status st = sparse_common(dims, q, idx, k, o, lse, d); st != MAGE_OK) return st;
+  KvArgs kv;
+  if (mage_status st = contiguous_kv(d, k_cache, v_cache, seq_len, kv); st != MAGE_OK) return st;
+  const Layout L = make_layout(d, kv.max_n, k);
+  if (mage_status st = check_ws(workspace, workspace_bytes, L); st != MAGE_OK) return st;
+  return d.D == 128 ? launch_sparse<128>(d, q, kv, idx, k, o, lse, workspace, L, stream)
+                    : launch_sparse<64>(d, q, kv, idx, k, o, lse, workspace, L, stream);
+}
+
+mage_status mage_sparse_attn_paged(const mage_dims* dims, const uint16_t* q, const mage_paged_kv* kvp,
+                                   const int32_t* idx, int32_t k, float* o, float* lse,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  Dims d;
+  if (mage_status st = sparse_common(dims, q, idx, k, o, lse, d); st != MAGE_OK) return st;
+  KvArgs kv;
+  if (mage_status st = paged_kv(d, kvp, kv); st != MAGE_OK) return st;
+  const Layout L = make_layout(d, kv.max_n, k);
+  if (mage_status st = check_ws(workspace, workspace_bytes, L); st != MAGE_OK) return st;
+  return d.D == 128 ? launch_sparse<128>(d, q, kv, idx, k, o, lse, workspace, L, stream)
+                    : launch_sparse<64>(d, q, kv, idx, k, o, lse, workspace, L, stream);
+}
+
+mage_status mage_topk(int32_t rows, const float* scores, int64_t row_stride, const int32_t* lens,
+                      int32_t n, int32_t k, int32_t* idx, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
+  if (rows < 1 || n < 1 || k < 1) return fail(MAGE_ERR_INVALID_ARG, "rows, n and k must be >= 1");
+  if (!scores || !idx) return fail(MAGE_ERR_INVALID_ARG, "scores and idx must not be null");
+  if (!aligned(scores, 4) || !aligned(idx, 4)) return fail(MAGE_ERR_INVALID_ARG, "scores and idx must be 4-byte aligned");
+  if (row_stride < n) return fail(MAGE_ERR_INVALID_ARG, "row_stride must be >= n");
+  if (lens && rows > MAGE_MAX_SEQS)
+    return fail(MAGE_ERR_UNSUPPORTED, "per-row lengths need rows <= MAGE_MAX_SEQS");
+  SeqLens sl;
+  std::memset(&sl, 0, sizeof sl);
+  if (lens) {
+    for (int r = 0; r < rows; ++r) {
+      if (lens[r] < 1 || lens[r] > n) return fail(MAGE_ERR_INVALID_ARG, "lens[r] must be in [1, n]");
+      sl.n[r] = lens[r];
+    }
+  }
+  if (rows > 8192) return fail(MAGE_ERR_UNSUPPORTED, "rows must be <= 8192");
+  // workspace: the full layout for one KV head per row
+  Dims d{};
+  d.S = rows; d.B = 1; d.Hq = 1; d.Hkv = 1; d.G = 1; d.R = 1; d.D = 64; d.nrb = 1; d.units = rows;
+  d.scale = 1.f;
+  const Layout L = make_layout(d, n, k);
+  if (mage_status st = check_ws(workspace, workspace_bytes, L); st != MAGE_OK) return st;
+  TopkParams tp{};
+  tp.scores = scores;
+  tp.stride = row_stride;
+  tp.idx = idx;
+  tp.k = k;
+  tp.counters = at<uint32_t>(workspace, L.cnt_topk);
+  tp.cand_bits = at<uint32_t>(workspace, L.cand_bits);
+  tp.cand_pos = at<int32_t>(workspace, L.cand_pos);
+  tp.cand_stride = L.cand_stride;
+  tp.rows = rows;
+  tp.rows_per_seq = 1;
+  tp.n_uniform = lens ? -1 : n;
+  tp.nchunk = static_cast<int>(cdiv(n, kTopkChunk));
+  tp.lens = sl;
+  hipLaunchKernelGGL(topk_kernel, dim3(static_cast<unsigned>(static_cast<int64_t>(rows) * tp.nchunk)),
+                     dim3(kTopkThreads), 0, stream, tp);
+  if (hipError_t e = hipGetLastError(); e != hipSuccess) return hip_fail(e, "top-k launch");
+  return MAGE_OK;
+}
+
+const char* mage_status_string(mage_status status) {
+  switch (status) {
+    case MAGE_OK: return "ok";
+    case MAGE_ERR_INVALID_ARG: return "invalid argument";
+    case MAGE_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MAGE_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case MAGE_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* mage_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,89 @@
+// Shared device-side definitions for the gfx950 kernels of the MAGE hot path.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mage {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr int kThreads = 256;      // attention / score work-groups: 4 waves
+constexpr int kTileKeys = 64;      // keys staged in LDS per iteration
+constexpr int kMaxRows = 128;      // R = B * G rows per KV head, 4 row blocks of 32
+constexpr int kMaxSeqs = 256;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Host-side sequence table carried in kernel arguments (ragged paged batches).
+struct SeqLens {
+  int32_t n[kMaxSeqs];
+};
+
+// KV row addressing shared by the exact pass, the score sweep and the sparse
+// step. Contiguous: [S][Hkv][N][d]. Paged: pool [P][Hkv][page][d] with
+// position p of sequence s in page table[s * max_pages + (p >> shift)].
+struct KvSource {
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* page_table;  // null for the contiguous layout
+  int32_t max_pages;
+  int32_t page_shift;
+  int32_t n_uniform;          // contiguous prefix length (all sequences)
+};
+
+__device__ __forceinline__ int64_t kv_row(const KvSource& kv, int s, int h, int hkv, int p,
+                                          int d) {
+  if (kv.page_table == nullptr) {
+    return ((static_cast<int64_t>(s) * hkv + h) * kv.n_uniform + p) * d;
+  }
+  const int64_t page = kv.page_table[static_cast<int64_t>(s) * kv.max_pages + (p >> kv.page_shift)];
+  const int slot = p & ((1 << kv.page_shift) - 1);
+  return (((page * hkv + h) << kv.page_shift) + slot) * d;
+}
+
+__device__ __forceinline__ int seq_len_of(const KvSource& kv, const SeqLens& lens, int s) {
+  return kv.page_table ? lens.n[s] : kv.n_uniform;
+}
+
+__device__ __forceinline__ float wave_max_pair(float x) {
+  // lanes l and l ^ 32 hold the two halves of one row
+  return fmaxf(x, __shfl_xor(x, 32));
+}
+
+__device__ __forceinline__ float wave_sum_pair(float x) { return x + __shfl_xor(x, 32); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ u32x4 load16(const uint16_t* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+// bf16 pair (packed in one dword) -> two fp32
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Two fp32 -> packed fp16 pair, round to nearest even (one v_cvt_pk_f16_f32 on
+// gfx950). Used for bf16 V values (exact in fp16 for |v| in [2^-14, 65504])
+// and for probabilities in [0, 1].
+__device__ __forceinline__ uint32_t pack_f16(float a, float b) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  h2 r;
+  r.x = static_cast<_Float16>(a);
+  r.y = static_cast<_Float16>(b);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+  const int lane = __lane_id();
+  return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+
+}  // namespace mage

@@ -1,0 +1,358 @@
+// Selection kernels of the MAGE hot path on gfx950: the block-averaged score
+// sweep and the per-(sequence, KV head) top-k.
+//
+// Score (MAGE page, atlas.scime.ai summary, "Problem" and "Approach": the
+// step-1 exact pass reveals one top-k subset for the whole block): for prefix
+// position p of KV head h,
+//     score[p] = (1/R) sum_r exp(scale q_r.k_p - M_r) / L_r
+// over the R = B*G rows sharing the head, with (M_r, L_r) the row's final
+// softmax max and sum from the exact pass. In log2 units the kernel computes
+// exp2(x_r[p] - c_r) with c_r = M_r + log2 L_r.
+//
+// Top-k: the k_eff largest scores, ties to the lower position, ascending
+// output. Scores are >= +0, so their fp32 bit patterns order like the values
+// and the selection is integer work on those bits: an MSB-first radix select
+// (digits of 12, 11 and 9 bits, LDS histograms) finds the k-th largest bit
+// pattern T and how many entries equal to T to keep; an index-ordered
+// compaction (wave ballots + prefix popcounts) then keeps every entry > T and
+// the lowest-positioned entries == T. Each work-group does this for a
+// 16384-position chunk held in LDS; the last chunk of a head to finish runs
+// the same selection over the concatenated per-chunk winners, which are in
+// position order, so its output is already ascending.
+#pragma once
+
+#include "mage_common.hpp"
+
+namespace mage {
+
+struct ScoreParams {
+  const uint16_t* q;
+  KvSource kv;
+  const float* rowstat;     // per (unit, row) max + log2(sum)
+  float* scores;            // [S][Hkv][stride]
+  int64_t stride;
+  int32_t S, B, Hq, Hkv, G, R;
+  int32_t chunk, nchunk;
+  int32_t reverse;          // sweep tiles last-to-first
+  float scale_log2;
+  SeqLens lens;
+};
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void score_kernel(ScoreParams p) {
+  constexpr int kCpr = D / 8;
+  constexpr int kKpt = kTileKeys * kCpr / kThreads;
+  constexpr int kNks = D / 16;
+  __shared__ __attribute__((aligned(16))) uint16_t s_k[kTileKeys * D];
+  __shared__ float s_col[4][kTileKeys];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int hh = lane >> 5, n = lane & 31;
+  const int u = blockIdx.x / p.nchunk, c = blockIdx.x % p.nchunk;
+  const int s = u / p.Hkv, h = u - s * p.Hkv;
+  const int ns = seq_len_of(p.kv, p.lens, s);
+  const int e0 = c * p.chunk, e1 = min(e0 + p.chunk, ns);
+  if (e0 >= e1) return;
+  const int nrb = (p.R + 31) >> 5;
+  const bool computes = w < nrb;
+
+  // A operand: Q row 32w + n, d slice 16ks + 8hh
+  bf16x8 qf[kNks];
+  {
+    const int r = 32 * w + n;
+    if (computes && r < p.R) {
+      const int b = r / p.G, g = r - b * p.G;
+      const uint16_t* qrow = p.q + ((static_cast<int64_t>(s) * p.B + b) * p.Hq + h * p.G + g) * D;
+#pragma unroll
+      for (int ks = 0; ks < kNks; ++ks)
+        qf[ks] = __builtin_bit_cast(bf16x8, load16(qrow + 16 * ks + 8 * hh));
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < kNks; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
+    }
+  }
+  // accumulator register i of this lane is row 32w + 8(i/4) + 4hh + (i%4)
+  float crow[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int r = 32 * w + 8 * (i >> 2) + 4 * hh + (i & 3);
+    crow[i] = (computes && r < p.R) ? p.rowstat[static_cast<int64_t>(u) * kMaxRows + r]
+                                    : __builtin_inff();
+  }
+  const float inv_r = 1.f / static_cast<float>(p.R);
+
+  const int lc = tid % kCpr, kg = tid / kCpr;
+  u32x4 kreg[kKpt];
+  const int ntiles = (e1 - e0 + kTileKeys - 1) / kTileKeys;
+  auto tile_of = [&](int t) { return p.reverse ? ntiles - 1 - t : t; };
+  auto issue = [&](int tile) {
+#pragma unroll
+    for (int j = 0; j < kKpt; ++j) {
+      const int e = e0 + tile * kTileKeys + kg * kKpt + j;
+      if (e < e1)
+        kreg[j] = load16(p.kv.k + kv_row(p.kv, s, h, p.Hkv, e, D) + lc * 8);
+      else
+        kreg[j] = u32x4{0, 0, 0, 0};
+    }
+  };
+
+  issue(tile_of(0));
+  for (int t = 0; t < ntiles; ++t) {
+    const int tile = tile_of(t);
+#pragma unroll
+    for (int j = 0; j < kKpt; ++j) {
+      const int key = kg * kKpt + j;
+      *reinterpret_cast<u32x4*>(&s_k[key * D + ((lc ^ (key % kCpr)) * 8)]) = kreg[j];
+    }
+    __syncthreads();
+    if (t + 1 < ntiles) issue(tile_of(t + 1));
+    if (computes) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        f32x16 acc;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+        const int krow = 32 * kb + n;
+#pragma unroll
+        for (int ks = 0; ks < kNks; ++ks) {
+          const int phys = (2 * ks + hh) ^ (krow % kCpr);
+          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&s_k[krow * D + phys * 8]);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[ks], kf, acc, 0, 0, 0);
+        }
+        // S[row][key 32kb + n]; sum the probabilities of this wave's 32 rows
+        float col = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) col += fast_exp2(acc[i] * p.scale_log2 - crow[i]);
+        col = wave_sum_pair(col);
+        if (hh == 0) s_col[w][krow] = col;
+      }
+    }
+    __syncthreads();
+    if (tid < kTileKeys) {
+      const int e = e0 + tile * kTileKeys + tid;
+      if (e < e1) {
+        float sum = 0.f;
+        for (int ww = 0; ww < nrb; ++ww) sum += s_col[ww][tid];
+        p.scores[static_cast<int64_t>(u) * p.stride + e] = sum * inv_r;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// top-k
+
+constexpr int kTopkThreads = 1024;
+constexpr int kTopkChunk = 16384;
+constexpr int kTopkWaves = kTopkThreads / kWave;
+
+struct TopkParams {
+  const float* scores;      // row u at scores + u * stride
+  int64_t stride;
+  int32_t* idx;             // [rows][k]
+  int32_t k;
+  uint32_t* cand_bits;      // per row: nchunk * min(k, chunk) winners
+  int32_t* cand_pos;
+  int64_t cand_stride;
+  uint32_t* counters;       // word 2u per row (self-resetting)
+  int32_t rows;
+  int32_t rows_per_seq;     // row u belongs to sequence u / rows_per_seq
+  int32_t n_uniform;        // >= 0: every row has this many entries; else lens
+  int32_t nchunk;
+  SeqLens lens;
+};
+
+struct TopkShared {
+  uint32_t hist[4096];
+  int32_t wsum[kTopkWaves];
+  int32_t wsum2[kTopkWaves];
+  int32_t res[2];
+};
+
+// Block-wide inclusive prefix sum of one int per thread; also returns the total.
+__device__ __forceinline__ int block_inclusive_scan(int v, int32_t* wsum, int& total) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(v, off);
+    if (lane >= off) v += y;
+  }
+  if (lane == 63) wsum[wv] = v;
+  __syncthreads();
+  int before = 0;
+  total = 0;
+  for (int i = 0; i < kTopkWaves; ++i) {
+    const int t = wsum[i];
+    before += i < wv ? t : 0;
+    total += t;
+  }
+  __syncthreads();
+  return v + before;
+}
+
+// MSB-first radix select over n bit patterns: the kk-th largest value T, and
+// how many entries equal to T belong to the top kk (need >= 1).
+__device__ void radix_select(const uint32_t* data, int n, int kk, TopkShared& sh, uint32_t& T,
+                             int& need) {
+  const int tid = threadIdx.x;
+  uint32_t prefix = 0, pmask = 0;
+  int rem = kk;
+  constexpr int kShift[3] = {20, 9, 0};
+  constexpr int kBits[3] = {12, 11, 9};
+#pragma unroll
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = kShift[pass], nb = 1 << kBits[pass];
+    for (int i = tid; i < nb; i += kTopkThreads) sh.hist[i] = 0u;
+    __syncthreads();
+    for (int i = tid; i < n; i += kTopkThreads) {
+      const uint32_t x = data[i];
+      if ((x & pmask) == prefix) atomicAdd(&sh.hist[(x >> shift) & (nb - 1)], 1u);
+    }
+    __syncthreads();
+    // thread t owns bins [t*per, t*per + per); count above = entries with larger digits
+    const int per = (nb + kTopkThreads - 1) / kTopkThreads;
+    const int lo = tid * per;
+    int mine = 0;
+    for (int b = 0; b < per; ++b)
+      if (lo + b < nb) mine += static_cast<int>(sh.hist[lo + b]);
+    int total;
+    const int incl = block_inclusive_scan(mine, sh.wsum, total);
+    int above = total - incl;  // entries in bins above this thread's range
+    for (int b = per - 1; b >= 0; --b) {
+      const int bin = lo + b;
+      if (bin >= nb) continue;
+      const int cnt = static_cast<int>(sh.hist[bin]);
+      if (above < rem && rem <= above + cnt) {
+        sh.res[0] = bin;
+        sh.res[1] = rem - above;
+      }
+      above += cnt;
+    }
+    __syncthreads();
+    const int digit = sh.res[0];
+    rem = sh.res[1];
+    prefix |= static_cast<uint32_t>(digit) << shift;
+    pmask |= static_cast<uint32_t>(nb - 1) << shift;
+    __syncthreads();
+  }
+  T = prefix;
+  need = rem;
+}
+
+// Keep entries > T and the first `need` entries == T, in index order.
+// Writes out_pos[j] = pos_of(i) (and out_bits[j] = data[i] if out_bits).
+template <class PosOf>
+__device__ void ordered_compact(const uint32_t* data, int n, uint32_t T, int need, PosOf pos_of,
+                                uint32_t* out_bits, int32_t* out_pos, TopkShared& sh) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const uint64_t below = lanemask_lt();
+  int eq_base = 0, out_base = 0;
+  for (int j0 = 0; j0 < n; j0 += kTopkThreads) {
+    const int i = j0 + tid;
+    const bool valid = i < n;
+    const uint32_t x = valid ? data[i] : 0u;
+    const bool gt = valid && x > T;
+    const bool eq = valid && x == T;
+    const uint64_t meq = __ballot(eq);
+    if (lane == 0) sh.wsum[wv] = __popcll(meq);
+    __syncthreads();
+    int eq_before = 0, eq_total = 0;
+    for (int v = 0; v < kTopkWaves; ++v) {
+      const int t = sh.wsum[v];
+      eq_before += v < wv ? t : 0;
+      eq_total += t;
+    }
+    const int eq_rank = eq_base + eq_before + __popcll(meq & below);
+    const bool sel = gt || (eq && eq_rank < need);
+    const uint64_t msel = __ballot(sel);
+    if (lane == 0) sh.wsum2[wv] = __popcll(msel);
+    __syncthreads();
+    int sel_before = 0, sel_total = 0;
+    for (int v = 0; v < kTopkWaves; ++v) {
+      const int t = sh.wsum2[v];
+      sel_before += v < wv ? t : 0;
+      sel_total += t;
+    }
+    if (sel) {
+      const int o = out_base + sel_before + __popcll(msel & below);
+      out_pos[o] = pos_of(i);
+      if (out_bits) out_bits[o] = x;
+    }
+    eq_base += eq_total;
+    out_base += sel_total;
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkParams p) {
+  __shared__ uint32_t s_data[kTopkChunk];
+  __shared__ TopkShared sh;
+  __shared__ int s_last;
+  const int tid = threadIdx.x;
+  const int u = blockIdx.x / p.nchunk, c = blockIdx.x % p.nchunk;
+  if (u >= p.rows) return;
+  const int n = p.n_uniform >= 0 ? p.n_uniform : p.lens.n[u / p.rows_per_seq];
+  const int kk = min(p.k, n);
+  const int start = c * kTopkChunk;
+  if (start >= n) return;
+  const int len = min(kTopkChunk, n - start);
+  int32_t* out = p.idx + static_cast<int64_t>(u) * p.k;
+  const float* src = p.scores + static_cast<int64_t>(u) * p.stride + start;
+
+  if (kk == n) {  // every position is selected
+    for (int i = tid; i < len; i += kTopkThreads) out[start + i] = start + i;
+    if (c == 0)
+      for (int i = n + tid; i < p.k; i += kTopkThreads) out[i] = -1;
+    return;
+  }
+  const int nch = (n + kTopkChunk - 1) / kTopkChunk;
+  const int kc_stride = min(kk, kTopkChunk);
+  const int kc = min(kk, len);
+  uint32_t* cb = p.cand_bits + static_cast<int64_t>(u) * p.cand_stride + static_cast<int64_t>(c) * kc_stride;
+  int32_t* cp = p.cand_pos + static_cast<int64_t>(u) * p.cand_stride + static_cast<int64_t>(c) * kc_stride;
+
+  for (int i = tid; i < len; i += kTopkThreads) s_data[i] = __float_as_uint(src[i]);
+  __syncthreads();
+  if (nch == 1) {
+    // a single chunk: its winners are the answer
+    uint32_t T;
+    int need;
+    radix_select(s_data, len, kk, sh, T, need);
+    ordered_compact(s_data, len, T, need, [&](int i) { return start + i; }, nullptr, out, sh);
+    for (int i = kk + tid; i < p.k; i += kTopkThreads) out[i] = -1;
+    return;
+  }
+  if (kc == len) {
+    for (int i = tid; i < len; i += kTopkThreads) {
+      cb[i] = s_data[i];
+      cp[i] = start + i;
+    }
+  } else {
+    uint32_t T;
+    int need;
+    radix_select(s_data, len, kc, sh, T, need);
+    ordered_compact(s_data, len, T, need, [&](int i) { return start + i; }, cb, cp, sh);
+  }
+
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) {
+    const unsigned prev = atomicAdd(&p.counters[2 * u], 1u);
+    __threadfence();
+    s_last = prev == static_cast<unsigned>(nch - 1);
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  if (tid == 0) p.counters[2 * u] = 0u;
+  const uint32_t* all_bits = p.cand_bits + static_cast<int64_t>(u) * p.cand_stride;
+  const int32_t* all_pos = p.cand_pos + static_cast<int64_t>(u) * p.cand_stride;
+  const int total = (nch - 1) * kc_stride + min(kc_stride, n - (nch - 1) * kTopkChunk);
+  uint32_t T;
+  int need;
+  radix_select(all_bits, total, kk, sh, T, need);
+  ordered_compact(all_bits, total, T, need, [&](int i) { return all_pos[i]; }, nullptr, out, sh);
+  for (int i = kk + tid; i < p.k; i += kTopkThreads) out[i] = -1;
+}
+
+}  // namespace mage

@@ -1,0 +1,172 @@
+/*
+ * mage.h -- C ABI of the MI355X (gfx950) library for block-shared top-k sparse
+ * KV attention in block-diffusion decoding (the MAGE scheme).
+ *
+ * Method: "MAGE: All-[MASK] Block Already Knows Where to Look in Block
+ * Diffusion LLM" (atlas.scime.ai summary page).
+ *   - At denoising step 1 one exact attention pass runs for the all-[MASK]
+ *     block over the prefix KV cache; it also yields, per (sequence, KV head),
+ *     the top-k prefix positions that the whole block then shares
+ *     (summary paragraph and "Approach").
+ *   - All B tokens of a block share one KV subset ("Problem").
+ *   - Every later step attends only to that subset ("Approach").
+ *   - Selection runs on a second stream, overlapped with the step-1 output
+ *     (summary paragraph; first-step overhead under "Key results").
+ * The score that ranks positions is the softmax probability averaged over the
+ * B block tokens and the G query heads that share the KV head; ties are
+ * broken by the lower position.
+ *
+ * Notation: S sequences, B block tokens, Hq query heads, Hkv KV heads,
+ * G = Hq / Hkv, d head dim, R = B * G query rows per KV head, N (N_s) prefix
+ * length, k top-k budget, k_eff = min(k, N_s). Query head j reads KV head
+ * j / G. Row r = b * G + g of KV head h is query (token b, head h * G + g).
+ *
+ * Layouts (all row-major, all buffers device memory unless stated):
+ *   Q        bf16 [S][B][Hq][d]        (bf16 passed as uint16_t bit patterns)
+ *   K, V     bf16 [S][Hkv][N][d]       contiguous cache, one N for all seqs
+ *   pools    bf16 [P][Hkv][page][d]    paged cache; position p of sequence s
+ *                                      is slot p % page of page
+ *                                      page_table[s * max_pages + p / page]
+ *   O        fp32 [S][B][Hq][d]
+ *   lse      fp32 [S][B][Hq]           natural-log log-sum-exp of scale*q.k
+ *   scores   fp32 [S][Hkv][stride]     stride = N (contiguous) or
+ *                                      max_seq_len (paged); entries at
+ *                                      p >= N_s are left untouched
+ *   idx      int32 [S][Hkv][k]         ascending positions, -1 past k_eff
+ *
+ * Ownership: the caller owns every buffer, stream and event. The library
+ * never allocates device memory in these calls; all scratch lives in the
+ * caller's workspace (size from mage_workspace_bytes). Calls are
+ * asynchronous and stream-ordered; host-side argument checks happen before
+ * any launch, and a failed check launches nothing.
+ *
+ * Workspace contract: pass it zero-filled the first time (or call
+ * mage_workspace_init once); every call leaves the counter region zero again
+ * when its kernels complete. Calls that may run concurrently need distinct
+ * workspaces; a workspace may be reused once the previous call's work
+ * (including its select stream) is ordered before the new call.
+ *
+ * Errors: every entry point returns a mage_status and never aborts.
+ * MAGE_ERR_HIP carries the runtime's message in mage_last_error() (thread
+ * local). Content preconditions (finite values, valid page ids, unique idx
+ * entries) are documented, not checked: idx entries outside [0, N_s) are
+ * skipped by the sparse step, never dereferenced.
+ */
+#ifndef MAGE_H_
+#define MAGE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mage_status {
+  MAGE_OK = 0,
+  MAGE_ERR_INVALID_ARG = 1,          /* null pointer, bad size, Hq % Hkv != 0 */
+  MAGE_ERR_UNSUPPORTED = 2,          /* d not in {64, 128}, R > 128, S > MAGE_MAX_SEQS */
+  MAGE_ERR_WORKSPACE_TOO_SMALL = 3,
+  MAGE_ERR_HIP = 4                   /* launch or runtime failure; see mage_last_error() */
+} mage_status;
+
+/* Largest number of sequences one paged call takes (their lengths travel in
+ * the kernel arguments). */
+#define MAGE_MAX_SEQS 256
+/* Largest R = B * G rows per KV head. */
+#define MAGE_MAX_ROWS 128
+
+typedef struct mage_dims {
+  int32_t num_seqs;      /* S >= 1 */
+  int32_t block;         /* B >= 1, query tokens per block */
+  int32_t num_q_heads;   /* Hq >= 1 */
+  int32_t num_kv_heads;  /* Hkv >= 1, Hq % Hkv == 0, B * Hq / Hkv <= 128 */
+  int32_t head_dim;      /* d in {64, 128} */
+  float scale;           /* softmax scale applied to q.k (finite, > 0) */
+} mage_dims;
+
+/* A paged KV cache. seq_lens is HOST memory (read during the call). */
+typedef struct mage_paged_kv {
+  const uint16_t* k_pool;     /* bf16 [P][Hkv][page_size][d] */
+  const uint16_t* v_pool;     /* bf16 [P][Hkv][page_size][d] */
+  const int32_t* page_table;  /* device int32 [S][max_pages] physical page ids */
+  int32_t max_pages;          /* row stride of page_table */
+  int32_t page_size;          /* power of two, 1..1024 */
+  const int32_t* seq_lens;    /* HOST int32 [S], 1 <= N_s <= max_pages * page_size */
+} mage_paged_kv;
+
+/* Bytes of workspace that every entry point below needs for these dims, any
+ * prefix length <= max_seq_len and any top-k budget <= k. */
+size_t mage_workspace_bytes(const mage_dims* dims, int32_t max_seq_len, int32_t k);
+
+/* Zero the workspace's counter region on `stream` (a fill kernel, no memset
+ * node). Needed once per workspace unless it was allocated zero-filled. */
+mage_status mage_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Step 1 of a block (MAGE page, summary and "Approach"): exact attention of
+ * the block's queries over the whole prefix, the block-averaged score of every
+ * prefix position, and the top-k positions per (sequence, KV head).
+ *
+ * Exact pass (split over N, MFMA, online softmax) then the split merge run on
+ * attn_stream; O and lse are final when attn_stream reaches that point. The
+ * score sweep and top-k run on select_stream (after waiting for the merge);
+ * idx and scores are final when select_stream completes, and idx_ready (if
+ * non-null) is recorded there. select_stream may be null (= attn_stream).
+ * lse and scores may be null.
+ */
+mage_status mage_select_exact(const mage_dims* dims, const uint16_t* q,
+                              const uint16_t* k_cache, const uint16_t* v_cache,
+                              int32_t seq_len, int32_t k, float* o, float* lse,
+                              int32_t* idx, float* scores, void* workspace,
+                              size_t workspace_bytes, hipStream_t attn_stream,
+                              hipStream_t select_stream, hipEvent_t idx_ready);
+
+mage_status mage_select_exact_paged(const mage_dims* dims, const uint16_t* q,
+                                    const mage_paged_kv* kv, int32_t k, float* o,
+                                    float* lse, int32_t* idx, float* scores,
+                                    void* workspace, size_t workspace_bytes,
+                                    hipStream_t attn_stream, hipStream_t select_stream,
+                                    hipEvent_t idx_ready);
+
+/*
+ * A later denoising step (MAGE page, "Approach": later steps reuse the step-1
+ * subset): for every (sequence, KV head), gather the K/V rows named by
+ * idx[s][h][0..k) and compute attention of the block's queries over them.
+ * idx may be in any order; entries outside [0, N_s) are skipped (a head with
+ * no valid entry gets O = 0, lse = -inf). lse may be null.
+ */
+mage_status mage_sparse_attn(const mage_dims* dims, const uint16_t* q,
+                             const uint16_t* k_cache, const uint16_t* v_cache,
+                             int32_t seq_len, const int32_t* idx, int32_t k, float* o,
+                             float* lse, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream);
+
+mage_status mage_sparse_attn_paged(const mage_dims* dims, const uint16_t* q,
+                                   const mage_paged_kv* kv, const int32_t* idx, int32_t k,
+                                   float* o, float* lse, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Top-k of `rows` non-negative fp32 score rows (the selection step on its own):
+ * row r has lens[r] valid entries (lens is HOST memory; null means all rows
+ * have n entries) at scores + r * row_stride. Output idx [rows][k]: the
+ * k_eff = min(k, lens[r]) positions with the largest scores, ties to the lower
+ * position, in ascending order, then -1. Scores must be >= +0 and not NaN.
+ * The workspace must come from mage_workspace_bytes with a max_seq_len >= n
+ * and num_seqs * num_kv_heads >= rows.
+ */
+mage_status mage_topk(int32_t rows, const float* scores, int64_t row_stride,
+                      const int32_t* lens, int32_t n, int32_t k, int32_t* idx,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+const char* mage_status_string(mage_status status);
+const char* mage_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MAGE_H_ */

@@ -1,0 +1,142 @@
+"""The C ABI without a GPU: the library loads, exports every declared entry
+point, sizes workspaces, and rejects bad arguments before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_sparse_kv_amd as mage
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "mage.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(mage_\w+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = mage.lib()
+    names = declared_functions()
+    assert len(names) >= 9
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_hip_library_is_separate_from_the_oracle():
+    # the product library must not link or embed the oracle
+    data = open(mage.LIB_PATH, "rb").read()
+    assert b"oracle_" not in data
+
+
+def test_status_strings():
+    lib = mage.lib()
+    for st in range(5):
+        assert lib.mage_status_string(st)
+
+
+def dims(**kw):
+    d = dict(num_seqs=1, block=32, num_q_heads=32, num_kv_heads=8, head_dim=128, scale=1.0)
+    d.update(kw)
+    return mage.Dims(**d)
+
+
+def test_workspace_bytes():
+    small = mage.workspace_bytes(dims(), 32768, 512)
+    big = mage.workspace_bytes(dims(), 131072, 1024)
+    assert 0 < small < big
+    assert mage.workspace_bytes(dims(head_dim=96), 1024, 64) == 0
+    assert mage.workspace_bytes(dims(num_q_heads=30), 1024, 64) == 0
+    assert mage.workspace_bytes(dims(), 0, 64) == 0
+
+
+FAKE = ctypes.c_void_p(1 << 20)   # never dereferenced: every call below fails its checks first
+
+
+def call_select(d, n=1024, k=64, ws_bytes=1 << 40, q=FAKE, o=FAKE, idx=FAKE):
+    lib = mage.lib()
+    return lib.mage_select_exact(ctypes.byref(d), q, FAKE, FAKE, n, k, o, None, idx, None, FAKE,
+                                 ws_bytes, None, None, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=96), mage.ERR_UNSUPPORTED),
+    (dict(num_q_heads=30), mage.ERR_INVALID_ARG),
+    (dict(block=64), mage.ERR_UNSUPPORTED),           # R = 64 * 4 > 128
+    (dict(num_seqs=0), mage.ERR_INVALID_ARG),
+    (dict(scale=float("nan")), mage.ERR_INVALID_ARG),
+    (dict(scale=-1.0), mage.ERR_INVALID_ARG),
+])
+def test_select_rejects_bad_dims(kw, status):
+    assert call_select(dims(**kw)) == status
+
+
+def test_select_rejects_bad_arguments():
+    d = dims()
+    assert call_select(d, n=0) == mage.ERR_INVALID_ARG
+    assert call_select(d, k=0) == mage.ERR_INVALID_ARG
+    assert call_select(d, q=None) == mage.ERR_INVALID_ARG
+    assert call_select(d, idx=None) == mage.ERR_INVALID_ARG
+    assert call_select(d, q=ctypes.c_void_p((1 << 20) + 2)) == mage.ERR_INVALID_ARG  # misaligned
+    assert call_select(d, ws_bytes=16) == mage.ERR_WORKSPACE_TOO_SMALL
+    assert b"workspace" in mage.lib().mage_last_error()
+    assert call_select(mage.Dims(1, 1, 1, 1, 64, 1.0), ws_bytes=16) == mage.ERR_WORKSPACE_TOO_SMALL
+    lib = mage.lib()
+    assert lib.mage_select_exact(None, FAKE, FAKE, FAKE, 8, 4, FAKE, None, FAKE, None, FAKE, 1 << 30,
+                                 None, None, None) == mage.ERR_INVALID_ARG
+
+
+def test_sparse_rejects_bad_arguments():
+    lib = mage.lib()
+    d = dims()
+    args = lambda n, idx, k, wsb: (ctypes.byref(d), FAKE, FAKE, FAKE, n, idx, k, FAKE, None, FAKE, wsb, None)
+    assert lib.mage_sparse_attn(*args(1024, None, 64, 1 << 40)) == mage.ERR_INVALID_ARG
+    assert lib.mage_sparse_attn(*args(1024, FAKE, 0, 1 << 40)) == mage.ERR_INVALID_ARG
+    assert lib.mage_sparse_attn(*args(-5, FAKE, 64, 1 << 40)) == mage.ERR_INVALID_ARG
+    assert lib.mage_sparse_attn(*args(1024, FAKE, 64, 100)) == mage.ERR_WORKSPACE_TOO_SMALL
+
+
+def test_paged_rejects_bad_arguments():
+    lib = mage.lib()
+    d = dims(num_seqs=2)
+    lens = (ctypes.c_int32 * 2)(100, 40)
+    lp = ctypes.cast(lens, ctypes.POINTER(ctypes.c_int32))
+
+    def kv(page_size=16, max_pages=8, table=FAKE.value):
+        return mage.PagedKv(FAKE.value, FAKE.value, table, max_pages, page_size, lp)
+
+    def sel(k):
+        return lib.mage_select_exact_paged(ctypes.byref(d), FAKE, ctypes.byref(k), 64, FAKE, None,
+                                           FAKE, None, FAKE, 1 << 40, None, None, None)
+    assert sel(kv(page_size=12)) == mage.ERR_INVALID_ARG
+    assert sel(kv(max_pages=4)) == mage.ERR_INVALID_ARG      # 100 > 4 * 16
+    assert sel(kv(table=None)) == mage.ERR_INVALID_ARG
+    lens[1] = 0
+    assert sel(kv()) == mage.ERR_INVALID_ARG
+    big = dims(num_seqs=300, num_kv_heads=8)
+    k = kv()
+    assert lib.mage_sparse_attn_paged(ctypes.byref(big), FAKE, ctypes.byref(k), FAKE, 64, FAKE, None,
+                                      FAKE, 1 << 40, None) == mage.ERR_UNSUPPORTED
+
+
+def test_topk_rejects_bad_arguments():
+    lib = mage.lib()
+    assert lib.mage_topk(0, FAKE, 10, None, 10, 4, FAKE, FAKE, 1 << 30, None) == mage.ERR_INVALID_ARG
+    assert lib.mage_topk(2, FAKE, 5, None, 10, 4, FAKE, FAKE, 1 << 30, None) == mage.ERR_INVALID_ARG
+    assert lib.mage_topk(2, FAKE, 10, None, 10, 4, FAKE, FAKE, 8, None) == mage.ERR_WORKSPACE_TOO_SMALL
+    lens = (ctypes.c_int32 * 2)(3, 11)
+    assert lib.mage_topk(2, FAKE, 10, ctypes.cast(lens, ctypes.POINTER(ctypes.c_int32)), 10, 4, FAKE,
+                         FAKE, 1 << 30, None) == mage.ERR_INVALID_ARG
+
+
+def test_calls_fail_loudly_without_a_gpu():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("GPU present")
+    q = torch.zeros(1, 2, 1, 64, dtype=torch.bfloat16)
+    with pytest.raises((ValueError, RuntimeError)):
+        mage.sparse_attn(q, torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16),
+                         torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16),
+                         torch.zeros(1, 1, 4, dtype=torch.int32), 0.125)
