@@ -68,12 +68,15 @@ def lib():
                                         _vp, _sz, _vp, _vp, _vp]
         L.mage_select_exact_paged.argtypes = [P(Dims), _vp, P(PagedKv), _i32, _vp, _vp, _vp, _vp,
                                               _vp, _sz, _vp, _vp, _vp]
+        L.mage_exact_attn.argtypes = [P(Dims), _vp, _vp, _vp, _i32, _vp, _vp, _vp, _sz, _vp]
+        L.mage_exact_attn_paged.argtypes = [P(Dims), _vp, P(PagedKv), _vp, _vp, _vp, _sz, _vp]
         L.mage_sparse_attn.argtypes = [P(Dims), _vp, _vp, _vp, _i32, _vp, _i32, _vp, _vp, _vp, _sz,
                                        _vp]
         L.mage_sparse_attn_paged.argtypes = [P(Dims), _vp, P(PagedKv), _vp, _i32, _vp, _vp, _vp,
                                              _sz, _vp]
         L.mage_topk.argtypes = [_i32, _vp, ctypes.c_int64, P(_i32), _i32, _i32, _vp, _vp, _sz, _vp]
         for f in ("mage_workspace_init", "mage_select_exact", "mage_select_exact_paged",
+                  "mage_exact_attn", "mage_exact_attn_paged",
                   "mage_sparse_attn", "mage_sparse_attn_paged", "mage_topk"):
             getattr(L, f).restype = ctypes.c_int
         L.mage_status_string.argtypes = [ctypes.c_int]
@@ -235,6 +238,38 @@ def select_exact_paged(q, k_pool, v_pool, page_table, seq_lens, k: int, scale: f
     if idx_ready is not None:
         idx_ready.record(select_stream if select_stream is not None else torch.cuda.current_stream())
     return o, lse, idx, scores
+
+
+def exact_attn(q, k_cache, v_cache, scale: float, *, o=None, lse=None, workspace=None, stream=None):
+    """Exact attention of the block over the whole contiguous prefix (no selection)."""
+    S, B, Hq, d = q.shape
+    _, Hkv, N, _ = k_cache.shape
+    dims = make_dims(q, Hkv, scale)
+    dev = q.device
+    o = _out(o, (S, B, Hq, d), torch.float32, dev)
+    lse = _out(lse, (S, B, Hq), torch.float32, dev)
+    ws = _ws_obj(workspace, dev).get(workspace_bytes(dims, N, 1), stream)
+    _check(lib().mage_exact_attn(ctypes.byref(dims), _bf16_ptr(q, "q"), _bf16_ptr(k_cache, "k_cache"),
+                                 _bf16_ptr(v_cache, "v_cache"), N, _ptr(o), _ptr(lse), _ptr(ws),
+                                 ws.numel(), _stream(stream)), "mage_exact_attn")
+    return o, lse
+
+
+def exact_attn_paged(q, k_pool, v_pool, page_table, seq_lens, scale: float, *, o=None, lse=None,
+                     workspace=None, stream=None):
+    """Exact attention over a paged cache (no selection)."""
+    S, B, Hq, d = q.shape
+    Hkv = k_pool.shape[1]
+    dims = make_dims(q, Hkv, scale)
+    kv, keep, lens = _paged(k_pool, v_pool, page_table, seq_lens)
+    dev = q.device
+    o = _out(o, (S, B, Hq, d), torch.float32, dev)
+    lse = _out(lse, (S, B, Hq), torch.float32, dev)
+    ws = _ws_obj(workspace, dev).get(workspace_bytes(dims, max(lens), 1), stream)
+    _check(lib().mage_exact_attn_paged(ctypes.byref(dims), _bf16_ptr(q, "q"), ctypes.byref(kv),
+                                       _ptr(o), _ptr(lse), _ptr(ws), ws.numel(), _stream(stream)),
+           "mage_exact_attn_paged")
+    return o, lse
 
 
 def sparse_attn(q, k_cache, v_cache, idx, scale: float, *, o=None, lse=None, workspace=None,

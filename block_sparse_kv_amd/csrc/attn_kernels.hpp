@@ -8,20 +8,25 @@
 //
 // Work-group = 4 waves. Wave w owns query rows 32w..32w+31 of one KV head
 // (row r = b * G + g), so the block's B tokens and the G query heads that
-// share the KV head are one MFMA tile and every K/V row staged in LDS is used
-// by all of them. Per 64-key tile:
-//   S^T[key][row] = K Q^T        v_mfma_f32_32x32x16_bf16 (A = K from LDS,
-//                                B = Q held in registers)
-//   online softmax on the rows   (exp2 with scale * log2(e) folded in)
-//   O^T[d][row] += V^T P^T       v_mfma_f32_32x32x16_f16 (A = V^T from LDS,
-//                                stored transposed as fp16, B = P as fp16)
-// K is loaded into its MFMA A operand with the row order pi(m) (bits 2 and 3
-// of m swapped); with that order the S^T accumulator registers 8s..8s+7 of a
-// lane hold 8 consecutive keys, which is exactly the B operand layout of the
-// PV product, so P never leaves registers.
+// share the KV head form one MFMA tile and every K/V row staged in LDS is used
+// by all of them. K/V tiles of 64 rows stream global->LDS through a ring of
+// kStages buffers (direct LDS loads). Per tile and wave:
+//   S^T[key][row] = K Q^T       v_mfma_f32_32x32x16_bf16 (A = K from LDS,
+//                               B = Q held in registers)
+//   online softmax on the rows  (exp2, scale * log2(e) folded in)
+//   O^T[d][row] += V^T P^T      v_mfma_f32_32x32x16_bf16, twice: P is split
+//                               into bf16 hi + lo (P - hi), so the product keeps
+//                               ~16 mantissa bits of P; V^T comes straight from
+//                               the row-major bf16 tile via transpose reads.
+// K rows enter the A operand in the order pi(m) (bits 2 and 3 of m swapped):
+// then accumulator registers 8s..8s+7 of a lane hold 8 consecutive keys, which
+// is the B operand layout of the PV product, so P never leaves registers.
 #pragma once
 
+#include <type_traits>
+
 #include "mage_common.hpp"
+#include "tile_io.hpp"
 
 namespace mage {
 
@@ -54,6 +59,10 @@ struct MergeParams {
   int32_t n_uniform;        // >= 0: contiguous prefix length; < 0: use lens
   SeqLens lens;
 };
+
+constexpr int kMaxSparseChunk = 4096;   // idx entries per sparse work-group (LDS row table)
+constexpr int kMaxChunkPages = 4096;    // page ids per exact-pass work-group (paged layout)
+constexpr int kMaxMerge = 8;            // sparse chunks per unit (in-kernel merge)
 
 __device__ __forceinline__ int swap_bits23(int m) {
   return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
@@ -91,18 +100,122 @@ __device__ __forceinline__ void store_rows(const AttnParams& p, int s, int h, in
     p.lse[row] = l > 0.f ? (m + __log2f(l)) * kLn2 : -__builtin_inff();
 }
 
-template <int D, bool kSparse>
-__global__ __launch_bounds__(kThreads) void attn_chunk_kernel(AttnParams p) {
-  constexpr int kCpr = D / 8;                          // 16-byte pieces per K/V row
-  constexpr int kKpt = kTileKeys * kCpr / kThreads;    // keys per thread per tile (4 or 2)
-  constexpr int kNdb = D / 32;
-  constexpr int kNks = D / 16;
-  __shared__ __attribute__((aligned(16))) uint16_t s_k[kTileKeys * D];
-  __shared__ __attribute__((aligned(16))) uint16_t s_vt[D * kTileKeys];
-  __shared__ int s_ok[kTileKeys];
+// A row's softmax reference max is raised only when a tile's max exceeds it by
+// more than 2^kLazyLog2 (log2 units): the running O and sum are then rescaled,
+// otherwise probabilities up to 2^kLazyLog2 are accumulated as they are. The
+// result is the same softmax; the rescale (64 multiplies per lane) becomes rare.
+constexpr float kLazyLog2 = 8.f;
+
+// 8 waves: wave w handles row block w % 4 and key half w / 4 (keys 32h..32h+31
+// of every 64-key tile); the two waves of a row block merge at the end. Two
+// waves per SIMD lets one wave's softmax run under the other's MFMAs.
+constexpr int kAttnThreads = 512;
+
+// Online-softmax update of one 32-key half tile for one wave, then PV.
+//   k_base: LDS address of the half's first K row; kofs: this lane's K
+//   fragment offsets; v_addr: LDS address of the V tile + half offset + this
+//   lane's transpose-read offset; okm: validity bits of the half's 32 keys.
+template <int D>
+__device__ __forceinline__ void attend_half(uint32_t k_base, uint32_t v_addr,
+                                            const uint32_t (&kofs)[D / 16],
+                                            const bf16x8 (&qf)[D / 16], uint32_t okm,
+                                            float scale_log2, float& m_run, float& l_run,
+                                            f32x16 (&oacc)[D / 32], int lane) {
+  constexpr int kNdb = D / 32, kNks = D / 16;
+  const int hh = lane >> 5;
+  f32x16 sacc;
+  {
+    bf16x8 kf[kNks];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
+    k_frags<D, 0>(k_base, kofs, kf);
+#pragma unroll
+    for (int ks = 0; ks < kNks; ++ks)
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], sacc, 0, 0, 0);
+  }
+  // register i holds key 16(i/8) + 8hh + (i%8) of the half; raw q.k here
+  float mt = -__builtin_inff();
+  if (okm == ~0u) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mt = fmaxf(mt, sacc[i]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int key = 16 * (i >> 3) + 8 * hh + (i & 7);
+      const float x = ((okm >> key) & 1) ? sacc[i] : -__builtin_inff();
+      sacc[i] = x;
+      mt = fmaxf(mt, x);
+    }
+  }
+  mt = wave_max_pair(mt) * scale_log2;  // scale > 0
+  const bool grow = mt > m_run + kLazyLog2;
+  if (__ballot(grow)) {
+    const float m_new = grow ? mt : m_run;
+    const float alpha = grow ? fast_exp2(m_run - m_new) : 1.f;
+    l_run *= alpha;
+#pragma unroll
+    for (int db = 0; db < kNdb; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+    m_run = m_new;
+  }
+  const float neg_m = m_run == -__builtin_inff() ? 0.f : -m_run;
+  float rs = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float pv = fast_exp2(__builtin_fmaf(sacc[i], scale_log2, neg_m));
+    sacc[i] = pv;
+    rs += pv;
+  }
+  l_run += wave_sum_pair(rs);
+  // P = hi + lo, both bf16 (hi rounded to nearest, lo = P - hi rounded again)
+  typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+  bf16x8 phi[2], plo[2];
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2) {
+    u32x4 hw, lw;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float x0 = sacc[8 * s2 + 2 * j], x1 = sacc[8 * s2 + 2 * j + 1];
+      bf2 h;
+      h.x = static_cast<__bf16>(x0);
+      h.y = static_cast<__bf16>(x1);
+      const uint32_t hb = __builtin_bit_cast(uint32_t, h);
+      bf2 l;
+      l.x = static_cast<__bf16>(x0 - __uint_as_float(hb << 16));
+      l.y = static_cast<__bf16>(x1 - __uint_as_float(hb & 0xffff0000u));
+      hw[j] = hb;
+      lw[j] = __builtin_bit_cast(uint32_t, l);
+    }
+    phi[s2] = __builtin_bit_cast(bf16x8, hw);
+    plo[s2] = __builtin_bit_cast(bf16x8, lw);
+  }
+  bf16x8 vf[kNdb][2];
+  vt_frags_half<D>(v_addr, vf);
+#pragma unroll
+  for (int db = 0; db < kNdb; ++db)
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db][s2], phi[s2], oacc[db], 0, 0, 0);
+      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db][s2], plo[s2], oacc[db], 0, 0, 0);
+    }
+}
+
+template <int D, bool kSparse, int kStages>
+__global__ __launch_bounds__(kAttnThreads) void attn_chunk_kernel(AttnParams p) {
+  using G = TileGeom<D, kAttnThreads>;
+  constexpr int kNdb = D / 32, kNks = D / 16;
+  constexpr int kStageBytes = 2 * G::kBytes;
+  static_assert(kStages * kStageBytes >= 4 * kWave * (2 + 16 * kNdb) * 4, "pair-merge area");
+  __shared__ __attribute__((aligned(1024))) uint8_t s_ring[kStages * kStageBytes];
+  // sparse: K/V row index of every entry of the chunk (-1 = skipped)
+  // exact, paged: page ids of the chunk
+  __shared__ int32_t s_tab[kSparse ? kMaxSparseChunk : kMaxChunkPages];
   __shared__ int s_last;
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rb = w & 3, kh = w >> 2;
   const int hh = lane >> 5, n = lane & 31;
   const int units = p.S * p.Hkv;
   int u, c;
@@ -119,14 +232,40 @@ __global__ __launch_bounds__(kThreads) void attn_chunk_kernel(AttnParams p) {
   const int ns = seq_len_of(p.kv, p.lens, s);
   const int e0 = c * p.chunk;
   const int e1 = kSparse ? min(e0 + p.chunk, p.idx_k) : min(e0 + p.chunk, ns);
-  if (e0 >= e1) return;  // exact pass: chunk past this sequence's end (never in the sparse grid)
+  if (e0 >= e1) return;  // exact pass: chunk past this sequence's end
   const int nrb = (p.R + 31) >> 5;
-  const bool computes = w < nrb;
+  const bool computes = rb < nrb;
+  const bool paged = p.kv.page_table != nullptr;
+  const int pshift = p.kv.page_shift, pmask = (1 << p.kv.page_shift) - 1;
+  const int64_t seq_base = paged ? 0 : (static_cast<int64_t>(s) * p.Hkv + h) * p.kv.n_uniform;
+  const int32_t* ptab = paged ? p.kv.page_table + static_cast<int64_t>(s) * p.kv.max_pages : nullptr;
 
-  // Q rows of this wave as MFMA B operand fragments (d slice 16ks + 8hh .. +7)
+  // ---- prologue: row tables in LDS -----------------------------------------
+  const int cnt = e1 - e0;
+  const int page0 = e0 >> pshift;
+  if constexpr (kSparse) {
+    for (int i = tid; i < cnt; i += kAttnThreads) {
+      const int pos = p.idx[static_cast<int64_t>(u) * p.idx_k + e0 + i];
+      int row = -1;
+      if (pos >= 0 && pos < ns) {
+        if (paged)
+          row = ((ptab[pos >> pshift] * p.Hkv + h) << pshift) + (pos & pmask);
+        else
+          row = static_cast<int>(seq_base + pos);
+      }
+      s_tab[i] = row;
+    }
+  } else {
+    if (paged) {
+      const int np = ((e1 - 1) >> pshift) - page0 + 1;
+      for (int i = tid; i < np; i += kAttnThreads) s_tab[i] = ptab[page0 + i];
+    }
+  }
+
+  // Q rows of this row block as MFMA B operand fragments (d slice 16ks + 8hh .. +7)
   bf16x8 qf[kNks];
   {
-    const int r = 32 * w + n;
+    const int r = 32 * rb + n;
     if (computes && r < p.R) {
       const int b = r / p.G, g = r - b * p.G;
       const uint16_t* qrow = p.q + ((static_cast<int64_t>(s) * p.B + b) * p.Hq + h * p.G + g) * D;
@@ -138,6 +277,26 @@ __global__ __launch_bounds__(kThreads) void attn_chunk_kernel(AttnParams p) {
       for (int ks = 0; ks < kNks; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
     }
   }
+  __syncthreads();  // row tables visible, Q loads complete (vmcnt drained)
+
+  // element offset of the K/V row holding chunk entry e (always a readable row)
+  auto row_of_entry = [&](int e) -> int64_t {
+    if constexpr (kSparse) {
+      const int row = s_tab[min(e, e1 - 1) - e0];
+      return static_cast<int64_t>(row < 0 ? 0 : row) * D;
+    } else {
+      const int pos = min(e, e1 - 1);
+      if (paged) {
+        const int64_t page = s_tab[(pos >> pshift) - page0];
+        return (((page * p.Hkv + h) << pshift) + (pos & pmask)) * D;
+      }
+      return (seq_base + pos) * D;
+    }
+  };
+  auto valid_entry = [&](int e) -> bool {
+    if constexpr (kSparse) return e < e1 && s_tab[e - e0] >= 0;
+    else return e < e1;
+  };
 
   f32x16 oacc[kNdb];
 #pragma unroll
@@ -145,177 +304,89 @@ __global__ __launch_bounds__(kThreads) void attn_chunk_kernel(AttnParams p) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
   float m_run = -__builtin_inff(), l_run = 0.f;
+  uint32_t kofs[kNks];
+  k_frag_offsets<D>(swap_bits23(n), hh, kofs);
+  const uint32_t ring_base = lds_addr(s_ring);
+  const uint32_t k_half = kh * 32 * G::kRowBytes;
+  const uint32_t v_half = G::kBytes + kh * 2048 + vt_lane_offset(lane);
 
-  // loader mapping: piece lc of keys kg*kKpt .. kg*kKpt + kKpt-1
-  const int lc = tid % kCpr, kg = tid / kCpr;
-  u32x4 kreg[kKpt], vreg[kKpt];
-  int okreg[kKpt];
-  const int ntiles = (e1 - e0 + kTileKeys - 1) / kTileKeys;
-
+  const int ntiles = (cnt + kTileKeys - 1) / kTileKeys;
   auto issue = [&](int tile) {
-#pragma unroll
-    for (int j = 0; j < kKpt; ++j) {
-      const int e = e0 + tile * kTileKeys + kg * kKpt + j;
-      bool ok = e < e1;
-      int pos = e;
-      if (kSparse) {
-        pos = ok ? p.idx[static_cast<int64_t>(u) * p.idx_k + e] : -1;
-        ok = ok && pos >= 0 && pos < ns;
-      }
-      okreg[j] = ok;
-      if (ok) {
-        const int64_t off = kv_row(p.kv, s, h, p.Hkv, pos, D) + lc * 8;
-        kreg[j] = load16(p.kv.k + off);
-        vreg[j] = load16(p.kv.v + off);
-      } else {
-        kreg[j] = u32x4{0, 0, 0, 0};
-        vreg[j] = u32x4{0, 0, 0, 0};
-      }
-    }
+    uint8_t* st = s_ring + (tile % kStages) * kStageBytes;
+    const int base = e0 + tile * kTileKeys;
+    issue_tile<D, true, kAttnThreads>(st, st + G::kBytes, p.kv.k, p.kv.v,
+                                      [&](int r) { return row_of_entry(base + r); }, w, lane);
   };
-
-  auto stage = [&]() {
+  // One barrier per tile: after it, every wave's loads of tile t have landed
+  // and every wave has finished tile t-1, whose stage is refilled right away.
 #pragma unroll
-    for (int j = 0; j < kKpt; ++j) {
-      const int key = kg * kKpt + j;
-      const int phys = lc ^ (key % kCpr);
-      *reinterpret_cast<u32x4*>(&s_k[key * D + phys * 8]) = kreg[j];
-      if (lc == 0) s_ok[key] = okreg[j];
-    }
-    // V^T in fp16: row d holds the tile's 64 keys; 16-byte key groups are
-    // XOR-swizzled by (d & 7)
-    const int key0 = kg * kKpt;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int d = lc * 8 + i;
-      float vals[kKpt];
-#pragma unroll
-      for (int j = 0; j < kKpt; ++j)
-        vals[j] = (i & 1) ? bf16_hi(vreg[j][i >> 1]) : bf16_lo(vreg[j][i >> 1]);
-      const int kc = key0 >> 3, within = key0 & 7;
-      uint16_t* dst = &s_vt[d * kTileKeys + ((kc ^ (d & 7)) << 3) + within];
-      if constexpr (kKpt == 4) {
-        u32x2 pk{pack_f16(vals[0], vals[1]), pack_f16(vals[2], vals[3])};
-        *reinterpret_cast<u32x2*>(dst) = pk;
-      } else {
-        *reinterpret_cast<uint32_t*>(dst) = pack_f16(vals[0], vals[1]);
-      }
-    }
-  };
-
-  issue(0);
-  const int krow_perm = swap_bits23(n);
+  for (int t = 0; t < kStages - 1; ++t)
+    if (t < ntiles) issue(t);
   for (int t = 0; t < ntiles; ++t) {
-    stage();
-    __syncthreads();
-    if (t + 1 < ntiles) issue(t + 1);
+    wait_tiles<2 * G::kInstr, kStages - 1>(min(kStages - 2, ntiles - 1 - t));
+    wg_barrier();
+    if (t + kStages - 1 < ntiles) issue(t + kStages - 1);
     if (computes) {
-      const uint64_t okm = __ballot(s_ok[lane] != 0);
-      f32x16 sacc[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
-        const int krow = 32 * kb + krow_perm;
-#pragma unroll
-        for (int ks = 0; ks < kNks; ++ks) {
-          const int phys = (2 * ks + hh) ^ (krow % kCpr);
-          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&s_k[krow * D + phys * 8]);
-          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc[kb], 0, 0, 0);
-        }
-      }
-      // register i of key block kb holds key 32kb + 16(i/8) + 8hh + (i%8)
-      float mt = -__builtin_inff();
-      if (okm == ~0ull) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            sacc[kb][i] *= p.scale_log2;
-            mt = fmaxf(mt, sacc[kb][i]);
-          }
-      } else {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = 32 * kb + 16 * (i >> 3) + 8 * hh + (i & 7);
-            const float x = ((okm >> key) & 1) ? sacc[kb][i] * p.scale_log2 : -__builtin_inff();
-            sacc[kb][i] = x;
-            mt = fmaxf(mt, x);
-          }
-      }
-      mt = wave_max_pair(mt);
-      const float m_new = fmaxf(m_run, mt);
-      const float m_use = m_new == -__builtin_inff() ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - m_use);
-      float rs = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float pv = fast_exp2(sacc[kb][i] - m_use);
-          sacc[kb][i] = pv;
-          rs += pv;
-        }
-      rs = wave_sum_pair(rs);
-      l_run = l_run * alpha + rs;
-      m_run = m_new;
+      const uint32_t st = ring_base + (t % kStages) * kStageBytes;
+      const uint64_t okm = __ballot(valid_entry(e0 + t * kTileKeys + lane));
+      attend_half<D>(st + k_half, st + v_half, kofs, qf, static_cast<uint32_t>(okm >> (32 * kh)),
+                     p.scale_log2, m_run, l_run, oacc, lane);
+    }
+    wait_lgkmcnt0();
+  }
+  __syncthreads();  // the ring is reused below
+
+  // ---- merge the two key halves of each row block through LDS ---------------
+  {
+    float* xch = reinterpret_cast<float*>(s_ring) + rb * kWave * (2 + 16 * kNdb);
+    if (computes && kh == 1) {
+      xch[lane] = m_run;
+      xch[kWave + lane] = l_run;
 #pragma unroll
       for (int db = 0; db < kNdb; ++db)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
-      f16x8 pf[2][2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          u32x4 pk{pack_f16(sacc[kb][8 * s2 + 0], sacc[kb][8 * s2 + 1]),
-                   pack_f16(sacc[kb][8 * s2 + 2], sacc[kb][8 * s2 + 3]),
-                   pack_f16(sacc[kb][8 * s2 + 4], sacc[kb][8 * s2 + 5]),
-                   pack_f16(sacc[kb][8 * s2 + 6], sacc[kb][8 * s2 + 7])};
-          pf[kb][s2] = __builtin_bit_cast(f16x8, pk);
-        }
-#pragma unroll
-      for (int db = 0; db < kNdb; ++db) {
-        const int d = 32 * db + n;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int s2 = 0; s2 < 2; ++s2) {
-            const int kc = 4 * kb + 2 * s2 + hh;
-            const f16x8 vf =
-                *reinterpret_cast<const f16x8*>(&s_vt[d * kTileKeys + ((kc ^ (d & 7)) << 3)]);
-            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[kb][s2], oacc[db], 0, 0, 0);
-          }
-      }
+        for (int i = 0; i < 16; ++i) xch[(2 + 16 * db + i) * kWave + lane] = oacc[db][i];
     }
     __syncthreads();
+    if (computes && kh == 0) {
+      const float m1 = xch[lane], l1 = xch[kWave + lane];
+      const float M = fmaxf(m_run, m1);
+      const float Mu = M == -__builtin_inff() ? 0.f : M;
+      const float a0 = fast_exp2(m_run - Mu), a1 = fast_exp2(m1 - Mu);
+      l_run = l_run * a0 + l1 * a1;
+      m_run = M;
+#pragma unroll
+      for (int db = 0; db < kNdb; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          oacc[db][i] = oacc[db][i] * a0 + xch[(2 + 16 * db + i) * kWave + lane] * a1;
+    }
   }
 
   if (kSparse && p.nchunk == 1) {
-    if (computes) store_rows<D>(p, s, h, w, lane, m_run, l_run, oacc);
+    if (computes && kh == 0) store_rows<D>(p, s, h, rb, lane, m_run, l_run, oacc);
     return;
   }
 
   // partial result of this chunk
   const int64_t slot = static_cast<int64_t>(u) * p.nchunk + c;
-  if (computes) {
+  if (computes && kh == 0) {
 #pragma unroll
     for (int db = 0; db < kNdb; ++db)
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
         f32x4 v{oacc[db][4 * i4], oacc[db][4 * i4 + 1], oacc[db][4 * i4 + 2], oacc[db][4 * i4 + 3]};
-        *reinterpret_cast<f32x4*>(p.part_o + 4 * part_o_index<D>(slot, w, db, i4, lane)) = v;
+        *reinterpret_cast<f32x4*>(p.part_o + 4 * part_o_index<D>(slot, rb, db, i4, lane)) = v;
       }
     if (hh == 0) {
-      p.part_ml[(slot * kMaxRows + 32 * w + n) * 2 + 0] = m_run;
-      p.part_ml[(slot * kMaxRows + 32 * w + n) * 2 + 1] = l_run;
+      p.part_ml[(slot * kMaxRows + 32 * rb + n) * 2 + 0] = m_run;
+      p.part_ml[(slot * kMaxRows + 32 * rb + n) * 2 + 1] = l_run;
     }
   }
   if (!kSparse) return;
 
-  // sparse pass: the last chunk of a unit to finish merges all of them
+  // sparse pass: the last chunk of a unit to finish merges all of them; the
+  // two waves of a row block split the d blocks
   __threadfence();
   __syncthreads();
   if (tid == 0) {
@@ -328,34 +399,58 @@ __global__ __launch_bounds__(kThreads) void attn_chunk_kernel(AttnParams p) {
   __threadfence();
   if (tid == 0) p.counters[2 * u] = 0u;
   if (!computes) return;
-  const int r = 32 * w + n;
+  const int r = 32 * rb + n;
   const int64_t slot0 = static_cast<int64_t>(u) * p.nchunk;
+  float mc[kMaxMerge], lc[kMaxMerge];
+#pragma unroll
+  for (int cc = 0; cc < kMaxMerge; ++cc) {  // clamped loads, masked after
+    const int64_t sl = slot0 + min(cc, p.nchunk - 1);
+    mc[cc] = p.part_ml[(sl * kMaxRows + r) * 2];
+    lc[cc] = p.part_ml[(sl * kMaxRows + r) * 2 + 1];
+  }
+#pragma unroll
+  for (int cc = 0; cc < kMaxMerge; ++cc)
+    if (cc >= p.nchunk) mc[cc] = -__builtin_inff();
   float M = -__builtin_inff();
-  for (int cc = 0; cc < p.nchunk; ++cc) M = fmaxf(M, p.part_ml[((slot0 + cc) * kMaxRows + r) * 2]);
+#pragma unroll
+  for (int cc = 0; cc < kMaxMerge; ++cc) M = fmaxf(M, mc[cc]);
   const float Mu = M == -__builtin_inff() ? 0.f : M;
   float L = 0.f;
 #pragma unroll
-  for (int db = 0; db < kNdb; ++db)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
-  for (int cc = 0; cc < p.nchunk; ++cc) {
-    const float mc = p.part_ml[((slot0 + cc) * kMaxRows + r) * 2];
-    const float lc2 = p.part_ml[((slot0 + cc) * kMaxRows + r) * 2 + 1];
-    const float wc = fast_exp2(mc - Mu);
-    L += lc2 * wc;
-#pragma unroll
-    for (int db = 0; db < kNdb; ++db)
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const f32x4 v =
-            *reinterpret_cast<const f32x4*>(p.part_o + 4 * part_o_index<D>(slot0 + cc, w, db, i4, lane));
-        oacc[db][4 * i4 + 0] += wc * v[0];
-        oacc[db][4 * i4 + 1] += wc * v[1];
-        oacc[db][4 * i4 + 2] += wc * v[2];
-        oacc[db][4 * i4 + 3] += wc * v[3];
-      }
+  for (int cc = 0; cc < kMaxMerge; ++cc) {
+    mc[cc] = fast_exp2(mc[cc] - Mu);  // now the weight of chunk cc
+    L += lc[cc] * mc[cc];
   }
-  store_rows<D>(p, s, h, w, lane, M, L, oacc);
+  const bool row_ok = r < p.R;
+  const int b = row_ok ? r / p.G : 0, g = r - b * p.G;
+  const int64_t orow = (static_cast<int64_t>(s) * p.B + b) * p.Hq + h * p.G + g;
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  // one d block at a time: all chunks' partials of the block are in flight together
+#pragma unroll
+  for (int dbh = 0; dbh < kNdb / 2; ++dbh) {
+    const int db = kh * (kNdb / 2) + dbh;
+    f32x4 part[kMaxMerge][4];
+#pragma unroll
+    for (int cc = 0; cc < kMaxMerge; ++cc)  // clamped: chunks past the end have weight 0
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4)
+        part[cc][i4] = *reinterpret_cast<const f32x4*>(
+            p.part_o + 4 * part_o_index<D>(slot0 + min(cc, p.nchunk - 1), rb, db, i4, lane));
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      f32x4 acc{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int cc = 0; cc < kMaxMerge; ++cc)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] += mc[cc] * part[cc][i4][e];
+      if (row_ok) {
+        f32x4 v{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
+        *reinterpret_cast<f32x4*>(p.o + orow * D + 32 * db + 8 * i4 + 4 * hh) = v;
+      }
+    }
+  }
+  if (row_ok && kh == 0 && hh == 0 && p.lse != nullptr)
+    p.lse[orow] = L > 0.f ? (M + __log2f(L)) * kLn2 : -__builtin_inff();
 }
 
 // Merge of the exact pass's split partials. One work-group per
@@ -364,6 +459,7 @@ __global__ __launch_bounds__(kThreads) void attn_chunk_kernel(AttnParams p) {
 template <int D>
 __global__ __launch_bounds__(kThreads) void exact_merge_kernel(MergeParams p) {
   constexpr int kNdb = D / 32;
+  constexpr int kBatch = 16;
   const int tid = threadIdx.x, lane = tid & 63, i4 = tid >> 6;
   const int n = lane & 31, hh = lane >> 5;
   int bid = blockIdx.x;
@@ -376,22 +472,44 @@ __global__ __launch_bounds__(kThreads) void exact_merge_kernel(MergeParams p) {
   const int nch = (ns + p.chunk - 1) / p.chunk;
   const int r = 32 * w + n;
   const int64_t slot0 = static_cast<int64_t>(u) * p.nchunk;
-  float M = -__builtin_inff();
-  for (int c = 0; c < nch; ++c) M = fmaxf(M, p.part_ml[((slot0 + c) * kMaxRows + r) * 2]);
-  const float Mu = M == -__builtin_inff() ? 0.f : M;
-  float L = 0.f;
+  // one pass: a running max; each batch's loads are all in flight together
+  float M = -__builtin_inff(), L = 0.f;
   f32x4 acc{0.f, 0.f, 0.f, 0.f};
-  for (int c = 0; c < nch; ++c) {
-    const float mc = p.part_ml[((slot0 + c) * kMaxRows + r) * 2];
-    const float lc = p.part_ml[((slot0 + c) * kMaxRows + r) * 2 + 1];
-    const float wc = fast_exp2(mc - Mu);
-    L += lc * wc;
-    const f32x4 v = *reinterpret_cast<const f32x4*>(
-        p.part_o + 4 * part_o_index<D>(slot0 + c, w, db, i4, lane));
-    acc[0] += wc * v[0];
-    acc[1] += wc * v[1];
-    acc[2] += wc * v[2];
-    acc[3] += wc * v[3];
+  for (int c0 = 0; c0 < nch; c0 += kBatch) {
+    float mb[kBatch], lb[kBatch];
+    f32x4 vb[kBatch];
+    // loads from clamped (always valid) slots, all issued before any use;
+    // slots past the end get weight 0 afterwards
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int64_t slot = slot0 + min(c0 + j, nch - 1);
+      mb[j] = p.part_ml[(slot * kMaxRows + r) * 2];
+      lb[j] = p.part_ml[(slot * kMaxRows + r) * 2 + 1];
+      vb[j] = *reinterpret_cast<const f32x4*>(p.part_o + 4 * part_o_index<D>(slot, w, db, i4, lane));
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j)
+      if (c0 + j >= nch) mb[j] = -__builtin_inff();
+    float Mb = M;
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) Mb = fmaxf(Mb, mb[j]);
+    if (Mb == -__builtin_inff()) continue;
+    const float f = fast_exp2(M - Mb);  // M = -inf gives 0
+    L *= f;
+    acc[0] *= f;
+    acc[1] *= f;
+    acc[2] *= f;
+    acc[3] *= f;
+    M = Mb;
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const float wc = fast_exp2(mb[j] - M);
+      L += lb[j] * wc;
+      acc[0] += wc * vb[j][0];
+      acc[1] += wc * vb[j][1];
+      acc[2] += wc * vb[j][2];
+      acc[3] += wc * vb[j][3];
+    }
   }
   if (r >= p.R) return;
   const int b = r / p.G, g = r - b * p.G, j = h * p.G + g;

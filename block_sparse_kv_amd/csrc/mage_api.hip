@@ -86,30 +86,43 @@ int exact_chunk_floor(int64_t units, int64_t max_n) {
                                             round_up(cdiv(units * max_n, kExactSlotBudget), 64)));
 }
 
-int exact_chunk(int64_t units, int64_t max_n, int64_t total_keys) {
+// Returns 0 when no chunk size satisfies both the workspace floor and the
+// per-work-group page table limit (paged layout with tiny pages).
+int exact_chunk(int64_t units, int64_t max_n, int64_t total_keys, int page_size) {
   int64_t c = round_up(cdiv(total_keys, env_int("MAGE_EXACT_WGS", kExactTargetWgs)), 64);
-  c = std::max<int64_t>(c, exact_chunk_floor(units, max_n));
+  const int64_t floor = exact_chunk_floor(units, max_n);
+  c = std::max<int64_t>(c, floor);
   const int forced = env_int("MAGE_EXACT_CHUNK", 0);
-  if (forced > 0) c = std::max<int64_t>(round_up(forced, 64), exact_chunk_floor(units, max_n));
+  if (forced > 0) c = std::max<int64_t>(round_up(forced, 64), floor);
+  if (page_size > 0) {
+    const int64_t cap = ((kMaxChunkPages - 1) * static_cast<int64_t>(page_size)) / 64 * 64;
+    c = std::min(c, cap);
+    if (c < floor || c < 64) return 0;
+  }
   return static_cast<int>(c);
 }
 
 // Sparse step: at most kSparseMaxChunks chunks per (seq, KV head), aiming at
 // one work-group per CU.
-constexpr int kSparseMaxChunks = 8;
+constexpr int kSparseMaxChunks = kMaxMerge;
 constexpr int kCus = 256;
 
+// k <= kSparseMaxChunks * kMaxSparseChunk (checked by the entry points).
 int sparse_chunk(int64_t units, int k) {
+  const int min_chunk = static_cast<int>(round_up(cdiv(k, kSparseMaxChunks), 64));
   const int forced = env_int("MAGE_SPARSE_CHUNK", 0);
-  if (forced > 0) {
-    const int c = static_cast<int>(round_up(forced, 64));
-    return std::max<int>(c, static_cast<int>(round_up(cdiv(k, kSparseMaxChunks), 64)));
-  }
+  if (forced > 0) return std::min(kMaxSparseChunk, std::max<int>(static_cast<int>(round_up(forced, 64)), min_chunk));
   const int64_t want = std::min<int64_t>(kSparseMaxChunks, std::max<int64_t>(1, cdiv(kCus, units)));
-  return static_cast<int>(round_up(cdiv(k, want), 64));
+  return std::min(kMaxSparseChunk, std::max(min_chunk, static_cast<int>(round_up(cdiv(k, want), 64))));
 }
 
 constexpr int kScoreChunk = 2048;
+// LDS ring depth: 3 x 32 KiB of K+V tiles at d = 128, 4 x 16 KiB at d = 64;
+// the score sweep streams K only: 4 x 16 KiB / 4 x 8 KiB (two work-groups per CU).
+template <int D>
+constexpr int kStagesFor = D == 128 ? 3 : 4;
+template <int D>
+constexpr int kScoreStagesFor = 4;
 constexpr int64_t kCounterBytes = 65536;
 
 // ---- workspace layout ------------------------------------------------------
@@ -213,12 +226,15 @@ mage_status paged_kv(const Dims& d, const mage_paged_kv* kv, KvArgs& a) {
   return MAGE_OK;
 }
 
+// k == 0: exact attention only (no score sweep, no top-k).
 template <int D>
 mage_status launch_select(const Dims& d, const uint16_t* q, const KvArgs& kv, int32_t k, float* o,
                           float* lse, int32_t* idx, float* scores, int64_t score_stride, void* ws,
                           const Layout& L, hipStream_t attn, hipStream_t sel, hipEvent_t idx_ready) {
   const int64_t U = d.units;
-  const int chunk = exact_chunk(U, kv.max_n, kv.total_keys);
+  const int chunk = exact_chunk(U, kv.max_n, kv.total_keys,
+                                kv.src.page_table ? (1 << kv.src.page_shift) : 0);
+  if (chunk == 0) return fail(MAGE_ERR_UNSUPPORTED, "page_size too small for this prefix length");
   const int nch = static_cast<int>(cdiv(kv.max_n, chunk));
   const float scale_log2 = d.scale * kLog2e;
 
@@ -238,8 +254,8 @@ mage_status launch_select(const Dims& d, const uint16_t* q, const KvArgs& kv, in
   ap.xcd_group = 0;
   ap.scale_log2 = scale_log2;
   ap.lens = kv.lens;
-  hipLaunchKernelGGL((attn_chunk_kernel<D, false>), dim3(static_cast<unsigned>(U * nch)),
-                     dim3(kThreads), 0, attn, ap);
+  hipLaunchKernelGGL((attn_chunk_kernel<D, false, kStagesFor<D>>), dim3(static_cast<unsigned>(U * nch)),
+                     dim3(kAttnThreads), 0, attn, ap);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return hip_fail(e, "exact pass launch");
 
   MergeParams mp{};
@@ -256,6 +272,7 @@ mage_status launch_select(const Dims& d, const uint16_t* q, const KvArgs& kv, in
   hipLaunchKernelGGL((exact_merge_kernel<D>), dim3(static_cast<unsigned>(U * d.nrb * (D / 32))),
                      dim3(kThreads), 0, attn, mp);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return hip_fail(e, "merge launch");
+  if (k == 0) return MAGE_OK;
 
   if (sel && sel != attn) {
     hipEvent_t ev = internal_event();
@@ -274,12 +291,12 @@ mage_status launch_select(const Dims& d, const uint16_t* q, const KvArgs& kv, in
   sp.scores = scores ? scores : at<float>(ws, L.scores);
   sp.stride = scores ? score_stride : kv.max_n;
   sp.S = d.S; sp.B = d.B; sp.Hq = d.Hq; sp.Hkv = d.Hkv; sp.G = d.G; sp.R = d.R;
-  sp.chunk = env_int("MAGE_SCORE_CHUNK", kScoreChunk);
+  sp.chunk = std::min(kScoreMaxChunk, env_int("MAGE_SCORE_CHUNK", kScoreChunk));
   sp.nchunk = static_cast<int>(cdiv(kv.max_n, sp.chunk));
   sp.reverse = env_int("MAGE_SCORE_REVERSE", 1);
   sp.scale_log2 = scale_log2;
   sp.lens = kv.lens;
-  hipLaunchKernelGGL((score_kernel<D>), dim3(static_cast<unsigned>(U * sp.nchunk)), dim3(kThreads), 0,
+  hipLaunchKernelGGL((score_kernel<D, kScoreStagesFor<D>>), dim3(static_cast<unsigned>(U * sp.nchunk)), dim3(kThreads), 0,
                      sel, sp);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return hip_fail(e, "score launch");
 
@@ -331,7 +348,7 @@ mage_status launch_sparse(const Dims& d, const uint16_t* q, const KvArgs& kv, co
   ap.scale_log2 = d.scale * kLog2e;
   ap.lens = kv.lens;
   const int64_t grid = ap.xcd_group ? round_up(U, 8) * nch : U * nch;
-  hipLaunchKernelGGL((attn_chunk_kernel<D, true>), dim3(static_cast<unsigned>(grid)), dim3(kThreads),
+  hipLaunchKernelGGL((attn_chunk_kernel<D, true, kStagesFor<D>>), dim3(static_cast<unsigned>(grid)), dim3(kAttnThreads),
                      0, stream, ap);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return hip_fail(e, "sparse launch");
   return MAGE_OK;
@@ -417,6 +434,40 @@ mage_status mage_select_exact_paged(const mage_dims* dims, const uint16_t* q, co
                                         attn_stream, select_stream, idx_ready);
 }
 
+mage_status mage_exact_attn(const mage_dims* dims, const uint16_t* q, const uint16_t* k_cache,
+                            const uint16_t* v_cache, int32_t seq_len, float* o, float* lse,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  Dims d;
+  if (mage_status st = check_dims(dims, d); st != MAGE_OK) return st;
+  int32_t dummy_idx = 0;
+  if (mage_status st = common_select_checks(q, 1, o, lse, &dummy_idx, nullptr); st != MAGE_OK) return st;
+  KvArgs kv;
+  if (mage_status st = contiguous_kv(d, k_cache, v_cache, seq_len, kv); st != MAGE_OK) return st;
+  const Layout L = make_layout(d, kv.max_n, 1);
+  if (mage_status st = check_ws(workspace, workspace_bytes, L); st != MAGE_OK) return st;
+  return d.D == 128 ? launch_select<128>(d, q, kv, 0, o, lse, nullptr, nullptr, 0, workspace, L,
+                                         stream, nullptr, nullptr)
+                    : launch_select<64>(d, q, kv, 0, o, lse, nullptr, nullptr, 0, workspace, L,
+                                        stream, nullptr, nullptr);
+}
+
+mage_status mage_exact_attn_paged(const mage_dims* dims, const uint16_t* q, const mage_paged_kv* kvp,
+                                  float* o, float* lse, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream) {
+  Dims d;
+  if (mage_status st = check_dims(dims, d); st != MAGE_OK) return st;
+  int32_t dummy_idx = 0;
+  if (mage_status st = common_select_checks(q, 1, o, lse, &dummy_idx, nullptr); st != MAGE_OK) return st;
+  KvArgs kv;
+  if (mage_status st = paged_kv(d, kvp, kv); st != MAGE_OK) return st;
+  const Layout L = make_layout(d, kv.max_n, 1);
+  if (mage_status st = check_ws(workspace, workspace_bytes, L); st != MAGE_OK) return st;
+  return d.D == 128 ? launch_select<128>(d, q, kv, 0, o, lse, nullptr, nullptr, 0, workspace, L,
+                                         stream, nullptr, nullptr)
+                    : launch_select<64>(d, q, kv, 0, o, lse, nullptr, nullptr, 0, workspace, L,
+                                        stream, nullptr, nullptr);
+}
+
 static mage_status sparse_common(const mage_dims* dims, const uint16_t* q, const int32_t* idx,
                                  int32_t k, float* o, float* lse, Dims& d) {
   if (mage_status st = check_dims(dims, d); st != MAGE_OK) return st;
@@ -425,6 +476,8 @@ static mage_status sparse_common(const mage_dims* dims, const uint16_t* q, const
   if (!aligned(idx, 4) || (lse && !aligned(lse, 4)))
     return fail(MAGE_ERR_INVALID_ARG, "idx and lse must be 4-byte aligned");
   if (k < 1) return fail(MAGE_ERR_INVALID_ARG, "k must be >= 1");
+  if (k > kSparseMaxChunks * kMaxSparseChunk)
+    return fail(MAGE_ERR_UNSUPPORTED, "sparse steps take k <= 32768 index entries");
   return MAGE_OK;
 }
 

@@ -21,7 +21,9 @@
 // position order, so its output is already ascending.
 #pragma once
 
+#include "attn_kernels.hpp"
 #include "mage_common.hpp"
+#include "tile_io.hpp"
 
 namespace mage {
 
@@ -38,15 +40,20 @@ struct ScoreParams {
   SeqLens lens;
 };
 
-template <int D>
-__global__ __launch_bounds__(kThreads) void score_kernel(ScoreParams p) {
-  constexpr int kCpr = D / 8;
-  constexpr int kKpt = kTileKeys * kCpr / kThreads;
-  constexpr int kNks = D / 16;
-  __shared__ __attribute__((aligned(16))) uint16_t s_k[kTileKeys * D];
-  __shared__ float s_col[4][kTileKeys];
+// Positions per score work-group (the host's chunk never exceeds it); sized
+// so that two work-groups fit in one CU's LDS.
+constexpr int kScoreMaxChunk = 2048;
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+template <int D, int kStages>
+__global__ __launch_bounds__(kThreads) void score_kernel(ScoreParams p) {
+  using G = TileGeom<D>;
+  constexpr int kNks = D / 16;
+  __shared__ __attribute__((aligned(1024))) uint8_t s_ring[kStages * G::kBytes];
+  __shared__ int32_t s_pages[kScoreMaxChunk + 1];
+  __shared__ float s_col[2][4][kTileKeys];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hh = lane >> 5, n = lane & 31;
   const int u = blockIdx.x / p.nchunk, c = blockIdx.x % p.nchunk;
   const int s = u / p.Hkv, h = u - s * p.Hkv;
@@ -55,6 +62,15 @@ __global__ __launch_bounds__(kThreads) void score_kernel(ScoreParams p) {
   if (e0 >= e1) return;
   const int nrb = (p.R + 31) >> 5;
   const bool computes = w < nrb;
+  const bool paged = p.kv.page_table != nullptr;
+  const int pshift = p.kv.page_shift, pmask = (1 << p.kv.page_shift) - 1;
+  const int64_t seq_base = paged ? 0 : (static_cast<int64_t>(s) * p.Hkv + h) * p.kv.n_uniform;
+  const int page0 = e0 >> pshift;
+  if (paged) {
+    const int32_t* ptab = p.kv.page_table + static_cast<int64_t>(s) * p.kv.max_pages;
+    const int np = ((e1 - 1) >> pshift) - page0 + 1;
+    for (int i = tid; i < np; i += kThreads) s_pages[i] = ptab[page0 + i];
+  }
 
   // A operand: Q row 32w + n, d slice 16ks + 8hh
   bf16x8 qf[kNks];
@@ -71,72 +87,91 @@ __global__ __launch_bounds__(kThreads) void score_kernel(ScoreParams p) {
       for (int ks = 0; ks < kNks; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
     }
   }
-  // accumulator register i of this lane is row 32w + 8(i/4) + 4hh + (i%4)
+  // accumulator register i of this lane is row 32w + 8(i/4) + 4hh + (i%4);
+  // crow = -(max + log2 sum) of that row
   float crow[16];
+  {
+    // every row slot of the unit exists in rowstat: load all 16 unconditionally
+    // (one round trip), then drop the rows past R
+    const float* rs = p.rowstat + static_cast<int64_t>(u) * kMaxRows;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int r = 32 * w + 8 * (i >> 2) + 4 * hh + (i & 3);
-    crow[i] = (computes && r < p.R) ? p.rowstat[static_cast<int64_t>(u) * kMaxRows + r]
-                                    : __builtin_inff();
+    for (int i = 0; i < 16; ++i) crow[i] = rs[32 * w + 8 * (i >> 2) + 4 * hh + (i & 3)];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = 32 * w + 8 * (i >> 2) + 4 * hh + (i & 3);
+      crow[i] = (computes && r < p.R) ? -crow[i] : -__builtin_inff();
+    }
   }
+  uint32_t kofs[kNks];
+  k_frag_offsets<D>(n, hh, kofs);
+  const uint32_t ring_base = lds_addr(s_ring);
   const float inv_r = 1.f / static_cast<float>(p.R);
+  __syncthreads();
 
-  const int lc = tid % kCpr, kg = tid / kCpr;
-  u32x4 kreg[kKpt];
+  auto row_off = [&](int e) -> int64_t {
+    const int pos = min(e, e1 - 1);
+    if (paged) {
+      const int64_t page = s_pages[(pos >> pshift) - page0];
+      return (((page * p.Hkv + h) << pshift) + (pos & pmask)) * D;
+    }
+    return (seq_base + pos) * D;
+  };
   const int ntiles = (e1 - e0 + kTileKeys - 1) / kTileKeys;
+  // sweep order: last tile first when p.reverse (re-reads what the exact pass read last)
   auto tile_of = [&](int t) { return p.reverse ? ntiles - 1 - t : t; };
-  auto issue = [&](int tile) {
-#pragma unroll
-    for (int j = 0; j < kKpt; ++j) {
-      const int e = e0 + tile * kTileKeys + kg * kKpt + j;
-      if (e < e1)
-        kreg[j] = load16(p.kv.k + kv_row(p.kv, s, h, p.Hkv, e, D) + lc * 8);
-      else
-        kreg[j] = u32x4{0, 0, 0, 0};
+  auto issue = [&](int t) {
+    const int base = e0 + tile_of(t) * kTileKeys;
+    issue_tile<D, false>(s_ring + (t % kStages) * G::kBytes, nullptr, p.kv.k, nullptr,
+                         [&](int r) { return row_off(base + r); }, w, lane);
+  };
+  // column sums of tile t live in s_col[t & 1]; wave 0 reduces them over the
+  // row blocks one iteration later (one barrier per tile)
+  auto reduce_store = [&](int t) {
+    const int e = e0 + tile_of(t) * kTileKeys + tid;
+    if (e < e1) {
+      float sum = 0.f;
+      for (int ww = 0; ww < nrb; ++ww) sum += s_col[t & 1][ww][tid];
+      p.scores[static_cast<int64_t>(u) * p.stride + e] = sum * inv_r;
     }
   };
-
-  issue(tile_of(0));
-  for (int t = 0; t < ntiles; ++t) {
-    const int tile = tile_of(t);
 #pragma unroll
-    for (int j = 0; j < kKpt; ++j) {
-      const int key = kg * kKpt + j;
-      *reinterpret_cast<u32x4*>(&s_k[key * D + ((lc ^ (key % kCpr)) * 8)]) = kreg[j];
-    }
-    __syncthreads();
-    if (t + 1 < ntiles) issue(tile_of(t + 1));
+  for (int t = 0; t < kStages - 1; ++t)
+    if (t < ntiles) issue(t);
+  for (int t = 0; t < ntiles; ++t) {
+    wait_tiles<G::kInstr, kStages - 1>(min(kStages - 2, ntiles - 1 - t));
+    wg_barrier();
+    if (t + kStages - 1 < ntiles) issue(t + kStages - 1);
+    if (t > 0 && tid < kTileKeys) reduce_store(t - 1);
+    const uint32_t k_base = ring_base + (t % kStages) * G::kBytes;
     if (computes) {
+      f32x16 acc[2];
+      bf16x8 kf[kNks];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[0][i] = 0.f;
+      k_frags<D, 0>(k_base, kofs, kf);
+#pragma unroll
+      for (int ks = 0; ks < kNks; ++ks)
+        acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[ks], kf[ks], acc[0], 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[1][i] = 0.f;
+      k_frags<D, 32 * G::kRowBytes>(k_base, kofs, kf);
+#pragma unroll
+      for (int ks = 0; ks < kNks; ++ks)
+        acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[ks], kf[ks], acc[1], 0, 0, 0);
+      // S[row][key 32kb + n]; sum the probabilities of this wave's 32 rows
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        f32x16 acc;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-        const int krow = 32 * kb + n;
-#pragma unroll
-        for (int ks = 0; ks < kNks; ++ks) {
-          const int phys = (2 * ks + hh) ^ (krow % kCpr);
-          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&s_k[krow * D + phys * 8]);
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[ks], kf, acc, 0, 0, 0);
-        }
-        // S[row][key 32kb + n]; sum the probabilities of this wave's 32 rows
         float col = 0.f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) col += fast_exp2(acc[i] * p.scale_log2 - crow[i]);
+        for (int i = 0; i < 16; ++i) col += fast_exp2(__builtin_fmaf(acc[kb][i], p.scale_log2, crow[i]));
         col = wave_sum_pair(col);
-        if (hh == 0) s_col[w][krow] = col;
+        if (hh == 0) s_col[t & 1][w][32 * kb + n] = col;
       }
     }
-    __syncthreads();
-    if (tid < kTileKeys) {
-      const int e = e0 + tile * kTileKeys + tid;
-      if (e < e1) {
-        float sum = 0.f;
-        for (int ww = 0; ww < nrb; ++ww) sum += s_col[ww][tid];
-        p.scores[static_cast<int64_t>(u) * p.stride + e] = sum * inv_r;
-      }
-    }
+    wait_lgkmcnt0();
   }
+  __syncthreads();
+  if (tid < kTileKeys) reduce_store(ntiles - 1);
 }
 
 // ---------------------------------------------------------------------------
@@ -192,8 +227,8 @@ __device__ __forceinline__ int block_inclusive_scan(int v, int32_t* wsum, int& t
 
 // MSB-first radix select over n bit patterns: the kk-th largest value T, and
 // how many entries equal to T belong to the top kk (need >= 1).
-__device__ void radix_select(const uint32_t* data, int n, int kk, TopkShared& sh, uint32_t& T,
-                             int& need) {
+template <class Get>
+__device__ void radix_select(Get data, int n, int kk, TopkShared& sh, uint32_t& T, int& need) {
   const int tid = threadIdx.x;
   uint32_t prefix = 0, pmask = 0;
   int rem = kk;
@@ -205,7 +240,7 @@ __device__ void radix_select(const uint32_t* data, int n, int kk, TopkShared& sh
     for (int i = tid; i < nb; i += kTopkThreads) sh.hist[i] = 0u;
     __syncthreads();
     for (int i = tid; i < n; i += kTopkThreads) {
-      const uint32_t x = data[i];
+      const uint32_t x = data(i);
       if ((x & pmask) == prefix) atomicAdd(&sh.hist[(x >> shift) & (nb - 1)], 1u);
     }
     __syncthreads();
@@ -241,8 +276,8 @@ __device__ void radix_select(const uint32_t* data, int n, int kk, TopkShared& sh
 
 // Keep entries > T and the first `need` entries == T, in index order.
 // Writes out_pos[j] = pos_of(i) (and out_bits[j] = data[i] if out_bits).
-template <class PosOf>
-__device__ void ordered_compact(const uint32_t* data, int n, uint32_t T, int need, PosOf pos_of,
+template <class Get, class PosOf>
+__device__ void ordered_compact(Get data, int n, uint32_t T, int need, PosOf pos_of,
                                 uint32_t* out_bits, int32_t* out_pos, TopkShared& sh) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const uint64_t below = lanemask_lt();
@@ -250,7 +285,7 @@ __device__ void ordered_compact(const uint32_t* data, int n, uint32_t T, int nee
   for (int j0 = 0; j0 < n; j0 += kTopkThreads) {
     const int i = j0 + tid;
     const bool valid = i < n;
-    const uint32_t x = valid ? data[i] : 0u;
+    const uint32_t x = data(min(i, n - 1));
     const bool gt = valid && x > T;
     const bool eq = valid && x == T;
     const uint64_t meq = __ballot(eq);
@@ -311,14 +346,23 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkParams p) {
   uint32_t* cb = p.cand_bits + static_cast<int64_t>(u) * p.cand_stride + static_cast<int64_t>(c) * kc_stride;
   int32_t* cp = p.cand_pos + static_cast<int64_t>(u) * p.cand_stride + static_cast<int64_t>(c) * kc_stride;
 
-  for (int i = tid; i < len; i += kTopkThreads) s_data[i] = __float_as_uint(src[i]);
+  {
+    // every thread issues all of its loads before the first use
+    constexpr int kPer = kTopkChunk / kTopkThreads;
+    uint32_t v[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) v[j] = __float_as_uint(src[min(tid + j * kTopkThreads, len - 1)]);
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) s_data[tid + j * kTopkThreads] = v[j];
+  }
   __syncthreads();
   if (nch == 1) {
     // a single chunk: its winners are the answer
     uint32_t T;
     int need;
-    radix_select(s_data, len, kk, sh, T, need);
-    ordered_compact(s_data, len, T, need, [&](int i) { return start + i; }, nullptr, out, sh);
+    auto get = [&](int i) { return s_data[i]; };
+    radix_select(get, len, kk, sh, T, need);
+    ordered_compact(get, len, T, need, [&](int i) { return start + i; }, nullptr, out, sh);
     for (int i = kk + tid; i < p.k; i += kTopkThreads) out[i] = -1;
     return;
   }
@@ -330,8 +374,9 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkParams p) {
   } else {
     uint32_t T;
     int need;
-    radix_select(s_data, len, kc, sh, T, need);
-    ordered_compact(s_data, len, T, need, [&](int i) { return start + i; }, cb, cp, sh);
+    auto get = [&](int i) { return s_data[i]; };
+    radix_select(get, len, kc, sh, T, need);
+    ordered_compact(get, len, T, need, [&](int i) { return start + i; }, cb, cp, sh);
   }
 
   __threadfence();
@@ -350,8 +395,32 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkParams p) {
   const int total = (nch - 1) * kc_stride + min(kc_stride, n - (nch - 1) * kTopkChunk);
   uint32_t T;
   int need;
-  radix_select(all_bits, total, kk, sh, T, need);
-  ordered_compact(all_bits, total, T, need, [&](int i) { return all_pos[i]; }, nullptr, out, sh);
+  if (total <= kTopkChunk / 2) {
+    // winners (bits, positions) fit in LDS: one batched pass from L2, then LDS only
+    constexpr int kPer = kTopkChunk / 2 / kTopkThreads;
+    uint32_t vb[kPer];
+    int32_t vp[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int i = min(tid + j * kTopkThreads, total - 1);  // clamped; entries past total are never read
+      vb[j] = all_bits[i];
+      vp[j] = all_pos[i];
+    }
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      s_data[tid + j * kTopkThreads] = vb[j];
+      s_data[kTopkChunk / 2 + tid + j * kTopkThreads] = static_cast<uint32_t>(vp[j]);
+    }
+    __syncthreads();
+    auto get = [&](int i) { return s_data[i]; };
+    radix_select(get, total, kk, sh, T, need);
+    ordered_compact(get, total, T, need, [&](int i) { return s_data[kTopkChunk / 2 + i]; }, nullptr,
+                    out, sh);
+  } else {
+    auto get = [&](int i) { return all_bits[i]; };
+    radix_select(get, total, kk, sh, T, need);
+    ordered_compact(get, total, T, need, [&](int i) { return all_pos[i]; }, nullptr, out, sh);
+  }
   for (int i = kk + tid; i < p.k; i += kTopkThreads) out[i] = -1;
 }
 

@@ -132,6 +132,20 @@ mage_status mage_select_exact_paged(const mage_dims* dims, const uint16_t* q,
                                     hipEvent_t idx_ready);
 
 /*
+ * Exact attention only (the step-1 pass without selection; also the
+ * exact-attention-at-every-step baseline the MAGE page compares against under
+ * "Key results"). Runs the split exact pass and merge on `stream`.
+ * lse may be null.
+ */
+mage_status mage_exact_attn(const mage_dims* dims, const uint16_t* q, const uint16_t* k_cache,
+                            const uint16_t* v_cache, int32_t seq_len, float* o, float* lse,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+mage_status mage_exact_attn_paged(const mage_dims* dims, const uint16_t* q,
+                                  const mage_paged_kv* kv, float* o, float* lse, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream);
+
+/*
  * A later denoising step (MAGE page, "Approach": later steps reuse the step-1
  * subset): for every (sequence, KV head), gather the K/V rows named by
  * idx[s][h][0..k) and compute attention of the block's queries over them.

@@ -59,10 +59,17 @@ def _load():
         lib.oracle_topk.argtypes = [_dp, ctypes.c_int, ctypes.c_int, ctypes.c_int, _i32p]
         lib.oracle_depage.argtypes = [_u16p, ctypes.c_int, ctypes.c_int, ctypes.c_int, _i32p,
                                       ctypes.c_int, _u16p]
+        lib.oracle_num_threads.argtypes = []
+        lib.oracle_num_threads.restype = ctypes.c_int
         for f in (lib.oracle_exact_seq, lib.oracle_sparse_seq, lib.oracle_topk, lib.oracle_depage):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
+
+
+def num_threads() -> int:
+    """Threads the oracle's OpenMP regions use."""
+    return int(_load().oracle_num_threads())
 
 
 def _u16(t) -> np.ndarray:

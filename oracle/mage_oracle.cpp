@@ -39,6 +39,8 @@
 #include <numeric>
 #include <vector>
 
+#include <omp.h>
+
 namespace {
 
 inline double widen_bf16(uint16_t b) {
@@ -95,6 +97,9 @@ void widen_rows(const uint16_t* src, int n, int d, std::vector<double>& dst) {
 }  // namespace
 
 extern "C" {
+
+// Threads an OpenMP region of the oracle uses.
+int oracle_num_threads(void) { return omp_get_max_threads(); }
 
 // One sequence. Q bf16 [B][Hq][d]; K, V bf16 [Hkv][N][d].
 // Outputs: O fp64 [B][Hq][d], lse fp64 [B][Hq], score fp64 [Hkv][N] (nullable).

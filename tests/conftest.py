@@ -19,3 +19,13 @@ def _oracle_built():
     if not os.path.exists(oracle._LIB_PATH):
         oracle.build(force=False)
     yield
+
+
+@pytest.fixture(scope="session", autouse=True)
+def _hip_runtime_first():
+    """Bring up the HIP runtime before any test draws inputs on worker threads."""
+    import torch
+    if torch.cuda.is_available():
+        torch.zeros(1, device="cuda")
+        torch.cuda.synchronize()
+    yield

@@ -131,6 +131,20 @@ def _bf16(a: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch.bfloat16)
 
 
+def _bf16_bits(a: np.ndarray) -> np.ndarray:
+    """fp32 -> bf16 bit patterns, round to nearest even (finite inputs), numpy only.
+
+    Used inside the generator's worker threads, which must not call torch (its
+    CPU kernels start an OpenMP team per calling thread)."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    return ((u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)).astype(np.uint16)
+
+
+def _u16_view(t: torch.Tensor) -> np.ndarray:
+    """numpy uint16 view sharing the storage of a bf16 CPU tensor."""
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
 def _q1_f32(w: Workload) -> np.ndarray:
     q = _rng(w.seed, _Q1).standard_normal(
         (w.num_seqs, w.block, w.num_q_heads, w.head_dim), dtype=np.float32)
@@ -216,12 +230,13 @@ def make_inputs(w: Workload | int | str, *, steps: int | None = None,
         n = w.seq_lens[0]
         k = torch.empty((S, Hkv, n, d), dtype=torch.bfloat16)
         v = torch.empty_like(k)
+        kn, vn = _u16_view(k), _u16_view(v)
 
         def fill(job):
             s, h = job
             kk, vv, pl = _kv_head(w, q1f, s, h)
-            k[s, h] = _bf16(kk)
-            v[s, h] = _bf16(vv)
+            kn[s, h] = _bf16_bits(kk)
+            vn[s, h] = _bf16_bits(vv)
             plants[job] = pl
         with ThreadPoolExecutor(_threads()) as ex:
             list(ex.map(fill, jobs))
@@ -238,17 +253,18 @@ def make_inputs(w: Workload | int | str, *, steps: int | None = None,
             off += np_
         k_pool = torch.zeros((P, Hkv, ps, d), dtype=torch.bfloat16)
         v_pool = torch.zeros_like(k_pool)
+        kpn, vpn = _u16_view(k_pool), _u16_view(v_pool)
 
         def fill(job):
             s, h = job
             kk, vv, pl = _kv_head(w, q1f, s, h)
             n = w.seq_lens[s]
             pad = npages[s] * ps - n
-            kb = _bf16(np.pad(kk, ((0, pad), (0, 0)))).view(npages[s], ps, d)
-            vb = _bf16(np.pad(vv, ((0, pad), (0, 0)))).view(npages[s], ps, d)
-            ids = torch.from_numpy(table[s, :npages[s]].astype(np.int64))
-            k_pool[ids, h] = kb
-            v_pool[ids, h] = vb
+            kb = _bf16_bits(np.pad(kk, ((0, pad), (0, 0)))).reshape(npages[s], ps, d)
+            vb = _bf16_bits(np.pad(vv, ((0, pad), (0, 0)))).reshape(npages[s], ps, d)
+            ids = table[s, :npages[s]].astype(np.int64)
+            kpn[ids, h] = kb
+            vpn[ids, h] = vb
             plants[job] = pl
         with ThreadPoolExecutor(_threads()) as ex:
             list(ex.map(fill, jobs))
