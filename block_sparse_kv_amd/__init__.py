@@ -112,7 +112,7 @@ def workspace_bytes(dims: Dims, max_seq_len: int, k: int) -> int:
 
 
 class Workspace:
-    """A zero-filled device workspace; grows (re-zeroed) when a call needs more.
+    """A device workspace; grows when a call needs more.
 
     Calls through one Workspace are ordered: a call made after a step-1 call
     whose selection ran on another stream first waits for that selection.
@@ -130,7 +130,7 @@ class Workspace:
             self.pending = None
         if self.buf is None or self.buf.numel() < nbytes:
             with torch.cuda.stream(st):
-                self.buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=self.device)
+                self.buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=self.device)
         return self.buf
 
     def mark(self, stream):

@@ -39,7 +39,6 @@ struct AttnParams {
   float* lse;               // fp32 [S][B][Hq] or null
   float* part_o;            // partial O, MFMA accumulator order, per (unit, chunk)
   float* part_ml;           // partial (max, sum) per (unit, chunk, row)
-  uint32_t* counters;       // word 2u per unit, sparse pass only (self-resetting)
   int32_t S, B, Hq, Hkv, G, R;
   int32_t chunk;            // keys (exact) or idx entries (sparse) per work-group
   int32_t nchunk;           // chunks per unit in the grid
@@ -56,13 +55,12 @@ struct MergeParams {
   float* rowstat;           // per (unit, row): max + log2(sum), log2 units
   int32_t S, B, Hq, Hkv, G, R, nrb;
   int32_t chunk, nchunk;
-  int32_t n_uniform;        // >= 0: contiguous prefix length; < 0: use lens
+  int32_t n_uniform;        // >= 0: entries per unit (prefix length or idx count); < 0: lens
   SeqLens lens;
 };
 
 constexpr int kMaxSparseChunk = 4096;   // idx entries per sparse work-group (LDS row table)
 constexpr int kMaxChunkPages = 4096;    // page ids per exact-pass work-group (paged layout)
-constexpr int kMaxMerge = 8;            // sparse chunks per unit (in-kernel merge)
 
 __device__ __forceinline__ int swap_bits23(int m) {
   return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
@@ -211,7 +209,6 @@ __global__ __launch_bounds__(kAttnThreads) void attn_chunk_kernel(AttnParams p) 
   // sparse: K/V row index of every entry of the chunk (-1 = skipped)
   // exact, paged: page ids of the chunk
   __shared__ int32_t s_tab[kSparse ? kMaxSparseChunk : kMaxChunkPages];
-  __shared__ int s_last;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -228,6 +225,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_chunk_kernel(AttnParams p) 
     c = blockIdx.x % p.nchunk;
   }
   if (u >= units) return;
+  MAGE_TRACE_POINT(0);
   const int s = u / p.Hkv, h = u - s * p.Hkv;
   const int ns = seq_len_of(p.kv, p.lens, s);
   const int e0 = c * p.chunk;
@@ -278,6 +276,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_chunk_kernel(AttnParams p) 
     }
   }
   __syncthreads();  // row tables visible, Q loads complete (vmcnt drained)
+  MAGE_TRACE_POINT(1);
 
   // element offset of the K/V row holding chunk entry e (always a readable row)
   auto row_of_entry = [&](int e) -> int64_t {
@@ -335,6 +334,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_chunk_kernel(AttnParams p) 
     wait_lgkmcnt0();
   }
   __syncthreads();  // the ring is reused below
+  MAGE_TRACE_POINT(2);
 
   // ---- merge the two key halves of each row block through LDS ---------------
   {
@@ -383,79 +383,15 @@ __global__ __launch_bounds__(kAttnThreads) void attn_chunk_kernel(AttnParams p) 
       p.part_ml[(slot * kMaxRows + 32 * rb + n) * 2 + 1] = l_run;
     }
   }
-  if (!kSparse) return;
-
-  // sparse pass: the last chunk of a unit to finish merges all of them; the
-  // two waves of a row block split the d blocks
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const unsigned prev = atomicAdd(&p.counters[2 * u], 1u);
-    __threadfence();
-    s_last = prev == static_cast<unsigned>(p.nchunk - 1);
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  if (tid == 0) p.counters[2 * u] = 0u;
-  if (!computes) return;
-  const int r = 32 * rb + n;
-  const int64_t slot0 = static_cast<int64_t>(u) * p.nchunk;
-  float mc[kMaxMerge], lc[kMaxMerge];
-#pragma unroll
-  for (int cc = 0; cc < kMaxMerge; ++cc) {  // clamped loads, masked after
-    const int64_t sl = slot0 + min(cc, p.nchunk - 1);
-    mc[cc] = p.part_ml[(sl * kMaxRows + r) * 2];
-    lc[cc] = p.part_ml[(sl * kMaxRows + r) * 2 + 1];
-  }
-#pragma unroll
-  for (int cc = 0; cc < kMaxMerge; ++cc)
-    if (cc >= p.nchunk) mc[cc] = -__builtin_inff();
-  float M = -__builtin_inff();
-#pragma unroll
-  for (int cc = 0; cc < kMaxMerge; ++cc) M = fmaxf(M, mc[cc]);
-  const float Mu = M == -__builtin_inff() ? 0.f : M;
-  float L = 0.f;
-#pragma unroll
-  for (int cc = 0; cc < kMaxMerge; ++cc) {
-    mc[cc] = fast_exp2(mc[cc] - Mu);  // now the weight of chunk cc
-    L += lc[cc] * mc[cc];
-  }
-  const bool row_ok = r < p.R;
-  const int b = row_ok ? r / p.G : 0, g = r - b * p.G;
-  const int64_t orow = (static_cast<int64_t>(s) * p.B + b) * p.Hq + h * p.G + g;
-  const float inv = L > 0.f ? 1.f / L : 0.f;
-  // one d block at a time: all chunks' partials of the block are in flight together
-#pragma unroll
-  for (int dbh = 0; dbh < kNdb / 2; ++dbh) {
-    const int db = kh * (kNdb / 2) + dbh;
-    f32x4 part[kMaxMerge][4];
-#pragma unroll
-    for (int cc = 0; cc < kMaxMerge; ++cc)  // clamped: chunks past the end have weight 0
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4)
-        part[cc][i4] = *reinterpret_cast<const f32x4*>(
-            p.part_o + 4 * part_o_index<D>(slot0 + min(cc, p.nchunk - 1), rb, db, i4, lane));
-#pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      f32x4 acc{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int cc = 0; cc < kMaxMerge; ++cc)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[e] += mc[cc] * part[cc][i4][e];
-      if (row_ok) {
-        f32x4 v{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
-        *reinterpret_cast<f32x4*>(p.o + orow * D + 32 * db + 8 * i4 + 4 * hh) = v;
-      }
-    }
-  }
-  if (row_ok && kh == 0 && hh == 0 && p.lse != nullptr)
-    p.lse[orow] = L > 0.f ? (M + __log2f(L)) * kLn2 : -__builtin_inff();
+  MAGE_TRACE_POINT(3);
 }
 
-// Merge of the exact pass's split partials. One work-group per
-// (unit, row block, d block); wave i4 handles accumulator registers 4*i4..4*i4+3.
-// Also writes lse and the per-row max + log2(sum) that the score sweep needs.
+// Merge of split partials (exact pass: chunks of the prefix; sparse pass:
+// chunks of the index list). One work-group per (unit, row block, d block);
+// wave i4 handles accumulator registers 4*i4..4*i4+3. Also writes lse and, if
+// rowstat is non-null, the per-row max + log2(sum) that the score sweep needs.
+// A separate launch rather than an in-kernel last-arriver merge: on gfx950 the
+// device-scope fence such a handoff needs writes back the XCD's whole L2.
 template <int D>
 __global__ __launch_bounds__(kThreads) void exact_merge_kernel(MergeParams p) {
   constexpr int kNdb = D / 32;
@@ -520,7 +456,7 @@ __global__ __launch_bounds__(kThreads) void exact_merge_kernel(MergeParams p) {
   if (db == 0 && i4 == 0 && hh == 0) {
     const float c2 = M + __log2f(L);
     if (p.lse != nullptr) p.lse[row] = c2 * kLn2;
-    p.rowstat[static_cast<int64_t>(u) * kMaxRows + r] = c2;
+    if (p.rowstat != nullptr) p.rowstat[static_cast<int64_t>(u) * kMaxRows + r] = c2;
   }
 }
 

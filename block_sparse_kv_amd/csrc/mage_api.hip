@@ -50,8 +50,8 @@ mage_status check_dims(const mage_dims* d, Dims& o) {
   o.G = o.Hq / o.Hkv;
   if (static_cast<int64_t>(o.B) * o.G > MAGE_MAX_ROWS)
     return fail(MAGE_ERR_UNSUPPORTED, "block * (num_q_heads / num_kv_heads) must be <= 128");
-  if (static_cast<int64_t>(o.S) * o.Hkv > 8192)
-    return fail(MAGE_ERR_UNSUPPORTED, "num_seqs * num_kv_heads must be <= 8192");
+  if (static_cast<int64_t>(o.S) * o.Hkv > (1 << 20))
+    return fail(MAGE_ERR_UNSUPPORTED, "num_seqs * num_kv_heads must be <= 2^20");
   o.R = o.B * o.G;
   o.D = d->head_dim;
   o.nrb = (o.R + 31) / 32;
@@ -104,7 +104,7 @@ int exact_chunk(int64_t units, int64_t max_n, int64_t total_keys, int page_size)
 
 // Sparse step: at most kSparseMaxChunks chunks per (seq, KV head), aiming at
 // one work-group per CU.
-constexpr int kSparseMaxChunks = kMaxMerge;
+constexpr int kSparseMaxChunks = 32;
 constexpr int kCus = 256;
 
 // k <= kSparseMaxChunks * kMaxSparseChunk (checked by the entry points).
@@ -123,11 +123,10 @@ template <int D>
 constexpr int kStagesFor = D == 128 ? 3 : 4;
 template <int D>
 constexpr int kScoreStagesFor = 4;
-constexpr int64_t kCounterBytes = 65536;
 
 // ---- workspace layout ------------------------------------------------------
 struct Layout {
-  size_t cnt_sparse, cnt_topk, rowstat, part_ml, part_o, cand_bits, cand_pos, scores, total;
+  size_t rowstat, part_ml, part_o, cand_bits, cand_pos, scores, total;
   int64_t slots, cand_stride;
 };
 
@@ -145,11 +144,6 @@ Layout make_layout(const Dims& d, int64_t max_n, int64_t k) {
     off = round_up(off + bytes, 256);
     return at;
   };
-  // fixed-size counter region at the start, shared by every entry point and
-  // left zero by every completed call: unit u uses words 2u (sparse merge)
-  // and 2u + 1 (top-k merge)
-  L.cnt_sparse = take(kCounterBytes);
-  L.cnt_topk = L.cnt_sparse + 4;
   L.rowstat = take(U * kMaxRows * 4);
   L.part_ml = take(L.slots * kMaxRows * 2 * 4);
   L.part_o = take(L.slots * 4 * (d.D / 32) * 4 * kWave * 16);
@@ -226,6 +220,18 @@ mage_status paged_kv(const Dims& d, const mage_paged_kv* kv, KvArgs& a) {
   return MAGE_OK;
 }
 
+mage_status launch_topk(const TopkParams& tp, hipStream_t stream) {
+  hipLaunchKernelGGL(topk_local_kernel, dim3(static_cast<unsigned>(static_cast<int64_t>(tp.rows) * tp.nchunk)),
+                     dim3(kTopkThreads), 0, stream, tp);
+  if (hipError_t e = hipGetLastError(); e != hipSuccess) return hip_fail(e, "top-k launch");
+  if (tp.nchunk > 1) {
+    hipLaunchKernelGGL(topk_final_kernel, dim3(static_cast<unsigned>(tp.rows)), dim3(kTopkThreads), 0,
+                       stream, tp);
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return hip_fail(e, "top-k merge launch");
+  }
+  return MAGE_OK;
+}
+
 // k == 0: exact attention only (no score sweep, no top-k).
 template <int D>
 mage_status launch_select(const Dims& d, const uint16_t* q, const KvArgs& kv, int32_t k, float* o,
@@ -247,7 +253,6 @@ mage_status launch_select(const Dims& d, const uint16_t* q, const KvArgs& kv, in
   ap.lse = lse;
   ap.part_o = at<float>(ws, L.part_o);
   ap.part_ml = at<float>(ws, L.part_ml);
-  ap.counters = at<uint32_t>(ws, L.cnt_sparse);
   ap.S = d.S; ap.B = d.B; ap.Hq = d.Hq; ap.Hkv = d.Hkv; ap.G = d.G; ap.R = d.R;
   ap.chunk = chunk;
   ap.nchunk = nch;
@@ -308,15 +313,12 @@ mage_status launch_select(const Dims& d, const uint16_t* q, const KvArgs& kv, in
   tp.cand_bits = at<uint32_t>(ws, L.cand_bits);
   tp.cand_pos = at<int32_t>(ws, L.cand_pos);
   tp.cand_stride = L.cand_stride;
-  tp.counters = at<uint32_t>(ws, L.cnt_topk);
   tp.rows = static_cast<int32_t>(U);
   tp.rows_per_seq = d.Hkv;
   tp.n_uniform = kv.src.page_table ? -1 : kv.src.n_uniform;
   tp.nchunk = static_cast<int>(cdiv(kv.max_n, kTopkChunk));
   tp.lens = kv.lens;
-  hipLaunchKernelGGL(topk_kernel, dim3(static_cast<unsigned>(U * tp.nchunk)), dim3(kTopkThreads), 0,
-                     sel, tp);
-  if (hipError_t e = hipGetLastError(); e != hipSuccess) return hip_fail(e, "top-k launch");
+  if (mage_status st = launch_topk(tp, sel); st != MAGE_OK) return st;
   if (idx_ready) {
     if (hipError_t e = hipEventRecord(idx_ready, sel); e != hipSuccess)
       return hip_fail(e, "hipEventRecord(idx_ready)");
@@ -340,17 +342,31 @@ mage_status launch_sparse(const Dims& d, const uint16_t* q, const KvArgs& kv, co
   ap.lse = lse;
   ap.part_o = at<float>(ws, L.part_o);
   ap.part_ml = at<float>(ws, L.part_ml);
-  ap.counters = at<uint32_t>(ws, L.cnt_sparse);
   ap.S = d.S; ap.B = d.B; ap.Hq = d.Hq; ap.Hkv = d.Hkv; ap.G = d.G; ap.R = d.R;
   ap.chunk = chunk;
   ap.nchunk = nch;
-  ap.xcd_group = env_int("MAGE_SPARSE_XCD", 1) && nch > 1;
+  ap.xcd_group = env_int("MAGE_SPARSE_XCD", 0) && nch > 1;
   ap.scale_log2 = d.scale * kLog2e;
   ap.lens = kv.lens;
   const int64_t grid = ap.xcd_group ? round_up(U, 8) * nch : U * nch;
   hipLaunchKernelGGL((attn_chunk_kernel<D, true, kStagesFor<D>>), dim3(static_cast<unsigned>(grid)), dim3(kAttnThreads),
                      0, stream, ap);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return hip_fail(e, "sparse launch");
+  if (nch == 1) return MAGE_OK;  // the single chunk wrote O and lse
+  MergeParams mp{};
+  mp.part_o = ap.part_o;
+  mp.part_ml = ap.part_ml;
+  mp.o = o;
+  mp.lse = lse;
+  mp.rowstat = nullptr;
+  mp.S = d.S; mp.B = d.B; mp.Hq = d.Hq; mp.Hkv = d.Hkv; mp.G = d.G; mp.R = d.R; mp.nrb = d.nrb;
+  mp.chunk = chunk;
+  mp.nchunk = nch;
+  mp.n_uniform = k;  // every unit has k index entries
+  std::memset(&mp.lens, 0, sizeof mp.lens);
+  hipLaunchKernelGGL((exact_merge_kernel<D>), dim3(static_cast<unsigned>(U * d.nrb * (D / 32))),
+                     dim3(kThreads), 0, stream, mp);
+  if (hipError_t e = hipGetLastError(); e != hipSuccess) return hip_fail(e, "sparse merge launch");
   return MAGE_OK;
 }
 
@@ -525,7 +541,7 @@ mage_status mage_topk(int32_t rows, const float* scores, int64_t row_stride, con
       sl.n[r] = lens[r];
     }
   }
-  if (rows > 8192) return fail(MAGE_ERR_UNSUPPORTED, "rows must be <= 8192");
+  if (rows > (1 << 20)) return fail(MAGE_ERR_UNSUPPORTED, "rows must be <= 2^20");
   // workspace: the full layout for one KV head per row
   Dims d{};
   d.S = rows; d.B = 1; d.Hq = 1; d.Hkv = 1; d.G = 1; d.R = 1; d.D = 64; d.nrb = 1; d.units = rows;
@@ -537,7 +553,6 @@ mage_status mage_topk(int32_t rows, const float* scores, int64_t row_stride, con
   tp.stride = row_stride;
   tp.idx = idx;
   tp.k = k;
-  tp.counters = at<uint32_t>(workspace, L.cnt_topk);
   tp.cand_bits = at<uint32_t>(workspace, L.cand_bits);
   tp.cand_pos = at<int32_t>(workspace, L.cand_pos);
   tp.cand_stride = L.cand_stride;
@@ -546,10 +561,7 @@ mage_status mage_topk(int32_t rows, const float* scores, int64_t row_stride, con
   tp.n_uniform = lens ? -1 : n;
   tp.nchunk = static_cast<int>(cdiv(n, kTopkChunk));
   tp.lens = sl;
-  hipLaunchKernelGGL(topk_kernel, dim3(static_cast<unsigned>(static_cast<int64_t>(rows) * tp.nchunk)),
-                     dim3(kTopkThreads), 0, stream, tp);
-  if (hipError_t e = hipGetLastError(); e != hipSuccess) return hip_fail(e, "top-k launch");
-  return MAGE_OK;
+  return launch_topk(tp, stream);
 }
 
 const char* mage_status_string(mage_status status) {
@@ -564,5 +576,16 @@ const char* mage_status_string(mage_status status) {
 }
 
 const char* mage_last_error(void) { return g_last_error.c_str(); }
+
+#ifdef MAGE_TRACE
+// Debug builds only: copy the per-work-group phase timestamps to host memory.
+int mage_debug_trace(void* host, size_t bytes) {
+  return hipMemcpyFromSymbol(host, HIP_SYMBOL(mage::g_trace), std::min(bytes, sizeof(mage::g_trace))) == hipSuccess ? 0 : -1;
+}
+int mage_debug_trace_clear(void) {
+  static uint64_t zeros[8192][8];
+  return hipMemcpyToSymbol(HIP_SYMBOL(mage::g_trace), zeros, sizeof(zeros)) == hipSuccess ? 0 : -1;
+}
+#endif
 
 }  // extern "C"

@@ -86,4 +86,18 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
   return lane == 0 ? 0ull : (~0ull >> (64 - lane));
 }
 
+#ifdef MAGE_TRACE
+// Debug-only phase timestamps (100 MHz real-time counter) per work-group.
+__device__ uint64_t g_trace[8192][8];
+#define MAGE_TRACE_POINT(slot)                                              \
+  do {                                                                      \
+    if (threadIdx.x == 0 && blockIdx.x < 8192)                               \
+      mage::g_trace[blockIdx.x][slot] = __builtin_amdgcn_s_memrealtime();  \
+  } while (0)
+#else
+#define MAGE_TRACE_POINT(slot) \
+  do {                         \
+  } while (0)
+#endif
+
 }  // namespace mage

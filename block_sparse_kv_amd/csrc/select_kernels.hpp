@@ -12,13 +12,14 @@
 // Top-k: the k_eff largest scores, ties to the lower position, ascending
 // output. Scores are >= +0, so their fp32 bit patterns order like the values
 // and the selection is integer work on those bits: an MSB-first radix select
-// (digits of 12, 11 and 9 bits, LDS histograms) finds the k-th largest bit
-// pattern T and how many entries equal to T to keep; an index-ordered
-// compaction (wave ballots + prefix popcounts) then keeps every entry > T and
-// the lowest-positioned entries == T. Each work-group does this for a
-// 16384-position chunk held in LDS; the last chunk of a head to finish runs
-// the same selection over the concatenated per-chunk winners, which are in
-// position order, so its output is already ascending.
+// (12-bit digits, LDS histograms) finds the k-th largest bit pattern T and how
+// many entries equal to T to keep; an index-ordered compaction (wave ballots +
+// prefix popcounts) then keeps every entry > T and the lowest-positioned
+// entries == T. A first kernel does this per 16384-position chunk held in LDS;
+// a second kernel runs the same selection over the concatenated per-chunk
+// winners, which are in position order, so its output is already ascending.
+// The two kernels replace an in-kernel last-arriver handoff: on gfx950 a
+// device-scope fence writes back the XCD's whole L2, which costs microseconds.
 #pragma once
 
 #include "attn_kernels.hpp"
@@ -189,7 +190,6 @@ struct TopkParams {
   uint32_t* cand_bits;      // per row: nchunk * min(k, chunk) winners
   int32_t* cand_pos;
   int64_t cand_stride;
-  uint32_t* counters;       // word 2u per row (self-resetting)
   int32_t rows;
   int32_t rows_per_seq;     // row u belongs to sequence u / rows_per_seq
   int32_t n_uniform;        // >= 0: every row has this many entries; else lens
@@ -199,10 +199,28 @@ struct TopkParams {
 
 struct TopkShared {
   uint32_t hist[4096];
-  int32_t wsum[kTopkWaves];
-  int32_t wsum2[kTopkWaves];
+  __attribute__((aligned(16))) int32_t wsum[kTopkWaves];
+  __attribute__((aligned(16))) int32_t wsum2[kTopkWaves];
   int32_t res[2];
 };
+
+// Sum of the 16 per-wave values in w[] (vector LDS reads, broadcast to all
+// lanes) and the part of it contributed by waves below `wv`.
+__device__ __forceinline__ void wave_totals(const int32_t* w, int wv, int& below, int& total) {
+  typedef int i4 __attribute__((ext_vector_type(4)));
+  const i4* v = reinterpret_cast<const i4*>(w);
+  below = 0;
+  total = 0;
+#pragma unroll
+  for (int q = 0; q < kTopkWaves / 4; ++q) {
+    const i4 x = v[q];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      total += x[e];
+      below += (4 * q + e < wv) ? x[e] : 0;
+    }
+  }
+}
 
 // Block-wide inclusive prefix sum of one int per thread; also returns the total.
 __device__ __forceinline__ int block_inclusive_scan(int v, int32_t* wsum, int& total) {
@@ -214,47 +232,73 @@ __device__ __forceinline__ int block_inclusive_scan(int v, int32_t* wsum, int& t
   }
   if (lane == 63) wsum[wv] = v;
   __syncthreads();
-  int before = 0;
-  total = 0;
-  for (int i = 0; i < kTopkWaves; ++i) {
-    const int t = wsum[i];
-    before += i < wv ? t : 0;
-    total += t;
-  }
+  int before;
+  wave_totals(wsum, wv, before, total);
   __syncthreads();
   return v + before;
 }
 
+// Bitwise OR over the work-group (one value per thread); result valid after return.
+__device__ __forceinline__ uint32_t block_or(uint32_t v, int32_t* wsum) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) v |= __shfl_xor(v, off);
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  if (lane == 0) wsum[wv] = static_cast<int32_t>(v);
+  __syncthreads();
+  typedef int i4 __attribute__((ext_vector_type(4)));
+  const i4* w = reinterpret_cast<const i4*>(wsum);
+  uint32_t all = 0;
+#pragma unroll
+  for (int q = 0; q < kTopkWaves / 4; ++q) {
+    const i4 x = w[q];
+    all |= static_cast<uint32_t>(x[0] | x[1] | x[2] | x[3]);
+  }
+  __syncthreads();
+  return all;
+}
+
 // MSB-first radix select over n bit patterns: the kk-th largest value T, and
-// how many entries equal to T belong to the top kk (need >= 1).
+// how many entries equal to T belong to the top kk (need >= 1). The bits
+// above the highest bit in which the entries differ are common to all of them
+// and are skipped, so the first 12-bit digit already separates the values
+// (a digit taken from the sign and exponent alone would send most scores to a
+// few histogram bins and serialize the LDS atomics).
 template <class Get>
 __device__ void radix_select(Get data, int n, int kk, TopkShared& sh, uint32_t& T, int& need) {
   const int tid = threadIdx.x;
-  uint32_t prefix = 0, pmask = 0;
+  const uint32_t first = data(0);
+  uint32_t diff = 0;
+  for (int i = tid; i < n; i += kTopkThreads) diff |= data(i) ^ first;
+  diff = block_or(diff, sh.wsum);
+  if (diff == 0) {  // all entries equal
+    T = first;
+    need = kk;
+    return;
+  }
+  int hi = 31 - __clz(diff);  // highest differing bit
+  uint32_t pmask = hi == 31 ? 0u : ~((2u << hi) - 1u);
+  uint32_t prefix = first & pmask;
   int rem = kk;
-  constexpr int kShift[3] = {20, 9, 0};
-  constexpr int kBits[3] = {12, 11, 9};
-#pragma unroll
-  for (int pass = 0; pass < 3; ++pass) {
-    const int shift = kShift[pass], nb = 1 << kBits[pass];
+  while (hi >= 0) {
+    const int width = min(12, hi + 1), lo = hi - width + 1, nb = 1 << width;
     for (int i = tid; i < nb; i += kTopkThreads) sh.hist[i] = 0u;
     __syncthreads();
     for (int i = tid; i < n; i += kTopkThreads) {
       const uint32_t x = data(i);
-      if ((x & pmask) == prefix) atomicAdd(&sh.hist[(x >> shift) & (nb - 1)], 1u);
+      if ((x & pmask) == prefix) atomicAdd(&sh.hist[(x >> lo) & (nb - 1)], 1u);
     }
     __syncthreads();
     // thread t owns bins [t*per, t*per + per); count above = entries with larger digits
     const int per = (nb + kTopkThreads - 1) / kTopkThreads;
-    const int lo = tid * per;
+    const int b0 = tid * per;
     int mine = 0;
     for (int b = 0; b < per; ++b)
-      if (lo + b < nb) mine += static_cast<int>(sh.hist[lo + b]);
+      if (b0 + b < nb) mine += static_cast<int>(sh.hist[b0 + b]);
     int total;
     const int incl = block_inclusive_scan(mine, sh.wsum, total);
     int above = total - incl;  // entries in bins above this thread's range
     for (int b = per - 1; b >= 0; --b) {
-      const int bin = lo + b;
+      const int bin = b0 + b;
       if (bin >= nb) continue;
       const int cnt = static_cast<int>(sh.hist[bin]);
       if (above < rem && rem <= above + cnt) {
@@ -266,63 +310,55 @@ __device__ void radix_select(Get data, int n, int kk, TopkShared& sh, uint32_t& 
     __syncthreads();
     const int digit = sh.res[0];
     rem = sh.res[1];
-    prefix |= static_cast<uint32_t>(digit) << shift;
-    pmask |= static_cast<uint32_t>(nb - 1) << shift;
+    prefix |= static_cast<uint32_t>(digit) << lo;
+    pmask |= static_cast<uint32_t>(nb - 1) << lo;
     __syncthreads();
+    hi = lo - 1;
   }
   T = prefix;
   need = rem;
 }
 
 // Keep entries > T and the first `need` entries == T, in index order.
-// Writes out_pos[j] = pos_of(i) (and out_bits[j] = data[i] if out_bits).
+// Writes out_pos[j] = pos_of(i) (and out_bits[j] = data(i) if out_bits).
+// Thread t owns the contiguous run [t*per, t*per + per); two block-wide scans
+// (of the runs' equal-to-T counts, then of their selected counts) give every
+// thread its output offset, so the loop over the data has no barriers.
 template <class Get, class PosOf>
 __device__ void ordered_compact(Get data, int n, uint32_t T, int need, PosOf pos_of,
                                 uint32_t* out_bits, int32_t* out_pos, TopkShared& sh) {
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const uint64_t below = lanemask_lt();
-  int eq_base = 0, out_base = 0;
-  for (int j0 = 0; j0 < n; j0 += kTopkThreads) {
-    const int i = j0 + tid;
-    const bool valid = i < n;
-    const uint32_t x = data(min(i, n - 1));
-    const bool gt = valid && x > T;
-    const bool eq = valid && x == T;
-    const uint64_t meq = __ballot(eq);
-    if (lane == 0) sh.wsum[wv] = __popcll(meq);
-    __syncthreads();
-    int eq_before = 0, eq_total = 0;
-    for (int v = 0; v < kTopkWaves; ++v) {
-      const int t = sh.wsum[v];
-      eq_before += v < wv ? t : 0;
-      eq_total += t;
-    }
-    const int eq_rank = eq_base + eq_before + __popcll(meq & below);
-    const bool sel = gt || (eq && eq_rank < need);
-    const uint64_t msel = __ballot(sel);
-    if (lane == 0) sh.wsum2[wv] = __popcll(msel);
-    __syncthreads();
-    int sel_before = 0, sel_total = 0;
-    for (int v = 0; v < kTopkWaves; ++v) {
-      const int t = sh.wsum2[v];
-      sel_before += v < wv ? t : 0;
-      sel_total += t;
-    }
+  const int tid = threadIdx.x;
+  const int per = (n + kTopkThreads - 1) / kTopkThreads;
+  const int i0 = min(tid * per, n), i1 = min(i0 + per, n);
+  int n_eq = 0;
+  for (int i = i0; i < i1; ++i) n_eq += data(i) == T;
+  int eq_total;
+  const int eq_before = block_inclusive_scan(n_eq, sh.wsum, eq_total) - n_eq;
+  // equal-to-T entries this run keeps: ranks eq_before .. eq_before + n_eq - 1, those below need
+  const int keep_eq = max(0, min(n_eq, need - eq_before));
+  int n_sel = keep_eq;
+  for (int i = i0; i < i1; ++i) n_sel += data(i) > T;
+  int sel_total;
+  int o = block_inclusive_scan(n_sel, sh.wsum2, sel_total) - n_sel;
+  int eq_seen = 0;
+  for (int i = i0; i < i1; ++i) {
+    const uint32_t x = data(i);
+    bool sel = x > T;
+    if (x == T) sel = eq_seen++ < keep_eq;
     if (sel) {
-      const int o = out_base + sel_before + __popcll(msel & below);
       out_pos[o] = pos_of(i);
       if (out_bits) out_bits[o] = x;
+      ++o;
     }
-    eq_base += eq_total;
-    out_base += sel_total;
-    __syncthreads();
   }
 }
 
-__global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkParams p) {
+// Pass 1: one work-group per (row, chunk of kTopkChunk positions). A row that
+// fits in one chunk is finished here; otherwise the chunk's top min(k, len)
+// entries (under the same order) go to the candidate buffer in position order.
+__global__ __launch_bounds__(kTopkThreads) void topk_local_kernel(TopkParams p) {
   __shared__ uint32_t s_data[kTopkChunk];
   __shared__ TopkShared sh;
-  __shared__ int s_last;
   const int tid = threadIdx.x;
   const int u = blockIdx.x / p.nchunk, c = blockIdx.x % p.nchunk;
   if (u >= p.rows) return;
@@ -333,6 +369,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkParams p) {
   const int len = min(kTopkChunk, n - start);
   int32_t* out = p.idx + static_cast<int64_t>(u) * p.k;
   const float* src = p.scores + static_cast<int64_t>(u) * p.stride + start;
+  MAGE_TRACE_POINT(0);
 
   if (kk == n) {  // every position is selected
     for (int i = tid; i < len; i += kTopkThreads) out[start + i] = start + i;
@@ -356,14 +393,17 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkParams p) {
     for (int j = 0; j < kPer; ++j) s_data[tid + j * kTopkThreads] = v[j];
   }
   __syncthreads();
+  MAGE_TRACE_POINT(1);
+  auto get = [&](int i) { return s_data[i]; };
   if (nch == 1) {
     // a single chunk: its winners are the answer
     uint32_t T;
     int need;
-    auto get = [&](int i) { return s_data[i]; };
     radix_select(get, len, kk, sh, T, need);
+    MAGE_TRACE_POINT(2);
     ordered_compact(get, len, T, need, [&](int i) { return start + i; }, nullptr, out, sh);
     for (int i = kk + tid; i < p.k; i += kTopkThreads) out[i] = -1;
+    MAGE_TRACE_POINT(3);
     return;
   }
   if (kc == len) {
@@ -374,22 +414,29 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkParams p) {
   } else {
     uint32_t T;
     int need;
-    auto get = [&](int i) { return s_data[i]; };
     radix_select(get, len, kc, sh, T, need);
+    MAGE_TRACE_POINT(2);
     ordered_compact(get, len, T, need, [&](int i) { return start + i; }, cb, cp, sh);
   }
+  MAGE_TRACE_POINT(3);
+}
 
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const unsigned prev = atomicAdd(&p.counters[2 * u], 1u);
-    __threadfence();
-    s_last = prev == static_cast<unsigned>(nch - 1);
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  if (tid == 0) p.counters[2 * u] = 0u;
+// Pass 2: one work-group per row with more than one chunk: the same selection
+// over the concatenated per-chunk winners (already in position order), so the
+// output comes out ascending.
+__global__ __launch_bounds__(kTopkThreads) void topk_final_kernel(TopkParams p) {
+  __shared__ uint32_t s_data[kTopkChunk];
+  __shared__ TopkShared sh;
+  const int tid = threadIdx.x;
+  const int u = blockIdx.x;
+  if (u >= p.rows) return;
+  const int n = p.n_uniform >= 0 ? p.n_uniform : p.lens.n[u / p.rows_per_seq];
+  const int kk = min(p.k, n);
+  const int nch = (n + kTopkChunk - 1) / kTopkChunk;
+  if (kk == n || nch == 1) return;  // finished by the first pass
+  MAGE_TRACE_POINT(4);
+  int32_t* out = p.idx + static_cast<int64_t>(u) * p.k;
+  const int kc_stride = min(kk, kTopkChunk);
   const uint32_t* all_bits = p.cand_bits + static_cast<int64_t>(u) * p.cand_stride;
   const int32_t* all_pos = p.cand_pos + static_cast<int64_t>(u) * p.cand_stride;
   const int total = (nch - 1) * kc_stride + min(kc_stride, n - (nch - 1) * kTopkChunk);
@@ -412,16 +459,19 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkParams p) {
       s_data[kTopkChunk / 2 + tid + j * kTopkThreads] = static_cast<uint32_t>(vp[j]);
     }
     __syncthreads();
+    MAGE_TRACE_POINT(5);
     auto get = [&](int i) { return s_data[i]; };
     radix_select(get, total, kk, sh, T, need);
-    ordered_compact(get, total, T, need, [&](int i) { return s_data[kTopkChunk / 2 + i]; }, nullptr,
-                    out, sh);
+    MAGE_TRACE_POINT(6);
+    ordered_compact(get, total, T, need, [&](int i) { return static_cast<int32_t>(s_data[kTopkChunk / 2 + i]); },
+                    nullptr, out, sh);
   } else {
     auto get = [&](int i) { return all_bits[i]; };
     radix_select(get, total, kk, sh, T, need);
     ordered_compact(get, total, T, need, [&](int i) { return all_pos[i]; }, nullptr, out, sh);
   }
   for (int i = kk + tid; i < p.k; i += kTopkThreads) out[i] = -1;
+  MAGE_TRACE_POINT(7);
 }
 
 }  // namespace mage

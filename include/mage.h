@@ -40,11 +40,10 @@
  * asynchronous and stream-ordered; host-side argument checks happen before
  * any launch, and a failed check launches nothing.
  *
- * Workspace contract: pass it zero-filled the first time (or call
- * mage_workspace_init once); every call leaves the counter region zero again
- * when its kernels complete. Calls that may run concurrently need distinct
- * workspaces; a workspace may be reused once the previous call's work
- * (including its select stream) is ordered before the new call.
+ * Workspace contract: any contents (no initialisation needed). Calls that may
+ * run concurrently need distinct workspaces; a workspace may be reused once
+ * the previous call's work (including its select stream) is ordered before
+ * the new call.
  *
  * Errors: every entry point returns a mage_status and never aborts.
  * MAGE_ERR_HIP carries the runtime's message in mage_last_error() (thread
@@ -67,7 +66,7 @@ extern "C" {
 typedef enum mage_status {
   MAGE_OK = 0,
   MAGE_ERR_INVALID_ARG = 1,          /* null pointer, bad size, Hq % Hkv != 0 */
-  MAGE_ERR_UNSUPPORTED = 2,          /* d not in {64, 128}, R > 128, S > MAGE_MAX_SEQS */
+  MAGE_ERR_UNSUPPORTED = 2,          /* d not in {64, 128}, R > 128, S > MAGE_MAX_SEQS (paged) */
   MAGE_ERR_WORKSPACE_TOO_SMALL = 3,
   MAGE_ERR_HIP = 4                   /* launch or runtime failure; see mage_last_error() */
 } mage_status;
@@ -101,8 +100,8 @@ typedef struct mage_paged_kv {
  * prefix length <= max_seq_len and any top-k budget <= k. */
 size_t mage_workspace_bytes(const mage_dims* dims, int32_t max_seq_len, int32_t k);
 
-/* Zero the workspace's counter region on `stream` (a fill kernel, no memset
- * node). Needed once per workspace unless it was allocated zero-filled. */
+/* Zero-fill a workspace on `stream` with a fill kernel (no memset node).
+ * Optional: no entry point depends on the workspace's prior contents. */
 mage_status mage_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
