@@ -6,18 +6,29 @@ T-1 sparse steps over the reused index set with fresh queries. Default
 workload: 1 sequence, 32 query / 8 KV heads, d=128, N=131072 prefix, B=32,
 k=1024, T=32 (the MAGE page's headline shape under "Key results").
 
-Protocol: inputs are resident in HBM before timing. Before every timed step a
+Protocol: inputs are resident in HBM before timing. Before every timed call a
 1 GiB scratch buffer is overwritten on the same stream (outside the timed
-window) so that K/V rows come from HBM, not from L2 or the 256 MB MALL; each
-step is bracketed by HIP events on the stream its kernels run on. `value` is
-sparse steps per second (cold); the warm (no flush) figure is reported
-separately as cache bandwidth.
+window) so that K/V rows come from HBM, not from L2 or the 256 MB MALL. Each
+kernel of a timed call is launched with HIP events attached to the launch
+itself (mage_arm_kernel_timers, hipExtLaunchKernel), so kernel durations are
+GPU start-to-end times on the stream the kernel runs on, the same quantity
+rocprofv3's kernel trace reports. A call's GPU time is the sum of its kernels'
+durations: on an uninstrumented stream the kernels of a call dispatch back to
+back, while the attached events themselves open gaps of several microseconds
+between kernels. The instrumented span (first start to last end) and an
+ordinary event pair around each call are reported beside it. `value` is
+sparse steps per second (cold).
 
     python bench.py [--steps K] [--warmup W] [--config head128k] [--no-cpu]
+    python bench.py --summarize-trace DIR           (rocprofv3 kernel-trace CSVs)
+    python bench.py --summarize-pmc FETCH_DIR WRITE_DIR   (rocprofv3 --pmc CSVs)
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import platform
@@ -26,26 +37,27 @@ import sys
 import time
 
 import numpy as np
-import torch
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-import block_sparse_kv_amd as mage  # noqa: E402
 import workloads  # noqa: E402
 
-HBM_PEAK_GBS = 8000.0
-BF16_PEAK_TFLOPS = 2500.0
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 METRIC = "sparse-step denoising steps/sec and HBM GB/s (% peak) at 128K ctx, k=1024, B=32"
+COPY_MIB = 256                 # size of the copy used to calibrate FETCH_SIZE / WRITE_SIZE
+KERNEL_SOURCES = ["attn_kernels.hpp", "tile_io.hpp", "mage_common.hpp", "select_kernels.hpp",
+                  "mage_api.hip"]
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+# ---- algorithmic bytes and flops -------------------------------------------------
 def sparse_bytes(w: workloads.Workload) -> int:
-    """Algorithmic bytes of one sparse step: k_eff rows of K and V per (seq, KV head),
-    plus Q (bf16) read and O (fp32) written."""
+    """One sparse step: k_eff rows of K and V per (seq, KV head), Q (bf16) read, O (fp32) written."""
     d = w.head_dim
     rows = sum(w.k_eff(s) for s in range(w.num_seqs)) * w.num_kv_heads
     q = w.num_seqs * w.block * w.num_q_heads * d * 2
@@ -53,9 +65,14 @@ def sparse_bytes(w: workloads.Workload) -> int:
     return rows * d * 2 * 2 + q + o
 
 
+def sparse_chunk_bytes(w: workloads.Workload) -> int:
+    """The sparse step's gather kernel: the K/V rows and Q (O is written by the merge)."""
+    d = w.head_dim
+    return sparse_bytes(w) - w.num_seqs * w.block * w.num_q_heads * d * 4
+
+
 def select_bytes(w: workloads.Workload) -> int:
-    """Algorithmic bytes of step 1: Q + K + V read once, O + lse written, the
-    scores written and read back once, idx written."""
+    """Step 1: Q + K + V read once, O + lse written, scores written and read back once, idx written."""
     d, S, Hkv = w.head_dim, w.num_seqs, w.num_kv_heads
     ntot = sum(w.seq_lens)
     q = S * w.block * w.num_q_heads * d * 2
@@ -66,12 +83,65 @@ def select_bytes(w: workloads.Workload) -> int:
     return q + kv + o + sc + idx
 
 
+def exact_pass_bytes(w: workloads.Workload) -> int:
+    """The exact pass kernel: Q, K and V read once (its partials stay in the workspace)."""
+    d = w.head_dim
+    return w.num_seqs * w.block * w.num_q_heads * d * 2 + sum(w.seq_lens) * w.num_kv_heads * d * 4
+
+
+def score_bytes(w: workloads.Workload) -> int:
+    """The score sweep: K read again, Q read, scores written."""
+    d = w.head_dim
+    ntot = sum(w.seq_lens) * w.num_kv_heads
+    return w.num_seqs * w.block * w.num_q_heads * d * 2 + ntot * d * 2 + ntot * 4
+
+
 def exact_flops(w: workloads.Workload) -> float:
     return 4.0 * w.block * w.num_q_heads * w.head_dim * sum(w.seq_lens)
 
 
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "block_sparse_kv_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+# ---- the GPU side --------------------------------------------------------------
+class KernelTimer:
+    """Events attached to the kernels of one library call, plus an outer event pair."""
+
+    def __init__(self, torch, n):
+        mk = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+        self.pairs = [(mk(), mk()) for _ in range(n)]
+        self.outer = (mk(), mk())
+        for a, b in self.pairs:   # torch creates the HIP events on first record
+            a.record()
+            b.record()
+        self.names = []
+
+    def kernels_ms(self):
+        return [a.elapsed_time(b) for a, b in self.pairs[:len(self.names)]]
+
+    def busy_ms(self):
+        """Sum of the call's kernel durations: its GPU time on a stream that dispatches
+        the kernels back to back."""
+        return sum(self.kernels_ms())
+
+    def span_ms(self):
+        """First kernel's start to last kernel's end; includes the gaps that the attached
+        events themselves add between kernels."""
+        n = len(self.names)
+        return self.pairs[0][0].elapsed_time(self.pairs[n - 1][1])
+
+    def outer_ms(self):
+        return self.outer[0].elapsed_time(self.outer[1])
+
+
 class Runner:
-    def __init__(self, w, inp, dev):
+    def __init__(self, torch, mage, w, inp, dev):
+        self.torch, self.mage = torch, mage
         self.w, self.dev = w, dev
         self.q1 = inp.q1.to(dev)
         self.qs = [t.to(dev) for t in inp.q_steps]
@@ -91,102 +161,417 @@ class Runner:
         self.idx = torch.empty(S, w.num_kv_heads, w.k, dtype=torch.int32, device=dev)
         self.scores = torch.empty(S, w.num_kv_heads, w.max_seq_len, dtype=torch.float32, device=dev)
 
-    def select(self):
+    def _call(self, timer, fn):
+        cur = self.torch.cuda.current_stream()
+        if timer is not None:
+            self.mage.arm_kernel_timers(timer.pairs)
+            timer.outer[0].record(cur)
+        fn()
+        if timer is not None:
+            timer.outer[1].record(cur)
+            timer.names = self.mage.last_launches()
+
+    def select(self, timer=None):
         w = self.w
         kw = dict(o=self.o, lse=self.lse, idx=self.idx, scores=self.scores, workspace=self.ws,
                   select_stream=self.side, idx_ready=self.ready)
-        if w.paged:
-            mage.select_exact_paged(self.q1, self.kp, self.vp, self.table, self.lens, w.k, w.scale, **kw)
-        else:
-            mage.select_exact(self.q1, self.k, self.v, w.k, w.scale, **kw)
-        torch.cuda.current_stream().wait_event(self.ready)
 
-    def exact_only(self):
+        def fn():
+            if w.paged:
+                self.mage.select_exact_paged(self.q1, self.kp, self.vp, self.table, self.lens, w.k,
+                                             w.scale, **kw)
+            else:
+                self.mage.select_exact(self.q1, self.k, self.v, w.k, w.scale, **kw)
+            self.torch.cuda.current_stream().wait_event(self.ready)
+        self._call(timer, fn)
+
+    def exact_only(self, timer=None):
         w = self.w
-        if w.paged:
-            mage.exact_attn_paged(self.q1, self.kp, self.vp, self.table, self.lens, w.scale,
-                                  o=self.o, lse=self.lse, workspace=self.ws)
-        else:
-            mage.exact_attn(self.q1, self.k, self.v, w.scale, o=self.o, lse=self.lse, workspace=self.ws)
 
-    def sparse(self, t):
+        def fn():
+            if w.paged:
+                self.mage.exact_attn_paged(self.q1, self.kp, self.vp, self.table, self.lens, w.scale,
+                                           o=self.o, lse=self.lse, workspace=self.ws)
+            else:
+                self.mage.exact_attn(self.q1, self.k, self.v, w.scale, o=self.o, lse=self.lse,
+                                     workspace=self.ws)
+        self._call(timer, fn)
+
+    def sparse(self, t, timer=None):
         w = self.w
         q = self.qs[t % len(self.qs)]
-        if w.paged:
-            mage.sparse_attn_paged(q, self.kp, self.vp, self.table, self.lens, self.idx, w.scale,
-                                   o=self.o2, lse=self.lse2, workspace=self.ws)
-        else:
-            mage.sparse_attn(q, self.k, self.v, self.idx, w.scale, o=self.o2, lse=self.lse2,
-                             workspace=self.ws)
 
-    def topk_only(self):
+        def fn():
+            if w.paged:
+                self.mage.sparse_attn_paged(q, self.kp, self.vp, self.table, self.lens, self.idx,
+                                            w.scale, o=self.o2, lse=self.lse2, workspace=self.ws)
+            else:
+                self.mage.sparse_attn(q, self.k, self.v, self.idx, w.scale, o=self.o2,
+                                      lse=self.lse2, workspace=self.ws)
+        self._call(timer, fn)
+
+    def topk_only(self, timer=None):
         w = self.w
         S, Hkv = w.num_seqs, w.num_kv_heads
         lens = None if not w.paged else [n for n in w.seq_lens for _ in range(Hkv)]
-        mage.topk(self.scores.view(S * Hkv, -1), w.k, lens=lens, idx=self.idx.view(S * Hkv, -1),
-                  workspace=self.ws)
+        self._call(timer, lambda: self.mage.topk(self.scores.view(S * Hkv, -1), w.k, lens=lens,
+                                                 idx=self.idx.view(S * Hkv, -1), workspace=self.ws))
 
 
-def timed(fn, flush, n):
-    """Per-call HIP-event durations (ms) of fn, each preceded by a cache flush."""
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
-    for i in range(n):
-        if flush is not None:
-            flush()
-        evs[i][0].record()
-        fn(i)
-        evs[i][1].record()
-    torch.cuda.synchronize()
-    return [a.elapsed_time(b) for a, b in evs]
+def by_kernel(timers):
+    """{kernel name: [durations in us]} over a list of finished timers."""
+    out = {}
+    for t in timers:
+        for name, ms in zip(t.names, t.kernels_ms()):
+            out.setdefault(name, []).append(ms * 1e3)
+    return out
 
 
-def cpu_baseline(w, inp, max_seconds=30.0):
-    """The fp64 oracle on the host cores over a bounded sample of the same workload."""
+def pct(a, p):
+    return float(np.percentile(a, p))
+
+
+# ---- the oracle on the host cores ------------------------------------------------
+def cpu_baseline(w, inp, budget_s=20.0):
+    """The fp64 oracle as it stands, timed on the host cores over a bounded sample of the
+    same workload: step 1 (exact + scores + top-k) per (seq, KV head) unit, longest first,
+    for about 45% of the budget, then whole-batch sparse steps with the oracle's own index
+    sets for about 45%. Returns sparse steps/s of the whole batch."""
     import oracle
-    res = {}
-    # one full sparse step (every KV head) with the GPU-independent oracle index set of head 0 reused
-    S, Hkv = w.num_seqs, w.num_kv_heads
-    G = w.group
-    n0 = w.seq_lens[0]
-    # step-1 exact + select for KV head 0 of sequence 0
-    q1 = inp.q1[:1, :, 0:G].contiguous()
-    if w.paged:
-        kc = torch.from_numpy(oracle.depage(inp.k_pool, inp.page_table[:1], [n0])[0][None, :1].copy()).view(torch.bfloat16)
-        vc = torch.from_numpy(oracle.depage(inp.v_pool, inp.page_table[:1], [n0])[0][None, :1].copy()).view(torch.bfloat16)
-        kfull = vfull = None
-    else:
-        kc, vc = inp.k[:1, :1].contiguous(), inp.v[:1, :1].contiguous()
-        kfull, vfull = inp.k, inp.v
+    S, Hkv, G = w.num_seqs, w.num_kv_heads, w.group
+    units = [(s, h) for s in range(S) for h in range(Hkv)]
+    # longest sequences first so the sample has the workload's heaviest units
+    units.sort(key=lambda u: (-w.seq_lens[u[0]], u))
+
+    def unit_kv(s, h):
+        n = w.seq_lens[s]
+        if w.paged:
+            kk = oracle.depage(inp.k_pool, inp.page_table[s:s + 1], [n])[0][h:h + 1][None]
+            vv = oracle.depage(inp.v_pool, inp.page_table[s:s + 1], [n])[0][h:h + 1][None]
+            return np.ascontiguousarray(kk), np.ascontiguousarray(vv)
+        return inp.k[s:s + 1, h:h + 1].contiguous(), inp.v[s:s + 1, h:h + 1].contiguous()
+
+    sel_t, keys_done, idx_of, runs = 0.0, 0, {}, 0
+    # step 1 over the units, cycling through them until about 45% of the budget is spent
+    while sel_t < 0.45 * budget_s:
+        s, h = units[runs % len(units)]
+        kc, vc = unit_kv(s, h)
+        q1 = inp.q1[s:s + 1, :, h * G:(h + 1) * G].contiguous()
+        t0 = time.perf_counter()
+        _, _, _, idx = oracle.select_exact(q1, kc, vc, w.scale, w.k)
+        sel_t += time.perf_counter() - t0
+        keys_done += w.seq_lens[s]
+        idx_of[(s, h)] = idx
+        runs += 1
+    n_sel = runs
+    sel_est = sel_t * (sum(w.seq_lens) * Hkv) / keys_done   # whole batch, by prefix keys
+    # sparse steps over every unit. Units without a step-1 result take the index set of a
+    # sampled unit, clipped to their length (any valid set costs the same gather work).
+    # Paged caches are de-paged before the clock starts.
+    some = next(iter(idx_of.values()))
+    work = []
+    for (s, h) in units:
+        kc, vc = unit_kv(s, h)
+        idx = idx_of.get((s, h), some)
+        idx = np.where(idx < w.seq_lens[s], idx, -1).astype(np.int32)
+        work.append((inp.q_steps[0][s:s + 1, :, h * G:(h + 1) * G].contiguous(), kc, vc, idx))
+    step_t = []
+    while len(step_t) < 3 or (sum(step_t) < 0.45 * budget_s and len(step_t) < 5000):
+        t0 = time.perf_counter()
+        for q2, kc, vc, idx in work:
+            oracle.sparse(q2, kc, vc, idx, w.scale)
+        step_t.append(time.perf_counter() - t0)
+    med = statistics.median(step_t)
+    sample = (f"oracle (C++ fp64, OpenMP) on the host: {n_sel} step-1 runs over the {len(units)} "
+              f"(seq, KV head) units ({sel_t:.1f} s, {keys_done} prefix keys), then "
+              f"{len(step_t)} whole-batch sparse steps (median {med * 1e3:.1f} ms per step)")
+    return {"value": 1.0 / med, "select_step_s_est": sel_est, "sample": sample,
+            "cores": oracle.num_threads(), "cpu_seconds": sel_t + sum(step_t)}
+
+
+# ---- traffic from committed counter summaries ------------------------------------
+def traffic_record(config: str):
+    """The per-launch HBM bytes of the sparse gather kernel from the committed counter
+    summary, or None when it is absent or was taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"sparse_traffic_{config}.md")
+    if not os.path.exists(path):
+        return None
+    rec = None
+    with open(path) as fh:
+        for line in fh:
+            if line.startswith("traffic: "):
+                rec = json.loads(line[len("traffic: "):])
+    if rec is None or rec.get("source_digest") != source_digest():
+        return None
+    return rec
+
+
+# ---- the benchmark ---------------------------------------------------------------
+def run_bench(args):
+    import torch
+    import block_sparse_kv_amd as mage
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    w = workloads.CONFIG_BY_NAME[args.config]
     t0 = time.perf_counter()
-    _, _, _, idx0 = oracle.select_exact(q1, kc, vc, w.scale, w.k)
-    t_sel_head = time.perf_counter() - t0
-    res["select_one_head_s"] = t_sel_head
-    # sparse steps over all heads (contiguous workloads) or head 0 (paged)
-    if kfull is not None:
-        idx = np.repeat(idx0, Hkv, axis=1)
-        runs = []
-        while len(runs) < 5 and sum(runs) < max_seconds / 3:
-            t0 = time.perf_counter()
-            oracle.sparse(inp.q_steps[0], kfull, vfull, idx, w.scale)
-            runs.append(time.perf_counter() - t0)
-        t_sparse = statistics.median(runs)
-        sample = (f"oracle: step-1 exact+select of 1 of {S * Hkv} (seq, KV head) units "
-                  f"({t_sel_head:.2f} s), then {len(runs)} full sparse steps over all {Hkv} KV heads "
-                  f"(median {t_sparse * 1e3:.1f} ms)")
-    else:
-        runs = []
-        while len(runs) < 5 and sum(runs) < max_seconds / 3:
-            t0 = time.perf_counter()
-            oracle.sparse(inp.q_steps[0][:1, :, 0:G].contiguous(), kc, vc, idx0, w.scale)
-            runs.append(time.perf_counter() - t0)
-        t_sparse = statistics.median(runs) * S * Hkv
-        sample = (f"oracle: step-1 exact+select and {len(runs)} sparse steps of (seq 0, KV head 0), "
-                  f"scaled x{S * Hkv} to the whole batch")
-    res["value"] = 1.0 / t_sparse
-    res["select_step_s_est"] = t_sel_head * S * Hkv * (sum(w.seq_lens) / (n0 * S))
-    res["sample"] = sample
-    res["cores"] = oracle.num_threads()
-    return res
+    inp = workloads.make_inputs(w)
+    log(f"[bench] inputs for {w.name} drawn in {time.perf_counter() - t0:.1f} s")
+    r = Runner(torch, mage, w, inp, dev)
+    scratch = torch.empty(256 * 1024 * 1024, dtype=torch.int32, device=dev)   # 1 GiB
+    fill = [0]
+
+    def flush():
+        fill[0] += 1
+        scratch.fill_(fill[0])
+
+    fl = (lambda: None) if args.no_flush else flush
+    T = w.steps
+    for _ in range(args.warmup):
+        r.select()
+        for t in range(T - 1):
+            r.sparse(t)
+    torch.cuda.synchronize()
+    log("[bench] warm-up done")
+
+    sel_timers = [KernelTimer(torch, mage.MAX_TIMED_LAUNCHES) for _ in range(args.steps)]
+    sp_timers = [KernelTimer(torch, 2) for _ in range(args.steps * (T - 1))]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for i in range(args.steps):
+        fl()
+        r.select(sel_timers[i])
+        for t in range(T - 1):
+            fl()
+            r.sparse(t, sp_timers[i * (T - 1) + t])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    log(f"[bench] timed {args.steps} blocks in {wall:.2f} s wall (with a 1 GiB flush before every call)")
+
+    # secondary measurements
+    ex_timers = []
+    for _ in range(5):
+        fl()
+        tm = KernelTimer(torch, 2)
+        r.exact_only(tm)
+        ex_timers.append(tm)
+    warm_timers = []
+    for t in range(2 * (T - 1)):
+        tm = KernelTimer(torch, 2)
+        r.sparse(t, tm)
+        warm_timers.append(tm)
+    r.select()
+    torch.cuda.synchronize()
+    tk_timers = []
+    for _ in range(5):
+        fl()
+        tm = KernelTimer(torch, 2)
+        r.topk_only(tm)
+        tk_timers.append(tm)
+    empty = []
+    for _ in range(20):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        b.record()
+        empty.append((a, b))
+    # plain copy of known size: the calibration kernel for FETCH_SIZE / WRITE_SIZE counter runs
+    src = torch.ones(COPY_MIB * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        fl()
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+
+    sp_busy = [t.busy_ms() * 1e3 for t in sp_timers]
+    sp_span = [t.span_ms() * 1e3 for t in sp_timers]
+    sp_outer = [t.outer_ms() * 1e3 for t in sp_timers]
+    sp_k = by_kernel(sp_timers)
+    chunk_name = "attn_chunk_kernel[sparse]"
+    chunk_us = sp_k[chunk_name]
+    sel_busy = [t.busy_ms() * 1e3 for t in sel_timers]
+    sel_span = [t.span_ms() * 1e3 for t in sel_timers]
+    sel_k = by_kernel(sel_timers)
+    ex_busy = [t.busy_ms() * 1e3 for t in ex_timers]
+    warm_busy = [t.busy_ms() * 1e3 for t in warm_timers]
+    tk_busy = [t.busy_ms() * 1e3 for t in tk_timers]
+    empty_us = statistics.median([a.elapsed_time(b) * 1e3 for a, b in empty])
+
+    sp_mean = statistics.mean(sp_busy)
+    sbytes = sparse_bytes(w)
+    cbytes = sparse_chunk_bytes(w) if len(sp_timers[0].names) > 1 else sbytes
+    chunk_mean = statistics.mean(chunk_us)
+    achieved = cbytes / (chunk_mean * 1e-6) / 1e9
+    bytes_sel = select_bytes(w)
+    ideal_sel_us = max(bytes_sel / (HBM_PEAK_GBS * 1e9), exact_flops(w) / (BF16_PEAK_TFLOPS * 1e12)) * 1e6
+    sel_med = statistics.median(sel_busy)
+    ex_med = statistics.median(ex_busy)
+    exact_k = statistics.median(sel_k["attn_chunk_kernel[exact]"])
+    score_k = statistics.median(sel_k["score_kernel"])
+    topk_names = [n for n in sel_k if n.startswith("topk")]
+    topk_k = sum(statistics.median(sel_k[n]) for n in topk_names)
+    ntot = sum(w.seq_lens)
+    block_us = statistics.mean(sel_busy) + (T - 1) * sp_mean
+    traffic = traffic_record(w.name)
+    us = lambda v: round(v, 2)  # noqa: E731
+    out = {
+        "metric": METRIC,
+        "value": round(1e6 / sp_mean, 1),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(block_us * 1e-3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: {w.num_seqs} seq, {w.num_q_heads} q / {w.num_kv_heads} KV heads, "
+                               f"d={w.head_dim}, N={'ragged ' + str(list(w.seq_lens)) if w.paged else ntot}, "
+                               f"B={w.block}, k={w.k}, {T} steps/block"
+                               f"{', 16-token pages, shuffled page table' if w.paged else ''}",
+                   "global_batch": w.num_seqs, "seq_len": w.max_seq_len, "parallelism": "single GPU",
+                   "step": f"1 bench step = 1 block = step-1 exact+select + {T - 1} sparse steps "
+                           f"(ms_per_step); value = sparse denoising steps/s, cold (1 GiB flush before "
+                           f"each call); a call's time is the sum of its kernels' GPU durations"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None if traffic is None else traffic["bytes_per_launch"],
+                     "kernel": f"{chunk_name} (sparse gather + attention, one launch per step)",
+                     "bytes_per_launch": cbytes, "kernel_us_mean": us(chunk_mean),
+                     "kernel_us_median": us(statistics.median(chunk_us)), "launches": len(chunk_us)},
+        "sparse_step": {"bytes": sbytes, "gpu_us_mean": us(sp_mean),
+                        "gpu_us_median": us(statistics.median(sp_busy)),
+                        "gpu_us_p10": us(pct(sp_busy, 10)), "gpu_us_p90": us(pct(sp_busy, 90)),
+                        "GBps": round(sbytes / (sp_mean * 1e-6) / 1e9, 1),
+                        "frac_of_peak": round(sbytes / (sp_mean * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                        "kernels_us_mean": {n: us(statistics.mean(v)) for n, v in sp_k.items()},
+                        "instrumented_span_us_mean": us(statistics.mean(sp_span)),
+                        "event_pair_us_mean": us(statistics.mean(sp_outer)),
+                        "empty_event_pair_us": us(empty_us),
+                        "warm_gpu_us_median": us(statistics.median(warm_busy)),
+                        "warm_GBps": round(sbytes / (statistics.median(warm_busy) * 1e-6) / 1e9, 1)},
+        "exact_select": {"gpu_us_median": round(sel_med, 1), "roofline_us": round(ideal_sel_us, 1),
+                         "roofline_frac": round(ideal_sel_us / sel_med, 4), "bytes": bytes_sel,
+                         "kernels_us_median": {n: us(statistics.median(v)) for n, v in sel_k.items()},
+                         "exact_pass_GBps": round(exact_pass_bytes(w) / (exact_k * 1e-6) / 1e9, 1),
+                         "exact_pass_TFLOPs": round(exact_flops(w) / (exact_k * 1e-6) / 1e12, 1),
+                         "exact_pass_mfma_frac": round(exact_flops(w) / (exact_k * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                         "score_GBps": round(score_bytes(w) / (score_k * 1e-6) / 1e9, 1),
+                         "topk_us": us(topk_k),
+                         "topk_GBps": round(ntot * w.num_kv_heads * 4 / (topk_k * 1e-6) / 1e9, 1),
+                         "topk_alone_gpu_us_median": us(statistics.median(tk_busy)),
+                         "exact_only_gpu_us_median": round(ex_med, 1),
+                         "first_step_overhead": round(sel_med / ex_med - 1, 4),
+                         "instrumented_span_us_median": round(statistics.median(sel_span), 1),
+                         "event_pair_us_median": round(statistics.median([t.outer_ms() * 1e3 for t in sel_timers]), 1)},
+        "speedup_vs_exact_per_step": round(ex_med / statistics.median(sp_busy), 2),
+        "wall_s_timed_region": round(wall, 3),
+        "flushes_in_timed_region": args.steps * T if not args.no_flush else 0,
+        "gpu": torch.cuda.get_device_name(0),
+        "kernel_source_digest": source_digest(),
+    }
+    if traffic is not None:
+        out["roofline"]["traffic_source"] = f"profiles/sparse_traffic_{w.name}.md"
+    if not args.no_cpu:
+        t0 = time.perf_counter()
+        cb = cpu_baseline(w, inp)
+        out["cpu_baseline"] = {"value": round(cb["value"], 3), "unit": "steps/s", "cores": cb["cores"],
+                               "kind": "oracle", "sample": cb["sample"],
+                               "select_step_s_est": round(cb["select_step_s_est"], 2),
+                               "cpu_seconds": round(cb["cpu_seconds"], 1),
+                               "host": platform.processor() or platform.machine()}
+        log(f"[bench] cpu baseline in {time.perf_counter() - t0:.1f} s")
+    print(json.dumps(out), flush=True)
+
+
+# ---- profile summaries -----------------------------------------------------------
+def _short(name: str) -> str:
+    for key in ("attn_chunk_kernel<", "exact_merge_kernel", "score_kernel", "topk_local_kernel",
+                "topk_final_kernel", "FillFunctor", "neg_kernel"):
+        if key in name:
+            if key == "attn_chunk_kernel<":
+                return "attn_chunk_kernel[sparse]" if ", true," in name else "attn_chunk_kernel[exact]"
+            return {"FillFunctor": "flush (fill)", "neg_kernel": "copy (neg)"}.get(key, key)
+    return name[:60]
+
+
+def _dispatches(path, value_col=None):
+    rows = list(csv.DictReader(open(path)))
+    rows.sort(key=lambda r: int(r.get("Dispatch_Id") or r.get("Correlation_Id") or 0))
+    return rows
+
+
+def _cold_flags(names):
+    """A dispatch is cold when the dispatch before it is the 1 GiB flush."""
+    return [i > 0 and names[i - 1] == "flush (fill)" for i in range(len(names))]
+
+
+def summarize_trace(d):
+    path = glob.glob(os.path.join(d, "*kernel_trace.csv"))[0]
+    rows = _dispatches(path)
+    names = [_short(r["Kernel_Name"]) for r in rows]
+    cold = _cold_flags(names)
+    dur = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows]
+    agg = {}
+    for n, c, t in zip(names, cold, dur):
+        a = agg.setdefault(n, {"all": [], "cold": []})
+        a["all"].append(t)
+        if c:
+            a["cold"].append(t)
+    print("| kernel | dispatches | mean us (all) | cold dispatches | mean us (cold) | median us (cold) |")
+    print("|---|---|---|---|---|---|")
+    for n, a in sorted(agg.items(), key=lambda kv: -sum(kv[1]["all"])):
+        c = a["cold"]
+        print(f"| {n} | {len(a['all'])} | {statistics.mean(a['all']):.2f} | {len(c)} | "
+              f"{statistics.mean(c) if c else float('nan'):.2f} | {statistics.median(c) if c else float('nan'):.2f} |")
+
+
+def summarize_pmc(fetch_dir, write_dir, config):
+    w = workloads.CONFIG_BY_NAME[config]
+
+    def load(d, counter):
+        path = glob.glob(os.path.join(d, "*counter_collection.csv"))[0]
+        rows = [r for r in _dispatches(path) if r["Counter_Name"] == counter]
+        names = [_short(r["Kernel_Name"]) for r in rows]
+        cold = _cold_flags(names)
+        vals = {}
+        for n, c, r in zip(names, cold, rows):
+            vals.setdefault(n, {"all": [], "cold": []})["all"].append(float(r["Counter_Value"]))
+            if c:
+                vals[n]["cold"].append(float(r["Counter_Value"]))
+        return vals
+
+    f, wr = load(fetch_dir, "FETCH_SIZE"), load(write_dir, "WRITE_SIZE")
+    copy_bytes = COPY_MIB * 1024 * 1024
+    cf = copy_bytes / (statistics.mean(f["copy (neg)"]["all"]) * 1024)
+    cw = copy_bytes / (statistics.mean(wr["copy (neg)"]["all"]) * 1024)
+    algo = {"attn_chunk_kernel[sparse]": sparse_chunk_bytes(w), "attn_chunk_kernel[exact]": exact_pass_bytes(w),
+            "score_kernel": score_bytes(w), "copy (neg)": 2 * copy_bytes}
+    print(f"Copy calibration: a {COPY_MIB} MiB fp32 copy (torch.neg) reads {COPY_MIB} MiB and writes "
+          f"{COPY_MIB} MiB; FETCH_SIZE reads {copy_bytes / cf / 1024:.0f} KiB and WRITE_SIZE "
+          f"{copy_bytes / cw / 1024:.0f} KiB per dispatch, so bytes = FETCH_SIZE KiB x 1024 x {cf:.4f} "
+          f"and WRITE_SIZE KiB x 1024 x {cw:.4f}.\n")
+    print("| kernel | cold dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | calibrated MB | algorithmic MB | ratio |")
+    print("|---|---|---|---|---|---|---|")
+    rec = None
+    for n in sorted(f):
+        fc = f[n]["cold"] or f[n]["all"]
+        wc = (wr.get(n, {}).get("cold") or wr.get(n, {}).get("all") or [0.0])
+        fb, wb = statistics.mean(fc) * 1024 * cf, statistics.mean(wc) * 1024 * cw
+        a = algo.get(n)
+        print(f"| {n} | {len(f[n]['cold'])} | {statistics.mean(fc):.0f} | {statistics.mean(wc):.0f} | "
+              f"{(fb + wb) / 1e6:.2f} | {'' if a is None else f'{a / 1e6:.2f}'} | "
+              f"{'' if a is None else f'{(fb + wb) / a:.3f}'} |")
+        if n == "attn_chunk_kernel[sparse]":
+            rec = {"config": config, "kernel": n, "bytes_per_launch": int(round(fb + wb)),
+                   "fetch_bytes": int(round(fb)), "write_bytes": int(round(wb)),
+                   "fetch_factor": round(cf, 5), "write_factor": round(cw, 5),
+                   "source_digest": source_digest()}
+    print()
+    if rec is not None:
+        print("traffic: " + json.dumps(rec))
 
 
 def main():
@@ -197,117 +582,18 @@ def main():
     ap.add_argument("--config", default="head128k", choices=sorted(workloads.CONFIG_BY_NAME))
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-flush", action="store_true")
+    ap.add_argument("--summarize-trace", metavar="DIR")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     args = ap.parse_args()
+    if args.summarize_trace:
+        return summarize_trace(args.summarize_trace)
+    if args.summarize_pmc:
+        return summarize_pmc(*args.summarize_pmc, args.config)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
+        print("bench.py measures one GPU: this library has no multi-GPU path; run with --gpus 1",
               file=sys.stderr)
         sys.exit(2)
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(2)
-    dev = torch.device("cuda:0")
-    w = workloads.CONFIG_BY_NAME[args.config]
-    t0 = time.perf_counter()
-    inp = workloads.make_inputs(w)
-    log(f"[bench] inputs for {w.name} drawn in {time.perf_counter() - t0:.1f} s")
-    r = Runner(w, inp, dev)
-    scratch = torch.empty(256 * 1024 * 1024, dtype=torch.int32, device=dev)   # 1 GiB
-    fill = [0]
-
-    def flush():
-        fill[0] += 1
-        scratch.fill_(fill[0])
-
-    fl = None if args.no_flush else flush
-    T = w.steps
-    # warm-up
-    for _ in range(args.warmup):
-        r.select()
-        for t in range(T - 1):
-            r.sparse(t)
-    torch.cuda.synchronize()
-    log("[bench] warm-up done")
-
-    # timed region: K blocks
-    sel_ms, sp_ms = [], []
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    for _ in range(args.steps):
-        sel_ms += timed(lambda i: r.select(), fl, 1)
-        sp_ms += timed(lambda i: r.sparse(i), fl, T - 1)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    log(f"[bench] timed {args.steps} blocks in {wall:.2f} s wall")
-
-    # secondary measurements
-    exact_ms = timed(lambda i: r.exact_only(), fl, 5)
-    warm = timed(lambda i: r.sparse(i), None, 3 * (T - 1))
-    r.select()
-    torch.cuda.synchronize()
-    topk_ms = timed(lambda i: r.topk_only(), fl, 5)
-    empty = timed(lambda i: None, None, 20)
-
-    sp_med = statistics.median(sp_ms)
-    sp_mean = statistics.mean(sp_ms)
-    sel_med = statistics.median(sel_ms)
-    block_ms = statistics.mean(sel_ms) + (T - 1) * sp_mean
-    sbytes = sparse_bytes(w)
-    gbs = sbytes / (sp_mean * 1e-3) / 1e9
-    bytes_sel = select_bytes(w)
-    ideal_sel_us = max(bytes_sel / (HBM_PEAK_GBS * 1e9), exact_flops(w) / (BF16_PEAK_TFLOPS * 1e12)) * 1e6
-    ntot = sum(w.seq_lens)
-    out = {
-        "metric": METRIC,
-        "value": round(1e3 / sp_mean, 1),
-        "unit": "steps/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(block_ms, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": f"{w.name}: {w.num_seqs} seq, {w.num_q_heads} q / {w.num_kv_heads} KV heads, "
-                               f"d={w.head_dim}, N={'ragged ' if w.paged else ''}{ntot if not w.paged else list(w.seq_lens)}, "
-                               f"B={w.block}, k={w.k}, {T} steps/block"
-                               f"{', 16-token pages' if w.paged else ''}",
-                   "global_batch": w.num_seqs, "seq_len": w.max_seq_len, "parallelism": "single GPU",
-                   "step": f"1 block = step-1 exact+select + {T - 1} sparse steps; value = sparse steps/s (cold)"},
-        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "attn_chunk_kernel<128, sparse> (one launch per sparse step)",
-                     "bytes_per_launch": sbytes},
-        "sparse_step_us": {"mean": round(sp_mean * 1e3, 2), "median": round(sp_med * 1e3, 2),
-                           "p10": round(float(np.percentile(sp_ms, 10)) * 1e3, 2),
-                           "p90": round(float(np.percentile(sp_ms, 90)) * 1e3, 2),
-                           "warm_median": round(statistics.median(warm) * 1e3, 2),
-                           "warm_GBps": round(sbytes / (statistics.median(warm) * 1e-3) / 1e9, 1),
-                           "empty_event_pair_us": round(statistics.median(empty) * 1e3, 2)},
-        "exact_select_us": {"median": round(sel_med * 1e3, 1),
-                            "roofline_us": round(ideal_sel_us, 1),
-                            "roofline_frac": round(ideal_sel_us / (sel_med * 1e3), 4),
-                            "bytes": bytes_sel,
-                            "exact_only_median_us": round(statistics.median(exact_ms) * 1e3, 1),
-                            "first_step_overhead": round(sel_med / statistics.median(exact_ms) - 1, 4),
-                            "exact_GBps": round(bytes_sel / (statistics.median(exact_ms) * 1e-3) / 1e9, 1),
-                            "exact_TFLOPs": round(exact_flops(w) / (statistics.median(exact_ms) * 1e-3) / 1e12, 1),
-                            "topk_median_us": round(statistics.median(topk_ms) * 1e3, 2),
-                            "topk_GBps": round(ntot * w.num_kv_heads * 4 / (statistics.median(topk_ms) * 1e-3) / 1e9, 1)},
-        "speedup_vs_exact_per_step": round(statistics.median(exact_ms) / sp_med, 2),
-        "wall_s_timed_region": round(wall, 3),
-        "gpu": torch.cuda.get_device_name(0),
-    }
-    if not args.no_cpu:
-        t0 = time.perf_counter()
-        cb = cpu_baseline(w, inp)
-        out["cpu_baseline"] = {"value": round(cb["value"], 4), "unit": "steps/s", "cores": cb["cores"],
-                               "kind": "oracle", "sample": cb["sample"],
-                               "select_step_s_est": round(cb["select_step_s_est"], 2),
-                               "host": platform.processor() or platform.machine()}
-        log(f"[bench] cpu baseline in {time.perf_counter() - t0:.1f} s")
-    print(json.dumps(out), flush=True)
+    run_bench(args)
 
 
 if __name__ == "__main__":

@@ -13,6 +13,8 @@ Entry points mirror the C ABI:
 * :func:`sparse_attn` / :func:`sparse_attn_paged` -- a later step over the
   reused index set.
 * :func:`topk` -- the selection on its own, over caller-provided scores.
+* :func:`arm_kernel_timers` / :func:`last_launches` -- per-kernel GPU timing
+  of the next call (HIP events attached to the kernel launches).
 """
 from __future__ import annotations
 
@@ -27,6 +29,8 @@ LIB_PATH = os.path.join(_PKG, "libmage.so")
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE_TOO_SMALL, ERR_HIP = range(5)
 MAX_SEQS = 256
 MAX_ROWS = 128
+MAX_SPARSE_K = 131072
+MAX_TIMED_LAUNCHES = 8
 
 
 class MageError(RuntimeError):
@@ -83,6 +87,10 @@ def lib():
         L.mage_status_string.restype = ctypes.c_char_p
         L.mage_last_error.argtypes = []
         L.mage_last_error.restype = ctypes.c_char_p
+        L.mage_arm_kernel_timers.argtypes = [P(_vp), P(_vp), _i32]
+        L.mage_arm_kernel_timers.restype = ctypes.c_int
+        L.mage_last_launches.argtypes = [P(ctypes.c_char_p), _i32]
+        L.mage_last_launches.restype = _i32
         _lib = L
     return _lib
 
@@ -329,3 +337,27 @@ def topk(scores, k: int, lens=None, *, idx=None, workspace=None, stream=None):
     _check(lib().mage_topk(rows, _ptr(scores), scores.stride(0), lp, n, int(k), _ptr(idx),
                            _ptr(ws), ws.numel(), _stream(stream)), "mage_topk")
     return idx
+
+
+def arm_kernel_timers(events):
+    """Arm [(start, stop), ...] torch.cuda.Event pairs (timing enabled) for the
+    kernels of the next call on this thread, in launch order."""
+    n = len(events)
+    if n > MAX_TIMED_LAUNCHES:
+        raise ValueError(f"at most {MAX_TIMED_LAUNCHES} timed launches")
+    starts = (ctypes.c_void_p * max(n, 1))()
+    stops = (ctypes.c_void_p * max(n, 1))()
+    for i, (a, b) in enumerate(events):
+        for ev in (a, b):
+            if ev.cuda_event == 0:   # torch creates the HIP event on first record
+                ev.record()
+        starts[i], stops[i] = a.cuda_event, b.cuda_event
+    _check(lib().mage_arm_kernel_timers(starts, stops, n), "mage_arm_kernel_timers")
+
+
+def last_launches() -> list:
+    """Names of the kernels that the last call on this thread launched."""
+    n = int(lib().mage_last_launches(None, 0))
+    buf = (ctypes.c_char_p * max(n, 1))()
+    lib().mage_last_launches(buf, n)
+    return [buf[i].decode() for i in range(min(n, MAX_TIMED_LAUNCHES))]

@@ -1,6 +1,7 @@
 // Host side of the C ABI declared in include/mage.h: argument checks, the
 // launch plan, the workspace layout, and the two-stream issue order of step 1.
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 
 #include <cmath>
 #include <cstdio>
@@ -26,6 +27,48 @@ mage_status fail(mage_status st, const char* what) {
 mage_status hip_fail(hipError_t e, const char* where) {
   g_last_error = std::string(where) + ": " + hipGetErrorString(e);
   return MAGE_ERR_HIP;
+}
+
+// ---- kernel launches and the optional kernel timers -----------------------
+// Every launch goes through launch(): it records the kernel's name for
+// mage_last_launches and, when the caller armed timers for this call, launches
+// through hipExtLaunchKernel so that the armed events mark the kernel's start
+// and end on the GPU.
+struct LaunchLog {
+  hipEvent_t start[MAGE_MAX_TIMED_LAUNCHES];
+  hipEvent_t stop[MAGE_MAX_TIMED_LAUNCHES];
+  int armed;
+  int used;
+  const char* names[MAGE_MAX_TIMED_LAUNCHES];
+};
+thread_local LaunchLog g_launches{};
+
+// Scope of one compute entry point: starts a fresh launch log, disarms on exit.
+struct CallScope {
+  CallScope() { g_launches.used = 0; }
+  ~CallScope() { g_launches.armed = 0; }
+};
+
+template <class P>
+mage_status launch(const void* kernel, const char* name, int64_t grid, int block, hipStream_t s,
+                   P params) {
+  if (grid < 1 || grid > 0x7fffffff) return fail(MAGE_ERR_UNSUPPORTED, "launch grid out of range");
+  void* args[] = {&params};
+  const int i = g_launches.used++;
+  if (i < MAGE_MAX_TIMED_LAUNCHES) g_launches.names[i] = name;
+  hipError_t e;
+  if (i < g_launches.armed)
+    e = hipExtLaunchKernel(kernel, dim3(static_cast<unsigned>(grid)), dim3(block), args, 0, s,
+                           g_launches.start[i], g_launches.stop[i], 0);
+  else
+    e = hipLaunchKernel(kernel, dim3(static_cast<unsigned>(grid)), dim3(block), args, 0, s);
+  if (e == hipSuccess) e = hipGetLastError();
+  return e == hipSuccess ? MAGE_OK : hip_fail(e, name);
+}
+
+template <class K>
+const void* kfn(K* kernel) {
+  return reinterpret_cast<const void*>(kernel);
 }
 
 struct Dims {
@@ -221,14 +264,12 @@ mage_status paged_kv(const Dims& d, const mage_paged_kv* kv, KvArgs& a) {
 }
 
 mage_status launch_topk(const TopkParams& tp, hipStream_t stream) {
-  hipLaunchKernelGGL(topk_local_kernel, dim3(static_cast<unsigned>(static_cast<int64_t>(tp.rows) * tp.nchunk)),
-                     dim3(kTopkThreads), 0, stream, tp);
-  if (hipError_t e = hipGetLastError(); e != hipSuccess) return hip_fail(e, "top-k launch");
-  if (tp.nchunk > 1) {
-    hipLaunchKernelGGL(topk_final_kernel, dim3(static_cast<unsigned>(tp.rows)), dim3(kTopkThreads), 0,
-                       stream, tp);
-    if (hipError_t e = hipGetLastError(); e != hipSuccess) return hip_fail(e, "top-k merge launch");
-  }
+  if (mage_status st = launch(kfn(topk_local_kernel), "topk_local_kernel",
+                              static_cast<int64_t>(tp.rows) * tp.nchunk, kTopkThreads, stream, tp);
+      st != MAGE_OK)
+    return st;
+  if (tp.nchunk > 1)
+    return launch(kfn(topk_final_kernel), "topk_final_kernel", tp.rows, kTopkThreads, stream, tp);
   return MAGE_OK;
 }
 
@@ -259,9 +300,10 @@ mage_status launch_select(const Dims& d, const uint16_t* q, const KvArgs& kv, in
   ap.xcd_group = 0;
   ap.scale_log2 = scale_log2;
   ap.lens = kv.lens;
-  hipLaunchKernelGGL((attn_chunk_kernel<D, false, kStagesFor<D>>), dim3(static_cast<unsigned>(U * nch)),
-                     dim3(kAttnThreads), 0, attn, ap);
-  if (hipError_t e = hipGetLastError(); e != hipSuccess) return hip_fail(e, "exact pass launch");
+  if (mage_status st = launch(kfn(attn_chunk_kernel<D, false, kStagesFor<D>>), "attn_chunk_kernel[exact]",
+                              U * nch, kAttnThreads, attn, ap);
+      st != MAGE_OK)
+    return st;
 
   MergeParams mp{};
   mp.part_o = ap.part_o;
@@ -274,9 +316,10 @@ mage_status launch_select(const Dims& d, const uint16_t* q, const KvArgs& kv, in
   mp.nchunk = nch;
   mp.n_uniform = kv.src.page_table ? -1 : kv.src.n_uniform;
   mp.lens = kv.lens;
-  hipLaunchKernelGGL((exact_merge_kernel<D>), dim3(static_cast<unsigned>(U * d.nrb * (D / 32))),
-                     dim3(kThreads), 0, attn, mp);
-  if (hipError_t e = hipGetLastError(); e != hipSuccess) return hip_fail(e, "merge launch");
+  if (mage_status st = launch(kfn(exact_merge_kernel<D>), "exact_merge_kernel[exact]",
+                              U * d.nrb * (D / 32), kThreads, attn, mp);
+      st != MAGE_OK)
+    return st;
   if (k == 0) return MAGE_OK;
 
   if (sel && sel != attn) {
@@ -301,9 +344,10 @@ mage_status launch_select(const Dims& d, const uint16_t* q, const KvArgs& kv, in
   sp.reverse = env_int("MAGE_SCORE_REVERSE", 1);
   sp.scale_log2 = scale_log2;
   sp.lens = kv.lens;
-  hipLaunchKernelGGL((score_kernel<D, kScoreStagesFor<D>>), dim3(static_cast<unsigned>(U * sp.nchunk)), dim3(kThreads), 0,
-                     sel, sp);
-  if (hipError_t e = hipGetLastError(); e != hipSuccess) return hip_fail(e, "score launch");
+  if (mage_status st = launch(kfn(score_kernel<D, kScoreStagesFor<D>>), "score_kernel",
+                              U * sp.nchunk, kThreads, sel, sp);
+      st != MAGE_OK)
+    return st;
 
   TopkParams tp{};
   tp.scores = sp.scores;
@@ -349,9 +393,10 @@ mage_status launch_sparse(const Dims& d, const uint16_t* q, const KvArgs& kv, co
   ap.scale_log2 = d.scale * kLog2e;
   ap.lens = kv.lens;
   const int64_t grid = ap.xcd_group ? round_up(U, 8) * nch : U * nch;
-  hipLaunchKernelGGL((attn_chunk_kernel<D, true, kStagesFor<D>>), dim3(static_cast<unsigned>(grid)), dim3(kAttnThreads),
-                     0, stream, ap);
-  if (hipError_t e = hipGetLastError(); e != hipSuccess) return hip_fail(e, "sparse launch");
+  if (mage_status st = launch(kfn(attn_chunk_kernel<D, true, kStagesFor<D>>), "attn_chunk_kernel[sparse]",
+                              grid, kAttnThreads, stream, ap);
+      st != MAGE_OK)
+    return st;
   if (nch == 1) return MAGE_OK;  // the single chunk wrote O and lse
   MergeParams mp{};
   mp.part_o = ap.part_o;
@@ -364,10 +409,8 @@ mage_status launch_sparse(const Dims& d, const uint16_t* q, const KvArgs& kv, co
   mp.nchunk = nch;
   mp.n_uniform = k;  // every unit has k index entries
   std::memset(&mp.lens, 0, sizeof mp.lens);
-  hipLaunchKernelGGL((exact_merge_kernel<D>), dim3(static_cast<unsigned>(U * d.nrb * (D / 32))),
-                     dim3(kThreads), 0, stream, mp);
-  if (hipError_t e = hipGetLastError(); e != hipSuccess) return hip_fail(e, "sparse merge launch");
-  return MAGE_OK;
+  return launch(kfn(exact_merge_kernel<D>), "exact_merge_kernel[sparse]", U * d.nrb * (D / 32),
+                kThreads, stream, mp);
 }
 
 mage_status check_ws(void* ws, size_t bytes, const Layout& L) {
@@ -420,6 +463,7 @@ mage_status mage_select_exact(const mage_dims* dims, const uint16_t* q, const ui
                               float* lse, int32_t* idx, float* scores, void* workspace,
                               size_t workspace_bytes, hipStream_t attn_stream,
                               hipStream_t select_stream, hipEvent_t idx_ready) {
+  CallScope scope;
   Dims d;
   if (mage_status st = check_dims(dims, d); st != MAGE_OK) return st;
   if (mage_status st = common_select_checks(q, k, o, lse, idx, scores); st != MAGE_OK) return st;
@@ -437,6 +481,7 @@ mage_status mage_select_exact_paged(const mage_dims* dims, const uint16_t* q, co
                                     int32_t k, float* o, float* lse, int32_t* idx, float* scores,
                                     void* workspace, size_t workspace_bytes, hipStream_t attn_stream,
                                     hipStream_t select_stream, hipEvent_t idx_ready) {
+  CallScope scope;
   Dims d;
   if (mage_status st = check_dims(dims, d); st != MAGE_OK) return st;
   if (mage_status st = common_select_checks(q, k, o, lse, idx, scores); st != MAGE_OK) return st;
@@ -453,6 +498,7 @@ mage_status mage_select_exact_paged(const mage_dims* dims, const uint16_t* q, co
 mage_status mage_exact_attn(const mage_dims* dims, const uint16_t* q, const uint16_t* k_cache,
                             const uint16_t* v_cache, int32_t seq_len, float* o, float* lse,
                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  CallScope scope;
   Dims d;
   if (mage_status st = check_dims(dims, d); st != MAGE_OK) return st;
   int32_t dummy_idx = 0;
@@ -470,6 +516,7 @@ mage_status mage_exact_attn(const mage_dims* dims, const uint16_t* q, const uint
 mage_status mage_exact_attn_paged(const mage_dims* dims, const uint16_t* q, const mage_paged_kv* kvp,
                                   float* o, float* lse, void* workspace, size_t workspace_bytes,
                                   hipStream_t stream) {
+  CallScope scope;
   Dims d;
   if (mage_status st = check_dims(dims, d); st != MAGE_OK) return st;
   int32_t dummy_idx = 0;
@@ -492,8 +539,9 @@ static mage_status sparse_common(const mage_dims* dims, const uint16_t* q, const
   if (!aligned(idx, 4) || (lse && !aligned(lse, 4)))
     return fail(MAGE_ERR_INVALID_ARG, "idx and lse must be 4-byte aligned");
   if (k < 1) return fail(MAGE_ERR_INVALID_ARG, "k must be >= 1");
-  if (k > kSparseMaxChunks * kMaxSparseChunk)
-    return fail(MAGE_ERR_UNSUPPORTED, "sparse steps take k <= 32768 index entries");
+  static_assert(MAGE_MAX_SPARSE_K <= kSparseMaxChunks * kMaxSparseChunk, "sparse plan limit");
+  if (k > MAGE_MAX_SPARSE_K)
+    return fail(MAGE_ERR_UNSUPPORTED, "sparse steps take k <= MAGE_MAX_SPARSE_K index entries");
   return MAGE_OK;
 }
 
@@ -501,6 +549,7 @@ mage_status mage_sparse_attn(const mage_dims* dims, const uint16_t* q, const uin
                              const uint16_t* v_cache, int32_t seq_len, const int32_t* idx, int32_t k,
                              float* o, float* lse, void* workspace, size_t workspace_bytes,
                              hipStream_t stream) {
+  CallScope scope;
   Dims d;
   if (mage_status st = sparse_common(dims, q, idx, k, o, lse, d); st != MAGE_OK) return st;
   KvArgs kv;
@@ -514,6 +563,7 @@ mage_status mage_sparse_attn(const mage_dims* dims, const uint16_t* q, const uin
 mage_status mage_sparse_attn_paged(const mage_dims* dims, const uint16_t* q, const mage_paged_kv* kvp,
                                    const int32_t* idx, int32_t k, float* o, float* lse,
                                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  CallScope scope;
   Dims d;
   if (mage_status st = sparse_common(dims, q, idx, k, o, lse, d); st != MAGE_OK) return st;
   KvArgs kv;
@@ -527,6 +577,7 @@ mage_status mage_sparse_attn_paged(const mage_dims* dims, const uint16_t* q, con
 mage_status mage_topk(int32_t rows, const float* scores, int64_t row_stride, const int32_t* lens,
                       int32_t n, int32_t k, int32_t* idx, void* workspace, size_t workspace_bytes,
                       hipStream_t stream) {
+  CallScope scope;
   if (rows < 1 || n < 1 || k < 1) return fail(MAGE_ERR_INVALID_ARG, "rows, n and k must be >= 1");
   if (!scores || !idx) return fail(MAGE_ERR_INVALID_ARG, "scores and idx must not be null");
   if (!aligned(scores, 4) || !aligned(idx, 4)) return fail(MAGE_ERR_INVALID_ARG, "scores and idx must be 4-byte aligned");
@@ -576,6 +627,25 @@ const char* mage_status_string(mage_status status) {
 }
 
 const char* mage_last_error(void) { return g_last_error.c_str(); }
+
+mage_status mage_arm_kernel_timers(const hipEvent_t* start, const hipEvent_t* stop, int32_t n) {
+  if (n < 0 || n > MAGE_MAX_TIMED_LAUNCHES)
+    return fail(MAGE_ERR_INVALID_ARG, "n must be in [0, MAGE_MAX_TIMED_LAUNCHES]");
+  if (n > 0 && (!start || !stop)) return fail(MAGE_ERR_INVALID_ARG, "event arrays must not be null");
+  for (int i = 0; i < n; ++i) {
+    g_launches.start[i] = start[i];
+    g_launches.stop[i] = stop[i];
+  }
+  g_launches.armed = n;
+  return MAGE_OK;
+}
+
+int32_t mage_last_launches(const char** names, int32_t max_names) {
+  const int n = g_launches.used;
+  if (names)
+    for (int i = 0; i < max_names && i < n && i < MAGE_MAX_TIMED_LAUNCHES; ++i) names[i] = g_launches.names[i];
+  return n;
+}
 
 #ifdef MAGE_TRACE
 // Debug builds only: copy the per-work-group phase timestamps to host memory.

@@ -149,8 +149,11 @@ mage_status mage_exact_attn_paged(const mage_dims* dims, const uint16_t* q,
  * subset): for every (sequence, KV head), gather the K/V rows named by
  * idx[s][h][0..k) and compute attention of the block's queries over them.
  * idx may be in any order; entries outside [0, N_s) are skipped (a head with
- * no valid entry gets O = 0, lse = -inf). lse may be null.
+ * no valid entry gets O = 0, lse = -inf). lse may be null. k (the index row
+ * length) must be in [1, MAGE_MAX_SPARSE_K], else MAGE_ERR_INVALID_ARG (k < 1)
+ * or MAGE_ERR_UNSUPPORTED (k too large).
  */
+#define MAGE_MAX_SPARSE_K 131072
 mage_status mage_sparse_attn(const mage_dims* dims, const uint16_t* q,
                              const uint16_t* k_cache, const uint16_t* v_cache,
                              int32_t seq_len, const int32_t* idx, int32_t k, float* o,
@@ -177,6 +180,27 @@ mage_status mage_topk(int32_t rows, const float* scores, int64_t row_stride,
 
 const char* mage_status_string(mage_status status);
 const char* mage_last_error(void);
+
+/*
+ * Kernel timing for benchmarks and profilers (not part of the method).
+ *
+ * mage_arm_kernel_timers arms up to MAGE_MAX_TIMED_LAUNCHES pairs of HIP
+ * events for the NEXT compute entry point called on this thread: its i-th
+ * kernel launch (launch order, i < n) is made with hipExtLaunchKernel so that
+ * start[i] / stop[i] record when that kernel begins and ends on the GPU. The
+ * events belong to the caller (created with timing enabled, on the device of
+ * the call); the arrays are copied, so they may be freed after the call. Any
+ * compute entry point disarms the timers when it returns. n = 0 disarms.
+ * Returns MAGE_ERR_INVALID_ARG for n outside [0, MAGE_MAX_TIMED_LAUNCHES] or
+ * a null array with n > 0.
+ *
+ * mage_last_launches reports the kernels that the last compute entry point on
+ * this thread launched, armed or not: it returns their number and stores up
+ * to max_names static, NUL-terminated kernel names into names (may be null).
+ */
+#define MAGE_MAX_TIMED_LAUNCHES 8
+mage_status mage_arm_kernel_timers(const hipEvent_t* start, const hipEvent_t* stop, int32_t n);
+int32_t mage_last_launches(const char** names, int32_t max_names);
 
 #ifdef __cplusplus
 }

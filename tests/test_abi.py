@@ -96,6 +96,22 @@ def test_sparse_rejects_bad_arguments():
     assert lib.mage_sparse_attn(*args(1024, FAKE, 0, 1 << 40)) == mage.ERR_INVALID_ARG
     assert lib.mage_sparse_attn(*args(-5, FAKE, 64, 1 << 40)) == mage.ERR_INVALID_ARG
     assert lib.mage_sparse_attn(*args(1024, FAKE, 64, 100)) == mage.ERR_WORKSPACE_TOO_SMALL
+    assert lib.mage_sparse_attn(*args(1 << 20, FAKE, mage.MAX_SPARSE_K + 1, 1 << 40)) == mage.ERR_UNSUPPORTED
+
+
+def test_kernel_timer_arguments():
+    """Arming checks its arguments on the host and is cleared by the next call."""
+    lib = mage.lib()
+    ev = (ctypes.c_void_p * 8)()
+    assert lib.mage_arm_kernel_timers(ev, ev, mage.MAX_TIMED_LAUNCHES + 1) == mage.ERR_INVALID_ARG
+    assert lib.mage_arm_kernel_timers(None, None, 2) == mage.ERR_INVALID_ARG
+    assert lib.mage_arm_kernel_timers(None, None, 0) == mage.OK
+    # a call that fails its checks launches nothing and reports no launches
+    d = dims()
+    assert lib.mage_sparse_attn(ctypes.byref(d), FAKE, FAKE, FAKE, 1024, None, 64, FAKE, None, FAKE,
+                                1 << 40, None) == mage.ERR_INVALID_ARG
+    assert lib.mage_last_launches(None, 0) == 0
+    assert mage.last_launches() == []
 
 
 def test_paged_rejects_bad_arguments():

@@ -1,0 +1,98 @@
+"""Parity at the full workload sizes, in the launch configuration bench.py times.
+
+The whole batch runs on the GPU through the C ABI (default plan, default
+workspace); the fp64 oracle recomputes sampled (sequence, KV head) units one
+by one (each is a plain, independent definition per unit). Bars as in
+test_gpu_parity: O and lse max-abs <= 2e-3, idx equal outside the 1e-6 tie
+band of the k-th oracle score, scores relative 1e-5.
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_kv_amd as mage
+import oracle
+import workloads
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+DEV = "cuda:0"
+TOL = 2e-3
+BAND = 1e-6
+
+# (config, sampled (seq, KV head) units)
+CASES = [
+    ("gqa32k", [(0, 0), (0, 5)]),
+    ("head128k", [(0, 3)]),
+    ("mha64k", [(0, 0), (0, 11)]),
+    ("ragged", [(7, 2), (0, 6), (3, 0)]),
+]
+
+
+def unit_inputs(inp, s, h):
+    """One unit's CPU inputs: q [1][B][G][d], k, v [1][1][N_s][d] (bf16 or their bits)."""
+    w = inp.w
+    G = w.group
+    q1 = inp.q1[s:s + 1, :, h * G:(h + 1) * G].contiguous()
+    q2 = inp.q_steps[0][s:s + 1, :, h * G:(h + 1) * G].contiguous()
+    if w.paged:
+        n = w.seq_lens[s]
+        kk = oracle.depage(inp.k_pool, inp.page_table[s:s + 1], [n])[0][h:h + 1][None]
+        vv = oracle.depage(inp.v_pool, inp.page_table[s:s + 1], [n])[0][h:h + 1][None]
+        k = np.ascontiguousarray(kk)  # uint16 bf16 bit patterns; the oracle takes either
+        v = np.ascontiguousarray(vv)
+    else:
+        k = inp.k[s:s + 1, h:h + 1].contiguous()
+        v = inp.v[s:s + 1, h:h + 1].contiguous()
+    return q1, q2, k, v
+
+
+@pytest.mark.parametrize("name,units", CASES, ids=[c[0] for c in CASES])
+def test_full_size_sampled_units(name, units):
+    w = workloads.CONFIG_BY_NAME[name]
+    print(f"[case] {name} lens={w.seq_lens[:3]}... units={units}", flush=True)
+    inp = workloads.make_inputs(w, steps=2)
+    q1 = inp.q1.to(DEV)
+    q2 = inp.q_steps[0].to(DEV)
+    side = torch.cuda.Stream(device=DEV)
+    ready = torch.cuda.Event()
+    if w.paged:
+        kp, vp = inp.k_pool.to(DEV), inp.v_pool.to(DEV)
+        tab, lens = inp.page_table.to(DEV), inp.seq_lens.tolist()
+        o, lse, idx, sc = mage.select_exact_paged(q1, kp, vp, tab, lens, w.k, w.scale,
+                                                  select_stream=side, idx_ready=ready)
+        torch.cuda.current_stream().wait_event(ready)
+        o2, lse2 = mage.sparse_attn_paged(q2, kp, vp, tab, lens, idx, w.scale)
+    else:
+        kc, vc = inp.k.to(DEV), inp.v.to(DEV)
+        o, lse, idx, sc = mage.select_exact(q1, kc, vc, w.k, w.scale, select_stream=side,
+                                            idx_ready=ready)
+        torch.cuda.current_stream().wait_event(ready)
+        o2, lse2 = mage.sparse_attn(q2, kc, vc, idx, w.scale)
+    torch.cuda.synchronize()
+    G = w.group
+    for s, h in units:
+        n = w.seq_lens[s]
+        keff = min(w.k, n)
+        uq1, uq2, uk, uv = unit_inputs(inp, s, h)
+        O, LSE, SC, IDX = oracle.select_exact(uq1, uk, uv, w.scale, w.k)
+        go = o[s:s + 1, :, h * G:(h + 1) * G].cpu().double().numpy()
+        gl = lse[s:s + 1, :, h * G:(h + 1) * G].cpu().double().numpy()
+        assert np.abs(go - O).max() <= TOL, (name, s, h)
+        assert np.abs(gl - LSE).max() <= TOL, (name, s, h)
+        gs = sc[s, h, :n].cpu().double().numpy()
+        ref = SC[0][0]
+        assert np.abs(gs - ref).max() <= 1e-5 * ref.max() + 1e-9
+        gi = idx[s, h].cpu().numpy()
+        assert (gi[keff:] == -1).all() and (np.diff(gi[:keff]) > 0).all()
+        kth = np.sort(ref)[::-1][keff - 1]
+        diff = set(gi[:keff].tolist()) ^ set(IDX[0, 0, :keff].tolist())
+        bad = [p for p in diff if abs(ref[p] - kth) > BAND]
+        assert not bad, (name, s, h, bad[:10])
+        print(f"   unit ({s},{h}): O err {np.abs(go - O).max():.2e}, idx diff {len(diff)} (in band)",
+              flush=True)
+        # later step over the GPU's own index set, both sides
+        O2, L2 = oracle.sparse(uq2, uk, uv, gi[None, None], w.scale)
+        g2 = o2[s:s + 1, :, h * G:(h + 1) * G].cpu().double().numpy()
+        assert np.abs(g2 - O2).max() <= TOL, (name, s, h)
+        assert np.abs(lse2[s:s + 1, :, h * G:(h + 1) * G].cpu().double().numpy() - L2).max() <= TOL

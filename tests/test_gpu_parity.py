@@ -240,3 +240,34 @@ def test_topk_ragged_rows():
     for r, n in enumerate(lens):
         ref = oracle.topk(sc[r, :n].numpy().astype(np.float64), 1024)[0]
         assert np.array_equal(idx[r].cpu().numpy(), ref)
+
+
+def test_kernel_timers_time_each_launch():
+    """Armed events mark each kernel of the next call; results are unchanged by timing."""
+    w = workloads.custom((20000,), 8, 2, 128, 16, 256)
+    inp = workloads.make_inputs(w, steps=2)
+    d = dev_inputs(inp)
+    _, _, idx, _ = gpu_select(inp, d)
+    ref, _ = gpu_sparse(inp, d, d["q"][0], idx)
+    mk = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    pairs = [(mk(), mk()) for _ in range(mage.MAX_TIMED_LAUNCHES)]
+    mage.arm_kernel_timers(pairs)
+    o, _ = gpu_sparse(inp, d, d["q"][0], idx)
+    names = mage.last_launches()
+    torch.cuda.synchronize()
+    assert names[0] == "attn_chunk_kernel[sparse]"
+    assert set(names[1:]) <= {"exact_merge_kernel[sparse]"}
+    ms = [a.elapsed_time(b) for a, b in pairs[:len(names)]]
+    assert all(0 < t < 100 for t in ms)
+    assert torch.equal(o, ref)
+    # the next call is untimed but still reports its launches
+    gpu_sparse(inp, d, d["q"][0], idx)
+    assert mage.last_launches() == names
+    mage.arm_kernel_timers(pairs)
+    gpu_select(inp, d)
+    names = mage.last_launches()
+    torch.cuda.synchronize()
+    assert names[:3] == ["attn_chunk_kernel[exact]", "exact_merge_kernel[exact]", "score_kernel"]
+    assert names[3] == "topk_local_kernel"
+    span = pairs[0][0].elapsed_time(pairs[len(names) - 1][1])
+    assert span >= max(a.elapsed_time(b) for a, b in pairs[:len(names)]) > 0
