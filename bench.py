@@ -387,7 +387,7 @@ def run_bench(args):
     sp_span = [t.span_ms() * 1e3 for t in sp_timers]
     sp_outer = [t.outer_ms() * 1e3 for t in sp_timers]
     sp_k = by_kernel(sp_timers)
-    chunk_name = "attn_chunk_kernel[sparse]"
+    chunk_name = "sparse_attn_kernel"
     chunk_us = sp_k[chunk_name]
     sel_busy = [t.busy_ms() * 1e3 for t in sel_timers]
     sel_span = [t.span_ms() * 1e3 for t in sel_timers]
@@ -406,7 +406,7 @@ def run_bench(args):
     ideal_sel_us = max(bytes_sel / (HBM_PEAK_GBS * 1e9), exact_flops(w) / (BF16_PEAK_TFLOPS * 1e12)) * 1e6
     sel_med = statistics.median(sel_busy)
     ex_med = statistics.median(ex_busy)
-    exact_k = statistics.median(sel_k["attn_chunk_kernel[exact]"])
+    exact_k = statistics.median(sel_k["exact_chunk_kernel"])
     score_k = statistics.median(sel_k["score_kernel"])
     topk_names = [n for n in sel_k if n.startswith("topk")]
     topk_k = sum(statistics.median(sel_k[n]) for n in topk_names)
@@ -488,11 +488,9 @@ def run_bench(args):
 
 # ---- profile summaries -----------------------------------------------------------
 def _short(name: str) -> str:
-    for key in ("attn_chunk_kernel<", "exact_merge_kernel", "score_kernel", "topk_local_kernel",
-                "topk_final_kernel", "FillFunctor", "neg_kernel"):
+    for key in ("exact_chunk_kernel", "sparse_attn_kernel", "exact_merge_kernel", "score_kernel",
+                "topk_local_kernel", "topk_final_kernel", "FillFunctor", "neg_kernel"):
         if key in name:
-            if key == "attn_chunk_kernel<":
-                return "attn_chunk_kernel[sparse]" if ", true," in name else "attn_chunk_kernel[exact]"
             return {"FillFunctor": "flush (fill)", "neg_kernel": "copy (neg)"}.get(key, key)
     return name[:60]
 
@@ -547,7 +545,7 @@ def summarize_pmc(fetch_dir, write_dir, config):
     copy_bytes = COPY_MIB * 1024 * 1024
     cf = copy_bytes / (statistics.mean(f["copy (neg)"]["all"]) * 1024)
     cw = copy_bytes / (statistics.mean(wr["copy (neg)"]["all"]) * 1024)
-    algo = {"attn_chunk_kernel[sparse]": sparse_chunk_bytes(w), "attn_chunk_kernel[exact]": exact_pass_bytes(w),
+    algo = {"sparse_attn_kernel": sparse_chunk_bytes(w), "exact_chunk_kernel": exact_pass_bytes(w),
             "score_kernel": score_bytes(w), "copy (neg)": 2 * copy_bytes}
     print(f"Copy calibration: a {COPY_MIB} MiB fp32 copy (torch.neg) reads {COPY_MIB} MiB and writes "
           f"{COPY_MIB} MiB; FETCH_SIZE reads {copy_bytes / cf / 1024:.0f} KiB and WRITE_SIZE "
@@ -564,7 +562,7 @@ def summarize_pmc(fetch_dir, write_dir, config):
         print(f"| {n} | {len(f[n]['cold'])} | {statistics.mean(fc):.0f} | {statistics.mean(wc):.0f} | "
               f"{(fb + wb) / 1e6:.2f} | {'' if a is None else f'{a / 1e6:.2f}'} | "
               f"{'' if a is None else f'{(fb + wb) / a:.3f}'} |")
-        if n == "attn_chunk_kernel[sparse]":
+        if n == "sparse_attn_kernel":
             rec = {"config": config, "kernel": n, "bytes_per_launch": int(round(fb + wb)),
                    "fetch_bytes": int(round(fb)), "write_bytes": int(round(wb)),
                    "fetch_factor": round(cf, 5), "write_factor": round(cw, 5),

@@ -1,16 +1,13 @@
-// Attention kernels of the MAGE hot path on gfx950.
+// Attention kernels of the MAGE hot path on gfx950: the step-1 exact pass
+// (split over the prefix), the later-step sparse pass (split over the reused
+// index list) and the merge of split partials. Method: "MAGE: All-[MASK]
+// Block Already Knows Where to Look in Block Diffusion LLM" (atlas.scime.ai
+// summary, "Approach"): exact attention at step 1, attention over the reused
+// top-k rows at every later step of the block.
 //
-// One kernel template serves the step-1 exact pass (split over the prefix)
-// and the later-step sparse pass (split over the gathered index list). Both
-// follow the MAGE page ("MAGE: All-[MASK] Block Already Knows Where to Look
-// in Block Diffusion LLM", atlas.scime.ai summary, "Approach"): exact
-// attention at step 1, attention over the reused top-k rows afterwards.
-//
-// Work-group = 4 waves. Wave w owns query rows 32w..32w+31 of one KV head
-// (row r = b * G + g), so the block's B tokens and the G query heads that
-// share the KV head form one MFMA tile and every K/V row staged in LDS is used
-// by all of them. K/V tiles of 64 rows stream global->LDS through a ring of
-// kStages buffers (direct LDS loads). Per tile and wave:
+// A wave owns 32 query rows of one KV head (row r = b * G + g), so the block's
+// B tokens and the G query heads that share the KV head form one MFMA tile and
+// every K/V row staged in LDS serves all of them. Per 32-key half tile:
 //   S^T[key][row] = K Q^T       v_mfma_f32_32x32x16_bf16 (A = K from LDS,
 //                               B = Q held in registers)
 //   online softmax on the rows  (exp2, scale * log2(e) folded in)
@@ -18,9 +15,6 @@
 //                               into bf16 hi + lo (P - hi), so the product keeps
 //                               ~16 mantissa bits of P; V^T comes straight from
 //                               the row-major bf16 tile via transpose reads.
-// K rows enter the A operand in the order pi(m) (bits 2 and 3 of m swapped):
-// then accumulator registers 8s..8s+7 of a lane hold 8 consecutive keys, which
-// is the B operand layout of the PV product, so P never leaves registers.
 #pragma once
 
 #include <type_traits>
@@ -42,7 +36,6 @@ struct AttnParams {
   int32_t S, B, Hq, Hkv, G, R;
   int32_t chunk;            // keys (exact) or idx entries (sparse) per work-group
   int32_t nchunk;           // chunks per unit in the grid
-  int32_t xcd_group;        // 1: keep the chunks of a unit on one XCD (grid padded to 8 units)
   float scale_log2;         // scale * log2(e)
   SeqLens lens;             // paged layout: N_s per sequence
 };
@@ -59,7 +52,6 @@ struct MergeParams {
   SeqLens lens;
 };
 
-constexpr int kMaxSparseChunk = 4096;   // idx entries per sparse work-group (LDS row table)
 constexpr int kMaxChunkPages = 4096;    // page ids per exact-pass work-group (paged layout)
 
 __device__ __forceinline__ int swap_bits23(int m) {
@@ -72,91 +64,66 @@ __device__ __forceinline__ int64_t part_o_index(int64_t slot, int w, int db, int
   return ((((slot * 4 + w) * (D / 32) + db) * 4 + i4) * kWave + lane);
 }
 
-// Write final O (and lse) of row 32w + (lane & 31) from an O^T accumulator.
-template <int D>
-__device__ __forceinline__ void store_rows(const AttnParams& p, int s, int h, int w, int lane,
-                                           float m, float l, const f32x16 (&acc)[D / 32]) {
-  const int n = lane & 31, hh = lane >> 5;
-  const int r = 32 * w + n;
-  if (r >= p.R) return;
-  const int b = r / p.G, g = r - b * p.G, j = h * p.G + g;
-  const int64_t row = (static_cast<int64_t>(s) * p.B + b) * p.Hq + j;
-  const float inv = l > 0.f ? 1.f / l : 0.f;
-  float* orow = p.o + row * D;
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      f32x4 v;
-      v[0] = acc[db][4 * i4 + 0] * inv;
-      v[1] = acc[db][4 * i4 + 1] * inv;
-      v[2] = acc[db][4 * i4 + 2] * inv;
-      v[3] = acc[db][4 * i4 + 3] * inv;
-      *reinterpret_cast<f32x4*>(orow + 32 * db + 8 * i4 + 4 * hh) = v;
-    }
-  if (hh == 0 && p.lse != nullptr)
-    p.lse[row] = l > 0.f ? (m + __log2f(l)) * kLn2 : -__builtin_inff();
-}
-
 // A row's softmax reference max is raised only when a tile's max exceeds it by
 // more than 2^kLazyLog2 (log2 units): the running O and sum are then rescaled,
 // otherwise probabilities up to 2^kLazyLog2 are accumulated as they are. The
 // result is the same softmax; the rescale (64 multiplies per lane) becomes rare.
 constexpr float kLazyLog2 = 8.f;
 
-// 8 waves: wave w handles row block w % 4 and key half w / 4 (keys 32h..32h+31
-// of every 64-key tile); the two waves of a row block merge at the end. Two
-// waves per SIMD lets one wave's softmax run under the other's MFMAs.
+// Exact-pass work-group: 8 waves, two per SIMD.
 constexpr int kAttnThreads = 512;
 
-// Online-softmax update of one 32-key half tile for one wave, then PV.
-//   k_base: LDS address of the half's first K row; kofs: this lane's K
-//   fragment offsets; v_addr: LDS address of the V tile + half offset + this
-//   lane's transpose-read offset; okm: validity bits of the half's 32 keys.
+// One 32-key half tile of one wave, in three phases so that a loop can issue
+// the QK product of the next tile before the softmax of the current one:
+//   qk_half      S^T[key][row] = K Q^T (8 MFMAs at d = 128)
+//   softmax_half online-softmax update, P = exp2(scale * S - m) split into
+//                bf16 hi + lo (P - hi), both rounded to nearest
+//   pv_half      O^T[d][row] += V^T hi^T + V^T lo^T
+// Register i of the S accumulator holds key 16(i/8) + 8hh + (i%8) of the half
+// (K rows enter in the order pi(m), bits 2 and 3 of m swapped), which is the B
+// operand layout of the PV product, so P never leaves registers.
+// l_part is the lane's share of its row's sum (the keys of its half); the two
+// shares of a row are added once, after the last tile (rescales apply to both).
 template <int D>
-__device__ __forceinline__ void attend_half(uint32_t k_base, uint32_t v_addr,
-                                            const uint32_t (&kofs)[D / 16],
-                                            const bf16x8 (&qf)[D / 16], uint32_t okm,
-                                            float scale_log2, float& m_run, float& l_run,
-                                            f32x16 (&oacc)[D / 32], int lane) {
-  constexpr int kNdb = D / 32, kNks = D / 16;
-  const int hh = lane >> 5;
+__device__ __forceinline__ f32x16 qk_half(uint32_t k_base, const uint32_t (&kofs)[D / 16],
+                                          const bf16x8 (&qf)[D / 16]) {
+  constexpr int kNks = D / 16;
+  bf16x8 kf[kNks];
   f32x16 sacc;
-  {
-    bf16x8 kf[kNks];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
-    k_frags<D, 0>(k_base, kofs, kf);
+  for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
+  k_frags<D, 0>(k_base, kofs, kf);
 #pragma unroll
-    for (int ks = 0; ks < kNks; ++ks)
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], sacc, 0, 0, 0);
-  }
-  // register i holds key 16(i/8) + 8hh + (i%8) of the half; raw q.k here
+  for (int ks = 0; ks < kNks; ++ks)
+    sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], sacc, 0, 0, 0);
+  return sacc;
+}
+
+// okm: validity bits of the half's 32 keys (only read when kMasked). No
+// branch: the rescale of the running O by `alpha` is left to the caller
+// (needed when __ballot(grow) is set), so the whole softmax is one scheduling
+// region that the MFMAs of another tile can interleave with.
+template <bool kMasked>
+__device__ __forceinline__ void softmax_half(f32x16 sacc, uint32_t okm, float scale_log2, float& m_run,
+                                             float& l_part, float& alpha, bool& grow, bf16x8 (&phi)[2],
+                                             bf16x8 (&plo)[2], int lane) {
+  const int hh = lane >> 5;
   float mt = -__builtin_inff();
-  if (okm == ~0u) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) mt = fmaxf(mt, sacc[i]);
-  } else {
+  if constexpr (kMasked) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int key = 16 * (i >> 3) + 8 * hh + (i & 7);
-      const float x = ((okm >> key) & 1) ? sacc[i] : -__builtin_inff();
-      sacc[i] = x;
-      mt = fmaxf(mt, x);
+      sacc[i] = ((okm >> key) & 1) ? sacc[i] : -__builtin_inff();
     }
   }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) mt = fmaxf(mt, sacc[i]);
   mt = wave_max_pair(mt) * scale_log2;  // scale > 0
-  const bool grow = mt > m_run + kLazyLog2;
-  if (__ballot(grow)) {
-    const float m_new = grow ? mt : m_run;
-    const float alpha = grow ? fast_exp2(m_run - m_new) : 1.f;
-    l_run *= alpha;
-#pragma unroll
-    for (int db = 0; db < kNdb; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
-    m_run = m_new;
-  }
+  grow = mt > m_run + kLazyLog2;
+  const float m_new = grow ? mt : m_run;
+  alpha = grow ? fast_exp2(m_run - m_new) : 1.f;   // m_run = -inf gives 0
+  l_part *= alpha;
+  m_run = m_new;
   const float neg_m = m_run == -__builtin_inff() ? 0.f : -m_run;
   float rs = 0.f;
 #pragma unroll
@@ -165,10 +132,8 @@ __device__ __forceinline__ void attend_half(uint32_t k_base, uint32_t v_addr,
     sacc[i] = pv;
     rs += pv;
   }
-  l_run += wave_sum_pair(rs);
-  // P = hi + lo, both bf16 (hi rounded to nearest, lo = P - hi rounded again)
+  l_part += rs;
   typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
-  bf16x8 phi[2], plo[2];
 #pragma unroll
   for (int s2 = 0; s2 < 2; ++s2) {
     u32x4 hw, lw;
@@ -188,8 +153,24 @@ __device__ __forceinline__ void attend_half(uint32_t k_base, uint32_t v_addr,
     phi[s2] = __builtin_bit_cast(bf16x8, hw);
     plo[s2] = __builtin_bit_cast(bf16x8, lw);
   }
+}
+
+template <int D>
+__device__ __forceinline__ void rescale_o(bool grow, float alpha, f32x16 (&oacc)[D / 32]) {
+  if (__ballot(grow)) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+  }
+}
+
+template <int D, int kVB = kTileKeys * 64>
+__device__ __forceinline__ void pv_half(uint32_t v_addr, const bf16x8 (&phi)[2], const bf16x8 (&plo)[2],
+                                        f32x16 (&oacc)[D / 32]) {
+  constexpr int kNdb = D / 32;
   bf16x8 vf[kNdb][2];
-  vt_frags_half<D>(v_addr, vf);
+  vt_frags_half<D, kVB>(v_addr, vf);
 #pragma unroll
   for (int db = 0; db < kNdb; ++db)
 #pragma unroll
@@ -199,65 +180,77 @@ __device__ __forceinline__ void attend_half(uint32_t k_base, uint32_t v_addr,
     }
 }
 
-template <int D, bool kSparse, int kStages>
-__global__ __launch_bounds__(kAttnThreads) void attn_chunk_kernel(AttnParams p) {
+// The three phases back to back (loops that do not pipeline).
+template <int D, int kVB = kTileKeys * 64>
+__device__ __forceinline__ void attend_half(uint32_t k_base, uint32_t v_addr,
+                                            const uint32_t (&kofs)[D / 16],
+                                            const bf16x8 (&qf)[D / 16], uint32_t okm,
+                                            float scale_log2, float& m_run, float& l_part,
+                                            f32x16 (&oacc)[D / 32], int lane) {
+  bf16x8 phi[2], plo[2];
+  float alpha;
+  bool grow;
+  const f32x16 sacc = qk_half<D>(k_base, kofs, qf);
+  if (okm == ~0u)
+    softmax_half<false>(sacc, okm, scale_log2, m_run, l_part, alpha, grow, phi, plo, lane);
+  else
+    softmax_half<true>(sacc, okm, scale_log2, m_run, l_part, alpha, grow, phi, plo, lane);
+  rescale_o<D>(grow, alpha, oacc);
+  pv_half<D, kVB>(v_addr, phi, plo, oacc);
+}
+
+// Scheduling shape of the QK product of one tile (8 MFMAs at d = 128)
+// interleaved with the softmax of the previous one (about 120 vector
+// instructions): one MFMA, then a run of vector instructions, eight times.
+__device__ __forceinline__ void interleave_qk_softmax() {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, 14, 0);  // VALU
+  }
+}
+
+// Exact pass (step 1): one work-group per (unit, chunk of the prefix).
+// 8 waves: wave w takes row block w % 4 and key half w / 4 (keys 32h..32h+31
+// of every 64-key tile); the two waves of a row block merge at the end.
+// K/V tiles stream global -> LDS through a ring of kStages stages with one
+// barrier per tile. The loop is software-pipelined: in iteration t a wave
+// issues the QK product of tile t+1 and then runs the softmax and PV of tile
+// t, so the MFMAs of one tile run under the vector work of the other.
+template <int D, int kStages>
+__global__ __launch_bounds__(kAttnThreads) void exact_chunk_kernel(AttnParams p) {
   using G = TileGeom<D, kAttnThreads>;
   constexpr int kNdb = D / 32, kNks = D / 16;
   constexpr int kStageBytes = 2 * G::kBytes;
+  static_assert(kStages >= 3, "tiles t and t+1 are read while tile t+2 loads");
   static_assert(kStages * kStageBytes >= 4 * kWave * (2 + 16 * kNdb) * 4, "pair-merge area");
   __shared__ __attribute__((aligned(1024))) uint8_t s_ring[kStages * kStageBytes];
-  // sparse: K/V row index of every entry of the chunk (-1 = skipped)
-  // exact, paged: page ids of the chunk
-  __shared__ int32_t s_tab[kSparse ? kMaxSparseChunk : kMaxChunkPages];
+  __shared__ int32_t s_pages[kMaxChunkPages];   // paged layout: page ids of the chunk
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int rb = w & 3, kh = w >> 2;
   const int hh = lane >> 5, n = lane & 31;
   const int units = p.S * p.Hkv;
-  int u, c;
-  if (p.xcd_group) {
-    const int x = blockIdx.x & 7, jj = blockIdx.x >> 3;
-    u = (jj / p.nchunk) * 8 + x;
-    c = jj % p.nchunk;
-  } else {
-    u = blockIdx.x / p.nchunk;
-    c = blockIdx.x % p.nchunk;
-  }
+  const int u = blockIdx.x / p.nchunk, c = blockIdx.x % p.nchunk;
   if (u >= units) return;
   MAGE_TRACE_POINT(0);
   const int s = u / p.Hkv, h = u - s * p.Hkv;
   const int ns = seq_len_of(p.kv, p.lens, s);
   const int e0 = c * p.chunk;
-  const int e1 = kSparse ? min(e0 + p.chunk, p.idx_k) : min(e0 + p.chunk, ns);
-  if (e0 >= e1) return;  // exact pass: chunk past this sequence's end
+  const int e1 = min(e0 + p.chunk, ns);
+  if (e0 >= e1) return;  // chunk past this sequence's end
   const int nrb = (p.R + 31) >> 5;
   const bool computes = rb < nrb;
   const bool paged = p.kv.page_table != nullptr;
   const int pshift = p.kv.page_shift, pmask = (1 << p.kv.page_shift) - 1;
   const int64_t seq_base = paged ? 0 : (static_cast<int64_t>(s) * p.Hkv + h) * p.kv.n_uniform;
   const int32_t* ptab = paged ? p.kv.page_table + static_cast<int64_t>(s) * p.kv.max_pages : nullptr;
-
-  // ---- prologue: row tables in LDS -----------------------------------------
   const int cnt = e1 - e0;
   const int page0 = e0 >> pshift;
-  if constexpr (kSparse) {
-    for (int i = tid; i < cnt; i += kAttnThreads) {
-      const int pos = p.idx[static_cast<int64_t>(u) * p.idx_k + e0 + i];
-      int row = -1;
-      if (pos >= 0 && pos < ns) {
-        if (paged)
-          row = ((ptab[pos >> pshift] * p.Hkv + h) << pshift) + (pos & pmask);
-        else
-          row = static_cast<int>(seq_base + pos);
-      }
-      s_tab[i] = row;
-    }
-  } else {
-    if (paged) {
-      const int np = ((e1 - 1) >> pshift) - page0 + 1;
-      for (int i = tid; i < np; i += kAttnThreads) s_tab[i] = ptab[page0 + i];
-    }
+  if (paged) {
+    const int np = ((e1 - 1) >> pshift) - page0 + 1;
+    for (int i = tid; i < np; i += kAttnThreads) s_pages[i] = ptab[page0 + i];
   }
 
   // Q rows of this row block as MFMA B operand fragments (d slice 16ks + 8hh .. +7)
@@ -275,26 +268,22 @@ __global__ __launch_bounds__(kAttnThreads) void attn_chunk_kernel(AttnParams p) 
       for (int ks = 0; ks < kNks; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
     }
   }
-  __syncthreads();  // row tables visible, Q loads complete (vmcnt drained)
+  __syncthreads();  // page table visible, Q loads complete (vmcnt drained)
   MAGE_TRACE_POINT(1);
 
-  // element offset of the K/V row holding chunk entry e (always a readable row)
-  auto row_of_entry = [&](int e) -> int64_t {
-    if constexpr (kSparse) {
-      const int row = s_tab[min(e, e1 - 1) - e0];
-      return static_cast<int64_t>(row < 0 ? 0 : row) * D;
-    } else {
-      const int pos = min(e, e1 - 1);
-      if (paged) {
-        const int64_t page = s_tab[(pos >> pshift) - page0];
-        return (((page * p.Hkv + h) << pshift) + (pos & pmask)) * D;
-      }
-      return (seq_base + pos) * D;
+  // element offset of the K/V row of prefix position e (clamped into the chunk)
+  auto row_of = [&](int e) -> int64_t {
+    const int pos = min(e, e1 - 1);
+    if (paged) {
+      const int64_t page = s_pages[(pos >> pshift) - page0];
+      return (((page * p.Hkv + h) << pshift) + (pos & pmask)) * D;
     }
+    return (seq_base + pos) * D;
   };
-  auto valid_entry = [&](int e) -> bool {
-    if constexpr (kSparse) return e < e1 && s_tab[e - e0] >= 0;
-    else return e < e1;
+  // validity bits of this wave's key half of tile t
+  auto half_mask = [&](int t) -> uint32_t {
+    const int nv = cnt - t * kTileKeys - 32 * kh;
+    return nv >= 32 ? ~0u : (nv <= 0 ? 0u : ((1u << nv) - 1u));
   };
 
   f32x16 oacc[kNdb];
@@ -314,25 +303,51 @@ __global__ __launch_bounds__(kAttnThreads) void attn_chunk_kernel(AttnParams p) 
     uint8_t* st = s_ring + (tile % kStages) * kStageBytes;
     const int base = e0 + tile * kTileKeys;
     issue_tile<D, true, kAttnThreads>(st, st + G::kBytes, p.kv.k, p.kv.v,
-                                      [&](int r) { return row_of_entry(base + r); }, w, lane);
+                                      [&](int r) { return row_of(base + r); }, w, lane);
   };
-  // One barrier per tile: after it, every wave's loads of tile t have landed
-  // and every wave has finished tile t-1, whose stage is refilled right away.
 #pragma unroll
   for (int t = 0; t < kStages - 1; ++t)
     if (t < ntiles) issue(t);
-  for (int t = 0; t < ntiles; ++t) {
-    wait_tiles<2 * G::kInstr, kStages - 1>(min(kStages - 2, ntiles - 1 - t));
-    wg_barrier();
-    if (t + kStages - 1 < ntiles) issue(t + kStages - 1);
-    if (computes) {
-      const uint32_t st = ring_base + (t % kStages) * kStageBytes;
-      const uint64_t okm = __ballot(valid_entry(e0 + t * kTileKeys + lane));
-      attend_half<D>(st + k_half, st + v_half, kofs, qf, static_cast<uint32_t>(okm >> (32 * kh)),
-                     p.scale_log2, m_run, l_run, oacc, lane);
+  wait_tiles<2 * G::kInstr, kStages - 1>(min(kStages - 2, ntiles - 1));
+  wg_barrier();
+  f32x16 s_cur;
+  if (computes) s_cur = qk_half<D>(ring_base + k_half, kofs, qf);
+  // One iteration: [tile t+1 resident, barrier, refill] then the QK product of
+  // tile t+1 interleaved with the softmax of tile t, then PV of tile t. In the
+  // last iteration the QK product re-reads tile t (result unused), which keeps
+  // the interleaved region free of branches.
+  auto step = [&](int t, auto masked) {
+    const bool has_next = t + 1 < ntiles;
+    if (has_next) {
+      // tile t+1 landed for every wave, and every wave is done with tile t-1
+      wait_tiles<2 * G::kInstr, kStages - 1>(min(kStages - 3, ntiles - 2 - t));
+      wg_barrier();
     }
-    wait_lgkmcnt0();
-  }
+    f32x16 s_nxt;
+    if (computes) {
+      const int tn = has_next ? t + 1 : t;
+      s_nxt = qk_half<D>(ring_base + (tn % kStages) * kStageBytes + k_half, kofs, qf);
+    }
+    if (t + kStages - 1 < ntiles) issue(t + kStages - 1);   // into the stage of tile t-1
+    if (computes) {
+      bf16x8 phi[2], plo[2];
+      float alpha;
+      bool grow;
+      softmax_half<decltype(masked)::value>(s_cur, half_mask(t), p.scale_log2, m_run, l_run, alpha,
+                                            grow, phi, plo, lane);
+      interleave_qk_softmax();
+      __builtin_amdgcn_sched_barrier(0);
+      rescale_o<D>(grow, alpha, oacc);
+      pv_half<D>(ring_base + (t % kStages) * kStageBytes + v_half, phi, plo, oacc);
+      s_cur = s_nxt;
+    }
+  };
+  for (int t = 0; t + 1 < ntiles; ++t) step(t, std::false_type{});
+  if (cnt % kTileKeys)
+    step(ntiles - 1, std::true_type{});
+  else
+    step(ntiles - 1, std::false_type{});
+  l_run = wave_sum_pair(l_run);
   __syncthreads();  // the ring is reused below
   MAGE_TRACE_POINT(2);
 
@@ -363,11 +378,6 @@ __global__ __launch_bounds__(kAttnThreads) void attn_chunk_kernel(AttnParams p) 
     }
   }
 
-  if (kSparse && p.nchunk == 1) {
-    if (computes && kh == 0) store_rows<D>(p, s, h, rb, lane, m_run, l_run, oacc);
-    return;
-  }
-
   // partial result of this chunk
   const int64_t slot = static_cast<int64_t>(u) * p.nchunk + c;
   if (computes && kh == 0) {
@@ -384,6 +394,229 @@ __global__ __launch_bounds__(kAttnThreads) void attn_chunk_kernel(AttnParams p) 
     }
   }
   MAGE_TRACE_POINT(3);
+}
+
+// ---------------------------------------------------------------------------
+// Sparse step (later denoising steps over the reused index set).
+//
+// Work-group = 4 waves = one (unit, 32-row block, chunk of the index list).
+// Wave w takes the contiguous quarter [w*kpw, (w+1)*kpw) of the chunk and
+// streams it in 32-key tiles through its own LDS ring: the wave issues its
+// own direct LDS loads and waits on its own vmcnt, so the key loop has no
+// barrier. The four waves' (max, sum, O) are merged through LDS at the end;
+// with one chunk per unit the result is final, else it is a partial in the
+// layout exact_merge_kernel reads. Work-groups of the same (unit, chunk) are
+// numbered 8 apart so that, with the round-robin placement of work-groups
+// on the 8 XCDs, they share one L2 for the rows they all gather.
+constexpr int kSparseWaves = 4;
+constexpr int kSparseThreads = kSparseWaves * kWave;
+constexpr int kSparseTileKeys = 32;
+constexpr int kSparseMaxKpw = 1024;     // index entries per wave (LDS row table)
+
+template <int D>
+struct SparseTile {
+  static constexpr int kRowBytes = D * 2;
+  static constexpr int kUnits = D / 8;                              // 16-byte units per row
+  static constexpr int kKBytes = kSparseTileKeys * kRowBytes;      // K part of a stage
+  static constexpr int kStageBytes = 2 * kKBytes;                  // K + V
+  static constexpr int kInstr = kKBytes / (kWave * 16);            // DMA instructions per part
+  static constexpr int kVBlock = kSparseTileKeys * 64;             // one 32-value d block of V
+};
+
+// DMA of one 32-key tile by one wave. K: row-major, unit u of row r at unit
+// u ^ (r mod kUnits). V: [d/32][32 rows][32 values]. row(r) = element offset
+// of tile row r in the K/V arrays (always a readable row).
+template <int D, class RowOff>
+__device__ __forceinline__ void issue_sparse_tile(uint8_t* k_lds, uint8_t* v_lds, const uint16_t* kbase,
+                                                  const uint16_t* vbase, RowOff row, int lane) {
+  using T = SparseTile<D>;
+#pragma unroll
+  for (int j = 0; j < T::kInstr; ++j) {
+    const int unit = j * kWave + lane;
+    const int r = unit / T::kUnits, phys = unit % T::kUnits;
+    const int uk = phys ^ (r & (T::kUnits - 1));
+    __builtin_amdgcn_global_load_lds(kbase + row(r) + uk * 8, k_lds + j * 1024, 16, 0, 0);
+  }
+#pragma unroll
+  for (int j = 0; j < T::kInstr; ++j) {
+    const int db = j >> 1, r = ((j & 1) << 4) + (lane >> 2);
+    __builtin_amdgcn_global_load_lds(vbase + row(r) + 32 * db + 8 * (lane & 3), v_lds + j * 1024, 16, 0,
+                                     0);
+  }
+}
+
+template <int D, int kStages>
+__global__ __launch_bounds__(kSparseThreads) void sparse_attn_kernel(AttnParams p) {
+  using T = SparseTile<D>;
+  constexpr int kNdb = D / 32, kNks = D / 16;
+  constexpr int kWaveRing = kStages * T::kStageBytes;
+  constexpr int kXchFloats = kWave * (2 + 16 * kNdb);
+  static_assert(kWaveRing >= kXchFloats * 4, "merge area fits in a wave's ring");
+  static_assert(2 * T::kInstr * (kStages - 1) < 64, "vmcnt is 6 bits");
+  __shared__ __attribute__((aligned(1024))) uint8_t s_ring[kSparseWaves * kWaveRing];
+  __shared__ int32_t s_tab[kSparseWaves][kSparseMaxKpw];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hh = lane >> 5, n = lane & 31;
+  const int units = p.S * p.Hkv;
+  const int nrb = (p.R + 31) >> 5;
+  // blockIdx -> (g = unit * nchunk + chunk, row block): same g, ids 8 apart
+  const int x = blockIdx.x & 7, jj = blockIdx.x >> 3;
+  const int rb = jj % nrb;
+  const int g = (jj / nrb) * 8 + x;
+  if (g >= units * p.nchunk) return;
+  MAGE_TRACE_POINT(0);
+  const int u = g / p.nchunk, c = g - u * p.nchunk;
+  const int s = u / p.Hkv, h = u - s * p.Hkv;
+  const int ns = seq_len_of(p.kv, p.lens, s);
+  const int kpw = p.chunk / kSparseWaves;
+  const int e0 = c * p.chunk + w * kpw;                 // this wave's entries [e0, e1)
+  const int e1 = min(e0 + kpw, p.idx_k);
+  const int cnt = max(0, e1 - e0);
+  const bool paged = p.kv.page_table != nullptr;
+  const int pshift = p.kv.page_shift, pmask = (1 << p.kv.page_shift) - 1;
+  const int64_t seq_base = paged ? 0 : (static_cast<int64_t>(s) * p.Hkv + h) * p.kv.n_uniform;
+  const int32_t* ptab = paged ? p.kv.page_table + static_cast<int64_t>(s) * p.kv.max_pages : nullptr;
+
+  // Q fragments of this row block (MFMA B operand; d slice 16ks + 8hh .. +7)
+  bf16x8 qf[kNks];
+  {
+    const int r = 32 * rb + n;
+    if (r < p.R) {
+      const int b = r / p.G, gg = r - b * p.G;
+      const uint16_t* qrow = p.q + ((static_cast<int64_t>(s) * p.B + b) * p.Hq + h * p.G + gg) * D;
+#pragma unroll
+      for (int ks = 0; ks < kNks; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, load16(qrow + 16 * ks + 8 * hh));
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < kNks; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
+    }
+  }
+  // this wave's row table (wave-private LDS; -1 = entry skipped). Four entries
+  // per lane and round: all index loads, then all page-table loads, are in
+  // flight together (loads from clamped, always valid addresses).
+  int32_t* tab = s_tab[w];
+  const int32_t* idx_w = p.idx + static_cast<int64_t>(u) * p.idx_k + e0;
+  for (int i0 = 0; i0 < cnt; i0 += 4 * kWave) {
+    int pos[4], page[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) pos[j] = idx_w[min(i0 + j * kWave + lane, cnt - 1)];
+    if (paged) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) page[j] = ptab[min(max(pos[j], 0), ns - 1) >> pshift];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = i0 + j * kWave + lane;
+      const int ps = pos[j];
+      int row = -1;
+      if (ps >= 0 && ps < ns)
+        row = paged ? ((page[j] * p.Hkv + h) << pshift) + (ps & pmask) : static_cast<int>(seq_base + ps);
+      if (i < cnt) tab[i] = row;
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);   // row table written and Q fragments in registers
+  __builtin_amdgcn_wave_barrier();
+  MAGE_TRACE_POINT(1);
+
+  uint8_t* ring = s_ring + w * kWaveRing;
+  const uint32_t ring_base = lds_addr(ring);
+  const int ntiles = (cnt + kSparseTileKeys - 1) / kSparseTileKeys;
+  auto issue = [&](int t) {
+    uint8_t* st = ring + (t % kStages) * T::kStageBytes;
+    const int base = t * kSparseTileKeys;
+    issue_sparse_tile<D>(st, st + T::kKBytes, p.kv.k, p.kv.v,
+                         [&](int r) {
+                           const int row = tab[min(base + r, cnt - 1)];
+                           return static_cast<int64_t>(row < 0 ? 0 : row) * D;
+                         },
+                         lane);
+  };
+  f32x16 oacc[kNdb];
+#pragma unroll
+  for (int db = 0; db < kNdb; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
+  float m_run = -__builtin_inff(), l_run = 0.f;
+  uint32_t kofs[kNks];
+  k_frag_offsets<D>(swap_bits23(n), hh, kofs);
+  const uint32_t v_lane = T::kKBytes + vt_lane_offset(lane);
+#pragma unroll
+  for (int t = 0; t < kStages - 1; ++t)
+    if (t < ntiles) issue(t);
+  for (int t = 0; t < ntiles; ++t) {
+    if (t + kStages - 1 < ntiles) {
+      issue(t + kStages - 1);   // refills the stage of tile t-1, whose reads are complete
+      wait_tiles<2 * T::kInstr, kStages>(kStages - 1);
+    } else {
+      wait_tiles<2 * T::kInstr, kStages>(min(kStages - 1, ntiles - 1 - t));
+    }
+    if (t == 0) MAGE_TRACE_POINT(2);
+    const int e = t * kSparseTileKeys + n;
+    const uint32_t okm = static_cast<uint32_t>(__ballot(e < cnt && tab[min(e, cnt - 1)] >= 0));
+    const uint32_t st = ring_base + (t % kStages) * T::kStageBytes;
+    attend_half<D, T::kVBlock>(st, st + v_lane, kofs, qf, okm, p.scale_log2, m_run, l_run, oacc, lane);
+  }
+
+  l_run = wave_sum_pair(l_run);
+  MAGE_TRACE_POINT(3);
+  // ---- merge the four waves through LDS ---------------------------------------
+  float* xch = reinterpret_cast<float*>(ring);   // this wave's ring is free now
+  xch[lane] = m_run;
+  xch[kWave + lane] = l_run;
+#pragma unroll
+  for (int db = 0; db < kNdb; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) xch[(2 + 16 * db + i) * kWave + lane] = oacc[db][i];
+  __syncthreads();
+  MAGE_TRACE_POINT(4);
+  if (w >= kNdb) return;
+  const int db = w;   // this wave merges d block db of all four waves
+  float mj[kSparseWaves], M = -__builtin_inff();
+#pragma unroll
+  for (int j = 0; j < kSparseWaves; ++j) {
+    mj[j] = reinterpret_cast<const float*>(s_ring + j * kWaveRing)[lane];
+    M = fmaxf(M, mj[j]);
+  }
+  const float Mu = M == -__builtin_inff() ? 0.f : M;
+  float L = 0.f;
+  f32x16 acc;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+#pragma unroll
+  for (int j = 0; j < kSparseWaves; ++j) {
+    const float* xj = reinterpret_cast<const float*>(s_ring + j * kWaveRing);
+    const float a = fast_exp2(mj[j] - Mu);
+    L += xj[kWave + lane] * a;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] += xj[(2 + 16 * db + i) * kWave + lane] * a;
+  }
+  const int r = 32 * rb + n;
+  if (p.nchunk == 1) {
+    if (r >= p.R) return;
+    const int b = r / p.G, gg = r - b * p.G, j = h * p.G + gg;
+    const int64_t row = (static_cast<int64_t>(s) * p.B + b) * p.Hq + j;
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    float* orow = p.o + row * D + 32 * db + 4 * hh;
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4)
+      *reinterpret_cast<f32x4*>(orow + 8 * i4) =
+          f32x4{acc[4 * i4] * inv, acc[4 * i4 + 1] * inv, acc[4 * i4 + 2] * inv, acc[4 * i4 + 3] * inv};
+    if (db == 0 && hh == 0 && p.lse != nullptr)
+      p.lse[row] = L > 0.f ? (M + __log2f(L)) * kLn2 : -__builtin_inff();
+    return;
+  }
+  const int64_t slot = static_cast<int64_t>(u) * p.nchunk + c;
+#pragma unroll
+  for (int i4 = 0; i4 < 4; ++i4)
+    *reinterpret_cast<f32x4*>(p.part_o + 4 * part_o_index<D>(slot, rb, db, i4, lane)) =
+        f32x4{acc[4 * i4], acc[4 * i4 + 1], acc[4 * i4 + 2], acc[4 * i4 + 3]};
+  if (db == 0 && hh == 0) {
+    p.part_ml[(slot * kMaxRows + r) * 2 + 0] = M;
+    p.part_ml[(slot * kMaxRows + r) * 2 + 1] = L;
+  }
+  MAGE_TRACE_POINT(5);
 }
 
 // Merge of split partials (exact pass: chunks of the prefix; sparse pass:

@@ -145,27 +145,43 @@ int exact_chunk(int64_t units, int64_t max_n, int64_t total_keys, int page_size)
   return static_cast<int>(c);
 }
 
-// Sparse step: at most kSparseMaxChunks chunks per (seq, KV head), aiming at
-// one work-group per CU.
+// Sparse step: work-group = (unit, 32-row block, chunk of the index list);
+// chunks are multiples of 4 waves x 32 keys. With enough (unit, row block)
+// pairs to fill the chip the index list is not split (one kernel, no merge);
+// otherwise it is split into up to kSparseMaxChunks chunks aiming at one
+// work-group per CU.
 constexpr int kSparseMaxChunks = 32;
 constexpr int kCus = 256;
+constexpr int kSparseChunkUnit = kSparseWaves * kSparseTileKeys;        // 128
+constexpr int kSparseMaxChunk = kSparseWaves * kSparseMaxKpw;           // 4096
 
-// k <= kSparseMaxChunks * kMaxSparseChunk (checked by the entry points).
-int sparse_chunk(int64_t units, int k) {
-  const int min_chunk = static_cast<int>(round_up(cdiv(k, kSparseMaxChunks), 64));
+int sparse_chunk(int64_t units, int nrb, int k) {
+  const int min_chunk =
+      static_cast<int>(round_up(cdiv(k, kSparseMaxChunks), kSparseChunkUnit));   // <= 4096 for valid k
   const int forced = env_int("MAGE_SPARSE_CHUNK", 0);
-  if (forced > 0) return std::min(kMaxSparseChunk, std::max<int>(static_cast<int>(round_up(forced, 64)), min_chunk));
-  const int64_t want = std::min<int64_t>(kSparseMaxChunks, std::max<int64_t>(1, cdiv(kCus, units)));
-  return std::min(kMaxSparseChunk, std::max(min_chunk, static_cast<int>(round_up(cdiv(k, want), 64))));
+  int c;
+  if (forced > 0) {
+    c = static_cast<int>(round_up(forced, kSparseChunkUnit));
+  } else if (k <= 2 * kSparseChunkUnit) {
+    // at most two 32-key tiles per wave, both in flight at once: one kernel
+    // beats a split plus a merge launch
+    c = static_cast<int>(round_up(k, kSparseChunkUnit));
+  } else {
+    const int64_t pairs = units * nrb;
+    const int64_t want = pairs >= kCus ? 1 : std::min<int64_t>(kSparseMaxChunks, cdiv(kCus, pairs));
+    c = static_cast<int>(round_up(cdiv(k, want), kSparseChunkUnit));
+  }
+  return std::min(kSparseMaxChunk, std::max(min_chunk, c));
 }
 
 constexpr int kScoreChunk = 2048;
-// LDS ring depth: 3 x 32 KiB of K+V tiles at d = 128, 4 x 16 KiB at d = 64;
+// LDS ring depth: 4 x 32 KiB of K+V tiles at d = 128, 4 x 16 KiB at d = 64;
 // the score sweep streams K only: 4 x 16 KiB / 4 x 8 KiB (two work-groups per CU).
 template <int D>
-constexpr int kStagesFor = D == 128 ? 3 : 4;
+constexpr int kStagesFor = 4;
 template <int D>
 constexpr int kScoreStagesFor = 4;
+constexpr int kSparseStages = 2;
 
 // ---- workspace layout ------------------------------------------------------
 struct Layout {
@@ -177,7 +193,7 @@ Layout make_layout(const Dims& d, int64_t max_n, int64_t k) {
   Layout L{};
   const int64_t U = d.units;
   const int64_t exact_slots = U * cdiv(max_n, exact_chunk_floor(U, max_n));
-  const int64_t sparse_slots = U * std::min<int64_t>(kSparseMaxChunks, cdiv(k, 64));
+  const int64_t sparse_slots = U * std::min<int64_t>(kSparseMaxChunks, cdiv(k, kSparseChunkUnit));
   L.slots = std::max(exact_slots, sparse_slots);
   const int64_t kc = std::min<int64_t>(k, kTopkChunk);
   L.cand_stride = cdiv(max_n, kTopkChunk) * kc;
@@ -297,10 +313,9 @@ mage_status launch_select(const Dims& d, const uint16_t* q, const KvArgs& kv, in
   ap.S = d.S; ap.B = d.B; ap.Hq = d.Hq; ap.Hkv = d.Hkv; ap.G = d.G; ap.R = d.R;
   ap.chunk = chunk;
   ap.nchunk = nch;
-  ap.xcd_group = 0;
   ap.scale_log2 = scale_log2;
   ap.lens = kv.lens;
-  if (mage_status st = launch(kfn(attn_chunk_kernel<D, false, kStagesFor<D>>), "attn_chunk_kernel[exact]",
+  if (mage_status st = launch(kfn(exact_chunk_kernel<D, kStagesFor<D>>), "exact_chunk_kernel",
                               U * nch, kAttnThreads, attn, ap);
       st != MAGE_OK)
     return st;
@@ -375,7 +390,7 @@ mage_status launch_sparse(const Dims& d, const uint16_t* q, const KvArgs& kv, co
                           int32_t k, float* o, float* lse, void* ws, const Layout& L,
                           hipStream_t stream) {
   const int64_t U = d.units;
-  const int chunk = sparse_chunk(U, k);
+  const int chunk = sparse_chunk(U, d.nrb, k);
   const int nch = static_cast<int>(cdiv(k, chunk));
   AttnParams ap{};
   ap.q = q;
@@ -389,12 +404,11 @@ mage_status launch_sparse(const Dims& d, const uint16_t* q, const KvArgs& kv, co
   ap.S = d.S; ap.B = d.B; ap.Hq = d.Hq; ap.Hkv = d.Hkv; ap.G = d.G; ap.R = d.R;
   ap.chunk = chunk;
   ap.nchunk = nch;
-  ap.xcd_group = env_int("MAGE_SPARSE_XCD", 0) && nch > 1;
   ap.scale_log2 = d.scale * kLog2e;
   ap.lens = kv.lens;
-  const int64_t grid = ap.xcd_group ? round_up(U, 8) * nch : U * nch;
-  if (mage_status st = launch(kfn(attn_chunk_kernel<D, true, kStagesFor<D>>), "attn_chunk_kernel[sparse]",
-                              grid, kAttnThreads, stream, ap);
+  const int64_t grid = round_up(U * nch, 8) * d.nrb;
+  if (mage_status st = launch(kfn(sparse_attn_kernel<D, kSparseStages>), "sparse_attn_kernel", grid,
+                              kSparseThreads, stream, ap);
       st != MAGE_OK)
     return st;
   if (nch == 1) return MAGE_OK;  // the single chunk wrote O and lse
@@ -539,7 +553,7 @@ static mage_status sparse_common(const mage_dims* dims, const uint16_t* q, const
   if (!aligned(idx, 4) || (lse && !aligned(lse, 4)))
     return fail(MAGE_ERR_INVALID_ARG, "idx and lse must be 4-byte aligned");
   if (k < 1) return fail(MAGE_ERR_INVALID_ARG, "k must be >= 1");
-  static_assert(MAGE_MAX_SPARSE_K <= kSparseMaxChunks * kMaxSparseChunk, "sparse plan limit");
+  static_assert(MAGE_MAX_SPARSE_K <= kSparseMaxChunks * kSparseMaxChunk, "sparse plan limit");
   if (k > MAGE_MAX_SPARSE_K)
     return fail(MAGE_ERR_UNSUPPORTED, "sparse steps take k <= MAGE_MAX_SPARSE_K index entries");
   return MAGE_OK;

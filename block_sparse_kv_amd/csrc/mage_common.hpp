@@ -53,12 +53,19 @@ __device__ __forceinline__ int seq_len_of(const KvSource& kv, const SeqLens& len
   return kv.page_table ? lens.n[s] : kv.n_uniform;
 }
 
+// Lanes l and l ^ 32 hold the two halves of one row. v_permlane32_swap
+// exchanges the upper half of one register with the lower half of another;
+// with both operands = x, the two results hold x and x[l ^ 32] in every lane
+// (in either order), so a symmetric combination of them is the pair result.
 __device__ __forceinline__ float wave_max_pair(float x) {
-  // lanes l and l ^ 32 hold the two halves of one row
-  return fmaxf(x, __shfl_xor(x, 32));
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-__device__ __forceinline__ float wave_sum_pair(float x) { return x + __shfl_xor(x, 32); }
+__device__ __forceinline__ float wave_sum_pair(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

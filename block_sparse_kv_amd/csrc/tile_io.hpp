@@ -185,13 +185,13 @@ __device__ __forceinline__ void vt_frags(uint32_t vaddr, bf16x8 (&frag)[4]) {
 
 // All V^T fragments of one 32-key half tile: frag[db][s] holds in lane l the
 // values V[32h + 16s + 8*(l/32) + j][32*db + (l%32)], j = 0..7 (vaddr includes
-// the half's 2048-byte offset and the lane's transpose-read offset). One asm
-// block, one wait, 4 * D/32 transpose reads.
-template <int D>
+// the half's offset and the lane's transpose-read offset). One asm block, one
+// wait, 4 * D/32 transpose reads. kB is the byte stride of one 32-value d
+// block: 64 rows x 64 bytes in a 64-key tile, 32 x 64 in a 32-key tile.
+template <int D, int kB = kTileKeys * 64>
 __device__ __forceinline__ void vt_frags_half(uint32_t vaddr, bf16x8 (&frag)[D / 32][2]) {
   typedef short s4 __attribute__((ext_vector_type(4)));
   typedef short s8 __attribute__((ext_vector_type(8)));
-  constexpr int kB = kTileKeys * 64;  // one d block
   if constexpr (D == 128) {
     s4 r[16];
     asm volatile(

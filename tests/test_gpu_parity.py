@@ -255,7 +255,7 @@ def test_kernel_timers_time_each_launch():
     o, _ = gpu_sparse(inp, d, d["q"][0], idx)
     names = mage.last_launches()
     torch.cuda.synchronize()
-    assert names[0] == "attn_chunk_kernel[sparse]"
+    assert names[0] == "sparse_attn_kernel"
     assert set(names[1:]) <= {"exact_merge_kernel[sparse]"}
     ms = [a.elapsed_time(b) for a, b in pairs[:len(names)]]
     assert all(0 < t < 100 for t in ms)
@@ -267,7 +267,7 @@ def test_kernel_timers_time_each_launch():
     gpu_select(inp, d)
     names = mage.last_launches()
     torch.cuda.synchronize()
-    assert names[:3] == ["attn_chunk_kernel[exact]", "exact_merge_kernel[exact]", "score_kernel"]
+    assert names[:3] == ["exact_chunk_kernel", "exact_merge_kernel[exact]", "score_kernel"]
     assert names[3] == "topk_local_kernel"
     span = pairs[0][0].elapsed_time(pairs[len(names) - 1][1])
     assert span >= max(a.elapsed_time(b) for a, b in pairs[:len(names)]) > 0
