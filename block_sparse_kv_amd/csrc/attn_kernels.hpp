@@ -199,17 +199,6 @@ __device__ __forceinline__ void attend_half(uint32_t k_base, uint32_t v_addr,
   pv_half<D, kVB>(v_addr, phi, plo, oacc);
 }
 
-// Scheduling shape of the QK product of one tile (8 MFMAs at d = 128)
-// interleaved with the softmax of the previous one (about 120 vector
-// instructions): one MFMA, then a run of vector instructions, eight times.
-__device__ __forceinline__ void interleave_qk_softmax() {
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x002, 14, 0);  // VALU
-  }
-}
-
 // Exact pass (step 1): one work-group per (unit, chunk of the prefix).
 // 8 waves: wave w takes row block w % 4 and key half w / 4 (keys 32h..32h+31
 // of every 64-key tile); the two waves of a row block merge at the end.
@@ -247,7 +236,10 @@ __global__ __launch_bounds__(kAttnThreads) void exact_chunk_kernel(AttnParams p)
   const int64_t seq_base = paged ? 0 : (static_cast<int64_t>(s) * p.Hkv + h) * p.kv.n_uniform;
   const int32_t* ptab = paged ? p.kv.page_table + static_cast<int64_t>(s) * p.kv.max_pages : nullptr;
   const int cnt = e1 - e0;
-  const int page0 = e0 >> pshift;
+  // the last tile of the chunk is read as the 64 rows ending at e1 when it is
+  // partial (shifted back into the prefix), so the page list starts 64 rows
+  // before the chunk
+  const int page0 = max(e0 - kTileKeys, 0) >> pshift;
   if (paged) {
     const int np = ((e1 - 1) >> pshift) - page0 + 1;
     for (int i = tid; i < np; i += kAttnThreads) s_pages[i] = ptab[page0 + i];
@@ -268,7 +260,10 @@ __global__ __launch_bounds__(kAttnThreads) void exact_chunk_kernel(AttnParams p)
       for (int ks = 0; ks < kNks; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
     }
   }
-  __syncthreads();  // page table visible, Q loads complete (vmcnt drained)
+  __syncthreads();   // page table visible
+  // Q fragments in registers before any tile load: the tile loads are asm the
+  // compiler does not count, so it must see its own loads complete here
+  wait_vmcnt<0>();
   MAGE_TRACE_POINT(1);
 
   // element offset of the K/V row of prefix position e (clamped into the chunk)
@@ -280,10 +275,28 @@ __global__ __launch_bounds__(kAttnThreads) void exact_chunk_kernel(AttnParams p)
     }
     return (seq_base + pos) * D;
   };
+  // A partial last tile is loaded as the 64 rows ending at e1 when e1 >= 64
+  // (all of them rows of this sequence); its first 64 - (cnt mod 64) keys
+  // belong to the previous tile and are masked. The same keys form the same
+  // tiles in both layouts, so paged and contiguous results are bit-identical.
+  // Prefixes shorter than 64 clamp the rows past e1 and mask them.
+  const int last_t = (cnt - 1) / kTileKeys;
+  const int tail = cnt - last_t * kTileKeys;            // keys in the last tile, 1..64
+  const bool shift_last = tail < kTileKeys && e1 >= kTileKeys;
+  auto tile_base = [&](int t) -> int {
+    return (t == last_t && shift_last) ? e1 - kTileKeys : e0 + t * kTileKeys;
+  };
   // validity bits of this wave's key half of tile t
   auto half_mask = [&](int t) -> uint32_t {
-    const int nv = cnt - t * kTileKeys - 32 * kh;
-    return nv >= 32 ? ~0u : (nv <= 0 ? 0u : ((1u << nv) - 1u));
+    if (t == last_t && tail < kTileKeys) {
+      if (shift_last) {
+        const int lo = kTileKeys - tail - 32 * kh;     // first valid key of the half
+        return lo <= 0 ? ~0u : (lo >= 32 ? 0u : ~((1u << lo) - 1u));
+      }
+      const int nv = tail - 32 * kh;
+      return nv >= 32 ? ~0u : (nv <= 0 ? 0u : ((1u << nv) - 1u));
+    }
+    return ~0u;
   };
 
   f32x16 oacc[kNdb];
@@ -299,11 +312,61 @@ __global__ __launch_bounds__(kAttnThreads) void exact_chunk_kernel(AttnParams p)
   const uint32_t v_half = G::kBytes + kh * 2048 + vt_lane_offset(lane);
 
   const int ntiles = (cnt + kTileKeys - 1) / kTileKeys;
+  // Full tiles: each DMA instruction covers 4 (K) or 16 (V) consecutive rows,
+  // which are contiguous in memory (contiguous layout, or one page when pages
+  // hold >= 16 rows). Its address is then a wave-uniform base (the slice's first
+  // row) plus a per-lane byte offset fixed for the whole loop, so the loop
+  // writes no VGPR that an in-flight load still reads. The last, partial tile
+  // takes the clamped per-lane path.
+  constexpr int kKRowsPerInstr = kWave / G::kUnits;        // 4 at d = 128
+  uint32_t koff[G::kInstr], voff[G::kInstr];
+#pragma unroll
+  for (int j = 0; j < G::kInstr; ++j) {
+    const int slot = w * G::kInstr + j;
+    const int unit = slot * kWave + lane;
+    const int r = unit / G::kUnits, uk = (unit % G::kUnits) ^ (r & (G::kUnits - 1));
+    koff[j] = static_cast<uint32_t>(((r - slot * kKRowsPerInstr) * D + uk * 8) * 2);
+    const int db = slot >> 2, rv = (lane >> 2);
+    voff[j] = static_cast<uint32_t>((rv * D + 32 * db + 8 * (lane & 3)) * 2);
+  }
+  const bool fast_rows = !paged || pshift >= 4;
+  // byte address of the K row of prefix position pos (wave-uniform pos)
+  auto row_bytes = [&](int pos) -> int64_t {
+    if (paged) {
+      const int64_t page = __builtin_amdgcn_readfirstlane(s_pages[(pos >> pshift) - page0]);
+      return ((((page * p.Hkv + h) << pshift) + (pos & pmask)) * D) * 2;
+    }
+    return ((seq_base + pos) * D) * 2;
+  };
+  // All tile loads are asm DMA that the compiler does not track; completion is
+  // accounted for with wait_tiles. Full (or shifted) tiles of contiguous rows
+  // take the uniform-base form; the rest load row by row and wait at once.
   auto issue = [&](int tile) {
     uint8_t* st = s_ring + (tile % kStages) * kStageBytes;
-    const int base = e0 + tile * kTileKeys;
-    issue_tile<D, true, kAttnThreads>(st, st + G::kBytes, p.kv.k, p.kv.v,
-                                      [&](int r) { return row_of(base + r); }, w, lane);
+    const uint32_t st_lds = lds_addr(st);
+    const int base = tile_base(tile);
+    // a shifted tile of a paged cache need not start on a 16-row page boundary
+    if (fast_rows && base + kTileKeys <= e1 && (!paged || (base & 15) == 0)) {
+      const char* kb = reinterpret_cast<const char*>(p.kv.k);
+      const char* vb = reinterpret_cast<const char*>(p.kv.v);
+#pragma unroll
+      for (int j = 0; j < G::kInstr; ++j) {
+        const int slot = w * G::kInstr + j;
+        const int64_t kr = row_bytes(base + slot * kKRowsPerInstr);
+        const int64_t vr = row_bytes(base + ((slot & 3) << 4));
+        dma16x2(kb + kr, koff[j], st_lds + slot * 1024, vb + vr, voff[j], st_lds + G::kBytes + slot * 1024);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < G::kInstr; ++j) {
+        const int slot = w * G::kInstr + j;
+        const int unit = slot * kWave + lane;
+        const int r = unit / G::kUnits, uk = (unit % G::kUnits) ^ (r & (G::kUnits - 1));
+        dma16_sync(p.kv.k + row_of(base + r) + uk * 8, st_lds + slot * 1024);
+        const int db = slot >> 2, rv = ((slot & 3) << 4) + (lane >> 2);
+        dma16_sync(p.kv.v + row_of(base + rv) + 32 * db + 8 * (lane & 3), st_lds + G::kBytes + slot * 1024);
+      }
+    }
   };
 #pragma unroll
   for (int t = 0; t < kStages - 1; ++t)
@@ -316,30 +379,36 @@ __global__ __launch_bounds__(kAttnThreads) void exact_chunk_kernel(AttnParams p)
   // tile t+1 interleaved with the softmax of tile t, then PV of tile t. In the
   // last iteration the QK product re-reads tile t (result unused), which keeps
   // the interleaved region free of branches.
+  [[maybe_unused]] uint64_t trace_acc[4] = {0, 0, 0, 0};
   auto step = [&](int t, auto masked) {
     const bool has_next = t + 1 < ntiles;
+    [[maybe_unused]] const uint64_t tr0 = MAGE_TRACE_NOW();
     if (has_next) {
       // tile t+1 landed for every wave, and every wave is done with tile t-1
       wait_tiles<2 * G::kInstr, kStages - 1>(min(kStages - 3, ntiles - 2 - t));
       wg_barrier();
     }
-    f32x16 s_nxt;
-    if (computes) {
-      const int tn = has_next ? t + 1 : t;
-      s_nxt = qk_half<D>(ring_base + (tn % kStages) * kStageBytes + k_half, kofs, qf);
-    }
+    [[maybe_unused]] const uint64_t tr1 = MAGE_TRACE_NOW();
     if (t + kStages - 1 < ntiles) issue(t + kStages - 1);   // into the stage of tile t-1
     if (computes) {
+      const int tn = has_next ? t + 1 : t;
+      // QK product of tile t+1 first: its MFMAs run under the softmax of tile t
+      const f32x16 s_nxt = qk_half<D>(ring_base + (tn % kStages) * kStageBytes + k_half, kofs, qf);
+      [[maybe_unused]] const uint64_t tr2 = MAGE_TRACE_NOW();
       bf16x8 phi[2], plo[2];
       float alpha;
       bool grow;
       softmax_half<decltype(masked)::value>(s_cur, half_mask(t), p.scale_log2, m_run, l_run, alpha,
                                             grow, phi, plo, lane);
-      interleave_qk_softmax();
-      __builtin_amdgcn_sched_barrier(0);
+      [[maybe_unused]] const uint64_t tr3 = MAGE_TRACE_NOW();
       rescale_o<D>(grow, alpha, oacc);
       pv_half<D>(ring_base + (t % kStages) * kStageBytes + v_half, phi, plo, oacc);
       s_cur = s_nxt;
+      [[maybe_unused]] const uint64_t tr4 = MAGE_TRACE_NOW();
+      trace_acc[0] += tr1 - tr0;
+      trace_acc[1] += tr2 - tr1;
+      trace_acc[2] += tr3 - tr2;
+      trace_acc[3] += tr4 - tr3;
     }
   };
   for (int t = 0; t + 1 < ntiles; ++t) step(t, std::false_type{});
@@ -348,6 +417,10 @@ __global__ __launch_bounds__(kAttnThreads) void exact_chunk_kernel(AttnParams p)
   else
     step(ntiles - 1, std::false_type{});
   l_run = wave_sum_pair(l_run);
+  MAGE_TRACE_ADD(4, trace_acc[0]);
+  MAGE_TRACE_ADD(5, trace_acc[1]);
+  MAGE_TRACE_ADD(6, trace_acc[2]);
+  MAGE_TRACE_ADD(7, trace_acc[3]);
   __syncthreads();  // the ring is reused below
   MAGE_TRACE_POINT(2);
 
@@ -493,6 +566,9 @@ __global__ __launch_bounds__(kSparseThreads) void sparse_attn_kernel(AttnParams 
       for (int ks = 0; ks < kNks; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
     }
   }
+  // row read for a skipped entry: position 0 of this (sequence, KV head), which
+  // always holds finite data (a pool row outside every sequence may not)
+  const int fallback_row = paged ? ((ptab[0] * p.Hkv + h) << pshift) : static_cast<int>(seq_base);
   // this wave's row table (wave-private LDS; -1 = entry skipped). Four entries
   // per lane and round: all index loads, then all page-table loads, are in
   // flight together (loads from clamped, always valid addresses).
@@ -529,7 +605,7 @@ __global__ __launch_bounds__(kSparseThreads) void sparse_attn_kernel(AttnParams 
     issue_sparse_tile<D>(st, st + T::kKBytes, p.kv.k, p.kv.v,
                          [&](int r) {
                            const int row = tab[min(base + r, cnt - 1)];
-                           return static_cast<int64_t>(row < 0 ? 0 : row) * D;
+                           return static_cast<int64_t>(row < 0 ? fallback_row : row) * D;
                          },
                          lane);
   };

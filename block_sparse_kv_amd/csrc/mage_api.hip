@@ -138,7 +138,8 @@ int exact_chunk(int64_t units, int64_t max_n, int64_t total_keys, int page_size)
   const int forced = env_int("MAGE_EXACT_CHUNK", 0);
   if (forced > 0) c = std::max<int64_t>(round_up(forced, 64), floor);
   if (page_size > 0) {
-    const int64_t cap = ((kMaxChunkPages - 1) * static_cast<int64_t>(page_size)) / 64 * 64;
+    // the chunk's pages plus the pages of the 64 rows before it
+    const int64_t cap = ((kMaxChunkPages - 2 - cdiv(64, page_size)) * static_cast<int64_t>(page_size)) / 64 * 64;
     c = std::min(c, cap);
     if (c < floor || c < 64) return 0;
   }

@@ -101,9 +101,18 @@ __device__ uint64_t g_trace[8192][8];
     if (threadIdx.x == 0 && blockIdx.x < 8192)                               \
       mage::g_trace[blockIdx.x][slot] = __builtin_amdgcn_s_memrealtime();  \
   } while (0)
+#define MAGE_TRACE_NOW() __builtin_amdgcn_s_memrealtime()
+#define MAGE_TRACE_ADD(slot, v)                                             \
+  do {                                                                      \
+    if (threadIdx.x == 0 && blockIdx.x < 8192) mage::g_trace[blockIdx.x][slot] += (v); \
+  } while (0)
 #else
 #define MAGE_TRACE_POINT(slot) \
   do {                         \
+  } while (0)
+#define MAGE_TRACE_NOW() 0ull
+#define MAGE_TRACE_ADD(slot, v) \
+  do {                          \
   } while (0)
 #endif
 

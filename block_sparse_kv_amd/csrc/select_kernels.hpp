@@ -198,7 +198,7 @@ struct TopkParams {
 };
 
 struct TopkShared {
-  uint32_t hist[4096];
+  uint32_t hist[4096 + 256];
   __attribute__((aligned(16))) int32_t wsum[kTopkWaves];
   __attribute__((aligned(16))) int32_t wsum2[kTopkWaves];
   int32_t res[2];
@@ -353,6 +353,142 @@ __device__ void ordered_compact(Get data, int n, uint32_t T, int need, PosOf pos
   }
 }
 
+// ---- register-resident variants -------------------------------------------
+// Thread t holds the contiguous run of elements [t*kPer, t*kPer + kPer) in
+// registers (entries at or past n are invalid). Histograms are per wave
+// (16 waves x 256 bins of 8-bit digits): atomics only meet inside a wave, where
+// scores sharing their top bits would otherwise queue on a few LDS words.
+template <int kPer>
+__device__ __forceinline__ int run_valid(int n) {
+  return max(0, min(kPer, n - static_cast<int>(threadIdx.x) * kPer));
+}
+
+template <int kPer>
+__device__ void radix_select_regs(const uint32_t (&v)[kPer], int n, int kk, TopkShared& sh, uint32_t& T,
+                                  int& need) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int nv = run_valid<kPer>(n);
+  if (tid == 0) sh.res[0] = static_cast<int32_t>(v[0]);
+  __syncthreads();
+  const uint32_t first = static_cast<uint32_t>(sh.res[0]);
+  uint32_t diff = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j)
+    if (j < nv) diff |= v[j] ^ first;
+  diff = block_or(diff, sh.wsum);
+  if (diff == 0) {  // all entries equal
+    T = first;
+    need = kk;
+    return;
+  }
+  int hi = 31 - __clz(diff);
+  uint32_t pmask = hi == 31 ? 0u : ~((2u << hi) - 1u);
+  uint32_t prefix = first & pmask;
+  int rem = kk;
+  uint32_t* hist = sh.hist + wv * 256;          // this wave's histogram
+  uint32_t* total = sh.hist + kTopkWaves * 256;  // bin totals over the waves
+  while (hi >= 0) {
+    const int width = min(8, hi + 1), lo = hi - width + 1, nb = 1 << width;
+#pragma unroll
+    for (int b = lane; b < 256; b += kWave) hist[b] = 0u;
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int j = 0; j < kPer; ++j)
+      if (j < nv && (v[j] & pmask) == prefix) atomicAdd(&hist[(v[j] >> lo) & (nb - 1)], 1u);
+    __syncthreads();
+    // wave w totals bins 16w .. 16w+15 over the 16 wave histograms
+    {
+      const int bin = wv * 16 + (lane & 15), part = lane >> 4;   // 4 lanes per bin, 4 histograms each
+      uint32_t c = 0;
+#pragma unroll
+      for (int q = 0; q < kTopkWaves / 4; ++q) c += sh.hist[(part * (kTopkWaves / 4) + q) * 256 + bin];
+      c += __shfl_xor(c, 16);
+      c += __shfl_xor(c, 32);
+      if (lane < 16) total[bin] = c;
+    }
+    __syncthreads();
+    if (wv == 0) {
+      // lane l holds the 4 bins of digits 4(63-l) .. 4(63-l)+3 (largest digits in lane 0)
+      typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+      const u4 c4 = reinterpret_cast<const u4*>(total)[63 - lane];
+      const int s = static_cast<int>(c4[0] + c4[1] + c4[2] + c4[3]);
+      int incl = s;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(incl, off);
+        if (lane >= off) incl += y;
+      }
+      int above = incl - s;
+      if (above < rem && rem <= incl) {
+        for (int e = 3; e >= 0; --e) {
+          const int c = static_cast<int>(c4[e]);
+          if (above < rem && rem <= above + c) {
+            sh.res[0] = 4 * (63 - lane) + e;
+            sh.res[1] = rem - above;
+          }
+          above += c;
+        }
+      }
+    }
+    __syncthreads();
+    const int digit = sh.res[0];
+    rem = sh.res[1];
+    prefix |= static_cast<uint32_t>(digit) << lo;
+    pmask |= static_cast<uint32_t>(nb - 1) << lo;
+    hi = lo - 1;
+  }
+  T = prefix;
+  need = rem;
+}
+
+// Keep entries > T and the first `need` entries == T, in index order:
+// out_pos[o] = pos_of(j) (and out_bits[o] = value if out_bits).
+template <int kPer, class PosOf>
+__device__ void ordered_compact_regs(const uint32_t (&v)[kPer], int n, uint32_t T, int need, PosOf pos_of,
+                                     uint32_t* out_bits, int32_t* out_pos, TopkShared& sh) {
+  const int nv = run_valid<kPer>(n);
+  int n_eq = 0, n_gt = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j)
+    if (j < nv) {
+      n_eq += v[j] == T;
+      n_gt += v[j] > T;
+    }
+  int eq_total;
+  const int eq_before = block_inclusive_scan(n_eq, sh.wsum, eq_total) - n_eq;
+  const int keep_eq = max(0, min(n_eq, need - eq_before));
+  const int n_sel = keep_eq + n_gt;
+  int sel_total;
+  int o = block_inclusive_scan(n_sel, sh.wsum2, sel_total) - n_sel;
+  int eq_seen = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    if (j >= nv) break;
+    bool sel = v[j] > T;
+    if (v[j] == T) sel = eq_seen++ < keep_eq;
+    if (sel) {
+      out_pos[o] = pos_of(j);
+      if (out_bits) out_bits[o] = v[j];
+      ++o;
+    }
+  }
+}
+
+// Read thread t's run [t*kPer, t*kPer + kPer) of an LDS array (16-byte reads).
+template <int kPer>
+__device__ __forceinline__ void load_run(const uint32_t* lds, uint32_t (&v)[kPer]) {
+  static_assert(kPer % 4 == 0, "runs of whole 16-byte words");
+  const u32x4* src = reinterpret_cast<const u32x4*>(lds + threadIdx.x * kPer);
+#pragma unroll
+  for (int q = 0; q < kPer / 4; ++q) {
+    const u32x4 x = src[q];
+    v[4 * q] = x[0];
+    v[4 * q + 1] = x[1];
+    v[4 * q + 2] = x[2];
+    v[4 * q + 3] = x[3];
+  }
+}
+
 // Pass 1: one work-group per (row, chunk of kTopkChunk positions). A row that
 // fits in one chunk is finished here; otherwise the chunk's top min(k, len)
 // entries (under the same order) go to the candidate buffer in position order.
@@ -393,15 +529,18 @@ __global__ __launch_bounds__(kTopkThreads) void topk_local_kernel(TopkParams p) 
     for (int j = 0; j < kPer; ++j) s_data[tid + j * kTopkThreads] = v[j];
   }
   __syncthreads();
+  constexpr int kPer = kTopkChunk / kTopkThreads;
+  uint32_t v[kPer];
+  load_run<kPer>(s_data, v);
   MAGE_TRACE_POINT(1);
-  auto get = [&](int i) { return s_data[i]; };
+  const int run0 = start + tid * kPer;
   if (nch == 1) {
     // a single chunk: its winners are the answer
     uint32_t T;
     int need;
-    radix_select(get, len, kk, sh, T, need);
+    radix_select_regs<kPer>(v, len, kk, sh, T, need);
     MAGE_TRACE_POINT(2);
-    ordered_compact(get, len, T, need, [&](int i) { return start + i; }, nullptr, out, sh);
+    ordered_compact_regs<kPer>(v, len, T, need, [&](int j) { return run0 + j; }, nullptr, out, sh);
     for (int i = kk + tid; i < p.k; i += kTopkThreads) out[i] = -1;
     MAGE_TRACE_POINT(3);
     return;
@@ -414,9 +553,9 @@ __global__ __launch_bounds__(kTopkThreads) void topk_local_kernel(TopkParams p) 
   } else {
     uint32_t T;
     int need;
-    radix_select(get, len, kc, sh, T, need);
+    radix_select_regs<kPer>(v, len, kc, sh, T, need);
     MAGE_TRACE_POINT(2);
-    ordered_compact(get, len, T, need, [&](int i) { return start + i; }, cb, cp, sh);
+    ordered_compact_regs<kPer>(v, len, T, need, [&](int j) { return run0 + j; }, cb, cp, sh);
   }
   MAGE_TRACE_POINT(3);
 }
@@ -443,28 +582,32 @@ __global__ __launch_bounds__(kTopkThreads) void topk_final_kernel(TopkParams p) 
   uint32_t T;
   int need;
   if (total <= kTopkChunk / 2) {
-    // winners (bits, positions) fit in LDS: one batched pass from L2, then LDS only
+    // winners (bits, positions) fit in LDS: one batched pass from L2, then registers
     constexpr int kPer = kTopkChunk / 2 / kTopkThreads;
-    uint32_t vb[kPer];
-    int32_t vp[kPer];
+    {
+      uint32_t vb[kPer];
+      int32_t vp[kPer];
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int i = min(tid + j * kTopkThreads, total - 1);  // clamped; entries past total are never read
-      vb[j] = all_bits[i];
-      vp[j] = all_pos[i];
-    }
+      for (int j = 0; j < kPer; ++j) {
+        const int i = min(tid + j * kTopkThreads, total - 1);  // clamped; entries past total are never used
+        vb[j] = all_bits[i];
+        vp[j] = all_pos[i];
+      }
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      s_data[tid + j * kTopkThreads] = vb[j];
-      s_data[kTopkChunk / 2 + tid + j * kTopkThreads] = static_cast<uint32_t>(vp[j]);
+      for (int j = 0; j < kPer; ++j) {
+        s_data[tid + j * kTopkThreads] = vb[j];
+        s_data[kTopkChunk / 2 + tid + j * kTopkThreads] = static_cast<uint32_t>(vp[j]);
+      }
     }
     __syncthreads();
+    uint32_t v[kPer], vpos[kPer];
+    load_run<kPer>(s_data, v);
+    load_run<kPer>(s_data + kTopkChunk / 2, vpos);
     MAGE_TRACE_POINT(5);
-    auto get = [&](int i) { return s_data[i]; };
-    radix_select(get, total, kk, sh, T, need);
+    radix_select_regs<kPer>(v, total, kk, sh, T, need);
     MAGE_TRACE_POINT(6);
-    ordered_compact(get, total, T, need, [&](int i) { return static_cast<int32_t>(s_data[kTopkChunk / 2 + i]); },
-                    nullptr, out, sh);
+    ordered_compact_regs<kPer>(v, total, T, need, [&](int j) { return static_cast<int32_t>(vpos[j]); }, nullptr,
+                               out, sh);
   } else {
     auto get = [&](int i) { return all_bits[i]; };
     radix_select(get, total, kk, sh, T, need);

@@ -72,6 +72,42 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
       reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)(p)));
 }
 
+// Direct LDS loads with a wave-uniform 64-bit base (SGPR pair) and a per-lane
+// 32-bit byte offset: lane i's 16 bytes at base + off_i land at LDS address
+// lds + 16 i. Written as one asm block so that the VGPR offsets stay the
+// loop-invariant registers the caller keeps them in, and M0 (the LDS base
+// register of the instruction) is set inside the block; the s_nop covers the
+// wait state between an M0 write and its use. Completion is tracked with
+// vmcnt by the caller (wait_vmcnt / wait_tiles). Nothing is returned in a
+// register, so nothing is live while the loads are in flight.
+__device__ __forceinline__ void dma16x2(const void* b0, uint32_t o0, uint32_t l0, const void* b1, uint32_t o1,
+                                        uint32_t l1) {
+  asm volatile(
+      "s_mov_b32 m0, %4\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %1\n\t"
+      "s_mov_b32 m0, %5\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, %3"
+      :
+      : "v"(o0), "s"(b0), "v"(o1), "s"(b1), "s"(l0), "s"(l1)
+      : "memory", "m0");
+}
+
+// One direct LDS load per lane from a per-lane 64-bit address, waited for in
+// the same asm block (the path for tiles whose rows are not contiguous in
+// memory; the wait frees the address registers before the block ends).
+__device__ __forceinline__ void dma16_sync(const void* addr, uint32_t lds) {
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, off\n\t"
+      "s_waitcnt vmcnt(0)"
+      :
+      : "v"(addr), "s"(lds)
+      : "memory", "m0");
+}
+
 // Issue the DMA loads of one tile. row_off(r) returns the element offset of
 // tile row r (0..63) in the K/V arrays; it must always name a readable row.
 template <int D, bool kWithV, int kNT = kThreads, class RowOff>

@@ -100,6 +100,13 @@ SMALL = [
     workloads.custom((20000,), 32, 8, 128, 32, 1024, name="two_topk_chunks"),
     workloads.custom((53, 200, 1000), 8, 2, 64, 4, 64, paged=True, name="paged_ragged"),
     workloads.custom((17, 4096, 900), 32, 8, 128, 32, 512, paged=True, name="paged_r128"),
+    # tile and chunk edges: exact pass tails of 63/64/65 keys, shifted last tiles,
+    # chunk boundaries inside pages, pages smaller than and larger than a tile
+    workloads.custom((64,), 8, 2, 64, 16, 32, name="n64"),
+    workloads.custom((65,), 8, 2, 128, 16, 32, name="n65"),
+    workloads.custom((63, 64, 65, 129, 577), 8, 2, 128, 16, 64, paged=True, name="paged_edges"),
+    workloads.custom((100, 1000), 8, 2, 128, 16, 64, paged=True, page_size=4, name="paged_p4"),
+    workloads.custom((100, 3000), 8, 2, 128, 16, 64, paged=True, page_size=256, name="paged_p256"),
 ]
 
 
