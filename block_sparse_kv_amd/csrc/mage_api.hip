@@ -117,10 +117,14 @@ int env_int(const char* name, int dflt) {
 }
 
 // ---- launch plan ----------------------------------------------------------
-// Exact pass: split each (seq, KV head) prefix into chunks of `chunk` keys so
-// that about kExactTargetWgs work-groups are busy; never below the floor that
-// bounds the partial-result workspace.
-constexpr int kExactTargetWgs = 512;
+// Exact pass: split each (seq, KV head) prefix into chunks of `chunk` keys.
+// One work-group fills a CU (LDS ring), so the chunk is chosen to make the
+// work-group count whole rounds of kCus with at most kExactRoundKeys keys per
+// work-group: one round of 4096-key chunks for 8 x 128K keys, about four rounds
+// for the ragged 8-sequence batch. Never below the floor that bounds the
+// partial-result workspace.
+constexpr int kCus = 256;
+constexpr int64_t kExactRoundKeys = 4096;
 constexpr int kExactMinChunk = 512;
 constexpr int kExactSlotBudget = 4096;
 
@@ -132,7 +136,8 @@ int exact_chunk_floor(int64_t units, int64_t max_n) {
 // Returns 0 when no chunk size satisfies both the workspace floor and the
 // per-work-group page table limit (paged layout with tiny pages).
 int exact_chunk(int64_t units, int64_t max_n, int64_t total_keys, int page_size) {
-  int64_t c = round_up(cdiv(total_keys, env_int("MAGE_EXACT_WGS", kExactTargetWgs)), 64);
+  const int64_t rounds = std::max<int64_t>(1, cdiv(total_keys, kCus * kExactRoundKeys));
+  int64_t c = round_up(cdiv(total_keys, env_int("MAGE_EXACT_WGS", static_cast<int>(kCus * rounds))), 64);
   const int64_t floor = exact_chunk_floor(units, max_n);
   c = std::max<int64_t>(c, floor);
   const int forced = env_int("MAGE_EXACT_CHUNK", 0);
@@ -152,7 +157,6 @@ int exact_chunk(int64_t units, int64_t max_n, int64_t total_keys, int page_size)
 // otherwise it is split into up to kSparseMaxChunks chunks aiming at one
 // work-group per CU.
 constexpr int kSparseMaxChunks = 32;
-constexpr int kCus = 256;
 constexpr int kSparseChunkUnit = kSparseWaves * kSparseTileKeys;        // 128
 constexpr int kSparseMaxChunk = kSparseWaves * kSparseMaxKpw;           // 4096
 
