@@ -201,7 +201,7 @@ struct TopkShared {
   uint32_t hist[4096 + 256];
   __attribute__((aligned(16))) int32_t wsum[kTopkWaves];
   __attribute__((aligned(16))) int32_t wsum2[kTopkWaves];
-  int32_t res[2];
+  int32_t res[3];
 };
 
 // Sum of the 16 per-wave values in w[] (vector LDS reads, broadcast to all
@@ -363,9 +363,11 @@ __device__ __forceinline__ int run_valid(int n) {
   return max(0, min(kPer, n - static_cast<int>(threadIdx.x) * kPer));
 }
 
+// eq_total (optional) receives the number of entries equal to T: the count of
+// the bin chosen in the last pass, which holds exactly the entries equal to T.
 template <int kPer>
 __device__ void radix_select_regs(const uint32_t (&v)[kPer], int n, int kk, TopkShared& sh, uint32_t& T,
-                                  int& need) {
+                                  int& need, int* eq_total = nullptr) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int nv = run_valid<kPer>(n);
   if (tid == 0) sh.res[0] = static_cast<int32_t>(v[0]);
@@ -379,12 +381,13 @@ __device__ void radix_select_regs(const uint32_t (&v)[kPer], int n, int kk, Topk
   if (diff == 0) {  // all entries equal
     T = first;
     need = kk;
+    if (eq_total) *eq_total = n;
     return;
   }
   int hi = 31 - __clz(diff);
   uint32_t pmask = hi == 31 ? 0u : ~((2u << hi) - 1u);
   uint32_t prefix = first & pmask;
-  int rem = kk;
+  int rem = kk, bin_count = 0;
   uint32_t* hist = sh.hist + wv * 256;          // this wave's histogram
   uint32_t* total = sh.hist + kTopkWaves * 256;  // bin totals over the waves
   while (hi >= 0) {
@@ -425,6 +428,7 @@ __device__ void radix_select_regs(const uint32_t (&v)[kPer], int n, int kk, Topk
           if (above < rem && rem <= above + c) {
             sh.res[0] = 4 * (63 - lane) + e;
             sh.res[1] = rem - above;
+            sh.res[2] = c;
           }
           above += c;
         }
@@ -433,19 +437,124 @@ __device__ void radix_select_regs(const uint32_t (&v)[kPer], int n, int kk, Topk
     __syncthreads();
     const int digit = sh.res[0];
     rem = sh.res[1];
+    bin_count = sh.res[2];
     prefix |= static_cast<uint32_t>(digit) << lo;
     pmask |= static_cast<uint32_t>(nb - 1) << lo;
     hi = lo - 1;
   }
   T = prefix;
   need = rem;
+  if (eq_total) *eq_total = bin_count;
+  __syncthreads();   // res is rewritten by the next select
+}
+
+// The same (T, need) as radix_select_regs, with less work when the k-th value
+// sits in a sparse part of the distribution (the usual case for top-k of a
+// softmax average): the first 8-bit digit is histogrammed over a sample (each
+// thread's first element), a window of digits around the sample's k-th value
+// is chosen with a margin, one packed block scan gives the exact numbers of
+// entries above (A) and inside (M) the window, the window's entries are
+// compacted to `cand` (LDS, kCand entries), and the remaining digits are
+// selected among them (the kk-th largest overall is the (kk - A)-th largest
+// candidate, and every entry equal to it is a candidate). When the window
+// misses the k-th value or holds more than kCand entries, the full select runs.
+constexpr int kCand = 2 * kTopkThreads;
+
+template <int kPer>
+__device__ void radix_select_sampled(const uint32_t (&v)[kPer], int n, int kk, TopkShared& sh, uint32_t* cand,
+                                     uint32_t& T, int& need, int& eq_total) {
+  eq_total = -1;   // unknown unless the candidate path computes it
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int nv = run_valid<kPer>(n);
+  if (tid == 0) sh.res[0] = static_cast<int32_t>(v[0]);
+  __syncthreads();
+  const uint32_t first = static_cast<uint32_t>(sh.res[0]);
+  uint32_t diff = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j)
+    if (j < nv) diff |= v[j] ^ first;
+  diff = block_or(diff, sh.wsum);
+  if (diff == 0) {  // all entries equal
+    T = first;
+    need = kk;
+    return;
+  }
+  const int hi = 31 - __clz(diff);
+  const int width = min(8, hi + 1), lo = hi - width + 1, nb = 1 << width;
+  uint32_t* total = sh.hist + kTopkWaves * 256;
+  if (tid < 256) total[tid] = 0u;
+  if (tid == 0) {
+    sh.res[0] = nb - 1;  // defaults: window from the top digit ...
+    sh.res[1] = 0;       // ... down to the bottom one
+  }
+  __syncthreads();
+  const int m = min(kTopkThreads, (n + kPer - 1) / kPer);  // threads holding data = sample size
+  if (nv > 0) atomicAdd(&total[(v[0] >> lo) & (nb - 1)], 1u);
+  __syncthreads();
+  if (wv == 0) {
+    // lane l holds digits 4(63-l)+3 .. 4(63-l) (largest digits in lane 0)
+    typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+    const u4 c4 = reinterpret_cast<const u4*>(total)[63 - lane];
+    const int s4 = static_cast<int>(c4[0] + c4[1] + c4[2] + c4[3]);
+    int incl = s4;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off);
+      if (lane >= off) incl += y;
+    }
+    // sample counts at the k-th value: kk * m / n; window edges a quarter + 4 away
+    const float tk = static_cast<float>(kk) * static_cast<float>(m) / static_cast<float>(n);
+    const float t_hi = 0.75f * tk - 4.f, t_lo = 1.25f * tk + 4.f;
+    int above = incl - s4;
+    for (int e = 3; e >= 0; --e) {
+      const int c = static_cast<int>(c4[e]);
+      const int d = 4 * (63 - lane) + e;
+      // the digit at which the count of samples >= digit first exceeds the edge
+      if (static_cast<float>(above) <= t_hi && static_cast<float>(above + c) > t_hi) sh.res[0] = d;
+      if (static_cast<float>(above) <= t_lo && static_cast<float>(above + c) > t_lo) sh.res[1] = d;
+      above += c;
+    }
+  }
+  __syncthreads();
+  const int d_hi = sh.res[0], d_lo = sh.res[1];
+  // exact counts above and inside the window, packed (both totals < 2^16)
+  int a_loc = 0, m_loc = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j)
+    if (j < nv) {
+      const int d = static_cast<int>((v[j] >> lo) & (nb - 1));
+      a_loc += d > d_hi;
+      m_loc += (d >= d_lo && d <= d_hi);
+    }
+  const int packed = (a_loc << 16) | m_loc;
+  int tot;
+  const int incl = block_inclusive_scan(packed, sh.wsum, tot);
+  const int A = tot >> 16, M = tot & 0xffff;
+  if (!(A < kk && kk <= A + M) || M > kCand) {
+    radix_select_regs<kPer>(v, n, kk, sh, T, need, &eq_total);
+    return;
+  }
+  int o = (incl - packed) & 0xffff;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j)
+    if (j < nv) {
+      const int d = static_cast<int>((v[j] >> lo) & (nb - 1));
+      if (d >= d_lo && d <= d_hi) cand[o++] = v[j];
+    }
+  __syncthreads();
+  uint32_t c2[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) c2[q] = cand[min(2 * tid + q, M - 1)];
+  radix_select_regs<2>(c2, M, kk - A, sh, T, need, &eq_total);
 }
 
 // Keep entries > T and the first `need` entries == T, in index order:
 // out_pos[o] = pos_of(j) (and out_bits[o] = value if out_bits).
+// eq_total: the number of entries equal to T if known (>= 0); when it equals
+// need, every such entry is kept and the scan of tie ranks is skipped.
 template <int kPer, class PosOf>
 __device__ void ordered_compact_regs(const uint32_t (&v)[kPer], int n, uint32_t T, int need, PosOf pos_of,
-                                     uint32_t* out_bits, int32_t* out_pos, TopkShared& sh) {
+                                     uint32_t* out_bits, int32_t* out_pos, TopkShared& sh, int eq_total = -1) {
   const int nv = run_valid<kPer>(n);
   int n_eq = 0, n_gt = 0;
 #pragma unroll
@@ -454,9 +563,12 @@ __device__ void ordered_compact_regs(const uint32_t (&v)[kPer], int n, uint32_t 
       n_eq += v[j] == T;
       n_gt += v[j] > T;
     }
-  int eq_total;
-  const int eq_before = block_inclusive_scan(n_eq, sh.wsum, eq_total) - n_eq;
-  const int keep_eq = max(0, min(n_eq, need - eq_before));
+  int keep_eq = n_eq;
+  if (eq_total != need) {
+    int eq_all;
+    const int eq_before = block_inclusive_scan(n_eq, sh.wsum, eq_all) - n_eq;
+    keep_eq = max(0, min(n_eq, need - eq_before));
+  }
   const int n_sel = keep_eq + n_gt;
   int sel_total;
   int o = block_inclusive_scan(n_sel, sh.wsum2, sel_total) - n_sel;
@@ -538,9 +650,10 @@ __global__ __launch_bounds__(kTopkThreads) void topk_local_kernel(TopkParams p) 
     // a single chunk: its winners are the answer
     uint32_t T;
     int need;
-    radix_select_regs<kPer>(v, len, kk, sh, T, need);
+    int eq_total;
+    radix_select_sampled<kPer>(v, len, kk, sh, s_data, T, need, eq_total);
     MAGE_TRACE_POINT(2);
-    ordered_compact_regs<kPer>(v, len, T, need, [&](int j) { return run0 + j; }, nullptr, out, sh);
+    ordered_compact_regs<kPer>(v, len, T, need, [&](int j) { return run0 + j; }, nullptr, out, sh, eq_total);
     for (int i = kk + tid; i < p.k; i += kTopkThreads) out[i] = -1;
     MAGE_TRACE_POINT(3);
     return;
@@ -553,9 +666,10 @@ __global__ __launch_bounds__(kTopkThreads) void topk_local_kernel(TopkParams p) 
   } else {
     uint32_t T;
     int need;
-    radix_select_regs<kPer>(v, len, kc, sh, T, need);
+    int eq_total;
+    radix_select_sampled<kPer>(v, len, kc, sh, s_data, T, need, eq_total);
     MAGE_TRACE_POINT(2);
-    ordered_compact_regs<kPer>(v, len, T, need, [&](int j) { return run0 + j; }, cb, cp, sh);
+    ordered_compact_regs<kPer>(v, len, T, need, [&](int j) { return run0 + j; }, cb, cp, sh, eq_total);
   }
   MAGE_TRACE_POINT(3);
 }
@@ -604,10 +718,11 @@ __global__ __launch_bounds__(kTopkThreads) void topk_final_kernel(TopkParams p) 
     load_run<kPer>(s_data, v);
     load_run<kPer>(s_data + kTopkChunk / 2, vpos);
     MAGE_TRACE_POINT(5);
-    radix_select_regs<kPer>(v, total, kk, sh, T, need);
+    int eq_total;
+    radix_select_sampled<kPer>(v, total, kk, sh, s_data, T, need, eq_total);
     MAGE_TRACE_POINT(6);
     ordered_compact_regs<kPer>(v, total, T, need, [&](int j) { return static_cast<int32_t>(vpos[j]); }, nullptr,
-                               out, sh);
+                               out, sh, eq_total);
   } else {
     auto get = [&](int i) { return all_bits[i]; };
     radix_select(get, total, kk, sh, T, need);
