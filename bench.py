@@ -7,8 +7,11 @@ workload: 1 sequence, 32 query / 8 KV heads, d=128, N=131072 prefix, B=32,
 k=1024, T=32 (the MAGE page's headline shape under "Key results").
 
 Protocol: inputs are resident in HBM before timing. Before every timed call a
-1 GiB scratch buffer is overwritten on the same stream (outside the timed
-window) so that K/V rows come from HBM, not from L2 or the 256 MB MALL. Each
+1 GiB scratch buffer is overwritten and then read back on the same stream
+(outside the timed window) so that K/V rows come from HBM, not from L2 or the
+256 MB MALL, and the caches hold clean lines: without the read-back the timed
+kernel would also pay for writing back the dirty lines the flush itself left
+in the MALL (--flush dirty measures that case; --flush none keeps caches). Each
 kernel of a timed call is launched with HIP events attached to the launch
 itself (mage_arm_kernel_timers, hipExtLaunchKernel), so kernel durations are
 GPU start-to-end times on the stream the kernel runs on, the same quantity
@@ -43,6 +46,11 @@ sys.path.insert(0, ROOT)
 
 import workloads  # noqa: E402
 
+FLUSH_DESC = {
+    "clean": "a 1 GiB write then a 1 GiB read of a scratch buffer",
+    "dirty": "a 1 GiB write of a scratch buffer (leaves dirty MALL lines)",
+    "none": "no flush",
+}
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 METRIC = "sparse-step denoising steps/sec and HBM GB/s (% peak) at 128K ctx, k=1024, B=32"
@@ -325,8 +333,12 @@ def run_bench(args):
     def flush():
         fill[0] += 1
         scratch.fill_(fill[0])
+        if args.flush == "clean":
+            scratch.sum()   # reads the 1 GiB back: evicts with clean lines
 
-    fl = (lambda: None) if args.no_flush else flush
+    if args.no_flush:
+        args.flush = "none"
+    fl = (lambda: None) if args.flush == "none" else flush
     T = w.steps
     for _ in range(args.warmup):
         r.select()
@@ -347,7 +359,7 @@ def run_bench(args):
             r.sparse(t, sp_timers[i * (T - 1) + t])
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    log(f"[bench] timed {args.steps} blocks in {wall:.2f} s wall (with a 1 GiB flush before every call)")
+    log(f"[bench] timed {args.steps} blocks in {wall:.2f} s wall (flush '{args.flush}' before every call)")
 
     # secondary measurements
     ex_timers = []
@@ -433,8 +445,9 @@ def run_bench(args):
                                f"{', 16-token pages, shuffled page table' if w.paged else ''}",
                    "global_batch": w.num_seqs, "seq_len": w.max_seq_len, "parallelism": "single GPU",
                    "step": f"1 bench step = 1 block = step-1 exact+select + {T - 1} sparse steps "
-                           f"(ms_per_step); value = sparse denoising steps/s, cold (1 GiB flush before "
-                           f"each call); a call's time is the sum of its kernels' GPU durations"},
+                           f"(ms_per_step); value = sparse denoising steps/s, cold (before each call "
+                           f"{FLUSH_DESC[args.flush]}); a call's time is the sum of its kernels' GPU "
+                           f"durations"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None if traffic is None else traffic["bytes_per_launch"],
@@ -468,7 +481,8 @@ def run_bench(args):
                          "event_pair_us_median": round(statistics.median([t.outer_ms() * 1e3 for t in sel_timers]), 1)},
         "speedup_vs_exact_per_step": round(ex_med / statistics.median(sp_busy), 2),
         "wall_s_timed_region": round(wall, 3),
-        "flushes_in_timed_region": args.steps * T if not args.no_flush else 0,
+        "flushes_in_timed_region": args.steps * T if args.flush != "none" else 0,
+        "flush": FLUSH_DESC[args.flush],
         "gpu": torch.cuda.get_device_name(0),
         "kernel_source_digest": source_digest(),
     }
@@ -489,9 +503,10 @@ def run_bench(args):
 # ---- profile summaries -----------------------------------------------------------
 def _short(name: str) -> str:
     for key in ("exact_chunk_kernel", "sparse_attn_kernel", "exact_merge_kernel", "score_kernel",
-                "topk_local_kernel", "topk_final_kernel", "FillFunctor", "neg_kernel"):
+                "topk_local_kernel", "topk_final_kernel", "FillFunctor", "neg_kernel", "reduce_kernel"):
         if key in name:
-            return {"FillFunctor": "flush (fill)", "neg_kernel": "copy (neg)"}.get(key, key)
+            return {"FillFunctor": "flush (fill)", "neg_kernel": "copy (neg)",
+                    "reduce_kernel": "flush (read)"}.get(key, key)
     return name[:60]
 
 
@@ -502,8 +517,10 @@ def _dispatches(path, value_col=None):
 
 
 def _cold_flags(names):
-    """A dispatch is cold when the dispatch before it is the 1 GiB flush."""
-    return [i > 0 and names[i - 1] == "flush (fill)" for i in range(len(names))]
+    """A dispatch is cold when the dispatch before it is the 1 GiB flush (its
+    read-back, or the fill itself with --flush dirty)."""
+    return [i > 0 and names[i - 1] in ("flush (fill)", "flush (read)") and not names[i].startswith("flush")
+            for i in range(len(names))]
 
 
 def summarize_trace(d):
@@ -579,7 +596,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", default="head128k", choices=sorted(workloads.CONFIG_BY_NAME))
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
-    ap.add_argument("--no-flush", action="store_true")
+    ap.add_argument("--flush", choices=sorted(FLUSH_DESC), default="clean",
+                    help="cache state before each timed call")
+    ap.add_argument("--no-flush", action="store_true", help="same as --flush none")
     ap.add_argument("--summarize-trace", metavar="DIR")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     args = ap.parse_args()

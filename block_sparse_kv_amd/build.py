@@ -16,7 +16,8 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-shared", "-fPIC",
-    # no packed-fp32 instructions are generated (see the design notes)
+    # keep packed-fp32 VALU instructions (v_pk_fma_f32 and kin) out of the code
+    # object: the kernels are written and checked for scalar fp32 arithmetic
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"),
 ]

@@ -210,10 +210,10 @@ template <int D, int kStages>
 __global__ __launch_bounds__(kAttnThreads) void exact_chunk_kernel(AttnParams p) {
   using G = TileGeom<D, kAttnThreads>;
   constexpr int kNdb = D / 32, kNks = D / 16;
-  constexpr int kStageBytes = 2 * G::kBytes;
-  static_assert(kStages >= 3, "tiles t and t+1 are read while tile t+2 loads");
-  static_assert(kStages * kStageBytes >= 4 * kWave * (2 + 16 * kNdb) * 4, "pair-merge area");
-  __shared__ __attribute__((aligned(1024))) uint8_t s_ring[kStages * kStageBytes];
+  static_assert(kStages == 4, "K(t+1)..K(t+4) and V(t-1)..V(t+2) are resident or in flight");
+  static_assert(2 * kStages * G::kBytes >= 4 * kWave * (2 + 16 * kNdb) * 4, "pair-merge area");
+  // K ring (kStages tiles) followed by the V ring (kStages tiles)
+  __shared__ __attribute__((aligned(1024))) uint8_t s_ring[2 * kStages * G::kBytes];
   __shared__ int32_t s_pages[kMaxChunkPages];   // paged layout: page ids of the chunk
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -265,6 +265,7 @@ __global__ __launch_bounds__(kAttnThreads) void exact_chunk_kernel(AttnParams p)
   // compiler does not count, so it must see its own loads complete here
   wait_vmcnt<0>();
   MAGE_TRACE_POINT(1);
+  MAGE_TRACE_CLK(1);
 
   // element offset of the K/V row of prefix position e (clamped into the chunk)
   auto row_of = [&](int e) -> int64_t {
@@ -309,15 +310,17 @@ __global__ __launch_bounds__(kAttnThreads) void exact_chunk_kernel(AttnParams p)
   k_frag_offsets<D>(swap_bits23(n), hh, kofs);
   const uint32_t ring_base = lds_addr(s_ring);
   const uint32_t k_half = kh * 32 * G::kRowBytes;
-  const uint32_t v_half = G::kBytes + kh * 2048 + vt_lane_offset(lane);
+  const uint32_t v_lane = kh * 2048 + vt_lane_offset(lane);
+  auto k_slot = [&](int tile) -> uint32_t { return ring_base + (tile % kStages) * G::kBytes; };
+  auto v_slot = [&](int tile) -> uint32_t { return ring_base + (kStages + tile % kStages) * G::kBytes; };
 
   const int ntiles = (cnt + kTileKeys - 1) / kTileKeys;
   // Full tiles: each DMA instruction covers 4 (K) or 16 (V) consecutive rows,
   // which are contiguous in memory (contiguous layout, or one page when pages
   // hold >= 16 rows). Its address is then a wave-uniform base (the slice's first
   // row) plus a per-lane byte offset fixed for the whole loop, so the loop
-  // writes no VGPR that an in-flight load still reads. The last, partial tile
-  // takes the clamped per-lane path.
+  // writes no VGPR that an in-flight load still reads. Other tiles take the
+  // clamped per-lane path.
   constexpr int kKRowsPerInstr = kWave / G::kUnits;        // 4 at d = 128
   uint32_t koff[G::kInstr], voff[G::kInstr];
 #pragma unroll
@@ -338,71 +341,152 @@ __global__ __launch_bounds__(kAttnThreads) void exact_chunk_kernel(AttnParams p)
     }
     return ((seq_base + pos) * D) * 2;
   };
-  // All tile loads are asm DMA that the compiler does not track; completion is
-  // accounted for with wait_tiles. Full (or shifted) tiles of contiguous rows
-  // take the uniform-base form; the rest load row by row and wait at once.
-  auto issue = [&](int tile) {
-    uint8_t* st = s_ring + (tile % kStages) * kStageBytes;
-    const uint32_t st_lds = lds_addr(st);
+  // a shifted tile of a paged cache need not start on a 16-row page boundary
+  auto fast_tile = [&](int tile) -> bool {
     const int base = tile_base(tile);
-    // a shifted tile of a paged cache need not start on a 16-row page boundary
-    if (fast_rows && base + kTileKeys <= e1 && (!paged || (base & 15) == 0)) {
-      const char* kb = reinterpret_cast<const char*>(p.kv.k);
-      const char* vb = reinterpret_cast<const char*>(p.kv.v);
+    return fast_rows && base + kTileKeys <= e1 && (!paged || (base & 15) == 0);
+  };
+  // All tile loads are asm DMA that the compiler does not track; completion is
+  // accounted for with wait_tiles. K rows of tile tk and V rows of tile tv
+  // (either may be -1: none) go to their ring slots.
+  const char* kbytes = reinterpret_cast<const char*>(p.kv.k);
+  const char* vbytes = reinterpret_cast<const char*>(p.kv.v);
+  auto issue = [&](int tk, int tv) {
+    const bool fk = tk >= 0 && fast_tile(tk), fv = tv >= 0 && fast_tile(tv);
+    const int bk = tk >= 0 ? tile_base(tk) : 0, bv = tv >= 0 ? tile_base(tv) : 0;
+    const uint32_t lk = tk >= 0 ? k_slot(tk) : 0u, lv = tv >= 0 ? v_slot(tv) : 0u;
+    if (fk && fv) {
 #pragma unroll
       for (int j = 0; j < G::kInstr; ++j) {
         const int slot = w * G::kInstr + j;
-        const int64_t kr = row_bytes(base + slot * kKRowsPerInstr);
-        const int64_t vr = row_bytes(base + ((slot & 3) << 4));
-        dma16x2(kb + kr, koff[j], st_lds + slot * 1024, vb + vr, voff[j], st_lds + G::kBytes + slot * 1024);
+        dma16x2(kbytes + row_bytes(bk + slot * kKRowsPerInstr), koff[j], lk + slot * 1024,
+                vbytes + row_bytes(bv + ((slot & 3) << 4)), voff[j], lv + slot * 1024);
       }
-    } else {
+      return;
+    }
 #pragma unroll
-      for (int j = 0; j < G::kInstr; ++j) {
-        const int slot = w * G::kInstr + j;
+    for (int j = 0; j < G::kInstr; ++j) {
+      const int slot = w * G::kInstr + j;
+      if (fk) {
+        dma16(kbytes + row_bytes(bk + slot * kKRowsPerInstr), koff[j], lk + slot * 1024);
+      } else if (tk >= 0) {
         const int unit = slot * kWave + lane;
         const int r = unit / G::kUnits, uk = (unit % G::kUnits) ^ (r & (G::kUnits - 1));
-        dma16_sync(p.kv.k + row_of(base + r) + uk * 8, st_lds + slot * 1024);
+        dma16_sync(p.kv.k + row_of(bk + r) + uk * 8, lk + slot * 1024);
+      }
+      if (fv) {
+        dma16(vbytes + row_bytes(bv + ((slot & 3) << 4)), voff[j], lv + slot * 1024);
+      } else if (tv >= 0) {
         const int db = slot >> 2, rv = ((slot & 3) << 4) + (lane >> 2);
-        dma16_sync(p.kv.v + row_of(base + rv) + 32 * db + 8 * (lane & 3), st_lds + G::kBytes + slot * 1024);
+        dma16_sync(p.kv.v + row_of(bv + rv) + 32 * db + 8 * (lane & 3), lv + slot * 1024);
       }
     }
   };
+  // Load group g = what iteration g reads: K rows of tile g+1 and V rows of
+  // tile g-1. Iteration t waits for group t, with groups t+1 and t+2 (issued
+  // in the two iterations before) still allowed in flight, then issues group
+  // t+3 into the slots of K(t) and V(t-2), which no wave reads any more once
+  // every wave has passed the barrier of iteration t.
+  auto group_k = [&](int g) { return g + 1 < ntiles ? g + 1 : -1; };
+  auto group_v = [&](int g) { return g >= 1 && g - 1 < ntiles ? g - 1 : -1; };
+  auto group_tiles = [&](int g) { return (group_k(g) >= 0) + (group_v(g) >= 0); };
+  auto wait_group = [&](int g) {
+    wait_tiles<G::kInstr, 5>(group_tiles(g + 1) + group_tiles(g + 2));
+    wg_barrier();
+  };
+
+  issue(0, -1);
 #pragma unroll
-  for (int t = 0; t < kStages - 1; ++t)
-    if (t < ntiles) issue(t);
-  wait_tiles<2 * G::kInstr, kStages - 1>(min(kStages - 2, ntiles - 1));
+  for (int g = 0; g < 3; ++g) issue(group_k(g), group_v(g));
+  wait_tiles<G::kInstr, 7>(group_tiles(0) + group_tiles(1) + group_tiles(2));   // K(0) landed
   wg_barrier();
   f32x16 s_cur;
-  if (computes) s_cur = qk_half<D>(ring_base + k_half, kofs, qf);
-  // One iteration: [tile t+1 resident, barrier, refill] then the QK product of
-  // tile t+1 interleaved with the softmax of tile t, then PV of tile t. In the
-  // last iteration the QK product re-reads tile t (result unused), which keeps
-  // the interleaved region free of branches.
+  if (computes) s_cur = qk_half<D>(k_slot(0) + k_half, kofs, qf);
+
+  // Iteration t: the PV product of tile t-1 (probabilities from iteration
+  // t-1), the QK product of tile t+1 and the softmax of tile t are
+  // independent, so the fragment reads are issued first and the MFMAs of
+  // both products are interleaved with the softmax's vector instructions.
+  // The running O takes the rescale of tile t's softmax after PV of tile t-1,
+  // whose probabilities were taken against the previous max. The last
+  // iteration's QK product re-reads tile t (result unused), which keeps the
+  // region free of branches.
+  bf16x8 ph[2], pl[2];
+  const bool partial = cnt % kTileKeys != 0;
   [[maybe_unused]] uint64_t trace_acc[4] = {0, 0, 0, 0};
-  auto step = [&](int t, auto masked) {
-    const bool has_next = t + 1 < ntiles;
-    [[maybe_unused]] const uint64_t tr0 = MAGE_TRACE_NOW();
-    if (has_next) {
-      // tile t+1 landed for every wave, and every wave is done with tile t-1
-      wait_tiles<2 * G::kInstr, kStages - 1>(min(kStages - 3, ntiles - 2 - t));
-      wg_barrier();
-    }
-    [[maybe_unused]] const uint64_t tr1 = MAGE_TRACE_NOW();
-    if (t + kStages - 1 < ntiles) issue(t + kStages - 1);   // into the stage of tile t-1
+  // t = 0: softmax of tile 0 and QK of tile 1
+  auto first = [&](auto masked) {
+    wait_group(0);
+    issue(group_k(3), group_v(3));
     if (computes) {
-      const int tn = has_next ? t + 1 : t;
-      // QK product of tile t+1 first: its MFMAs run under the softmax of tile t
-      const f32x16 s_nxt = qk_half<D>(ring_base + (tn % kStages) * kStageBytes + k_half, kofs, qf);
-      [[maybe_unused]] const uint64_t tr2 = MAGE_TRACE_NOW();
-      bf16x8 phi[2], plo[2];
       float alpha;
       bool grow;
-      softmax_half<decltype(masked)::value>(s_cur, half_mask(t), p.scale_log2, m_run, l_run, alpha,
-                                            grow, phi, plo, lane);
+      softmax_half<decltype(masked)::value>(s_cur, half_mask(0), p.scale_log2, m_run, l_run, alpha, grow,
+                                            ph, pl, lane);
+      if (ntiles > 1) s_cur = qk_half<D>(k_slot(1) + k_half, kofs, qf);
+    }
+  };
+  auto middle = [&](int t, auto masked) {
+    [[maybe_unused]] const uint64_t tr0 = MAGE_TRACE_NOW();
+    wait_group(t);
+    [[maybe_unused]] const uint64_t tr1 = MAGE_TRACE_NOW();
+    issue(group_k(t + 3), group_v(t + 3));
+    if (computes) {
+      const uint32_t okm = half_mask(t);
+      const uint32_t kb = k_slot(t + 1 < ntiles ? t + 1 : t) + k_half;
+      [[maybe_unused]] const uint64_t tr2 = MAGE_TRACE_NOW();
+      bf16x8 vf[kNdb][2], kf[kNks];
+      vt_frags_half_lds<D>(v_slot(t - 1) + v_lane, vf);
+      k_frags_lds<D>(kb, kofs, kf);
+#pragma unroll
+      for (int db = 0; db < kNdb; ++db)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db][s2], ph[s2], oacc[db], 0, 0, 0);
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db][s2], pl[s2], oacc[db], 0, 0, 0);
+        }
+      f32x16 s_nxt;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s_nxt[i] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < kNks; ++ks)
+        s_nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], s_nxt, 0, 0, 0);
+      bf16x8 phn[2], pln[2];
+      float alpha;
+      bool grow;
+      softmax_half<decltype(masked)::value>(s_cur, okm, p.scale_log2, m_run, l_run, alpha, grow, phn, pln,
+                                            lane);
+      // order: half the V reads, the start of the softmax, the other V reads,
+      // PV MFMAs of the first d blocks, the K reads, the remaining MFMAs, each
+      // MFMA followed by five vector instructions (at most 16 LDS reads are
+      // ever outstanding, so every wait can name the read it needs)
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * kNdb, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * kNdb, 0);
+#pragma unroll
+      for (int i = 0; i < 2 * kNdb; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, kNks, 0);
+#pragma unroll
+      for (int i = 0; i < 2 * kNdb + kNks; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+      }
+      // the softmax results are complete here, ahead of the rescale branch
+      // (otherwise the compiler sinks their computation past it, out of the
+      // region shared with the MFMAs)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) asm volatile("" : "+v"(phn[s2]), "+v"(pln[s2]));
+      asm volatile("" : "+v"(l_run));
       [[maybe_unused]] const uint64_t tr3 = MAGE_TRACE_NOW();
       rescale_o<D>(grow, alpha, oacc);
-      pv_half<D>(ring_base + (t % kStages) * kStageBytes + v_half, phi, plo, oacc);
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        ph[s2] = phn[s2];
+        pl[s2] = pln[s2];
+      }
       s_cur = s_nxt;
       [[maybe_unused]] const uint64_t tr4 = MAGE_TRACE_NOW();
       trace_acc[0] += tr1 - tr0;
@@ -411,11 +495,30 @@ __global__ __launch_bounds__(kAttnThreads) void exact_chunk_kernel(AttnParams p)
       trace_acc[3] += tr4 - tr3;
     }
   };
-  for (int t = 0; t + 1 < ntiles; ++t) step(t, std::false_type{});
-  if (cnt % kTileKeys)
-    step(ntiles - 1, std::true_type{});
+  if (ntiles == 1 && partial)
+    first(std::true_type{});
   else
-    step(ntiles - 1, std::false_type{});
+    first(std::false_type{});
+  for (int t = 1; t + 1 < ntiles; ++t) middle(t, std::false_type{});
+  if (ntiles > 1) {
+    if (partial)
+      middle(ntiles - 1, std::true_type{});
+    else
+      middle(ntiles - 1, std::false_type{});
+  }
+  // t = ntiles: PV of the last tile
+  wait_group(ntiles);
+  if (computes) {
+    bf16x8 vf[kNdb][2];
+    vt_frags_half_lds<D>(v_slot(ntiles - 1) + v_lane, vf);
+#pragma unroll
+    for (int db = 0; db < kNdb; ++db)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db][s2], ph[s2], oacc[db], 0, 0, 0);
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db][s2], pl[s2], oacc[db], 0, 0, 0);
+      }
+  }
   l_run = wave_sum_pair(l_run);
   MAGE_TRACE_ADD(4, trace_acc[0]);
   MAGE_TRACE_ADD(5, trace_acc[1]);
@@ -423,6 +526,7 @@ __global__ __launch_bounds__(kAttnThreads) void exact_chunk_kernel(AttnParams p)
   MAGE_TRACE_ADD(7, trace_acc[3]);
   __syncthreads();  // the ring is reused below
   MAGE_TRACE_POINT(2);
+  MAGE_TRACE_CLK(2);
 
   // ---- merge the two key halves of each row block through LDS ---------------
   {
@@ -529,6 +633,7 @@ __global__ __launch_bounds__(kSparseThreads) void sparse_attn_kernel(AttnParams 
   __shared__ __attribute__((aligned(1024))) uint8_t s_ring[kSparseWaves * kWaveRing];
   __shared__ int32_t s_tab[kSparseWaves][kSparseMaxKpw];
 
+  MAGE_TRACE_POINT(6);
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hh = lane >> 5, n = lane & 31;

@@ -102,6 +102,12 @@ __device__ uint64_t g_trace[8192][8];
       mage::g_trace[blockIdx.x][slot] = __builtin_amdgcn_s_memrealtime();  \
   } while (0)
 #define MAGE_TRACE_NOW() __builtin_amdgcn_s_memrealtime()
+// shader-clock counter beside the real-time one (row 4096 + work-group)
+#define MAGE_TRACE_CLK(slot)                                                            \
+  do {                                                                                  \
+    if (threadIdx.x == 0 && blockIdx.x < 4096)                                          \
+      mage::g_trace[4096 + blockIdx.x][slot] = __builtin_amdgcn_s_memtime();            \
+  } while (0)
 #define MAGE_TRACE_ADD(slot, v)                                             \
   do {                                                                      \
     if (threadIdx.x == 0 && blockIdx.x < 8192) mage::g_trace[blockIdx.x][slot] += (v); \
@@ -111,6 +117,9 @@ __device__ uint64_t g_trace[8192][8];
   do {                         \
   } while (0)
 #define MAGE_TRACE_NOW() 0ull
+#define MAGE_TRACE_CLK(slot) \
+  do {                       \
+  } while (0)
 #define MAGE_TRACE_ADD(slot, v) \
   do {                          \
   } while (0)

@@ -12,10 +12,12 @@
 // Top-k: the k_eff largest scores, ties to the lower position, ascending
 // output. Scores are >= +0, so their fp32 bit patterns order like the values
 // and the selection is integer work on those bits: an MSB-first radix select
-// (12-bit digits, LDS histograms) finds the k-th largest bit pattern T and how
-// many entries equal to T to keep; an index-ordered compaction (wave ballots +
-// prefix popcounts) then keeps every entry > T and the lowest-positioned
-// entries == T. A first kernel does this per 16384-position chunk held in LDS;
+// (8-bit digits, per-wave LDS histograms, a sampled first digit that narrows
+// the search to a small candidate window) finds the k-th largest bit pattern T
+// and how many entries equal to T to keep; an index-ordered compaction (each
+// thread owns a contiguous run, block prefix sums give the output offsets)
+// then keeps every entry > T and the lowest-positioned entries == T. A first
+// kernel does this per 16384-position chunk held in LDS;
 // a second kernel runs the same selection over the concatenated per-chunk
 // winners, which are in position order, so its output is already ascending.
 // The two kernels replace an in-kernel last-arriver handoff: on gfx950 a
@@ -222,14 +224,56 @@ __device__ __forceinline__ void wave_totals(const int32_t* w, int wv, int& below
   }
 }
 
+// Cross-lane steps through DPP (data-parallel primitives: a VALU operand
+// read from another lane of the same row of 16, or a row broadcast), which
+// cost one dependent VALU operation each instead of an LDS permute round trip.
+// dpp_ctrl codes: row_shr:n = 0x110 + n; row_bcast:15 = 0x142; row_bcast:31 = 0x143.
+// Lanes whose source is outside the row, or whose row is masked off, read 0.
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ uint32_t dpp_read(uint32_t v) {
+  return static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(v), kCtrl, kRowMask, 0xf, false));
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave: Hillis-Steele steps
+// 1, 2, 4, 8 inside each row of 16, then row 0's total is added to row 1 and
+// row 2's to row 3 (row_bcast:15), then lane 31's sum to rows 2 and 3.
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  v += static_cast<int>(dpp_read<0x111, 0xf>(static_cast<uint32_t>(v)));
+  v += static_cast<int>(dpp_read<0x112, 0xf>(static_cast<uint32_t>(v)));
+  v += static_cast<int>(dpp_read<0x114, 0xf>(static_cast<uint32_t>(v)));
+  v += static_cast<int>(dpp_read<0x118, 0xf>(static_cast<uint32_t>(v)));
+  v += static_cast<int>(dpp_read<0x142, 0xa>(static_cast<uint32_t>(v)));
+  v += static_cast<int>(dpp_read<0x143, 0xc>(static_cast<uint32_t>(v)));
+  return v;
+}
+
+// Bitwise OR over the 64 lanes of a wave (the same steps as the scan; lane 63
+// ends with the OR of every lane), returned uniform.
+__device__ __forceinline__ uint32_t wave_or(uint32_t v) {
+  v |= dpp_read<0x111, 0xf>(v);
+  v |= dpp_read<0x112, 0xf>(v);
+  v |= dpp_read<0x114, 0xf>(v);
+  v |= dpp_read<0x118, 0xf>(v);
+  v |= dpp_read<0x142, 0xa>(v);
+  v |= dpp_read<0x143, 0xc>(v);
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 63));
+}
+
+// x + x[l ^ 16] + x[l ^ 32] + x[l ^ 48] in every lane: v_permlane16_swap and
+// v_permlane32_swap with both operands = x give x and its partner lane's value
+// (in either order), and the sum is symmetric.
+__device__ __forceinline__ uint32_t sum_over_rows(uint32_t x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  x = a[0] + a[1];
+  const auto b = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return b[0] + b[1];
+}
+
 // Block-wide inclusive prefix sum of one int per thread; also returns the total.
 __device__ __forceinline__ int block_inclusive_scan(int v, int32_t* wsum, int& total) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(v, off);
-    if (lane >= off) v += y;
-  }
+  v = wave_inclusive_scan(v);
   if (lane == 63) wsum[wv] = v;
   __syncthreads();
   int before;
@@ -240,8 +284,7 @@ __device__ __forceinline__ int block_inclusive_scan(int v, int32_t* wsum, int& t
 
 // Bitwise OR over the work-group (one value per thread); result valid after return.
 __device__ __forceinline__ uint32_t block_or(uint32_t v, int32_t* wsum) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) v |= __shfl_xor(v, off);
+  v = wave_or(v);
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   if (lane == 0) wsum[wv] = static_cast<int32_t>(v);
   __syncthreads();
@@ -405,8 +448,7 @@ __device__ void radix_select_regs(const uint32_t (&v)[kPer], int n, int kk, Topk
       uint32_t c = 0;
 #pragma unroll
       for (int q = 0; q < kTopkWaves / 4; ++q) c += sh.hist[(part * (kTopkWaves / 4) + q) * 256 + bin];
-      c += __shfl_xor(c, 16);
-      c += __shfl_xor(c, 32);
+      c = sum_over_rows(c);
       if (lane < 16) total[bin] = c;
     }
     __syncthreads();
@@ -415,12 +457,7 @@ __device__ void radix_select_regs(const uint32_t (&v)[kPer], int n, int kk, Topk
       typedef uint32_t u4 __attribute__((ext_vector_type(4)));
       const u4 c4 = reinterpret_cast<const u4*>(total)[63 - lane];
       const int s = static_cast<int>(c4[0] + c4[1] + c4[2] + c4[3]);
-      int incl = s;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(incl, off);
-        if (lane >= off) incl += y;
-      }
+      const int incl = wave_inclusive_scan(s);
       int above = incl - s;
       if (above < rem && rem <= incl) {
         for (int e = 3; e >= 0; --e) {
@@ -474,6 +511,7 @@ __device__ void radix_select_sampled(const uint32_t (&v)[kPer], int n, int kk, T
   for (int j = 0; j < kPer; ++j)
     if (j < nv) diff |= v[j] ^ first;
   diff = block_or(diff, sh.wsum);
+  MAGE_TRACE_POINT(4);
   if (diff == 0) {  // all entries equal
     T = first;
     need = kk;
@@ -496,12 +534,7 @@ __device__ void radix_select_sampled(const uint32_t (&v)[kPer], int n, int kk, T
     typedef uint32_t u4 __attribute__((ext_vector_type(4)));
     const u4 c4 = reinterpret_cast<const u4*>(total)[63 - lane];
     const int s4 = static_cast<int>(c4[0] + c4[1] + c4[2] + c4[3]);
-    int incl = s4;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int y = __shfl_up(incl, off);
-      if (lane >= off) incl += y;
-    }
+    const int incl = wave_inclusive_scan(s4);
     // sample counts at the k-th value: kk * m / n; window edges a quarter + 4 away
     const float tk = static_cast<float>(kk) * static_cast<float>(m) / static_cast<float>(n);
     const float t_hi = 0.75f * tk - 4.f, t_lo = 1.25f * tk + 4.f;
@@ -517,6 +550,7 @@ __device__ void radix_select_sampled(const uint32_t (&v)[kPer], int n, int kk, T
   }
   __syncthreads();
   const int d_hi = sh.res[0], d_lo = sh.res[1];
+  MAGE_TRACE_POINT(5);
   // exact counts above and inside the window, packed (both totals < 2^16)
   int a_loc = 0, m_loc = 0;
 #pragma unroll
@@ -530,6 +564,7 @@ __device__ void radix_select_sampled(const uint32_t (&v)[kPer], int n, int kk, T
   int tot;
   const int incl = block_inclusive_scan(packed, sh.wsum, tot);
   const int A = tot >> 16, M = tot & 0xffff;
+  MAGE_TRACE_POINT(6);
   if (!(A < kk && kk <= A + M) || M > kCand) {
     radix_select_regs<kPer>(v, n, kk, sh, T, need, &eq_total);
     return;
@@ -542,6 +577,7 @@ __device__ void radix_select_sampled(const uint32_t (&v)[kPer], int n, int kk, T
       if (d >= d_lo && d <= d_hi) cand[o++] = v[j];
     }
   __syncthreads();
+  MAGE_TRACE_POINT(7);
   uint32_t c2[2];
 #pragma unroll
   for (int q = 0; q < 2; ++q) c2[q] = cand[min(2 * tid + q, M - 1)];
@@ -667,8 +703,29 @@ __global__ __launch_bounds__(kTopkThreads) void topk_local_kernel(TopkParams p) 
     uint32_t T;
     int need;
     int eq_total;
+#ifdef MAGE_TRACE_REPEAT
+    const uint64_t c0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
+#endif
     radix_select_sampled<kPer>(v, len, kc, sh, s_data, T, need, eq_total);
     MAGE_TRACE_POINT(2);
+#ifdef MAGE_TRACE_REPEAT
+    {
+      __syncthreads();
+      const uint64_t c1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
+      uint32_t T2;
+      int need2, eq2;
+      radix_select_sampled<kPer>(v, len, kc, sh, s_data, T2, need2, eq2);
+      __syncthreads();
+      const uint64_t c2 = __builtin_amdgcn_s_memtime(), r2 = __builtin_amdgcn_s_memrealtime();
+      if (tid == 0 && blockIdx.x < 4096) {
+        g_trace[4096 + blockIdx.x][0] = c1 - c0;
+        g_trace[4096 + blockIdx.x][1] = r1 - r0;
+        g_trace[4096 + blockIdx.x][2] = c2 - c1;
+        g_trace[4096 + blockIdx.x][3] = r2 - r1;
+        g_trace[4096 + blockIdx.x][4] = (T2 == T && need2 == need) ? 1 : 2;
+      }
+    }
+#endif
     ordered_compact_regs<kPer>(v, len, T, need, [&](int j) { return run0 + j; }, cb, cp, sh, eq_total);
   }
   MAGE_TRACE_POINT(3);

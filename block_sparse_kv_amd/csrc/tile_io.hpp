@@ -94,6 +94,17 @@ __device__ __forceinline__ void dma16x2(const void* b0, uint32_t o0, uint32_t l0
       : "memory", "m0");
 }
 
+// A single load of the dma16x2 form.
+__device__ __forceinline__ void dma16(const void* b, uint32_t o, uint32_t l) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(o), "s"(b), "s"(l)
+      : "memory", "m0");
+}
+
 // One direct LDS load per lane from a per-lane 64-bit address, waited for in
 // the same asm block (the path for tiles whose rows are not contiguous in
 // memory; the wait frees the address registers before the block ends).
@@ -180,6 +191,21 @@ __device__ __forceinline__ void k_frags(uint32_t base, const uint32_t (&ofs)[D /
   }
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) f[ks] = __builtin_bit_cast(bf16x8, r[ks]);
+}
+
+// LDS pointer of a byte address (LDS pointers are 32-bit).
+template <class T>
+__device__ __forceinline__ __attribute__((address_space(3))) T* lds_ptr(uint32_t addr) {
+  return (__attribute__((address_space(3))) T*)(addr);
+}
+
+// k_frags as ordinary LDS loads, for loops whose tile loads are all asm DMA:
+// the compiler then tracks these reads itself, issues them early and waits
+// (lgkmcnt) only where a fragment is first used.
+template <int D>
+__device__ __forceinline__ void k_frags_lds(uint32_t base, const uint32_t (&ofs)[D / 16], bf16x8 (&f)[D / 16]) {
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) f[ks] = __builtin_bit_cast(bf16x8, *lds_ptr<const u32x4>(base + ofs[ks]));
 }
 
 // Per-lane byte offset of the V^T fragment reads (inside a V tile).
@@ -285,6 +311,23 @@ __device__ __forceinline__ void vt_frags_half(uint32_t vaddr, bf16x8 (&frag)[D /
         frag[db][s2] = __builtin_bit_cast(bf16x8, s8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
       }
   }
+}
+
+// vt_frags_half as compiler-visible transpose loads (same fragments and
+// addresses), for the same loops as k_frags_lds.
+template <int D, int kB = kTileKeys * 64>
+__device__ __forceinline__ void vt_frags_half_lds(uint32_t vaddr, bf16x8 (&frag)[D / 32][2]) {
+  typedef short s4 __attribute__((ext_vector_type(4)));
+  typedef short s8 __attribute__((ext_vector_type(8)));
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const uint32_t a = vaddr + db * kB + s2 * 1024;
+      const s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_ptr<s4>(a));
+      const s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_ptr<s4>(a + 256));
+      frag[db][s2] = __builtin_bit_cast(bf16x8, s8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+    }
 }
 
 }  // namespace mage
