@@ -503,7 +503,8 @@ def run_bench(args):
 # ---- profile summaries -----------------------------------------------------------
 def _short(name: str) -> str:
     for key in ("exact_chunk_kernel", "sparse_attn_kernel", "exact_merge_kernel", "score_kernel",
-                "topk_local_kernel", "topk_final_kernel", "FillFunctor", "neg_kernel", "reduce_kernel"):
+                "topk_local_kernel", "topk_final_kernel", "topk_hist_kernel", "hist_zero_kernel", "FillFunctor",
+                "neg_kernel", "reduce_kernel"):
         if key in name:
             return {"FillFunctor": "flush (fill)", "neg_kernel": "copy (neg)",
                     "reduce_kernel": "flush (read)"}.get(key, key)

@@ -179,7 +179,6 @@ int sparse_chunk(int64_t units, int nrb, int k) {
   return std::min(kSparseMaxChunk, std::max(min_chunk, c));
 }
 
-constexpr int kScoreChunk = 2048;
 // LDS ring depth: 4 x 32 KiB of K+V tiles at d = 128, 4 x 16 KiB at d = 64;
 // the score sweep streams K only: 4 x 16 KiB / 4 x 8 KiB (two work-groups per CU).
 template <int D>
@@ -190,7 +189,7 @@ constexpr int kSparseStages = 2;
 
 // ---- workspace layout ------------------------------------------------------
 struct Layout {
-  size_t rowstat, part_ml, part_o, cand_bits, cand_pos, scores, total;
+  size_t rowstat, part_ml, part_o, cand_bits, cand_pos, cand_count, hist, hist_parts, scores, total;
   int64_t slots, cand_stride;
 };
 
@@ -200,8 +199,8 @@ Layout make_layout(const Dims& d, int64_t max_n, int64_t k) {
   const int64_t exact_slots = U * cdiv(max_n, exact_chunk_floor(U, max_n));
   const int64_t sparse_slots = U * std::min<int64_t>(kSparseMaxChunks, cdiv(k, kSparseChunkUnit));
   L.slots = std::max(exact_slots, sparse_slots);
-  const int64_t kc = std::min<int64_t>(k, kTopkChunk);
-  L.cand_stride = cdiv(max_n, kTopkChunk) * kc;
+  const int64_t nchunk = cdiv(max_n, kLocalChunk);
+  L.cand_stride = nchunk * kLocalChunk;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t at = off;
@@ -213,6 +212,10 @@ Layout make_layout(const Dims& d, int64_t max_n, int64_t k) {
   L.part_o = take(L.slots * 4 * (d.D / 32) * 4 * kWave * 16);
   L.cand_bits = take(U * L.cand_stride * 4);
   L.cand_pos = take(U * L.cand_stride * 4);
+  L.cand_count = take(U * nchunk * 4);
+  L.hist = take(U * kHistBins * 4);
+  // histogram parts: one per score chunk (standalone top-k: one per 4096-entry chunk)
+  L.hist_parts = take(U * cdiv(max_n, kScoreChunk) * kHistBins * 4);
   L.scores = take(U * max_n * 4);
   L.total = off;
   return L;
@@ -284,14 +287,28 @@ mage_status paged_kv(const Dims& d, const mage_paged_kv* kv, KvArgs& a) {
   return MAGE_OK;
 }
 
-mage_status launch_topk(const TopkParams& tp, hipStream_t stream) {
-  if (mage_status st = launch(kfn(topk_local_kernel), "topk_local_kernel",
-                              static_cast<int64_t>(tp.rows) * tp.nchunk, kTopkThreads, stream, tp);
+// Rows longer than this are beyond the final pass's chunk table.
+constexpr int64_t kMaxTopkLen = static_cast<int64_t>(kMaxLocalChunks) * kLocalChunk;
+
+// The row histograms are the sums of the parts in hr.parts; with
+// build_parts (standalone top-k) the parts are first taken from the scores,
+// else the score sweep has written them.
+mage_status launch_topk(const TopkParams& tp, const HistReduceParams& hr, hipStream_t stream,
+                        bool build_parts) {
+  const int64_t wgs = static_cast<int64_t>(tp.rows) * tp.nchunk;
+  if (build_parts) {
+    if (mage_status st = launch(kfn(topk_hist_kernel), "topk_hist_kernel", wgs, kLocalThreads, stream, tp);
+        st != MAGE_OK)
+      return st;
+  }
+  if (mage_status st = launch(kfn(hist_reduce_kernel), "hist_reduce_kernel",
+                              static_cast<int64_t>(hr.rows) * (kHistBins / 256), 256, stream, hr);
       st != MAGE_OK)
     return st;
-  if (tp.nchunk > 1)
-    return launch(kfn(topk_final_kernel), "topk_final_kernel", tp.rows, kTopkThreads, stream, tp);
-  return MAGE_OK;
+  if (mage_status st = launch(kfn(topk_local_kernel), "topk_local_kernel", wgs, kLocalThreads, stream, tp);
+      st != MAGE_OK)
+    return st;
+  return launch(kfn(topk_final_kernel), "topk_final_kernel", tp.rows, kTopkThreads, stream, tp);
 }
 
 // k == 0: exact attention only (no score sweep, no top-k).
@@ -303,6 +320,7 @@ mage_status launch_select(const Dims& d, const uint16_t* q, const KvArgs& kv, in
   const int chunk = exact_chunk(U, kv.max_n, kv.total_keys,
                                 kv.src.page_table ? (1 << kv.src.page_shift) : 0);
   if (chunk == 0) return fail(MAGE_ERR_UNSUPPORTED, "page_size too small for this prefix length");
+  if (k > 0 && kv.max_n > kMaxTopkLen) return fail(MAGE_ERR_UNSUPPORTED, "top-k of a prefix longer than 2^25");
   const int nch = static_cast<int>(cdiv(kv.max_n, chunk));
   const float scale_log2 = d.scale * kLog2e;
 
@@ -356,10 +374,11 @@ mage_status launch_select(const Dims& d, const uint16_t* q, const KvArgs& kv, in
   sp.q = q;
   sp.kv = kv.src;
   sp.rowstat = mp.rowstat;
+  sp.hist_parts = at<uint32_t>(ws, L.hist_parts);
   sp.scores = scores ? scores : at<float>(ws, L.scores);
   sp.stride = scores ? score_stride : kv.max_n;
   sp.S = d.S; sp.B = d.B; sp.Hq = d.Hq; sp.Hkv = d.Hkv; sp.G = d.G; sp.R = d.R;
-  sp.chunk = std::min(kScoreMaxChunk, env_int("MAGE_SCORE_CHUNK", kScoreChunk));
+  sp.chunk = kScoreChunk;
   sp.nchunk = static_cast<int>(cdiv(kv.max_n, sp.chunk));
   sp.reverse = env_int("MAGE_SCORE_REVERSE", 1);
   sp.scale_log2 = scale_log2;
@@ -374,15 +393,27 @@ mage_status launch_select(const Dims& d, const uint16_t* q, const KvArgs& kv, in
   tp.stride = sp.stride;
   tp.idx = idx;
   tp.k = k;
+  tp.hist = at<uint32_t>(ws, L.hist);
   tp.cand_bits = at<uint32_t>(ws, L.cand_bits);
   tp.cand_pos = at<int32_t>(ws, L.cand_pos);
   tp.cand_stride = L.cand_stride;
+  tp.cand_count = at<int32_t>(ws, L.cand_count);
   tp.rows = static_cast<int32_t>(U);
   tp.rows_per_seq = d.Hkv;
   tp.n_uniform = kv.src.page_table ? -1 : kv.src.n_uniform;
-  tp.nchunk = static_cast<int>(cdiv(kv.max_n, kTopkChunk));
+  tp.nchunk = static_cast<int>(cdiv(kv.max_n, kLocalChunk));
   tp.lens = kv.lens;
-  if (mage_status st = launch_topk(tp, sel); st != MAGE_OK) return st;
+  HistReduceParams hr{};
+  hr.parts = sp.hist_parts;
+  hr.hist = tp.hist;
+  hr.rows = tp.rows;
+  hr.nparts = sp.nchunk;
+  hr.part_len = sp.chunk;
+  hr.rows_per_seq = tp.rows_per_seq;
+  hr.n_uniform = tp.n_uniform;
+  hr.k = k;
+  hr.lens = kv.lens;
+  if (mage_status st = launch_topk(tp, hr, sel, false); st != MAGE_OK) return st;
   if (idx_ready) {
     if (hipError_t e = hipEventRecord(idx_ready, sel); e != hipSuccess)
       return hip_fail(e, "hipEventRecord(idx_ready)");
@@ -612,6 +643,7 @@ mage_status mage_topk(int32_t rows, const float* scores, int64_t row_stride, con
     }
   }
   if (rows > (1 << 20)) return fail(MAGE_ERR_UNSUPPORTED, "rows must be <= 2^20");
+  if (n > kMaxTopkLen) return fail(MAGE_ERR_UNSUPPORTED, "rows longer than 2^25 entries");
   // workspace: the full layout for one KV head per row
   Dims d{};
   d.S = rows; d.B = 1; d.Hq = 1; d.Hkv = 1; d.G = 1; d.R = 1; d.D = 64; d.nrb = 1; d.units = rows;
@@ -623,15 +655,28 @@ mage_status mage_topk(int32_t rows, const float* scores, int64_t row_stride, con
   tp.stride = row_stride;
   tp.idx = idx;
   tp.k = k;
+  tp.hist = at<uint32_t>(workspace, L.hist);
+  tp.hist_parts = at<uint32_t>(workspace, L.hist_parts);
   tp.cand_bits = at<uint32_t>(workspace, L.cand_bits);
   tp.cand_pos = at<int32_t>(workspace, L.cand_pos);
   tp.cand_stride = L.cand_stride;
+  tp.cand_count = at<int32_t>(workspace, L.cand_count);
   tp.rows = rows;
   tp.rows_per_seq = 1;
   tp.n_uniform = lens ? -1 : n;
-  tp.nchunk = static_cast<int>(cdiv(n, kTopkChunk));
+  tp.nchunk = static_cast<int>(cdiv(n, kLocalChunk));
   tp.lens = sl;
-  return launch_topk(tp, stream);
+  HistReduceParams hr{};
+  hr.parts = tp.hist_parts;
+  hr.hist = tp.hist;
+  hr.rows = rows;
+  hr.nparts = tp.nchunk;
+  hr.part_len = kLocalChunk;
+  hr.rows_per_seq = 1;
+  hr.n_uniform = tp.n_uniform;
+  hr.k = k;
+  hr.lens = sl;
+  return launch_topk(tp, hr, stream, true);
 }
 
 const char* mage_status_string(mage_status status) {

@@ -30,12 +30,118 @@
 
 namespace mage {
 
+// Cross-lane steps through DPP (data-parallel primitives: a VALU operand
+// read from another lane of the same row of 16, or a row broadcast), which
+// cost one dependent VALU operation each instead of an LDS permute round trip.
+// dpp_ctrl codes: row_shr:n = 0x110 + n; row_bcast:15 = 0x142; row_bcast:31 = 0x143.
+// Lanes whose source is outside the row, or whose row is masked off, read 0.
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ uint32_t dpp_read(uint32_t v) {
+  return static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(v), kCtrl, kRowMask, 0xf, false));
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave: Hillis-Steele steps
+// 1, 2, 4, 8 inside each row of 16, then row 0's total is added to row 1 and
+// row 2's to row 3 (row_bcast:15), then lane 31's sum to rows 2 and 3.
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  v += static_cast<int>(dpp_read<0x111, 0xf>(static_cast<uint32_t>(v)));
+  v += static_cast<int>(dpp_read<0x112, 0xf>(static_cast<uint32_t>(v)));
+  v += static_cast<int>(dpp_read<0x114, 0xf>(static_cast<uint32_t>(v)));
+  v += static_cast<int>(dpp_read<0x118, 0xf>(static_cast<uint32_t>(v)));
+  v += static_cast<int>(dpp_read<0x142, 0xa>(static_cast<uint32_t>(v)));
+  v += static_cast<int>(dpp_read<0x143, 0xc>(static_cast<uint32_t>(v)));
+  return v;
+}
+
+// Bitwise OR over the 64 lanes of a wave (the same steps as the scan; lane 63
+// ends with the OR of every lane), returned uniform.
+__device__ __forceinline__ uint32_t wave_or(uint32_t v) {
+  v |= dpp_read<0x111, 0xf>(v);
+  v |= dpp_read<0x112, 0xf>(v);
+  v |= dpp_read<0x114, 0xf>(v);
+  v |= dpp_read<0x118, 0xf>(v);
+  v |= dpp_read<0x142, 0xa>(v);
+  v |= dpp_read<0x143, 0xc>(v);
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 63));
+}
+
+// x + x[l ^ 16] + x[l ^ 32] + x[l ^ 48] in every lane: v_permlane16_swap and
+// v_permlane32_swap with both operands = x give x and its partner lane's value
+// (in either order), and the sum is symmetric.
+__device__ __forceinline__ uint32_t sum_over_rows(uint32_t x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  x = a[0] + a[1];
+  const auto b = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return b[0] + b[1];
+}
+
+
+// Score histogram: bin of a non-negative fp32 score = its bit pattern >> 21
+// (sign, exponent, two mantissa bits: quarter-octave bins covering every
+// non-negative value). Bit patterns order like the values, so the bin of the
+// k-th largest score, read off a row's histogram, bounds the top-k: every
+// score in a higher bin is in it, every score in a lower bin is not.
+constexpr int kHistBins = 1024;
+constexpr int kHistShift = 21;
+
+// hist[bin] += 1 for every lane with `active` (one LDS atomic per lane: the
+// LDS serializes same-bin lanes in hardware, which costs less than peeling
+// off the wave's distinct bins in a loop).
+__device__ __forceinline__ void wave_hist_add(uint32_t* hist, uint32_t bin, bool active) {
+  if (active) atomicAdd(&hist[bin], 1u);
+}
+
+// Stores a work-group's LDS histogram as its part of the row histogram
+// (plain stores: hist_reduce_kernel adds the parts up after a kernel
+// boundary; device-scope atomics from every work-group of a row into the same
+// bins serialize at the memory side and cost far more).
+template <int kNT>
+__device__ __forceinline__ void store_hist_part(const uint32_t* s_hist, uint32_t* part) {
+  for (int b = threadIdx.x; b < kHistBins; b += kNT) part[b] = s_hist[b];
+}
+
+// Row histogram = the sum of its parts: part j of row u covers positions
+// [j * part_len, (j + 1) * part_len), and only parts holding a position of
+// the row were written. One work-group per (row, 256 bins).
+struct HistReduceParams {
+  const uint32_t* parts;    // [rows][nparts][kHistBins]
+  uint32_t* hist;           // [rows][kHistBins]
+  int32_t rows, nparts, part_len;
+  int32_t rows_per_seq;     // row u belongs to sequence u / rows_per_seq
+  int32_t n_uniform;        // >= 0: every row has this many entries; else lens
+  int32_t k;                // rows with min(k, n) == n need no histogram
+  SeqLens lens;
+};
+
+__global__ __launch_bounds__(256) void hist_reduce_kernel(HistReduceParams p) {
+  constexpr int kBlocks = kHistBins / 256;
+  const int u = blockIdx.x / kBlocks, b = (blockIdx.x % kBlocks) * 256 + threadIdx.x;
+  if (u >= p.rows) return;
+  const int n = p.n_uniform >= 0 ? p.n_uniform : p.lens.n[u / p.rows_per_seq];
+  if (min(p.k, n) == n) return;
+  const int np = (n + p.part_len - 1) / p.part_len;
+  const uint32_t* src = p.parts + static_cast<int64_t>(u) * p.nparts * kHistBins + b;
+  uint32_t sum = 0;
+  int j = 0;
+  for (; j + 8 <= np; j += 8) {   // eight loads in flight per step
+    uint32_t x[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) x[q] = src[static_cast<int64_t>(j + q) * kHistBins];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) sum += x[q];
+  }
+  for (; j < np; ++j) sum += src[static_cast<int64_t>(j) * kHistBins];
+  p.hist[static_cast<int64_t>(u) * kHistBins + b] = sum;
+}
+
 struct ScoreParams {
   const uint16_t* q;
   KvSource kv;
   const float* rowstat;     // per (unit, row) max + log2(sum)
   float* scores;            // [S][Hkv][stride]
   int64_t stride;
+  uint32_t* hist_parts;     // [S * Hkv][nchunk][kHistBins]: each chunk's score histogram
   int32_t S, B, Hq, Hkv, G, R;
   int32_t chunk, nchunk;
   int32_t reverse;          // sweep tiles last-to-first
@@ -43,17 +149,18 @@ struct ScoreParams {
   SeqLens lens;
 };
 
-// Positions per score work-group (the host's chunk never exceeds it); sized
-// so that two work-groups fit in one CU's LDS.
-constexpr int kScoreMaxChunk = 2048;
+// Positions per score work-group; sized so that two work-groups fit in one
+// CU's LDS. Each work-group stores its chunk's part of the row histogram.
+constexpr int kScoreChunk = 2048;
 
 template <int D, int kStages>
 __global__ __launch_bounds__(kThreads) void score_kernel(ScoreParams p) {
   using G = TileGeom<D>;
   constexpr int kNks = D / 16;
   __shared__ __attribute__((aligned(1024))) uint8_t s_ring[kStages * G::kBytes];
-  __shared__ int32_t s_pages[kScoreMaxChunk + 1];
+  __shared__ int32_t s_pages[kScoreChunk + 1];
   __shared__ float s_col[2][4][kTileKeys];
+  __shared__ uint32_t s_hist[kHistBins];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -109,6 +216,7 @@ __global__ __launch_bounds__(kThreads) void score_kernel(ScoreParams p) {
   k_frag_offsets<D>(n, hh, kofs);
   const uint32_t ring_base = lds_addr(s_ring);
   const float inv_r = 1.f / static_cast<float>(p.R);
+  for (int b = tid; b < kHistBins; b += kThreads) s_hist[b] = 0u;
   __syncthreads();
 
   auto row_off = [&](int e) -> int64_t {
@@ -122,20 +230,59 @@ __global__ __launch_bounds__(kThreads) void score_kernel(ScoreParams p) {
   const int ntiles = (e1 - e0 + kTileKeys - 1) / kTileKeys;
   // sweep order: last tile first when p.reverse (re-reads what the exact pass read last)
   auto tile_of = [&](int t) { return p.reverse ? ntiles - 1 - t : t; };
+  // Tile loads are asm DMA (so the fragment reads below can be ordinary LDS
+  // loads the compiler schedules): a full tile of contiguous rows (contiguous
+  // layout, or 16-row-aligned in pages of >= 16 rows) takes the wave-uniform
+  // base + fixed per-lane offset form; other tiles load row by row.
+  constexpr int kKRowsPerInstr = kWave / G::kUnits;
+  uint32_t koff[G::kInstr];
+#pragma unroll
+  for (int j = 0; j < G::kInstr; ++j) {
+    const int slot = w * G::kInstr + j;
+    const int unit = slot * kWave + lane;
+    const int r = unit / G::kUnits, uk = (unit % G::kUnits) ^ (r & (G::kUnits - 1));
+    koff[j] = static_cast<uint32_t>(((r - slot * kKRowsPerInstr) * D + uk * 8) * 2);
+  }
+  const bool fast_rows = !paged || pshift >= 4;
+  const char* kbytes = reinterpret_cast<const char*>(p.kv.k);
+  auto row_bytes = [&](int pos) -> int64_t {
+    if (paged) {
+      const int64_t page = __builtin_amdgcn_readfirstlane(s_pages[(pos >> pshift) - page0]);
+      return ((((page * p.Hkv + h) << pshift) + (pos & pmask)) * D) * 2;
+    }
+    return ((seq_base + pos) * D) * 2;
+  };
   auto issue = [&](int t) {
     const int base = e0 + tile_of(t) * kTileKeys;
-    issue_tile<D, false>(s_ring + (t % kStages) * G::kBytes, nullptr, p.kv.k, nullptr,
-                         [&](int r) { return row_off(base + r); }, w, lane);
+    const uint32_t st = ring_base + (t % kStages) * G::kBytes;
+    if (fast_rows && base + kTileKeys <= e1 && (!paged || (base & 15) == 0)) {
+#pragma unroll
+      for (int j = 0; j < G::kInstr; ++j) {
+        const int slot = w * G::kInstr + j;
+        dma16(kbytes + row_bytes(base + slot * kKRowsPerInstr), koff[j], st + slot * 1024);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < G::kInstr; ++j) {
+        const int slot = w * G::kInstr + j;
+        const int unit = slot * kWave + lane;
+        const int r = unit / G::kUnits, uk = (unit % G::kUnits) ^ (r & (G::kUnits - 1));
+        dma16_sync(p.kv.k + row_off(base + r) + uk * 8, st + slot * 1024);
+      }
+    }
   };
   // column sums of tile t live in s_col[t & 1]; wave 0 reduces them over the
   // row blocks one iteration later (one barrier per tile)
   auto reduce_store = [&](int t) {
     const int e = e0 + tile_of(t) * kTileKeys + tid;
+    float sc = 0.f;
     if (e < e1) {
       float sum = 0.f;
       for (int ww = 0; ww < nrb; ++ww) sum += s_col[t & 1][ww][tid];
-      p.scores[static_cast<int64_t>(u) * p.stride + e] = sum * inv_r;
+      sc = sum * inv_r;
+      p.scores[static_cast<int64_t>(u) * p.stride + e] = sc;
     }
+    wave_hist_add(s_hist, __float_as_uint(sc) >> kHistShift, e < e1);
   };
 #pragma unroll
   for (int t = 0; t < kStages - 1; ++t)
@@ -148,19 +295,19 @@ __global__ __launch_bounds__(kThreads) void score_kernel(ScoreParams p) {
     const uint32_t k_base = ring_base + (t % kStages) * G::kBytes;
     if (computes) {
       f32x16 acc[2];
-      bf16x8 kf[kNks];
+      bf16x8 kf[2][kNks];
+      // both halves' fragment reads go out together; each product starts
+      // when its own fragments have landed
+      k_frags_lds<D>(k_base, kofs, kf[0]);
+      k_frags_lds<D>(k_base + 32 * G::kRowBytes, kofs, kf[1]);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[0][i] = 0.f;
-      k_frags<D, 0>(k_base, kofs, kf);
+      for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-      for (int ks = 0; ks < kNks; ++ks)
-        acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[ks], kf[ks], acc[0], 0, 0, 0);
+        for (int i = 0; i < 16; ++i) acc[kb][i] = 0.f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[1][i] = 0.f;
-      k_frags<D, 32 * G::kRowBytes>(k_base, kofs, kf);
-#pragma unroll
-      for (int ks = 0; ks < kNks; ++ks)
-        acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[ks], kf[ks], acc[1], 0, 0, 0);
+        for (int ks = 0; ks < kNks; ++ks)
+          acc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[ks], kf[kb][ks], acc[kb], 0, 0, 0);
+      }
       // S[row][key 32kb + n]; sum the probabilities of this wave's 32 rows
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -175,23 +322,37 @@ __global__ __launch_bounds__(kThreads) void score_kernel(ScoreParams p) {
   }
   __syncthreads();
   if (tid < kTileKeys) reduce_store(ntiles - 1);
+  __syncthreads();
+  store_hist_part<kThreads>(s_hist, p.hist_parts + (static_cast<int64_t>(u) * p.nchunk + c) * kHistBins);
 }
 
 // ---------------------------------------------------------------------------
 // top-k
 
+// Final selection work-group: 1024 threads; its register path holds up to
+// kFinalMax entries (8 per thread).
 constexpr int kTopkThreads = 1024;
-constexpr int kTopkChunk = 16384;
 constexpr int kTopkWaves = kTopkThreads / kWave;
+constexpr int kFinalMax = 8192;
+// Candidate pass: one 256-thread work-group per 4096-position chunk.
+constexpr int kLocalThreads = 256;
+constexpr int kLocalWaves = kLocalThreads / kWave;
+constexpr int kLocalChunk = 4096;
+constexpr int kLocalPer = kLocalChunk / kLocalThreads;
+// chunks per row the final pass can index (rows up to 2^25 positions)
+constexpr int kMaxLocalChunks = 8192;
 
 struct TopkParams {
   const float* scores;      // row u at scores + u * stride
   int64_t stride;
   int32_t* idx;             // [rows][k]
   int32_t k;
-  uint32_t* cand_bits;      // per row: nchunk * min(k, chunk) winners
+  uint32_t* hist;           // [rows][kHistBins]: the row's score histogram
+  uint32_t* hist_parts;     // standalone path: [rows][nchunk][kHistBins]
+  uint32_t* cand_bits;      // per row: chunk c's candidates at c * kLocalChunk
   int32_t* cand_pos;
-  int64_t cand_stride;
+  int64_t cand_stride;      // nchunk * kLocalChunk
+  int32_t* cand_count;      // [rows][nchunk]
   int32_t rows;
   int32_t rows_per_seq;     // row u belongs to sequence u / rows_per_seq
   int32_t n_uniform;        // >= 0: every row has this many entries; else lens
@@ -206,15 +367,17 @@ struct TopkShared {
   int32_t res[3];
 };
 
-// Sum of the 16 per-wave values in w[] (vector LDS reads, broadcast to all
+// Sum of the kW per-wave values in w[] (vector LDS reads, broadcast to all
 // lanes) and the part of it contributed by waves below `wv`.
+template <int kW>
 __device__ __forceinline__ void wave_totals(const int32_t* w, int wv, int& below, int& total) {
+  static_assert(kW % 4 == 0, "whole 16-byte reads");
   typedef int i4 __attribute__((ext_vector_type(4)));
   const i4* v = reinterpret_cast<const i4*>(w);
   below = 0;
   total = 0;
 #pragma unroll
-  for (int q = 0; q < kTopkWaves / 4; ++q) {
+  for (int q = 0; q < kW / 4; ++q) {
     const i4 x = v[q];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -224,60 +387,16 @@ __device__ __forceinline__ void wave_totals(const int32_t* w, int wv, int& below
   }
 }
 
-// Cross-lane steps through DPP (data-parallel primitives: a VALU operand
-// read from another lane of the same row of 16, or a row broadcast), which
-// cost one dependent VALU operation each instead of an LDS permute round trip.
-// dpp_ctrl codes: row_shr:n = 0x110 + n; row_bcast:15 = 0x142; row_bcast:31 = 0x143.
-// Lanes whose source is outside the row, or whose row is masked off, read 0.
-template <int kCtrl, int kRowMask>
-__device__ __forceinline__ uint32_t dpp_read(uint32_t v) {
-  return static_cast<uint32_t>(
-      __builtin_amdgcn_update_dpp(0, static_cast<int>(v), kCtrl, kRowMask, 0xf, false));
-}
-
-// Inclusive prefix sum over the 64 lanes of a wave: Hillis-Steele steps
-// 1, 2, 4, 8 inside each row of 16, then row 0's total is added to row 1 and
-// row 2's to row 3 (row_bcast:15), then lane 31's sum to rows 2 and 3.
-__device__ __forceinline__ int wave_inclusive_scan(int v) {
-  v += static_cast<int>(dpp_read<0x111, 0xf>(static_cast<uint32_t>(v)));
-  v += static_cast<int>(dpp_read<0x112, 0xf>(static_cast<uint32_t>(v)));
-  v += static_cast<int>(dpp_read<0x114, 0xf>(static_cast<uint32_t>(v)));
-  v += static_cast<int>(dpp_read<0x118, 0xf>(static_cast<uint32_t>(v)));
-  v += static_cast<int>(dpp_read<0x142, 0xa>(static_cast<uint32_t>(v)));
-  v += static_cast<int>(dpp_read<0x143, 0xc>(static_cast<uint32_t>(v)));
-  return v;
-}
-
-// Bitwise OR over the 64 lanes of a wave (the same steps as the scan; lane 63
-// ends with the OR of every lane), returned uniform.
-__device__ __forceinline__ uint32_t wave_or(uint32_t v) {
-  v |= dpp_read<0x111, 0xf>(v);
-  v |= dpp_read<0x112, 0xf>(v);
-  v |= dpp_read<0x114, 0xf>(v);
-  v |= dpp_read<0x118, 0xf>(v);
-  v |= dpp_read<0x142, 0xa>(v);
-  v |= dpp_read<0x143, 0xc>(v);
-  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 63));
-}
-
-// x + x[l ^ 16] + x[l ^ 32] + x[l ^ 48] in every lane: v_permlane16_swap and
-// v_permlane32_swap with both operands = x give x and its partner lane's value
-// (in either order), and the sum is symmetric.
-__device__ __forceinline__ uint32_t sum_over_rows(uint32_t x) {
-  const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
-  x = a[0] + a[1];
-  const auto b = __builtin_amdgcn_permlane32_swap(x, x, false, false);
-  return b[0] + b[1];
-}
-
-// Block-wide inclusive prefix sum of one int per thread; also returns the total.
+// Block-wide inclusive prefix sum of one int per thread (kW waves); also
+// returns the total. wsum: kW ints of LDS, 16-byte aligned.
+template <int kW = kTopkWaves>
 __device__ __forceinline__ int block_inclusive_scan(int v, int32_t* wsum, int& total) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   v = wave_inclusive_scan(v);
   if (lane == 63) wsum[wv] = v;
   __syncthreads();
   int before;
-  wave_totals(wsum, wv, before, total);
+  wave_totals<kW>(wsum, wv, before, total);
   __syncthreads();
   return v + before;
 }
@@ -637,143 +756,182 @@ __device__ __forceinline__ void load_run(const uint32_t* lds, uint32_t (&v)[kPer
   }
 }
 
-// Pass 1: one work-group per (row, chunk of kTopkChunk positions). A row that
-// fits in one chunk is finished here; otherwise the chunk's top min(k, len)
-// entries (under the same order) go to the candidate buffer in position order.
-__global__ __launch_bounds__(kTopkThreads) void topk_local_kernel(TopkParams p) {
-  __shared__ uint32_t s_data[kTopkChunk];
-  __shared__ TopkShared sh;
+__device__ __forceinline__ int topk_row_len(const TopkParams& p, int u) {
+  return p.n_uniform >= 0 ? p.n_uniform : p.lens.n[u / p.rows_per_seq];
+}
+
+// Histogram parts of user-supplied rows (the standalone top-k entry point;
+// the selection path builds them in the score sweep). One work-group per
+// (row, chunk): part c of the row in p.hist_parts.
+__global__ __launch_bounds__(kLocalThreads) void topk_hist_kernel(TopkParams p) {
+  __shared__ uint32_t s_hist[kHistBins];
   const int tid = threadIdx.x;
   const int u = blockIdx.x / p.nchunk, c = blockIdx.x % p.nchunk;
   if (u >= p.rows) return;
-  const int n = p.n_uniform >= 0 ? p.n_uniform : p.lens.n[u / p.rows_per_seq];
-  const int kk = min(p.k, n);
-  const int start = c * kTopkChunk;
-  if (start >= n) return;
-  const int len = min(kTopkChunk, n - start);
-  int32_t* out = p.idx + static_cast<int64_t>(u) * p.k;
+  const int n = topk_row_len(p, u);
+  const int start = c * kLocalChunk;
+  if (min(p.k, n) == n || start >= n) return;   // such rows need no histogram
+  const int len = min(kLocalChunk, n - start);
+  for (int b = tid; b < kHistBins; b += kLocalThreads) s_hist[b] = 0u;
+  __syncthreads();
   const float* src = p.scores + static_cast<int64_t>(u) * p.stride + start;
+  uint32_t v[kLocalPer];
+#pragma unroll
+  for (int j = 0; j < kLocalPer; ++j) v[j] = __float_as_uint(src[min(tid + j * kLocalThreads, len - 1)]);
+#pragma unroll
+  for (int j = 0; j < kLocalPer; ++j) wave_hist_add(s_hist, v[j] >> kHistShift, tid + j * kLocalThreads < len);
+  __syncthreads();
+  store_hist_part<kLocalThreads>(s_hist, p.hist_parts + (static_cast<int64_t>(u) * p.nchunk + c) * kHistBins);
+}
+
+// Candidate pass: one work-group per (row, chunk of kLocalChunk positions).
+// From the row histogram it finds the bin b* that holds the row's k-th
+// largest score; the chunk's entries in bins >= b* (every entry of the top-k
+// is one of them) go, in position order, to the chunk's candidate slice.
+// Rows whose every position is selected are finished here.
+__global__ __launch_bounds__(kLocalThreads) void topk_local_kernel(TopkParams p) {
+  __shared__ uint32_t s_data[kLocalChunk];
+  __shared__ __attribute__((aligned(16))) int32_t s_wsum[2][kLocalWaves];
+  __shared__ int32_t s_bin;
+  const int tid = threadIdx.x;
+  const int u = blockIdx.x / p.nchunk, c = blockIdx.x % p.nchunk;
+  if (u >= p.rows) return;
+  const int n = topk_row_len(p, u);
+  const int kk = min(p.k, n);
+  const int start = c * kLocalChunk;
+  if (start >= n) return;
+  const int len = min(kLocalChunk, n - start);
+  int32_t* out = p.idx + static_cast<int64_t>(u) * p.k;
   MAGE_TRACE_POINT(0);
 
   if (kk == n) {  // every position is selected
-    for (int i = tid; i < len; i += kTopkThreads) out[start + i] = start + i;
+    for (int i = tid; i < len; i += kLocalThreads) out[start + i] = start + i;
     if (c == 0)
-      for (int i = n + tid; i < p.k; i += kTopkThreads) out[i] = -1;
+      for (int i = n + tid; i < p.k; i += kLocalThreads) out[i] = -1;
     return;
   }
-  const int nch = (n + kTopkChunk - 1) / kTopkChunk;
-  const int kc_stride = min(kk, kTopkChunk);
-  const int kc = min(kk, len);
-  uint32_t* cb = p.cand_bits + static_cast<int64_t>(u) * p.cand_stride + static_cast<int64_t>(c) * kc_stride;
-  int32_t* cp = p.cand_pos + static_cast<int64_t>(u) * p.cand_stride + static_cast<int64_t>(c) * kc_stride;
-
   {
     // every thread issues all of its loads before the first use
-    constexpr int kPer = kTopkChunk / kTopkThreads;
-    uint32_t v[kPer];
+    const float* src = p.scores + static_cast<int64_t>(u) * p.stride + start;
+    uint32_t v[kLocalPer];
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) v[j] = __float_as_uint(src[min(tid + j * kTopkThreads, len - 1)]);
+    for (int j = 0; j < kLocalPer; ++j) v[j] = __float_as_uint(src[min(tid + j * kLocalThreads, len - 1)]);
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) s_data[tid + j * kTopkThreads] = v[j];
+    for (int j = 0; j < kLocalPer; ++j) s_data[tid + j * kLocalThreads] = v[j];
   }
-  __syncthreads();
-  constexpr int kPer = kTopkChunk / kTopkThreads;
-  uint32_t v[kPer];
-  load_run<kPer>(s_data, v);
-  MAGE_TRACE_POINT(1);
-  const int run0 = start + tid * kPer;
-  if (nch == 1) {
-    // a single chunk: its winners are the answer
-    uint32_t T;
-    int need;
-    int eq_total;
-    radix_select_sampled<kPer>(v, len, kk, sh, s_data, T, need, eq_total);
-    MAGE_TRACE_POINT(2);
-    ordered_compact_regs<kPer>(v, len, T, need, [&](int j) { return run0 + j; }, nullptr, out, sh, eq_total);
-    for (int i = kk + tid; i < p.k; i += kTopkThreads) out[i] = -1;
-    MAGE_TRACE_POINT(3);
-    return;
-  }
-  if (kc == len) {
-    for (int i = tid; i < len; i += kTopkThreads) {
-      cb[i] = s_data[i];
-      cp[i] = start + i;
-    }
-  } else {
-    uint32_t T;
-    int need;
-    int eq_total;
-#ifdef MAGE_TRACE_REPEAT
-    const uint64_t c0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
-#endif
-    radix_select_sampled<kPer>(v, len, kc, sh, s_data, T, need, eq_total);
-    MAGE_TRACE_POINT(2);
-#ifdef MAGE_TRACE_REPEAT
-    {
-      __syncthreads();
-      const uint64_t c1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
-      uint32_t T2;
-      int need2, eq2;
-      radix_select_sampled<kPer>(v, len, kc, sh, s_data, T2, need2, eq2);
-      __syncthreads();
-      const uint64_t c2 = __builtin_amdgcn_s_memtime(), r2 = __builtin_amdgcn_s_memrealtime();
-      if (tid == 0 && blockIdx.x < 4096) {
-        g_trace[4096 + blockIdx.x][0] = c1 - c0;
-        g_trace[4096 + blockIdx.x][1] = r1 - r0;
-        g_trace[4096 + blockIdx.x][2] = c2 - c1;
-        g_trace[4096 + blockIdx.x][3] = r2 - r1;
-        g_trace[4096 + blockIdx.x][4] = (T2 == T && need2 == need) ? 1 : 2;
+  // b*: thread t holds bins 1023-4t .. 1020-4t (the largest in thread 0); the
+  // scan of their counts is the number of scores at or above each bin
+  if (tid == 0) s_bin = 0;   // (a histogram that misses kk scores keeps everything)
+  {
+    typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+    const u4 h = reinterpret_cast<const u4*>(p.hist + static_cast<int64_t>(u) * kHistBins)[kHistBins / 4 - 1 - tid];
+    const int s4 = static_cast<int>(h[0] + h[1] + h[2] + h[3]);
+    int total;
+    const int incl = block_inclusive_scan<kLocalWaves>(s4, s_wsum[0], total);
+    int above = incl - s4;
+    if (above < kk && kk <= incl) {
+#pragma unroll
+      for (int e = 3; e >= 0; --e) {
+        const int cnt = static_cast<int>(h[e]);
+        if (above < kk && kk <= above + cnt) s_bin = kHistBins - 4 - 4 * tid + e;
+        above += cnt;
       }
     }
-#endif
-    ordered_compact_regs<kPer>(v, len, T, need, [&](int j) { return run0 + j; }, cb, cp, sh, eq_total);
   }
-  MAGE_TRACE_POINT(3);
+  __syncthreads();   // s_data and s_bin
+  MAGE_TRACE_POINT(1);
+  const uint32_t lo = static_cast<uint32_t>(s_bin) << kHistShift;   // smallest pattern of bin b*
+  uint32_t v[kLocalPer];
+  load_run<kLocalPer>(s_data, v);
+  const int nv = run_valid<kLocalPer>(len);
+  int nkeep = 0;
+#pragma unroll
+  for (int j = 0; j < kLocalPer; ++j) nkeep += (j < nv && v[j] >= lo);
+  int total;
+  int o = block_inclusive_scan<kLocalWaves>(nkeep, s_wsum[1], total) - nkeep;
+  uint32_t* cb = p.cand_bits + static_cast<int64_t>(u) * p.cand_stride + start;
+  int32_t* cp = p.cand_pos + static_cast<int64_t>(u) * p.cand_stride + start;
+  const int run0 = start + tid * kLocalPer;
+#pragma unroll
+  for (int j = 0; j < kLocalPer; ++j)
+    if (j < nv && v[j] >= lo) {
+      cb[o] = v[j];
+      cp[o] = run0 + j;
+      ++o;
+    }
+  if (tid == 0) p.cand_count[static_cast<int64_t>(u) * p.nchunk + c] = total;
+  MAGE_TRACE_POINT(2);
 }
 
-// Pass 2: one work-group per row with more than one chunk: the same selection
-// over the concatenated per-chunk winners (already in position order), so the
-// output comes out ascending.
+// Final pass: one work-group per row. The chunks' candidate slices, taken in
+// chunk order, are in position order; the kk-th largest among them is the
+// row's kk-th largest (all larger scores are candidates), and the ordered
+// compaction keeps ties at the lowest positions, so the output is ascending.
 __global__ __launch_bounds__(kTopkThreads) void topk_final_kernel(TopkParams p) {
-  __shared__ uint32_t s_data[kTopkChunk];
+  __shared__ uint32_t s_data[2 * kFinalMax];   // bits, then positions
+  __shared__ int32_t s_off[kMaxLocalChunks + 1];
   __shared__ TopkShared sh;
   const int tid = threadIdx.x;
   const int u = blockIdx.x;
   if (u >= p.rows) return;
-  const int n = p.n_uniform >= 0 ? p.n_uniform : p.lens.n[u / p.rows_per_seq];
+  const int n = topk_row_len(p, u);
   const int kk = min(p.k, n);
-  const int nch = (n + kTopkChunk - 1) / kTopkChunk;
-  if (kk == n || nch == 1) return;  // finished by the first pass
+  if (kk == n) return;  // finished by the candidate pass
   MAGE_TRACE_POINT(4);
   int32_t* out = p.idx + static_cast<int64_t>(u) * p.k;
-  const int kc_stride = min(kk, kTopkChunk);
-  const uint32_t* all_bits = p.cand_bits + static_cast<int64_t>(u) * p.cand_stride;
-  const int32_t* all_pos = p.cand_pos + static_cast<int64_t>(u) * p.cand_stride;
-  const int total = (nch - 1) * kc_stride + min(kc_stride, n - (nch - 1) * kTopkChunk);
+  const int nch = (n + kLocalChunk - 1) / kLocalChunk;
+  const int32_t* cnt = p.cand_count + static_cast<int64_t>(u) * p.nchunk;
+  // s_off[c] = candidates before chunk c (thread t sums a contiguous run of chunks)
+  {
+    const int per = (nch + kTopkThreads - 1) / kTopkThreads;
+    const int c0 = min(tid * per, nch), c1 = min(c0 + per, nch);
+    int mine = 0;
+    for (int c = c0; c < c1; ++c) mine += cnt[c];
+    int total;
+    int o = block_inclusive_scan(mine, sh.wsum, total) - mine;
+    for (int c = c0; c < c1; ++c) {
+      s_off[c] = o;
+      o += cnt[c];
+    }
+    if (tid == 0) s_off[nch] = total;
+  }
+  __syncthreads();
+  const int total = s_off[nch];
+  const uint32_t* bits = p.cand_bits + static_cast<int64_t>(u) * p.cand_stride;
+  const int32_t* pos = p.cand_pos + static_cast<int64_t>(u) * p.cand_stride;
+  // candidate i -> its index in the chunk slices (binary search over s_off)
+  auto slot_of = [&](int i) -> int64_t {
+    int lo = 0, hi = nch - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_off[mid] <= i) lo = mid; else hi = mid - 1;
+    }
+    return static_cast<int64_t>(lo) * kLocalChunk + (i - s_off[lo]);
+  };
   uint32_t T;
   int need;
-  if (total <= kTopkChunk / 2) {
-    // winners (bits, positions) fit in LDS: one batched pass from L2, then registers
-    constexpr int kPer = kTopkChunk / 2 / kTopkThreads;
+  if (total <= kFinalMax) {
+    constexpr int kPer = kFinalMax / kTopkThreads;
     {
       uint32_t vb[kPer];
       int32_t vp[kPer];
 #pragma unroll
       for (int j = 0; j < kPer; ++j) {
-        const int i = min(tid + j * kTopkThreads, total - 1);  // clamped; entries past total are never used
-        vb[j] = all_bits[i];
-        vp[j] = all_pos[i];
+        const int i = min(tid + j * kTopkThreads, total - 1);   // clamped; entries past total are never used
+        const int64_t sl = slot_of(i);
+        vb[j] = bits[sl];
+        vp[j] = pos[sl];
       }
 #pragma unroll
       for (int j = 0; j < kPer; ++j) {
         s_data[tid + j * kTopkThreads] = vb[j];
-        s_data[kTopkChunk / 2 + tid + j * kTopkThreads] = static_cast<uint32_t>(vp[j]);
+        s_data[kFinalMax + tid + j * kTopkThreads] = static_cast<uint32_t>(vp[j]);
       }
     }
     __syncthreads();
     uint32_t v[kPer], vpos[kPer];
     load_run<kPer>(s_data, v);
-    load_run<kPer>(s_data + kTopkChunk / 2, vpos);
+    load_run<kPer>(s_data + kFinalMax, vpos);
     MAGE_TRACE_POINT(5);
     int eq_total;
     radix_select_sampled<kPer>(v, total, kk, sh, s_data, T, need, eq_total);
@@ -781,9 +939,9 @@ __global__ __launch_bounds__(kTopkThreads) void topk_final_kernel(TopkParams p) 
     ordered_compact_regs<kPer>(v, total, T, need, [&](int j) { return static_cast<int32_t>(vpos[j]); }, nullptr,
                                out, sh, eq_total);
   } else {
-    auto get = [&](int i) { return all_bits[i]; };
+    auto get = [&](int i) { return bits[slot_of(i)]; };
     radix_select(get, total, kk, sh, T, need);
-    ordered_compact(get, total, T, need, [&](int i) { return all_pos[i]; }, nullptr, out, sh);
+    ordered_compact(get, total, T, need, [&](int i) { return pos[slot_of(i)]; }, nullptr, out, sh);
   }
   for (int i = kk + tid; i < p.k; i += kTopkThreads) out[i] = -1;
   MAGE_TRACE_POINT(7);

@@ -274,7 +274,7 @@ def test_kernel_timers_time_each_launch():
     gpu_select(inp, d)
     names = mage.last_launches()
     torch.cuda.synchronize()
-    assert names[:3] == ["exact_chunk_kernel", "exact_merge_kernel[exact]", "score_kernel"]
-    assert names[3] == "topk_local_kernel"
+    assert names == ["exact_chunk_kernel", "exact_merge_kernel[exact]", "score_kernel", "hist_reduce_kernel",
+                     "topk_local_kernel", "topk_final_kernel"]
     span = pairs[0][0].elapsed_time(pairs[len(names) - 1][1])
     assert span >= max(a.elapsed_time(b) for a, b in pairs[:len(names)]) > 0
