@@ -189,7 +189,7 @@ constexpr int kSparseStages = 2;
 
 // ---- workspace layout ------------------------------------------------------
 struct Layout {
-  size_t rowstat, part_ml, part_o, cand_bits, cand_pos, cand_count, hist, hist_parts, scores, total;
+  size_t rowstat, part_ml, part_o, cand_bits, cand_pos, cand_count, row_info, hist, hist_parts, scores, total;
   int64_t slots, cand_stride;
 };
 
@@ -213,6 +213,7 @@ Layout make_layout(const Dims& d, int64_t max_n, int64_t k) {
   L.cand_bits = take(U * L.cand_stride * 4);
   L.cand_pos = take(U * L.cand_stride * 4);
   L.cand_count = take(U * nchunk * 4);
+  L.row_info = take(U * 2 * 4);
   L.hist = take(U * kHistBins * 4);
   // histogram parts: one per score chunk (standalone top-k: one per 4096-entry chunk)
   L.hist_parts = take(U * cdiv(max_n, kScoreChunk) * kHistBins * 4);
@@ -398,6 +399,7 @@ mage_status launch_select(const Dims& d, const uint16_t* q, const KvArgs& kv, in
   tp.cand_pos = at<int32_t>(ws, L.cand_pos);
   tp.cand_stride = L.cand_stride;
   tp.cand_count = at<int32_t>(ws, L.cand_count);
+  tp.row_info = at<int32_t>(ws, L.row_info);
   tp.rows = static_cast<int32_t>(U);
   tp.rows_per_seq = d.Hkv;
   tp.n_uniform = kv.src.page_table ? -1 : kv.src.n_uniform;
@@ -661,6 +663,7 @@ mage_status mage_topk(int32_t rows, const float* scores, int64_t row_stride, con
   tp.cand_pos = at<int32_t>(workspace, L.cand_pos);
   tp.cand_stride = L.cand_stride;
   tp.cand_count = at<int32_t>(workspace, L.cand_count);
+  tp.row_info = at<int32_t>(workspace, L.row_info);
   tp.rows = rows;
   tp.rows_per_seq = 1;
   tp.n_uniform = lens ? -1 : n;

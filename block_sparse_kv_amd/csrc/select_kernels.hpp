@@ -77,13 +77,18 @@ __device__ __forceinline__ uint32_t sum_over_rows(uint32_t x) {
 }
 
 
-// Score histogram: bin of a non-negative fp32 score = its bit pattern >> 21
-// (sign, exponent, two mantissa bits: quarter-octave bins covering every
-// non-negative value). Bit patterns order like the values, so the bin of the
-// k-th largest score, read off a row's histogram, bounds the top-k: every
-// score in a higher bin is in it, every score in a lower bin is not.
+// Score histogram: bin of a non-negative fp32 score = its bit pattern >> 20
+// (exponent and three mantissa bits: eighth-octave bins over [0, 2); every
+// score >= 2 shares the top bin). Bit patterns order like the values, so the
+// bin of the k-th largest score, read off a row's histogram, bounds the
+// top-k: every score in a higher bin is in it, every score in a lower bin is
+// not.
 constexpr int kHistBins = 1024;
-constexpr int kHistShift = 21;
+constexpr int kHistShift = 20;
+
+__device__ __forceinline__ uint32_t hist_bin(uint32_t bits) {
+  return min(bits >> kHistShift, static_cast<uint32_t>(kHistBins - 1));
+}
 
 // hist[bin] += 1 for every lane with `active` (one LDS atomic per lane: the
 // LDS serializes same-bin lanes in hardware, which costs less than peeling
@@ -282,7 +287,7 @@ __global__ __launch_bounds__(kThreads) void score_kernel(ScoreParams p) {
       sc = sum * inv_r;
       p.scores[static_cast<int64_t>(u) * p.stride + e] = sc;
     }
-    wave_hist_add(s_hist, __float_as_uint(sc) >> kHistShift, e < e1);
+    wave_hist_add(s_hist, hist_bin(__float_as_uint(sc)), e < e1);
   };
 #pragma unroll
   for (int t = 0; t < kStages - 1; ++t)
@@ -353,6 +358,7 @@ struct TopkParams {
   int32_t* cand_pos;
   int64_t cand_stride;      // nchunk * kLocalChunk
   int32_t* cand_count;      // [rows][nchunk]
+  int32_t* row_info;        // [rows][2]: b* and the number of scores in bins above it
   int32_t rows;
   int32_t rows_per_seq;     // row u belongs to sequence u / rows_per_seq
   int32_t n_uniform;        // >= 0: every row has this many entries; else lens
@@ -488,7 +494,7 @@ __device__ void radix_select(Get data, int n, int kk, TopkShared& sh, uint32_t& 
 // thread its output offset, so the loop over the data has no barriers.
 template <class Get, class PosOf>
 __device__ void ordered_compact(Get data, int n, uint32_t T, int need, PosOf pos_of,
-                                uint32_t* out_bits, int32_t* out_pos, TopkShared& sh) {
+                                uint32_t* out_bits, int32_t* out_pos, TopkShared& sh, int cap) {
   const int tid = threadIdx.x;
   const int per = (n + kTopkThreads - 1) / kTopkThreads;
   const int i0 = min(tid * per, n), i1 = min(i0 + per, n);
@@ -508,8 +514,10 @@ __device__ void ordered_compact(Get data, int n, uint32_t T, int need, PosOf pos
     bool sel = x > T;
     if (x == T) sel = eq_seen++ < keep_eq;
     if (sel) {
-      out_pos[o] = pos_of(i);
-      if (out_bits) out_bits[o] = x;
+      if (o < cap) {
+        out_pos[o] = pos_of(i);
+        if (out_bits) out_bits[o] = x;
+      }
       ++o;
     }
   }
@@ -709,7 +717,8 @@ __device__ void radix_select_sampled(const uint32_t (&v)[kPer], int n, int kk, T
 // need, every such entry is kept and the scan of tie ranks is skipped.
 template <int kPer, class PosOf>
 __device__ void ordered_compact_regs(const uint32_t (&v)[kPer], int n, uint32_t T, int need, PosOf pos_of,
-                                     uint32_t* out_bits, int32_t* out_pos, TopkShared& sh, int eq_total = -1) {
+                                     uint32_t* out_bits, int32_t* out_pos, TopkShared& sh, int eq_total,
+                                     int cap) {
   const int nv = run_valid<kPer>(n);
   int n_eq = 0, n_gt = 0;
 #pragma unroll
@@ -734,8 +743,10 @@ __device__ void ordered_compact_regs(const uint32_t (&v)[kPer], int n, uint32_t 
     bool sel = v[j] > T;
     if (v[j] == T) sel = eq_seen++ < keep_eq;
     if (sel) {
-      out_pos[o] = pos_of(j);
-      if (out_bits) out_bits[o] = v[j];
+      if (o < cap) {   // (a consistent T and need select exactly cap entries)
+        out_pos[o] = pos_of(j);
+        if (out_bits) out_bits[o] = v[j];
+      }
       ++o;
     }
   }
@@ -779,7 +790,7 @@ __global__ __launch_bounds__(kLocalThreads) void topk_hist_kernel(TopkParams p) 
 #pragma unroll
   for (int j = 0; j < kLocalPer; ++j) v[j] = __float_as_uint(src[min(tid + j * kLocalThreads, len - 1)]);
 #pragma unroll
-  for (int j = 0; j < kLocalPer; ++j) wave_hist_add(s_hist, v[j] >> kHistShift, tid + j * kLocalThreads < len);
+  for (int j = 0; j < kLocalPer; ++j) wave_hist_add(s_hist, hist_bin(v[j]), tid + j * kLocalThreads < len);
   __syncthreads();
   store_hist_part<kLocalThreads>(s_hist, p.hist_parts + (static_cast<int64_t>(u) * p.nchunk + c) * kHistBins);
 }
@@ -821,7 +832,10 @@ __global__ __launch_bounds__(kLocalThreads) void topk_local_kernel(TopkParams p)
   }
   // b*: thread t holds bins 1023-4t .. 1020-4t (the largest in thread 0); the
   // scan of their counts is the number of scores at or above each bin
-  if (tid == 0) s_bin = 0;   // (a histogram that misses kk scores keeps everything)
+  if (tid == 0) {
+    s_bin = 0;   // (a histogram that misses kk scores keeps everything)
+    if (c == 0) p.row_info[2 * u] = -1;
+  }
   {
     typedef uint32_t u4 __attribute__((ext_vector_type(4)));
     const u4 h = reinterpret_cast<const u4*>(p.hist + static_cast<int64_t>(u) * kHistBins)[kHistBins / 4 - 1 - tid];
@@ -833,7 +847,13 @@ __global__ __launch_bounds__(kLocalThreads) void topk_local_kernel(TopkParams p)
 #pragma unroll
       for (int e = 3; e >= 0; --e) {
         const int cnt = static_cast<int>(h[e]);
-        if (above < kk && kk <= above + cnt) s_bin = kHistBins - 4 - 4 * tid + e;
+        if (above < kk && kk <= above + cnt) {
+          s_bin = kHistBins - 4 - 4 * tid + e;
+          if (c == 0) {
+            p.row_info[2 * u] = kHistBins - 4 - 4 * tid + e;
+            p.row_info[2 * u + 1] = above;
+          }
+        }
         above += cnt;
       }
     }
@@ -861,6 +881,59 @@ __global__ __launch_bounds__(kLocalThreads) void topk_local_kernel(TopkParams p)
     }
   if (tid == 0) p.cand_count[static_cast<int64_t>(u) * p.nchunk + c] = total;
   MAGE_TRACE_POINT(2);
+}
+
+// Selection inside bin b* (< kHistBins - 1) by one wave: the rem-th largest
+// (rem >= 1) of the m <= kWaveSelMax values in cand[] (all of them in bin b*,
+// so only their low kHistShift = 20 bits differ), in MSB-first radix passes of
+// 7, 7 and 6 bits over a wave-private LDS histogram (no work-group barriers).
+// Returns the value T, how many values equal to T are among the rem largest
+// (need), and how many values equal T (eq).
+constexpr int kWaveSelMax = 512;
+
+__device__ void wave_select_in_bin(const uint32_t* cand, int m, int rem, uint32_t bin_lo, uint32_t* whist,
+                                   uint32_t& T, int& need, int& eq) {
+  constexpr int kPer = kWaveSelMax / kWave;
+  const int lane = threadIdx.x & 63;
+  uint32_t c[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) c[j] = cand[min(lane + j * kWave, max(m - 1, 0))];
+  uint32_t prefix = 0, pmask = 0;
+  int cnt = 0;
+  static_assert(kHistShift == 20, "passes cover bits 19..0");
+#pragma unroll
+  for (int pass = 0; pass < 3; ++pass) {
+    const int width = pass < 2 ? 7 : 6, shift = pass == 0 ? 13 : (pass == 1 ? 6 : 0);
+    const uint32_t dmask = (1u << width) - 1u;
+    whist[2 * lane] = 0u;
+    whist[2 * lane + 1] = 0u;
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int j = 0; j < kPer; ++j)
+      if (lane + j * kWave < m && (c[j] & pmask) == prefix) atomicAdd(&whist[(c[j] >> shift) & dmask], 1u);
+    __builtin_amdgcn_wave_barrier();
+    // lane l holds digits 127-2l and 126-2l (largest digits in lane 0)
+    const int h0 = static_cast<int>(whist[127 - 2 * lane]), h1 = static_cast<int>(whist[126 - 2 * lane]);
+    const int incl = wave_inclusive_scan(h0 + h1), above = incl - h0 - h1;
+    const bool mine = above < rem && rem <= incl;
+    const int src = __builtin_ctzll(__ballot(mine));
+    int digit = 0, r2 = 0, c2 = 0;
+    if (mine) {
+      const bool first = rem <= above + h0;
+      digit = first ? 127 - 2 * lane : 126 - 2 * lane;
+      r2 = first ? rem - above : rem - above - h0;
+      c2 = first ? h0 : h1;
+    }
+    digit = __builtin_amdgcn_readlane(digit, src);
+    rem = __builtin_amdgcn_readlane(r2, src);
+    cnt = __builtin_amdgcn_readlane(c2, src);
+    prefix |= static_cast<uint32_t>(digit) << shift;
+    pmask |= dmask << shift;
+    __builtin_amdgcn_wave_barrier();
+  }
+  T = bin_lo | prefix;
+  need = rem;
+  eq = cnt;
 }
 
 // Final pass: one work-group per row. The chunks' candidate slices, taken in
@@ -934,14 +1007,47 @@ __global__ __launch_bounds__(kTopkThreads) void topk_final_kernel(TopkParams p) 
     load_run<kPer>(s_data + kFinalMax, vpos);
     MAGE_TRACE_POINT(5);
     int eq_total;
-    radix_select_sampled<kPer>(v, total, kk, sh, s_data, T, need, eq_total);
+    const int b_star = p.row_info[2 * u], above = p.row_info[2 * u + 1];
+    // the bin-b* candidates to LDS (s_data's first half is free again: every
+    // thread holds its entries in registers); when they are as many as the
+    // histogram says and few enough, one wave selects among them
+    const int nv = run_valid<kPer>(total);
+    int nb = 0;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) nb += (j < nv && static_cast<int>(hist_bin(v[j])) == b_star);
+    int mt;
+    int o = block_inclusive_scan(nb, sh.wsum, mt) - nb;
+    if (b_star >= 0 && b_star < kHistBins - 1 && mt == total - above && mt <= kWaveSelMax && above < kk &&
+        kk <= total) {
+#pragma unroll
+      for (int j = 0; j < kPer; ++j)
+        if (j < nv && static_cast<int>(hist_bin(v[j])) == b_star) s_data[o++] = v[j];
+      __syncthreads();
+      if (tid < kWave) {
+        uint32_t t;
+        int nd, eq;
+        wave_select_in_bin(s_data, mt, kk - above, static_cast<uint32_t>(b_star) << kHistShift, sh.hist, t, nd, eq);
+        if (tid == 0) {
+          sh.res[0] = static_cast<int32_t>(t);
+          sh.res[1] = nd;
+          sh.res[2] = eq;
+        }
+      }
+      __syncthreads();
+      T = static_cast<uint32_t>(sh.res[0]);
+      need = sh.res[1];
+      eq_total = sh.res[2];
+      __syncthreads();   // sh is reused by the compaction
+    } else {
+      radix_select_sampled<kPer>(v, total, kk, sh, s_data, T, need, eq_total);
+    }
     MAGE_TRACE_POINT(6);
     ordered_compact_regs<kPer>(v, total, T, need, [&](int j) { return static_cast<int32_t>(vpos[j]); }, nullptr,
-                               out, sh, eq_total);
+                               out, sh, eq_total, kk);
   } else {
     auto get = [&](int i) { return bits[slot_of(i)]; };
     radix_select(get, total, kk, sh, T, need);
-    ordered_compact(get, total, T, need, [&](int i) { return pos[slot_of(i)]; }, nullptr, out, sh);
+    ordered_compact(get, total, T, need, [&](int i) { return pos[slot_of(i)]; }, nullptr, out, sh, kk);
   }
   for (int i = kk + tid; i < p.k; i += kTopkThreads) out[i] = -1;
   MAGE_TRACE_POINT(7);
