@@ -38,6 +38,7 @@ struct AttnParams {
   int32_t nchunk;           // chunks per unit in the grid
   float scale_log2;         // scale * log2(e)
   SeqLens lens;             // paged layout: N_s per sequence
+  ChunkMap map;             // exact pass: work-group -> (unit, chunk)
 };
 
 struct MergeParams {
@@ -221,7 +222,8 @@ __global__ __launch_bounds__(kAttnThreads) void exact_chunk_kernel(AttnParams p)
   const int rb = w & 3, kh = w >> 2;
   const int hh = lane >> 5, n = lane & 31;
   const int units = p.S * p.Hkv;
-  const int u = blockIdx.x / p.nchunk, c = blockIdx.x % p.nchunk;
+  int u, c;
+  map_chunk(p.map, p.lens, p.S, p.Hkv, p.chunk, p.nchunk, blockIdx.x, u, c);
   if (u >= units) return;
   MAGE_TRACE_POINT(0);
   const int s = u / p.Hkv, h = u - s * p.Hkv;

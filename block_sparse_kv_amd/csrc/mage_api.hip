@@ -135,9 +135,22 @@ int exact_chunk_floor(int64_t units, int64_t max_n) {
 
 // Returns 0 when no chunk size satisfies both the workspace floor and the
 // per-work-group page table limit (paged layout with tiny pages).
-int exact_chunk(int64_t units, int64_t max_n, int64_t total_keys, int page_size) {
+// seq_n: per-sequence prefix lengths (S of them, each repeated for Hkv
+// units), or null when every unit has max_n keys. With unequal lengths the
+// last chunk of each unit is partial, so the chunk is grown (in steps of 64)
+// until the work-group count again fits the whole rounds.
+int exact_chunk(int64_t units, int64_t max_n, int64_t total_keys, int page_size, const int32_t* seq_n, int S,
+                int Hkv) {
   const int64_t rounds = std::max<int64_t>(1, cdiv(total_keys, kCus * kExactRoundKeys));
-  int64_t c = round_up(cdiv(total_keys, env_int("MAGE_EXACT_WGS", static_cast<int>(kCus * rounds))), 64);
+  const int64_t target = env_int("MAGE_EXACT_WGS", static_cast<int>(kCus * rounds));
+  int64_t c = round_up(cdiv(total_keys, target), 64);
+  auto wgs = [&](int64_t chunk) {
+    if (!seq_n) return units * cdiv(max_n, chunk);
+    int64_t w = 0;
+    for (int s = 0; s < S; ++s) w += cdiv(seq_n[s], chunk);
+    return w * Hkv;
+  };
+  while (wgs(c) > target && c < max_n) c += 64;
   const int64_t floor = exact_chunk_floor(units, max_n);
   c = std::max<int64_t>(c, floor);
   const int forced = env_int("MAGE_EXACT_CHUNK", 0);
@@ -247,6 +260,26 @@ struct KvArgs {
   int64_t total_keys;  // sum over sequences of N_s, times Hkv
 };
 
+// Work-group numbering over (unit, chunk) pairs; `grid` receives the number
+// of work-groups. Unequal lengths (paged layout) get the dense numbering.
+ChunkMap chunk_map(const KvArgs& kv, const Dims& d, int chunk, int64_t& grid) {
+  ChunkMap m;
+  std::memset(&m, 0, sizeof m);
+  if (!kv.src.page_table) {
+    grid = d.units * cdiv(kv.max_n, chunk);
+    return m;
+  }
+  m.on = 1;
+  int64_t acc = 0;
+  for (int s = 0; s < d.S; ++s) {
+    m.first[s] = static_cast<int32_t>(acc);
+    acc += cdiv(kv.lens.n[s], chunk) * d.Hkv;
+  }
+  m.first[d.S] = static_cast<int32_t>(acc);
+  grid = acc;
+  return m;
+}
+
 mage_status contiguous_kv(const Dims& d, const uint16_t* k, const uint16_t* v, int32_t n,
                           KvArgs& a) {
   if (!k || !v) return fail(MAGE_ERR_INVALID_ARG, "k_cache / v_cache is null");
@@ -288,6 +321,22 @@ mage_status paged_kv(const Dims& d, const mage_paged_kv* kv, KvArgs& a) {
   return MAGE_OK;
 }
 
+// Dense (row, chunk) numbering of the candidate pass when row lengths differ
+// (tp.n_uniform < 0): seqs groups of tp.rows_per_seq rows.
+ChunkMap topk_map(const TopkParams& tp, int seqs) {
+  ChunkMap m;
+  std::memset(&m, 0, sizeof m);
+  if (tp.n_uniform >= 0) return m;
+  m.on = 1;
+  int64_t acc = 0;
+  for (int s = 0; s < seqs; ++s) {
+    m.first[s] = static_cast<int32_t>(acc);
+    acc += cdiv(tp.lens.n[s], kLocalChunk) * tp.rows_per_seq;
+  }
+  m.first[seqs] = static_cast<int32_t>(acc);
+  return m;
+}
+
 // Rows longer than this are beyond the final pass's chunk table.
 constexpr int64_t kMaxTopkLen = static_cast<int64_t>(kMaxLocalChunks) * kLocalChunk;
 
@@ -296,7 +345,7 @@ constexpr int64_t kMaxTopkLen = static_cast<int64_t>(kMaxLocalChunks) * kLocalCh
 // else the score sweep has written them.
 mage_status launch_topk(const TopkParams& tp, const HistReduceParams& hr, hipStream_t stream,
                         bool build_parts) {
-  const int64_t wgs = static_cast<int64_t>(tp.rows) * tp.nchunk;
+  const int64_t wgs = tp.map.on ? tp.map.first[tp.rows / tp.rows_per_seq] : static_cast<int64_t>(tp.rows) * tp.nchunk;
   if (build_parts) {
     if (mage_status st = launch(kfn(topk_hist_kernel), "topk_hist_kernel", wgs, kLocalThreads, stream, tp);
         st != MAGE_OK)
@@ -318,8 +367,8 @@ mage_status launch_select(const Dims& d, const uint16_t* q, const KvArgs& kv, in
                           float* lse, int32_t* idx, float* scores, int64_t score_stride, void* ws,
                           const Layout& L, hipStream_t attn, hipStream_t sel, hipEvent_t idx_ready) {
   const int64_t U = d.units;
-  const int chunk = exact_chunk(U, kv.max_n, kv.total_keys,
-                                kv.src.page_table ? (1 << kv.src.page_shift) : 0);
+  const int chunk = exact_chunk(U, kv.max_n, kv.total_keys, kv.src.page_table ? (1 << kv.src.page_shift) : 0,
+                                kv.src.page_table ? kv.lens.n : nullptr, d.S, d.Hkv);
   if (chunk == 0) return fail(MAGE_ERR_UNSUPPORTED, "page_size too small for this prefix length");
   if (k > 0 && kv.max_n > kMaxTopkLen) return fail(MAGE_ERR_UNSUPPORTED, "top-k of a prefix longer than 2^25");
   const int nch = static_cast<int>(cdiv(kv.max_n, chunk));
@@ -339,8 +388,10 @@ mage_status launch_select(const Dims& d, const uint16_t* q, const KvArgs& kv, in
   ap.nchunk = nch;
   ap.scale_log2 = scale_log2;
   ap.lens = kv.lens;
+  int64_t exact_grid = 0;
+  ap.map = chunk_map(kv, d, chunk, exact_grid);
   if (mage_status st = launch(kfn(exact_chunk_kernel<D, kStagesFor<D>>), "exact_chunk_kernel",
-                              U * nch, kAttnThreads, attn, ap);
+                              exact_grid, kAttnThreads, attn, ap);
       st != MAGE_OK)
     return st;
 
@@ -384,8 +435,10 @@ mage_status launch_select(const Dims& d, const uint16_t* q, const KvArgs& kv, in
   sp.reverse = env_int("MAGE_SCORE_REVERSE", 1);
   sp.scale_log2 = scale_log2;
   sp.lens = kv.lens;
+  int64_t score_grid = 0;
+  sp.map = chunk_map(kv, d, sp.chunk, score_grid);
   if (mage_status st = launch(kfn(score_kernel<D, kScoreStagesFor<D>>), "score_kernel",
-                              U * sp.nchunk, kThreads, sel, sp);
+                              score_grid, kThreads, sel, sp);
       st != MAGE_OK)
     return st;
 
@@ -405,6 +458,7 @@ mage_status launch_select(const Dims& d, const uint16_t* q, const KvArgs& kv, in
   tp.n_uniform = kv.src.page_table ? -1 : kv.src.n_uniform;
   tp.nchunk = static_cast<int>(cdiv(kv.max_n, kLocalChunk));
   tp.lens = kv.lens;
+  tp.map = topk_map(tp, d.S);
   HistReduceParams hr{};
   hr.parts = sp.hist_parts;
   hr.hist = tp.hist;
@@ -669,6 +723,7 @@ mage_status mage_topk(int32_t rows, const float* scores, int64_t row_stride, con
   tp.n_uniform = lens ? -1 : n;
   tp.nchunk = static_cast<int>(cdiv(n, kLocalChunk));
   tp.lens = sl;
+  tp.map = topk_map(tp, rows);
   HistReduceParams hr{};
   hr.parts = tp.hist_parts;
   hr.hist = tp.hist;

@@ -27,6 +27,36 @@ struct SeqLens {
   int32_t n[kMaxSeqs];
 };
 
+// Dense work-group numbering over (unit, chunk) pairs when the units' lengths
+// differ (paged layout): the work-groups [first[s], first[s+1]) belong to
+// sequence s, which has Hkv units of cdiv(n_s, chunk) chunks each (unit-major).
+// A grid of first[S] work-groups then holds no empty (unit, chunk) slots,
+// whose dispatch would delay the real ones.
+struct ChunkMap {
+  int32_t first[kMaxSeqs + 1];
+  int32_t on;               // 0: uniform lengths, unit = wg / nchunk, chunk = wg % nchunk
+};
+
+__device__ __forceinline__ void map_chunk(const ChunkMap& m, const SeqLens& lens, int S, int Hkv, int chunk,
+                                          int nchunk, int wg, int& u, int& c) {
+  if (!m.on) {
+    u = wg / nchunk;
+    c = wg - u * nchunk;
+    return;
+  }
+  int lo = 0, hi = S - 1;   // the last sequence whose first work-group is <= wg
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (m.first[mid] <= wg) lo = mid;
+    else hi = mid - 1;
+  }
+  const int nch = (lens.n[lo] + chunk - 1) / chunk;
+  const int local = wg - m.first[lo];
+  const int h = local / nch;
+  u = lo * Hkv + h;
+  c = local - h * nch;
+}
+
 // KV row addressing shared by the exact pass, the score sweep and the sparse
 // step. Contiguous: [S][Hkv][N][d]. Paged: pool [P][Hkv][page][d] with
 // position p of sequence s in page table[s * max_pages + (p >> shift)].

@@ -152,6 +152,7 @@ struct ScoreParams {
   int32_t reverse;          // sweep tiles last-to-first
   float scale_log2;
   SeqLens lens;
+  ChunkMap map;             // work-group -> (unit, chunk)
 };
 
 // Positions per score work-group; sized so that two work-groups fit in one
@@ -170,7 +171,8 @@ __global__ __launch_bounds__(kThreads) void score_kernel(ScoreParams p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hh = lane >> 5, n = lane & 31;
-  const int u = blockIdx.x / p.nchunk, c = blockIdx.x % p.nchunk;
+  int u, c;
+  map_chunk(p.map, p.lens, p.S, p.Hkv, p.chunk, p.nchunk, blockIdx.x, u, c);
   const int s = u / p.Hkv, h = u - s * p.Hkv;
   const int ns = seq_len_of(p.kv, p.lens, s);
   const int e0 = c * p.chunk, e1 = min(e0 + p.chunk, ns);
@@ -364,6 +366,7 @@ struct TopkParams {
   int32_t n_uniform;        // >= 0: every row has this many entries; else lens
   int32_t nchunk;
   SeqLens lens;
+  ChunkMap map;             // candidate pass and histogram parts: work-group -> (row, chunk)
 };
 
 struct TopkShared {
@@ -777,7 +780,8 @@ __device__ __forceinline__ int topk_row_len(const TopkParams& p, int u) {
 __global__ __launch_bounds__(kLocalThreads) void topk_hist_kernel(TopkParams p) {
   __shared__ uint32_t s_hist[kHistBins];
   const int tid = threadIdx.x;
-  const int u = blockIdx.x / p.nchunk, c = blockIdx.x % p.nchunk;
+  int u, c;
+  map_chunk(p.map, p.lens, p.rows / p.rows_per_seq, p.rows_per_seq, kLocalChunk, p.nchunk, blockIdx.x, u, c);
   if (u >= p.rows) return;
   const int n = topk_row_len(p, u);
   const int start = c * kLocalChunk;
@@ -805,7 +809,8 @@ __global__ __launch_bounds__(kLocalThreads) void topk_local_kernel(TopkParams p)
   __shared__ __attribute__((aligned(16))) int32_t s_wsum[2][kLocalWaves];
   __shared__ int32_t s_bin;
   const int tid = threadIdx.x;
-  const int u = blockIdx.x / p.nchunk, c = blockIdx.x % p.nchunk;
+  int u, c;
+  map_chunk(p.map, p.lens, p.rows / p.rows_per_seq, p.rows_per_seq, kLocalChunk, p.nchunk, blockIdx.x, u, c);
   if (u >= p.rows) return;
   const int n = topk_row_len(p, u);
   const int kk = min(p.k, n);
