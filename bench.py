@@ -334,7 +334,7 @@ def run_bench(args):
         fill[0] += 1
         scratch.fill_(fill[0])
         if args.flush == "clean":
-            scratch.sum()   # reads the 1 GiB back: evicts with clean lines
+            scratch.view(torch.float32).sum()   # reads the 1 GiB back (no widening copy): clean lines
 
     if args.no_flush:
         args.flush = "none"
@@ -420,7 +420,7 @@ def run_bench(args):
     ex_med = statistics.median(ex_busy)
     exact_k = statistics.median(sel_k["exact_chunk_kernel"])
     score_k = statistics.median(sel_k["score_kernel"])
-    topk_names = [n for n in sel_k if n.startswith("topk")]
+    topk_names = [n for n in sel_k if n.startswith("topk") or n == "hist_reduce_kernel"]
     topk_k = sum(statistics.median(sel_k[n]) for n in topk_names)
     ntot = sum(w.seq_lens)
     block_us = statistics.mean(sel_busy) + (T - 1) * sp_mean
@@ -503,7 +503,7 @@ def run_bench(args):
 # ---- profile summaries -----------------------------------------------------------
 def _short(name: str) -> str:
     for key in ("exact_chunk_kernel", "sparse_attn_kernel", "exact_merge_kernel", "score_kernel",
-                "topk_local_kernel", "topk_final_kernel", "topk_hist_kernel", "hist_zero_kernel", "FillFunctor",
+                "topk_local_kernel", "topk_final_kernel", "topk_hist_kernel", "hist_reduce_kernel", "FillFunctor",
                 "neg_kernel", "reduce_kernel"):
         if key in name:
             return {"FillFunctor": "flush (fill)", "neg_kernel": "copy (neg)",
