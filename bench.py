@@ -104,6 +104,13 @@ def score_bytes(w: workloads.Workload) -> int:
     return w.num_seqs * w.block * w.num_q_heads * d * 2 + ntot * d * 2 + ntot * 4
 
 
+def block_bytes(w: workloads.Workload) -> int:
+    """Block attention: q and the block's K/V rows in bf16, the prefix O/lse read and the
+    merged O/lse written in fp32."""
+    S, B, Hq, Hkv, d = w.num_seqs, w.block, w.num_q_heads, w.num_kv_heads, w.head_dim
+    return S * B * (Hq * d * 2 + 2 * Hkv * d * 2 + 2 * Hq * (d + 1) * 4)
+
+
 def exact_flops(w: workloads.Workload) -> float:
     return 4.0 * w.block * w.num_q_heads * w.head_dim * sum(w.seq_lens)
 
@@ -168,6 +175,11 @@ class Runner:
         self.lse2 = torch.empty_like(self.lse)
         self.idx = torch.empty(S, w.num_kv_heads, w.k, dtype=torch.int32, device=dev)
         self.scores = torch.empty(S, w.num_kv_heads, w.max_seq_len, dtype=torch.float32, device=dev)
+        g = torch.Generator().manual_seed(w.seed + 7)
+        kb = torch.randn(S, w.num_kv_heads, B, d, generator=g).to(torch.bfloat16)
+        self.kb, self.vb = kb.to(dev), torch.randn(kb.shape, generator=g).to(torch.bfloat16).to(dev)
+        self.o3 = torch.empty_like(self.o)
+        self.lse3 = torch.empty_like(self.lse)
 
     def _call(self, timer, fn):
         cur = self.torch.cuda.current_stream()
@@ -216,6 +228,27 @@ class Runner:
             else:
                 self.mage.sparse_attn(q, self.k, self.v, self.idx, w.scale, o=self.o2,
                                       lse=self.lse2, workspace=self.ws)
+        self._call(timer, fn)
+
+    def block(self, t, timer=None):
+        """The block's own rows merged into the prefix result of the last sparse step."""
+        q = self.qs[t % len(self.qs)]
+        self._call(timer, lambda: self.mage.block_attn(q, self.kb, self.vb, self.o2, self.lse2, self.w.scale,
+                                                       o=self.o3, lse=self.lse3))
+
+    def sparse_block(self, t, timer=None):
+        """A later step with the block's own rows fused in as one more split."""
+        w = self.w
+        q = self.qs[t % len(self.qs)]
+
+        def fn():
+            if w.paged:
+                self.mage.sparse_block_attn_paged(q, self.kp, self.vp, self.table, self.lens, self.idx,
+                                                  self.kb, self.vb, w.scale, o=self.o3, lse=self.lse3,
+                                                  workspace=self.ws)
+            else:
+                self.mage.sparse_block_attn(q, self.k, self.v, self.idx, self.kb, self.vb, w.scale,
+                                            o=self.o3, lse=self.lse3, workspace=self.ws)
         self._call(timer, fn)
 
     def topk_only(self, timer=None):
@@ -375,6 +408,19 @@ def run_bench(args):
         warm_timers.append(tm)
     r.select()
     torch.cuda.synchronize()
+    blk_timers = []
+    for t in range(5):
+        r.sparse(t)
+        fl()
+        tm = KernelTimer(torch, 1)
+        r.block(t, tm)
+        blk_timers.append(tm)
+    fused_timers = []
+    for t in range(5):
+        fl()
+        tm = KernelTimer(torch, 2)
+        r.sparse_block(t, tm)
+        fused_timers.append(tm)
     tk_timers = []
     for _ in range(5):
         fl()
@@ -407,6 +453,8 @@ def run_bench(args):
     ex_busy = [t.busy_ms() * 1e3 for t in ex_timers]
     warm_busy = [t.busy_ms() * 1e3 for t in warm_timers]
     tk_busy = [t.busy_ms() * 1e3 for t in tk_timers]
+    blk_med = statistics.median([t.busy_ms() * 1e3 for t in blk_timers])
+    fused_med = statistics.median([t.busy_ms() * 1e3 for t in fused_timers])
     empty_us = statistics.median([a.elapsed_time(b) * 1e3 for a, b in empty])
 
     sp_mean = statistics.mean(sp_busy)
@@ -479,6 +527,17 @@ def run_bench(args):
                          "first_step_overhead": round(sel_med / ex_med - 1, 4),
                          "instrumented_span_us_median": round(statistics.median(sel_span), 1),
                          "event_pair_us_median": round(statistics.median([t.outer_ms() * 1e3 for t in sel_timers]), 1)},
+        "block_attn": {"gpu_us_median": us(blk_med), "bytes": block_bytes(w),
+                       "GBps": round(block_bytes(w) / (blk_med * 1e-6) / 1e9, 1),
+                       "sparse_plus_block_us": us(statistics.median(sp_busy) + blk_med),
+                       "fused_step_gpu_us_median": us(fused_med),
+                       "fused_step_kernels_us_median": {n: us(v) for n, v in
+                                                        ((n, statistics.median(v)) for n, v in
+                                                         by_kernel(fused_timers).items())},
+                       "note": "cold, not part of value: gpu_us_median = the block's queries over "
+                               "its own B rows merged into a sparse step's output through "
+                               "log-sum-exp (separate launch); fused_step = the sparse step with "
+                               "the block rows as one more split (one call)"},
         "speedup_vs_exact_per_step": round(ex_med / statistics.median(sp_busy), 2),
         "wall_s_timed_region": round(wall, 3),
         "flushes_in_timed_region": args.steps * T if args.flush != "none" else 0,
@@ -503,7 +562,8 @@ def run_bench(args):
 # ---- profile summaries -----------------------------------------------------------
 def _short(name: str) -> str:
     for key in ("exact_chunk_kernel", "sparse_attn_kernel", "exact_merge_kernel", "score_kernel",
-                "topk_local_kernel", "topk_final_kernel", "topk_hist_kernel", "hist_reduce_kernel", "FillFunctor",
+                "topk_local_kernel", "topk_final_kernel", "topk_hist_kernel", "hist_reduce_kernel",
+                "block_attn_kernel", "FillFunctor",
                 "neg_kernel", "reduce_kernel"):
         if key in name:
             return {"FillFunctor": "flush (fill)", "neg_kernel": "copy (neg)",

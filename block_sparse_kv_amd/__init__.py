@@ -79,9 +79,15 @@ def lib():
         L.mage_sparse_attn_paged.argtypes = [P(Dims), _vp, P(PagedKv), _vp, _i32, _vp, _vp, _vp,
                                              _sz, _vp]
         L.mage_topk.argtypes = [_i32, _vp, ctypes.c_int64, P(_i32), _i32, _i32, _vp, _vp, _sz, _vp]
+        L.mage_block_attn.argtypes = [P(Dims), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+        L.mage_sparse_block_attn.argtypes = [P(Dims), _vp, _vp, _vp, _i32, _vp, _i32, _vp, _vp, _vp, _vp,
+                                             _vp, _sz, _vp]
+        L.mage_sparse_block_attn_paged.argtypes = [P(Dims), _vp, P(PagedKv), _vp, _i32, _vp, _vp, _vp,
+                                                   _vp, _vp, _sz, _vp]
         for f in ("mage_workspace_init", "mage_select_exact", "mage_select_exact_paged",
                   "mage_exact_attn", "mage_exact_attn_paged",
-                  "mage_sparse_attn", "mage_sparse_attn_paged", "mage_topk"):
+                  "mage_sparse_attn", "mage_sparse_attn_paged", "mage_topk", "mage_block_attn",
+                  "mage_sparse_block_attn", "mage_sparse_block_attn_paged"):
             getattr(L, f).restype = ctypes.c_int
         L.mage_status_string.argtypes = [ctypes.c_int]
         L.mage_status_string.restype = ctypes.c_char_p
@@ -317,6 +323,78 @@ def sparse_attn_paged(q, k_pool, v_pool, page_table, seq_lens, idx, scale: float
     _check(lib().mage_sparse_attn_paged(ctypes.byref(dims), _bf16_ptr(q, "q"), ctypes.byref(kv),
                                         _ptr(idx), int(k), _ptr(o), _ptr(lse), _ptr(ws),
                                         ws.numel(), _stream(stream)), "mage_sparse_attn_paged")
+    return o, lse
+
+
+def _block_rows(q, Hkv, k_blk, v_blk):
+    S, B, _, d = q.shape
+    for t, name in ((k_blk, "k_blk"), (v_blk, "v_blk")):
+        if tuple(t.shape) != (S, Hkv, B, d):
+            raise ValueError(f"{name} must be [S][Hkv][B][d] = {(S, Hkv, B, d)}")
+    return _bf16_ptr(k_blk, "k_blk"), _bf16_ptr(v_blk, "v_blk")
+
+
+def sparse_block_attn(q, k_cache, v_cache, idx, k_blk, v_blk, scale: float, *, o=None, lse=None,
+                      workspace=None, stream=None):
+    """A later step over the idx rows of the prefix together with the block's own
+    rows k_blk/v_blk [S][Hkv][B][d], in one pass."""
+    S, B, Hq, d = q.shape
+    _, Hkv, N, _ = k_cache.shape
+    k = idx.shape[-1]
+    if idx.dtype != torch.int32 or not idx.is_contiguous() or tuple(idx.shape[:2]) != (S, Hkv):
+        raise ValueError("idx must be contiguous int32 [S][Hkv][k]")
+    kb, vb = _block_rows(q, Hkv, k_blk, v_blk)
+    dims = make_dims(q, Hkv, scale)
+    dev = q.device
+    o = _out(o, (S, B, Hq, d), torch.float32, dev)
+    lse = _out(lse, (S, B, Hq), torch.float32, dev)
+    ws = _ws_obj(workspace, dev).get(workspace_bytes(dims, N, k), stream)
+    _check(lib().mage_sparse_block_attn(ctypes.byref(dims), _bf16_ptr(q, "q"),
+                                        _bf16_ptr(k_cache, "k_cache"), _bf16_ptr(v_cache, "v_cache"), N,
+                                        _ptr(idx), int(k), kb, vb, _ptr(o), _ptr(lse), _ptr(ws),
+                                        ws.numel(), _stream(stream)), "mage_sparse_block_attn")
+    return o, lse
+
+
+def sparse_block_attn_paged(q, k_pool, v_pool, page_table, seq_lens, idx, k_blk, v_blk, scale: float, *,
+                            o=None, lse=None, workspace=None, stream=None):
+    """sparse_block_attn over a paged cache; idx holds logical positions."""
+    S, B, Hq, d = q.shape
+    Hkv = k_pool.shape[1]
+    k = idx.shape[-1]
+    if idx.dtype != torch.int32 or not idx.is_contiguous() or tuple(idx.shape[:2]) != (S, Hkv):
+        raise ValueError("idx must be contiguous int32 [S][Hkv][k]")
+    kb, vb = _block_rows(q, Hkv, k_blk, v_blk)
+    dims = make_dims(q, Hkv, scale)
+    kv, keep, lens = _paged(k_pool, v_pool, page_table, seq_lens)
+    dev = q.device
+    o = _out(o, (S, B, Hq, d), torch.float32, dev)
+    lse = _out(lse, (S, B, Hq), torch.float32, dev)
+    ws = _ws_obj(workspace, dev).get(workspace_bytes(dims, max(lens), k), stream)
+    _check(lib().mage_sparse_block_attn_paged(ctypes.byref(dims), _bf16_ptr(q, "q"), ctypes.byref(kv),
+                                              _ptr(idx), int(k), kb, vb, _ptr(o), _ptr(lse), _ptr(ws),
+                                              ws.numel(), _stream(stream)), "mage_sparse_block_attn_paged")
+    return o, lse
+
+
+def block_attn(q, k_blk, v_blk, o_prefix, lse_prefix, scale: float, *, o=None, lse=None, stream=None):
+    """The block's queries over the prefix part (o_prefix, lse_prefix from a
+    prefix pass) together with the block's own keys k_blk/v_blk [S][Hkv][B][d];
+    o / lse may be the prefix tensors themselves (in place)."""
+    S, B, Hq, d = q.shape
+    Hkv = k_blk.shape[1]
+    if tuple(k_blk.shape) != (S, Hkv, B, d) or tuple(v_blk.shape) != (S, Hkv, B, d):
+        raise ValueError("k_blk and v_blk must be [S][Hkv][B][d]")
+    for t, shape, name in ((o_prefix, (S, B, Hq, d), "o_prefix"), (lse_prefix, (S, B, Hq), "lse_prefix")):
+        if tuple(t.shape) != shape or t.dtype != torch.float32 or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"{name} must be a contiguous fp32 CUDA tensor of shape {shape}")
+    dims = make_dims(q, Hkv, scale)
+    dev = q.device
+    o = _out(o, (S, B, Hq, d), torch.float32, dev)
+    lse = _out(lse, (S, B, Hq), torch.float32, dev)
+    _check(lib().mage_block_attn(ctypes.byref(dims), _bf16_ptr(q, "q"), _bf16_ptr(k_blk, "k_blk"),
+                                 _bf16_ptr(v_blk, "v_blk"), _ptr(o_prefix), _ptr(lse_prefix), _ptr(o),
+                                 _ptr(lse), _stream(stream)), "mage_block_attn")
     return o, lse
 
 

@@ -39,6 +39,8 @@ struct AttnParams {
   float scale_log2;         // scale * log2(e)
   SeqLens lens;             // paged layout: N_s per sequence
   ChunkMap map;             // exact pass: work-group -> (unit, chunk)
+  const uint16_t* k_blk;    // sparse pass: bf16 [S][Hkv][B][d], the block's own rows, taken by
+  const uint16_t* v_blk;    //   the last chunk of every unit; null = prefix rows only
 };
 
 struct MergeParams {
@@ -654,6 +656,14 @@ __global__ __launch_bounds__(kSparseThreads) void sparse_attn_kernel(AttnParams 
   const int e0 = c * p.chunk + w * kpw;                 // this wave's entries [e0, e1)
   const int e1 = min(e0 + kpw, p.idx_k);
   const int cnt = max(0, e1 - e0);
+  // the last chunk of a unit also takes the block's own rows: at most one more
+  // 32-row tile per wave, rows [b0, b0 + nb) of this unit's B
+  int b0 = 0, nb = 0;
+  if (p.k_blk != nullptr && c == p.nchunk - 1) {
+    const int bpw = (p.B + kSparseWaves - 1) / kSparseWaves;   // <= kSparseTileKeys (B <= 128)
+    b0 = w * bpw;
+    nb = max(0, min(b0 + bpw, p.B) - b0);
+  }
   const bool paged = p.kv.page_table != nullptr;
   const int pshift = p.kv.page_shift, pmask = (1 << p.kv.page_shift) - 1;
   const int64_t seq_base = paged ? 0 : (static_cast<int64_t>(s) * p.Hkv + h) * p.kv.n_uniform;
@@ -705,16 +715,23 @@ __global__ __launch_bounds__(kSparseThreads) void sparse_attn_kernel(AttnParams 
 
   uint8_t* ring = s_ring + w * kWaveRing;
   const uint32_t ring_base = lds_addr(ring);
-  const int ntiles = (cnt + kSparseTileKeys - 1) / kSparseTileKeys;
+  const int ntp = (cnt + kSparseTileKeys - 1) / kSparseTileKeys;   // index-entry tiles
+  const int ntiles = ntp + (nb > 0 ? 1 : 0);
   auto issue = [&](int t) {
     uint8_t* st = ring + (t % kStages) * T::kStageBytes;
-    const int base = t * kSparseTileKeys;
-    issue_sparse_tile<D>(st, st + T::kKBytes, p.kv.k, p.kv.v,
-                         [&](int r) {
-                           const int row = tab[min(base + r, cnt - 1)];
-                           return static_cast<int64_t>(row < 0 ? fallback_row : row) * D;
-                         },
-                         lane);
+    if (t < ntp) {
+      const int base = t * kSparseTileKeys;
+      issue_sparse_tile<D>(st, st + T::kKBytes, p.kv.k, p.kv.v,
+                           [&](int r) {
+                             const int row = tab[min(base + r, cnt - 1)];
+                             return static_cast<int64_t>(row < 0 ? fallback_row : row) * D;
+                           },
+                           lane);
+    } else {
+      const int64_t row0 = static_cast<int64_t>(u) * p.B + b0;
+      issue_sparse_tile<D>(st, st + T::kKBytes, p.k_blk, p.v_blk,
+                           [&](int r) { return (row0 + min(r, nb - 1)) * D; }, lane);
+    }
   };
   f32x16 oacc[kNdb];
 #pragma unroll
@@ -737,7 +754,8 @@ __global__ __launch_bounds__(kSparseThreads) void sparse_attn_kernel(AttnParams 
     }
     if (t == 0) MAGE_TRACE_POINT(2);
     const int e = t * kSparseTileKeys + n;
-    const uint32_t okm = static_cast<uint32_t>(__ballot(e < cnt && tab[min(e, cnt - 1)] >= 0));
+    const bool ok = t < ntp ? e < cnt && tab[min(e, cnt - 1)] >= 0 : n < nb;
+    const uint32_t okm = static_cast<uint32_t>(__ballot(ok));
     const uint32_t st = ring_base + (t % kStages) * T::kStageBytes;
     attend_half<D, T::kVBlock>(st, st + v_lane, kofs, qf, okm, p.scale_log2, m_run, l_run, oacc, lane);
   }
@@ -874,6 +892,113 @@ __global__ __launch_bounds__(kThreads) void exact_merge_kernel(MergeParams p) {
     if (p.lse != nullptr) p.lse[row] = c2 * kLn2;
     if (p.rowstat != nullptr) p.rowstat[static_cast<int64_t>(u) * kMaxRows + r] = c2;
   }
+}
+
+// ---------------------------------------------------------------------------
+// Block attention: a block-diffusion layer's attention for the B tokens of the
+// current block is the softmax over the selected prefix rows together with
+// the block's own B rows, which every token of the block sees (the block is
+// denoised jointly; MAGE page, "Problem" and "Approach" select only the
+// prefix rows). The prefix part comes from the exact or sparse pass as a
+// normalised O and its log-sum-exp; this kernel attends the block's queries
+// to the block's keys and merges the two parts through their log-sum-exps:
+//   O = (e^{lse_p} O_p + e^{lse_b} O_b) / (e^{lse_p} + e^{lse_b}),
+//   lse = log(e^{lse_p} + e^{lse_b}).
+// One wave per (unit, 32-row block); the B <= 128 block keys stream through a
+// two-stage LDS ring of 32-key tiles.
+struct BlockParams {
+  const uint16_t* q;        // bf16 [S][B][Hq][d]
+  const uint16_t* k_blk;    // bf16 [S][Hkv][B][d]: the block's own keys
+  const uint16_t* v_blk;    // bf16 [S][Hkv][B][d]
+  const float* o_pre;       // fp32 [S][B][Hq][d]: normalised attention over the prefix rows
+  const float* lse_pre;     // fp32 [S][B][Hq]: its natural log-sum-exp (-inf: no prefix row)
+  float* o;                 // fp32 [S][B][Hq][d]; may be o_pre
+  float* lse;               // fp32 [S][B][Hq] or null; may be lse_pre
+  int32_t S, B, Hq, Hkv, G, R;
+  float scale_log2;         // scale * log2(e)
+};
+
+template <int D>
+__global__ __launch_bounds__(kWave) void block_attn_kernel(BlockParams p) {
+  using T = SparseTile<D>;
+  constexpr int kNdb = D / 32, kNks = D / 16;
+  static_assert(2 * T::kInstr < 64, "vmcnt is 6 bits");
+  __shared__ __attribute__((aligned(1024))) uint8_t s_ring[2 * T::kStageBytes];
+  const int lane = threadIdx.x, hh = lane >> 5, n = lane & 31;
+  const int nrb = (p.R + 31) >> 5;
+  const int u = blockIdx.x / nrb, rb = blockIdx.x - (blockIdx.x / nrb) * nrb;
+  if (u >= p.S * p.Hkv) return;
+  const int s = u / p.Hkv, h = u - s * p.Hkv;
+
+  bf16x8 qf[kNks];
+  const int r = 32 * rb + n;
+  {
+    if (r < p.R) {
+      const int b = r / p.G, gg = r - b * p.G;
+      const uint16_t* qrow = p.q + ((static_cast<int64_t>(s) * p.B + b) * p.Hq + h * p.G + gg) * D;
+#pragma unroll
+      for (int ks = 0; ks < kNks; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, load16(qrow + 16 * ks + 8 * hh));
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < kNks; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
+    }
+  }
+  wait_vmcnt<0>();   // Q in registers before the untracked tile loads start
+
+  const int64_t row0 = (static_cast<int64_t>(s) * p.Hkv + h) * p.B;   // first block row of this unit
+  const int ntiles = (p.B + kSparseTileKeys - 1) / kSparseTileKeys;
+  auto issue = [&](int t) {
+    uint8_t* st = s_ring + (t & 1) * T::kStageBytes;
+    issue_sparse_tile<D>(st, st + T::kKBytes, p.k_blk, p.v_blk,
+                         [&](int rr) { return (row0 + min(t * kSparseTileKeys + rr, p.B - 1)) * D; }, lane);
+  };
+  f32x16 oacc[kNdb];
+#pragma unroll
+  for (int db = 0; db < kNdb; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
+  float m_run = -__builtin_inff(), l_run = 0.f;
+  uint32_t kofs[kNks];
+  k_frag_offsets<D>(swap_bits23(n), hh, kofs);
+  const uint32_t ring_base = lds_addr(s_ring);
+  const uint32_t v_lane = T::kKBytes + vt_lane_offset(lane);
+  issue(0);
+  for (int t = 0; t < ntiles; ++t) {
+    if (t + 1 < ntiles) {
+      issue(t + 1);
+      wait_vmcnt<2 * T::kInstr>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    const uint32_t okm = static_cast<uint32_t>(__ballot(t * kSparseTileKeys + n < p.B));
+    const uint32_t st = ring_base + (t & 1) * T::kStageBytes;
+    attend_half<D, T::kVBlock>(st, st + v_lane, kofs, qf, okm, p.scale_log2, m_run, l_run, oacc, lane);
+    // the stage of tile t is refilled by the issue of tile t+2, after the
+    // next iteration's wait: its reads above have completed by then
+  }
+  l_run = wave_sum_pair(l_run);
+  if (r >= p.R) return;
+  const int b = r / p.G, gg = r - b * p.G;
+  const int64_t row = (static_cast<int64_t>(s) * p.B + b) * p.Hq + h * p.G + gg;
+  // log2 units: the block part's log-sum-exp is m + log2(l) (l >= 1)
+  const float lb = m_run + __log2f(l_run);
+  const float lp = p.lse_pre[row] * kLog2e;
+  const float M = fmaxf(lb, lp);
+  const float wp = fast_exp2(lp - M), wb = fast_exp2(lb - M);   // lp = -inf gives 0
+  const float inv = 1.f / (wp + wb);
+  const float cp = wp * inv, cb = wb * inv / l_run;
+  const float* opre = p.o_pre + row * D + 4 * hh;
+  float* orow = p.o + row * D + 4 * hh;
+#pragma unroll
+  for (int db = 0; db < kNdb; ++db)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(opre + 32 * db + 8 * i4);
+      *reinterpret_cast<f32x4*>(orow + 32 * db + 8 * i4) =
+          f32x4{cp * x[0] + cb * oacc[db][4 * i4], cp * x[1] + cb * oacc[db][4 * i4 + 1],
+                cp * x[2] + cb * oacc[db][4 * i4 + 2], cp * x[3] + cb * oacc[db][4 * i4 + 3]};
+    }
+  if (hh == 0 && p.lse != nullptr) p.lse[row] = (M + __log2f(wp + wb)) * kLn2;
 }
 
 }  // namespace mage

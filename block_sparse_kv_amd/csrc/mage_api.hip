@@ -480,10 +480,11 @@ mage_status launch_select(const Dims& d, const uint16_t* q, const KvArgs& kv, in
 template <int D>
 mage_status launch_sparse(const Dims& d, const uint16_t* q, const KvArgs& kv, const int32_t* idx,
                           int32_t k, float* o, float* lse, void* ws, const Layout& L,
-                          hipStream_t stream) {
+                          hipStream_t stream, const uint16_t* k_blk = nullptr,
+                          const uint16_t* v_blk = nullptr) {
   const int64_t U = d.units;
   const int chunk = sparse_chunk(U, d.nrb, k);
-  const int nch = static_cast<int>(cdiv(k, chunk));
+  const int nch = static_cast<int>(cdiv(k, chunk));   // block rows, if any, ride in the last chunk
   AttnParams ap{};
   ap.q = q;
   ap.kv = kv.src;
@@ -498,6 +499,8 @@ mage_status launch_sparse(const Dims& d, const uint16_t* q, const KvArgs& kv, co
   ap.nchunk = nch;
   ap.scale_log2 = d.scale * kLog2e;
   ap.lens = kv.lens;
+  ap.k_blk = k_blk;
+  ap.v_blk = v_blk;
   const int64_t grid = round_up(U * nch, 8) * d.nrb;
   if (mage_status st = launch(kfn(sparse_attn_kernel<D, kSparseStages>), "sparse_attn_kernel", grid,
                               kSparseThreads, stream, ap);
@@ -678,6 +681,72 @@ mage_status mage_sparse_attn_paged(const mage_dims* dims, const uint16_t* q, con
   if (mage_status st = check_ws(workspace, workspace_bytes, L); st != MAGE_OK) return st;
   return d.D == 128 ? launch_sparse<128>(d, q, kv, idx, k, o, lse, workspace, L, stream)
                     : launch_sparse<64>(d, q, kv, idx, k, o, lse, workspace, L, stream);
+}
+
+static mage_status block_rows_checks(const uint16_t* k_blk, const uint16_t* v_blk) {
+  if (!k_blk || !v_blk) return fail(MAGE_ERR_INVALID_ARG, "k_blk and v_blk must not be null");
+  if (!aligned(k_blk, 16) || !aligned(v_blk, 16))
+    return fail(MAGE_ERR_INVALID_ARG, "k_blk and v_blk must be 16-byte aligned");
+  return MAGE_OK;
+}
+
+mage_status mage_sparse_block_attn(const mage_dims* dims, const uint16_t* q, const uint16_t* k_cache,
+                                   const uint16_t* v_cache, int32_t seq_len, const int32_t* idx, int32_t k,
+                                   const uint16_t* k_blk, const uint16_t* v_blk, float* o, float* lse,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  CallScope scope;
+  Dims d;
+  if (mage_status st = sparse_common(dims, q, idx, k, o, lse, d); st != MAGE_OK) return st;
+  if (mage_status st = block_rows_checks(k_blk, v_blk); st != MAGE_OK) return st;
+  KvArgs kv;
+  if (mage_status st = contiguous_kv(d, k_cache, v_cache, seq_len, kv); st != MAGE_OK) return st;
+  const Layout L = make_layout(d, kv.max_n, k);
+  if (mage_status st = check_ws(workspace, workspace_bytes, L); st != MAGE_OK) return st;
+  return d.D == 128 ? launch_sparse<128>(d, q, kv, idx, k, o, lse, workspace, L, stream, k_blk, v_blk)
+                    : launch_sparse<64>(d, q, kv, idx, k, o, lse, workspace, L, stream, k_blk, v_blk);
+}
+
+mage_status mage_sparse_block_attn_paged(const mage_dims* dims, const uint16_t* q, const mage_paged_kv* kvp,
+                                         const int32_t* idx, int32_t k, const uint16_t* k_blk,
+                                         const uint16_t* v_blk, float* o, float* lse, void* workspace,
+                                         size_t workspace_bytes, hipStream_t stream) {
+  CallScope scope;
+  Dims d;
+  if (mage_status st = sparse_common(dims, q, idx, k, o, lse, d); st != MAGE_OK) return st;
+  if (mage_status st = block_rows_checks(k_blk, v_blk); st != MAGE_OK) return st;
+  KvArgs kv;
+  if (mage_status st = paged_kv(d, kvp, kv); st != MAGE_OK) return st;
+  const Layout L = make_layout(d, kv.max_n, k);
+  if (mage_status st = check_ws(workspace, workspace_bytes, L); st != MAGE_OK) return st;
+  return d.D == 128 ? launch_sparse<128>(d, q, kv, idx, k, o, lse, workspace, L, stream, k_blk, v_blk)
+                    : launch_sparse<64>(d, q, kv, idx, k, o, lse, workspace, L, stream, k_blk, v_blk);
+}
+
+mage_status mage_block_attn(const mage_dims* dims, const uint16_t* q, const uint16_t* k_blk,
+                            const uint16_t* v_blk, const float* o_prefix, const float* lse_prefix, float* o,
+                            float* lse, hipStream_t stream) {
+  CallScope scope;
+  Dims d;
+  if (mage_status st = check_dims(dims, d); st != MAGE_OK) return st;
+  if (!q || !k_blk || !v_blk || !o_prefix || !lse_prefix || !o)
+    return fail(MAGE_ERR_INVALID_ARG, "q, k_blk, v_blk, o_prefix, lse_prefix and o must not be null");
+  if (!aligned(q, 16) || !aligned(k_blk, 16) || !aligned(v_blk, 16) || !aligned(o_prefix, 16) || !aligned(o, 16))
+    return fail(MAGE_ERR_INVALID_ARG, "q, k_blk, v_blk, o_prefix and o must be 16-byte aligned");
+  if (!aligned(lse_prefix, 4) || (lse && !aligned(lse, 4)))
+    return fail(MAGE_ERR_INVALID_ARG, "lse_prefix and lse must be 4-byte aligned");
+  BlockParams bp{};
+  bp.q = q;
+  bp.k_blk = k_blk;
+  bp.v_blk = v_blk;
+  bp.o_pre = o_prefix;
+  bp.lse_pre = lse_prefix;
+  bp.o = o;
+  bp.lse = lse;
+  bp.S = d.S; bp.B = d.B; bp.Hq = d.Hq; bp.Hkv = d.Hkv; bp.G = d.G; bp.R = d.R;
+  bp.scale_log2 = d.scale * kLog2e;
+  const int64_t grid = d.units * d.nrb;
+  return d.D == 128 ? launch(kfn(block_attn_kernel<128>), "block_attn_kernel", grid, kWave, stream, bp)
+                    : launch(kfn(block_attn_kernel<64>), "block_attn_kernel", grid, kWave, stream, bp);
 }
 
 mage_status mage_topk(int32_t rows, const float* scores, int64_t row_stride, const int32_t* lens,

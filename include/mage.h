@@ -166,6 +166,56 @@ mage_status mage_sparse_attn_paged(const mage_dims* dims, const uint16_t* q,
                                    size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Block attention (the op a block-diffusion layer calls after the prefix
+ * pass): every query of the current block attends to the selected prefix
+ * rows and to all B rows of its own block, which the block's tokens share
+ * (they are denoised jointly; MAGE page, "Problem" and "Approach" select
+ * prefix rows only). The prefix part is given as the normalised output and
+ * natural log-sum-exp of mage_select_exact / mage_exact_attn /
+ * mage_sparse_attn; the block part is computed here, and the two are merged:
+ *   O = (e^{lse_p} O_p + e^{lse_b} O_b) / (e^{lse_p} + e^{lse_b}),
+ *   lse = log(e^{lse_p} + e^{lse_b}), with lse_p = -inf for rows that had no
+ *   prefix entry.
+ * q: bf16 [S][B][Hq][d] (as for the other entry points); k_blk, v_blk: bf16
+ * [S][Hkv][B][d], the block's own keys and values; o_prefix: fp32
+ * [S][B][Hq][d]; lse_prefix: fp32 [S][B][Hq]. Outputs o: fp32 [S][B][Hq][d]
+ * and lse: fp32 [S][B][Hq] (nullable). o may be o_prefix and lse may be
+ * lse_prefix (in place). All pointers are device memory, q/k_blk/v_blk/
+ * o_prefix/o 16-byte aligned, the lse arrays 4-byte aligned, else
+ * MAGE_ERR_INVALID_ARG; dims are checked as for the other entry points. No
+ * workspace.
+ */
+mage_status mage_block_attn(const mage_dims* dims, const uint16_t* q, const uint16_t* k_blk,
+                            const uint16_t* v_blk, const float* o_prefix, const float* lse_prefix,
+                            float* o, float* lse, hipStream_t stream);
+
+/*
+ * A later denoising step with the block's own rows, in one pass: the result
+ * mage_sparse_attn followed by mage_block_attn would give (attention of the
+ * block's queries over the k gathered prefix rows together with the block's B
+ * rows, MAGE page, "Approach", with the block rows read as above), but the
+ * block rows are one more 32-row tile for each wave of the last split of the
+ * sparse pass, so they fold into the same online softmax and split merge: no
+ * separate launch and no prefix O round trip. Arguments as for mage_sparse_attn / mage_sparse_attn_paged,
+ * plus k_blk, v_blk: bf16 [S][Hkv][B][d] device memory, 16-byte aligned, not
+ * null, else MAGE_ERR_INVALID_ARG. The workspace is the same as for
+ * mage_sparse_attn. A head with no valid index entry still sees its block
+ * rows.
+ */
+mage_status mage_sparse_block_attn(const mage_dims* dims, const uint16_t* q,
+                                   const uint16_t* k_cache, const uint16_t* v_cache,
+                                   int32_t seq_len, const int32_t* idx, int32_t k,
+                                   const uint16_t* k_blk, const uint16_t* v_blk, float* o,
+                                   float* lse, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream);
+
+mage_status mage_sparse_block_attn_paged(const mage_dims* dims, const uint16_t* q,
+                                         const mage_paged_kv* kv, const int32_t* idx, int32_t k,
+                                         const uint16_t* k_blk, const uint16_t* v_blk, float* o,
+                                         float* lse, void* workspace, size_t workspace_bytes,
+                                         hipStream_t stream);
+
+/*
  * Top-k of `rows` non-negative fp32 score rows (the selection step on its own):
  * row r has lens[r] valid entries (lens is HOST memory; null means all rows
  * have n entries) at scores + r * row_stride. Output idx [rows][k]: the

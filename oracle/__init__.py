@@ -57,11 +57,15 @@ def _load():
         lib.oracle_sparse_seq.argtypes = [ctypes.c_int] * 4 + [ctypes.c_double, _u16p, _u16p, _u16p,
                                                               ctypes.c_int, _i32p, ctypes.c_int, _dp, _dp]
         lib.oracle_topk.argtypes = [_dp, ctypes.c_int, ctypes.c_int, ctypes.c_int, _i32p]
+        lib.oracle_block_seq.argtypes = [ctypes.c_int] * 4 + [ctypes.c_double, _u16p, _u16p, _u16p,
+                                                             ctypes.c_int, _i32p, ctypes.c_int, _u16p,
+                                                             _u16p, _dp, _dp]
         lib.oracle_depage.argtypes = [_u16p, ctypes.c_int, ctypes.c_int, ctypes.c_int, _i32p,
                                       ctypes.c_int, _u16p]
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = ctypes.c_int
-        for f in (lib.oracle_exact_seq, lib.oracle_sparse_seq, lib.oracle_topk, lib.oracle_depage):
+        for f in (lib.oracle_exact_seq, lib.oracle_sparse_seq, lib.oracle_topk, lib.oracle_depage,
+                  lib.oracle_block_seq):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -170,6 +174,38 @@ def sparse(q, k, v, idx, scale: float, seq_lens=None):
     return O, lse
 
 
+def block(q, k, v, idx, k_blk, v_blk, scale: float, seq_lens=None):
+    """Block attention: the block's queries over the prefix rows idx[s][h][:]
+    (idx None: every prefix row) together with the block's own rows
+    k_blk/v_blk [S][Hkv][B][d], as one softmax over the union."""
+    lib = _load()
+    qn, kn, vn = _u16(q), _u16(k), _u16(v)
+    kbn, vbn = _u16(k_blk), _u16(v_blk)
+    S, B, Hq, d = qn.shape
+    _, Hkv, N, _ = kn.shape
+    if kbn.shape != (S, Hkv, B, d) or vbn.shape != (S, Hkv, B, d):
+        raise ValueError("k_blk and v_blk must be [S][Hkv][B][d]")
+    idn = None if idx is None else np.ascontiguousarray(np.asarray(idx, dtype=np.int32))
+    kk = 0 if idn is None else idn.shape[-1]
+    O = np.zeros((S, B, Hq, d))
+    lse = np.zeros((S, B, Hq))
+    for s in range(S):
+        n = N if seq_lens is None else int(seq_lens[s])
+        ks = np.ascontiguousarray(kn[s, :, :n])
+        vs = np.ascontiguousarray(vn[s, :, :n])
+        ids = None if idn is None else np.ascontiguousarray(idn[s])
+        Os = np.zeros((B, Hq, d))
+        ls = np.zeros((B, Hq))
+        _check(lib.oracle_block_seq(B, Hq, Hkv, d, float(scale), _ptr(np.ascontiguousarray(qn[s]), _u16p),
+                                    _ptr(ks, _u16p), _ptr(vs, _u16p), n,
+                                    None if ids is None else _ptr(ids, _i32p), kk,
+                                    _ptr(np.ascontiguousarray(kbn[s]), _u16p),
+                                    _ptr(np.ascontiguousarray(vbn[s]), _u16p), _ptr(Os, _dp), _ptr(ls, _dp)),
+               "block")
+        O[s], lse[s] = Os, ls
+    return O, lse
+
+
 def depage(pool, page_table, seq_lens, num_kv_heads: int | None = None):
     """Copy a page pool [P][Hkv][page][d] back to per-sequence [Hkv][N_s][d] uint16 arrays."""
     lib = _load()
@@ -202,6 +238,13 @@ def select_exact_paged(q, k_pool, v_pool, page_table, seq_lens, scale: float, to
     kc = _padded(depage(k_pool, page_table, seq_lens))
     vc = _padded(depage(v_pool, page_table, seq_lens))
     return select_exact(q, kc, vc, scale, topk_k, seq_lens=np.asarray(seq_lens))
+
+
+def block_paged(q, k_pool, v_pool, page_table, seq_lens, idx, k_blk, v_blk, scale: float):
+    """Block attention over a paged prefix: de-page, then as block()."""
+    kc = _padded(depage(k_pool, page_table, seq_lens))
+    vc = _padded(depage(v_pool, page_table, seq_lens))
+    return block(q, kc, vc, idx, k_blk, v_blk, scale, seq_lens=np.asarray(seq_lens))
 
 
 def sparse_paged(q, k_pool, v_pool, page_table, seq_lens, idx, scale: float):

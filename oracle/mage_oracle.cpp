@@ -29,6 +29,12 @@
 //    outside [0, N) are skipped; with no valid entry O = 0 and lse = -inf.
 //  * Paged caches are first copied back to contiguous rows (logical position
 //    p lives in page table[p / page] at slot p % page), then handled as above.
+//  * Block attention, the op a block-diffusion layer calls: the queries of the
+//    current block attend to the selected prefix rows (all of them, or the
+//    idx set) together with all B rows of their own block, which the block's
+//    tokens share (same page, "Problem": the block is denoised jointly and
+//    only the prefix rows are selected). Written as its definition: one
+//    softmax over the union of the two row sets, formulas as above.
 //
 // bf16 inputs are widened exactly (bits << 16 is the fp32 value).
 #include <algorithm>
@@ -190,6 +196,59 @@ int oracle_sparse_seq(int B, int Hq, int Hkv, int d, double scale,
         Vd[static_cast<size_t>(t) * d + i] = widen_bf16(vr[i]);
       }
     }
+    std::vector<const uint16_t*> qr(R);
+    std::vector<double*> orow(R), lrow(R);
+    for (int b = 0; b < B; ++b)
+      for (int g = 0; g < G; ++g) {
+        const int r = b * G + g, j = h * G + g;
+        qr[r] = Q + (static_cast<size_t>(b) * Hq + j) * d;
+        orow[r] = O + (static_cast<size_t>(b) * Hq + j) * d;
+        lrow[r] = lse + static_cast<size_t>(b) * Hq + j;
+      }
+    dense_attention(R, n, d, scale, qr, Kd, Vd, orow, lrow, nullptr);
+  }
+  return 0;
+}
+
+// Block attention of one sequence: softmax over the prefix rows idx[h][0..k)
+// (idx null: all N rows; entries outside [0, N) skipped) followed by the B
+// block rows Kb/Vb [Hkv][B][d]. Q bf16 [B][Hq][d]; K, V bf16 [Hkv][N][d].
+// Outputs O fp64 [B][Hq][d], lse fp64 [B][Hq].
+int oracle_block_seq(int B, int Hq, int Hkv, int d, double scale,
+                     const uint16_t* Q, const uint16_t* K, const uint16_t* V, int N,
+                     const int32_t* idx, int k, const uint16_t* Kb, const uint16_t* Vb,
+                     double* O, double* lse) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || N < 0 || k < 0 || Hq % Hkv) return -1;
+  const int G = Hq / Hkv, R = B * G;
+  std::vector<double> Kd, Vd;
+  for (int h = 0; h < Hkv; ++h) {
+    std::vector<const uint16_t*> krow, vrow;   // the union, prefix rows first
+    if (idx) {
+      for (int i = 0; i < k; ++i) {
+        const int32_t p = idx[static_cast<size_t>(h) * k + i];
+        if (p >= 0 && p < N) {
+          krow.push_back(K + (static_cast<size_t>(h) * N + p) * d);
+          vrow.push_back(V + (static_cast<size_t>(h) * N + p) * d);
+        }
+      }
+    } else {
+      for (int p = 0; p < N; ++p) {
+        krow.push_back(K + (static_cast<size_t>(h) * N + p) * d);
+        vrow.push_back(V + (static_cast<size_t>(h) * N + p) * d);
+      }
+    }
+    for (int t = 0; t < B; ++t) {
+      krow.push_back(Kb + (static_cast<size_t>(h) * B + t) * d);
+      vrow.push_back(Vb + (static_cast<size_t>(h) * B + t) * d);
+    }
+    const int n = static_cast<int>(krow.size());
+    Kd.assign(static_cast<size_t>(n) * d, 0.0);
+    Vd.assign(static_cast<size_t>(n) * d, 0.0);
+    for (int t = 0; t < n; ++t)
+      for (int i = 0; i < d; ++i) {
+        Kd[static_cast<size_t>(t) * d + i] = widen_bf16(krow[t][i]);
+        Vd[static_cast<size_t>(t) * d + i] = widen_bf16(vrow[t][i]);
+      }
     std::vector<const uint16_t*> qr(R);
     std::vector<double*> orow(R), lrow(R);
     for (int b = 0; b < B; ++b)

@@ -156,3 +156,46 @@ def test_calls_fail_loudly_without_a_gpu():
         mage.sparse_attn(q, torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16),
                          torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16),
                          torch.zeros(1, 1, 4, dtype=torch.int32), 0.125)
+
+
+def test_block_attn_argument_checks():
+    lib = mage.lib()
+    d = dims()
+    ok = [ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None]
+    # null inputs / output
+    for i in (1, 2, 3, 4, 5, 6):
+        args = list(ok)
+        args[i] = None
+        assert lib.mage_block_attn(*args) == mage.ERR_INVALID_ARG
+    # misaligned bf16 input and fp32 output
+    for i in (1, 4, 6):
+        args = list(ok)
+        args[i] = ctypes.c_void_p((1 << 20) + 4)
+        assert lib.mage_block_attn(*args) == mage.ERR_INVALID_ARG
+    # unsupported head dim, bad group
+    assert lib.mage_block_attn(ctypes.byref(dims(head_dim=96)), *ok[1:]) == mage.ERR_UNSUPPORTED
+    assert lib.mage_block_attn(ctypes.byref(dims(num_q_heads=30)), *ok[1:]) != mage.OK
+
+
+def test_sparse_block_attn_argument_checks():
+    lib = mage.lib()
+    d = dims()
+    # dims, q, k_cache, v_cache, seq_len, idx, k, k_blk, v_blk, o, lse, workspace, bytes, stream
+    ok = [ctypes.byref(d), FAKE, FAKE, FAKE, 1024, FAKE, 64, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None]
+    for i in (7, 8):
+        args = list(ok)
+        args[i] = None
+        assert lib.mage_sparse_block_attn(*args) == mage.ERR_INVALID_ARG
+        args[i] = ctypes.c_void_p((1 << 20) + 4)
+        assert lib.mage_sparse_block_attn(*args) == mage.ERR_INVALID_ARG
+    args = list(ok)
+    args[6] = 0
+    assert lib.mage_sparse_block_attn(*args) == mage.ERR_INVALID_ARG
+    # paged: dims, q, kv, idx, k, k_blk, v_blk, o, lse, workspace, bytes, stream
+    pk = mage.PagedKv()
+    okp = [ctypes.byref(d), FAKE, ctypes.byref(pk), FAKE, 64, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None]
+    for i in (5, 6):
+        args = list(okp)
+        args[i] = None
+        assert lib.mage_sparse_block_attn_paged(*args) == mage.ERR_INVALID_ARG
+    assert lib.mage_sparse_block_attn_paged(ctypes.byref(dims(head_dim=96)), *okp[1:]) == mage.ERR_UNSUPPORTED

@@ -278,3 +278,118 @@ def test_kernel_timers_time_each_launch():
                      "topk_local_kernel", "topk_final_kernel"]
     span = pairs[0][0].elapsed_time(pairs[len(names) - 1][1])
     assert span >= max(a.elapsed_time(b) for a, b in pairs[:len(names)]) > 0
+
+
+# ---- block attention: the block's queries over the prefix part and the block's own rows ----
+
+def _block_inputs(S, B, Hq, Hkv, d, N, k, seed):
+    g = torch.Generator().manual_seed(seed)
+    q = (torch.randn(S, B, Hq, d, generator=g) / d ** 0.5).to(torch.bfloat16)
+    kk = torch.randn(S, Hkv, N, d, generator=g).to(torch.bfloat16)
+    vv = torch.randn(S, Hkv, N, d, generator=g).to(torch.bfloat16)
+    kb = torch.randn(S, Hkv, B, d, generator=g).to(torch.bfloat16)
+    vb = torch.randn(S, Hkv, B, d, generator=g).to(torch.bfloat16)
+    rng = np.random.default_rng(seed)
+    idx = np.stack([np.stack([np.sort(rng.choice(N, size=k, replace=False)).astype(np.int32)
+                              for _ in range(Hkv)]) for _ in range(S)])
+    idx[0, 0, -1] = -1                       # a skipped entry
+    if Hkv > 1:
+        idx[-1, -1, :] = -1                  # a head with no prefix row: lse_prefix = -inf
+    return q, kk, vv, kb, vb, idx
+
+
+@pytest.mark.parametrize("S,B,Hq,Hkv,d,N,k", [
+    (1, 32, 32, 8, 128, 3000, 256),    # the 128K workload's block shape (prefix shortened)
+    (2, 5, 8, 2, 64, 700, 100),        # ragged rows: R = 20, one 32-row block, 5 block keys
+    (1, 64, 16, 16, 128, 2048, 300),   # MHA, B = 64: two 32-key tiles
+    (1, 128, 8, 8, 64, 500, 64),       # B = 128: four 32-key tiles, four row blocks
+    (1, 33, 2, 1, 128, 90, 90),        # B = 33: a second tile with one key
+])
+def test_block_attn_matches_oracle(S, B, Hq, Hkv, d, N, k):
+    scale = 1.0
+    q, kk, vv, kb, vb, idx = _block_inputs(S, B, Hq, Hkv, d, N, k, seed=S * 1000 + B * 7 + d)
+    Op, lp = oracle.sparse(q, kk, vv, idx, scale)          # the prefix part, from the oracle
+    O_ref, l_ref = oracle.block(q, kk, vv, idx, kb, vb, scale)
+    o_pre = torch.from_numpy(Op.astype(np.float32)).to(DEV)
+    lse_pre = torch.from_numpy(lp.astype(np.float32)).to(DEV)
+    o, lse = mage.block_attn(q.to(DEV), kb.to(DEV), vb.to(DEV), o_pre, lse_pre, scale)
+    torch.cuda.synchronize()
+    assert np.abs(o.cpu().numpy() - O_ref).max() <= 2e-3
+    assert np.abs(lse.cpu().numpy() - l_ref).max() <= 2e-3
+    # in place: the prefix tensors receive the result
+    o2, lse2 = mage.block_attn(q.to(DEV), kb.to(DEV), vb.to(DEV), o_pre, lse_pre, scale, o=o_pre, lse=lse_pre)
+    torch.cuda.synchronize()
+    assert torch.equal(o2.cpu(), o.cpu()) and torch.equal(lse2.cpu(), lse.cpu())
+
+
+def test_block_attn_after_the_gpu_prefix_pass():
+    # the end-to-end use: a sparse step's (o, lse) on the GPU merged with the
+    # block rows (the index set is the oracle's, so every expected value is too)
+    w = workloads.custom((2000,), 8, 2, 128, 16, 128, steps=2, seed=21)
+    inp = workloads.make_inputs(w, steps=2)
+    d = dev_inputs(inp)
+    idx = ora_select(inp)[3]
+    qt = d["q"][0]
+    o_pre, lse_pre = gpu_sparse(inp, d, qt, torch.from_numpy(np.ascontiguousarray(idx)).to(DEV))
+    g = torch.Generator().manual_seed(5)
+    kb = torch.randn(1, 2, 16, 128, generator=g).to(torch.bfloat16)
+    vb = torch.randn(1, 2, 16, 128, generator=g).to(torch.bfloat16)
+    o, lse = mage.block_attn(qt, kb.to(DEV), vb.to(DEV), o_pre, lse_pre, w.scale)
+    torch.cuda.synchronize()
+    O_ref, l_ref = oracle.block(inp.q_steps[0], inp.k, inp.v, idx, kb, vb, w.scale)
+    assert np.abs(o.cpu().numpy() - O_ref).max() <= 2e-3
+    assert np.abs(lse.cpu().numpy() - l_ref).max() <= 2e-3
+
+
+# ---- the fused later step: index rows and the block's own rows in one pass ----
+
+@pytest.mark.parametrize("S,B,Hq,Hkv,d,N,k", [
+    (1, 32, 32, 8, 128, 3000, 256),    # the 128K workload's block shape (prefix shortened)
+    (1, 32, 32, 8, 128, 6000, 1024),   # several index chunks, then the block chunk
+    (2, 5, 8, 2, 64, 700, 100),        # ragged rows; one sequence's head has no prefix row
+    (1, 64, 16, 16, 128, 2048, 300),   # MHA, B = 64: 16 block rows per wave
+    (1, 128, 8, 8, 64, 500, 64),       # B = 128: 32 block rows per wave, four row blocks
+    (1, 33, 2, 1, 128, 90, 90),        # B = 33: waves with 9, 9, 9 and 6 block rows
+    (1, 2, 4, 1, 128, 300, 40),        # B = 2: two waves without block rows
+])
+def test_sparse_block_attn_matches_oracle(S, B, Hq, Hkv, d, N, k):
+    scale = 1.0
+    q, kk, vv, kb, vb, idx = _block_inputs(S, B, Hq, Hkv, d, N, k, seed=S * 1000 + B * 7 + d + k)
+    O_ref, l_ref = oracle.block(q, kk, vv, idx, kb, vb, scale)
+    o, lse = mage.sparse_block_attn(q.to(DEV), kk.to(DEV), vv.to(DEV), torch.from_numpy(idx).to(DEV),
+                                    kb.to(DEV), vb.to(DEV), scale)
+    torch.cuda.synchronize()
+    assert np.abs(o.cpu().numpy() - O_ref).max() <= 2e-3
+    assert np.abs(lse.cpu().numpy() - l_ref).max() <= 2e-3
+
+
+def test_sparse_block_attn_paged_matches_oracle():
+    # ragged paged prefix, shuffled 16-token pages; the oracle's own index set
+    w = workloads.custom((53, 200, 1000), 8, 2, 64, 4, 64, paged=True, steps=2, name="paged_ragged", seed=31)
+    inp = workloads.make_inputs(w, steps=2)
+    d = dev_inputs(inp)
+    idx = np.ascontiguousarray(ora_select(inp)[3])
+    g = torch.Generator().manual_seed(9)
+    S = len(w.seq_lens)
+    kb = torch.randn(S, 2, 4, 64, generator=g).to(torch.bfloat16)
+    vb = torch.randn(S, 2, 4, 64, generator=g).to(torch.bfloat16)
+    qt = d["q"][0]
+    o, lse = mage.sparse_block_attn_paged(qt, d["k_pool"], d["v_pool"], d["table"], d["lens"],
+                                          torch.from_numpy(idx).to(DEV), kb.to(DEV), vb.to(DEV), w.scale)
+    torch.cuda.synchronize()
+    O_ref, l_ref = oracle.block_paged(inp.q_steps[0], inp.k_pool, inp.v_pool, inp.page_table, inp.seq_lens,
+                                      idx, kb, vb, w.scale)
+    assert np.abs(o.cpu().numpy() - O_ref).max() <= 2e-3
+    assert np.abs(lse.cpu().numpy() - l_ref).max() <= 2e-3
+
+
+def test_sparse_block_attn_equals_sparse_then_block():
+    # the fused pass and the two-pass composition agree to rounding on the same inputs
+    q, kk, vv, kb, vb, idx = _block_inputs(1, 32, 32, 8, 128, 4000, 512, seed=77)
+    args = [t.to(DEV) for t in (q, kk, vv)] + [torch.from_numpy(idx).to(DEV)]
+    o1, l1 = mage.sparse_block_attn(*args, kb.to(DEV), vb.to(DEV), 0.09)
+    op, lp = mage.sparse_attn(*args, 0.09)
+    o2, l2 = mage.block_attn(args[0], kb.to(DEV), vb.to(DEV), op, lp, 0.09)
+    torch.cuda.synchronize()
+    assert (o1 - o2).abs().max().item() <= 1e-4
+    assert (l1 - l2).abs().max().item() <= 1e-4

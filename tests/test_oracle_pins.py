@@ -267,3 +267,79 @@ def test_tiny_workload_plants_are_selected():
     _, _, sc, idx = oracle.select_exact(inp.q1, inp.k, inp.v, w.scale, w.k)
     assert set(inp.plants[(0, 0)].tolist()) <= set(idx[0, 0].tolist())
     assert abs(sc[0][0].sum() - 1) < 1e-12
+
+
+# ---- block attention (the block's queries over prefix rows + its own rows) ----
+
+def block_case(S, B, Hq, Hkv, d, N, seed):
+    q, k, v = rand_case(S, B, Hq, Hkv, d, N, seed)
+    g = torch.Generator().manual_seed(seed + 1)
+    kb = torch.randn(S, Hkv, B, d, generator=g).to(torch.bfloat16)
+    vb = torch.randn(S, Hkv, B, d, generator=g).to(torch.bfloat16)
+    return q, k, v, kb, vb
+
+
+@pytest.mark.parametrize("S,B,Hq,Hkv,d,N", [(1, 3, 4, 1, 64, 17), (2, 5, 8, 2, 128, 40), (1, 32, 4, 1, 64, 7)])
+def test_block_attention_is_attention_over_the_concatenation(S, B, Hq, Hkv, d, N):
+    q, k, v, kb, vb = block_case(S, B, Hq, Hkv, d, N, seed=S * 100 + B)
+    O, lse = oracle.block(q, k, v, None, kb, vb, 0.7)
+    kc, vc = torch.cat([k, kb], dim=2), torch.cat([v, vb], dim=2)
+    ref = sdpa_ref(q, kc, vc, 0.7).numpy()
+    assert np.abs(O - ref).max() < 1e-12
+    assert np.abs(lse - lse_ref(q, kc, 0.7).numpy()).max() < 1e-12
+
+
+def test_block_attention_with_a_selected_subset_is_masked_attention():
+    S, B, Hq, Hkv, d, N = 1, 4, 4, 2, 64, 50
+    q, k, v, kb, vb = block_case(S, B, Hq, Hkv, d, N, seed=9)
+    idx = np.array([[[3, 7, 7, 49, -1, 60]], [[0, 1, 2, 3, 4, 5]]], dtype=np.int32).reshape(S, Hkv, 6)
+    O, lse = oracle.block(q, k, v, idx, kb, vb, 1.3)
+    # mask over the concatenated rows: the selected prefix rows (a repeated
+    # index counts once per entry, as in the gather) and every block row
+    kc = torch.cat([k, kb], dim=2)
+    vc = torch.cat([v, vb], dim=2)
+    G = Hq // Hkv
+    mask = torch.full((S, Hq, B, N + B), -math.inf, dtype=torch.float64)
+    mask[..., N:] = 0.0
+    for h in range(Hkv):
+        for p in idx[0, h]:
+            if 0 <= p < N:
+                for g in range(G):
+                    if mask[0, h * G + g, 0, p] == -math.inf:
+                        mask[0, h * G + g, :, p] = 0.0
+                    else:   # a repeated row: double its weight
+                        mask[0, h * G + g, :, p] += math.log(2.0)
+    ref = sdpa_ref(q, kc, vc, 1.3, mask=mask).numpy()
+    assert np.abs(O - ref).max() < 1e-12
+
+
+def test_block_attention_merges_through_log_sum_exp():
+    # the prefix part and the block-only part, merged by their lse, give the union
+    S, B, Hq, Hkv, d, N = 1, 6, 4, 2, 128, 33
+    q, k, v, kb, vb = block_case(S, B, Hq, Hkv, d, N, seed=4)
+    idx = np.stack([np.arange(0, 33, 2, dtype=np.int32), np.arange(1, 34, 2, dtype=np.int32)])[None]
+    Op, lp = oracle.sparse(q, k, v, idx, 0.9)
+    empty = torch.zeros(S, Hkv, 0, d, dtype=torch.bfloat16)
+    Ob, lb = oracle.block(q, empty, empty, None, kb, vb, 0.9)
+    M = np.maximum(lp, lb)
+    wp, wb = np.exp(lp - M), np.exp(lb - M)
+    merged = (wp[..., None] * Op + wb[..., None] * Ob) / (wp + wb)[..., None]
+    O, lse = oracle.block(q, k, v, idx, kb, vb, 0.9)
+    assert np.abs(merged - O).max() < 1e-12
+    assert np.abs(M + np.log(wp + wb) - lse).max() < 1e-12
+
+
+def test_block_attention_closed_form_equal_logits():
+    # zero queries give equal logits: O is the mean of the block's V rows
+    S, B, Hq, Hkv, d = 1, 5, 2, 1, 64
+    q = torch.zeros(S, B, Hq, d, dtype=torch.bfloat16)
+    empty = torch.zeros(S, Hkv, 0, d, dtype=torch.bfloat16)
+    g = torch.Generator().manual_seed(3)
+    kb = torch.randn(S, Hkv, B, d, generator=g).to(torch.bfloat16)
+    vb = torch.randn(S, Hkv, B, d, generator=g).to(torch.bfloat16)
+    O, lse = oracle.block(q, empty, empty, None, kb, vb, 1.0)
+    mean_v = vb.double().mean(dim=2).numpy()          # [S][Hkv][d]
+    for b in range(B):
+        for j in range(Hq):
+            assert np.abs(O[0, b, j] - mean_v[0, 0]).max() < 1e-12
+    assert np.abs(lse - math.log(B)).max() < 1e-12
