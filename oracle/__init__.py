@@ -252,3 +252,93 @@ def sparse_paged(q, k_pool, v_pool, page_table, seq_lens, idx, scale: float):
     kc = _padded(depage(k_pool, page_table, seq_lens))
     vc = _padded(depage(v_pool, page_table, seq_lens))
     return sparse(q, kc, vc, idx, scale, seq_lens=np.asarray(seq_lens))
+
+
+# ---- anchor re-selection diagnostics: the mean-query score and set overlap ----
+#
+# Step-dLLM page (abstract): the sparse mask is refreshed at anchor steps and
+# reused in between; the diagnostic measures how much of each step's own top-k
+# set the set in use still covers. MAGE page ("Approach") motivates the block
+# query with the block-average query; read literally, the probability under the
+# mean query is an alternative to the averaged probability that the main path
+# uses. Both functions below are exact (rational arithmetic, plain sets).
+
+def _bf16_bits_of(x) -> int:
+    """Round an exact rational to the nearest bf16 (8 significant bits, ties to
+    even) and return its 16-bit pattern. x must be 0 or of magnitude in the
+    normal range [2^-126, 2^128)."""
+    from fractions import Fraction
+    x = Fraction(x)
+    if x == 0:
+        return 0
+    sign = 0x8000 if x < 0 else 0
+    a = -x if x < 0 else x
+    e = a.numerator.bit_length() - a.denominator.bit_length()   # 2^e <= a < 2^(e+2)
+    if a < Fraction(2) ** e:
+        e -= 1
+    elif a >= Fraction(2) ** (e + 1):
+        e += 1
+    if not -126 <= e < 128:
+        raise ValueError("value outside the bf16 normal range")
+    ulp = Fraction(2) ** (e - 7)
+    q, r = divmod(a, ulp)
+    half = ulp / 2
+    if r > half or (r == half and q % 2 == 1):
+        q += 1
+    v = float(q * ulp)                    # at most 9 significant bits: exact in fp32
+    return sign | (int(np.array(v, dtype=np.float32).view(np.uint32)) >> 16)
+
+
+def mean_query(q, num_kv_heads: int):
+    """The block's mean query per (sequence, KV head): the exact mean of the
+    B*G bf16 query rows that share KV head h (tokens b, heads h*G + g), rounded
+    once to bf16 (nearest, ties to even). q: bf16 [S][B][Hq][d]; returns a bf16
+    tensor [S][1][Hkv][d], the query of a one-token, one-head-per-group block."""
+    from fractions import Fraction
+    qn = _u16(q)
+    S, B, Hq, d = qn.shape
+    Hkv = int(num_kv_heads)
+    G = Hq // Hkv
+    vals = qn.astype(np.uint32) << 16
+    f = vals.view(np.float32).astype(np.float64)          # exact widening
+    out = np.zeros((S, 1, Hkv, d), dtype=np.uint16)
+    for s in range(S):
+        for h in range(Hkv):
+            rows = f[s, :, h * G:(h + 1) * G, :].reshape(B * G, d)
+            for e in range(d):
+                tot = sum((Fraction(float(v)) for v in rows[:, e]), Fraction(0))
+                out[s, 0, h, e] = _bf16_bits_of(tot / (B * G))
+    return torch.from_numpy(out.view(np.int16)).view(torch.bfloat16)
+
+
+def select_mean_query(q, k, v, scale: float, topk_k: int, seq_lens=None):
+    """Top-k by the probability under the mean query: step-1 selection with the
+    block replaced by its mean query (one row per KV head). Returns (scores,
+    idx) as select_exact does."""
+    Hkv = np.asarray(_u16(k)).shape[1]
+    qm = mean_query(q, Hkv)
+    _, _, scores, idx = select_exact(qm, k, v, scale, topk_k, seq_lens)
+    return scores, idx
+
+
+def select_mean_query_paged(q, k_pool, v_pool, page_table, seq_lens, scale: float, topk_k: int):
+    kc = _padded(depage(k_pool, page_table, seq_lens))
+    vc = _padded(depage(v_pool, page_table, seq_lens))
+    return select_mean_query(q, kc, vc, scale, topk_k, seq_lens=np.asarray(seq_lens))
+
+
+def idx_overlap(a, b):
+    """Per row of two index lists [rows][k] (entries < 0 are padding): the size
+    of the intersection of their valid entries, and the number of valid
+    entries of each. Returns three int64 arrays (common, count_a, count_b);
+    the recall of a against the reference b is common / count_b."""
+    a = np.asarray(a).reshape(-1, np.asarray(a).shape[-1])
+    b = np.asarray(b).reshape(-1, np.asarray(b).shape[-1])
+    common, ca, cb = [], [], []
+    for ra, rb in zip(a.tolist(), b.tolist()):
+        sa = {x for x in ra if x >= 0}
+        sb = {x for x in rb if x >= 0}
+        common.append(len(sa & sb))
+        ca.append(len(sa))
+        cb.append(len(sb))
+    return np.array(common), np.array(ca), np.array(cb)

@@ -343,3 +343,94 @@ def test_block_attention_closed_form_equal_logits():
         for j in range(Hq):
             assert np.abs(O[0, b, j] - mean_v[0, 0]).max() < 1e-12
     assert np.abs(lse - math.log(B)).max() < 1e-12
+
+
+# ---- anchor re-selection diagnostics: mean-query selection and set overlap ----
+
+def _bits(t):
+    return t.contiguous().view(torch.int16).numpy().view(np.uint16).astype(np.int64)
+
+
+def test_bf16_rounding_matches_torch_single_rounding_from_fp32():
+    # torch rounds fp32 -> bf16 to nearest, ties to even, in one step: for values
+    # that fp32 holds exactly the oracle's exact rounding must agree bit for bit
+    rng = np.random.default_rng(3)
+    x = (rng.standard_normal(4000) * 2.0 ** rng.integers(-40, 40, 4000)).astype(np.float32)
+    ties = (x.view(np.uint32) & np.uint32(0xFFFF0000)) | np.uint32(0x8000)      # exact midpoints
+    near = (x.view(np.uint32) & np.uint32(0xFFFF0000)) | np.uint32(0x7FFF)      # just below
+    for arr in (x, ties.view(np.float32), near.view(np.float32)):
+        want = _bits(torch.from_numpy(arr).to(torch.bfloat16))
+        got = np.array([oracle._bf16_bits_of(float(v)) for v in arr])
+        assert np.array_equal(got, want)
+
+
+def test_mean_query_special_cases():
+    g = torch.Generator().manual_seed(4)
+    # one row per group: the mean query is the query itself, bit for bit
+    q = torch.randn(2, 1, 3, 16, generator=g).to(torch.bfloat16)
+    assert torch.equal(oracle.mean_query(q, 3), q)
+    # identical rows: their mean is that row
+    row = torch.randn(1, 1, 1, 16, generator=g).to(torch.bfloat16)
+    assert torch.equal(oracle.mean_query(row.expand(1, 5, 4, 16).contiguous(), 2)[0, 0, 0], row[0, 0, 0])
+    # worked values: mean(1, 2) = 1.5; mean(1, 1, 1, 2^-8 + 1) = 1 + 2^-10 -> ties... below half: 1
+    q = bf16([[[[1.0], [2.0]]]]).reshape(1, 2, 1, 1)
+    assert oracle.mean_query(q, 1).float().item() == 1.5
+    q = bf16([1.0, 1.0, 1.0, 1.0 + 2 ** -7]).reshape(1, 4, 1, 1)
+    assert oracle.mean_query(q, 1).float().item() == 1.0            # 1 + 2^-9: below half an ulp
+    q = bf16([1.0, 1.0 + 2 ** -7]).reshape(1, 2, 1, 1)
+    assert oracle.mean_query(q, 1).float().item() == 1.0            # 1 + 2^-8: a tie, to even
+
+
+def test_mean_query_matches_float64_mean_where_fp32_holds_it():
+    # power-of-two row counts: the float64 mean is exact; where fp32 also holds
+    # it exactly, torch's fp32 -> bf16 rounding is the single rounding required
+    g = torch.Generator().manual_seed(5)
+    q = torch.randn(2, 8, 8, 32, generator=g).to(torch.bfloat16)    # B*G = 8 * 4 = 32 rows per group
+    got = oracle.mean_query(q, 2)
+    m = q.double().reshape(2, 8, 2, 4, 32).mean(dim=(1, 3))          # [S][Hkv][d]
+    m32 = m.float()
+    exact = (m32.double() == m)
+    assert exact.float().mean() > 0.9
+    ref = m32.to(torch.bfloat16)
+    assert torch.equal(got[:, 0][exact], ref[exact])
+    # permuting the rows of a group does not change it
+    perm = torch.randperm(8, generator=g)
+    assert torch.equal(oracle.mean_query(q[:, perm].contiguous(), 2), got)
+
+
+def test_mean_query_selection_is_top_k_of_the_mean_query_logits():
+    # with one query row, the softmax is monotone in the logit: the top-k by
+    # probability is the top-k of scale * qbar . k (lower position on ties)
+    q, k, v = rand_case(2, 8, 8, 2, 32, 300, seed=6)
+    qm = oracle.mean_query(q, 2)
+    scale = 0.3
+    scores, idx = oracle.select_mean_query(q, k, v, scale, 40)
+    logits = torch.einsum("shd,shnd->shn", qm[:, 0].double(), k.double()) * scale
+    for s in range(2):
+        for h in range(2):
+            order = sorted(range(300), key=lambda p: (-logits[s, h, p].item(), p))[:40]
+            assert idx[s, h].tolist() == sorted(order)
+            # the scores are that row's softmax probabilities
+            np.testing.assert_allclose(scores[s][h], torch.softmax(logits[s, h], 0).numpy(), rtol=1e-12,
+                                       atol=1e-15)
+    # one row per group: identical to the main selection
+    q1 = q[:, :1, ::4].contiguous()                                   # B = 1, G = 1
+    assert np.array_equal(oracle.select_mean_query(q1, k, v, scale, 40)[1],
+                          oracle.select_exact(q1, k, v, scale, 40)[3])
+
+
+def test_idx_overlap_counts():
+    a = [[0, 3, 5, 9, -1, -1], [1, 2, 3, 4, 5, 6], [-1] * 6, [7, 8, -1, -1, -1, -1]]
+    b = [[3, 4, 5, 6, 9, -1], [1, 2, 3, 4, 5, 6], [0, 1, -1, -1, -1, -1], [9, 10, 11, -1, -1, -1]]
+    c, ca, cb = oracle.idx_overlap(a, b)
+    assert c.tolist() == [3, 6, 0, 0]
+    assert ca.tolist() == [4, 6, 0, 2] and cb.tolist() == [5, 6, 2, 3]
+    c2, _, _ = oracle.idx_overlap(b, a)
+    assert c2.tolist() == c.tolist()                                  # symmetric
+    rng = np.random.default_rng(7)
+    for _ in range(20):
+        n, k = 200, int(rng.integers(1, 60))
+        ra = np.sort(rng.choice(n, k, replace=False))
+        rb = np.sort(rng.choice(n, k, replace=False))
+        c, _, _ = oracle.idx_overlap([ra], [rb])
+        assert c[0] == np.intersect1d(ra, rb).size
