@@ -259,6 +259,47 @@ class Runner:
                                                  idx=self.idx.view(S * Hkv, -1), workspace=self.ws))
 
 
+def anchor_diag(torch, mage, r, w, qs, sel_us, sparse_us):
+    """Recall of the set in use against every step's own top-k set under a
+    query drift (qs = Q_1..Q_T on the GPU), for anchor periods A (the set is
+    chosen again at steps 1, 1 + A, ...; A = T is selection at step 1 only),
+    and of the set chosen by the mean query at step 1. Every set and count
+    comes from the GPU (the own sets are the main selection run on each step's
+    queries)."""
+    T = w.steps
+
+    def select(q):
+        if w.paged:
+            return mage.select_exact_paged(q, r.kp, r.vp, r.table, r.lens, w.k, w.scale, want_scores=False,
+                                           workspace=r.ws)[2]
+        return mage.select_exact(q, r.k, r.v, w.k, w.scale, want_scores=False, workspace=r.ws)[2]
+
+    own = [select(q).clone() for q in qs]
+    if w.paged:
+        mq = mage.select_mean_query_paged(qs[0], r.kp, r.vp, r.table, r.lens, w.k, w.scale, workspace=r.ws)[0]
+    else:
+        mq = mage.select_mean_query(qs[0], r.k, r.v, w.k, w.scale, workspace=r.ws)[0]
+
+    def recall(a, b):
+        c, _, cb = mage.idx_overlap(a, b)
+        return (c.double() / cb.double().clamp(min=1)).cpu().numpy().ravel()
+
+    out = {"first_sparse_step_recall": round(float(recall(own[0], own[1]).mean()), 4), "anchor_periods": {}}
+    for A in sorted({T, 16, 8, 4, 2}, reverse=True):
+        if A > T:
+            continue
+        rec = np.concatenate([recall(own[((t) // A) * A], own[t]) for t in range(1, T)])
+        n_anchor = -(-T // A)
+        block_us = n_anchor * sel_us + (T - n_anchor) * sparse_us
+        out["anchor_periods"][str(A)] = {"mean_recall": round(float(rec.mean()), 4),
+                                         "min_recall": round(float(rec.min()), 4),
+                                         "anchors_per_block": n_anchor, "block_us": round(block_us, 1)}
+    mq_rec = np.concatenate([recall(mq, own[t]) for t in range(T)])
+    out["mean_query_step1_set"] = {"recall_vs_step1_own": round(float(recall(mq, own[0]).mean()), 4),
+                                   "mean_recall_over_steps": round(float(mq_rec.mean()), 4)}
+    return out
+
+
 def by_kernel(timers):
     """{kernel name: [durations in us]} over a list of finished timers."""
     out = {}
@@ -474,6 +515,17 @@ def run_bench(args):
     block_us = statistics.mean(sel_busy) + (T - 1) * sp_mean
     traffic = traffic_record(w.name)
     us = lambda v: round(v, 2)  # noqa: E731
+    t0 = time.perf_counter()
+    sp_med = statistics.median(sp_busy)
+    anchor = {"iid": anchor_diag(torch, mage, r, w, [r.q1] + r.qs[:T - 1], sel_med, sp_med),
+              "walk": anchor_diag(torch, mage, r, w,
+                                  [r.q1] + [q.to(dev) for q in workloads.walk_queries(w)], sel_med, sp_med),
+              "note": "recall = |set in use ∩ step's own top-k| / |own|, mean over (seq, KV head) and "
+                      "steps 2..T; iid: the workload's fresh per-step noise around Q1; walk: Q_t = "
+                      "Q_(t-1) + N(0, (sigma*sqrt(2/T))^2), a random walk from Q1; block_us = anchors x "
+                      "cold exact+select + the rest x cold sparse step"}
+    torch.cuda.synchronize()
+    log(f"[bench] anchor/recall diagnostic in {time.perf_counter() - t0:.1f} s")
     out = {
         "metric": METRIC,
         "value": round(1e6 / sp_mean, 1),
@@ -538,6 +590,7 @@ def run_bench(args):
                                "its own B rows merged into a sparse step's output through "
                                "log-sum-exp (separate launch); fused_step = the sparse step with "
                                "the block rows as one more split (one call)"},
+        "anchor_recall": anchor,
         "speedup_vs_exact_per_step": round(ex_med / statistics.median(sp_busy), 2),
         "wall_s_timed_region": round(wall, 3),
         "flushes_in_timed_region": args.steps * T if args.flush != "none" else 0,

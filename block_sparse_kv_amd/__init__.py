@@ -84,10 +84,15 @@ def lib():
                                              _vp, _sz, _vp]
         L.mage_sparse_block_attn_paged.argtypes = [P(Dims), _vp, P(PagedKv), _vp, _i32, _vp, _vp, _vp,
                                                    _vp, _vp, _sz, _vp]
+        L.mage_select_mean_query.argtypes = [P(Dims), _vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _sz, _vp]
+        L.mage_select_mean_query_paged.argtypes = [P(Dims), _vp, P(PagedKv), _i32, _vp, _vp, _vp, _sz, _vp]
+        L.mage_idx_overlap.argtypes = [_i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp]
+        L.mage_mean_query.argtypes = [P(Dims), _vp, _vp, _vp]
         for f in ("mage_workspace_init", "mage_select_exact", "mage_select_exact_paged",
                   "mage_exact_attn", "mage_exact_attn_paged",
                   "mage_sparse_attn", "mage_sparse_attn_paged", "mage_topk", "mage_block_attn",
-                  "mage_sparse_block_attn", "mage_sparse_block_attn_paged"):
+                  "mage_sparse_block_attn", "mage_sparse_block_attn_paged", "mage_select_mean_query",
+                  "mage_select_mean_query_paged", "mage_idx_overlap", "mage_mean_query"):
             getattr(L, f).restype = ctypes.c_int
         L.mage_status_string.argtypes = [ctypes.c_int]
         L.mage_status_string.restype = ctypes.c_char_p
@@ -252,6 +257,69 @@ def select_exact_paged(q, k_pool, v_pool, page_table, seq_lens, k: int, scale: f
     if idx_ready is not None:
         idx_ready.record(select_stream if select_stream is not None else torch.cuda.current_stream())
     return o, lse, idx, scores
+
+
+def mean_query(q, num_kv_heads: int, *, out=None, stream=None):
+    """The block's mean query per KV head, rounded once to bf16: [S][1][Hkv][d]."""
+    S, B, Hq, d = q.shape
+    dims = make_dims(q, num_kv_heads, 1.0)
+    out = _out(out, (S, 1, num_kv_heads, d), torch.bfloat16, q.device)
+    _check(lib().mage_mean_query(ctypes.byref(dims), _bf16_ptr(q, "q"), _bf16_ptr(out, "out"), _stream(stream)),
+           "mage_mean_query")
+    return out
+
+
+def select_mean_query(q, k_cache, v_cache, k: int, scale: float, *, idx=None, scores=None,
+                      want_scores=False, workspace=None, stream=None):
+    """Top-k by the probability under the block's mean query (one bf16 row per
+    KV head). Returns (idx int32 [S][Hkv][k], scores fp32 [S][Hkv][N] or None)."""
+    S, B, Hq, d = q.shape
+    _, Hkv, N, _ = k_cache.shape
+    dims = make_dims(q, Hkv, scale)
+    dev = q.device
+    idx = _out(idx, (S, Hkv, k), torch.int32, dev)
+    if want_scores or scores is not None:
+        scores = _out(scores, (S, Hkv, N), torch.float32, dev)
+    ws = _ws_obj(workspace, dev).get(workspace_bytes(dims, N, k), stream)
+    _check(lib().mage_select_mean_query(ctypes.byref(dims), _bf16_ptr(q, "q"), _bf16_ptr(k_cache, "k_cache"),
+                                        _bf16_ptr(v_cache, "v_cache"), N, int(k), _ptr(idx), _ptr(scores),
+                                        _ptr(ws), ws.numel(), _stream(stream)), "mage_select_mean_query")
+    return idx, scores
+
+
+def select_mean_query_paged(q, k_pool, v_pool, page_table, seq_lens, k: int, scale: float, *, idx=None,
+                            scores=None, want_scores=False, workspace=None, stream=None):
+    """select_mean_query over a paged cache; scores fp32 [S][Hkv][max(seq_lens)]."""
+    S, B, Hq, d = q.shape
+    Hkv = k_pool.shape[1]
+    dims = make_dims(q, Hkv, scale)
+    kv, keep, lens = _paged(k_pool, v_pool, page_table, seq_lens)
+    dev = q.device
+    idx = _out(idx, (S, Hkv, k), torch.int32, dev)
+    if want_scores or scores is not None:
+        scores = _out(scores, (S, Hkv, max(lens)), torch.float32, dev)
+    ws = _ws_obj(workspace, dev).get(workspace_bytes(dims, max(lens), k), stream)
+    _check(lib().mage_select_mean_query_paged(ctypes.byref(dims), _bf16_ptr(q, "q"), ctypes.byref(kv), int(k),
+                                              _ptr(idx), _ptr(scores), _ptr(ws), ws.numel(), _stream(stream)),
+           "mage_select_mean_query_paged")
+    return idx, scores
+
+
+def idx_overlap(a, b, *, stream=None):
+    """Per row of two int32 index tensors [..., k] in idx form: (common, count_a,
+    count_b) int32 tensors; the recall of a against b is common / count_b."""
+    if a.shape != b.shape or a.dtype != torch.int32 or b.dtype != torch.int32:
+        raise ValueError("a and b must be int32 tensors of one shape")
+    if not (a.is_cuda and b.is_cuda and a.is_contiguous() and b.is_contiguous()):
+        raise ValueError("a and b must be contiguous CUDA tensors")
+    k = a.shape[-1]
+    rows = a.numel() // k
+    common = torch.empty(a.shape[:-1], dtype=torch.int32, device=a.device)
+    ca = torch.empty_like(common)
+    cb = torch.empty_like(common)
+    _check(lib().mage_idx_overlap(rows, k, _ptr(a), _ptr(b), _ptr(common), _ptr(ca), _ptr(cb),
+                                  _stream(stream)), "mage_idx_overlap")
+    return common, ca, cb
 
 
 def exact_attn(q, k_cache, v_cache, scale: float, *, o=None, lse=None, workspace=None, stream=None):

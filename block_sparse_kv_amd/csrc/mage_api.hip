@@ -11,6 +11,7 @@
 
 #include "../../include/mage.h"
 #include "attn_kernels.hpp"
+#include "diag_kernels.hpp"
 #include "select_kernels.hpp"
 
 namespace {
@@ -202,7 +203,9 @@ constexpr int kSparseStages = 2;
 
 // ---- workspace layout ------------------------------------------------------
 struct Layout {
-  size_t rowstat, part_ml, part_o, cand_bits, cand_pos, cand_count, row_info, hist, hist_parts, scores, total;
+  size_t rowstat, part_ml, part_o, cand_bits, cand_pos, cand_count, row_info, hist, hist_parts, scores;
+  size_t qbar, qbar_o;   // mean-query selection: the mean query and its (unused) attention output
+  size_t total;
   int64_t slots, cand_stride;
 };
 
@@ -231,6 +234,8 @@ Layout make_layout(const Dims& d, int64_t max_n, int64_t k) {
   // histogram parts: one per score chunk (standalone top-k: one per 4096-entry chunk)
   L.hist_parts = take(U * cdiv(max_n, kScoreChunk) * kHistBins * 4);
   L.scores = take(U * max_n * 4);
+  L.qbar = take(U * d.D * 2);
+  L.qbar_o = take(U * d.D * 4);
   L.total = off;
   return L;
 }
@@ -522,6 +527,32 @@ mage_status launch_sparse(const Dims& d, const uint16_t* q, const KvArgs& kv, co
                 kThreads, stream, mp);
 }
 
+// Selection by the probability under the block's mean query: the mean query
+// (one bf16 row per KV head) goes through the step-1 selection as a block of
+// one token with one query head per KV head. Its attention output lands in
+// the workspace and is not used.
+template <int D>
+mage_status launch_mean_query_select(const Dims& d, const uint16_t* q, const KvArgs& kv, int32_t k,
+                                     int32_t* idx, float* scores, int64_t score_stride, void* ws,
+                                     const Layout& L, hipStream_t stream) {
+  MeanQueryParams mq{};
+  mq.q = q;
+  mq.qbar = at<uint16_t>(ws, L.qbar);
+  mq.S = d.S; mq.B = d.B; mq.Hq = d.Hq; mq.Hkv = d.Hkv; mq.G = d.G; mq.D = D;
+  if (mage_status st = launch(kfn(mean_query_kernel), "mean_query_kernel",
+                              cdiv(static_cast<int64_t>(d.units) * D, 256), 256, stream, mq);
+      st != MAGE_OK)
+    return st;
+  Dims d1 = d;
+  d1.B = 1;
+  d1.Hq = d.Hkv;
+  d1.G = 1;
+  d1.R = 1;
+  d1.nrb = 1;
+  return launch_select<D>(d1, mq.qbar, kv, k, at<float>(ws, L.qbar_o), nullptr, idx, scores, score_stride,
+                          ws, L, stream, nullptr, nullptr);
+}
+
 mage_status check_ws(void* ws, size_t bytes, const Layout& L) {
   if (!ws) return fail(MAGE_ERR_INVALID_ARG, "workspace is null");
   if (!aligned(ws, 256)) return fail(MAGE_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
@@ -638,6 +669,71 @@ mage_status mage_exact_attn_paged(const mage_dims* dims, const uint16_t* q, cons
                                          stream, nullptr, nullptr)
                     : launch_select<64>(d, q, kv, 0, o, lse, nullptr, nullptr, 0, workspace, L,
                                         stream, nullptr, nullptr);
+}
+
+static mage_status mean_query_checks(const uint16_t* q, int32_t k, int32_t* idx, float* scores) {
+  if (!q || !idx) return fail(MAGE_ERR_INVALID_ARG, "q and idx must not be null");
+  if (!aligned(q, 16)) return fail(MAGE_ERR_INVALID_ARG, "q must be 16-byte aligned");
+  if (!aligned(idx, 4) || (scores && !aligned(scores, 4)))
+    return fail(MAGE_ERR_INVALID_ARG, "idx and scores must be 4-byte aligned");
+  if (k < 1) return fail(MAGE_ERR_INVALID_ARG, "k must be >= 1");
+  return MAGE_OK;
+}
+
+mage_status mage_select_mean_query(const mage_dims* dims, const uint16_t* q, const uint16_t* k_cache,
+                                   const uint16_t* v_cache, int32_t seq_len, int32_t k, int32_t* idx,
+                                   float* scores, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  CallScope scope;
+  Dims d;
+  if (mage_status st = check_dims(dims, d); st != MAGE_OK) return st;
+  if (mage_status st = mean_query_checks(q, k, idx, scores); st != MAGE_OK) return st;
+  KvArgs kv;
+  if (mage_status st = contiguous_kv(d, k_cache, v_cache, seq_len, kv); st != MAGE_OK) return st;
+  const Layout L = make_layout(d, kv.max_n, k);
+  if (mage_status st = check_ws(workspace, workspace_bytes, L); st != MAGE_OK) return st;
+  return d.D == 128 ? launch_mean_query_select<128>(d, q, kv, k, idx, scores, seq_len, workspace, L, stream)
+                    : launch_mean_query_select<64>(d, q, kv, k, idx, scores, seq_len, workspace, L, stream);
+}
+
+mage_status mage_select_mean_query_paged(const mage_dims* dims, const uint16_t* q, const mage_paged_kv* kvp,
+                                         int32_t k, int32_t* idx, float* scores, void* workspace,
+                                         size_t workspace_bytes, hipStream_t stream) {
+  CallScope scope;
+  Dims d;
+  if (mage_status st = check_dims(dims, d); st != MAGE_OK) return st;
+  if (mage_status st = mean_query_checks(q, k, idx, scores); st != MAGE_OK) return st;
+  KvArgs kv;
+  if (mage_status st = paged_kv(d, kvp, kv); st != MAGE_OK) return st;
+  const Layout L = make_layout(d, kv.max_n, k);
+  if (mage_status st = check_ws(workspace, workspace_bytes, L); st != MAGE_OK) return st;
+  return d.D == 128 ? launch_mean_query_select<128>(d, q, kv, k, idx, scores, kv.max_n, workspace, L, stream)
+                    : launch_mean_query_select<64>(d, q, kv, k, idx, scores, kv.max_n, workspace, L, stream);
+}
+
+mage_status mage_mean_query(const mage_dims* dims, const uint16_t* q, uint16_t* qbar, hipStream_t stream) {
+  CallScope scope;
+  Dims d;
+  if (mage_status st = check_dims(dims, d); st != MAGE_OK) return st;
+  if (!q || !qbar) return fail(MAGE_ERR_INVALID_ARG, "q and qbar must not be null");
+  if (!aligned(q, 2) || !aligned(qbar, 2)) return fail(MAGE_ERR_INVALID_ARG, "q and qbar must be 2-byte aligned");
+  MeanQueryParams mq{};
+  mq.q = q;
+  mq.qbar = qbar;
+  mq.S = d.S; mq.B = d.B; mq.Hq = d.Hq; mq.Hkv = d.Hkv; mq.G = d.G; mq.D = d.D;
+  return launch(kfn(mean_query_kernel), "mean_query_kernel", cdiv(static_cast<int64_t>(d.units) * d.D, 256),
+                256, stream, mq);
+}
+
+mage_status mage_idx_overlap(int32_t rows, int32_t k, const int32_t* a, const int32_t* b, int32_t* common,
+                             int32_t* count_a, int32_t* count_b, hipStream_t stream) {
+  CallScope scope;
+  if (rows < 1 || k < 1) return fail(MAGE_ERR_INVALID_ARG, "rows and k must be >= 1");
+  if (!a || !b || !common) return fail(MAGE_ERR_INVALID_ARG, "a, b and common must not be null");
+  if (!aligned(a, 4) || !aligned(b, 4) || !aligned(common, 4) || (count_a && !aligned(count_a, 4)) ||
+      (count_b && !aligned(count_b, 4)))
+    return fail(MAGE_ERR_INVALID_ARG, "index and count arrays must be 4-byte aligned");
+  OverlapParams op{a, b, common, count_a, count_b, rows, k};
+  return launch(kfn(idx_overlap_kernel), "idx_overlap_kernel", rows, kOverlapThreads, stream, op);
 }
 
 static mage_status sparse_common(const mage_dims* dims, const uint16_t* q, const int32_t* idx,

@@ -228,6 +228,53 @@ mage_status mage_topk(int32_t rows, const float* scores, int64_t row_stride,
                       const int32_t* lens, int32_t n, int32_t k, int32_t* idx,
                       void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Anchor re-selection diagnostics. The Step-dLLM page (abstract) refreshes the
+ * sparse set at anchor steps and reuses it in between; re-running
+ * mage_select_exact with an anchor step's queries is that refresh, and the
+ * two calls below measure what it buys.
+ *
+ * mage_mean_query: the mean query alone, written to qbar, bf16 [S][Hkv][d]
+ * (the q of a one-token block with one query head per KV head); q and qbar
+ * are device memory, 2-byte aligned, not null, else MAGE_ERR_INVALID_ARG.
+ *
+ * mage_select_mean_query: top-k by the probability under the block's mean
+ * query instead of the probability averaged over the block's rows (the other
+ * reading of the MAGE page's block-average query, "Approach"). The mean query
+ * of KV head h is the exact mean of its R = B*G query rows, rounded once to
+ * bf16 (nearest, ties to even; exact whenever those rows' magnitudes span
+ * less than about 2^38). It then goes through the step-1 selection as a
+ * one-token block with one query head per KV head. Arguments as for
+ * mage_select_exact without o/lse (scores nullable, [S][Hkv][N] or
+ * [S][Hkv][max N_s] paged); everything runs on `stream`. Same workspace as
+ * mage_select_exact.
+ */
+mage_status mage_mean_query(const mage_dims* dims, const uint16_t* q, uint16_t* qbar,
+                            hipStream_t stream);
+
+mage_status mage_select_mean_query(const mage_dims* dims, const uint16_t* q,
+                                   const uint16_t* k_cache, const uint16_t* v_cache,
+                                   int32_t seq_len, int32_t k, int32_t* idx, float* scores,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+mage_status mage_select_mean_query_paged(const mage_dims* dims, const uint16_t* q,
+                                         const mage_paged_kv* kv, int32_t k, int32_t* idx,
+                                         float* scores, void* workspace, size_t workspace_bytes,
+                                         hipStream_t stream);
+
+/*
+ * mage_idx_overlap: for `rows` pairs of index rows a[r], b[r] (int32 [rows][k],
+ * each in idx form: ascending non-negative entries, then negative padding),
+ * common[r] = the number of valid entries present in both; count_a[r] and
+ * count_b[r] (nullable) = the number of valid entries of each. The recall of
+ * a against the reference b is common / count_b. Device memory, 4-byte
+ * aligned; rows, k >= 1, else MAGE_ERR_INVALID_ARG. Rows that are not in idx
+ * form give unspecified counts (every read stays inside its row).
+ */
+mage_status mage_idx_overlap(int32_t rows, int32_t k, const int32_t* a, const int32_t* b,
+                             int32_t* common, int32_t* count_a, int32_t* count_b,
+                             hipStream_t stream);
+
 const char* mage_status_string(mage_status status);
 const char* mage_last_error(void);
 

@@ -199,3 +199,33 @@ def test_sparse_block_attn_argument_checks():
         args[i] = None
         assert lib.mage_sparse_block_attn_paged(*args) == mage.ERR_INVALID_ARG
     assert lib.mage_sparse_block_attn_paged(ctypes.byref(dims(head_dim=96)), *okp[1:]) == mage.ERR_UNSUPPORTED
+
+
+def test_anchor_diagnostics_argument_checks():
+    lib = mage.lib()
+    d = dims()
+    # dims, q, k_cache, v_cache, seq_len, k, idx, scores, workspace, bytes, stream
+    ok = [ctypes.byref(d), FAKE, FAKE, FAKE, 1024, 64, FAKE, None, FAKE, 1 << 30, None]
+    for i, bad in ((1, None), (6, None), (5, 0), (1, ctypes.c_void_p((1 << 20) + 2)),
+                   (7, ctypes.c_void_p((1 << 20) + 2))):
+        args = list(ok)
+        args[i] = bad
+        assert lib.mage_select_mean_query(*args) == mage.ERR_INVALID_ARG
+    assert lib.mage_select_mean_query(ctypes.byref(dims(head_dim=96)), *ok[1:]) == mage.ERR_UNSUPPORTED
+    pk = mage.PagedKv()
+    okp = [ctypes.byref(d), FAKE, ctypes.byref(pk), 64, FAKE, None, FAKE, 1 << 30, None]
+    assert lib.mage_select_mean_query_paged(*okp) == mage.ERR_INVALID_ARG      # empty paged cache
+    args = list(okp)
+    args[4] = None
+    assert lib.mage_select_mean_query_paged(*args) == mage.ERR_INVALID_ARG
+    # mean query alone
+    assert lib.mage_mean_query(ctypes.byref(d), None, FAKE, None) == mage.ERR_INVALID_ARG
+    assert lib.mage_mean_query(ctypes.byref(d), FAKE, None, None) == mage.ERR_INVALID_ARG
+    assert lib.mage_mean_query(ctypes.byref(dims(num_q_heads=30)), FAKE, FAKE, None) == mage.ERR_INVALID_ARG
+    # overlap: rows, k, a, b, common, count_a, count_b, stream
+    assert lib.mage_idx_overlap(0, 4, FAKE, FAKE, FAKE, None, None, None) == mage.ERR_INVALID_ARG
+    assert lib.mage_idx_overlap(4, 0, FAKE, FAKE, FAKE, None, None, None) == mage.ERR_INVALID_ARG
+    assert lib.mage_idx_overlap(4, 4, None, FAKE, FAKE, None, None, None) == mage.ERR_INVALID_ARG
+    assert lib.mage_idx_overlap(4, 4, FAKE, FAKE, None, None, None, None) == mage.ERR_INVALID_ARG
+    assert lib.mage_idx_overlap(4, 4, FAKE, FAKE, FAKE, ctypes.c_void_p((1 << 20) + 2), None,
+                                None) == mage.ERR_INVALID_ARG

@@ -64,3 +64,15 @@ def test_oracle_reproduces_tiny_regression_fixture():
     np.testing.assert_allclose(O[0, :, 0].sum(-1), g["o_step1_row_sums"], rtol=0, atol=1e-12)
     Os, lses = oracle.sparse(inp.q_steps[0], inp.k, inp.v, idx, w.scale)
     np.testing.assert_allclose(lses[0, :, 0], g["lse_step2"], rtol=0, atol=1e-12)
+
+
+def test_walk_queries_drift_from_q1():
+    w = workloads.custom((64,), 8, 2, 128, 16, 8, steps=32, name="walk")
+    q1 = workloads.make_inputs(w, with_steps=False).q1.float()
+    walk = workloads.walk_queries(w)
+    assert len(walk) == 31
+    assert all(torch.equal(a, b) for a, b in zip(walk, workloads.walk_queries(w)))   # seeded
+    # the drift from Q1 has standard deviation sigma half-way (step 17) and grows
+    sd = [float((q.float() - q1).std()) for q in walk]
+    assert abs(sd[15] - w.q_noise) < 0.1 * w.q_noise
+    assert sd[-1] > sd[15] > sd[3]

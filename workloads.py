@@ -31,6 +31,10 @@ Recipe (values drawn in fp32, rounded to bf16 once, round-to-nearest-even):
   c_j + N(0, 0.01^2), centroids c_j ~ N(0, I_d), j uniform over 64 centroids.
 * Later steps: Q_t = Q1 + N(0, sigma^2) with fresh noise per step (sigma 0.1
   for ``tiny``, 0.05 otherwise).
+* Random-walk drift (``walk_queries``, for the anchor re-selection
+  diagnostic only): Q_t = Q_{t-1} + N(0, tau^2) with tau = sigma * sqrt(2/T),
+  so the drift from Q1 has standard deviation sigma half-way through the
+  block and keeps growing after that.
 * Paged: the pool is [P][Hkv][page][d]; physical page ids are a seeded
   permutation of 0..P-1 handed out in order to each sequence's logical pages.
 
@@ -49,7 +53,7 @@ import numpy as np
 import torch
 
 # spawn-key purposes
-_Q1, _K, _V, _PLANT, _CLUSTER, _NOISE, _PERM = range(7)
+_Q1, _K, _V, _PLANT, _CLUSTER, _NOISE, _PERM, _WALK = range(8)
 
 
 @dataclass(frozen=True)
@@ -194,6 +198,19 @@ def step_queries(w: Workload, q1f: np.ndarray | None = None, steps=None):
     for t in range(2, (steps or w.steps) + 1):
         noise = _rng(w.seed, _NOISE, t).standard_normal(q1f.shape, dtype=np.float32)
         out.append(_bf16(q1f + np.float32(w.q_noise) * noise))
+    return out
+
+
+def walk_queries(w: Workload, q1f: np.ndarray | None = None, steps=None):
+    """Q_t for t = 2..T as bf16 tensors under a random-walk drift from Q1."""
+    if q1f is None:
+        q1f = _q1_f32(w)
+    T = steps or w.steps
+    tau = np.float32(w.q_noise * math.sqrt(2.0 / T))
+    out, cur = [], q1f.copy()
+    for t in range(2, T + 1):
+        cur = cur + tau * _rng(w.seed, _WALK, t).standard_normal(q1f.shape, dtype=np.float32)
+        out.append(_bf16(cur))
     return out
 
 
