@@ -342,3 +342,56 @@ def idx_overlap(a, b):
         ca.append(len(sa))
         cb.append(len(sb))
     return np.array(common), np.array(ca), np.array(cb)
+
+
+# ---- page-granular selection ----
+#
+# The block-sparse view of the same selection (Step-dLLM page, abstract: a
+# block-sparse mask; the KV cache's pages as the unit of a gather): positions
+# are grouped into pages of P consecutive positions, a page's score is the
+# sum of its positions' block-averaged scores, and the top pages by that score
+# are kept whole.
+
+def page_scores(score_row, page_tokens: int) -> np.ndarray:
+    """Sum of the scores of each run of page_tokens consecutive positions (the
+    last page holds what is left), fp64."""
+    a = np.asarray(score_row, dtype=np.float64)
+    n = a.shape[-1]
+    npg = -(-n // page_tokens)
+    pad = np.zeros(npg * page_tokens - n)
+    return np.concatenate([a, pad]).reshape(npg, page_tokens).sum(axis=1)
+
+
+def pages_to_positions(page_idx, page_tokens: int, n: int) -> np.ndarray:
+    """Expand ascending page ids (negative: none) into their positions, page by
+    page: row of len(page_idx) * page_tokens entries, -1 for positions past n
+    or slots of a missing page."""
+    out = []
+    for pg in np.asarray(page_idx).tolist():
+        for t in range(page_tokens):
+            p = pg * page_tokens + t
+            out.append(p if pg >= 0 and p < n else -1)
+    return np.array(out, dtype=np.int32)
+
+
+def select_pages(q, k, v, scale: float, page_tokens: int, k_pages: int, seq_lens=None):
+    """Step 1 with page-granular selection. Returns (scores list of [Hkv][N_s],
+    page_idx int32 [S][Hkv][k_pages] ascending with -1 padding, idx int32
+    [S][Hkv][k_pages * page_tokens] of positions)."""
+    _, _, scores, _ = select_exact(q, k, v, scale, 1, seq_lens)
+    S = len(scores)
+    Hkv = scores[0].shape[0]
+    pidx = np.zeros((S, Hkv, k_pages), dtype=np.int32)
+    idx = np.zeros((S, Hkv, k_pages * page_tokens), dtype=np.int32)
+    for s in range(S):
+        n = scores[s].shape[1]
+        for h in range(Hkv):
+            pidx[s, h] = topk(page_scores(scores[s][h], page_tokens), k_pages)[0]
+            idx[s, h] = pages_to_positions(pidx[s, h], page_tokens, n)
+    return scores, pidx, idx
+
+
+def select_pages_paged(q, k_pool, v_pool, page_table, seq_lens, scale: float, page_tokens: int, k_pages: int):
+    kc = _padded(depage(k_pool, page_table, seq_lens))
+    vc = _padded(depage(v_pool, page_table, seq_lens))
+    return select_pages(q, kc, vc, scale, page_tokens, k_pages, seq_lens=np.asarray(seq_lens))

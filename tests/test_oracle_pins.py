@@ -434,3 +434,45 @@ def test_idx_overlap_counts():
         rb = np.sort(rng.choice(n, k, replace=False))
         c, _, _ = oracle.idx_overlap([ra], [rb])
         assert c[0] == np.intersect1d(ra, rb).size
+
+
+# ---- page-granular selection ----
+
+def test_page_scores_and_expansion_by_hand():
+    np.testing.assert_array_equal(oracle.page_scores([1, 2, 3, 4, 5], 2), [3, 7, 5])
+    np.testing.assert_array_equal(oracle.page_scores([0.5, 0.25], 4), [0.75])
+    np.testing.assert_array_equal(oracle.pages_to_positions([0, 2, -1], 3, 8), [0, 1, 2, 6, 7, -1, -1, -1, -1])
+
+
+def test_page_selection_with_one_token_pages_is_the_token_selection():
+    q, k, v = rand_case(1, 8, 8, 2, 32, 257, seed=21)
+    _, _, _, idx = oracle.select_exact(q, k, v, 0.5, 40)
+    _, pidx, pos = oracle.select_pages(q, k, v, 0.5, 1, 40)
+    assert np.array_equal(pidx, idx) and np.array_equal(pos, idx)
+
+
+def test_page_selection_by_brute_force():
+    # every page's score from the oracle's own position scores, ranked by
+    # counting (score desc, page asc), on a ragged last page
+    q, k, v = rand_case(1, 4, 4, 1, 32, 203, seed=22)
+    P, kp = 16, 5
+    scores, pidx, pos = oracle.select_pages(q, k, v, 0.7, P, kp)
+    sc = scores[0][0]
+    npg = -(-203 // P)
+    ps = [sum(sc[p] for p in range(g * P, min(203, (g + 1) * P))) for g in range(npg)]
+    rank = [sum(1 for h in range(npg) if ps[h] > ps[g] or (ps[h] == ps[g] and h < g)) for g in range(npg)]
+    want = sorted(g for g in range(npg) if rank[g] < kp)
+    assert pidx[0, 0].tolist() == want
+    assert abs(sum(ps) - 1.0) < 1e-12                      # page scores still sum to one
+    exp = [p for g in want for p in range(g * P, (g + 1) * P)]
+    assert [p if p < 203 else -1 for p in exp] == pos[0, 0].tolist()
+
+
+def test_page_selection_keeps_the_page_of_a_dominant_key():
+    # one key far above the rest: its page must be chosen first
+    q, k, v = rand_case(1, 4, 4, 1, 32, 512, seed=23)
+    m = q.double()[0, :, :, :].mean(dim=(0, 1))
+    k2 = k.clone()
+    k2[0, 0, 333] = (m / m.norm() * 40).to(torch.bfloat16)
+    _, pidx, _ = oracle.select_pages(q, k2, v, 1.0, 16, 1)
+    assert pidx[0, 0, 0] == 333 // 16
