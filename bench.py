@@ -251,6 +251,35 @@ class Runner:
                                             o=self.o3, lse=self.lse3, workspace=self.ws)
         self._call(timer, fn)
 
+    def pages(self, P, kp, timer=None):
+        """Step 1 with page-granular selection into self.pidx / self.pidx_pages."""
+        w = self.w
+        if not hasattr(self, "pidx") or self.pidx.shape[-1] != P * kp:
+            S, Hkv = w.num_seqs, w.num_kv_heads
+            self.pidx = self.torch.empty(S, Hkv, P * kp, dtype=self.torch.int32, device=self.dev)
+            self.pidx_pages = self.torch.empty(S, Hkv, kp, dtype=self.torch.int32, device=self.dev)
+
+        def fn():
+            kw = dict(o=self.o, lse=self.lse, idx=self.pidx, page_idx=self.pidx_pages, workspace=self.ws)
+            if w.paged:
+                self.mage.select_pages_paged(self.q1, self.kp, self.vp, self.table, self.lens, P, kp, w.scale, **kw)
+            else:
+                self.mage.select_pages(self.q1, self.k, self.v, P, kp, w.scale, **kw)
+        self._call(timer, fn)
+
+    def sparse_idx(self, t, idx, timer=None):
+        """A later step over the given index rows."""
+        w = self.w
+        q = self.qs[t % len(self.qs)]
+
+        def fn():
+            if w.paged:
+                self.mage.sparse_attn_paged(q, self.kp, self.vp, self.table, self.lens, idx, w.scale, o=self.o2,
+                                            lse=self.lse2, workspace=self.ws)
+            else:
+                self.mage.sparse_attn(q, self.k, self.v, idx, w.scale, o=self.o2, lse=self.lse2, workspace=self.ws)
+        self._call(timer, fn)
+
     def topk_only(self, timer=None):
         w = self.w
         S, Hkv = w.num_seqs, w.num_kv_heads
@@ -298,6 +327,43 @@ def anchor_diag(torch, mage, r, w, qs, sel_us, sparse_us):
     out["mean_query_step1_set"] = {"recall_vs_step1_own": round(float(recall(mq, own[0]).mean()), 4),
                                    "mean_recall_over_steps": round(float(mq_rec.mean()), 4)}
     return out
+
+
+def page_diag(torch, mage, r, w, fl, P=16):
+    """Page-granular selection at the same position budget (k / P pages of P
+    positions): cold step-1 and later-step times, the recall of the page set
+    against the position set, and the block-averaged score mass each keeps."""
+    kp = max(1, w.k // P)
+    T = w.steps
+    r.select()                       # the position set and scores of Q1
+    torch.cuda.synchronize()
+    sel_t, sp_t = [], []
+    for i in range(5):
+        fl()
+        tm = KernelTimer(torch, mage.MAX_TIMED_LAUNCHES)
+        r.pages(P, kp, tm)
+        sel_t.append(tm)
+    for i in range(2 * (T - 1) if T > 1 else 2):
+        fl()
+        tm = KernelTimer(torch, 2)
+        r.sparse_idx(i, r.pidx, tm)
+        sp_t.append(tm)
+    torch.cuda.synchronize()
+    c, _, cb = mage.idx_overlap(r.pidx, r.idx)
+    recall = (c.double() / cb.double().clamp(min=1)).mean().item()
+    sc = r.scores.double()
+
+    def mass(idx):
+        m = idx >= 0
+        return (sc.gather(2, idx.clamp(min=0).long()) * m).sum(-1).mean().item()
+
+    sel_k = by_kernel(sel_t)
+    return {"page_tokens": P, "k_pages": kp,
+            "select_gpu_us_median": round(statistics.median([t.busy_ms() * 1e3 for t in sel_t]), 1),
+            "select_kernels_us_median": {n: round(statistics.median(v), 2) for n, v in sel_k.items()},
+            "sparse_step_gpu_us_median": round(statistics.median([t.busy_ms() * 1e3 for t in sp_t]), 2),
+            "recall_vs_position_set": round(recall, 4),
+            "score_mass_pages": round(mass(r.pidx), 4), "score_mass_positions": round(mass(r.idx), 4)}
 
 
 def by_kernel(timers):
@@ -516,6 +582,8 @@ def run_bench(args):
     traffic = traffic_record(w.name)
     us = lambda v: round(v, 2)  # noqa: E731
     t0 = time.perf_counter()
+    pages = page_diag(torch, mage, r, w, fl)
+    log(f"[bench] page-granular selection measured")
     sp_med = statistics.median(sp_busy)
     anchor = {"iid": anchor_diag(torch, mage, r, w, [r.q1] + r.qs[:T - 1], sel_med, sp_med),
               "walk": anchor_diag(torch, mage, r, w,
@@ -591,6 +659,7 @@ def run_bench(args):
                                "log-sum-exp (separate launch); fused_step = the sparse step with "
                                "the block rows as one more split (one call)"},
         "anchor_recall": anchor,
+        "page_selection": pages,
         "speedup_vs_exact_per_step": round(ex_med / statistics.median(sp_busy), 2),
         "wall_s_timed_region": round(wall, 3),
         "flushes_in_timed_region": args.steps * T if args.flush != "none" else 0,
@@ -616,7 +685,8 @@ def run_bench(args):
 def _short(name: str) -> str:
     for key in ("exact_chunk_kernel", "sparse_attn_kernel", "exact_merge_kernel", "score_kernel",
                 "topk_local_kernel", "topk_final_kernel", "topk_hist_kernel", "hist_reduce_kernel",
-                "block_attn_kernel", "FillFunctor",
+                "block_attn_kernel", "mean_query_kernel", "idx_overlap_kernel", "page_sum_kernel",
+                "page_expand_kernel", "FillFunctor",
                 "neg_kernel", "reduce_kernel"):
         if key in name:
             return {"FillFunctor": "flush (fill)", "neg_kernel": "copy (neg)",

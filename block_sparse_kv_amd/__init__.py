@@ -30,7 +30,7 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE_TOO_SMALL, ERR_HIP = range(5
 MAX_SEQS = 256
 MAX_ROWS = 128
 MAX_SPARSE_K = 131072
-MAX_TIMED_LAUNCHES = 8
+MAX_TIMED_LAUNCHES = 12
 
 
 class MageError(RuntimeError):
@@ -88,11 +88,16 @@ def lib():
         L.mage_select_mean_query_paged.argtypes = [P(Dims), _vp, P(PagedKv), _i32, _vp, _vp, _vp, _sz, _vp]
         L.mage_idx_overlap.argtypes = [_i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp]
         L.mage_mean_query.argtypes = [P(Dims), _vp, _vp, _vp]
+        L.mage_select_pages.argtypes = [P(Dims), _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
+                                        _sz, _vp, _vp, _vp]
+        L.mage_select_pages_paged.argtypes = [P(Dims), _vp, P(PagedKv), _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
+                                              _sz, _vp, _vp, _vp]
         for f in ("mage_workspace_init", "mage_select_exact", "mage_select_exact_paged",
                   "mage_exact_attn", "mage_exact_attn_paged",
                   "mage_sparse_attn", "mage_sparse_attn_paged", "mage_topk", "mage_block_attn",
                   "mage_sparse_block_attn", "mage_sparse_block_attn_paged", "mage_select_mean_query",
-                  "mage_select_mean_query_paged", "mage_idx_overlap", "mage_mean_query"):
+                  "mage_select_mean_query_paged", "mage_idx_overlap", "mage_mean_query",
+                  "mage_select_pages", "mage_select_pages_paged"):
             getattr(L, f).restype = ctypes.c_int
         L.mage_status_string.argtypes = [ctypes.c_int]
         L.mage_status_string.restype = ctypes.c_char_p
@@ -257,6 +262,54 @@ def select_exact_paged(q, k_pool, v_pool, page_table, seq_lens, k: int, scale: f
     if idx_ready is not None:
         idx_ready.record(select_stream if select_stream is not None else torch.cuda.current_stream())
     return o, lse, idx, scores
+
+
+def select_pages(q, k_cache, v_cache, page_tokens: int, k_pages: int, scale: float, *, o=None, lse=None,
+                 idx=None, page_idx=None, scores=None, want_scores=False, workspace=None, stream=None):
+    """Step 1 with page-granular selection. Returns (o, lse, idx int32
+    [S][Hkv][k_pages * page_tokens] positions, page_idx int32 [S][Hkv][k_pages],
+    scores or None); everything on `stream`."""
+    S, B, Hq, d = q.shape
+    _, Hkv, N, _ = k_cache.shape
+    dims = make_dims(q, Hkv, scale)
+    dev = q.device
+    k = k_pages * page_tokens
+    o = _out(o, (S, B, Hq, d), torch.float32, dev)
+    lse = _out(lse, (S, B, Hq), torch.float32, dev)
+    idx = _out(idx, (S, Hkv, k), torch.int32, dev)
+    page_idx = _out(page_idx, (S, Hkv, k_pages), torch.int32, dev)
+    if want_scores or scores is not None:
+        scores = _out(scores, (S, Hkv, N), torch.float32, dev)
+    ws = _ws_obj(workspace, dev).get(workspace_bytes(dims, N, k), stream)
+    _check(lib().mage_select_pages(ctypes.byref(dims), _bf16_ptr(q, "q"), _bf16_ptr(k_cache, "k_cache"),
+                                   _bf16_ptr(v_cache, "v_cache"), N, int(page_tokens), int(k_pages), _ptr(o),
+                                   _ptr(lse), _ptr(idx), _ptr(page_idx), _ptr(scores), _ptr(ws), ws.numel(),
+                                   _stream(stream), None, None), "mage_select_pages")
+    return o, lse, idx, page_idx, scores
+
+
+def select_pages_paged(q, k_pool, v_pool, page_table, seq_lens, page_tokens: int, k_pages: int, scale: float, *,
+                       o=None, lse=None, idx=None, page_idx=None, scores=None, want_scores=False, workspace=None,
+                       stream=None):
+    """select_pages over a paged cache; scores fp32 [S][Hkv][max(seq_lens)]."""
+    S, B, Hq, d = q.shape
+    Hkv = k_pool.shape[1]
+    dims = make_dims(q, Hkv, scale)
+    kv, keep, lens = _paged(k_pool, v_pool, page_table, seq_lens)
+    dev = q.device
+    k = k_pages * page_tokens
+    o = _out(o, (S, B, Hq, d), torch.float32, dev)
+    lse = _out(lse, (S, B, Hq), torch.float32, dev)
+    idx = _out(idx, (S, Hkv, k), torch.int32, dev)
+    page_idx = _out(page_idx, (S, Hkv, k_pages), torch.int32, dev)
+    if want_scores or scores is not None:
+        scores = _out(scores, (S, Hkv, max(lens)), torch.float32, dev)
+    ws = _ws_obj(workspace, dev).get(workspace_bytes(dims, max(lens), k), stream)
+    _check(lib().mage_select_pages_paged(ctypes.byref(dims), _bf16_ptr(q, "q"), ctypes.byref(kv), int(page_tokens),
+                                         int(k_pages), _ptr(o), _ptr(lse), _ptr(idx), _ptr(page_idx), _ptr(scores),
+                                         _ptr(ws), ws.numel(), _stream(stream), None, None),
+           "mage_select_pages_paged")
+    return o, lse, idx, page_idx, scores
 
 
 def mean_query(q, num_kv_heads: int, *, out=None, stream=None):

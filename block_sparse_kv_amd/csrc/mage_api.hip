@@ -12,6 +12,7 @@
 #include "../../include/mage.h"
 #include "attn_kernels.hpp"
 #include "diag_kernels.hpp"
+#include "page_kernels.hpp"
 #include "select_kernels.hpp"
 
 namespace {
@@ -205,6 +206,7 @@ constexpr int kSparseStages = 2;
 struct Layout {
   size_t rowstat, part_ml, part_o, cand_bits, cand_pos, cand_count, row_info, hist, hist_parts, scores;
   size_t qbar, qbar_o;   // mean-query selection: the mean query and its (unused) attention output
+  size_t page_scores, page_idx;   // page-granular selection (pages of >= 1 positions; <= k page ids)
   size_t total;
   int64_t slots, cand_stride;
 };
@@ -236,6 +238,8 @@ Layout make_layout(const Dims& d, int64_t max_n, int64_t k) {
   L.scores = take(U * max_n * 4);
   L.qbar = take(U * d.D * 2);
   L.qbar_o = take(U * d.D * 4);
+  L.page_scores = take(U * max_n * 4);
+  L.page_idx = take(U * k * 4);
   L.total = off;
   return L;
 }
@@ -366,11 +370,24 @@ mage_status launch_topk(const TopkParams& tp, const HistReduceParams& hr, hipStr
   return launch(kfn(topk_final_kernel), "topk_final_kernel", tp.rows, kTopkThreads, stream, tp);
 }
 
-// k == 0: exact attention only (no score sweep, no top-k).
+struct PagePlan;
+mage_status launch_page_topk(const Dims& d, const KvArgs& kv, const float* scores, int64_t stride,
+                             const PagePlan& pp, int32_t* idx, void* ws, const Layout& L, hipStream_t stream);
+
+// Page-granular selection: P positions per page and k_pages pages per row;
+// page_idx may be null (then the workspace holds it).
+struct PagePlan {
+  int32_t page_tokens, k_pages;
+  int32_t* page_idx;
+};
+
+// k == 0: exact attention only (no score sweep, no top-k). With a page plan,
+// k = k_pages * page_tokens and the top-k runs over page scores.
 template <int D>
 mage_status launch_select(const Dims& d, const uint16_t* q, const KvArgs& kv, int32_t k, float* o,
                           float* lse, int32_t* idx, float* scores, int64_t score_stride, void* ws,
-                          const Layout& L, hipStream_t attn, hipStream_t sel, hipEvent_t idx_ready) {
+                          const Layout& L, hipStream_t attn, hipStream_t sel, hipEvent_t idx_ready,
+                          const PagePlan* pages = nullptr) {
   const int64_t U = d.units;
   const int chunk = exact_chunk(U, kv.max_n, kv.total_keys, kv.src.page_table ? (1 << kv.src.page_shift) : 0,
                                 kv.src.page_table ? kv.lens.n : nullptr, d.S, d.Hkv);
@@ -446,6 +463,15 @@ mage_status launch_select(const Dims& d, const uint16_t* q, const KvArgs& kv, in
                               score_grid, kThreads, sel, sp);
       st != MAGE_OK)
     return st;
+  if (pages) {
+    if (mage_status st = launch_page_topk(d, kv, sp.scores, sp.stride, *pages, idx, ws, L, sel); st != MAGE_OK)
+      return st;
+    if (idx_ready) {
+      if (hipError_t e = hipEventRecord(idx_ready, sel); e != hipSuccess)
+        return hip_fail(e, "hipEventRecord(idx_ready)");
+    }
+    return MAGE_OK;
+  }
 
   TopkParams tp{};
   tp.scores = sp.scores;
@@ -480,6 +506,75 @@ mage_status launch_select(const Dims& d, const uint16_t* q, const KvArgs& kv, in
       return hip_fail(e, "hipEventRecord(idx_ready)");
   }
   return MAGE_OK;
+}
+
+// Page scores, the top k_pages pages of every row (the standalone top-k path
+// over the page scores) and their expansion into positions.
+mage_status launch_page_topk(const Dims& d, const KvArgs& kv, const float* scores, int64_t stride,
+                             const PagePlan& pp, int32_t* idx, void* ws, const Layout& L, hipStream_t stream) {
+  const bool ragged = kv.src.page_table != nullptr;
+  const int P = pp.page_tokens;
+  const int64_t pages_max = cdiv(kv.max_n, P);
+  SeqLens plens;
+  std::memset(&plens, 0, sizeof plens);
+  if (ragged)
+    for (int s = 0; s < d.S; ++s) plens.n[s] = static_cast<int32_t>(cdiv(kv.lens.n[s], P));
+  PageSumParams ps{};
+  ps.scores = scores;
+  ps.stride = stride;
+  ps.page_scores = at<float>(ws, L.page_scores);
+  ps.pstride = pages_max;
+  ps.rows = d.units;
+  ps.rows_per_seq = d.Hkv;
+  ps.n_uniform = ragged ? -1 : kv.src.n_uniform;
+  ps.page_tokens = P;
+  ps.pages_max = static_cast<int32_t>(pages_max);
+  ps.lens = kv.lens;
+  if (mage_status st = launch(kfn(page_sum_kernel), "page_sum_kernel", cdiv(d.units * pages_max, 256), 256,
+                              stream, ps);
+      st != MAGE_OK)
+    return st;
+  int32_t* page_idx = pp.page_idx ? pp.page_idx : at<int32_t>(ws, L.page_idx);
+  TopkParams tp{};
+  tp.scores = ps.page_scores;
+  tp.stride = pages_max;
+  tp.idx = page_idx;
+  tp.k = pp.k_pages;
+  tp.hist = at<uint32_t>(ws, L.hist);
+  tp.hist_parts = at<uint32_t>(ws, L.hist_parts);
+  tp.cand_bits = at<uint32_t>(ws, L.cand_bits);
+  tp.cand_pos = at<int32_t>(ws, L.cand_pos);
+  tp.cand_stride = L.cand_stride;
+  tp.cand_count = at<int32_t>(ws, L.cand_count);
+  tp.row_info = at<int32_t>(ws, L.row_info);
+  tp.rows = d.units;
+  tp.rows_per_seq = d.Hkv;
+  tp.n_uniform = ragged ? -1 : static_cast<int32_t>(pages_max);
+  tp.nchunk = static_cast<int>(cdiv(pages_max, kLocalChunk));
+  tp.lens = plens;
+  tp.map = topk_map(tp, d.S);
+  HistReduceParams hr{};
+  hr.parts = tp.hist_parts;
+  hr.hist = tp.hist;
+  hr.rows = tp.rows;
+  hr.nparts = tp.nchunk;
+  hr.part_len = kLocalChunk;
+  hr.rows_per_seq = tp.rows_per_seq;
+  hr.n_uniform = tp.n_uniform;
+  hr.k = tp.k;
+  hr.lens = plens;
+  if (mage_status st = launch_topk(tp, hr, stream, true); st != MAGE_OK) return st;
+  PageExpandParams pe{};
+  pe.page_idx = page_idx;
+  pe.idx = idx;
+  pe.rows = d.units;
+  pe.rows_per_seq = d.Hkv;
+  pe.n_uniform = ragged ? -1 : kv.src.n_uniform;
+  pe.k_pages = pp.k_pages;
+  pe.page_tokens = P;
+  pe.lens = kv.lens;
+  return launch(kfn(page_expand_kernel), "page_expand_kernel",
+                cdiv(static_cast<int64_t>(d.units) * pp.k_pages * P, 256), 256, stream, pe);
 }
 
 template <int D>
@@ -708,6 +803,59 @@ mage_status mage_select_mean_query_paged(const mage_dims* dims, const uint16_t* 
   if (mage_status st = check_ws(workspace, workspace_bytes, L); st != MAGE_OK) return st;
   return d.D == 128 ? launch_mean_query_select<128>(d, q, kv, k, idx, scores, kv.max_n, workspace, L, stream)
                     : launch_mean_query_select<64>(d, q, kv, k, idx, scores, kv.max_n, workspace, L, stream);
+}
+
+static mage_status page_checks(const uint16_t* q, int32_t page_tokens, int32_t k_pages, float* o, float* lse,
+                               int32_t* idx, int32_t* page_idx, float* scores) {
+  if (page_tokens < 1 || page_tokens > 4096) return fail(MAGE_ERR_INVALID_ARG, "page_tokens must be in [1, 4096]");
+  if (k_pages < 1) return fail(MAGE_ERR_INVALID_ARG, "k_pages must be >= 1");
+  if (static_cast<int64_t>(k_pages) * page_tokens > MAGE_MAX_SPARSE_K)
+    return fail(MAGE_ERR_UNSUPPORTED, "k_pages * page_tokens must be <= MAGE_MAX_SPARSE_K");
+  if (page_idx && !aligned(page_idx, 4)) return fail(MAGE_ERR_INVALID_ARG, "page_idx must be 4-byte aligned");
+  return common_select_checks(q, k_pages * page_tokens, o, lse, idx, scores);
+}
+
+mage_status mage_select_pages(const mage_dims* dims, const uint16_t* q, const uint16_t* k_cache,
+                              const uint16_t* v_cache, int32_t seq_len, int32_t page_tokens, int32_t k_pages,
+                              float* o, float* lse, int32_t* idx, int32_t* page_idx, float* scores,
+                              void* workspace, size_t workspace_bytes, hipStream_t attn_stream,
+                              hipStream_t select_stream, hipEvent_t idx_ready) {
+  CallScope scope;
+  Dims d;
+  if (mage_status st = check_dims(dims, d); st != MAGE_OK) return st;
+  if (mage_status st = page_checks(q, page_tokens, k_pages, o, lse, idx, page_idx, scores); st != MAGE_OK)
+    return st;
+  KvArgs kv;
+  if (mage_status st = contiguous_kv(d, k_cache, v_cache, seq_len, kv); st != MAGE_OK) return st;
+  const int32_t k = k_pages * page_tokens;
+  const Layout L = make_layout(d, kv.max_n, k);
+  if (mage_status st = check_ws(workspace, workspace_bytes, L); st != MAGE_OK) return st;
+  const PagePlan pp{page_tokens, k_pages, page_idx};
+  return d.D == 128 ? launch_select<128>(d, q, kv, k, o, lse, idx, scores, seq_len, workspace, L, attn_stream,
+                                         select_stream, idx_ready, &pp)
+                    : launch_select<64>(d, q, kv, k, o, lse, idx, scores, seq_len, workspace, L, attn_stream,
+                                        select_stream, idx_ready, &pp);
+}
+
+mage_status mage_select_pages_paged(const mage_dims* dims, const uint16_t* q, const mage_paged_kv* kvp,
+                                    int32_t page_tokens, int32_t k_pages, float* o, float* lse, int32_t* idx,
+                                    int32_t* page_idx, float* scores, void* workspace, size_t workspace_bytes,
+                                    hipStream_t attn_stream, hipStream_t select_stream, hipEvent_t idx_ready) {
+  CallScope scope;
+  Dims d;
+  if (mage_status st = check_dims(dims, d); st != MAGE_OK) return st;
+  if (mage_status st = page_checks(q, page_tokens, k_pages, o, lse, idx, page_idx, scores); st != MAGE_OK)
+    return st;
+  KvArgs kv;
+  if (mage_status st = paged_kv(d, kvp, kv); st != MAGE_OK) return st;
+  const int32_t k = k_pages * page_tokens;
+  const Layout L = make_layout(d, kv.max_n, k);
+  if (mage_status st = check_ws(workspace, workspace_bytes, L); st != MAGE_OK) return st;
+  const PagePlan pp{page_tokens, k_pages, page_idx};
+  return d.D == 128 ? launch_select<128>(d, q, kv, k, o, lse, idx, scores, kv.max_n, workspace, L, attn_stream,
+                                         select_stream, idx_ready, &pp)
+                    : launch_select<64>(d, q, kv, k, o, lse, idx, scores, kv.max_n, workspace, L, attn_stream,
+                                        select_stream, idx_ready, &pp);
 }
 
 mage_status mage_mean_query(const mage_dims* dims, const uint16_t* q, uint16_t* qbar, hipStream_t stream) {

@@ -229,6 +229,38 @@ mage_status mage_topk(int32_t rows, const float* scores, int64_t row_stride,
                       void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Page-granular selection (the block-sparse form of step 1): positions are
+ * grouped into pages of page_tokens consecutive positions (the last page of a
+ * prefix holds what is left), a page's score is the sum of its positions'
+ * block-averaged scores, and the k_pages pages with the largest scores per
+ * (sequence, KV head) are kept whole (ties to the lower page). Step-dLLM page
+ * (abstract): a block-sparse mask; pages of a paged cache are the natural
+ * unit of a gather. Outputs: idx int32 [S][Hkv][k_pages * page_tokens], the
+ * chosen pages' positions page by page in ascending order, -1 past N_s and
+ * for missing pages (k_pages > pages in the prefix) -- a valid idx for
+ * mage_sparse_attn with k = k_pages * page_tokens; page_idx (nullable) int32
+ * [S][Hkv][k_pages], the ascending page ids, -1 padded. o, lse, scores,
+ * streams and idx_ready as for mage_select_exact. page_tokens in [1, 4096]
+ * (it need not match a paged cache's page size), k_pages >= 1, else
+ * MAGE_ERR_INVALID_ARG; k_pages * page_tokens <= MAGE_MAX_SPARSE_K, else
+ * MAGE_ERR_UNSUPPORTED. Workspace: mage_workspace_bytes(dims, max_seq_len,
+ * k_pages * page_tokens).
+ */
+mage_status mage_select_pages(const mage_dims* dims, const uint16_t* q,
+                              const uint16_t* k_cache, const uint16_t* v_cache,
+                              int32_t seq_len, int32_t page_tokens, int32_t k_pages, float* o,
+                              float* lse, int32_t* idx, int32_t* page_idx, float* scores,
+                              void* workspace, size_t workspace_bytes, hipStream_t attn_stream,
+                              hipStream_t select_stream, hipEvent_t idx_ready);
+
+mage_status mage_select_pages_paged(const mage_dims* dims, const uint16_t* q,
+                                    const mage_paged_kv* kv, int32_t page_tokens, int32_t k_pages,
+                                    float* o, float* lse, int32_t* idx, int32_t* page_idx,
+                                    float* scores, void* workspace, size_t workspace_bytes,
+                                    hipStream_t attn_stream, hipStream_t select_stream,
+                                    hipEvent_t idx_ready);
+
+/*
  * Anchor re-selection diagnostics. The Step-dLLM page (abstract) refreshes the
  * sparse set at anchor steps and reuses it in between; re-running
  * mage_select_exact with an anchor step's queries is that refresh, and the
@@ -295,7 +327,7 @@ const char* mage_last_error(void);
  * this thread launched, armed or not: it returns their number and stores up
  * to max_names static, NUL-terminated kernel names into names (may be null).
  */
-#define MAGE_MAX_TIMED_LAUNCHES 8
+#define MAGE_MAX_TIMED_LAUNCHES 12
 mage_status mage_arm_kernel_timers(const hipEvent_t* start, const hipEvent_t* stop, int32_t n);
 int32_t mage_last_launches(const char** names, int32_t max_names);
 

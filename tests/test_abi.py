@@ -229,3 +229,28 @@ def test_anchor_diagnostics_argument_checks():
     assert lib.mage_idx_overlap(4, 4, FAKE, FAKE, None, None, None, None) == mage.ERR_INVALID_ARG
     assert lib.mage_idx_overlap(4, 4, FAKE, FAKE, FAKE, ctypes.c_void_p((1 << 20) + 2), None,
                                 None) == mage.ERR_INVALID_ARG
+
+
+def test_select_pages_argument_checks():
+    lib = mage.lib()
+    d = dims()
+    # dims, q, k_cache, v_cache, seq_len, page_tokens, k_pages, o, lse, idx, page_idx, scores, ws, bytes,
+    # attn stream, select stream, event
+    ok = [ctypes.byref(d), FAKE, FAKE, FAKE, 1024, 16, 8, FAKE, None, FAKE, None, None, FAKE, 1 << 40, None,
+          None, None]
+    for i, bad, st in ((5, 0, mage.ERR_INVALID_ARG), (5, 5000, mage.ERR_INVALID_ARG), (6, 0, mage.ERR_INVALID_ARG),
+                       (6, 1 << 20, mage.ERR_UNSUPPORTED), (10, ctypes.c_void_p((1 << 20) + 2), mage.ERR_INVALID_ARG),
+                       (9, None, mage.ERR_INVALID_ARG), (1, None, mage.ERR_INVALID_ARG)):
+        args = list(ok)
+        args[i] = bad
+        assert lib.mage_select_pages(*args) == st, (i, bad)
+    args = list(ok)
+    args[13] = 1024
+    assert lib.mage_select_pages(*args) == mage.ERR_WORKSPACE_TOO_SMALL
+    pk = mage.PagedKv()
+    okp = [ctypes.byref(d), FAKE, ctypes.byref(pk), 16, 8, FAKE, None, FAKE, None, None, FAKE, 1 << 40, None, None,
+           None]
+    assert lib.mage_select_pages_paged(*okp) == mage.ERR_INVALID_ARG       # empty paged cache
+    args = list(okp)
+    args[3] = 0
+    assert lib.mage_select_pages_paged(*args) == mage.ERR_INVALID_ARG
