@@ -395,3 +395,41 @@ def select_pages_paged(q, k_pool, v_pool, page_table, seq_lens, scale: float, pa
     kc = _padded(depage(k_pool, page_table, seq_lens))
     vc = _padded(depage(v_pool, page_table, seq_lens))
     return select_pages(q, kc, vc, scale, page_tokens, k_pages, seq_lens=np.asarray(seq_lens))
+
+
+# ---- head-adaptive budgets ----
+#
+# Step-dLLM page (abstract): one global budget per sequence, shared by its
+# heads so that heads whose attention is concentrated are compressed harder.
+# Read here: the sequence keeps the K = k * Hkv largest block-averaged scores
+# over all of its (KV head, position) pairs, ties to the lower head, then the
+# lower position; head h's budget k_h is how many of them are its own. Each
+# head's scores sum to one, so a head whose mass sits on few positions wins
+# few slots and a head with diffuse mass wins many.
+
+def select_adaptive(q, k, v, scale: float, topk_k: int, seq_lens=None):
+    """Step 1 with head-adaptive budgets. Returns (scores list of [Hkv][N_s],
+    idx int32 [S][Hkv][k * Hkv] ascending positions then -1, counts int64
+    [S][Hkv])."""
+    _, _, scores, _ = select_exact(q, k, v, scale, 1, seq_lens)
+    S = len(scores)
+    Hkv, _ = scores[0].shape
+    K = topk_k * Hkv
+    idx = np.full((S, Hkv, K), -1, dtype=np.int32)
+    counts = np.zeros((S, Hkv), dtype=np.int64)
+    for s in range(S):
+        n = scores[s].shape[1]
+        flat = scores[s].reshape(-1)                       # (h, p) -> h * n + p
+        chosen = topk(flat, min(K, flat.size))[0]
+        chosen = chosen[chosen >= 0]
+        for h in range(Hkv):
+            mine = chosen[(chosen >= h * n) & (chosen < (h + 1) * n)] - h * n
+            counts[s, h] = mine.size
+            idx[s, h, :mine.size] = np.sort(mine)
+    return scores, idx, counts
+
+
+def select_adaptive_paged(q, k_pool, v_pool, page_table, seq_lens, scale: float, topk_k: int):
+    kc = _padded(depage(k_pool, page_table, seq_lens))
+    vc = _padded(depage(v_pool, page_table, seq_lens))
+    return select_adaptive(q, kc, vc, scale, topk_k, seq_lens=np.asarray(seq_lens))

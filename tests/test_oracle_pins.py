@@ -476,3 +476,60 @@ def test_page_selection_keeps_the_page_of_a_dominant_key():
     k2[0, 0, 333] = (m / m.norm() * 40).to(torch.bfloat16)
     _, pidx, _ = oracle.select_pages(q, k2, v, 1.0, 16, 1)
     assert pidx[0, 0, 0] == 333 // 16
+
+
+# ---- head-adaptive budgets ----
+
+def test_adaptive_budgets_of_identical_heads_are_equal():
+    # every KV head sees the same keys and queries: the global top-(k * Hkv) is
+    # the top k of each head
+    q, k, v = rand_case(1, 8, 2, 1, 32, 300, seed=31)
+    q4 = q.repeat(1, 1, 4, 1).contiguous()                  # 8 query heads, G = 2 per KV head
+    k4 = k.repeat(1, 4, 1, 1).contiguous()
+    v4 = v.repeat(1, 4, 1, 1).contiguous()
+    _, idx, counts = oracle.select_adaptive(q4, k4, v4, 0.4, 30)
+    _, _, _, ref = oracle.select_exact(q4, k4, v4, 0.4, 30)
+    assert counts.tolist() == [[30, 30, 30, 30]]
+    assert np.array_equal(idx[..., :30], ref)
+    assert (idx[..., 30:] == -1).all()
+
+
+def test_adaptive_budgets_by_brute_force():
+    # the kept (head, position) pairs are exactly those ranked below K by
+    # (score desc, head asc, position asc), counted pair against pair
+    q, k, v = rand_case(1, 4, 6, 3, 32, 60, seed=32)
+    scores, idx, counts = oracle.select_adaptive(q, k, v, 0.9, 7)
+    sc = scores[0]
+    pairs = [(h, p) for h in range(3) for p in range(60)]
+    def ahead(a, b):
+        return sc[a] > sc[b] or (sc[a] == sc[b] and a < b)
+    kept = {a for a in pairs if sum(ahead(b, a) for b in pairs) < 21}
+    for h in range(3):
+        assert set(idx[0, h, :counts[0, h]].tolist()) == {p for (hh, p) in kept if hh == h}
+        assert (np.diff(idx[0, h, :counts[0, h]]) > 0).all() and (idx[0, h, counts[0, h]:] == -1).all()
+    assert counts.sum() == 21
+
+
+def test_adaptive_budgets_favour_the_diffuse_head():
+    # head 0: a few keys carry its mass; head 1: every key equal (uniform). The
+    # concentrated head needs only its heavy keys, the rest goes to head 1
+    d, n = 32, 400
+    g = torch.Generator().manual_seed(33)
+    q = torch.zeros(1, 1, 2, d)
+    q[0, 0, 0, 0] = 1.0
+    k = torch.zeros(1, 2, n, d)
+    k[0, 0, :, 0] = -30.0
+    k[0, 0, [5, 50, 77], 0] = 10.0                          # head 0: three dominant keys
+    v = torch.randn(1, 2, n, d, generator=g)
+    _, idx, counts = oracle.select_adaptive(q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16),
+                                            1.0, 20)
+    assert idx[0, 0, :3].tolist() == [5, 50, 77]
+    assert counts[0, 0] == 3 and counts[0, 1] == 37         # head 1's uniform 1/400 beats head 0's tail
+    assert idx[0, 1, :37].tolist() == list(range(37))         # equal scores: lowest positions
+
+
+def test_adaptive_budget_of_one_head_is_the_top_k():
+    q, k, v = rand_case(2, 4, 4, 1, 32, 250, seed=34)
+    _, idx, counts = oracle.select_adaptive(q, k, v, 0.6, 33)
+    _, _, _, ref = oracle.select_exact(q, k, v, 0.6, 33)
+    assert (counts == 33).all() and np.array_equal(idx, ref)
