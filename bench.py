@@ -267,6 +267,37 @@ class Runner:
                 self.mage.select_pages(self.q1, self.k, self.v, P, kp, w.scale, **kw)
         self._call(timer, fn)
 
+    def adaptive(self, timer=None):
+        """Step 1 with head-adaptive budgets into self.aidx / self.acounts."""
+        w = self.w
+        if not hasattr(self, "aidx"):
+            S, Hkv = w.num_seqs, w.num_kv_heads
+            self.aidx = self.torch.empty(S, Hkv, w.k * Hkv, dtype=self.torch.int32, device=self.dev)
+            self.acounts = self.torch.empty(S, Hkv, dtype=self.torch.int32, device=self.dev)
+
+        def fn():
+            kw = dict(o=self.o, lse=self.lse, idx=self.aidx, counts=self.acounts, workspace=self.ws)
+            if w.paged:
+                self.mage.select_adaptive_paged(self.q1, self.kp, self.vp, self.table, self.lens, w.k, w.scale, **kw)
+            else:
+                self.mage.select_adaptive(self.q1, self.k, self.v, w.k, w.scale, **kw)
+        self._call(timer, fn)
+
+    def sparse_counts(self, t, timer=None):
+        """A later step over the adaptive rows and counts."""
+        w = self.w
+        q = self.qs[t % len(self.qs)]
+        k_seq = w.k * w.num_kv_heads
+
+        def fn():
+            if w.paged:
+                self.mage.sparse_attn_counts_paged(q, self.kp, self.vp, self.table, self.lens, self.aidx, self.acounts,
+                                                   k_seq, w.scale, o=self.o2, lse=self.lse2, workspace=self.ws)
+            else:
+                self.mage.sparse_attn_counts(q, self.k, self.v, self.aidx, self.acounts, k_seq, w.scale, o=self.o2,
+                                             lse=self.lse2, workspace=self.ws)
+        self._call(timer, fn)
+
     def sparse_idx(self, t, idx, timer=None):
         """A later step over the given index rows."""
         w = self.w
@@ -364,6 +395,44 @@ def page_diag(torch, mage, r, w, fl, P=16):
             "sparse_step_gpu_us_median": round(statistics.median([t.busy_ms() * 1e3 for t in sp_t]), 2),
             "recall_vs_position_set": round(recall, 4),
             "score_mass_pages": round(mass(r.pidx), 4), "score_mass_positions": round(mass(r.idx), 4)}
+
+
+def budget_diag(torch, mage, r, w, fl):
+    """Head-adaptive budgets at the same total (k * Hkv positions per sequence):
+    cold step-1 and later-step times, the spread of the per-head counts, and
+    the block-averaged score mass kept per head against the uniform k."""
+    T = w.steps
+    r.select()
+    torch.cuda.synchronize()
+    sel_t, sp_t = [], []
+    for i in range(5):
+        fl()
+        tm = KernelTimer(torch, mage.MAX_TIMED_LAUNCHES)
+        r.adaptive(tm)
+        sel_t.append(tm)
+    for i in range(2 * (T - 1) if T > 1 else 2):
+        fl()
+        tm = KernelTimer(torch, 2)
+        r.sparse_counts(i, tm)
+        sp_t.append(tm)
+    torch.cuda.synchronize()
+    sc = r.scores.double()
+
+    def mass(idx):
+        m = idx >= 0
+        return (sc.gather(2, idx.clamp(min=0).long()) * m).sum(-1)
+
+    c = r.acounts.cpu().numpy().ravel()
+    m_u, m_a = mass(r.idx), mass(r.aidx)
+    return {"k_per_sequence": w.k * w.num_kv_heads,
+            "select_gpu_us_median": round(statistics.median([t.busy_ms() * 1e3 for t in sel_t]), 1),
+            "select_kernels_us_median": {n: round(statistics.median(v), 2) for n, v in by_kernel(sel_t).items()},
+            "sparse_step_gpu_us_median": round(statistics.median([t.busy_ms() * 1e3 for t in sp_t]), 2),
+            "counts_min_median_max": [int(c.min()), int(np.median(c)), int(c.max())],
+            "score_mass_per_head_uniform": round(m_u.mean().item(), 4),
+            "score_mass_per_head_adaptive": round(m_a.mean().item(), 4),
+            "worst_head_mass_uniform": round(m_u.min().item(), 4),
+            "worst_head_mass_adaptive": round(m_a.min().item(), 4)}
 
 
 def by_kernel(timers):
@@ -583,6 +652,7 @@ def run_bench(args):
     us = lambda v: round(v, 2)  # noqa: E731
     t0 = time.perf_counter()
     pages = page_diag(torch, mage, r, w, fl)
+    budgets = budget_diag(torch, mage, r, w, fl)
     log(f"[bench] page-granular selection measured")
     sp_med = statistics.median(sp_busy)
     anchor = {"iid": anchor_diag(torch, mage, r, w, [r.q1] + r.qs[:T - 1], sel_med, sp_med),
@@ -660,6 +730,7 @@ def run_bench(args):
                                "the block rows as one more split (one call)"},
         "anchor_recall": anchor,
         "page_selection": pages,
+        "head_adaptive_budgets": budgets,
         "speedup_vs_exact_per_step": round(ex_med / statistics.median(sp_busy), 2),
         "wall_s_timed_region": round(wall, 3),
         "flushes_in_timed_region": args.steps * T if args.flush != "none" else 0,
@@ -686,7 +757,7 @@ def _short(name: str) -> str:
     for key in ("exact_chunk_kernel", "sparse_attn_kernel", "exact_merge_kernel", "score_kernel",
                 "topk_local_kernel", "topk_final_kernel", "topk_hist_kernel", "hist_reduce_kernel",
                 "block_attn_kernel", "mean_query_kernel", "idx_overlap_kernel", "page_sum_kernel",
-                "page_expand_kernel", "FillFunctor",
+                "page_expand_kernel", "gap_zero_kernel", "budget_split_kernel", "FillFunctor",
                 "neg_kernel", "reduce_kernel"):
         if key in name:
             return {"FillFunctor": "flush (fill)", "neg_kernel": "copy (neg)",

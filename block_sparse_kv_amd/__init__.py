@@ -88,6 +88,14 @@ def lib():
         L.mage_select_mean_query_paged.argtypes = [P(Dims), _vp, P(PagedKv), _i32, _vp, _vp, _vp, _sz, _vp]
         L.mage_idx_overlap.argtypes = [_i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp]
         L.mage_mean_query.argtypes = [P(Dims), _vp, _vp, _vp]
+        L.mage_select_adaptive.argtypes = [P(Dims), _vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp,
+                                           _vp, _vp]
+        L.mage_select_adaptive_paged.argtypes = [P(Dims), _vp, P(PagedKv), _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp,
+                                                 _vp, _vp]
+        L.mage_sparse_attn_counts.argtypes = [P(Dims), _vp, _vp, _vp, _i32, _vp, _i32, _vp, _i32, _vp, _vp, _vp,
+                                              _sz, _vp]
+        L.mage_sparse_attn_counts_paged.argtypes = [P(Dims), _vp, P(PagedKv), _vp, _i32, _vp, _i32, _vp, _vp, _vp,
+                                                    _sz, _vp]
         L.mage_select_pages.argtypes = [P(Dims), _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
                                         _sz, _vp, _vp, _vp]
         L.mage_select_pages_paged.argtypes = [P(Dims), _vp, P(PagedKv), _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
@@ -97,7 +105,8 @@ def lib():
                   "mage_sparse_attn", "mage_sparse_attn_paged", "mage_topk", "mage_block_attn",
                   "mage_sparse_block_attn", "mage_sparse_block_attn_paged", "mage_select_mean_query",
                   "mage_select_mean_query_paged", "mage_idx_overlap", "mage_mean_query",
-                  "mage_select_pages", "mage_select_pages_paged"):
+                  "mage_select_pages", "mage_select_pages_paged", "mage_select_adaptive",
+                  "mage_select_adaptive_paged", "mage_sparse_attn_counts", "mage_sparse_attn_counts_paged"):
             getattr(L, f).restype = ctypes.c_int
         L.mage_status_string.argtypes = [ctypes.c_int]
         L.mage_status_string.restype = ctypes.c_char_p
@@ -310,6 +319,98 @@ def select_pages_paged(q, k_pool, v_pool, page_table, seq_lens, page_tokens: int
                                          _ptr(ws), ws.numel(), _stream(stream), None, None),
            "mage_select_pages_paged")
     return o, lse, idx, page_idx, scores
+
+
+def select_adaptive(q, k_cache, v_cache, k: int, scale: float, *, o=None, lse=None, idx=None, counts=None,
+                    workspace=None, stream=None):
+    """Step 1 with head-adaptive budgets (k * Hkv positions per sequence shared by
+    its KV heads). Returns (o, lse, idx int32 [S][Hkv][k * Hkv], counts int32
+    [S][Hkv]); everything on `stream`."""
+    S, B, Hq, d = q.shape
+    _, Hkv, N, _ = k_cache.shape
+    dims = make_dims(q, Hkv, scale)
+    dev = q.device
+    K = k * Hkv
+    o = _out(o, (S, B, Hq, d), torch.float32, dev)
+    lse = _out(lse, (S, B, Hq), torch.float32, dev)
+    idx = _out(idx, (S, Hkv, K), torch.int32, dev)
+    counts = _out(counts, (S, Hkv), torch.int32, dev)
+    ws = _ws_obj(workspace, dev).get(workspace_bytes(dims, N, K), stream)
+    _check(lib().mage_select_adaptive(ctypes.byref(dims), _bf16_ptr(q, "q"), _bf16_ptr(k_cache, "k_cache"),
+                                      _bf16_ptr(v_cache, "v_cache"), N, int(k), _ptr(o), _ptr(lse), _ptr(idx),
+                                      _ptr(counts), _ptr(ws), ws.numel(), _stream(stream), None, None),
+           "mage_select_adaptive")
+    return o, lse, idx, counts
+
+
+def select_adaptive_paged(q, k_pool, v_pool, page_table, seq_lens, k: int, scale: float, *, o=None, lse=None,
+                          idx=None, counts=None, workspace=None, stream=None):
+    """select_adaptive over a paged cache."""
+    S, B, Hq, d = q.shape
+    Hkv = k_pool.shape[1]
+    dims = make_dims(q, Hkv, scale)
+    kv, keep, lens = _paged(k_pool, v_pool, page_table, seq_lens)
+    dev = q.device
+    K = k * Hkv
+    o = _out(o, (S, B, Hq, d), torch.float32, dev)
+    lse = _out(lse, (S, B, Hq), torch.float32, dev)
+    idx = _out(idx, (S, Hkv, K), torch.int32, dev)
+    counts = _out(counts, (S, Hkv), torch.int32, dev)
+    ws = _ws_obj(workspace, dev).get(workspace_bytes(dims, max(lens), K), stream)
+    _check(lib().mage_select_adaptive_paged(ctypes.byref(dims), _bf16_ptr(q, "q"), ctypes.byref(kv), int(k),
+                                            _ptr(o), _ptr(lse), _ptr(idx), _ptr(counts), _ptr(ws), ws.numel(),
+                                            _stream(stream), None, None), "mage_select_adaptive_paged")
+    return o, lse, idx, counts
+
+
+def _counts_arg(counts, S, Hkv):
+    if counts.dtype != torch.int32 or not counts.is_cuda or not counts.is_contiguous() or \
+            tuple(counts.shape) != (S, Hkv):
+        raise ValueError("counts must be a contiguous int32 CUDA tensor [S][Hkv]")
+    return _ptr(counts)
+
+
+def sparse_attn_counts(q, k_cache, v_cache, idx, counts, k_seq: int, scale: float, *, o=None, lse=None,
+                       workspace=None, stream=None):
+    """A later step over idx[s][h][:counts[s][h]] (head-adaptive budgets); k_seq
+    bounds the entries of a sequence summed over its heads."""
+    S, B, Hq, d = q.shape
+    _, Hkv, N, _ = k_cache.shape
+    k_row = idx.shape[-1]
+    if idx.dtype != torch.int32 or not idx.is_contiguous() or tuple(idx.shape[:2]) != (S, Hkv):
+        raise ValueError("idx must be contiguous int32 [S][Hkv][k_row]")
+    cp = _counts_arg(counts, S, Hkv)
+    dims = make_dims(q, Hkv, scale)
+    dev = q.device
+    o = _out(o, (S, B, Hq, d), torch.float32, dev)
+    lse = _out(lse, (S, B, Hq), torch.float32, dev)
+    ws = _ws_obj(workspace, dev).get(workspace_bytes(dims, N, k_row), stream)
+    _check(lib().mage_sparse_attn_counts(ctypes.byref(dims), _bf16_ptr(q, "q"), _bf16_ptr(k_cache, "k_cache"),
+                                         _bf16_ptr(v_cache, "v_cache"), N, _ptr(idx), int(k_row), cp, int(k_seq),
+                                         _ptr(o), _ptr(lse), _ptr(ws), ws.numel(), _stream(stream)),
+           "mage_sparse_attn_counts")
+    return o, lse
+
+
+def sparse_attn_counts_paged(q, k_pool, v_pool, page_table, seq_lens, idx, counts, k_seq: int, scale: float, *,
+                             o=None, lse=None, workspace=None, stream=None):
+    """sparse_attn_counts over a paged cache."""
+    S, B, Hq, d = q.shape
+    Hkv = k_pool.shape[1]
+    k_row = idx.shape[-1]
+    if idx.dtype != torch.int32 or not idx.is_contiguous() or tuple(idx.shape[:2]) != (S, Hkv):
+        raise ValueError("idx must be contiguous int32 [S][Hkv][k_row]")
+    cp = _counts_arg(counts, S, Hkv)
+    dims = make_dims(q, Hkv, scale)
+    kv, keep, lens = _paged(k_pool, v_pool, page_table, seq_lens)
+    dev = q.device
+    o = _out(o, (S, B, Hq, d), torch.float32, dev)
+    lse = _out(lse, (S, B, Hq), torch.float32, dev)
+    ws = _ws_obj(workspace, dev).get(workspace_bytes(dims, max(lens), k_row), stream)
+    _check(lib().mage_sparse_attn_counts_paged(ctypes.byref(dims), _bf16_ptr(q, "q"), ctypes.byref(kv), _ptr(idx),
+                                               int(k_row), cp, int(k_seq), _ptr(o), _ptr(lse), _ptr(ws),
+                                               ws.numel(), _stream(stream)), "mage_sparse_attn_counts_paged")
+    return o, lse
 
 
 def mean_query(q, num_kv_heads: int, *, out=None, stream=None):

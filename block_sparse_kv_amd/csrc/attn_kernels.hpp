@@ -41,6 +41,9 @@ struct AttnParams {
   ChunkMap map;             // exact pass: work-group -> (unit, chunk)
   const uint16_t* k_blk;    // sparse pass: bf16 [S][Hkv][B][d], the block's own rows, taken by
   const uint16_t* v_blk;    //   the last chunk of every unit; null = prefix rows only
+  const int32_t* counts;    // sparse pass: per-unit entry counts (head-adaptive budgets); null =
+                            //   idx_k entries each. Work-groups are then numbered densely per
+  int32_t seq_slots;        //   sequence: seq_slots (unit, chunk) slots, units in head order
 };
 
 struct MergeParams {
@@ -53,6 +56,8 @@ struct MergeParams {
   int32_t chunk, nchunk;
   int32_t n_uniform;        // >= 0: entries per unit (prefix length or idx count); < 0: lens
   SeqLens lens;
+  const int32_t* counts;    // sparse pass with per-unit counts (capped at n_uniform): the chunks
+  int32_t seq_slots;        //   of sequence s are slots s * seq_slots + (chunks of lower heads) + c
 };
 
 constexpr int kMaxChunkPages = 4096;    // page ids per exact-pass work-group (paged layout)
@@ -647,14 +652,40 @@ __global__ __launch_bounds__(kSparseThreads) void sparse_attn_kernel(AttnParams 
   const int x = blockIdx.x & 7, jj = blockIdx.x >> 3;
   const int rb = jj % nrb;
   const int g = (jj / nrb) * 8 + x;
-  if (g >= units * p.nchunk) return;
+  int u, c, n_idx = p.idx_k;   // (unit, chunk) and the unit's index entries
+  int64_t slot;                // partial slot
+  bool direct = p.nchunk == 1; // the unit's only chunk: O and lse written here, no merge
+  if (p.counts == nullptr) {
+    if (g >= units * p.nchunk) return;
+    u = g / p.nchunk;
+    c = g - u * p.nchunk;
+    slot = static_cast<int64_t>(u) * p.nchunk + c;
+  } else {
+    // per-unit counts: g = sequence * seq_slots + the chunk's place among the
+    // sequence's chunks, heads in order
+    const int sq = g / p.seq_slots;
+    if (sq >= p.S) return;
+    int lc = g - sq * p.seq_slots, head = 0;
+    for (; head < p.Hkv; ++head) {
+      const int nc = (max(0, min(p.counts[sq * p.Hkv + head], p.idx_k)) + p.chunk - 1) / p.chunk;
+      if (lc < nc) {
+        direct = nc == 1;
+        break;
+      }
+      lc -= nc;
+    }
+    if (head == p.Hkv) return;   // past the sequence's last chunk
+    u = sq * p.Hkv + head;
+    c = lc;
+    slot = g;
+    n_idx = max(0, min(p.counts[u], p.idx_k));
+  }
   MAGE_TRACE_POINT(0);
-  const int u = g / p.nchunk, c = g - u * p.nchunk;
   const int s = u / p.Hkv, h = u - s * p.Hkv;
   const int ns = seq_len_of(p.kv, p.lens, s);
   const int kpw = p.chunk / kSparseWaves;
   const int e0 = c * p.chunk + w * kpw;                 // this wave's entries [e0, e1)
-  const int e1 = min(e0 + kpw, p.idx_k);
+  const int e1 = min(e0 + kpw, n_idx);
   const int cnt = max(0, e1 - e0);
   // the last chunk of a unit also takes the block's own rows: at most one more
   // 32-row tile per wave, rows [b0, b0 + nb) of this unit's B
@@ -794,7 +825,7 @@ __global__ __launch_bounds__(kSparseThreads) void sparse_attn_kernel(AttnParams 
     for (int i = 0; i < 16; ++i) acc[i] += xj[(2 + 16 * db + i) * kWave + lane] * a;
   }
   const int r = 32 * rb + n;
-  if (p.nchunk == 1) {
+  if (direct) {
     if (r >= p.R) return;
     const int b = r / p.G, gg = r - b * p.G, j = h * p.G + gg;
     const int64_t row = (static_cast<int64_t>(s) * p.B + b) * p.Hq + j;
@@ -808,7 +839,6 @@ __global__ __launch_bounds__(kSparseThreads) void sparse_attn_kernel(AttnParams 
       p.lse[row] = L > 0.f ? (M + __log2f(L)) * kLn2 : -__builtin_inff();
     return;
   }
-  const int64_t slot = static_cast<int64_t>(u) * p.nchunk + c;
 #pragma unroll
   for (int i4 = 0; i4 < 4; ++i4)
     *reinterpret_cast<f32x4*>(p.part_o + 4 * part_o_index<D>(slot, rb, db, i4, lane)) =
@@ -839,9 +869,19 @@ __global__ __launch_bounds__(kThreads) void exact_merge_kernel(MergeParams p) {
   const int u = bid / p.nrb;
   const int s = u / p.Hkv, h = u - s * p.Hkv;
   const int ns = p.n_uniform >= 0 ? p.n_uniform : p.lens.n[s];
-  const int nch = (ns + p.chunk - 1) / p.chunk;
+  int nch = (ns + p.chunk - 1) / p.chunk;
   const int r = 32 * w + n;
-  const int64_t slot0 = static_cast<int64_t>(u) * p.nchunk;
+  int64_t slot0 = static_cast<int64_t>(u) * p.nchunk;
+  if (p.counts != nullptr) {
+    // this unit's chunks follow those of the sequence's lower heads; never
+    // past the sequence's slots (counts above the plan's bound lose chunks)
+    int before = 0;
+    for (int h2 = 0; h2 < h; ++h2) before += (max(0, min(p.counts[s * p.Hkv + h2], ns)) + p.chunk - 1) / p.chunk;
+    nch = (max(0, min(p.counts[u], ns)) + p.chunk - 1) / p.chunk;
+    if (nch == 1 && before < p.seq_slots) return;   // its one chunk wrote O and lse
+    nch = max(0, min(nch, p.seq_slots - before));
+    slot0 = static_cast<int64_t>(s) * p.seq_slots + before;
+  }
   // one pass: a running max; each batch's loads are all in flight together
   float M = -__builtin_inff(), L = 0.f;
   f32x4 acc{0.f, 0.f, 0.f, 0.f};

@@ -11,6 +11,7 @@
 
 #include "../../include/mage.h"
 #include "attn_kernels.hpp"
+#include "budget_kernels.hpp"
 #include "diag_kernels.hpp"
 #include "page_kernels.hpp"
 #include "select_kernels.hpp"
@@ -215,7 +216,9 @@ Layout make_layout(const Dims& d, int64_t max_n, int64_t k) {
   Layout L{};
   const int64_t U = d.units;
   const int64_t exact_slots = U * cdiv(max_n, exact_chunk_floor(U, max_n));
-  const int64_t sparse_slots = U * std::min<int64_t>(kSparseMaxChunks, cdiv(k, kSparseChunkUnit));
+  // sparse pass: up to kSparseMaxChunks chunks per unit, plus one per unit for
+  // per-unit counts (each head's last chunk may be partly empty)
+  const int64_t sparse_slots = U * (std::min<int64_t>(kSparseMaxChunks, cdiv(k, kSparseChunkUnit)) + 1);
   L.slots = std::max(exact_slots, sparse_slots);
   const int64_t nchunk = cdiv(max_n, kLocalChunk);
   L.cand_stride = nchunk * kLocalChunk;
@@ -361,18 +364,29 @@ mage_status launch_topk(const TopkParams& tp, const HistReduceParams& hr, hipStr
       return st;
   }
   if (mage_status st = launch(kfn(hist_reduce_kernel), "hist_reduce_kernel",
-                              static_cast<int64_t>(hr.rows) * (kHistBins / 256), 256, stream, hr);
+                              static_cast<int64_t>(hr.rows) * (kHistBins / 256), kHistReduceThreads, stream, hr);
       st != MAGE_OK)
     return st;
   if (mage_status st = launch(kfn(topk_local_kernel), "topk_local_kernel", wgs, kLocalThreads, stream, tp);
       st != MAGE_OK)
     return st;
-  return launch(kfn(topk_final_kernel), "topk_final_kernel", tp.rows, kTopkThreads, stream, tp);
+  // the wide final pass for large k: more candidates stay on the register path
+  if (tp.k > kFinalMax / 2)
+    return launch(kfn(topk_final_kernel<kFinalMaxWide>), "topk_final_kernel", tp.rows, kTopkThreads, stream, tp);
+  return launch(kfn(topk_final_kernel<kFinalMax>), "topk_final_kernel", tp.rows, kTopkThreads, stream, tp);
 }
 
 struct PagePlan;
 mage_status launch_page_topk(const Dims& d, const KvArgs& kv, const float* scores, int64_t stride,
                              const PagePlan& pp, int32_t* idx, void* ws, const Layout& L, hipStream_t stream);
+
+// Head-adaptive budgets: k_per_head * Hkv positions per sequence; counts [S][Hkv].
+struct BudgetPlan {
+  int32_t k_per_head;
+  int32_t* counts;
+};
+mage_status launch_budget_topk(const Dims& d, const KvArgs& kv, float* scores, int64_t stride,
+                               const BudgetPlan& bp, int32_t* idx, void* ws, const Layout& L, hipStream_t stream);
 
 // Page-granular selection: P positions per page and k_pages pages per row;
 // page_idx may be null (then the workspace holds it).
@@ -387,7 +401,7 @@ template <int D>
 mage_status launch_select(const Dims& d, const uint16_t* q, const KvArgs& kv, int32_t k, float* o,
                           float* lse, int32_t* idx, float* scores, int64_t score_stride, void* ws,
                           const Layout& L, hipStream_t attn, hipStream_t sel, hipEvent_t idx_ready,
-                          const PagePlan* pages = nullptr) {
+                          const PagePlan* pages = nullptr, const BudgetPlan* budget = nullptr) {
   const int64_t U = d.units;
   const int chunk = exact_chunk(U, kv.max_n, kv.total_keys, kv.src.page_table ? (1 << kv.src.page_shift) : 0,
                                 kv.src.page_table ? kv.lens.n : nullptr, d.S, d.Hkv);
@@ -463,9 +477,10 @@ mage_status launch_select(const Dims& d, const uint16_t* q, const KvArgs& kv, in
                               score_grid, kThreads, sel, sp);
       st != MAGE_OK)
     return st;
-  if (pages) {
-    if (mage_status st = launch_page_topk(d, kv, sp.scores, sp.stride, *pages, idx, ws, L, sel); st != MAGE_OK)
-      return st;
+  if (pages || budget) {
+    mage_status st = pages ? launch_page_topk(d, kv, sp.scores, sp.stride, *pages, idx, ws, L, sel)
+                           : launch_budget_topk(d, kv, sp.scores, sp.stride, *budget, idx, ws, L, sel);
+    if (st != MAGE_OK) return st;
     if (idx_ready) {
       if (hipError_t e = hipEventRecord(idx_ready, sel); e != hipSuccess)
         return hip_fail(e, "hipEventRecord(idx_ready)");
@@ -506,6 +521,67 @@ mage_status launch_select(const Dims& d, const uint16_t* q, const KvArgs& kv, in
       return hip_fail(e, "hipEventRecord(idx_ready)");
   }
   return MAGE_OK;
+}
+
+// One top-k per sequence over its Hkv score rows taken as one row (entry
+// h * stride + p), then the split into per-head rows and counts.
+mage_status launch_budget_topk(const Dims& d, const KvArgs& kv, float* scores, int64_t stride,
+                               const BudgetPlan& bp, int32_t* idx, void* ws, const Layout& L, hipStream_t stream) {
+  const bool ragged = kv.src.page_table != nullptr;
+  const int64_t row_len = stride * d.Hkv;
+  if (row_len > kMaxTopkLen) return fail(MAGE_ERR_UNSUPPORTED, "num_kv_heads * prefix length must be <= 2^25");
+  if (ragged) {
+    GapZeroParams gz{};
+    gz.scores = scores;
+    gz.stride = stride;
+    gz.rows = d.units;
+    gz.rows_per_seq = d.Hkv;
+    gz.lens = kv.lens;
+    if (mage_status st = launch(kfn(gap_zero_kernel), "gap_zero_kernel", d.units, 256, stream, gz); st != MAGE_OK)
+      return st;
+  }
+  const int32_t K = bp.k_per_head * d.Hkv;
+  int32_t* gidx = at<int32_t>(ws, L.page_idx);   // [S][K]
+  TopkParams tp{};
+  tp.scores = scores;
+  tp.stride = row_len;
+  tp.idx = gidx;
+  tp.k = K;
+  tp.hist = at<uint32_t>(ws, L.hist);
+  tp.hist_parts = at<uint32_t>(ws, L.hist_parts);
+  tp.cand_bits = at<uint32_t>(ws, L.cand_bits);
+  tp.cand_pos = at<int32_t>(ws, L.cand_pos);
+  tp.nchunk = static_cast<int>(cdiv(row_len, kLocalChunk));
+  tp.cand_stride = static_cast<int64_t>(tp.nchunk) * kLocalChunk;
+  tp.cand_count = at<int32_t>(ws, L.cand_count);
+  tp.row_info = at<int32_t>(ws, L.row_info);
+  tp.rows = d.S;
+  tp.rows_per_seq = 1;
+  tp.n_uniform = static_cast<int32_t>(row_len);
+  std::memset(&tp.lens, 0, sizeof tp.lens);
+  tp.map = topk_map(tp, d.S);
+  HistReduceParams hr{};
+  hr.parts = tp.hist_parts;
+  hr.hist = tp.hist;
+  hr.rows = tp.rows;
+  hr.nparts = tp.nchunk;
+  hr.part_len = kLocalChunk;
+  hr.rows_per_seq = 1;
+  hr.n_uniform = tp.n_uniform;
+  hr.k = K;
+  hr.lens = tp.lens;
+  if (mage_status st = launch_topk(tp, hr, stream, true); st != MAGE_OK) return st;
+  BudgetSplitParams bs{};
+  bs.gidx = gidx;
+  bs.idx = idx;
+  bs.counts = bp.counts;
+  bs.stride = stride;
+  bs.S = d.S;
+  bs.Hkv = d.Hkv;
+  bs.K = K;
+  bs.n_uniform = ragged ? -1 : kv.src.n_uniform;
+  bs.lens = kv.lens;
+  return launch(kfn(budget_split_kernel), "budget_split_kernel", d.units, 256, stream, bs);
 }
 
 // Page scores, the top k_pages pages of every row (the standalone top-k path
@@ -581,9 +657,25 @@ template <int D>
 mage_status launch_sparse(const Dims& d, const uint16_t* q, const KvArgs& kv, const int32_t* idx,
                           int32_t k, float* o, float* lse, void* ws, const Layout& L,
                           hipStream_t stream, const uint16_t* k_blk = nullptr,
-                          const uint16_t* v_blk = nullptr) {
+                          const uint16_t* v_blk = nullptr, const int32_t* counts = nullptr, int32_t k_seq = 0) {
   const int64_t U = d.units;
-  const int chunk = sparse_chunk(U, d.nrb, k);
+  int chunk = sparse_chunk(U, d.nrb, counts ? std::max(1, k_seq / d.Hkv) : k);
+  int64_t seq_slots = 0;
+  if (counts) {
+    // per-unit counts: a sequence's chunks are numbered densely; its heads
+    // hold at most k_seq entries, so cdiv(k_seq, chunk) + Hkv slots suffice.
+    // The chunk doubles until the grid fits one round of the CUs, but not past
+    // the average entries per head (a larger chunk hands a long head's entries
+    // to one work-group); it grows further only if the workspace needs it. A
+    // unit whose entries fit one chunk writes O itself.
+    auto slots_for = [&](int ch) { return cdiv(k_seq, ch) + d.Hkv; };
+    const int64_t avg = round_up(cdiv(k_seq, d.Hkv), kSparseChunkUnit);
+    while (chunk < kSparseMaxChunk && 2 * chunk <= avg && d.S * slots_for(chunk) * d.nrb > kCus)
+      chunk = std::min(kSparseMaxChunk, 2 * chunk);
+    while (chunk < kSparseMaxChunk && d.S * slots_for(chunk) > L.slots) chunk = std::min(kSparseMaxChunk, 2 * chunk);
+    if (d.S * slots_for(chunk) > L.slots) return fail(MAGE_ERR_UNSUPPORTED, "workspace plan too small for k_seq");
+    seq_slots = slots_for(chunk);
+  }
   const int nch = static_cast<int>(cdiv(k, chunk));   // block rows, if any, ride in the last chunk
   AttnParams ap{};
   ap.q = q;
@@ -601,12 +693,14 @@ mage_status launch_sparse(const Dims& d, const uint16_t* q, const KvArgs& kv, co
   ap.lens = kv.lens;
   ap.k_blk = k_blk;
   ap.v_blk = v_blk;
-  const int64_t grid = round_up(U * nch, 8) * d.nrb;
+  ap.counts = counts;
+  ap.seq_slots = static_cast<int32_t>(seq_slots);
+  const int64_t grid = round_up(counts ? d.S * seq_slots : U * nch, 8) * d.nrb;
   if (mage_status st = launch(kfn(sparse_attn_kernel<D, kSparseStages>), "sparse_attn_kernel", grid,
                               kSparseThreads, stream, ap);
       st != MAGE_OK)
     return st;
-  if (nch == 1) return MAGE_OK;  // the single chunk wrote O and lse
+  if (nch == 1 && !counts) return MAGE_OK;  // the single chunk wrote O and lse
   MergeParams mp{};
   mp.part_o = ap.part_o;
   mp.part_ml = ap.part_ml;
@@ -616,7 +710,9 @@ mage_status launch_sparse(const Dims& d, const uint16_t* q, const KvArgs& kv, co
   mp.S = d.S; mp.B = d.B; mp.Hq = d.Hq; mp.Hkv = d.Hkv; mp.G = d.G; mp.R = d.R; mp.nrb = d.nrb;
   mp.chunk = chunk;
   mp.nchunk = nch;
-  mp.n_uniform = k;  // every unit has k index entries
+  mp.n_uniform = k;  // every unit has k index entries (per-unit counts: at most k)
+  mp.counts = counts;
+  mp.seq_slots = static_cast<int32_t>(seq_slots);
   std::memset(&mp.lens, 0, sizeof mp.lens);
   return launch(kfn(exact_merge_kernel<D>), "exact_merge_kernel[sparse]", U * d.nrb * (D / 32),
                 kThreads, stream, mp);
@@ -858,6 +954,52 @@ mage_status mage_select_pages_paged(const mage_dims* dims, const uint16_t* q, co
                                         select_stream, idx_ready, &pp);
 }
 
+mage_status mage_select_adaptive(const mage_dims* dims, const uint16_t* q, const uint16_t* k_cache,
+                                 const uint16_t* v_cache, int32_t seq_len, int32_t k, float* o, float* lse,
+                                 int32_t* idx, int32_t* counts, void* workspace, size_t workspace_bytes,
+                                 hipStream_t attn_stream, hipStream_t select_stream, hipEvent_t idx_ready) {
+  CallScope scope;
+  Dims d;
+  if (mage_status st = check_dims(dims, d); st != MAGE_OK) return st;
+  if (mage_status st = common_select_checks(q, k, o, lse, idx, nullptr); st != MAGE_OK) return st;
+  if (!counts || !aligned(counts, 4)) return fail(MAGE_ERR_INVALID_ARG, "counts must be non-null and 4-byte aligned");
+  if (static_cast<int64_t>(k) * d.Hkv > MAGE_MAX_SPARSE_K)
+    return fail(MAGE_ERR_UNSUPPORTED, "k * num_kv_heads must be <= MAGE_MAX_SPARSE_K");
+  KvArgs kv;
+  if (mage_status st = contiguous_kv(d, k_cache, v_cache, seq_len, kv); st != MAGE_OK) return st;
+  const int32_t K = k * d.Hkv;
+  const Layout L = make_layout(d, kv.max_n, K);
+  if (mage_status st = check_ws(workspace, workspace_bytes, L); st != MAGE_OK) return st;
+  const BudgetPlan bp{k, counts};
+  return d.D == 128 ? launch_select<128>(d, q, kv, K, o, lse, idx, nullptr, 0, workspace, L, attn_stream,
+                                         select_stream, idx_ready, nullptr, &bp)
+                    : launch_select<64>(d, q, kv, K, o, lse, idx, nullptr, 0, workspace, L, attn_stream,
+                                        select_stream, idx_ready, nullptr, &bp);
+}
+
+mage_status mage_select_adaptive_paged(const mage_dims* dims, const uint16_t* q, const mage_paged_kv* kvp,
+                                       int32_t k, float* o, float* lse, int32_t* idx, int32_t* counts,
+                                       void* workspace, size_t workspace_bytes, hipStream_t attn_stream,
+                                       hipStream_t select_stream, hipEvent_t idx_ready) {
+  CallScope scope;
+  Dims d;
+  if (mage_status st = check_dims(dims, d); st != MAGE_OK) return st;
+  if (mage_status st = common_select_checks(q, k, o, lse, idx, nullptr); st != MAGE_OK) return st;
+  if (!counts || !aligned(counts, 4)) return fail(MAGE_ERR_INVALID_ARG, "counts must be non-null and 4-byte aligned");
+  if (static_cast<int64_t>(k) * d.Hkv > MAGE_MAX_SPARSE_K)
+    return fail(MAGE_ERR_UNSUPPORTED, "k * num_kv_heads must be <= MAGE_MAX_SPARSE_K");
+  KvArgs kv;
+  if (mage_status st = paged_kv(d, kvp, kv); st != MAGE_OK) return st;
+  const int32_t K = k * d.Hkv;
+  const Layout L = make_layout(d, kv.max_n, K);
+  if (mage_status st = check_ws(workspace, workspace_bytes, L); st != MAGE_OK) return st;
+  const BudgetPlan bp{k, counts};
+  return d.D == 128 ? launch_select<128>(d, q, kv, K, o, lse, idx, nullptr, 0, workspace, L, attn_stream,
+                                         select_stream, idx_ready, nullptr, &bp)
+                    : launch_select<64>(d, q, kv, K, o, lse, idx, nullptr, 0, workspace, L, attn_stream,
+                                        select_stream, idx_ready, nullptr, &bp);
+}
+
 mage_status mage_mean_query(const mage_dims* dims, const uint16_t* q, uint16_t* qbar, hipStream_t stream) {
   CallScope scope;
   Dims d;
@@ -964,6 +1106,46 @@ mage_status mage_sparse_block_attn_paged(const mage_dims* dims, const uint16_t* 
   if (mage_status st = check_ws(workspace, workspace_bytes, L); st != MAGE_OK) return st;
   return d.D == 128 ? launch_sparse<128>(d, q, kv, idx, k, o, lse, workspace, L, stream, k_blk, v_blk)
                     : launch_sparse<64>(d, q, kv, idx, k, o, lse, workspace, L, stream, k_blk, v_blk);
+}
+
+static mage_status counts_checks(const int32_t* counts, int32_t k_seq) {
+  if (!counts || !aligned(counts, 4)) return fail(MAGE_ERR_INVALID_ARG, "counts must be non-null and 4-byte aligned");
+  if (k_seq < 1) return fail(MAGE_ERR_INVALID_ARG, "k_seq must be >= 1");
+  return MAGE_OK;
+}
+
+mage_status mage_sparse_attn_counts(const mage_dims* dims, const uint16_t* q, const uint16_t* k_cache,
+                                    const uint16_t* v_cache, int32_t seq_len, const int32_t* idx, int32_t k_row,
+                                    const int32_t* counts, int32_t k_seq, float* o, float* lse, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream) {
+  CallScope scope;
+  Dims d;
+  if (mage_status st = sparse_common(dims, q, idx, k_row, o, lse, d); st != MAGE_OK) return st;
+  if (mage_status st = counts_checks(counts, k_seq); st != MAGE_OK) return st;
+  KvArgs kv;
+  if (mage_status st = contiguous_kv(d, k_cache, v_cache, seq_len, kv); st != MAGE_OK) return st;
+  const Layout L = make_layout(d, kv.max_n, k_row);
+  if (mage_status st = check_ws(workspace, workspace_bytes, L); st != MAGE_OK) return st;
+  return d.D == 128
+             ? launch_sparse<128>(d, q, kv, idx, k_row, o, lse, workspace, L, stream, nullptr, nullptr, counts, k_seq)
+             : launch_sparse<64>(d, q, kv, idx, k_row, o, lse, workspace, L, stream, nullptr, nullptr, counts, k_seq);
+}
+
+mage_status mage_sparse_attn_counts_paged(const mage_dims* dims, const uint16_t* q, const mage_paged_kv* kvp,
+                                          const int32_t* idx, int32_t k_row, const int32_t* counts, int32_t k_seq,
+                                          float* o, float* lse, void* workspace, size_t workspace_bytes,
+                                          hipStream_t stream) {
+  CallScope scope;
+  Dims d;
+  if (mage_status st = sparse_common(dims, q, idx, k_row, o, lse, d); st != MAGE_OK) return st;
+  if (mage_status st = counts_checks(counts, k_seq); st != MAGE_OK) return st;
+  KvArgs kv;
+  if (mage_status st = paged_kv(d, kvp, kv); st != MAGE_OK) return st;
+  const Layout L = make_layout(d, kv.max_n, k_row);
+  if (mage_status st = check_ws(workspace, workspace_bytes, L); st != MAGE_OK) return st;
+  return d.D == 128
+             ? launch_sparse<128>(d, q, kv, idx, k_row, o, lse, workspace, L, stream, nullptr, nullptr, counts, k_seq)
+             : launch_sparse<64>(d, q, kv, idx, k_row, o, lse, workspace, L, stream, nullptr, nullptr, counts, k_seq);
 }
 
 mage_status mage_block_attn(const mage_dims* dims, const uint16_t* q, const uint16_t* k_blk,

@@ -119,25 +119,33 @@ struct HistReduceParams {
   SeqLens lens;
 };
 
-__global__ __launch_bounds__(256) void hist_reduce_kernel(HistReduceParams p) {
+// Work-group = 256 bins x 4 slices of the parts (1024 threads): slice t sums
+// parts t*8 .. t*8+7, then every 32nd batch after it, eight loads in flight
+// per step; the four slice sums meet in LDS. Rows with many parts (long
+// prefixes, or one row per sequence over all its heads) then wait for a
+// quarter of the dependent steps.
+constexpr int kHistReduceThreads = 1024;
+__global__ __launch_bounds__(kHistReduceThreads) void hist_reduce_kernel(HistReduceParams p) {
   constexpr int kBlocks = kHistBins / 256;
-  const int u = blockIdx.x / kBlocks, b = (blockIdx.x % kBlocks) * 256 + threadIdx.x;
+  __shared__ uint32_t s_sum[3][256];
+  const int u = blockIdx.x / kBlocks, bl = threadIdx.x & 255, slice = threadIdx.x >> 8;
+  const int b = (blockIdx.x % kBlocks) * 256 + bl;
   if (u >= p.rows) return;
   const int n = p.n_uniform >= 0 ? p.n_uniform : p.lens.n[u / p.rows_per_seq];
   if (min(p.k, n) == n) return;
   const int np = (n + p.part_len - 1) / p.part_len;
   const uint32_t* src = p.parts + static_cast<int64_t>(u) * p.nparts * kHistBins + b;
   uint32_t sum = 0;
-  int j = 0;
-  for (; j + 8 <= np; j += 8) {   // eight loads in flight per step
+  for (int j = slice * 8; j < np; j += 32) {
     uint32_t x[8];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) x[q] = src[static_cast<int64_t>(j + q) * kHistBins];
+    for (int q = 0; q < 8; ++q) x[q] = j + q < np ? src[static_cast<int64_t>(j + q) * kHistBins] : 0u;
 #pragma unroll
     for (int q = 0; q < 8; ++q) sum += x[q];
   }
-  for (; j < np; ++j) sum += src[static_cast<int64_t>(j) * kHistBins];
-  p.hist[static_cast<int64_t>(u) * kHistBins + b] = sum;
+  if (slice > 0) s_sum[slice - 1][bl] = sum;
+  __syncthreads();
+  if (slice == 0) p.hist[static_cast<int64_t>(u) * kHistBins + b] = sum + s_sum[0][bl] + s_sum[1][bl] + s_sum[2][bl];
 }
 
 struct ScoreParams {
@@ -337,10 +345,12 @@ __global__ __launch_bounds__(kThreads) void score_kernel(ScoreParams p) {
 // top-k
 
 // Final selection work-group: 1024 threads; its register path holds up to
-// kFinalMax entries (8 per thread).
+// kFinalMax entries (8 per thread), or kFinalMaxWide (12 per thread, for
+// large k: 96 KiB of LDS staging) in the wide variant.
 constexpr int kTopkThreads = 1024;
 constexpr int kTopkWaves = kTopkThreads / kWave;
 constexpr int kFinalMax = 8192;
+constexpr int kFinalMaxWide = 12288;
 // Candidate pass: one 256-thread work-group per 4096-position chunk.
 constexpr int kLocalThreads = 256;
 constexpr int kLocalWaves = kLocalThreads / kWave;
@@ -945,8 +955,9 @@ __device__ void wave_select_in_bin(const uint32_t* cand, int m, int rem, uint32_
 // chunk order, are in position order; the kk-th largest among them is the
 // row's kk-th largest (all larger scores are candidates), and the ordered
 // compaction keeps ties at the lowest positions, so the output is ascending.
+template <int kMax>
 __global__ __launch_bounds__(kTopkThreads) void topk_final_kernel(TopkParams p) {
-  __shared__ uint32_t s_data[2 * kFinalMax];   // bits, then positions
+  __shared__ uint32_t s_data[2 * kMax];   // bits, then positions
   __shared__ int32_t s_off[kMaxLocalChunks + 1];
   __shared__ TopkShared sh;
   const int tid = threadIdx.x;
@@ -988,8 +999,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_final_kernel(TopkParams p) 
   };
   uint32_t T;
   int need;
-  if (total <= kFinalMax) {
-    constexpr int kPer = kFinalMax / kTopkThreads;
+  if (total <= kMax) {
+    constexpr int kPer = kMax / kTopkThreads;
     {
       uint32_t vb[kPer];
       int32_t vp[kPer];
@@ -1003,13 +1014,13 @@ __global__ __launch_bounds__(kTopkThreads) void topk_final_kernel(TopkParams p) 
 #pragma unroll
       for (int j = 0; j < kPer; ++j) {
         s_data[tid + j * kTopkThreads] = vb[j];
-        s_data[kFinalMax + tid + j * kTopkThreads] = static_cast<uint32_t>(vp[j]);
+        s_data[kMax + tid + j * kTopkThreads] = static_cast<uint32_t>(vp[j]);
       }
     }
     __syncthreads();
     uint32_t v[kPer], vpos[kPer];
     load_run<kPer>(s_data, v);
-    load_run<kPer>(s_data + kFinalMax, vpos);
+    load_run<kPer>(s_data + kMax, vpos);
     MAGE_TRACE_POINT(5);
     int eq_total;
     const int b_star = p.row_info[2 * u], above = p.row_info[2 * u + 1];

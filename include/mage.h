@@ -261,6 +261,56 @@ mage_status mage_select_pages_paged(const mage_dims* dims, const uint16_t* q,
                                     hipEvent_t idx_ready);
 
 /*
+ * Head-adaptive budgets (Step-dLLM page, abstract: one global budget shared
+ * by the heads, compressing heads with concentrated attention harder). Step 1
+ * as mage_select_exact, except that each sequence keeps the K = k * Hkv
+ * largest block-averaged scores over all of its (KV head, position) pairs,
+ * ties to the lower head, then the lower position: head h keeps counts[s][h]
+ * positions (a head whose scores sit on few positions keeps few, a diffuse
+ * head many; the counts of a sequence sum to min(K, Hkv * N_s)). Outputs
+ * idx int32 [S][Hkv][K], each row ascending then -1, and counts int32
+ * [S][Hkv] (device, not null, 4-byte aligned). o/lse/streams/idx_ready as
+ * for mage_select_exact; no scores output. k * Hkv <= MAGE_MAX_SPARSE_K and
+ * Hkv * N <= 2^25, else MAGE_ERR_UNSUPPORTED. Workspace:
+ * mage_workspace_bytes(dims, max_seq_len, k * num_kv_heads).
+ */
+mage_status mage_select_adaptive(const mage_dims* dims, const uint16_t* q,
+                                 const uint16_t* k_cache, const uint16_t* v_cache,
+                                 int32_t seq_len, int32_t k, float* o, float* lse, int32_t* idx,
+                                 int32_t* counts, void* workspace, size_t workspace_bytes,
+                                 hipStream_t attn_stream, hipStream_t select_stream,
+                                 hipEvent_t idx_ready);
+
+mage_status mage_select_adaptive_paged(const mage_dims* dims, const uint16_t* q,
+                                       const mage_paged_kv* kv, int32_t k, float* o, float* lse,
+                                       int32_t* idx, int32_t* counts, void* workspace,
+                                       size_t workspace_bytes, hipStream_t attn_stream,
+                                       hipStream_t select_stream, hipEvent_t idx_ready);
+
+/*
+ * A later step with per-head entry counts (the index rows of
+ * mage_select_adaptive): unit (s, h) attends over idx[s][h][0 .. min(counts,
+ * k_row)), where k_row is the row length of idx (entries outside [0, N_s)
+ * are skipped as in mage_sparse_attn). Work scales with the counts, not with
+ * k_row: a sequence's chunks are numbered densely, planned for at most k_seq
+ * entries per sequence (sum over its heads of min(counts, k_row)); chunks
+ * beyond that plan are not computed. counts: device int32 [S][Hkv], not null,
+ * 4-byte aligned; k_seq >= 1; other arguments and the workspace as for
+ * mage_sparse_attn with k = k_row. A head with count 0 gets O = 0, lse = -inf.
+ */
+mage_status mage_sparse_attn_counts(const mage_dims* dims, const uint16_t* q,
+                                    const uint16_t* k_cache, const uint16_t* v_cache,
+                                    int32_t seq_len, const int32_t* idx, int32_t k_row,
+                                    const int32_t* counts, int32_t k_seq, float* o, float* lse,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+mage_status mage_sparse_attn_counts_paged(const mage_dims* dims, const uint16_t* q,
+                                          const mage_paged_kv* kv, const int32_t* idx,
+                                          int32_t k_row, const int32_t* counts, int32_t k_seq,
+                                          float* o, float* lse, void* workspace,
+                                          size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Anchor re-selection diagnostics. The Step-dLLM page (abstract) refreshes the
  * sparse set at anchor steps and reuses it in between; re-running
  * mage_select_exact with an anchor step's queries is that refresh, and the

@@ -254,3 +254,26 @@ def test_select_pages_argument_checks():
     args = list(okp)
     args[3] = 0
     assert lib.mage_select_pages_paged(*args) == mage.ERR_INVALID_ARG
+
+
+def test_adaptive_budget_argument_checks():
+    lib = mage.lib()
+    d = dims()
+    # dims, q, k_cache, v_cache, seq_len, k, o, lse, idx, counts, ws, bytes, attn, select, event
+    ok = [ctypes.byref(d), FAKE, FAKE, FAKE, 1024, 64, FAKE, None, FAKE, FAKE, FAKE, 1 << 40, None, None, None]
+    for i, bad, st in ((9, None, mage.ERR_INVALID_ARG), (9, ctypes.c_void_p((1 << 20) + 2), mage.ERR_INVALID_ARG),
+                       (5, 0, mage.ERR_INVALID_ARG), (5, 1 << 15, mage.ERR_UNSUPPORTED), (8, None, mage.ERR_INVALID_ARG)):
+        args = list(ok)
+        args[i] = bad
+        assert lib.mage_select_adaptive(*args) == st, (i, bad)
+    pk = mage.PagedKv()
+    okp = [ctypes.byref(d), FAKE, ctypes.byref(pk), 64, FAKE, None, FAKE, FAKE, FAKE, 1 << 40, None, None, None]
+    assert lib.mage_select_adaptive_paged(*okp) == mage.ERR_INVALID_ARG
+    # counts step: dims, q, k_cache, v_cache, seq_len, idx, k_row, counts, k_seq, o, lse, ws, bytes, stream
+    oks = [ctypes.byref(d), FAKE, FAKE, FAKE, 1024, FAKE, 64, FAKE, 512, FAKE, None, FAKE, 1 << 40, None]
+    for i, bad in ((7, None), (8, 0), (6, 0), (5, None)):
+        args = list(oks)
+        args[i] = bad
+        assert lib.mage_sparse_attn_counts(*args) == mage.ERR_INVALID_ARG, (i, bad)
+    okps = [ctypes.byref(d), FAKE, ctypes.byref(pk), FAKE, 64, FAKE, 512, FAKE, None, FAKE, 1 << 40, None]
+    assert lib.mage_sparse_attn_counts_paged(*okps) == mage.ERR_INVALID_ARG
