@@ -584,15 +584,14 @@ def run_bench(args):
         warm_timers.append(tm)
     r.select()
     torch.cuda.synchronize()
-    blk_timers = []
-    for t in range(5):
+    blk_timers, fused_timers = [], []
+    for t in range(0 if args.no_diag else 5):
         r.sparse(t)
         fl()
         tm = KernelTimer(torch, 1)
         r.block(t, tm)
         blk_timers.append(tm)
-    fused_timers = []
-    for t in range(5):
+    for t in range(0 if args.no_diag else 5):
         fl()
         tm = KernelTimer(torch, 2)
         r.sparse_block(t, tm)
@@ -629,8 +628,6 @@ def run_bench(args):
     ex_busy = [t.busy_ms() * 1e3 for t in ex_timers]
     warm_busy = [t.busy_ms() * 1e3 for t in warm_timers]
     tk_busy = [t.busy_ms() * 1e3 for t in tk_timers]
-    blk_med = statistics.median([t.busy_ms() * 1e3 for t in blk_timers])
-    fused_med = statistics.median([t.busy_ms() * 1e3 for t in fused_timers])
     empty_us = statistics.median([a.elapsed_time(b) * 1e3 for a, b in empty])
 
     sp_mean = statistics.mean(sp_busy)
@@ -651,17 +648,32 @@ def run_bench(args):
     traffic = traffic_record(w.name)
     us = lambda v: round(v, 2)  # noqa: E731
     t0 = time.perf_counter()
-    pages = page_diag(torch, mage, r, w, fl)
-    budgets = budget_diag(torch, mage, r, w, fl)
+    diag = {}
+    if not args.no_diag:
+        blk_med = statistics.median([t.busy_ms() * 1e3 for t in blk_timers])
+        fused_med = statistics.median([t.busy_ms() * 1e3 for t in fused_timers])
+        diag["block_attn"] = {
+            "gpu_us_median": us(blk_med), "bytes": block_bytes(w),
+            "GBps": round(block_bytes(w) / (blk_med * 1e-6) / 1e9, 1),
+            "sparse_plus_block_us": us(statistics.median(sp_busy) + blk_med),
+            "fused_step_gpu_us_median": us(fused_med),
+            "fused_step_kernels_us_median": {n: us(statistics.median(v)) for n, v in by_kernel(fused_timers).items()},
+            "note": "cold, not part of value: gpu_us_median = the block's queries over its own B rows merged "
+                    "into a sparse step's output through log-sum-exp (separate launch); fused_step = the "
+                    "sparse step with the block rows as one more tile per wave of the last split (one call)"}
+        diag["page_selection"] = page_diag(torch, mage, r, w, fl)
+        diag["head_adaptive_budgets"] = budget_diag(torch, mage, r, w, fl)
     log(f"[bench] page-granular selection measured")
     sp_med = statistics.median(sp_busy)
-    anchor = {"iid": anchor_diag(torch, mage, r, w, [r.q1] + r.qs[:T - 1], sel_med, sp_med),
-              "walk": anchor_diag(torch, mage, r, w,
-                                  [r.q1] + [q.to(dev) for q in workloads.walk_queries(w)], sel_med, sp_med),
-              "note": "recall = |set in use ∩ step's own top-k| / |own|, mean over (seq, KV head) and "
-                      "steps 2..T; iid: the workload's fresh per-step noise around Q1; walk: Q_t = "
-                      "Q_(t-1) + N(0, (sigma*sqrt(2/T))^2), a random walk from Q1; block_us = anchors x "
-                      "cold exact+select + the rest x cold sparse step"}
+    if not args.no_diag:
+        diag["anchor_recall"] = {
+            "iid": anchor_diag(torch, mage, r, w, [r.q1] + r.qs[:T - 1], sel_med, sp_med),
+            "walk": anchor_diag(torch, mage, r, w, [r.q1] + [q.to(dev) for q in workloads.walk_queries(w)],
+                                sel_med, sp_med),
+            "note": "recall = |set in use ∩ step's own top-k| / |own|, mean over (seq, KV head) and "
+                    "steps 2..T; iid: the workload's fresh per-step noise around Q1; walk: Q_t = "
+                    "Q_(t-1) + N(0, (sigma*sqrt(2/T))^2), a random walk from Q1; block_us = anchors x "
+                    "cold exact+select + the rest x cold sparse step"}
     torch.cuda.synchronize()
     log(f"[bench] anchor/recall diagnostic in {time.perf_counter() - t0:.1f} s")
     out = {
@@ -717,20 +729,6 @@ def run_bench(args):
                          "first_step_overhead": round(sel_med / ex_med - 1, 4),
                          "instrumented_span_us_median": round(statistics.median(sel_span), 1),
                          "event_pair_us_median": round(statistics.median([t.outer_ms() * 1e3 for t in sel_timers]), 1)},
-        "block_attn": {"gpu_us_median": us(blk_med), "bytes": block_bytes(w),
-                       "GBps": round(block_bytes(w) / (blk_med * 1e-6) / 1e9, 1),
-                       "sparse_plus_block_us": us(statistics.median(sp_busy) + blk_med),
-                       "fused_step_gpu_us_median": us(fused_med),
-                       "fused_step_kernels_us_median": {n: us(v) for n, v in
-                                                        ((n, statistics.median(v)) for n, v in
-                                                         by_kernel(fused_timers).items())},
-                       "note": "cold, not part of value: gpu_us_median = the block's queries over "
-                               "its own B rows merged into a sparse step's output through "
-                               "log-sum-exp (separate launch); fused_step = the sparse step with "
-                               "the block rows as one more split (one call)"},
-        "anchor_recall": anchor,
-        "page_selection": pages,
-        "head_adaptive_budgets": budgets,
         "speedup_vs_exact_per_step": round(ex_med / statistics.median(sp_busy), 2),
         "wall_s_timed_region": round(wall, 3),
         "flushes_in_timed_region": args.steps * T if args.flush != "none" else 0,
@@ -738,6 +736,7 @@ def run_bench(args):
         "gpu": torch.cuda.get_device_name(0),
         "kernel_source_digest": source_digest(),
     }
+    out.update(diag)
     if traffic is not None:
         out["roofline"]["traffic_source"] = f"profiles/sparse_traffic_{w.name}.md"
     if not args.no_cpu:
@@ -851,6 +850,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", default="head128k", choices=sorted(workloads.CONFIG_BY_NAME))
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--no-diag", action="store_true",
+                    help="skip the next-row measurements (block attention, anchors and recall, page "
+                         "selection, head-adaptive budgets): profiler runs of the main path")
     ap.add_argument("--flush", choices=sorted(FLUSH_DESC), default="clean",
                     help="cache state before each timed call")
     ap.add_argument("--no-flush", action="store_true", help="same as --flush none")

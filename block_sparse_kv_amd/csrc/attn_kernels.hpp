@@ -611,26 +611,22 @@ struct SparseTile {
 
 // DMA of one 32-key tile by one wave. K: row-major, unit u of row r at unit
 // u ^ (r mod kUnits). V: [d/32][32 rows][32 values]. row(r) = element offset
-// of tile row r (always a readable row). The loads are asm (per-lane 64-bit
-// addresses): the compiler does not know they write LDS, so LDS reads of the
-// row table between issues do not make it wait for the tiles in flight; the
-// caller waits with vmcnt before it reads a tile.
+// of tile row r (always a readable row).
 template <int D, class RowOff>
 __device__ __forceinline__ void issue_sparse_tile(uint8_t* k_lds, uint8_t* v_lds, const uint16_t* kbase,
                                                   const uint16_t* vbase, RowOff row, int lane) {
   using T = SparseTile<D>;
-  const uint32_t kl = lds_addr(k_lds), vl = lds_addr(v_lds);
 #pragma unroll
   for (int j = 0; j < T::kInstr; ++j) {
     const int unit = j * kWave + lane;
     const int r = unit / T::kUnits, phys = unit % T::kUnits;
     const int uk = phys ^ (r & (T::kUnits - 1));
-    dma16_addr(kbase + row(r) + uk * 8, kl + j * 1024);
+    __builtin_amdgcn_global_load_lds(kbase + row(r) + uk * 8, k_lds + j * 1024, 16, 0, 0);
   }
 #pragma unroll
   for (int j = 0; j < T::kInstr; ++j) {
     const int db = j >> 1, r = ((j & 1) << 4) + (lane >> 2);
-    dma16_addr(vbase + row(r) + 32 * db + 8 * (lane & 3), vl + j * 1024);
+    __builtin_amdgcn_global_load_lds(vbase + row(r) + 32 * db + 8 * (lane & 3), v_lds + j * 1024, 16, 0, 0);
   }
 }
 

@@ -119,21 +119,6 @@ __device__ __forceinline__ void dma16_sync(const void* addr, uint32_t lds) {
       : "memory", "m0");
 }
 
-// One direct LDS load per lane from a per-lane 64-bit address, not waited for
-// here: completion is tracked with vmcnt by the caller. The instruction
-// returns nothing in a register (its data goes to LDS) and reads its address
-// operands when it issues, so the address registers are free once the block
-// ends. Used where every lane's row lies anywhere in memory (a gather).
-__device__ __forceinline__ void dma16_addr(const void* addr, uint32_t lds) {
-  asm volatile(
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %0, off"
-      :
-      : "v"(addr), "s"(lds)
-      : "memory", "m0");
-}
-
 // Issue the DMA loads of one tile. row_off(r) returns the element offset of
 // tile row r (0..63) in the K/V arrays; it must always name a readable row.
 template <int D, bool kWithV, int kNT = kThreads, class RowOff>
