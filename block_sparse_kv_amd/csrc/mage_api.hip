@@ -237,7 +237,7 @@ Layout make_layout(const Dims& d, int64_t max_n, int64_t k) {
   L.row_info = take(U * 2 * 4);
   L.hist = take(U * kHistBins * 4);
   // histogram parts: one per score chunk (standalone top-k: one per 4096-entry chunk)
-  L.hist_parts = take(U * cdiv(max_n, kScoreChunk) * kHistBins * 4);
+  L.hist_parts = take(U * cdiv(max_n, kScoreChunkMin) * kHistBins * 4);
   L.scores = take(U * max_n * 4);
   L.qbar = take(U * d.D * 2);
   L.qbar_o = take(U * d.D * 4);
@@ -466,7 +466,13 @@ mage_status launch_select(const Dims& d, const uint16_t* q, const KvArgs& kv, in
   sp.scores = scores ? scores : at<float>(ws, L.scores);
   sp.stride = scores ? score_stride : kv.max_n;
   sp.S = d.S; sp.B = d.B; sp.Hq = d.Hq; sp.Hkv = d.Hkv; sp.G = d.G; sp.R = d.R;
+  // positions per work-group: halved from kScoreChunk (down to kScoreChunkMin)
+  // until the sweep has two rounds of work-groups (two per CU fit at once)
   sp.chunk = kScoreChunk;
+  for (int64_t g = 0; sp.chunk > kScoreChunkMin; sp.chunk /= 2) {
+    chunk_map(kv, d, sp.chunk, g);
+    if (g >= 2 * kCus) break;
+  }
   sp.nchunk = static_cast<int>(cdiv(kv.max_n, sp.chunk));
   sp.reverse = env_int("MAGE_SCORE_REVERSE", 1);
   sp.scale_log2 = scale_log2;

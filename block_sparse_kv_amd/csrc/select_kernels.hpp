@@ -165,7 +165,8 @@ struct ScoreParams {
 
 // Positions per score work-group; sized so that two work-groups fit in one
 // CU's LDS. Each work-group stores its chunk's part of the row histogram.
-constexpr int kScoreChunk = 2048;
+constexpr int kScoreChunk = 2048;      // positions per work-group (largest)
+constexpr int kScoreChunkMin = 512;    // smallest, for short prefixes
 
 template <int D, int kStages>
 __global__ __launch_bounds__(kThreads) void score_kernel(ScoreParams p) {
