@@ -55,8 +55,6 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 METRIC = "sparse-step denoising steps/sec and HBM GB/s (% peak) at 128K ctx, k=1024, B=32"
 COPY_MIB = 256                 # size of the copy used to calibrate FETCH_SIZE / WRITE_SIZE
-KERNEL_SOURCES = ["attn_kernels.hpp", "tile_io.hpp", "mage_common.hpp", "select_kernels.hpp",
-                  "mage_api.hip"]
 
 
 def log(*a):
@@ -116,10 +114,13 @@ def exact_flops(w: workloads.Workload) -> float:
 
 
 def source_digest() -> str:
+    """Digest of every HIP source of the library (the counter records name the sources they were taken on)."""
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "block_sparse_kv_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+    csrc = os.path.join(ROOT, "block_sparse_kv_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hpp", ".hip")):
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
 
 
@@ -609,12 +610,19 @@ def run_bench(args):
         b.record()
         empty.append((a, b))
     # plain copy of known size: the calibration kernel for FETCH_SIZE / WRITE_SIZE counter runs
+    # (timed: the measured copy bandwidth, a second roofline beside the 8 TB/s spec)
     src = torch.ones(COPY_MIB * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
+    copy_ms = []
     for _ in range(2):
         fl()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
         torch.neg(src, out=dst)
+        b.record()
+        copy_ms.append((a, b))
     torch.cuda.synchronize()
+    copy_gbps = 2 * COPY_MIB * 1024 * 1024 / (min(a.elapsed_time(b) for a, b in copy_ms) * 1e-3) / 1e9
 
     sp_busy = [t.busy_ms() * 1e3 for t in sp_timers]
     sp_span = [t.span_ms() * 1e3 for t in sp_timers]
@@ -703,7 +711,9 @@ def run_bench(args):
                      "traffic": None if traffic is None else traffic["bytes_per_launch"],
                      "kernel": f"{chunk_name} (sparse gather + attention, one launch per step)",
                      "bytes_per_launch": cbytes, "kernel_us_mean": us(chunk_mean),
-                     "kernel_us_median": us(statistics.median(chunk_us)), "launches": len(chunk_us)},
+                     "kernel_us_median": us(statistics.median(chunk_us)), "launches": len(chunk_us),
+                     "copy_GBps_measured": round(copy_gbps, 1),
+                     "frac_of_measured_copy": round(achieved / copy_gbps, 4)},
         "sparse_step": {"bytes": sbytes, "gpu_us_mean": us(sp_mean),
                         "gpu_us_median": us(statistics.median(sp_busy)),
                         "gpu_us_p10": us(pct(sp_busy, 10)), "gpu_us_p90": us(pct(sp_busy, 90)),
@@ -843,6 +853,38 @@ def summarize_pmc(fetch_dir, write_dir, config):
         print("traffic: " + json.dumps(rec))
 
 
+def summarize_counters(d, config):
+    """Per kernel class, from one rocprofv3 --pmc run of MfmaUtil (rocprofv3's
+    derived metric: SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE times the
+    SIMD count), TCC_HIT_sum and TCC_MISS_sum: the MFMA busy share of the SIMD
+    cycles and the L2 hit rate."""
+    path = glob.glob(os.path.join(d, "*counter_collection.csv"))[0]
+    per = {}
+    for r in _dispatches(path):
+        key = int(r["Dispatch_Id"])
+        e = per.setdefault(key, {"name": _short(r["Kernel_Name"]),
+                                 "ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+        e[r["Counter_Name"]] = float(r["Counter_Value"])
+    keys = sorted(per)
+    cold = dict(zip(keys, _cold_flags([per[k]["name"] for k in keys])))
+    print(f"Config {config}. MfmaUtil = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x SIMDs), as rocprofv3 "
+          "derives it; L2 hit = TCC_HIT / (TCC_HIT + TCC_MISS). Cold dispatches (right after the flush) "
+          "are averaged where there are any.\n")
+    print("| kernel | dispatches (cold) | MFMA busy | L2 hit |")
+    print("|---|---|---|---|")
+    by = {}
+    for k in keys:
+        by.setdefault(per[k]["name"], []).append(k)
+    for n in sorted(by):
+        e = [per[k] for k in ([k for k in by[n] if cold[k]] or by[n])]
+        util = statistics.mean(x.get("MfmaUtil", 0.0) for x in e)
+        hit = statistics.mean(x.get("TCC_HIT_sum", 0.0) for x in e)
+        miss = statistics.mean(x.get("TCC_MISS_sum", 0.0) for x in e)
+        print(f"| {n} | {len(by[n])} ({sum(cold[k] for k in by[n])}) | {util:.1f}% | "
+              f"{'' if hit + miss == 0 else f'{100 * hit / (hit + miss):.1f}%'} |")
+    print()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -858,11 +900,15 @@ def main():
     ap.add_argument("--no-flush", action="store_true", help="same as --flush none")
     ap.add_argument("--summarize-trace", metavar="DIR")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--summarize-counters", metavar="DIR",
+                    help="MFMA busy, L2 hit rate and clock per kernel from a counter run")
     args = ap.parse_args()
     if args.summarize_trace:
         return summarize_trace(args.summarize_trace)
     if args.summarize_pmc:
         return summarize_pmc(*args.summarize_pmc, args.config)
+    if args.summarize_counters:
+        return summarize_counters(args.summarize_counters, args.config)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this library has no multi-GPU path; run with --gpus 1",
               file=sys.stderr)
