@@ -214,7 +214,7 @@ __device__ __forceinline__ void attend_half(uint32_t k_base, uint32_t v_addr,
 // barrier per tile. The loop is software-pipelined: in iteration t a wave
 // issues the QK product of tile t+1 and then runs the softmax and PV of tile
 // t, so the MFMAs of one tile run under the vector work of the other.
-template <int D, int kStages>
+template <int D, int kStages, bool kSplitIssue = true>
 __global__ __launch_bounds__(kAttnThreads) void exact_chunk_kernel(AttnParams p) {
   using G = TileGeom<D, kAttnThreads>;
   constexpr int kNdb = D / 32, kNks = D / 16;
@@ -331,10 +331,20 @@ __global__ __launch_bounds__(kAttnThreads) void exact_chunk_kernel(AttnParams p)
   // writes no VGPR that an in-flight load still reads. Other tiles take the
   // clamped per-lane path.
   constexpr int kKRowsPerInstr = kWave / G::kUnits;        // 4 at d = 128
+  // Tile loads are issued by the four key-half-1 waves only: wave w (w >= 4)
+  // issues the slices of waves w - 4 and w in two passes. Each SIMD holds one
+  // wave of each key half, so while one issues the next tiles the other is
+  // already in its MFMA region. The per-lane offsets of the slices of waves
+  // w - 4 and w are equal for K and kInstr d blocks apart for V.
+  // (kSplitIssue false, used for paged caches: every wave issues its own
+  // slices, since each slice's base needs a page-table lookup and one wave
+  // doing twice as many serializes them)
+  constexpr bool split_issue = kSplitIssue;
+  const bool issuer = !split_issue || w >= 4;
   uint32_t koff[G::kInstr], voff[G::kInstr];
 #pragma unroll
   for (int j = 0; j < G::kInstr; ++j) {
-    const int slot = w * G::kInstr + j;
+    const int slot = (w & 3) * G::kInstr + j;
     const int unit = slot * kWave + lane;
     const int r = unit / G::kUnits, uk = (unit % G::kUnits) ^ (r & (G::kUnits - 1));
     koff[j] = static_cast<uint32_t>(((r - slot * kKRowsPerInstr) * D + uk * 8) * 2);
@@ -360,22 +370,24 @@ __global__ __launch_bounds__(kAttnThreads) void exact_chunk_kernel(AttnParams p)
   // (either may be -1: none) go to their ring slots.
   const char* kbytes = reinterpret_cast<const char*>(p.kv.k);
   const char* vbytes = reinterpret_cast<const char*>(p.kv.v);
-  auto issue = [&](int tk, int tv) {
+  auto issue_slices = [&](int tk, int tv, int ws) {   // the slices of wave ws of the 8-wave layout
     const bool fk = tk >= 0 && fast_tile(tk), fv = tv >= 0 && fast_tile(tv);
     const int bk = tk >= 0 ? tile_base(tk) : 0, bv = tv >= 0 ? tile_base(tv) : 0;
     const uint32_t lk = tk >= 0 ? k_slot(tk) : 0u, lv = tv >= 0 ? v_slot(tv) : 0u;
+    // slices ws and ws - 4 are 4 * kInstr slices apart: kInstr V d blocks of 32 values
+    const uint32_t vadd = ws >= 4 ? static_cast<uint32_t>(G::kInstr * 32 * 2) : 0u;
     if (fk && fv) {
 #pragma unroll
       for (int j = 0; j < G::kInstr; ++j) {
-        const int slot = w * G::kInstr + j;
+        const int slot = ws * G::kInstr + j;
         dma16x2(kbytes + row_bytes(bk + slot * kKRowsPerInstr), koff[j], lk + slot * 1024,
-                vbytes + row_bytes(bv + ((slot & 3) << 4)), voff[j], lv + slot * 1024);
+                vbytes + row_bytes(bv + ((slot & 3) << 4)), voff[j] + vadd, lv + slot * 1024);
       }
       return;
     }
 #pragma unroll
     for (int j = 0; j < G::kInstr; ++j) {
-      const int slot = w * G::kInstr + j;
+      const int slot = ws * G::kInstr + j;
       if (fk) {
         dma16(kbytes + row_bytes(bk + slot * kKRowsPerInstr), koff[j], lk + slot * 1024);
       } else if (tk >= 0) {
@@ -384,11 +396,20 @@ __global__ __launch_bounds__(kAttnThreads) void exact_chunk_kernel(AttnParams p)
         dma16_sync(p.kv.k + row_of(bk + r) + uk * 8, lk + slot * 1024);
       }
       if (fv) {
-        dma16(vbytes + row_bytes(bv + ((slot & 3) << 4)), voff[j], lv + slot * 1024);
+        dma16(vbytes + row_bytes(bv + ((slot & 3) << 4)), voff[j] + vadd, lv + slot * 1024);
       } else if (tv >= 0) {
         const int db = slot >> 2, rv = ((slot & 3) << 4) + (lane >> 2);
         dma16_sync(p.kv.v + row_of(bv + rv) + 32 * db + 8 * (lane & 3), lv + slot * 1024);
       }
+    }
+  };
+  auto issue = [&](int tk, int tv) {
+    if constexpr (split_issue) {
+      if (!issuer) return;
+#pragma unroll 1
+      for (int pass = 0; pass < 2; ++pass) issue_slices(tk, tv, __builtin_amdgcn_readfirstlane((w & 3) + 4 * pass));
+    } else {
+      issue_slices(tk, tv, w);
     }
   };
   // Load group g = what iteration g reads: K rows of tile g+1 and V rows of
@@ -400,14 +421,15 @@ __global__ __launch_bounds__(kAttnThreads) void exact_chunk_kernel(AttnParams p)
   auto group_v = [&](int g) { return g >= 1 && g - 1 < ntiles ? g - 1 : -1; };
   auto group_tiles = [&](int g) { return (group_k(g) >= 0) + (group_v(g) >= 0); };
   auto wait_group = [&](int g) {
-    wait_tiles<G::kInstr, 5>(group_tiles(g + 1) + group_tiles(g + 2));
+    // issuers wait for two slices' loads per tile; the others have none in flight
+    wait_tiles<(split_issue ? 2 : 1) * G::kInstr, 5>(group_tiles(g + 1) + group_tiles(g + 2));
     wg_barrier();
   };
 
   issue(0, -1);
 #pragma unroll
   for (int g = 0; g < 3; ++g) issue(group_k(g), group_v(g));
-  wait_tiles<G::kInstr, 7>(group_tiles(0) + group_tiles(1) + group_tiles(2));   // K(0) landed
+  wait_tiles<(split_issue ? 2 : 1) * G::kInstr, 7>(group_tiles(0) + group_tiles(1) + group_tiles(2));   // K(0)
   wg_barrier();
   f32x16 s_cur;
   if (computes) s_cur = qk_half<D>(k_slot(0) + k_half, kofs, qf);

@@ -426,9 +426,10 @@ mage_status launch_select(const Dims& d, const uint16_t* q, const KvArgs& kv, in
   ap.lens = kv.lens;
   int64_t exact_grid = 0;
   ap.map = chunk_map(kv, d, chunk, exact_grid);
-  if (mage_status st = launch(kfn(exact_chunk_kernel<D, kStagesFor<D>>), "exact_chunk_kernel",
-                              exact_grid, kAttnThreads, attn, ap);
-      st != MAGE_OK)
+  // contiguous caches: tile loads issued by half the waves; paged: by all
+  const void* exact_fn = kv.src.page_table ? kfn(exact_chunk_kernel<D, kStagesFor<D>, false>)
+                                           : kfn(exact_chunk_kernel<D, kStagesFor<D>, true>);
+  if (mage_status st = launch(exact_fn, "exact_chunk_kernel", exact_grid, kAttnThreads, attn, ap); st != MAGE_OK)
     return st;
 
   MergeParams mp{};
