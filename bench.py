@@ -436,6 +436,61 @@ def budget_diag(torch, mage, r, w, fl):
             "worst_head_mass_adaptive": round(m_a.min().item(), 4)}
 
 
+def batch_diag(torch, mage, w, dev, fl, batches=(1, 2, 4, 8, 16), reps=10):
+    """The sparse step of this workload's per-sequence shape at several batch
+    sizes, cold: inputs drawn on the GPU (K, V ~ N(0, 1), Q ~ N(0, 1/d), each
+    (seq, KV head) a uniform random set of k positions), timed like the main
+    sparse step. Shows how far the gather kernel gets once the step is large
+    enough to leave its latency floor."""
+    N, Hkv, Hq, d, B = w.seq_lens[0], w.num_kv_heads, w.num_q_heads, w.head_dim, w.block
+    ws = mage.Workspace(dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(w.seed + 99)
+    out = []
+    # the largest batch twice: random positions, then each unit's k positions as one
+    # contiguous run (a control: the same work with streaming row addresses)
+    plan = [(S, "random") for S in batches] + [(batches[-1], "contiguous run")]
+    for S, pattern in plan:
+        wb = workloads.Workload(f"{w.name}-x{S}", (N,) * S, Hq, Hkv, d, B, w.k, w.steps)
+        k = torch.randn(S, Hkv, N, d, generator=g, device=dev).to(torch.bfloat16)
+        v = torch.randn(S, Hkv, N, d, generator=g, device=dev).to(torch.bfloat16)
+        q = (torch.randn(S, B, Hq, d, generator=g, device=dev) * d ** -0.5).to(torch.bfloat16)
+        ke = w.k_eff(0)
+        if pattern == "random":
+            idx = torch.rand(S, Hkv, N, generator=g, device=dev).topk(ke, dim=-1).indices
+            idx = idx.sort(dim=-1).values.to(torch.int32).contiguous()
+        else:
+            start = torch.randint(0, N - ke + 1, (S, Hkv, 1), generator=g, device=dev)
+            idx = (start + torch.arange(ke, device=dev)).to(torch.int32).contiguous()
+        o = torch.empty(S, B, Hq, d, dtype=torch.float32, device=dev)
+        lse = torch.empty(S, B, Hq, dtype=torch.float32, device=dev)
+        mage.sparse_attn(q, k, v, idx, 1.0, o=o, lse=lse, workspace=ws)   # sizes the workspace
+        timers = []
+        for _ in range(reps):
+            fl()
+            tm = KernelTimer(torch, 2)
+            cur = torch.cuda.current_stream()
+            mage.arm_kernel_timers(tm.pairs)
+            tm.outer[0].record(cur)
+            mage.sparse_attn(q, k, v, idx, 1.0, o=o, lse=lse, workspace=ws)
+            tm.outer[1].record(cur)
+            tm.names = mage.last_launches()
+            timers.append(tm)
+        torch.cuda.synchronize()
+        med = statistics.median([t.busy_ms() * 1e3 for t in timers])
+        gather = statistics.median(by_kernel(timers)["sparse_attn_kernel"])
+        nb = sparse_bytes(wb)
+        cb = sparse_chunk_bytes(wb) if len(timers[0].names) > 1 else nb
+        out.append({"seqs": S, "positions": pattern, "bytes": nb, "gpu_us_median": round(med, 2), "GBps": round(nb / (med * 1e-6) / 1e9, 1),
+                    "frac_of_peak": round(nb / (med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                    "gather_kernel_us_median": round(gather, 2),
+                    "gather_kernel_frac_of_peak": round(cb / (gather * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                    "kernels": timers[0].names})
+        del k, v, q, idx, o, lse
+        torch.cuda.empty_cache()
+    return out
+
+
 def by_kernel(timers):
     """{kernel name: [durations in us]} over a list of finished timers."""
     out = {}
@@ -671,6 +726,9 @@ def run_bench(args):
                     "sparse step with the block rows as one more tile per wave of the last split (one call)"}
         diag["page_selection"] = page_diag(torch, mage, r, w, fl)
         diag["head_adaptive_budgets"] = budget_diag(torch, mage, r, w, fl)
+        if not w.paged:
+            diag["sparse_batch_scaling"] = batch_diag(torch, mage, w, dev, fl)
+            log("[bench] sparse batch scaling measured")
     log(f"[bench] page-granular selection measured")
     sp_med = statistics.median(sp_busy)
     if not args.no_diag:
