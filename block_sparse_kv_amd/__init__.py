@@ -147,6 +147,10 @@ def workspace_bytes(dims: Dims, max_seq_len: int, k: int) -> int:
 class Workspace:
     """A device workspace; grows when a call needs more.
 
+    Every new buffer is zeroed (mage_workspace_init) on the stream of the call
+    that needs it: the sparse calls keep arrival counters in it, which must
+    start at zero and which every call leaves at zero.
+
     Calls through one Workspace are ordered: a call made after a step-1 call
     whose selection ran on another stream first waits for that selection.
     """
@@ -164,6 +168,8 @@ class Workspace:
         if self.buf is None or self.buf.numel() < nbytes:
             with torch.cuda.stream(st):
                 self.buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=self.device)
+            _check(lib().mage_workspace_init(_ptr(self.buf), self.buf.numel(), _stream(st)),
+                   "mage_workspace_init")
         return self.buf
 
     def mark(self, stream):

@@ -44,6 +44,9 @@ struct AttnParams {
   const int32_t* counts;    // sparse pass: per-unit entry counts (head-adaptive budgets); null =
                             //   idx_k entries each. Work-groups are then numbered densely per
   int32_t seq_slots;        //   sequence: seq_slots (unit, chunk) slots, units in head order
+  uint32_t* arrivals;       // sparse pass, uniform chunks: one counter per (unit, row block), zero
+                            //   between launches; non-null = the last work-group of a (unit, row
+                            //   block) to finish merges its chunks (no merge launch)
 };
 
 struct MergeParams {
@@ -70,6 +73,96 @@ __device__ __forceinline__ int swap_bits23(int m) {
 template <int D>
 __device__ __forceinline__ int64_t part_o_index(int64_t slot, int w, int db, int i4, int lane) {
   return ((((slot * 4 + w) * (D / 32) + db) * 4 + i4) * kWave + lane);
+}
+
+// Partials handed from work-group to work-group inside one launch use
+// device-scope accesses (cache-policy bit sc1): a store with it is complete at
+// device scope, in every XCD's view, once the wave's vmcnt has drained, and a
+// load with it reads device-coherent data. Ordering the stores before an
+// arrival count then needs only that drain, not a release fence (which on
+// gfx950 writes back the XCD's whole L2).
+constexpr int kScopeDevice = 16;   // sc1
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), 0x00020000);
+}
+
+// One lane's share of the merge of a (unit, row block)'s split partials:
+// accumulator registers 4*i4..4*i4+3 of d block db, for kTasks consecutive
+// register groups i4 = i40 .. i40 + kTasks - 1, of row r, over chunks slot0 ..
+// slot0 + nch - 1. Returns the max M (log2 units), the sum L and the
+// unnormalised O (kTasks float4). Batches of kBatch chunks keep all their
+// loads in flight together (loads from clamped, always valid slots; slots past
+// the end get weight 0). kHandoff: the partials were stored in this launch by
+// other work-groups and are read with device-scope loads.
+template <int D, int kBatch, int kTasks, bool kHandoff>
+__device__ __forceinline__ void merge_chunks(const float* part_o, const float* part_ml, int64_t slot0, int nch,
+                                             int rb, int db, int i40, int lane, int r, float& M, float& L,
+                                             f32x4 (&acc)[kTasks]) {
+  constexpr int64_t kSlotF4 = 4 * (D / 32) * 4 * kWave;   // float4 per slot
+  const float* o0 = part_o + 4 * part_o_index<D>(slot0, 0, 0, 0, 0);
+  const float* ml0 = part_ml + slot0 * kMaxRows * 2;
+  const __amdgpu_buffer_rsrc_t ro = raw_rsrc(o0, static_cast<uint32_t>(nch * kSlotF4 * 16));
+  M = -__builtin_inff();
+  L = 0.f;
+#pragma unroll
+  for (int q = 0; q < kTasks; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int c0 = 0; c0 < nch; c0 += kBatch) {
+    float mb[kBatch], lb[kBatch];
+    f32x4 vb[kBatch][kTasks];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int c = min(c0 + j, nch - 1);
+      const int mf = (c * kMaxRows + r) * 2;
+      if constexpr (kHandoff) {
+        // (M, L) as two device-scope atomic loads: this compiler narrows a
+        // buffer load whose result is only partly read (a b64 load split into
+        // two floats comes out as one dword); each float4 of O is read whole
+        mb[j] = __hip_atomic_load(ml0 + mf, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        lb[j] = __hip_atomic_load(ml0 + mf + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      } else {
+        mb[j] = ml0[mf];
+        lb[j] = ml0[mf + 1];
+      }
+#pragma unroll
+      for (int q = 0; q < kTasks; ++q) {
+        const int of = static_cast<int>(part_o_index<D>(c, rb, db, i40 + q, lane));
+        if constexpr (kHandoff)
+          vb[j][q] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ro, of * 16, 0, kScopeDevice));
+        else
+          vb[j][q] = *reinterpret_cast<const f32x4*>(o0 + 4 * static_cast<int64_t>(of));
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j)
+      if (c0 + j >= nch) mb[j] = -__builtin_inff();
+    float Mb = M;
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) Mb = fmaxf(Mb, mb[j]);
+    if (Mb == -__builtin_inff()) continue;
+    const float f = fast_exp2(M - Mb);  // M = -inf gives 0
+    L *= f;
+#pragma unroll
+    for (int q = 0; q < kTasks; ++q) {
+      acc[q][0] *= f;
+      acc[q][1] *= f;
+      acc[q][2] *= f;
+      acc[q][3] *= f;
+    }
+    M = Mb;
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const float wc = fast_exp2(mb[j] - M);
+      L += lb[j] * wc;
+#pragma unroll
+      for (int q = 0; q < kTasks; ++q) {
+        acc[q][0] += wc * vb[j][q][0];
+        acc[q][1] += wc * vb[j][q][1];
+        acc[q][2] += wc * vb[j][q][2];
+        acc[q][3] += wc * vb[j][q][3];
+      }
+    }
+  }
 }
 
 // A row's softmax reference max is raised only when a tile's max exceeds it by
@@ -617,6 +710,7 @@ __global__ __launch_bounds__(kAttnThreads) void exact_chunk_kernel(AttnParams p)
 // numbered 8 apart so that, with the round-robin placement of work-groups
 // on the 8 XCDs, they share one L2 for the rows they all gather.
 constexpr int kSparseWaves = 4;
+constexpr int kHandoffBatch = 8;   // chunks whose partials the last arriver loads at once
 constexpr int kSparseThreads = kSparseWaves * kWave;
 constexpr int kSparseTileKeys = 32;
 constexpr int kSparseMaxKpw = 1024;     // index entries per wave (LDS row table)
@@ -824,59 +918,113 @@ __global__ __launch_bounds__(kSparseThreads) void sparse_attn_kernel(AttnParams 
     for (int i = 0; i < 16; ++i) xch[(2 + 16 * db + i) * kWave + lane] = oacc[db][i];
   __syncthreads();
   MAGE_TRACE_POINT(4);
-  if (w >= kNdb) return;
-  const int db = w;   // this wave merges d block db of all four waves
-  float mj[kSparseWaves], M = -__builtin_inff();
-#pragma unroll
-  for (int j = 0; j < kSparseWaves; ++j) {
-    mj[j] = reinterpret_cast<const float*>(s_ring + j * kWaveRing)[lane];
-    M = fmaxf(M, mj[j]);
-  }
-  const float Mu = M == -__builtin_inff() ? 0.f : M;
-  float L = 0.f;
-  f32x16 acc;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-#pragma unroll
-  for (int j = 0; j < kSparseWaves; ++j) {
-    const float* xj = reinterpret_cast<const float*>(s_ring + j * kWaveRing);
-    const float a = fast_exp2(mj[j] - Mu);
-    L += xj[kWave + lane] * a;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] += xj[(2 + 16 * db + i) * kWave + lane] * a;
-  }
+  // split chunks with arrival counters: this work-group stores its partial at
+  // device scope and counts itself in; the last of the (unit, row block) merges
+  const bool handoff = p.arrivals != nullptr && !direct;
+  if (w >= kNdb && !handoff) return;
   const int r = 32 * rb + n;
-  if (direct) {
-    if (r >= p.R) return;
-    const int b = r / p.G, gg = r - b * p.G, j = h * p.G + gg;
-    const int64_t row = (static_cast<int64_t>(s) * p.B + b) * p.Hq + j;
-    const float inv = L > 0.f ? 1.f / L : 0.f;
-    float* orow = p.o + row * D + 32 * db + 4 * hh;
+  if (w < kNdb) {
+    const int db = w;   // this wave merges d block db of all four waves
+    float mj[kSparseWaves], M = -__builtin_inff();
 #pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4)
-      *reinterpret_cast<f32x4*>(orow + 8 * i4) =
-          f32x4{acc[4 * i4] * inv, acc[4 * i4 + 1] * inv, acc[4 * i4 + 2] * inv, acc[4 * i4 + 3] * inv};
-    if (db == 0 && hh == 0 && p.lse != nullptr)
-      p.lse[row] = L > 0.f ? (M + __log2f(L)) * kLn2 : -__builtin_inff();
-    return;
-  }
+    for (int j = 0; j < kSparseWaves; ++j) {
+      mj[j] = reinterpret_cast<const float*>(s_ring + j * kWaveRing)[lane];
+      M = fmaxf(M, mj[j]);
+    }
+    const float Mu = M == -__builtin_inff() ? 0.f : M;
+    float L = 0.f;
+    f32x16 acc;
 #pragma unroll
-  for (int i4 = 0; i4 < 4; ++i4)
-    *reinterpret_cast<f32x4*>(p.part_o + 4 * part_o_index<D>(slot, rb, db, i4, lane)) =
-        f32x4{acc[4 * i4], acc[4 * i4 + 1], acc[4 * i4 + 2], acc[4 * i4 + 3]};
-  if (db == 0 && hh == 0) {
-    p.part_ml[(slot * kMaxRows + r) * 2 + 0] = M;
-    p.part_ml[(slot * kMaxRows + r) * 2 + 1] = L;
+    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+#pragma unroll
+    for (int j = 0; j < kSparseWaves; ++j) {
+      const float* xj = reinterpret_cast<const float*>(s_ring + j * kWaveRing);
+      const float a = fast_exp2(mj[j] - Mu);
+      L += xj[kWave + lane] * a;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[i] += xj[(2 + 16 * db + i) * kWave + lane] * a;
+    }
+    if (direct) {
+      if (r >= p.R) return;
+      const int b = r / p.G, gg = r - b * p.G, j = h * p.G + gg;
+      const int64_t row = (static_cast<int64_t>(s) * p.B + b) * p.Hq + j;
+      const float inv = L > 0.f ? 1.f / L : 0.f;
+      float* orow = p.o + row * D + 32 * db + 4 * hh;
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4)
+        *reinterpret_cast<f32x4*>(orow + 8 * i4) =
+            f32x4{acc[4 * i4] * inv, acc[4 * i4 + 1] * inv, acc[4 * i4 + 2] * inv, acc[4 * i4 + 3] * inv};
+      if (db == 0 && hh == 0 && p.lse != nullptr)
+        p.lse[row] = L > 0.f ? (M + __log2f(L)) * kLn2 : -__builtin_inff();
+      return;
+    }
+    if (handoff) {
+      const __amdgpu_buffer_rsrc_t ro = raw_rsrc(p.part_o + 4 * part_o_index<D>(slot, 0, 0, 0, 0),
+                                                 4 * (D / 32) * 4 * kWave * 16);
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4)
+        __builtin_amdgcn_raw_buffer_store_b128(
+            __builtin_bit_cast(u32x4, f32x4{acc[4 * i4], acc[4 * i4 + 1], acc[4 * i4 + 2], acc[4 * i4 + 3]}), ro,
+            static_cast<int>(part_o_index<D>(0, rb, db, i4, lane)) * 16, 0, kScopeDevice);
+      if (db == 0 && hh == 0) {
+        const __amdgpu_buffer_rsrc_t rm = raw_rsrc(p.part_ml + slot * kMaxRows * 2, kMaxRows * 8);
+        using u32x2 = __attribute__((ext_vector_type(2))) unsigned;
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(M), __float_as_uint(L)}, rm, r * 8, 0,
+                                              kScopeDevice);
+      }
+    } else {
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4)
+        *reinterpret_cast<f32x4*>(p.part_o + 4 * part_o_index<D>(slot, rb, db, i4, lane)) =
+            f32x4{acc[4 * i4], acc[4 * i4 + 1], acc[4 * i4 + 2], acc[4 * i4 + 3]};
+      if (db == 0 && hh == 0) {
+        p.part_ml[(slot * kMaxRows + r) * 2 + 0] = M;
+        p.part_ml[(slot * kMaxRows + r) * 2 + 1] = L;
+      }
+    }
   }
   MAGE_TRACE_POINT(5);
+  if (!handoff) return;
+  // every wave's partial stores are complete at device scope before the count
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  int32_t* s_last = &s_tab[0][0];   // the row tables are free once every wave has left its tiles
+  if (tid == 0) {
+    uint32_t* arrived = p.arrivals + static_cast<int64_t>(u) * (kMaxRows / 32) + rb;
+    const uint32_t before = __hip_atomic_fetch_add(arrived, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = before == static_cast<uint32_t>(p.nchunk - 1);
+    if (last) __hip_atomic_store(arrived, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // ready for the next launch
+    *s_last = last;
+  }
+  __syncthreads();
+  if (!*s_last) return;
+  // the last arriver: wave w merges kTasks consecutive (d block, register
+  // group) pairs of the 4 * kNdb, all chunks' loads of a batch in flight at once
+  constexpr int kTasks = kNdb;
+  const int t0 = w * kTasks, db = t0 >> 2, i40 = t0 & 3;
+  float M, L;
+  f32x4 acc[kTasks];
+  merge_chunks<D, kHandoffBatch, kTasks, true>(p.part_o, p.part_ml, static_cast<int64_t>(u) * p.nchunk, p.nchunk,
+                                               rb, db, i40, lane, r, M, L, acc);
+  if (r < p.R) {
+    const int b = r / p.G, gg = r - b * p.G;
+    const int64_t row = (static_cast<int64_t>(s) * p.B + b) * p.Hq + h * p.G + gg;
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+#pragma unroll
+    for (int q = 0; q < kTasks; ++q)
+      *reinterpret_cast<f32x4*>(p.o + row * D + 32 * db + 8 * (i40 + q) + 4 * hh) =
+          f32x4{acc[q][0] * inv, acc[q][1] * inv, acc[q][2] * inv, acc[q][3] * inv};
+    if (t0 == 0 && hh == 0 && p.lse != nullptr) p.lse[row] = (M + __log2f(L)) * kLn2;
+  }
 }
 
 // Merge of split partials (exact pass: chunks of the prefix; sparse pass:
 // chunks of the index list). One work-group per (unit, row block, d block);
 // wave i4 handles accumulator registers 4*i4..4*i4+3. Also writes lse and, if
 // rowstat is non-null, the per-row max + log2(sum) that the score sweep needs.
-// A separate launch rather than an in-kernel last-arriver merge: on gfx950 the
-// device-scope fence such a handoff needs writes back the XCD's whole L2.
+// Used by the exact pass (whose merged row statistics feed the score sweep on
+// the select stream) and by the sparse pass with per-unit counts; the sparse
+// pass with uniform chunks merges inside its own launch (arrival counters).
 template <int D>
 __global__ __launch_bounds__(kThreads) void exact_merge_kernel(MergeParams p) {
   constexpr int kNdb = D / 32;
@@ -903,45 +1051,10 @@ __global__ __launch_bounds__(kThreads) void exact_merge_kernel(MergeParams p) {
     nch = max(0, min(nch, p.seq_slots - before));
     slot0 = static_cast<int64_t>(s) * p.seq_slots + before;
   }
-  // one pass: a running max; each batch's loads are all in flight together
-  float M = -__builtin_inff(), L = 0.f;
-  f32x4 acc{0.f, 0.f, 0.f, 0.f};
-  for (int c0 = 0; c0 < nch; c0 += kBatch) {
-    float mb[kBatch], lb[kBatch];
-    f32x4 vb[kBatch];
-    // loads from clamped (always valid) slots, all issued before any use;
-    // slots past the end get weight 0 afterwards
-#pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-      const int64_t slot = slot0 + min(c0 + j, nch - 1);
-      mb[j] = p.part_ml[(slot * kMaxRows + r) * 2];
-      lb[j] = p.part_ml[(slot * kMaxRows + r) * 2 + 1];
-      vb[j] = *reinterpret_cast<const f32x4*>(p.part_o + 4 * part_o_index<D>(slot, w, db, i4, lane));
-    }
-#pragma unroll
-    for (int j = 0; j < kBatch; ++j)
-      if (c0 + j >= nch) mb[j] = -__builtin_inff();
-    float Mb = M;
-#pragma unroll
-    for (int j = 0; j < kBatch; ++j) Mb = fmaxf(Mb, mb[j]);
-    if (Mb == -__builtin_inff()) continue;
-    const float f = fast_exp2(M - Mb);  // M = -inf gives 0
-    L *= f;
-    acc[0] *= f;
-    acc[1] *= f;
-    acc[2] *= f;
-    acc[3] *= f;
-    M = Mb;
-#pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-      const float wc = fast_exp2(mb[j] - M);
-      L += lb[j] * wc;
-      acc[0] += wc * vb[j][0];
-      acc[1] += wc * vb[j][1];
-      acc[2] += wc * vb[j][2];
-      acc[3] += wc * vb[j][3];
-    }
-  }
+  float M, L;
+  f32x4 accs[1];
+  merge_chunks<D, kBatch, 1, false>(p.part_o, p.part_ml, slot0, nch, w, db, i4, lane, r, M, L, accs);
+  const f32x4 acc = accs[0];
   if (r >= p.R) return;
   const int b = r / p.G, g = r - b * p.G, j = h * p.G + g;
   const int64_t row = (static_cast<int64_t>(s) * p.B + b) * p.Hq + j;

@@ -205,12 +205,17 @@ constexpr int kSparseStages = 2;
 
 // ---- workspace layout ------------------------------------------------------
 struct Layout {
+  size_t arrivals;       // sparse pass: per (unit, row block) arrival counters; first, at a fixed place
   size_t rowstat, part_ml, part_o, cand_bits, cand_pos, cand_count, row_info, hist, hist_parts, scores;
   size_t qbar, qbar_o;   // mean-query selection: the mean query and its (unused) attention output
   size_t page_scores, page_idx;   // page-granular selection (pages of >= 1 positions; <= k page ids)
   size_t total;
   int64_t slots, cand_stride;
 };
+
+// Units (sequence, KV head) that a sparse launch can merge in-kernel; larger
+// batches fall back to the merge launch.
+constexpr int64_t kArrivalUnits = 16384;
 
 Layout make_layout(const Dims& d, int64_t max_n, int64_t k) {
   Layout L{};
@@ -228,6 +233,10 @@ Layout make_layout(const Dims& d, int64_t max_n, int64_t k) {
     off = round_up(off + bytes, 256);
     return at;
   };
+  // The arrival counters sit at the start of every layout with a fixed
+  // capacity, so no other region of any call shape overlaps them: a zeroed
+  // workspace keeps them zero through every call.
+  L.arrivals = take(kArrivalUnits * (kMaxRows / 32) * 4);
   L.rowstat = take(U * kMaxRows * 4);
   L.part_ml = take(L.slots * kMaxRows * 2 * 4);
   L.part_o = take(L.slots * 4 * (d.D / 32) * 4 * kWave * 16);
@@ -702,12 +711,17 @@ mage_status launch_sparse(const Dims& d, const uint16_t* q, const KvArgs& kv, co
   ap.v_blk = v_blk;
   ap.counts = counts;
   ap.seq_slots = static_cast<int32_t>(seq_slots);
+  // uniform chunks: the last work-group of each (unit, row block) merges its
+  // chunks inside the launch (arrival counters); per-unit counts keep the
+  // merge launch
+  const bool handoff = !counts && nch > 1 && U <= kArrivalUnits && env_int("MAGE_SPARSE_HANDOFF", 1) != 0;
+  ap.arrivals = handoff ? at<uint32_t>(ws, L.arrivals) : nullptr;
   const int64_t grid = round_up(counts ? d.S * seq_slots : U * nch, 8) * d.nrb;
   if (mage_status st = launch(kfn(sparse_attn_kernel<D, kSparseStages>), "sparse_attn_kernel", grid,
                               kSparseThreads, stream, ap);
       st != MAGE_OK)
     return st;
-  if (nch == 1 && !counts) return MAGE_OK;  // the single chunk wrote O and lse
+  if ((nch == 1 && !counts) || handoff) return MAGE_OK;  // O and lse written by the launch
   MergeParams mp{};
   mp.part_o = ap.part_o;
   mp.part_ml = ap.part_ml;

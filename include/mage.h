@@ -40,10 +40,17 @@
  * asynchronous and stream-ordered; host-side argument checks happen before
  * any launch, and a failed check launches nothing.
  *
- * Workspace contract: any contents (no initialisation needed). Calls that may
- * run concurrently need distinct workspaces; a workspace may be reused once
- * the previous call's work (including its select stream) is ordered before
- * the new call.
+ * Workspace contract: zero-fill a new workspace once with
+ * mage_workspace_init before its first call (again only if the caller writes
+ * over it). Its first 256 KiB hold arrival counters that the later-step calls
+ * (mage_sparse_attn, mage_sparse_block_attn and their paged forms) use to
+ * merge split work inside one launch; every call leaves them at zero, and no
+ * other part of any call's layout overlaps them. The rest of the workspace is
+ * scratch that no call expects to hold anything. Calls that may run
+ * concurrently need distinct workspaces; a workspace may be reused once the
+ * previous call's work (including its select stream) is ordered before the
+ * new call. A workspace with non-zero counters makes a later step return
+ * wrong values (it does not fault or hang).
  *
  * Errors: every entry point returns a mage_status and never aborts.
  * MAGE_ERR_HIP carries the runtime's message in mage_last_error() (thread
@@ -101,7 +108,10 @@ typedef struct mage_paged_kv {
 size_t mage_workspace_bytes(const mage_dims* dims, int32_t max_seq_len, int32_t k);
 
 /* Zero-fill a workspace on `stream` with a fill kernel (no memset node).
- * Optional: no entry point depends on the workspace's prior contents. */
+ * Required once on a new workspace: the later-step calls keep arrival
+ * counters in it, which must start at zero (every call leaves them at zero).
+ * workspace 4-byte aligned, workspace_bytes a multiple of 4, else
+ * MAGE_ERR_INVALID_ARG. */
 mage_status mage_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
@@ -152,6 +162,10 @@ mage_status mage_exact_attn_paged(const mage_dims* dims, const uint16_t* q,
  * no valid entry gets O = 0, lse = -inf). lse may be null. k (the index row
  * length) must be in [1, MAGE_MAX_SPARSE_K], else MAGE_ERR_INVALID_ARG (k < 1)
  * or MAGE_ERR_UNSUPPORTED (k too large).
+ * One launch: when the index rows are split over several work-groups, the
+ * last of them to finish for a (unit, 32-row block) merges the split results,
+ * counted through the workspace's arrival counters (zeroed once by
+ * mage_workspace_init).
  */
 #define MAGE_MAX_SPARSE_K 131072
 mage_status mage_sparse_attn(const mage_dims* dims, const uint16_t* q,
