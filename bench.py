@@ -884,7 +884,8 @@ def summarize_pmc(fetch_dir, write_dir, config):
     copy_bytes = COPY_MIB * 1024 * 1024
     cf = copy_bytes / (statistics.mean(f["copy (neg)"]["all"]) * 1024)
     cw = copy_bytes / (statistics.mean(wr["copy (neg)"]["all"]) * 1024)
-    algo = {"sparse_attn_kernel": sparse_chunk_bytes(w), "exact_chunk_kernel": exact_pass_bytes(w),
+    # the later step is one launch (its split merge runs in its last work-groups): K/V rows, Q and O
+    algo = {"sparse_attn_kernel": sparse_bytes(w), "exact_chunk_kernel": exact_pass_bytes(w),
             "score_kernel": score_bytes(w), "copy (neg)": 2 * copy_bytes}
     print(f"Copy calibration: a {COPY_MIB} MiB fp32 copy (torch.neg) reads {COPY_MIB} MiB and writes "
           f"{COPY_MIB} MiB; FETCH_SIZE reads {copy_bytes / cf / 1024:.0f} KiB and WRITE_SIZE "
