@@ -50,6 +50,9 @@ def test_workspace_bytes():
     assert mage.workspace_bytes(dims(head_dim=96), 1024, 64) == 0
     assert mage.workspace_bytes(dims(num_q_heads=30), 1024, 64) == 0
     assert mage.workspace_bytes(dims(), 0, 64) == 0
+    # every layout starts with the fixed 256 KiB arrival-counter region of the later steps
+    tiny = mage.workspace_bytes(dims(block=1, num_q_heads=1, num_kv_heads=1, head_dim=64), 1, 1)
+    assert tiny >= 16384 * 4 * 4
 
 
 FAKE = ctypes.c_void_p(1 << 20)   # never dereferenced: every call below fails its checks first
