@@ -998,6 +998,7 @@ __global__ __launch_bounds__(kSparseThreads) void sparse_attn_kernel(AttnParams 
   }
   __syncthreads();
   if (!*s_last) return;
+  MAGE_TRACE_POINT(7);
   // the last arriver: wave w merges kTasks consecutive (d block, register
   // group) pairs of the 4 * kNdb, all chunks' loads of a batch in flight at once
   constexpr int kTasks = kNdb;
