@@ -364,9 +364,10 @@ def test_sparse_block_attn_matches_oracle(S, B, Hq, Hkv, d, N, k):
     assert np.abs(lse.cpu().numpy() - l_ref).max() <= 2e-3
 
 
-def test_sparse_block_attn_paged_matches_oracle():
+@pytest.mark.parametrize("k", [64, 700])   # 700: six index chunks merged in the launch, some only padding
+def test_sparse_block_attn_paged_matches_oracle(k):
     # ragged paged prefix, shuffled 16-token pages; the oracle's own index set
-    w = workloads.custom((53, 200, 1000), 8, 2, 64, 4, 64, paged=True, steps=2, name="paged_ragged", seed=31)
+    w = workloads.custom((53, 200, 1000), 8, 2, 64, 4, k, paged=True, steps=2, name="paged_ragged", seed=31)
     inp = workloads.make_inputs(w, steps=2)
     d = dev_inputs(inp)
     idx = np.ascontiguousarray(ora_select(inp)[3])
