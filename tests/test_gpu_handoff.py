@@ -42,6 +42,7 @@ CASES = [
     ((53, 900, 4000), 8, 2, 64, 8, 2048, True),
     ((20000,), 16, 16, 64, 64, 256, False),
     ((6000,), 32, 8, 128, 32, 4096, False),
+    ((5000,), 4, 1, 128, 8, 4096, False),    # one unit, 32 rows: 32 chunks, merged in four batches
 ]
 
 
@@ -71,7 +72,7 @@ def test_back_to_back_calls_share_one_workspace():
         assert np.abs(lse.cpu().double().numpy() - lr).max() <= TOL, w.name
         fresh.append((o.cpu(), lse.cpu()))
     ws = mage.Workspace(DEV)
-    order = [0, 1, 2, 3, 4, 4, 0, 2, 1, 3, 0, 0]
+    order = [0, 1, 2, 3, 4, 5, 4, 0, 5, 2, 1, 3, 0, 0]
     for rep, i in enumerate(order):
         w, inp, idx = cases[i]
         o, lse = _run(w, inp, idx, ws)
