@@ -123,11 +123,13 @@ int env_int(const char* name, int dflt) {
 // Exact pass: split each (seq, KV head) prefix into chunks of `chunk` keys.
 // One work-group fills a CU (LDS ring), so the chunk is chosen to make the
 // work-group count whole rounds of kCus with at most kExactRoundKeys keys per
-// work-group: one round of 4096-key chunks for 8 x 128K keys, about four rounds
-// for the ragged 8-sequence batch. Never below the floor that bounds the
+// work-group: one round of 4096-key chunks for 8 x 128K keys, two rounds of
+// about 6.6K keys for the ragged 8-sequence batch (3.4M keys; against four
+// rounds of 3.3K keys: 435 against 453 us and 449 against 451 us in two A/Bs;
+// one round of 13K keys: 482 us). Never below the floor that bounds the
 // partial-result workspace.
 constexpr int kCus = 256;
-constexpr int64_t kExactRoundKeys = 4096;
+constexpr int64_t kExactRoundKeys = 8192;
 constexpr int kExactMinChunk = 512;
 constexpr int kExactSlotBudget = 4096;
 
