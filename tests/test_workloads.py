@@ -76,3 +76,51 @@ def test_walk_queries_drift_from_q1():
     sd = [float((q.float() - q1).std()) for q in walk]
     assert abs(sd[15] - w.q_noise) < 0.1 * w.q_noise
     assert sd[-1] > sd[15] > sd[3]
+
+
+def _torch_calls_on_worker_threads(fn):
+    """Run fn() and return the torch functions entered on threads other than
+    the calling one (Python frames of torch modules, or torch builtins)."""
+    import threading
+    main = threading.get_ident()
+    seen = []
+
+    def prof(frame, event, arg):
+        if threading.get_ident() == main:
+            return
+        if event == "call":
+            mod = frame.f_globals.get("__name__", "")
+            if mod.startswith("torch"):
+                seen.append(f"{mod}.{frame.f_code.co_name}")
+        elif event == "c_call":
+            owner = getattr(arg, "__module__", None) or getattr(getattr(arg, "__objclass__", None), "__module__", "")
+            if str(owner).startswith("torch"):
+                seen.append(f"{owner}.{getattr(arg, '__name__', arg)}")
+
+    threading.setprofile(prof)
+    try:
+        fn()
+    finally:
+        threading.setprofile(None)
+    return seen
+
+
+def test_generator_worker_threads_never_enter_torch():
+    # torch's CPU kernels start an OpenMP team per calling thread; on the GPU box a
+    # worker thread inside torch during the first CUDA initialisation crashed the
+    # process, so the draws on worker threads are numpy only
+    for w in (workloads.custom((700,), 8, 2, 64, 4, 16, seed=9),
+              workloads.custom((300, 45), 8, 2, 64, 4, 16, paged=True, seed=10)):
+        assert _torch_calls_on_worker_threads(lambda: workloads.make_inputs(w)) == []
+
+
+def test_worker_thread_check_sees_a_torch_call(monkeypatch):
+    # the detector itself: a generator whose workers call torch is caught
+    real = workloads._bf16_bits
+
+    def leaky(a):
+        torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch.bfloat16)
+        return real(a)
+    monkeypatch.setattr(workloads, "_bf16_bits", leaky)
+    w = workloads.custom((200,), 8, 2, 64, 4, 16, seed=11)
+    assert _torch_calls_on_worker_threads(lambda: workloads.make_inputs(w))
