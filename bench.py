@@ -218,17 +218,18 @@ class Runner:
                                      workspace=self.ws)
         self._call(timer, fn)
 
-    def sparse(self, t, timer=None):
+    def sparse(self, t, timer=None, stream=None):
         w = self.w
         q = self.qs[t % len(self.qs)]
 
         def fn():
             if w.paged:
                 self.mage.sparse_attn_paged(q, self.kp, self.vp, self.table, self.lens, self.idx,
-                                            w.scale, o=self.o2, lse=self.lse2, workspace=self.ws)
+                                            w.scale, o=self.o2, lse=self.lse2, workspace=self.ws,
+                                            stream=stream)
             else:
                 self.mage.sparse_attn(q, self.k, self.v, self.idx, w.scale, o=self.o2,
-                                      lse=self.lse2, workspace=self.ws)
+                                      lse=self.lse2, workspace=self.ws, stream=stream)
         self._call(timer, fn)
 
     def block(self, t, timer=None):
@@ -491,6 +492,149 @@ def batch_diag(torch, mage, w, dev, fl, batches=(1, 2, 4, 8, 16), reps=10):
     return out
 
 
+MAIN_STREAM = ("exact_chunk_kernel", "exact_merge_kernel[exact]")
+
+
+def select_chain_us(tm):
+    """Step 1's GPU time from its kernels' durations: the exact pass, then the
+    longer of the split merge (main stream) and the selection kernels (score
+    sweep and top-k, select stream), which run side by side."""
+    d = {}
+    for name, ms in zip(tm.names, tm.kernels_ms()):
+        d[name] = d.get(name, 0.0) + ms * 1e3
+    side = sum(v for n, v in d.items() if n not in MAIN_STREAM)
+    return d.get("exact_chunk_kernel", 0.0) + max(d.get("exact_merge_kernel[exact]", 0.0), side)
+
+
+def event_pair_us(torch, fn, fl, reps):
+    """Median GPU time between an event recorded before fn() and one recorded after
+    it on the current stream (uninstrumented kernels), a flush before each."""
+    pairs = []
+    for _ in range(reps):
+        fl()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        pairs.append((a, b))
+    torch.cuda.synchronize()
+    return statistics.median([a.elapsed_time(b) * 1e3 for a, b in pairs])
+
+
+def overlap_diag(torch, mage, r, w, fl, empty_us, reps=7):
+    """The selection overlapped with other work (the MAGE page's summary and
+    "Key results": selection runs on a second stream during the rest of step 1).
+    Stand-in for the rest of the step: the next layer's exact pass over a second
+    KV cache of the same shape, issued on the main stream while the score sweep
+    and top-k of this layer run on the select stream. Uninstrumented event pairs
+    (minus the empty pair), cold."""
+    dev = r.dev
+    g = torch.Generator(device=dev)
+    g.manual_seed(w.seed + 123)
+    if w.paged:
+        kp2 = torch.randn(r.kp.shape, generator=g, device=dev).to(torch.bfloat16)
+        vp2 = torch.randn(r.vp.shape, generator=g, device=dev).to(torch.bfloat16)
+    else:
+        k2 = torch.randn(r.k.shape, generator=g, device=dev).to(torch.bfloat16)
+        v2 = torch.randn(r.v.shape, generator=g, device=dev).to(torch.bfloat16)
+    ws2 = mage.Workspace(dev)
+    o2 = torch.empty_like(r.o)
+    l2 = torch.empty_like(r.lse)
+
+    def exact_next():
+        if w.paged:
+            mage.exact_attn_paged(r.q1, kp2, vp2, r.table, r.lens, w.scale, o=o2, lse=l2, workspace=ws2)
+        else:
+            mage.exact_attn(r.q1, k2, v2, w.scale, o=o2, lse=l2, workspace=ws2)
+
+    def select(side):
+        kw = dict(o=r.o, lse=r.lse, idx=r.idx, scores=r.scores, workspace=r.ws,
+                  select_stream=side, idx_ready=r.ready if side is not None else None)
+        if w.paged:
+            mage.select_exact_paged(r.q1, r.kp, r.vp, r.table, r.lens, w.k, w.scale, **kw)
+        else:
+            mage.select_exact(r.q1, r.k, r.v, w.k, w.scale, **kw)
+
+    def overlapped():
+        select(r.side)
+        exact_next()
+        torch.cuda.current_stream().wait_event(r.ready)
+
+    def serial():
+        select(None)
+        exact_next()
+
+    def exact_both():
+        r.exact_only()
+        exact_next()
+
+    for fn in (overlapped, serial, exact_both):   # sizes the workspaces
+        fn()
+    torch.cuda.synchronize()
+    t_ov = event_pair_us(torch, overlapped, fl, reps) - empty_us
+    t_se = event_pair_us(torch, serial, fl, reps) - empty_us
+    t_ex = event_pair_us(torch, exact_both, fl, reps) - empty_us
+    t_one = event_pair_us(torch, lambda: select(r.side) or torch.cuda.current_stream().wait_event(r.ready),
+                          fl, reps) - empty_us
+    t_ex1 = event_pair_us(torch, r.exact_only, fl, reps) - empty_us
+    sel_cost = max(t_se - t_ex, 1e-9)
+    return {"two_layers_overlapped_us": round(t_ov, 1), "two_layers_one_stream_us": round(t_se, 1),
+            "two_exact_passes_us": round(t_ex, 1),
+            "first_step_overhead_overlapped": round(t_ov / t_ex - 1, 4),
+            "first_step_overhead_one_stream": round(t_se / t_ex - 1, 4),
+            "selection_hidden_frac": round((t_se - t_ov) / sel_cost, 4),
+            "one_layer_select_us": round(t_one, 1), "one_layer_exact_us": round(t_ex1, 1),
+            "one_layer_first_step_overhead": round(t_one / t_ex1 - 1, 4),
+            "note": "uninstrumented event pairs minus the empty pair, cold (flush before each); layer 1 = "
+                    "exact+select, layer 2 = exact pass over a second cache of the same shape (the rest of "
+                    "step 1); overlapped: layer 1's score sweep and top-k on the select stream while the main "
+                    "stream runs layer 2; one stream: the same kernels in order; overhead = time / (two exact "
+                    "passes) - 1; hidden = share of the selection's one-stream cost that the overlap removes"}
+
+
+def graph_diag(torch, mage, r, w, reps=5):
+    """The T-1 later steps of a block launched back to back, warm (no flush between
+    steps): replayed from one captured HIP graph (no host work per step) and
+    launched eagerly; per-step GPU time from one event pair around all of them."""
+    T = w.steps
+    n = T - 1
+    s = torch.cuda.Stream(device=r.dev)
+    for t in range(n):   # eager warm-up: the workspace has its size before capture
+        r.sparse(t)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for t in range(n):
+                r.sparse(t, stream=s)
+    torch.cuda.current_stream().wait_stream(s)
+    g.replay()
+    torch.cuda.synchronize()
+
+    def replay():
+        g.replay()
+
+    def eager():
+        for t in range(n):
+            r.sparse(t)
+    out = {}
+    for name, fn in (("graph", replay), ("eager", eager)):
+        per = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            per.append(a.elapsed_time(b) * 1e3 / n)
+        out[f"{name}_us_per_step_median"] = round(statistics.median(per), 2)
+    out["steps_per_replay"] = n
+    out["note"] = ("warm (rows stay in the caches across steps, no flush); graph = one captured graph of the "
+                   "T-1 later-step launches replayed, eager = the same launches from Python")
+    return out
+
+
 def by_kernel(timers):
     """{kernel name: [durations in us]} over a list of finished timers."""
     out = {}
@@ -504,17 +648,79 @@ def pct(a, p):
     return float(np.percentile(a, p))
 
 
+def ragged_side(torch, mage, dev, fl, sparse_calls=40, select_calls=6):
+    """The ragged paged batch (8 sequences of 8K-128K, 16-token pages, shuffled page
+    table) measured beside the headline workload with the same protocol: cold calls,
+    kernel durations from the launches' own events."""
+    w = workloads.CONFIG_BY_NAME["ragged"]
+    t0 = time.perf_counter()
+    inp = workloads.make_inputs(w, steps=4)
+    r = Runner(torch, mage, w, inp, dev)
+    del inp
+    log(f"[bench] ragged inputs in {time.perf_counter() - t0:.1f} s")
+    for t in range(3):
+        r.select()
+        r.sparse(t)
+    torch.cuda.synchronize()
+    sp, sel = [], []
+    for i in range(sparse_calls):
+        fl()
+        tm = KernelTimer(torch, 2)
+        r.sparse(i, tm)
+        sp.append(tm)
+    for _ in range(select_calls):
+        fl()
+        tm = KernelTimer(torch, mage.MAX_TIMED_LAUNCHES)
+        r.select(tm)
+        sel.append(tm)
+    torch.cuda.synchronize()
+    sp_us = [t.busy_ms() * 1e3 for t in sp]
+    k_us = by_kernel(sp)["sparse_attn_kernel"]
+    sel_us = [select_chain_us(t) for t in sel]
+    nb = sparse_bytes(w)
+    kmean = statistics.mean(k_us)
+    bytes_sel = select_bytes(w)
+    ideal_sel = max(bytes_sel / (HBM_PEAK_GBS * 1e9), exact_flops(w) / (BF16_PEAK_TFLOPS * 1e12)) * 1e6
+    traffic = traffic_record(w.name)
+    out = {"workload": f"ragged: {w.num_seqs} seqs, N={list(w.seq_lens)}, {w.num_q_heads} q / {w.num_kv_heads} KV "
+                       f"heads, d={w.head_dim}, B={w.block}, k={w.k}, 16-token pages, shuffled page table",
+           "sparse_step_us_mean": round(statistics.mean(sp_us), 2),
+           "sparse_step_us_median": round(statistics.median(sp_us), 2),
+           "steps_per_s": round(1e6 / statistics.mean(sp_us), 1),
+           "bytes_per_step": nb,
+           "GBps": round(nb / (kmean * 1e-6) / 1e9, 1),
+           "frac": round(nb / (kmean * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+           "traffic_bytes_per_launch": None if traffic is None else traffic["bytes_per_launch"],
+           "traffic_ratio": None if traffic is None else round(traffic["bytes_per_launch"] / nb, 3),
+           "exact_select_us_median": round(statistics.median(sel_us), 1),
+           "exact_select_roofline_us": round(ideal_sel, 1),
+           "exact_select_roofline_frac": round(ideal_sel / statistics.median(sel_us), 4),
+           "exact_select_kernels_us_median": {n: round(statistics.median(v), 2) for n, v in by_kernel(sel).items()}}
+    del r
+    torch.cuda.empty_cache()
+    return out
+
+
 # ---- the oracle on the host cores ------------------------------------------------
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
 def cpu_baseline(w, inp, budget_s=20.0):
-    """The fp64 oracle as it stands, timed on the host cores over a bounded sample of the
-    same workload: step 1 (exact + scores + top-k) per (seq, KV head) unit, longest first,
-    for about 45% of the budget, then whole-batch sparse steps with the oracle's own index
-    sets for about 45%. Returns sparse steps/s of the whole batch."""
+    """The fp64 oracle as it stands, timed on the host cores over the same workload:
+    step 1 (exact + scores + top-k) over every (seq, KV head) unit, whole, repeated
+    while it fits about 45% of the budget; then whole-batch sparse steps with the
+    oracle's own index sets for about 45%. Returns sparse steps/s of the whole batch."""
     import oracle
     S, Hkv, G = w.num_seqs, w.num_kv_heads, w.group
     units = [(s, h) for s in range(S) for h in range(Hkv)]
-    # longest sequences first so the sample has the workload's heaviest units
-    units.sort(key=lambda u: (-w.seq_lens[u[0]], u))
 
     def unit_kv(s, h):
         n = w.seq_lens[s]
@@ -524,30 +730,21 @@ def cpu_baseline(w, inp, budget_s=20.0):
             return np.ascontiguousarray(kk), np.ascontiguousarray(vv)
         return inp.k[s:s + 1, h:h + 1].contiguous(), inp.v[s:s + 1, h:h + 1].contiguous()
 
-    sel_t, keys_done, idx_of, runs = 0.0, 0, {}, 0
-    # step 1 over the units, cycling through them until about 45% of the budget is spent
-    while sel_t < 0.45 * budget_s:
-        s, h = units[runs % len(units)]
-        kc, vc = unit_kv(s, h)
-        q1 = inp.q1[s:s + 1, :, h * G:(h + 1) * G].contiguous()
+    # paged caches are de-paged before any clock starts
+    kv = {u: unit_kv(*u) for u in units}
+    sel_runs, idx_of = [], {}
+    while not sel_runs or (sum(sel_runs) + sel_runs[0] < 0.45 * budget_s and len(sel_runs) < 3):
         t0 = time.perf_counter()
-        _, _, _, idx = oracle.select_exact(q1, kc, vc, w.scale, w.k)
-        sel_t += time.perf_counter() - t0
-        keys_done += w.seq_lens[s]
-        idx_of[(s, h)] = idx
-        runs += 1
-    n_sel = runs
-    sel_est = sel_t * (sum(w.seq_lens) * Hkv) / keys_done   # whole batch, by prefix keys
-    # sparse steps over every unit. Units without a step-1 result take the index set of a
-    # sampled unit, clipped to their length (any valid set costs the same gather work).
-    # Paged caches are de-paged before the clock starts.
-    some = next(iter(idx_of.values()))
+        for (s, h) in units:
+            kc, vc = kv[(s, h)]
+            q1 = inp.q1[s:s + 1, :, h * G:(h + 1) * G].contiguous()
+            _, _, _, idx = oracle.select_exact(q1, kc, vc, w.scale, w.k)
+            idx_of[(s, h)] = idx
+        sel_runs.append(time.perf_counter() - t0)
     work = []
     for (s, h) in units:
-        kc, vc = unit_kv(s, h)
-        idx = idx_of.get((s, h), some)
-        idx = np.where(idx < w.seq_lens[s], idx, -1).astype(np.int32)
-        work.append((inp.q_steps[0][s:s + 1, :, h * G:(h + 1) * G].contiguous(), kc, vc, idx))
+        kc, vc = kv[(s, h)]
+        work.append((inp.q_steps[0][s:s + 1, :, h * G:(h + 1) * G].contiguous(), kc, vc, idx_of[(s, h)]))
     step_t = []
     while len(step_t) < 3 or (sum(step_t) < 0.45 * budget_s and len(step_t) < 5000):
         t0 = time.perf_counter()
@@ -555,11 +752,12 @@ def cpu_baseline(w, inp, budget_s=20.0):
             oracle.sparse(q2, kc, vc, idx, w.scale)
         step_t.append(time.perf_counter() - t0)
     med = statistics.median(step_t)
-    sample = (f"oracle (C++ fp64, OpenMP) on the host: {n_sel} step-1 runs over the {len(units)} "
-              f"(seq, KV head) units ({sel_t:.1f} s, {keys_done} prefix keys), then "
-              f"{len(step_t)} whole-batch sparse steps (median {med * 1e3:.1f} ms per step)")
-    return {"value": 1.0 / med, "select_step_s_est": sel_est, "sample": sample,
-            "cores": oracle.num_threads(), "cpu_seconds": sel_t + sum(step_t)}
+    sel_med = statistics.median(sel_runs)
+    sample = (f"oracle (C++ fp64, OpenMP) on the host: step 1 over all {len(units)} (seq, KV head) units "
+              f"{len(sel_runs)}x (median {sel_med:.2f} s), then {len(step_t)} whole-batch sparse steps "
+              f"(median {med * 1e3:.1f} ms per step)")
+    return {"value": 1.0 / med, "select_step_s": sel_med, "select_runs": len(sel_runs), "sample": sample,
+            "cores": oracle.num_threads(), "cpu_seconds": sum(sel_runs) + sum(step_t)}
 
 
 # ---- traffic from committed counter summaries ------------------------------------
@@ -664,6 +862,14 @@ def run_bench(args):
         a.record()
         b.record()
         empty.append((a, b))
+    torch.cuda.synchronize()
+    empty_pre = statistics.median([a.elapsed_time(b) * 1e3 for a, b in empty])
+    sel_outer = event_pair_us(torch, r.select, fl, 7) - empty_pre
+    ex_outer = event_pair_us(torch, r.exact_only, fl, 7) - empty_pre
+    overlap = overlap_diag(torch, mage, r, w, fl, empty_pre)
+    log("[bench] selection overlap measured")
+    graphs = graph_diag(torch, mage, r, w)
+    log("[bench] graph replay measured")
     # plain copy of known size: the calibration kernel for FETCH_SIZE / WRITE_SIZE counter runs
     # (timed: the measured copy bandwidth, a second roofline beside the 8 TB/s spec)
     src = torch.ones(COPY_MIB * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
@@ -685,7 +891,8 @@ def run_bench(args):
     sp_k = by_kernel(sp_timers)
     chunk_name = "sparse_attn_kernel"
     chunk_us = sp_k[chunk_name]
-    sel_busy = [t.busy_ms() * 1e3 for t in sel_timers]
+    sel_busy = [select_chain_us(t) for t in sel_timers]
+    sel_serial = [t.busy_ms() * 1e3 for t in sel_timers]
     sel_span = [t.span_ms() * 1e3 for t in sel_timers]
     sel_k = by_kernel(sel_timers)
     ex_busy = [t.busy_ms() * 1e3 for t in ex_timers]
@@ -704,7 +911,7 @@ def run_bench(args):
     ex_med = statistics.median(ex_busy)
     exact_k = statistics.median(sel_k["exact_chunk_kernel"])
     score_k = statistics.median(sel_k["score_kernel"])
-    topk_names = [n for n in sel_k if n.startswith("topk") or n == "hist_reduce_kernel"]
+    topk_names = [n for n in sel_k if n.startswith("topk")]
     topk_k = sum(statistics.median(sel_k[n]) for n in topk_names)
     ntot = sum(w.seq_lens)
     block_us = statistics.mean(sel_busy) + (T - 1) * sp_mean
@@ -785,6 +992,12 @@ def run_bench(args):
                         "warm_GBps": round(sbytes / (statistics.median(warm_busy) * 1e-6) / 1e9, 1)},
         "exact_select": {"gpu_us_median": round(sel_med, 1), "roofline_us": round(ideal_sel_us, 1),
                          "roofline_frac": round(ideal_sel_us / sel_med, 4), "bytes": bytes_sel,
+                         "timing": "exact pass + the longer of (split merge on the main stream, score sweep + "
+                                   "top-k on the select stream), from the kernels' own start/end events",
+                         "serial_kernel_sum_us_median": round(statistics.median(sel_serial), 1),
+                         "uninstrumented_event_pair_us_median": round(sel_outer, 1),
+                         "uninstrumented_roofline_frac": round(ideal_sel_us / sel_outer, 4),
+                         "exact_only_uninstrumented_us_median": round(ex_outer, 1),
                          "kernels_us_median": {n: us(statistics.median(v)) for n, v in sel_k.items()},
                          "exact_pass_GBps": round(exact_pass_bytes(w) / (exact_k * 1e-6) / 1e9, 1),
                          "exact_pass_TFLOPs": round(exact_flops(w) / (exact_k * 1e-6) / 1e12, 1),
@@ -797,6 +1010,8 @@ def run_bench(args):
                          "first_step_overhead": round(sel_med / ex_med - 1, 4),
                          "instrumented_span_us_median": round(statistics.median(sel_span), 1),
                          "event_pair_us_median": round(statistics.median([t.outer_ms() * 1e3 for t in sel_timers]), 1)},
+        "selection_overlap": overlap,
+        "sparse_graph_replay": graphs,
         "speedup_vs_exact_per_step": round(ex_med / statistics.median(sp_busy), 2),
         "wall_s_timed_region": round(wall, 3),
         "flushes_in_timed_region": args.steps * T if args.flush != "none" else 0,
@@ -805,6 +1020,9 @@ def run_bench(args):
         "kernel_source_digest": source_digest(),
     }
     out.update(diag)
+    if not args.no_ragged and not w.paged:
+        out["ragged_paged"] = ragged_side(torch, mage, dev, fl)
+        log("[bench] ragged paged batch measured")
     if traffic is not None:
         out["roofline"]["traffic_source"] = f"profiles/sparse_traffic_{w.name}.md"
     if not args.no_cpu:
@@ -812,9 +1030,10 @@ def run_bench(args):
         cb = cpu_baseline(w, inp)
         out["cpu_baseline"] = {"value": round(cb["value"], 3), "unit": "steps/s", "cores": cb["cores"],
                                "kind": "oracle", "sample": cb["sample"],
-                               "select_step_s_est": round(cb["select_step_s_est"], 2),
+                               "select_step_s": round(cb["select_step_s"], 3),
+                               "select_step_runs": cb["select_runs"],
                                "cpu_seconds": round(cb["cpu_seconds"], 1),
-                               "host": platform.processor() or platform.machine()}
+                               "cpu_model": cpu_model(), "host": platform.machine()}
         log(f"[bench] cpu baseline in {time.perf_counter() - t0:.1f} s")
     print(json.dumps(out), flush=True)
 
@@ -822,7 +1041,7 @@ def run_bench(args):
 # ---- profile summaries -----------------------------------------------------------
 def _short(name: str) -> str:
     for key in ("exact_chunk_kernel", "sparse_attn_kernel", "exact_merge_kernel", "score_kernel",
-                "topk_local_kernel", "topk_final_kernel", "topk_hist_kernel", "hist_reduce_kernel",
+                "topk_select_kernel", "topk_hist_kernel", "topk_prep_kernel",
                 "block_attn_kernel", "mean_query_kernel", "idx_overlap_kernel", "page_sum_kernel",
                 "page_expand_kernel", "gap_zero_kernel", "budget_split_kernel", "FillFunctor",
                 "neg_kernel", "reduce_kernel"):
@@ -863,6 +1082,27 @@ def summarize_trace(d):
         c = a["cold"]
         print(f"| {n} | {len(a['all'])} | {statistics.mean(a['all']):.2f} | {len(c)} | "
               f"{statistics.mean(c) if c else float('nan'):.2f} | {statistics.median(c) if c else float('nan'):.2f} |")
+    # step-1 timelines: every cold exact pass and the dispatches after it up to the next flush,
+    # in start order, relative to the exact pass's start (both streams)
+    order = sorted(range(len(rows)), key=lambda i: int(rows[i]["Start_Timestamp"]))
+    lines = []
+    for j, i in enumerate(order):
+        if names[i] != "exact_chunk_kernel" or not cold[i]:
+            continue
+        t0 = int(rows[i]["Start_Timestamp"])
+        seq = []
+        for i2 in order[j:]:
+            if names[i2].startswith("flush"):
+                break
+            seq.append(f"{names[i2]} {(int(rows[i2]['Start_Timestamp']) - t0) / 1e3:.1f}-"
+                       f"{(int(rows[i2]['End_Timestamp']) - t0) / 1e3:.1f}")
+        lines.append("; ".join(seq))
+    if lines:
+        print()
+        print("Step-1 timelines (cold exact pass and what follows it until the next flush; us from its start):")
+        print()
+        for ln in lines[:6]:
+            print(f"- {ln}")
 
 
 def summarize_pmc(fetch_dir, write_dir, config):
@@ -951,6 +1191,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", default="head128k", choices=sorted(workloads.CONFIG_BY_NAME))
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--no-ragged", action="store_true",
+                    help="skip the ragged paged batch measured beside a contiguous workload")
     ap.add_argument("--no-diag", action="store_true",
                     help="skip the next-row measurements (block attention, anchors and recall, page "
                          "selection, head-adaptive budgets): profiler runs of the main path")

@@ -68,6 +68,7 @@ def lib():
         L.mage_workspace_bytes.argtypes = [P(Dims), _i32, _i32]
         L.mage_workspace_bytes.restype = _sz
         L.mage_workspace_init.argtypes = [_vp, _sz, _vp]
+        L.mage_workspace_check.argtypes = [_vp, _sz, _vp, _vp]
         L.mage_select_exact.argtypes = [P(Dims), _vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp,
                                         _vp, _sz, _vp, _vp, _vp]
         L.mage_select_exact_paged.argtypes = [P(Dims), _vp, P(PagedKv), _i32, _vp, _vp, _vp, _vp,
@@ -100,7 +101,7 @@ def lib():
                                         _sz, _vp, _vp, _vp]
         L.mage_select_pages_paged.argtypes = [P(Dims), _vp, P(PagedKv), _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
                                               _sz, _vp, _vp, _vp]
-        for f in ("mage_workspace_init", "mage_select_exact", "mage_select_exact_paged",
+        for f in ("mage_workspace_init", "mage_workspace_check", "mage_select_exact", "mage_select_exact_paged",
                   "mage_exact_attn", "mage_exact_attn_paged",
                   "mage_sparse_attn", "mage_sparse_attn_paged", "mage_topk", "mage_block_attn",
                   "mage_sparse_block_attn", "mage_sparse_block_attn_paged", "mage_select_mean_query",
@@ -144,6 +145,14 @@ def workspace_bytes(dims: Dims, max_seq_len: int, k: int) -> int:
     return int(lib().mage_workspace_bytes(ctypes.byref(dims), int(max_seq_len), int(k)))
 
 
+def _capturing(stream) -> bool:
+    """True while `stream` (a torch stream, None = the current one) is being captured into a graph."""
+    if stream is None:
+        return torch.cuda.is_current_stream_capturing()
+    with torch.cuda.stream(stream):
+        return torch.cuda.is_current_stream_capturing()
+
+
 class Workspace:
     """A device workspace; grows when a call needs more.
 
@@ -151,32 +160,74 @@ class Workspace:
     that needs it: the sparse calls keep arrival counters in it, which must
     start at zero and which every call leaves at zero.
 
-    Calls through one Workspace are ordered: a call made after a step-1 call
-    whose selection ran on another stream first waits for that selection.
+    Calls through one Workspace are ordered, whatever streams they run on:
+    after every call an event is recorded on each stream the call used (its
+    stream and, for step 1, its select stream), and the next call's stream
+    waits for those of other streams before the library touches the buffer.
+    A buffer that is replaced by a larger one goes back to the allocator only
+    after the work queued on every stream that used it (record_stream). Under
+    graph capture no event is recorded or waited for: the graph's own edges
+    order the captured calls.
     """
 
     def __init__(self, device=None):
         self.device = torch.device(device or "cuda")
         self.buf = None
-        self.pending = None
+        self.pending = []          # [(stream, event)] of the previous call
+        self._users = set()        # streams (handles) the current buffer was used on
 
     def get(self, nbytes: int, stream=None) -> torch.Tensor:
         st = stream if stream is not None else torch.cuda.current_stream(self.device)
-        if self.pending is not None:
-            st.wait_event(self.pending)
-            self.pending = None
+        if not _capturing(st):
+            for s, ev in self.pending or []:
+                if s.cuda_stream != st.cuda_stream:
+                    st.wait_event(ev)
+            self.pending = []
         if self.buf is None or self.buf.numel() < nbytes:
             with torch.cuda.stream(st):
                 self.buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=self.device)
+            self._users = {st.cuda_stream}
             _check(lib().mage_workspace_init(_ptr(self.buf), self.buf.numel(), _stream(st)),
                    "mage_workspace_init")
         return self.buf
 
+    def done(self, stream=None, *others):
+        """Record that the call just issued used this workspace on `stream`
+        (None = the current stream) and on `others` (None entries ignored)."""
+        first = stream if stream is not None else torch.cuda.current_stream(self.device)
+        sts = [first] + [s for s in others if s is not None]
+        if any(_capturing(s) for s in sts):
+            return
+        out, seen = [], set()
+        for s in sts:
+            if s.cuda_stream in seen:
+                continue
+            seen.add(s.cuda_stream)
+            ev = torch.cuda.Event()
+            ev.record(s)
+            out.append((s, ev))
+            if s.cuda_stream not in self._users:
+                self.buf.record_stream(s)
+                self._users.add(s.cuda_stream)
+        self.pending = out
+
     def mark(self, stream):
         """Record that work using this workspace is still running on `stream`."""
-        ev = torch.cuda.Event()
-        ev.record(stream)
-        self.pending = ev
+        self.done(stream)
+
+    def check(self, stream=None) -> int:
+        """Number of non-zero arrival counters (0 for a healthy workspace);
+        waits for `stream`."""
+        st = stream if stream is not None else torch.cuda.current_stream(self.device)
+        if self.buf is None:
+            return 0
+        for s, ev in self.pending or []:
+            if s.cuda_stream != st.cuda_stream:
+                st.wait_event(ev)
+        out = torch.empty(1, dtype=torch.int32, device=self.device)
+        _check(lib().mage_workspace_check(_ptr(self.buf), self.buf.numel(), _ptr(out), _stream(st)),
+               "mage_workspace_check")
+        return int(out.item())
 
 
 _default_ws = {}
@@ -229,8 +280,7 @@ def select_exact(q, k_cache, v_cache, k: int, scale: float, *, o=None, lse=None,
                                    _ptr(ws), ws.numel(), _stream(stream),
                                    None if select_stream is None else _stream(select_stream),
                                    None), "mage_select_exact")
-    if select_stream is not None:
-        wso.mark(select_stream)
+    wso.done(stream, select_stream)
     if idx_ready is not None:
         idx_ready.record(select_stream if select_stream is not None else torch.cuda.current_stream())
     return o, lse, idx, scores
@@ -272,8 +322,7 @@ def select_exact_paged(q, k_pool, v_pool, page_table, seq_lens, k: int, scale: f
                                          _ptr(ws), ws.numel(), _stream(stream),
                                          None if select_stream is None else _stream(select_stream),
                                          None), "mage_select_exact_paged")
-    if select_stream is not None:
-        wso.mark(select_stream)
+    wso.done(stream, select_stream)
     if idx_ready is not None:
         idx_ready.record(select_stream if select_stream is not None else torch.cuda.current_stream())
     return o, lse, idx, scores
@@ -295,11 +344,13 @@ def select_pages(q, k_cache, v_cache, page_tokens: int, k_pages: int, scale: flo
     page_idx = _out(page_idx, (S, Hkv, k_pages), torch.int32, dev)
     if want_scores or scores is not None:
         scores = _out(scores, (S, Hkv, N), torch.float32, dev)
-    ws = _ws_obj(workspace, dev).get(workspace_bytes(dims, N, k), stream)
+    wso = _ws_obj(workspace, dev)
+    ws = wso.get(workspace_bytes(dims, N, k), stream)
     _check(lib().mage_select_pages(ctypes.byref(dims), _bf16_ptr(q, "q"), _bf16_ptr(k_cache, "k_cache"),
                                    _bf16_ptr(v_cache, "v_cache"), N, int(page_tokens), int(k_pages), _ptr(o),
                                    _ptr(lse), _ptr(idx), _ptr(page_idx), _ptr(scores), _ptr(ws), ws.numel(),
                                    _stream(stream), None, None), "mage_select_pages")
+    wso.done(stream)
     return o, lse, idx, page_idx, scores
 
 
@@ -319,11 +370,13 @@ def select_pages_paged(q, k_pool, v_pool, page_table, seq_lens, page_tokens: int
     page_idx = _out(page_idx, (S, Hkv, k_pages), torch.int32, dev)
     if want_scores or scores is not None:
         scores = _out(scores, (S, Hkv, max(lens)), torch.float32, dev)
-    ws = _ws_obj(workspace, dev).get(workspace_bytes(dims, max(lens), k), stream)
+    wso = _ws_obj(workspace, dev)
+    ws = wso.get(workspace_bytes(dims, max(lens), k), stream)
     _check(lib().mage_select_pages_paged(ctypes.byref(dims), _bf16_ptr(q, "q"), ctypes.byref(kv), int(page_tokens),
                                          int(k_pages), _ptr(o), _ptr(lse), _ptr(idx), _ptr(page_idx), _ptr(scores),
                                          _ptr(ws), ws.numel(), _stream(stream), None, None),
            "mage_select_pages_paged")
+    wso.done(stream)
     return o, lse, idx, page_idx, scores
 
 
@@ -341,11 +394,13 @@ def select_adaptive(q, k_cache, v_cache, k: int, scale: float, *, o=None, lse=No
     lse = _out(lse, (S, B, Hq), torch.float32, dev)
     idx = _out(idx, (S, Hkv, K), torch.int32, dev)
     counts = _out(counts, (S, Hkv), torch.int32, dev)
-    ws = _ws_obj(workspace, dev).get(workspace_bytes(dims, N, K), stream)
+    wso = _ws_obj(workspace, dev)
+    ws = wso.get(workspace_bytes(dims, N, K), stream)
     _check(lib().mage_select_adaptive(ctypes.byref(dims), _bf16_ptr(q, "q"), _bf16_ptr(k_cache, "k_cache"),
                                       _bf16_ptr(v_cache, "v_cache"), N, int(k), _ptr(o), _ptr(lse), _ptr(idx),
                                       _ptr(counts), _ptr(ws), ws.numel(), _stream(stream), None, None),
            "mage_select_adaptive")
+    wso.done(stream)
     return o, lse, idx, counts
 
 
@@ -362,10 +417,12 @@ def select_adaptive_paged(q, k_pool, v_pool, page_table, seq_lens, k: int, scale
     lse = _out(lse, (S, B, Hq), torch.float32, dev)
     idx = _out(idx, (S, Hkv, K), torch.int32, dev)
     counts = _out(counts, (S, Hkv), torch.int32, dev)
-    ws = _ws_obj(workspace, dev).get(workspace_bytes(dims, max(lens), K), stream)
+    wso = _ws_obj(workspace, dev)
+    ws = wso.get(workspace_bytes(dims, max(lens), K), stream)
     _check(lib().mage_select_adaptive_paged(ctypes.byref(dims), _bf16_ptr(q, "q"), ctypes.byref(kv), int(k),
                                             _ptr(o), _ptr(lse), _ptr(idx), _ptr(counts), _ptr(ws), ws.numel(),
                                             _stream(stream), None, None), "mage_select_adaptive_paged")
+    wso.done(stream)
     return o, lse, idx, counts
 
 
@@ -390,11 +447,13 @@ def sparse_attn_counts(q, k_cache, v_cache, idx, counts, k_seq: int, scale: floa
     dev = q.device
     o = _out(o, (S, B, Hq, d), torch.float32, dev)
     lse = _out(lse, (S, B, Hq), torch.float32, dev)
-    ws = _ws_obj(workspace, dev).get(workspace_bytes(dims, N, k_row), stream)
+    wso = _ws_obj(workspace, dev)
+    ws = wso.get(workspace_bytes(dims, N, k_row), stream)
     _check(lib().mage_sparse_attn_counts(ctypes.byref(dims), _bf16_ptr(q, "q"), _bf16_ptr(k_cache, "k_cache"),
                                          _bf16_ptr(v_cache, "v_cache"), N, _ptr(idx), int(k_row), cp, int(k_seq),
                                          _ptr(o), _ptr(lse), _ptr(ws), ws.numel(), _stream(stream)),
            "mage_sparse_attn_counts")
+    wso.done(stream)
     return o, lse
 
 
@@ -412,10 +471,12 @@ def sparse_attn_counts_paged(q, k_pool, v_pool, page_table, seq_lens, idx, count
     dev = q.device
     o = _out(o, (S, B, Hq, d), torch.float32, dev)
     lse = _out(lse, (S, B, Hq), torch.float32, dev)
-    ws = _ws_obj(workspace, dev).get(workspace_bytes(dims, max(lens), k_row), stream)
+    wso = _ws_obj(workspace, dev)
+    ws = wso.get(workspace_bytes(dims, max(lens), k_row), stream)
     _check(lib().mage_sparse_attn_counts_paged(ctypes.byref(dims), _bf16_ptr(q, "q"), ctypes.byref(kv), _ptr(idx),
                                                int(k_row), cp, int(k_seq), _ptr(o), _ptr(lse), _ptr(ws),
                                                ws.numel(), _stream(stream)), "mage_sparse_attn_counts_paged")
+    wso.done(stream)
     return o, lse
 
 
@@ -440,10 +501,12 @@ def select_mean_query(q, k_cache, v_cache, k: int, scale: float, *, idx=None, sc
     idx = _out(idx, (S, Hkv, k), torch.int32, dev)
     if want_scores or scores is not None:
         scores = _out(scores, (S, Hkv, N), torch.float32, dev)
-    ws = _ws_obj(workspace, dev).get(workspace_bytes(dims, N, k), stream)
+    wso = _ws_obj(workspace, dev)
+    ws = wso.get(workspace_bytes(dims, N, k), stream)
     _check(lib().mage_select_mean_query(ctypes.byref(dims), _bf16_ptr(q, "q"), _bf16_ptr(k_cache, "k_cache"),
                                         _bf16_ptr(v_cache, "v_cache"), N, int(k), _ptr(idx), _ptr(scores),
                                         _ptr(ws), ws.numel(), _stream(stream)), "mage_select_mean_query")
+    wso.done(stream)
     return idx, scores
 
 
@@ -458,10 +521,12 @@ def select_mean_query_paged(q, k_pool, v_pool, page_table, seq_lens, k: int, sca
     idx = _out(idx, (S, Hkv, k), torch.int32, dev)
     if want_scores or scores is not None:
         scores = _out(scores, (S, Hkv, max(lens)), torch.float32, dev)
-    ws = _ws_obj(workspace, dev).get(workspace_bytes(dims, max(lens), k), stream)
+    wso = _ws_obj(workspace, dev)
+    ws = wso.get(workspace_bytes(dims, max(lens), k), stream)
     _check(lib().mage_select_mean_query_paged(ctypes.byref(dims), _bf16_ptr(q, "q"), ctypes.byref(kv), int(k),
                                               _ptr(idx), _ptr(scores), _ptr(ws), ws.numel(), _stream(stream)),
            "mage_select_mean_query_paged")
+    wso.done(stream)
     return idx, scores
 
 
@@ -490,10 +555,12 @@ def exact_attn(q, k_cache, v_cache, scale: float, *, o=None, lse=None, workspace
     dev = q.device
     o = _out(o, (S, B, Hq, d), torch.float32, dev)
     lse = _out(lse, (S, B, Hq), torch.float32, dev)
-    ws = _ws_obj(workspace, dev).get(workspace_bytes(dims, N, 1), stream)
+    wso = _ws_obj(workspace, dev)
+    ws = wso.get(workspace_bytes(dims, N, 1), stream)
     _check(lib().mage_exact_attn(ctypes.byref(dims), _bf16_ptr(q, "q"), _bf16_ptr(k_cache, "k_cache"),
                                  _bf16_ptr(v_cache, "v_cache"), N, _ptr(o), _ptr(lse), _ptr(ws),
                                  ws.numel(), _stream(stream)), "mage_exact_attn")
+    wso.done(stream)
     return o, lse
 
 
@@ -507,10 +574,12 @@ def exact_attn_paged(q, k_pool, v_pool, page_table, seq_lens, scale: float, *, o
     dev = q.device
     o = _out(o, (S, B, Hq, d), torch.float32, dev)
     lse = _out(lse, (S, B, Hq), torch.float32, dev)
-    ws = _ws_obj(workspace, dev).get(workspace_bytes(dims, max(lens), 1), stream)
+    wso = _ws_obj(workspace, dev)
+    ws = wso.get(workspace_bytes(dims, max(lens), 1), stream)
     _check(lib().mage_exact_attn_paged(ctypes.byref(dims), _bf16_ptr(q, "q"), ctypes.byref(kv),
                                        _ptr(o), _ptr(lse), _ptr(ws), ws.numel(), _stream(stream)),
            "mage_exact_attn_paged")
+    wso.done(stream)
     return o, lse
 
 
@@ -526,11 +595,13 @@ def sparse_attn(q, k_cache, v_cache, idx, scale: float, *, o=None, lse=None, wor
     dev = q.device
     o = _out(o, (S, B, Hq, d), torch.float32, dev)
     lse = _out(lse, (S, B, Hq), torch.float32, dev)
-    ws = _ws_obj(workspace, dev).get(workspace_bytes(dims, N, k), stream)
+    wso = _ws_obj(workspace, dev)
+    ws = wso.get(workspace_bytes(dims, N, k), stream)
     _check(lib().mage_sparse_attn(ctypes.byref(dims), _bf16_ptr(q, "q"),
                                   _bf16_ptr(k_cache, "k_cache"), _bf16_ptr(v_cache, "v_cache"), N,
                                   _ptr(idx), int(k), _ptr(o), _ptr(lse), _ptr(ws), ws.numel(),
                                   _stream(stream)), "mage_sparse_attn")
+    wso.done(stream)
     return o, lse
 
 
@@ -547,10 +618,12 @@ def sparse_attn_paged(q, k_pool, v_pool, page_table, seq_lens, idx, scale: float
     dev = q.device
     o = _out(o, (S, B, Hq, d), torch.float32, dev)
     lse = _out(lse, (S, B, Hq), torch.float32, dev)
-    ws = _ws_obj(workspace, dev).get(workspace_bytes(dims, max(lens), k), stream)
+    wso = _ws_obj(workspace, dev)
+    ws = wso.get(workspace_bytes(dims, max(lens), k), stream)
     _check(lib().mage_sparse_attn_paged(ctypes.byref(dims), _bf16_ptr(q, "q"), ctypes.byref(kv),
                                         _ptr(idx), int(k), _ptr(o), _ptr(lse), _ptr(ws),
                                         ws.numel(), _stream(stream)), "mage_sparse_attn_paged")
+    wso.done(stream)
     return o, lse
 
 
@@ -576,11 +649,13 @@ def sparse_block_attn(q, k_cache, v_cache, idx, k_blk, v_blk, scale: float, *, o
     dev = q.device
     o = _out(o, (S, B, Hq, d), torch.float32, dev)
     lse = _out(lse, (S, B, Hq), torch.float32, dev)
-    ws = _ws_obj(workspace, dev).get(workspace_bytes(dims, N, k), stream)
+    wso = _ws_obj(workspace, dev)
+    ws = wso.get(workspace_bytes(dims, N, k), stream)
     _check(lib().mage_sparse_block_attn(ctypes.byref(dims), _bf16_ptr(q, "q"),
                                         _bf16_ptr(k_cache, "k_cache"), _bf16_ptr(v_cache, "v_cache"), N,
                                         _ptr(idx), int(k), kb, vb, _ptr(o), _ptr(lse), _ptr(ws),
                                         ws.numel(), _stream(stream)), "mage_sparse_block_attn")
+    wso.done(stream)
     return o, lse
 
 
@@ -598,10 +673,12 @@ def sparse_block_attn_paged(q, k_pool, v_pool, page_table, seq_lens, idx, k_blk,
     dev = q.device
     o = _out(o, (S, B, Hq, d), torch.float32, dev)
     lse = _out(lse, (S, B, Hq), torch.float32, dev)
-    ws = _ws_obj(workspace, dev).get(workspace_bytes(dims, max(lens), k), stream)
+    wso = _ws_obj(workspace, dev)
+    ws = wso.get(workspace_bytes(dims, max(lens), k), stream)
     _check(lib().mage_sparse_block_attn_paged(ctypes.byref(dims), _bf16_ptr(q, "q"), ctypes.byref(kv),
                                               _ptr(idx), int(k), kb, vb, _ptr(o), _ptr(lse), _ptr(ws),
                                               ws.numel(), _stream(stream)), "mage_sparse_block_attn_paged")
+    wso.done(stream)
     return o, lse
 
 
@@ -639,9 +716,11 @@ def topk(scores, k: int, lens=None, *, idx=None, workspace=None, stream=None):
         keep = (ctypes.c_int32 * rows)(*lens)
         lp = ctypes.cast(keep, ctypes.POINTER(ctypes.c_int32))
     dims = Dims(rows, 1, 1, 1, 64, 1.0)
-    ws = _ws_obj(workspace, scores.device).get(workspace_bytes(dims, n, k), stream)
+    wso = _ws_obj(workspace, scores.device)
+    ws = wso.get(workspace_bytes(dims, n, k), stream)
     _check(lib().mage_topk(rows, _ptr(scores), scores.stride(0), lp, n, int(k), _ptr(idx),
                            _ptr(ws), ws.numel(), _stream(stream)), "mage_topk")
+    wso.done(stream)
     return idx
 
 

@@ -47,6 +47,8 @@ struct AttnParams {
   uint32_t* arrivals;       // sparse pass, uniform chunks: one counter per (unit, row block), zero
                             //   between launches; non-null = the last work-group of a (unit, row
                             //   block) to finish merges its chunks (no merge launch)
+  uint32_t* zero_hist;      // exact pass before a selection: the unit's score histogram [U][1024]
+  uint32_t* zero_count;     //   and its top-k arrival counter [U] are zeroed by chunk 0 (or null)
 };
 
 struct MergeParams {
@@ -54,7 +56,6 @@ struct MergeParams {
   const float* part_ml;
   float* o;
   float* lse;               // nullable
-  float* rowstat;           // per (unit, row): max + log2(sum), log2 units
   int32_t S, B, Hq, Hkv, G, R, nrb;
   int32_t chunk, nchunk;
   int32_t n_uniform;        // >= 0: entries per unit (prefix length or idx count); < 0: lens
@@ -161,6 +162,41 @@ __device__ __forceinline__ void merge_chunks(const float* part_o, const float* p
         acc[q][2] += wc * vb[j][q][2];
         acc[q][3] += wc * vb[j][q][3];
       }
+    }
+  }
+}
+
+// The merged (max, sum) of row r over the split chunks slot0 .. slot0 + nch - 1
+// (log2 units): the (M, L) half of merge_chunks, same batches and order, so
+// both give the same bits for the same kBatch.
+template <int kBatch>
+__device__ __forceinline__ void merge_row_stats(const float* part_ml, int64_t slot0, int nch, int r, float& M,
+                                                float& L) {
+  const float* ml0 = part_ml + slot0 * kMaxRows * 2;
+  M = -__builtin_inff();
+  L = 0.f;
+  for (int c0 = 0; c0 < nch; c0 += kBatch) {
+    float mb[kBatch], lb[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int mf = (min(c0 + j, nch - 1) * kMaxRows + r) * 2;
+      mb[j] = ml0[mf];
+      lb[j] = ml0[mf + 1];
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j)
+      if (c0 + j >= nch) mb[j] = -__builtin_inff();
+    float Mb = M;
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) Mb = fmaxf(Mb, mb[j]);
+    if (Mb == -__builtin_inff()) continue;
+    const float f = fast_exp2(M - Mb);
+    L *= f;
+    M = Mb;
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const float wc = fast_exp2(mb[j] - M);
+      L += lb[j] * wc;
     }
   }
 }
@@ -307,6 +343,8 @@ __device__ __forceinline__ void attend_half(uint32_t k_base, uint32_t v_addr,
 // barrier per tile. The loop is software-pipelined: in iteration t a wave
 // issues the QK product of tile t+1 and then runs the softmax and PV of tile
 // t, so the MFMAs of one tile run under the vector work of the other.
+// kSplitIssue (contiguous caches only): the tile loads are issued by the four
+// key-half-1 waves; else (paged caches) every wave issues its own slices.
 template <int D, int kStages, bool kSplitIssue = true>
 __global__ __launch_bounds__(kAttnThreads) void exact_chunk_kernel(AttnParams p) {
   using G = TileGeom<D, kAttnThreads>;
@@ -315,7 +353,7 @@ __global__ __launch_bounds__(kAttnThreads) void exact_chunk_kernel(AttnParams p)
   static_assert(2 * kStages * G::kBytes >= 4 * kWave * (2 + 16 * kNdb) * 4, "pair-merge area");
   // K ring (kStages tiles) followed by the V ring (kStages tiles)
   __shared__ __attribute__((aligned(1024))) uint8_t s_ring[2 * kStages * G::kBytes];
-  __shared__ int32_t s_pages[kMaxChunkPages];   // paged layout: page ids of the chunk
+  __shared__ int32_t s_pages[kSplitIssue ? 1 : kMaxChunkPages];   // paged layout: page ids of the chunk
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -333,7 +371,7 @@ __global__ __launch_bounds__(kAttnThreads) void exact_chunk_kernel(AttnParams p)
   if (e0 >= e1) return;  // chunk past this sequence's end
   const int nrb = (p.R + 31) >> 5;
   const bool computes = rb < nrb;
-  const bool paged = p.kv.page_table != nullptr;
+  const bool paged = !kSplitIssue && p.kv.page_table != nullptr;   // the split-issue form is contiguous only
   const int pshift = p.kv.page_shift, pmask = (1 << p.kv.page_shift) - 1;
   const int64_t seq_base = paged ? 0 : (static_cast<int64_t>(s) * p.Hkv + h) * p.kv.n_uniform;
   const int32_t* ptab = paged ? p.kv.page_table + static_cast<int64_t>(s) * p.kv.max_pages : nullptr;
@@ -345,6 +383,12 @@ __global__ __launch_bounds__(kAttnThreads) void exact_chunk_kernel(AttnParams p)
   if (paged) {
     const int np = ((e1 - 1) >> pshift) - page0 + 1;
     for (int i = tid; i < np; i += kAttnThreads) s_pages[i] = ptab[page0 + i];
+  }
+  if (c == 0 && p.zero_hist != nullptr) {
+    // the selection that follows adds its score histogram into this row and
+    // counts its top-k work-groups here
+    for (int b = tid; b < 1024; b += kAttnThreads) p.zero_hist[static_cast<int64_t>(u) * 1024 + b] = 0u;
+    if (tid == 0) p.zero_count[u] = 0u;
   }
 
   // Q rows of this row block as MFMA B operand fragments (d slice 16ks + 8hh .. +7)
@@ -473,8 +517,8 @@ __global__ __launch_bounds__(kAttnThreads) void exact_chunk_kernel(AttnParams p)
 #pragma unroll
       for (int j = 0; j < G::kInstr; ++j) {
         const int slot = ws * G::kInstr + j;
-        dma16x2(kbytes + row_bytes(bk + slot * kKRowsPerInstr), koff[j], lk + slot * 1024,
-                vbytes + row_bytes(bv + ((slot & 3) << 4)), voff[j] + vadd, lv + slot * 1024);
+        dma16x2<true>(kbytes + row_bytes(bk + slot * kKRowsPerInstr), koff[j], lk + slot * 1024,
+                      vbytes + row_bytes(bv + ((slot & 3) << 4)), voff[j] + vadd, lv + slot * 1024);
       }
       return;
     }
@@ -489,10 +533,10 @@ __global__ __launch_bounds__(kAttnThreads) void exact_chunk_kernel(AttnParams p)
         dma16_sync(p.kv.k + row_of(bk + r) + uk * 8, lk + slot * 1024);
       }
       if (fv) {
-        dma16(vbytes + row_bytes(bv + ((slot & 3) << 4)), voff[j] + vadd, lv + slot * 1024);
+        dma16<true>(vbytes + row_bytes(bv + ((slot & 3) << 4)), voff[j] + vadd, lv + slot * 1024);
       } else if (tv >= 0) {
         const int db = slot >> 2, rv = ((slot & 3) << 4) + (lane >> 2);
-        dma16_sync(p.kv.v + row_of(bv + rv) + 32 * db + 8 * (lane & 3), lv + slot * 1024);
+        dma16_sync<true>(p.kv.v + row_of(bv + rv) + 32 * db + 8 * (lane & 3), lv + slot * 1024);
       }
     }
   };
@@ -506,23 +550,33 @@ __global__ __launch_bounds__(kAttnThreads) void exact_chunk_kernel(AttnParams p)
     }
   };
   // Load group g = what iteration g reads: K rows of tile g+1 and V rows of
-  // tile g-1. Iteration t waits for group t, with groups t+1 and t+2 (issued
-  // in the two iterations before) still allowed in flight, then issues group
-  // t+3 into the slots of K(t) and V(t-2), which no wave reads any more once
-  // every wave has passed the barrier of iteration t.
+  // tile g-1. Iteration t waits for group t, with the kStages - 2 groups after
+  // it still allowed in flight, and issues group t + kStages - 1 into the
+  // slots of K(t) and V(t-2), which no wave reads any more once every wave
+  // has passed the barrier of iteration t (K(t) was read by the QK product and
+  // V(t-2) by the PV product of iteration t-1).
+  constexpr int kPerTile = (split_issue ? 2 : 1) * G::kInstr;   // issuers: two slices per tile
   auto group_k = [&](int g) { return g + 1 < ntiles ? g + 1 : -1; };
   auto group_v = [&](int g) { return g >= 1 && g - 1 < ntiles ? g - 1 : -1; };
   auto group_tiles = [&](int g) { return (group_k(g) >= 0) + (group_v(g) >= 0); };
   auto wait_group = [&](int g) {
-    // issuers wait for two slices' loads per tile; the others have none in flight
-    wait_tiles<(split_issue ? 2 : 1) * G::kInstr, 5>(group_tiles(g + 1) + group_tiles(g + 2));
+    // the others have none in flight
+    int pending = 0;
+#pragma unroll
+    for (int j = 1; j <= kStages - 2; ++j) pending += group_tiles(g + j);
+    wait_tiles<kPerTile, 2 * (kStages - 2) + 1>(pending);
     wg_barrier();
   };
 
   issue(0, -1);
 #pragma unroll
-  for (int g = 0; g < 3; ++g) issue(group_k(g), group_v(g));
-  wait_tiles<(split_issue ? 2 : 1) * G::kInstr, 7>(group_tiles(0) + group_tiles(1) + group_tiles(2));   // K(0)
+  for (int g = 0; g < kStages - 1; ++g) issue(group_k(g), group_v(g));
+  {
+    int pending = 0;   // everything but K(0)
+#pragma unroll
+    for (int g = 0; g < kStages - 1; ++g) pending += group_tiles(g);
+    wait_tiles<kPerTile, 2 * (kStages - 1) + 1>(pending);
+  }
   wg_barrier();
   f32x16 s_cur;
   if (computes) s_cur = qk_half<D>(k_slot(0) + k_half, kofs, qf);
@@ -541,7 +595,7 @@ __global__ __launch_bounds__(kAttnThreads) void exact_chunk_kernel(AttnParams p)
   // t = 0: softmax of tile 0 and QK of tile 1
   auto first = [&](auto masked) {
     wait_group(0);
-    issue(group_k(3), group_v(3));
+    issue(group_k(kStages - 1), group_v(kStages - 1));
     if (computes) {
       float alpha;
       bool grow;
@@ -554,7 +608,7 @@ __global__ __launch_bounds__(kAttnThreads) void exact_chunk_kernel(AttnParams p)
     [[maybe_unused]] const uint64_t tr0 = MAGE_TRACE_NOW();
     wait_group(t);
     [[maybe_unused]] const uint64_t tr1 = MAGE_TRACE_NOW();
-    issue(group_k(t + 3), group_v(t + 3));
+    issue(group_k(t + kStages - 1), group_v(t + kStages - 1));
     if (computes) {
       const uint32_t okm = half_mask(t);
       const uint32_t kb = k_slot(t + 1 < ntiles ? t + 1 : t) + k_half;
@@ -1021,11 +1075,11 @@ __global__ __launch_bounds__(kSparseThreads) void sparse_attn_kernel(AttnParams 
 
 // Merge of split partials (exact pass: chunks of the prefix; sparse pass:
 // chunks of the index list). One work-group per (unit, row block, d block);
-// wave i4 handles accumulator registers 4*i4..4*i4+3. Also writes lse and, if
-// rowstat is non-null, the per-row max + log2(sum) that the score sweep needs.
-// Used by the exact pass (whose merged row statistics feed the score sweep on
-// the select stream) and by the sparse pass with per-unit counts; the sparse
-// pass with uniform chunks merges inside its own launch (arrival counters).
+// wave i4 handles accumulator registers 4*i4..4*i4+3. Also writes lse. Used
+// by the exact pass (its O and lse; the score sweep on the select stream
+// merges the row statistics it needs itself, so this launch runs beside it)
+// and by the sparse pass with per-unit counts; the sparse pass with uniform
+// chunks merges inside its own launch (arrival counters).
 template <int D>
 __global__ __launch_bounds__(kThreads) void exact_merge_kernel(MergeParams p) {
   constexpr int kNdb = D / 32;
@@ -1062,11 +1116,7 @@ __global__ __launch_bounds__(kThreads) void exact_merge_kernel(MergeParams p) {
   const float inv = L > 0.f ? 1.f / L : 0.f;
   f32x4 v{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
   *reinterpret_cast<f32x4*>(p.o + row * D + 32 * db + 8 * i4 + 4 * hh) = v;
-  if (db == 0 && i4 == 0 && hh == 0) {
-    const float c2 = M + __log2f(L);
-    if (p.lse != nullptr) p.lse[row] = c2 * kLn2;
-    if (p.rowstat != nullptr) p.rowstat[static_cast<int64_t>(u) * kMaxRows + r] = c2;
-  }
+  if (db == 0 && i4 == 0 && hh == 0 && p.lse != nullptr) p.lse[row] = (M + __log2f(L)) * kLn2;
 }
 
 // ---------------------------------------------------------------------------

@@ -209,7 +209,7 @@ constexpr int kSparseStages = 2;
 // ---- workspace layout ------------------------------------------------------
 struct Layout {
   size_t arrivals;       // sparse pass: per (unit, row block) arrival counters; first, at a fixed place
-  size_t rowstat, part_ml, part_o, cand_bits, cand_pos, cand_count, row_info, hist, hist_parts, scores;
+  size_t part_ml, part_o, cand_bits, cand_pos, cand_count, topk_arrivals, hist, scores;
   size_t qbar, qbar_o;   // mean-query selection: the mean query and its (unused) attention output
   size_t page_scores, page_idx;   // page-granular selection (pages of >= 1 positions; <= k page ids)
   size_t total;
@@ -240,16 +240,13 @@ Layout make_layout(const Dims& d, int64_t max_n, int64_t k) {
   // capacity, so no other region of any call shape overlaps them: a zeroed
   // workspace keeps them zero through every call.
   L.arrivals = take(kArrivalUnits * (kMaxRows / 32) * 4);
-  L.rowstat = take(U * kMaxRows * 4);
   L.part_ml = take(L.slots * kMaxRows * 2 * 4);
   L.part_o = take(L.slots * 4 * (d.D / 32) * 4 * kWave * 16);
   L.cand_bits = take(U * L.cand_stride * 4);
   L.cand_pos = take(U * L.cand_stride * 4);
   L.cand_count = take(U * nchunk * 4);
-  L.row_info = take(U * 2 * 4);
+  L.topk_arrivals = take(U * 4);
   L.hist = take(U * kHistBins * 4);
-  // histogram parts: one per score chunk (standalone top-k: one per 4096-entry chunk)
-  L.hist_parts = take(U * cdiv(max_n, kScoreChunkMin) * kHistBins * 4);
   L.scores = take(U * max_n * 4);
   L.qbar = take(U * d.D * 2);
   L.qbar_o = take(U * d.D * 4);
@@ -364,28 +361,47 @@ ChunkMap topk_map(const TopkParams& tp, int seqs) {
 // Rows longer than this are beyond the final pass's chunk table.
 constexpr int64_t kMaxTopkLen = static_cast<int64_t>(kMaxLocalChunks) * kLocalChunk;
 
-// The row histograms are the sums of the parts in hr.parts; with
-// build_parts (standalone top-k) the parts are first taken from the scores,
-// else the score sweep has written them.
-mage_status launch_topk(const TopkParams& tp, const HistReduceParams& hr, hipStream_t stream,
-                        bool build_parts) {
+// Top-k of tp.rows rows. build_hist: the rows' histograms (and their arrival
+// counters) are first zeroed and built from the scores (standalone top-k);
+// else the score sweep has built them after the exact pass zeroed them.
+mage_status launch_topk(const TopkParams& tp, hipStream_t stream, bool build_hist) {
   const int64_t wgs = tp.map.on ? tp.map.first[tp.rows / tp.rows_per_seq] : static_cast<int64_t>(tp.rows) * tp.nchunk;
-  if (build_parts) {
-    if (mage_status st = launch(kfn(topk_hist_kernel), "topk_hist_kernel", wgs, kLocalThreads, stream, tp);
+  if (build_hist) {
+    if (mage_status st = launch(kfn(topk_prep_kernel), "topk_prep_kernel", tp.rows, kHistThreads, stream, tp);
+        st != MAGE_OK)
+      return st;
+    if (mage_status st = launch(kfn(topk_hist_kernel), "topk_hist_kernel", wgs, kHistThreads, stream, tp);
         st != MAGE_OK)
       return st;
   }
-  if (mage_status st = launch(kfn(hist_reduce_kernel), "hist_reduce_kernel",
-                              static_cast<int64_t>(hr.rows) * (kHistBins / 256), kHistReduceThreads, stream, hr);
-      st != MAGE_OK)
-    return st;
-  if (mage_status st = launch(kfn(topk_local_kernel), "topk_local_kernel", wgs, kLocalThreads, stream, tp);
-      st != MAGE_OK)
-    return st;
   // the wide final pass for large k: more candidates stay on the register path
   if (tp.k > kFinalMax / 2)
-    return launch(kfn(topk_final_kernel<kFinalMaxWide>), "topk_final_kernel", tp.rows, kTopkThreads, stream, tp);
-  return launch(kfn(topk_final_kernel<kFinalMax>), "topk_final_kernel", tp.rows, kTopkThreads, stream, tp);
+    return launch(kfn(topk_select_kernel<kFinalMaxWide>), "topk_select_kernel", wgs, kTopkThreads, stream, tp);
+  return launch(kfn(topk_select_kernel<kFinalMax>), "topk_select_kernel", wgs, kTopkThreads, stream, tp);
+}
+
+// The shared fields of a top-k over `rows` rows of the workspace's buffers.
+TopkParams topk_params(void* ws, const Layout& L, const float* scores, int64_t stride, int32_t* idx, int32_t k,
+                       int32_t rows, int32_t rows_per_seq, int32_t n_uniform, int64_t row_len_max,
+                       const SeqLens& lens, int seqs) {
+  TopkParams tp{};
+  tp.scores = scores;
+  tp.stride = stride;
+  tp.idx = idx;
+  tp.k = k;
+  tp.hist = at<uint32_t>(ws, L.hist);
+  tp.cand_bits = at<uint32_t>(ws, L.cand_bits);
+  tp.cand_pos = at<int32_t>(ws, L.cand_pos);
+  tp.nchunk = static_cast<int>(cdiv(row_len_max, kLocalChunk));
+  tp.cand_stride = static_cast<int64_t>(tp.nchunk) * kLocalChunk;
+  tp.cand_count = at<int32_t>(ws, L.cand_count);
+  tp.arrivals = at<uint32_t>(ws, L.topk_arrivals);
+  tp.rows = rows;
+  tp.rows_per_seq = rows_per_seq;
+  tp.n_uniform = n_uniform;
+  tp.lens = lens;
+  tp.map = topk_map(tp, seqs);
+  return tp;
 }
 
 struct PagePlan;
@@ -438,18 +454,35 @@ mage_status launch_select(const Dims& d, const uint16_t* q, const KvArgs& kv, in
   ap.lens = kv.lens;
   int64_t exact_grid = 0;
   ap.map = chunk_map(kv, d, chunk, exact_grid);
+  // the main selection adds its score histogram into zeroed rows: chunk 0 of
+  // every unit zeroes its row and the row's top-k arrival counter
+  const bool main_topk = k > 0 && !pages && !budget;
+  ap.zero_hist = main_topk ? at<uint32_t>(ws, L.hist) : nullptr;
+  ap.zero_count = main_topk ? at<uint32_t>(ws, L.topk_arrivals) : nullptr;
   // contiguous caches: tile loads issued by half the waves; paged: by all
   const void* exact_fn = kv.src.page_table ? kfn(exact_chunk_kernel<D, kStagesFor<D>, false>)
                                            : kfn(exact_chunk_kernel<D, kStagesFor<D>, true>);
   if (mage_status st = launch(exact_fn, "exact_chunk_kernel", exact_grid, kAttnThreads, attn, ap); st != MAGE_OK)
     return st;
 
+  // The select stream starts right after the exact pass: the score sweep
+  // merges the row statistics it needs from the chunk partials itself, so the
+  // merge of O below runs on attn_stream beside it.
+  if (k > 0 && sel && sel != attn) {
+    hipEvent_t ev = internal_event();
+    if (!ev) return fail(MAGE_ERR_HIP, "could not create the stream-ordering event");
+    if (hipError_t e = hipEventRecord(ev, attn); e != hipSuccess) return hip_fail(e, "hipEventRecord");
+    if (hipError_t e = hipStreamWaitEvent(sel, ev, 0); e != hipSuccess)
+      return hip_fail(e, "hipStreamWaitEvent");
+  } else {
+    sel = attn;
+  }
+
   MergeParams mp{};
   mp.part_o = ap.part_o;
   mp.part_ml = ap.part_ml;
   mp.o = o;
   mp.lse = lse;
-  mp.rowstat = at<float>(ws, L.rowstat);
   mp.S = d.S; mp.B = d.B; mp.Hq = d.Hq; mp.Hkv = d.Hkv; mp.G = d.G; mp.R = d.R; mp.nrb = d.nrb;
   mp.chunk = chunk;
   mp.nchunk = nch;
@@ -461,26 +494,19 @@ mage_status launch_select(const Dims& d, const uint16_t* q, const KvArgs& kv, in
     return st;
   if (k == 0) return MAGE_OK;
 
-  if (sel && sel != attn) {
-    hipEvent_t ev = internal_event();
-    if (!ev) return fail(MAGE_ERR_HIP, "could not create the stream-ordering event");
-    if (hipError_t e = hipEventRecord(ev, attn); e != hipSuccess) return hip_fail(e, "hipEventRecord");
-    if (hipError_t e = hipStreamWaitEvent(sel, ev, 0); e != hipSuccess)
-      return hip_fail(e, "hipStreamWaitEvent");
-  } else {
-    sel = attn;
-  }
-
   ScoreParams sp{};
   sp.q = q;
   sp.kv = kv.src;
-  sp.rowstat = mp.rowstat;
-  sp.hist_parts = at<uint32_t>(ws, L.hist_parts);
+  sp.part_ml = ap.part_ml;
+  sp.exact_chunk = chunk;
+  sp.exact_nchunk = nch;
+  sp.hist = main_topk ? at<uint32_t>(ws, L.hist) : nullptr;
+  sp.k = k;
   sp.scores = scores ? scores : at<float>(ws, L.scores);
   sp.stride = scores ? score_stride : kv.max_n;
   sp.S = d.S; sp.B = d.B; sp.Hq = d.Hq; sp.Hkv = d.Hkv; sp.G = d.G; sp.R = d.R;
   // positions per work-group: halved from kScoreChunk (down to kScoreChunkMin)
-  // until the sweep has two rounds of work-groups (two per CU fit at once)
+  // until the sweep has two rounds of work-groups (two fit on a CU)
   sp.chunk = kScoreChunk;
   for (int64_t g = 0; sp.chunk > kScoreChunkMin; sp.chunk /= 2) {
     chunk_map(kv, d, sp.chunk, g);
@@ -492,49 +518,19 @@ mage_status launch_select(const Dims& d, const uint16_t* q, const KvArgs& kv, in
   sp.lens = kv.lens;
   int64_t score_grid = 0;
   sp.map = chunk_map(kv, d, sp.chunk, score_grid);
-  if (mage_status st = launch(kfn(score_kernel<D, kScoreStagesFor<D>>), "score_kernel",
-                              score_grid, kThreads, sel, sp);
-      st != MAGE_OK)
+  const void* score_fn = env_int("MAGE_SCORE_NT", 1) ? kfn(score_kernel<D, kScoreStagesFor<D>, true>)
+                                                      : kfn(score_kernel<D, kScoreStagesFor<D>, false>);
+  if (mage_status st = launch(score_fn, "score_kernel", score_grid, kThreads, sel, sp); st != MAGE_OK)
     return st;
-  if (pages || budget) {
+  if (main_topk) {
+    const TopkParams tp = topk_params(ws, L, sp.scores, sp.stride, idx, k, static_cast<int32_t>(U), d.Hkv,
+                                      kv.src.page_table ? -1 : kv.src.n_uniform, kv.max_n, kv.lens, d.S);
+    if (mage_status st = launch_topk(tp, sel, false); st != MAGE_OK) return st;
+  } else {
     mage_status st = pages ? launch_page_topk(d, kv, sp.scores, sp.stride, *pages, idx, ws, L, sel)
                            : launch_budget_topk(d, kv, sp.scores, sp.stride, *budget, idx, ws, L, sel);
     if (st != MAGE_OK) return st;
-    if (idx_ready) {
-      if (hipError_t e = hipEventRecord(idx_ready, sel); e != hipSuccess)
-        return hip_fail(e, "hipEventRecord(idx_ready)");
-    }
-    return MAGE_OK;
   }
-
-  TopkParams tp{};
-  tp.scores = sp.scores;
-  tp.stride = sp.stride;
-  tp.idx = idx;
-  tp.k = k;
-  tp.hist = at<uint32_t>(ws, L.hist);
-  tp.cand_bits = at<uint32_t>(ws, L.cand_bits);
-  tp.cand_pos = at<int32_t>(ws, L.cand_pos);
-  tp.cand_stride = L.cand_stride;
-  tp.cand_count = at<int32_t>(ws, L.cand_count);
-  tp.row_info = at<int32_t>(ws, L.row_info);
-  tp.rows = static_cast<int32_t>(U);
-  tp.rows_per_seq = d.Hkv;
-  tp.n_uniform = kv.src.page_table ? -1 : kv.src.n_uniform;
-  tp.nchunk = static_cast<int>(cdiv(kv.max_n, kLocalChunk));
-  tp.lens = kv.lens;
-  tp.map = topk_map(tp, d.S);
-  HistReduceParams hr{};
-  hr.parts = sp.hist_parts;
-  hr.hist = tp.hist;
-  hr.rows = tp.rows;
-  hr.nparts = sp.nchunk;
-  hr.part_len = sp.chunk;
-  hr.rows_per_seq = tp.rows_per_seq;
-  hr.n_uniform = tp.n_uniform;
-  hr.k = k;
-  hr.lens = kv.lens;
-  if (mage_status st = launch_topk(tp, hr, sel, false); st != MAGE_OK) return st;
   if (idx_ready) {
     if (hipError_t e = hipEventRecord(idx_ready, sel); e != hipSuccess)
       return hip_fail(e, "hipEventRecord(idx_ready)");
@@ -561,35 +557,11 @@ mage_status launch_budget_topk(const Dims& d, const KvArgs& kv, float* scores, i
   }
   const int32_t K = bp.k_per_head * d.Hkv;
   int32_t* gidx = at<int32_t>(ws, L.page_idx);   // [S][K]
-  TopkParams tp{};
-  tp.scores = scores;
-  tp.stride = row_len;
-  tp.idx = gidx;
-  tp.k = K;
-  tp.hist = at<uint32_t>(ws, L.hist);
-  tp.hist_parts = at<uint32_t>(ws, L.hist_parts);
-  tp.cand_bits = at<uint32_t>(ws, L.cand_bits);
-  tp.cand_pos = at<int32_t>(ws, L.cand_pos);
-  tp.nchunk = static_cast<int>(cdiv(row_len, kLocalChunk));
-  tp.cand_stride = static_cast<int64_t>(tp.nchunk) * kLocalChunk;
-  tp.cand_count = at<int32_t>(ws, L.cand_count);
-  tp.row_info = at<int32_t>(ws, L.row_info);
-  tp.rows = d.S;
-  tp.rows_per_seq = 1;
-  tp.n_uniform = static_cast<int32_t>(row_len);
-  std::memset(&tp.lens, 0, sizeof tp.lens);
-  tp.map = topk_map(tp, d.S);
-  HistReduceParams hr{};
-  hr.parts = tp.hist_parts;
-  hr.hist = tp.hist;
-  hr.rows = tp.rows;
-  hr.nparts = tp.nchunk;
-  hr.part_len = kLocalChunk;
-  hr.rows_per_seq = 1;
-  hr.n_uniform = tp.n_uniform;
-  hr.k = K;
-  hr.lens = tp.lens;
-  if (mage_status st = launch_topk(tp, hr, stream, true); st != MAGE_OK) return st;
+  SeqLens none;
+  std::memset(&none, 0, sizeof none);
+  const TopkParams tp = topk_params(ws, L, scores, row_len, gidx, K, d.S, 1, static_cast<int32_t>(row_len),
+                                    row_len, none, d.S);
+  if (mage_status st = launch_topk(tp, stream, true); st != MAGE_OK) return st;
   BudgetSplitParams bs{};
   bs.gidx = gidx;
   bs.idx = idx;
@@ -630,35 +602,9 @@ mage_status launch_page_topk(const Dims& d, const KvArgs& kv, const float* score
       st != MAGE_OK)
     return st;
   int32_t* page_idx = pp.page_idx ? pp.page_idx : at<int32_t>(ws, L.page_idx);
-  TopkParams tp{};
-  tp.scores = ps.page_scores;
-  tp.stride = pages_max;
-  tp.idx = page_idx;
-  tp.k = pp.k_pages;
-  tp.hist = at<uint32_t>(ws, L.hist);
-  tp.hist_parts = at<uint32_t>(ws, L.hist_parts);
-  tp.cand_bits = at<uint32_t>(ws, L.cand_bits);
-  tp.cand_pos = at<int32_t>(ws, L.cand_pos);
-  tp.cand_stride = L.cand_stride;
-  tp.cand_count = at<int32_t>(ws, L.cand_count);
-  tp.row_info = at<int32_t>(ws, L.row_info);
-  tp.rows = d.units;
-  tp.rows_per_seq = d.Hkv;
-  tp.n_uniform = ragged ? -1 : static_cast<int32_t>(pages_max);
-  tp.nchunk = static_cast<int>(cdiv(pages_max, kLocalChunk));
-  tp.lens = plens;
-  tp.map = topk_map(tp, d.S);
-  HistReduceParams hr{};
-  hr.parts = tp.hist_parts;
-  hr.hist = tp.hist;
-  hr.rows = tp.rows;
-  hr.nparts = tp.nchunk;
-  hr.part_len = kLocalChunk;
-  hr.rows_per_seq = tp.rows_per_seq;
-  hr.n_uniform = tp.n_uniform;
-  hr.k = tp.k;
-  hr.lens = plens;
-  if (mage_status st = launch_topk(tp, hr, stream, true); st != MAGE_OK) return st;
+  const TopkParams tp = topk_params(ws, L, ps.page_scores, pages_max, page_idx, pp.k_pages, d.units, d.Hkv,
+                                    ragged ? -1 : static_cast<int32_t>(pages_max), pages_max, plens, d.S);
+  if (mage_status st = launch_topk(tp, stream, true); st != MAGE_OK) return st;
   PageExpandParams pe{};
   pe.page_idx = page_idx;
   pe.idx = idx;
@@ -730,7 +676,6 @@ mage_status launch_sparse(const Dims& d, const uint16_t* q, const KvArgs& kv, co
   mp.part_ml = ap.part_ml;
   mp.o = o;
   mp.lse = lse;
-  mp.rowstat = nullptr;
   mp.S = d.S; mp.B = d.B; mp.Hq = d.Hq; mp.Hkv = d.Hkv; mp.G = d.G; mp.R = d.R; mp.nrb = d.nrb;
   mp.chunk = chunk;
   mp.nchunk = nch;
@@ -791,6 +736,25 @@ __global__ void fill_zero_kernel(uint32_t* p, size_t words) {
     p[i] = 0u;
 }
 
+// Number of non-zero words among the first `words` of p, written to *out (one
+// work-group: no cross-group accumulation, no atomics).
+constexpr int kCheckThreads = 1024;
+__global__ __launch_bounds__(kCheckThreads) void count_nonzero_kernel(const uint32_t* p, int32_t words,
+                                                                       int32_t* out) {
+  __shared__ int32_t s_part[kCheckThreads / kWave];
+  int32_t n = 0;
+  for (int32_t i = threadIdx.x; i < words; i += kCheckThreads) n += p[i] != 0u;
+  n = static_cast<int32_t>(sum_over_rows(static_cast<uint32_t>(n)));   // 4 rows of 16 lanes
+  for (int off = 1; off < 16; off <<= 1) n += __shfl_xor(n, off, 16);
+  if ((threadIdx.x & 63) == 0) s_part[threadIdx.x >> 6] = n;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int32_t t = 0;
+    for (int w = 0; w < kCheckThreads / kWave; ++w) t += s_part[w];
+    *out = t;
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -810,6 +774,19 @@ mage_status mage_workspace_init(void* workspace, size_t workspace_bytes, hipStre
   hipLaunchKernelGGL(fill_zero_kernel, dim3(blocks), dim3(256), 0, stream,
                      static_cast<uint32_t*>(workspace), words);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return hip_fail(e, "workspace init launch");
+  return MAGE_OK;
+}
+
+mage_status mage_workspace_check(const void* workspace, size_t workspace_bytes, int32_t* nonzero,
+                                 hipStream_t stream) {
+  if (!workspace || !nonzero || !aligned(workspace, 4) || !aligned(nonzero, 4))
+    return fail(MAGE_ERR_INVALID_ARG, "workspace and nonzero must be non-null and 4-byte aligned");
+  const size_t counter_bytes = kArrivalUnits * (kMaxRows / 32) * 4;
+  if (workspace_bytes < counter_bytes)
+    return fail(MAGE_ERR_WORKSPACE_TOO_SMALL, "workspace smaller than its arrival-counter region");
+  hipLaunchKernelGGL(count_nonzero_kernel, dim3(1), dim3(kCheckThreads), 0, stream,
+                     static_cast<const uint32_t*>(workspace), static_cast<int32_t>(counter_bytes / 4), nonzero);
+  if (hipError_t e = hipGetLastError(); e != hipSuccess) return hip_fail(e, "workspace check launch");
   return MAGE_OK;
 }
 
@@ -1225,35 +1202,8 @@ mage_status mage_topk(int32_t rows, const float* scores, int64_t row_stride, con
   d.scale = 1.f;
   const Layout L = make_layout(d, n, k);
   if (mage_status st = check_ws(workspace, workspace_bytes, L); st != MAGE_OK) return st;
-  TopkParams tp{};
-  tp.scores = scores;
-  tp.stride = row_stride;
-  tp.idx = idx;
-  tp.k = k;
-  tp.hist = at<uint32_t>(workspace, L.hist);
-  tp.hist_parts = at<uint32_t>(workspace, L.hist_parts);
-  tp.cand_bits = at<uint32_t>(workspace, L.cand_bits);
-  tp.cand_pos = at<int32_t>(workspace, L.cand_pos);
-  tp.cand_stride = L.cand_stride;
-  tp.cand_count = at<int32_t>(workspace, L.cand_count);
-  tp.row_info = at<int32_t>(workspace, L.row_info);
-  tp.rows = rows;
-  tp.rows_per_seq = 1;
-  tp.n_uniform = lens ? -1 : n;
-  tp.nchunk = static_cast<int>(cdiv(n, kLocalChunk));
-  tp.lens = sl;
-  tp.map = topk_map(tp, rows);
-  HistReduceParams hr{};
-  hr.parts = tp.hist_parts;
-  hr.hist = tp.hist;
-  hr.rows = rows;
-  hr.nparts = tp.nchunk;
-  hr.part_len = kLocalChunk;
-  hr.rows_per_seq = 1;
-  hr.n_uniform = tp.n_uniform;
-  hr.k = k;
-  hr.lens = sl;
-  return launch_topk(tp, hr, stream, true);
+  const TopkParams tp = topk_params(workspace, L, scores, row_stride, idx, k, rows, 1, lens ? -1 : n, n, sl, rows);
+  return launch_topk(tp, stream, true);
 }
 
 const char* mage_status_string(mage_status status) {

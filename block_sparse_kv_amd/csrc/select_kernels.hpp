@@ -97,64 +97,30 @@ __device__ __forceinline__ void wave_hist_add(uint32_t* hist, uint32_t bin, bool
   if (active) atomicAdd(&hist[bin], 1u);
 }
 
-// Stores a work-group's LDS histogram as its part of the row histogram
-// (plain stores: hist_reduce_kernel adds the parts up after a kernel
-// boundary; device-scope atomics from every work-group of a row into the same
-// bins serialize at the memory side and cost far more).
+// Adds a work-group's LDS histogram into the row's histogram in global memory
+// (zero before the first work-group of the row adds to it): one device-scope
+// atomic add per non-zero bin. A chunk's scores occupy a few dozen of the
+// 1024 bins, so the adds of all the row's work-groups meet on few addresses
+// and little at a time; adding every bin instead serializes 1024 adds per
+// work-group at the memory side.
 template <int kNT>
-__device__ __forceinline__ void store_hist_part(const uint32_t* s_hist, uint32_t* part) {
-  for (int b = threadIdx.x; b < kHistBins; b += kNT) part[b] = s_hist[b];
-}
-
-// Row histogram = the sum of its parts: part j of row u covers positions
-// [j * part_len, (j + 1) * part_len), and only parts holding a position of
-// the row were written. One work-group per (row, 256 bins).
-struct HistReduceParams {
-  const uint32_t* parts;    // [rows][nparts][kHistBins]
-  uint32_t* hist;           // [rows][kHistBins]
-  int32_t rows, nparts, part_len;
-  int32_t rows_per_seq;     // row u belongs to sequence u / rows_per_seq
-  int32_t n_uniform;        // >= 0: every row has this many entries; else lens
-  int32_t k;                // rows with min(k, n) == n need no histogram
-  SeqLens lens;
-};
-
-// Work-group = 256 bins x 4 slices of the parts (1024 threads): slice t sums
-// parts t*8 .. t*8+7, then every 32nd batch after it, eight loads in flight
-// per step; the four slice sums meet in LDS. Rows with many parts (long
-// prefixes, or one row per sequence over all its heads) then wait for a
-// quarter of the dependent steps.
-constexpr int kHistReduceThreads = 1024;
-__global__ __launch_bounds__(kHistReduceThreads) void hist_reduce_kernel(HistReduceParams p) {
-  constexpr int kBlocks = kHistBins / 256;
-  __shared__ uint32_t s_sum[3][256];
-  const int u = blockIdx.x / kBlocks, bl = threadIdx.x & 255, slice = threadIdx.x >> 8;
-  const int b = (blockIdx.x % kBlocks) * 256 + bl;
-  if (u >= p.rows) return;
-  const int n = p.n_uniform >= 0 ? p.n_uniform : p.lens.n[u / p.rows_per_seq];
-  if (min(p.k, n) == n) return;
-  const int np = (n + p.part_len - 1) / p.part_len;
-  const uint32_t* src = p.parts + static_cast<int64_t>(u) * p.nparts * kHistBins + b;
-  uint32_t sum = 0;
-  for (int j = slice * 8; j < np; j += 32) {
-    uint32_t x[8];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) x[q] = j + q < np ? src[static_cast<int64_t>(j + q) * kHistBins] : 0u;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) sum += x[q];
+__device__ __forceinline__ void publish_hist(const uint32_t* s_hist, uint32_t* row_hist) {
+  for (int b = threadIdx.x; b < kHistBins; b += kNT) {
+    const uint32_t v = s_hist[b];
+    if (v != 0u) __hip_atomic_fetch_add(row_hist + b, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  if (slice > 0) s_sum[slice - 1][bl] = sum;
-  __syncthreads();
-  if (slice == 0) p.hist[static_cast<int64_t>(u) * kHistBins + b] = sum + s_sum[0][bl] + s_sum[1][bl] + s_sum[2][bl];
 }
 
 struct ScoreParams {
   const uint16_t* q;
   KvSource kv;
-  const float* rowstat;     // per (unit, row) max + log2(sum)
+  const float* part_ml;     // the exact pass's split (max, sum) per (unit, chunk, row), log2 units
+  int32_t exact_chunk;      // its keys per chunk and chunks per unit (slot = unit * exact_nchunk + chunk)
+  int32_t exact_nchunk;
   float* scores;            // [S][Hkv][stride]
   int64_t stride;
-  uint32_t* hist_parts;     // [S * Hkv][nchunk][kHistBins]: each chunk's score histogram
+  uint32_t* hist;           // [S * Hkv][kHistBins], zero on entry: each row's score histogram (or null)
+  int32_t k;                // rows with min(k, N_s) == N_s take no histogram
   int32_t S, B, Hq, Hkv, G, R;
   int32_t chunk, nchunk;
   int32_t reverse;          // sweep tiles last-to-first
@@ -164,11 +130,14 @@ struct ScoreParams {
 };
 
 // Positions per score work-group; sized so that two work-groups fit in one
-// CU's LDS. Each work-group stores its chunk's part of the row histogram.
+// CU's LDS. Each work-group adds its chunk's histogram into the row's.
 constexpr int kScoreChunk = 2048;      // positions per work-group (largest)
 constexpr int kScoreChunkMin = 512;    // smallest, for short prefixes
+constexpr int kStatBatch = 16;         // chunk statistics merged per batch (as the step-1 merge)
 
-template <int D, int kStages>
+// kNt: the K tiles are loaded non-temporally (this sweep is their last use in
+// the step).
+template <int D, int kStages, bool kNt>
 __global__ __launch_bounds__(kThreads) void score_kernel(ScoreParams p) {
   using G = TileGeom<D>;
   constexpr int kNks = D / 16;
@@ -176,6 +145,7 @@ __global__ __launch_bounds__(kThreads) void score_kernel(ScoreParams p) {
   __shared__ int32_t s_pages[kScoreChunk + 1];
   __shared__ float s_col[2][4][kTileKeys];
   __shared__ uint32_t s_hist[kHistBins];
+  __shared__ float s_crow[kMaxRows];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -211,21 +181,6 @@ __global__ __launch_bounds__(kThreads) void score_kernel(ScoreParams p) {
     } else {
 #pragma unroll
       for (int ks = 0; ks < kNks; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
-    }
-  }
-  // accumulator register i of this lane is row 32w + 8(i/4) + 4hh + (i%4);
-  // crow = -(max + log2 sum) of that row
-  float crow[16];
-  {
-    // every row slot of the unit exists in rowstat: load all 16 unconditionally
-    // (one round trip), then drop the rows past R
-    const float* rs = p.rowstat + static_cast<int64_t>(u) * kMaxRows;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) crow[i] = rs[32 * w + 8 * (i >> 2) + 4 * hh + (i & 3)];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int r = 32 * w + 8 * (i >> 2) + 4 * hh + (i & 3);
-      crow[i] = (computes && r < p.R) ? -crow[i] : -__builtin_inff();
     }
   }
   uint32_t kofs[kNks];
@@ -275,7 +230,7 @@ __global__ __launch_bounds__(kThreads) void score_kernel(ScoreParams p) {
 #pragma unroll
       for (int j = 0; j < G::kInstr; ++j) {
         const int slot = w * G::kInstr + j;
-        dma16(kbytes + row_bytes(base + slot * kKRowsPerInstr), koff[j], st + slot * 1024);
+        dma16<kNt>(kbytes + row_bytes(base + slot * kKRowsPerInstr), koff[j], st + slot * 1024);
       }
     } else {
 #pragma unroll
@@ -283,7 +238,7 @@ __global__ __launch_bounds__(kThreads) void score_kernel(ScoreParams p) {
         const int slot = w * G::kInstr + j;
         const int unit = slot * kWave + lane;
         const int r = unit / G::kUnits, uk = (unit % G::kUnits) ^ (r & (G::kUnits - 1));
-        dma16_sync(p.kv.k + row_off(base + r) + uk * 8, st + slot * 1024);
+        dma16_sync<kNt>(p.kv.k + row_off(base + r) + uk * 8, st + slot * 1024);
       }
     }
   };
@@ -303,6 +258,25 @@ __global__ __launch_bounds__(kThreads) void score_kernel(ScoreParams p) {
 #pragma unroll
   for (int t = 0; t < kStages - 1; ++t)
     if (t < ntiles) issue(t);
+  // while the first tiles load: each row's final max + log2(sum) over the
+  // whole prefix, the merge of the exact pass's chunk statistics (the same
+  // arithmetic as the step-1 merge), one row per thread. (The wait for these
+  // loads also covers the tile loads issued before them.)
+  if (tid < kMaxRows) {
+    float M, L;
+    const int nchx = (ns + p.exact_chunk - 1) / p.exact_chunk;
+    merge_row_stats<kStatBatch>(p.part_ml, static_cast<int64_t>(u) * p.exact_nchunk, nchx, tid, M, L);
+    s_crow[tid] = M + __log2f(L);
+  }
+  __syncthreads();
+  // accumulator register i of this lane is row 32w + 8(i/4) + 4hh + (i%4);
+  // crow = -(max + log2 sum) of that row (rows past R: -inf, probability 0)
+  float crow[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int r = 32 * w + 8 * (i >> 2) + 4 * hh + (i & 3);
+    crow[i] = (computes && r < p.R) ? -s_crow[r] : -__builtin_inff();
+  }
   for (int t = 0; t < ntiles; ++t) {
     wait_tiles<G::kInstr, kStages - 1>(min(kStages - 2, ntiles - 1 - t));
     wg_barrier();
@@ -338,25 +312,27 @@ __global__ __launch_bounds__(kThreads) void score_kernel(ScoreParams p) {
   }
   __syncthreads();
   if (tid < kTileKeys) reduce_store(ntiles - 1);
+  if (p.hist == nullptr || min(p.k, ns) == ns) return;   // every position is selected: no histogram
   __syncthreads();
-  store_hist_part<kThreads>(s_hist, p.hist_parts + (static_cast<int64_t>(u) * p.nchunk + c) * kHistBins);
+  publish_hist<kThreads>(s_hist, p.hist + static_cast<int64_t>(u) * kHistBins);
 }
 
 // ---------------------------------------------------------------------------
 // top-k
 
-// Final selection work-group: 1024 threads; its register path holds up to
-// kFinalMax entries (8 per thread), or kFinalMaxWide (12 per thread, for
-// large k: 96 KiB of LDS staging) in the wide variant.
+// Top-k work-group: 1024 threads. In its candidate phase it takes
+// kLocalChunk positions of one row (kLocalPer per thread); the last of a
+// row's work-groups then selects among the row's candidates on its register
+// path, which holds up to kFinalMax entries (8 per thread), or kFinalMaxWide
+// (12 per thread, for large k) in the wide variant.
 constexpr int kTopkThreads = 1024;
 constexpr int kTopkWaves = kTopkThreads / kWave;
 constexpr int kFinalMax = 8192;
 constexpr int kFinalMaxWide = 12288;
-// Candidate pass: one 256-thread work-group per 4096-position chunk.
-constexpr int kLocalThreads = 256;
-constexpr int kLocalWaves = kLocalThreads / kWave;
 constexpr int kLocalChunk = 4096;
-constexpr int kLocalPer = kLocalChunk / kLocalThreads;
+constexpr int kLocalPer = kLocalChunk / kTopkThreads;
+// histogram pass of the standalone top-k: one 256-thread work-group per chunk
+constexpr int kHistThreads = 256;
 // chunks per row the final pass can index (rows up to 2^25 positions)
 constexpr int kMaxLocalChunks = 8192;
 
@@ -365,19 +341,19 @@ struct TopkParams {
   int64_t stride;
   int32_t* idx;             // [rows][k]
   int32_t k;
-  uint32_t* hist;           // [rows][kHistBins]: the row's score histogram
-  uint32_t* hist_parts;     // standalone path: [rows][nchunk][kHistBins]
+  uint32_t* hist;           // [rows][kHistBins]: the row's score histogram (complete before the
+                            //   top-k launch: built by the score sweep or topk_hist_kernel)
   uint32_t* cand_bits;      // per row: chunk c's candidates at c * kLocalChunk
   int32_t* cand_pos;
   int64_t cand_stride;      // nchunk * kLocalChunk
   int32_t* cand_count;      // [rows][nchunk]
-  int32_t* row_info;        // [rows][2]: b* and the number of scores in bins above it
+  uint32_t* arrivals;       // [rows]: work-groups of the row done with their candidates; zero on entry
   int32_t rows;
   int32_t rows_per_seq;     // row u belongs to sequence u / rows_per_seq
   int32_t n_uniform;        // >= 0: every row has this many entries; else lens
   int32_t nchunk;
   SeqLens lens;
-  ChunkMap map;             // candidate pass and histogram parts: work-group -> (row, chunk)
+  ChunkMap map;             // work-group -> (row, chunk of kLocalChunk positions)
 };
 
 struct TopkShared {
@@ -785,10 +761,20 @@ __device__ __forceinline__ int topk_row_len(const TopkParams& p, int u) {
   return p.n_uniform >= 0 ? p.n_uniform : p.lens.n[u / p.rows_per_seq];
 }
 
-// Histogram parts of user-supplied rows (the standalone top-k entry point;
-// the selection path builds them in the score sweep). One work-group per
-// (row, chunk): part c of the row in p.hist_parts.
-__global__ __launch_bounds__(kLocalThreads) void topk_hist_kernel(TopkParams p) {
+// Zeroes the histograms and arrival counters of the standalone top-k's rows
+// (the step-1 path has the exact pass do this). One work-group per row.
+__global__ __launch_bounds__(kHistThreads) void topk_prep_kernel(TopkParams p) {
+  const int u = blockIdx.x;
+  if (u >= p.rows) return;
+  for (int b = threadIdx.x; b < kHistBins; b += kHistThreads) p.hist[static_cast<int64_t>(u) * kHistBins + b] = 0u;
+  if (threadIdx.x == 0) p.arrivals[u] = 0u;
+}
+
+// Histograms of user-supplied rows (the standalone top-k entry point; the
+// selection path builds them in the score sweep). One work-group per (row,
+// chunk) adds its chunk's histogram into the row's.
+__global__ __launch_bounds__(kHistThreads) void topk_hist_kernel(TopkParams p) {
+  constexpr int kPer = kLocalChunk / kHistThreads;
   __shared__ uint32_t s_hist[kHistBins];
   const int tid = threadIdx.x;
   int u, c;
@@ -798,105 +784,32 @@ __global__ __launch_bounds__(kLocalThreads) void topk_hist_kernel(TopkParams p) 
   const int start = c * kLocalChunk;
   if (min(p.k, n) == n || start >= n) return;   // such rows need no histogram
   const int len = min(kLocalChunk, n - start);
-  for (int b = tid; b < kHistBins; b += kLocalThreads) s_hist[b] = 0u;
+  for (int b = tid; b < kHistBins; b += kHistThreads) s_hist[b] = 0u;
   __syncthreads();
   const float* src = p.scores + static_cast<int64_t>(u) * p.stride + start;
-  uint32_t v[kLocalPer];
+  uint32_t v[kPer];
 #pragma unroll
-  for (int j = 0; j < kLocalPer; ++j) v[j] = __float_as_uint(src[min(tid + j * kLocalThreads, len - 1)]);
+  for (int j = 0; j < kPer; ++j) v[j] = __float_as_uint(src[min(tid + j * kHistThreads, len - 1)]);
 #pragma unroll
-  for (int j = 0; j < kLocalPer; ++j) wave_hist_add(s_hist, hist_bin(v[j]), tid + j * kLocalThreads < len);
+  for (int j = 0; j < kPer; ++j) wave_hist_add(s_hist, hist_bin(v[j]), tid + j * kHistThreads < len);
   __syncthreads();
-  store_hist_part<kLocalThreads>(s_hist, p.hist_parts + (static_cast<int64_t>(u) * p.nchunk + c) * kHistBins);
+  publish_hist<kHistThreads>(s_hist, p.hist + static_cast<int64_t>(u) * kHistBins);
 }
 
-// Candidate pass: one work-group per (row, chunk of kLocalChunk positions).
-// From the row histogram it finds the bin b* that holds the row's k-th
-// largest score; the chunk's entries in bins >= b* (every entry of the top-k
-// is one of them) go, in position order, to the chunk's candidate slice.
-// Rows whose every position is selected are finished here.
-__global__ __launch_bounds__(kLocalThreads) void topk_local_kernel(TopkParams p) {
-  __shared__ uint32_t s_data[kLocalChunk];
-  __shared__ __attribute__((aligned(16))) int32_t s_wsum[2][kLocalWaves];
-  __shared__ int32_t s_bin;
-  const int tid = threadIdx.x;
-  int u, c;
-  map_chunk(p.map, p.lens, p.rows / p.rows_per_seq, p.rows_per_seq, kLocalChunk, p.nchunk, blockIdx.x, u, c);
-  if (u >= p.rows) return;
-  const int n = topk_row_len(p, u);
-  const int kk = min(p.k, n);
-  const int start = c * kLocalChunk;
-  if (start >= n) return;
-  const int len = min(kLocalChunk, n - start);
-  int32_t* out = p.idx + static_cast<int64_t>(u) * p.k;
-  MAGE_TRACE_POINT(0);
-
-  if (kk == n) {  // every position is selected
-    for (int i = tid; i < len; i += kLocalThreads) out[start + i] = start + i;
-    if (c == 0)
-      for (int i = n + tid; i < p.k; i += kLocalThreads) out[i] = -1;
-    return;
-  }
-  {
-    // every thread issues all of its loads before the first use
-    const float* src = p.scores + static_cast<int64_t>(u) * p.stride + start;
-    uint32_t v[kLocalPer];
-#pragma unroll
-    for (int j = 0; j < kLocalPer; ++j) v[j] = __float_as_uint(src[min(tid + j * kLocalThreads, len - 1)]);
-#pragma unroll
-    for (int j = 0; j < kLocalPer; ++j) s_data[tid + j * kLocalThreads] = v[j];
-  }
-  // b*: thread t holds bins 1023-4t .. 1020-4t (the largest in thread 0); the
-  // scan of their counts is the number of scores at or above each bin
-  if (tid == 0) {
-    s_bin = 0;   // (a histogram that misses kk scores keeps everything)
-    if (c == 0) p.row_info[2 * u] = -1;
-  }
-  {
-    typedef uint32_t u4 __attribute__((ext_vector_type(4)));
-    const u4 h = reinterpret_cast<const u4*>(p.hist + static_cast<int64_t>(u) * kHistBins)[kHistBins / 4 - 1 - tid];
-    const int s4 = static_cast<int>(h[0] + h[1] + h[2] + h[3]);
-    int total;
-    const int incl = block_inclusive_scan<kLocalWaves>(s4, s_wsum[0], total);
-    int above = incl - s4;
-    if (above < kk && kk <= incl) {
-#pragma unroll
-      for (int e = 3; e >= 0; --e) {
-        const int cnt = static_cast<int>(h[e]);
-        if (above < kk && kk <= above + cnt) {
-          s_bin = kHistBins - 4 - 4 * tid + e;
-          if (c == 0) {
-            p.row_info[2 * u] = kHistBins - 4 - 4 * tid + e;
-            p.row_info[2 * u + 1] = above;
-          }
-        }
-        above += cnt;
-      }
-    }
-  }
-  __syncthreads();   // s_data and s_bin
-  MAGE_TRACE_POINT(1);
-  const uint32_t lo = static_cast<uint32_t>(s_bin) << kHistShift;   // smallest pattern of bin b*
-  uint32_t v[kLocalPer];
-  load_run<kLocalPer>(s_data, v);
-  const int nv = run_valid<kLocalPer>(len);
-  int nkeep = 0;
-#pragma unroll
-  for (int j = 0; j < kLocalPer; ++j) nkeep += (j < nv && v[j] >= lo);
-  int total;
-  int o = block_inclusive_scan<kLocalWaves>(nkeep, s_wsum[1], total) - nkeep;
-  uint32_t* cb = p.cand_bits + static_cast<int64_t>(u) * p.cand_stride + start;
-  int32_t* cp = p.cand_pos + static_cast<int64_t>(u) * p.cand_stride + start;
-  const int run0 = start + tid * kLocalPer;
-#pragma unroll
-  for (int j = 0; j < kLocalPer; ++j)
-    if (j < nv && v[j] >= lo) {
-      cb[o] = v[j];
-      cp[o] = run0 + j;
-      ++o;
-    }
-  if (tid == 0) p.cand_count[static_cast<int64_t>(u) * p.nchunk + c] = total;
-  MAGE_TRACE_POINT(2);
+// Device-scope (cache bit sc1) accesses for what one work-group of a launch
+// hands to another: complete in every XCD's view once the writer's vmcnt has
+// drained, read from the coherent level rather than from a stale L2 line.
+__device__ __forceinline__ void st_dev(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev(int32_t* p, int32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld_dev(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int32_t ld_dev(const int32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Selection inside bin b* (< kHistBins - 1) by one wave: the rem-th largest
@@ -952,36 +865,111 @@ __device__ void wave_select_in_bin(const uint32_t* cand, int m, int rem, uint32_
   eq = cnt;
 }
 
-// Final pass: one work-group per row. The chunks' candidate slices, taken in
-// chunk order, are in position order; the kk-th largest among them is the
-// row's kk-th largest (all larger scores are candidates), and the ordered
-// compaction keeps ties at the lowest positions, so the output is ascending.
+// Top-k of every row, one launch. Work-group (row u, chunk c of kLocalChunk
+// positions):
+//   1. From the row's histogram, the bin b* that holds the row's k-th largest
+//      score: every score in a higher bin is in the top k, none in a lower one.
+//   2. The chunk's scores in bins >= b*, in position order, go to the chunk's
+//      candidate slice (device-scope stores), and their number to cand_count.
+//   3. The work-group counts itself in on the row's arrival counter (after its
+//      stores have drained); the last of the row's work-groups selects among
+//      the row's candidates: the chunks' slices taken in chunk order are in
+//      position order, the kk-th largest among them is the row's kk-th largest
+//      (every larger score is a candidate), and the ordered compaction keeps
+//      ties at the lowest positions, so the output is ascending.
+// Rows whose every position is selected are written in step 1's place.
 template <int kMax>
-__global__ __launch_bounds__(kTopkThreads) void topk_final_kernel(TopkParams p) {
-  __shared__ uint32_t s_data[2 * kMax];   // bits, then positions
+__global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(TopkParams p) {
+  __shared__ uint32_t s_data[2 * kMax];   // bits, then positions (final pass)
   __shared__ int32_t s_off[kMaxLocalChunks + 1];
   __shared__ TopkShared sh;
+  __shared__ int32_t s_sel[3];           // b*, scores in bins above b*, last arriver
   const int tid = threadIdx.x;
-  const int u = blockIdx.x;
+  int u, c;
+  map_chunk(p.map, p.lens, p.rows / p.rows_per_seq, p.rows_per_seq, kLocalChunk, p.nchunk, blockIdx.x, u, c);
   if (u >= p.rows) return;
   const int n = topk_row_len(p, u);
   const int kk = min(p.k, n);
-  if (kk == n) return;  // finished by the candidate pass
-  MAGE_TRACE_POINT(4);
+  const int start = c * kLocalChunk;
+  if (start >= n) return;
+  const int len = min(kLocalChunk, n - start);
   int32_t* out = p.idx + static_cast<int64_t>(u) * p.k;
+  MAGE_TRACE_POINT(0);
+  if (kk == n) {  // every position is selected
+    for (int i = tid; i < len; i += kTopkThreads) out[start + i] = start + i;
+    if (c == 0)
+      for (int i = n + tid; i < p.k; i += kTopkThreads) out[i] = -1;
+    return;
+  }
+  // ---- 1. b* from the row histogram: thread t holds bin kHistBins-1-t (the largest in thread 0)
+  uint32_t v[kLocalPer];
+  {
+    // this thread's run [start + t*kLocalPer, +kLocalPer) of the chunk, loads issued first
+    const float* src = p.scores + static_cast<int64_t>(u) * p.stride + start;
+#pragma unroll
+    for (int j = 0; j < kLocalPer; ++j) v[j] = __float_as_uint(src[min(tid * kLocalPer + j, len - 1)]);
+  }
+  if (tid == 0) {
+    s_sel[0] = 0;   // (a histogram that misses kk scores keeps everything)
+    s_sel[1] = 0;
+  }
+  {
+    const int h = static_cast<int>(p.hist[static_cast<int64_t>(u) * kHistBins + (kHistBins - 1 - tid)]);
+    int total;
+    const int incl = block_inclusive_scan(h, sh.wsum, total);
+    const int above = incl - h;
+    if (above < kk && kk <= incl) {
+      s_sel[0] = kHistBins - 1 - tid;
+      s_sel[1] = above;
+    }
+  }
+  __syncthreads();
+  MAGE_TRACE_POINT(1);
+  const int b_star = s_sel[0], above = s_sel[1];
+  // ---- 2. candidates: the chunk's scores in bins >= b*, in position order
+  const uint32_t lo = static_cast<uint32_t>(b_star) << kHistShift;   // smallest pattern of bin b*
+  const int nv = run_valid<kLocalPer>(len);
+  int nkeep = 0;
+#pragma unroll
+  for (int j = 0; j < kLocalPer; ++j) nkeep += (j < nv && v[j] >= lo);
+  int kept;
+  int o = block_inclusive_scan(nkeep, sh.wsum2, kept) - nkeep;
+  {
+    uint32_t* cb = p.cand_bits + static_cast<int64_t>(u) * p.cand_stride + start;
+    int32_t* cp = p.cand_pos + static_cast<int64_t>(u) * p.cand_stride + start;
+    const int run0 = start + tid * kLocalPer;
+#pragma unroll
+    for (int j = 0; j < kLocalPer; ++j)
+      if (j < nv && v[j] >= lo) {
+        st_dev(cb + o, v[j]);
+        st_dev(cp + o, run0 + j);
+        ++o;
+      }
+    if (tid == 0) st_dev(p.cand_count + static_cast<int64_t>(u) * p.nchunk + c, kept);
+  }
+  // ---- 3. count in; the row's last work-group selects
+  __builtin_amdgcn_s_waitcnt(0);   // this thread's candidate stores are complete at device scope
+  __syncthreads();
   const int nch = (n + kLocalChunk - 1) / kLocalChunk;
+  if (tid == 0) {
+    const uint32_t before = __hip_atomic_fetch_add(p.arrivals + u, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_sel[2] = before == static_cast<uint32_t>(nch - 1);
+  }
+  __syncthreads();
+  if (!s_sel[2]) return;
+  MAGE_TRACE_POINT(2);
   const int32_t* cnt = p.cand_count + static_cast<int64_t>(u) * p.nchunk;
   // s_off[c] = candidates before chunk c (thread t sums a contiguous run of chunks)
   {
     const int per = (nch + kTopkThreads - 1) / kTopkThreads;
     const int c0 = min(tid * per, nch), c1 = min(c0 + per, nch);
     int mine = 0;
-    for (int c = c0; c < c1; ++c) mine += cnt[c];
+    for (int cc = c0; cc < c1; ++cc) mine += ld_dev(cnt + cc);
     int total;
-    int o = block_inclusive_scan(mine, sh.wsum, total) - mine;
-    for (int c = c0; c < c1; ++c) {
-      s_off[c] = o;
-      o += cnt[c];
+    int oo = block_inclusive_scan(mine, sh.wsum, total) - mine;
+    for (int cc = c0; cc < c1; ++cc) {
+      s_off[cc] = oo;
+      oo += ld_dev(cnt + cc);
     }
     if (tid == 0) s_off[nch] = total;
   }
@@ -991,12 +979,12 @@ __global__ __launch_bounds__(kTopkThreads) void topk_final_kernel(TopkParams p) 
   const int32_t* pos = p.cand_pos + static_cast<int64_t>(u) * p.cand_stride;
   // candidate i -> its index in the chunk slices (binary search over s_off)
   auto slot_of = [&](int i) -> int64_t {
-    int lo = 0, hi = nch - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (s_off[mid] <= i) lo = mid; else hi = mid - 1;
+    int a = 0, b = nch - 1;
+    while (a < b) {
+      const int mid = (a + b + 1) >> 1;
+      if (s_off[mid] <= i) a = mid; else b = mid - 1;
     }
-    return static_cast<int64_t>(lo) * kLocalChunk + (i - s_off[lo]);
+    return static_cast<int64_t>(a) * kLocalChunk + (i - s_off[a]);
   };
   uint32_t T;
   int need;
@@ -1009,8 +997,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_final_kernel(TopkParams p) 
       for (int j = 0; j < kPer; ++j) {
         const int i = min(tid + j * kTopkThreads, total - 1);   // clamped; entries past total are never used
         const int64_t sl = slot_of(i);
-        vb[j] = bits[sl];
-        vp[j] = pos[sl];
+        vb[j] = ld_dev(bits + sl);
+        vp[j] = ld_dev(pos + sl);
       }
 #pragma unroll
       for (int j = 0; j < kPer; ++j) {
@@ -1019,26 +1007,24 @@ __global__ __launch_bounds__(kTopkThreads) void topk_final_kernel(TopkParams p) 
       }
     }
     __syncthreads();
-    uint32_t v[kPer], vpos[kPer];
-    load_run<kPer>(s_data, v);
-    load_run<kPer>(s_data + kMax, vpos);
-    MAGE_TRACE_POINT(5);
+    uint32_t w[kPer], wpos[kPer];
+    load_run<kPer>(s_data, w);
+    load_run<kPer>(s_data + kMax, wpos);
+    MAGE_TRACE_POINT(3);
     int eq_total;
-    const int b_star = p.row_info[2 * u], above = p.row_info[2 * u + 1];
     // the bin-b* candidates to LDS (s_data's first half is free again: every
     // thread holds its entries in registers); when they are as many as the
     // histogram says and few enough, one wave selects among them
-    const int nv = run_valid<kPer>(total);
+    const int nw = run_valid<kPer>(total);
     int nb = 0;
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) nb += (j < nv && static_cast<int>(hist_bin(v[j])) == b_star);
+    for (int j = 0; j < kPer; ++j) nb += (j < nw && static_cast<int>(hist_bin(w[j])) == b_star);
     int mt;
-    int o = block_inclusive_scan(nb, sh.wsum, mt) - nb;
-    if (b_star >= 0 && b_star < kHistBins - 1 && mt == total - above && mt <= kWaveSelMax && above < kk &&
-        kk <= total) {
+    int ob = block_inclusive_scan(nb, sh.wsum, mt) - nb;
+    if (b_star < kHistBins - 1 && mt == total - above && mt <= kWaveSelMax && above < kk && kk <= total) {
 #pragma unroll
       for (int j = 0; j < kPer; ++j)
-        if (j < nv && static_cast<int>(hist_bin(v[j])) == b_star) s_data[o++] = v[j];
+        if (j < nw && static_cast<int>(hist_bin(w[j])) == b_star) s_data[ob++] = w[j];
       __syncthreads();
       if (tid < kWave) {
         uint32_t t;
@@ -1056,18 +1042,18 @@ __global__ __launch_bounds__(kTopkThreads) void topk_final_kernel(TopkParams p) 
       eq_total = sh.res[2];
       __syncthreads();   // sh is reused by the compaction
     } else {
-      radix_select_sampled<kPer>(v, total, kk, sh, s_data, T, need, eq_total);
+      radix_select_sampled<kPer>(w, total, kk, sh, s_data, T, need, eq_total);
     }
-    MAGE_TRACE_POINT(6);
-    ordered_compact_regs<kPer>(v, total, T, need, [&](int j) { return static_cast<int32_t>(vpos[j]); }, nullptr,
+    MAGE_TRACE_POINT(4);
+    ordered_compact_regs<kPer>(w, total, T, need, [&](int j) { return static_cast<int32_t>(wpos[j]); }, nullptr,
                                out, sh, eq_total, kk);
   } else {
-    auto get = [&](int i) { return bits[slot_of(i)]; };
+    auto get = [&](int i) { return ld_dev(bits + slot_of(i)); };
     radix_select(get, total, kk, sh, T, need);
-    ordered_compact(get, total, T, need, [&](int i) { return pos[slot_of(i)]; }, nullptr, out, sh, kk);
+    ordered_compact(get, total, T, need, [&](int i) { return ld_dev(pos + slot_of(i)); }, nullptr, out, sh, kk);
   }
   for (int i = kk + tid; i < p.k; i += kTopkThreads) out[i] = -1;
-  MAGE_TRACE_POINT(7);
+  MAGE_TRACE_POINT(5);
 }
 
 }  // namespace mage

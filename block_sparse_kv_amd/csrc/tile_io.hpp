@@ -80,43 +80,82 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // wait state between an M0 write and its use. Completion is tracked with
 // vmcnt by the caller (wait_vmcnt / wait_tiles). Nothing is returned in a
 // register, so nothing is live while the loads are in flight.
+// kNt1: the second load is non-temporal (cache policy nt: its lines are
+// streamed, not kept, so they do not evict data that is read again soon).
+template <bool kNt1 = false>
 __device__ __forceinline__ void dma16x2(const void* b0, uint32_t o0, uint32_t l0, const void* b1, uint32_t o1,
                                         uint32_t l1) {
-  asm volatile(
-      "s_mov_b32 m0, %4\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %0, %1\n\t"
-      "s_mov_b32 m0, %5\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %2, %3"
-      :
-      : "v"(o0), "s"(b0), "v"(o1), "s"(b1), "s"(l0), "s"(l1)
-      : "memory", "m0");
+  if constexpr (kNt1) {
+    asm volatile(
+        "s_mov_b32 m0, %4\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, %1\n\t"
+        "s_mov_b32 m0, %5\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %2, %3 nt"
+        :
+        : "v"(o0), "s"(b0), "v"(o1), "s"(b1), "s"(l0), "s"(l1)
+        : "memory", "m0");
+  } else {
+    asm volatile(
+        "s_mov_b32 m0, %4\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, %1\n\t"
+        "s_mov_b32 m0, %5\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %2, %3"
+        :
+        : "v"(o0), "s"(b0), "v"(o1), "s"(b1), "s"(l0), "s"(l1)
+        : "memory", "m0");
+  }
 }
 
-// A single load of the dma16x2 form.
+// A single load of the dma16x2 form (kNt: non-temporal).
+template <bool kNt = false>
 __device__ __forceinline__ void dma16(const void* b, uint32_t o, uint32_t l) {
-  asm volatile(
-      "s_mov_b32 m0, %2\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %0, %1"
-      :
-      : "v"(o), "s"(b), "s"(l)
-      : "memory", "m0");
+  if constexpr (kNt) {
+    asm volatile(
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, %1 nt"
+        :
+        : "v"(o), "s"(b), "s"(l)
+        : "memory", "m0");
+  } else {
+    asm volatile(
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, %1"
+        :
+        : "v"(o), "s"(b), "s"(l)
+        : "memory", "m0");
+  }
 }
 
 // One direct LDS load per lane from a per-lane 64-bit address, waited for in
 // the same asm block (the path for tiles whose rows are not contiguous in
 // memory; the wait frees the address registers before the block ends).
+template <bool kNt = false>
 __device__ __forceinline__ void dma16_sync(const void* addr, uint32_t lds) {
-  asm volatile(
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %0, off\n\t"
-      "s_waitcnt vmcnt(0)"
-      :
-      : "v"(addr), "s"(lds)
-      : "memory", "m0");
+  if constexpr (kNt) {
+    asm volatile(
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, off nt\n\t"
+        "s_waitcnt vmcnt(0)"
+        :
+        : "v"(addr), "s"(lds)
+        : "memory", "m0");
+  } else {
+    asm volatile(
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, off\n\t"
+        "s_waitcnt vmcnt(0)"
+        :
+        : "v"(addr), "s"(lds)
+        : "memory", "m0");
+  }
 }
 
 // Issue the DMA loads of one tile. row_off(r) returns the element offset of

@@ -50,7 +50,8 @@
  * concurrently need distinct workspaces; a workspace may be reused once the
  * previous call's work (including its select stream) is ordered before the
  * new call. A workspace with non-zero counters makes a later step return
- * wrong values (it does not fault or hang).
+ * wrong values (it does not fault or hang); mage_workspace_check detects that
+ * state.
  *
  * Errors: every entry point returns a mage_status and never aborts.
  * MAGE_ERR_HIP carries the runtime's message in mage_last_error() (thread
@@ -113,6 +114,17 @@ size_t mage_workspace_bytes(const mage_dims* dims, int32_t max_seq_len, int32_t 
  * workspace 4-byte aligned, workspace_bytes a multiple of 4, else
  * MAGE_ERR_INVALID_ARG. */
 mage_status mage_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Count the non-zero arrival counters of a workspace (the first 256 KiB) on
+ * `stream`: *nonzero (device int32, 4-byte aligned) receives their number once
+ * the stream reaches this point. Every call leaves them at zero, so a
+ * non-zero count means the workspace was not zeroed with mage_workspace_init,
+ * was written over, or saw a call overlap another on a second stream; a later
+ * step on it would return wrong values. Null or misaligned pointers give
+ * MAGE_ERR_INVALID_ARG, a workspace smaller than the counter region
+ * MAGE_ERR_WORKSPACE_TOO_SMALL. */
+mage_status mage_workspace_check(const void* workspace, size_t workspace_bytes, int32_t* nonzero,
+                                 hipStream_t stream);
 
 /*
  * Step 1 of a block (MAGE page, summary and "Approach"): exact attention of

@@ -280,3 +280,4 @@ def test_adaptive_budget_argument_checks():
         assert lib.mage_sparse_attn_counts(*args) == mage.ERR_INVALID_ARG, (i, bad)
     okps = [ctypes.byref(d), FAKE, ctypes.byref(pk), FAKE, 64, FAKE, 512, FAKE, None, FAKE, 1 << 40, None]
     assert lib.mage_sparse_attn_counts_paged(*okps) == mage.ERR_INVALID_ARG
+
