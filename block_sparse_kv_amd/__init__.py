@@ -79,6 +79,7 @@ def lib():
                                        _vp]
         L.mage_sparse_attn_paged.argtypes = [P(Dims), _vp, P(PagedKv), _vp, _i32, _vp, _vp, _vp,
                                              _sz, _vp]
+        L.mage_sparse_attn_noalloc.argtypes = [P(Dims), _vp, _vp, _vp, _i32, _vp, _i32, _vp, _vp, _vp]
         L.mage_topk.argtypes = [_i32, _vp, ctypes.c_int64, P(_i32), _i32, _i32, _vp, _vp, _sz, _vp]
         L.mage_block_attn.argtypes = [P(Dims), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
         L.mage_sparse_block_attn.argtypes = [P(Dims), _vp, _vp, _vp, _i32, _vp, _i32, _vp, _vp, _vp, _vp,
@@ -103,7 +104,7 @@ def lib():
                                               _sz, _vp, _vp, _vp]
         for f in ("mage_workspace_init", "mage_workspace_check", "mage_select_exact", "mage_select_exact_paged",
                   "mage_exact_attn", "mage_exact_attn_paged",
-                  "mage_sparse_attn", "mage_sparse_attn_paged", "mage_topk", "mage_block_attn",
+                  "mage_sparse_attn", "mage_sparse_attn_paged", "mage_sparse_attn_noalloc", "mage_topk", "mage_block_attn",
                   "mage_sparse_block_attn", "mage_sparse_block_attn_paged", "mage_select_mean_query",
                   "mage_select_mean_query_paged", "mage_idx_overlap", "mage_mean_query",
                   "mage_select_pages", "mage_select_pages_paged", "mage_select_adaptive",
@@ -602,6 +603,24 @@ def sparse_attn(q, k_cache, v_cache, idx, scale: float, *, o=None, lse=None, wor
                                   _ptr(idx), int(k), _ptr(o), _ptr(lse), _ptr(ws), ws.numel(),
                                   _stream(stream)), "mage_sparse_attn")
     wso.done(stream)
+    return o, lse
+
+
+def sparse_attn_noalloc(q, k_cache, v_cache, idx, scale: float, *, o, lse=None, stream=None):
+    """sparse_attn with the library's fixed scratch instead of a workspace: the
+    call allocates nothing (o, and lse if given, are the caller's)."""
+    S, B, Hq, d = q.shape
+    _, Hkv, N, _ = k_cache.shape
+    k = idx.shape[-1]
+    if idx.dtype != torch.int32 or not idx.is_contiguous() or tuple(idx.shape[:2]) != (S, Hkv):
+        raise ValueError("idx must be contiguous int32 [S][Hkv][k]")
+    dims = make_dims(q, Hkv, scale)
+    o = _out(o, (S, B, Hq, d), torch.float32, q.device)
+    if lse is not None:
+        lse = _out(lse, (S, B, Hq), torch.float32, q.device)
+    _check(lib().mage_sparse_attn_noalloc(ctypes.byref(dims), _bf16_ptr(q, "q"), _bf16_ptr(k_cache, "k_cache"),
+                                          _bf16_ptr(v_cache, "v_cache"), N, _ptr(idx), int(k), _ptr(o), _ptr(lse),
+                                          _stream(stream)), "mage_sparse_attn_noalloc")
     return o, lse
 
 

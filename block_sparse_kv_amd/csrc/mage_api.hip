@@ -7,6 +7,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "../../include/mage.h"
@@ -755,6 +756,48 @@ __global__ __launch_bounds__(kCheckThreads) void count_nonzero_kernel(const uint
   }
 }
 
+// ---- the allocation-free later step -----------------------------------------
+// mage_sparse_attn_noalloc keeps its scratch (the arrival counters, then the
+// split partials, in the workspace layout of the later step) in this
+// file-scope array: one copy per GPU, held until the process ends. Host code
+// never passes the array's name to a kernel (on the host it is only a
+// stand-in); it passes the device address that hipGetSymbolAddress returns,
+// kept per device.
+constexpr size_t kScratchCounterBytes = kArrivalUnits * (kMaxRows / 32) * 4;   // 256 KiB
+constexpr size_t kScratchBytes = kScratchCounterBytes + (size_t(8) << 20);    // + 8 MiB of partials
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+struct ScratchSlot {
+  std::once_flag once;
+  void* ptr = nullptr;
+  hipError_t err = hipSuccess;
+};
+ScratchSlot g_scratch[kMaxDevices];
+
+// The scratch's device address on the current device. The first call on a
+// device looks it up (with that device current) and zeroes its counters with
+// a fill kernel on `stream` (the array starts zeroed when the code object is
+// loaded; every call leaves the counters at zero again).
+mage_status scratch_on_device(hipStream_t stream, void** out) {
+  int dev = 0;
+  if (hipError_t e = hipGetDevice(&dev); e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(MAGE_ERR_UNSUPPORTED, "device index beyond the scratch table");
+  ScratchSlot& slot = g_scratch[dev];
+  std::call_once(slot.once, [&] {
+    void* p = nullptr;
+    slot.err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (slot.err != hipSuccess) return;
+    hipLaunchKernelGGL(fill_zero_kernel, dim3(static_cast<unsigned>(cdiv(kScratchCounterBytes / 4, 256))),
+                       dim3(256), 0, stream, static_cast<uint32_t*>(p), kScratchCounterBytes / 4);
+    slot.err = hipGetLastError();
+    if (slot.err == hipSuccess) slot.ptr = p;
+  });
+  if (slot.err != hipSuccess) return hip_fail(slot.err, "scratch set-up (hipGetSymbolAddress / zero fill)");
+  *out = slot.ptr;
+  return MAGE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1054,6 +1097,30 @@ mage_status mage_sparse_attn(const mage_dims* dims, const uint16_t* q, const uin
   if (mage_status st = check_ws(workspace, workspace_bytes, L); st != MAGE_OK) return st;
   return d.D == 128 ? launch_sparse<128>(d, q, kv, idx, k, o, lse, workspace, L, stream)
                     : launch_sparse<64>(d, q, kv, idx, k, o, lse, workspace, L, stream);
+}
+
+mage_status mage_sparse_attn_noalloc(const mage_dims* dims, const uint16_t* q, const uint16_t* k_cache,
+                                     const uint16_t* v_cache, int32_t seq_len, const int32_t* idx, int32_t k,
+                                     float* o, float* lse, hipStream_t stream) {
+  CallScope scope;
+  Dims d;
+  if (mage_status st = sparse_common(dims, q, idx, k, o, lse, d); st != MAGE_OK) return st;
+  KvArgs kv;
+  if (mage_status st = contiguous_kv(d, k_cache, v_cache, seq_len, kv); st != MAGE_OK) return st;
+  // the later step's part of the workspace layout, sized for this call's plan
+  const int64_t nch = cdiv(k, sparse_chunk(d.units, d.nrb, k));
+  Layout L{};
+  L.slots = nch > 1 ? d.units * nch : 0;
+  L.arrivals = 0;
+  L.part_ml = round_up(kScratchCounterBytes, 256);
+  L.part_o = round_up(L.part_ml + L.slots * kMaxRows * 2 * 4, 256);
+  L.total = L.part_o + L.slots * 4 * (d.D / 32) * 4 * kWave * 16;
+  if (L.total > kScratchBytes)
+    return fail(MAGE_ERR_UNSUPPORTED, "this later step's split partials exceed the fixed scratch (8 MiB)");
+  void* ws = nullptr;
+  if (mage_status st = scratch_on_device(stream, &ws); st != MAGE_OK) return st;
+  return d.D == 128 ? launch_sparse<128>(d, q, kv, idx, k, o, lse, ws, L, stream)
+                    : launch_sparse<64>(d, q, kv, idx, k, o, lse, ws, L, stream);
 }
 
 mage_status mage_sparse_attn_paged(const mage_dims* dims, const uint16_t* q, const mage_paged_kv* kvp,

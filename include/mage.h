@@ -192,6 +192,26 @@ mage_status mage_sparse_attn_paged(const mage_dims* dims, const uint16_t* q,
                                    size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * mage_sparse_attn without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, hosts
+ * that forbid hipMalloc). Same arguments and results as mage_sparse_attn
+ * (the same kernels and launch plan, so the same bits) minus the workspace.
+ * Its scratch (arrival counters and split partials) is a fixed array in the
+ * library's code object: 256 KiB of counters plus 8 MiB of partials per GPU,
+ * held until the process ends. A call whose split partials need more (for
+ * example more than 126 (sequence, KV head) x chunk slots at d = 128) returns
+ * MAGE_ERR_UNSUPPORTED before any launch. The call allocates nothing; its
+ * first use on a device looks up the array's address and zeroes its counters
+ * on `stream`. Every call on one GPU shares that array and leaves the
+ * counters at zero: calls that overlap on one GPU (other streams, other
+ * threads) race and must be ordered by the caller.
+ */
+mage_status mage_sparse_attn_noalloc(const mage_dims* dims, const uint16_t* q,
+                                     const uint16_t* k_cache, const uint16_t* v_cache,
+                                     int32_t seq_len, const int32_t* idx, int32_t k, float* o,
+                                     float* lse, hipStream_t stream);
+
+/*
  * Block attention (the op a block-diffusion layer calls after the prefix
  * pass): every query of the current block attends to the selected prefix
  * rows and to all B rows of its own block, which the block's tokens share

@@ -281,3 +281,15 @@ def test_adaptive_budget_argument_checks():
     okps = [ctypes.byref(d), FAKE, ctypes.byref(pk), FAKE, 64, FAKE, 512, FAKE, None, FAKE, 1 << 40, None]
     assert lib.mage_sparse_attn_counts_paged(*okps) == mage.ERR_INVALID_ARG
 
+
+def test_noalloc_rejects_a_plan_beyond_its_scratch():
+    # 32 units of one 32-row block, k = 1024: 8 chunks per unit, 256 partial slots of
+    # 64 KiB (16 MiB) > the 8 MiB scratch; rejected before any HIP call
+    lib = mage.lib()
+    d = dims(num_seqs=4, block=8, num_q_heads=32, num_kv_heads=8)
+    st = lib.mage_sparse_attn_noalloc(ctypes.byref(d), FAKE, FAKE, FAKE, 4096, FAKE, 1024, FAKE, None, None)
+    assert st == mage.ERR_UNSUPPORTED
+    assert b"scratch" in lib.mage_last_error()
+    # and argument checks come first: null q
+    assert lib.mage_sparse_attn_noalloc(ctypes.byref(dims()), None, FAKE, FAKE, 4096, FAKE, 64, FAKE, None,
+                                        None) == mage.ERR_INVALID_ARG
