@@ -138,6 +138,8 @@ class KernelTimer:
         self.names = []
 
     def kernels_ms(self):
+        if len(self.names) > len(self.pairs):
+            raise RuntimeError(f"{len(self.names)} launches but {len(self.pairs)} timer pairs")
         return [a.elapsed_time(b) for a, b in self.pairs[:len(self.names)]]
 
     def busy_ms(self):
@@ -378,7 +380,7 @@ def page_diag(torch, mage, r, w, fl, P=16):
         sel_t.append(tm)
     for i in range(2 * (T - 1) if T > 1 else 2):
         fl()
-        tm = KernelTimer(torch, 2)
+        tm = KernelTimer(torch, mage.MAX_TIMED_LAUNCHES)
         r.sparse_idx(i, r.pidx, tm)
         sp_t.append(tm)
     torch.cuda.synchronize()
@@ -414,7 +416,7 @@ def budget_diag(torch, mage, r, w, fl):
         sel_t.append(tm)
     for i in range(2 * (T - 1) if T > 1 else 2):
         fl()
-        tm = KernelTimer(torch, 2)
+        tm = KernelTimer(torch, mage.MAX_TIMED_LAUNCHES)
         r.sparse_counts(i, tm)
         sp_t.append(tm)
     torch.cuda.synchronize()
@@ -469,7 +471,7 @@ def batch_diag(torch, mage, w, dev, fl, batches=(1, 2, 4, 8, 16), reps=10):
         timers = []
         for _ in range(reps):
             fl()
-            tm = KernelTimer(torch, 2)
+            tm = KernelTimer(torch, mage.MAX_TIMED_LAUNCHES)
             cur = torch.cuda.current_stream()
             mage.arm_kernel_timers(tm.pairs)
             tm.outer[0].record(cur)
@@ -665,7 +667,7 @@ def ragged_side(torch, mage, dev, fl, sparse_calls=40, select_calls=6):
     sp, sel = [], []
     for i in range(sparse_calls):
         fl()
-        tm = KernelTimer(torch, 2)
+        tm = KernelTimer(torch, mage.MAX_TIMED_LAUNCHES)
         r.sparse(i, tm)
         sp.append(tm)
     for _ in range(select_calls):
@@ -811,7 +813,7 @@ def run_bench(args):
     log("[bench] warm-up done")
 
     sel_timers = [KernelTimer(torch, mage.MAX_TIMED_LAUNCHES) for _ in range(args.steps)]
-    sp_timers = [KernelTimer(torch, 2) for _ in range(args.steps * (T - 1))]
+    sp_timers = [KernelTimer(torch, mage.MAX_TIMED_LAUNCHES) for _ in range(args.steps * (T - 1))]
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     for i in range(args.steps):
@@ -828,12 +830,12 @@ def run_bench(args):
     ex_timers = []
     for _ in range(5):
         fl()
-        tm = KernelTimer(torch, 2)
+        tm = KernelTimer(torch, mage.MAX_TIMED_LAUNCHES)
         r.exact_only(tm)
         ex_timers.append(tm)
     warm_timers = []
     for t in range(2 * (T - 1)):
-        tm = KernelTimer(torch, 2)
+        tm = KernelTimer(torch, mage.MAX_TIMED_LAUNCHES)
         r.sparse(t, tm)
         warm_timers.append(tm)
     r.select()
@@ -842,18 +844,18 @@ def run_bench(args):
     for t in range(0 if args.no_diag else 5):
         r.sparse(t)
         fl()
-        tm = KernelTimer(torch, 1)
+        tm = KernelTimer(torch, mage.MAX_TIMED_LAUNCHES)
         r.block(t, tm)
         blk_timers.append(tm)
     for t in range(0 if args.no_diag else 5):
         fl()
-        tm = KernelTimer(torch, 2)
+        tm = KernelTimer(torch, mage.MAX_TIMED_LAUNCHES)
         r.sparse_block(t, tm)
         fused_timers.append(tm)
     tk_timers = []
     for _ in range(5):
         fl()
-        tm = KernelTimer(torch, 2)
+        tm = KernelTimer(torch, mage.MAX_TIMED_LAUNCHES)
         r.topk_only(tm)
         tk_timers.append(tm)
     empty = []

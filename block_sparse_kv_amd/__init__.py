@@ -148,7 +148,7 @@ def workspace_bytes(dims: Dims, max_seq_len: int, k: int) -> int:
 
 def _capturing(stream) -> bool:
     """True while `stream` (a torch stream, None = the current one) is being captured into a graph."""
-    if stream is None:
+    if stream is None or stream == torch.cuda.current_stream(stream.device):
         return torch.cuda.is_current_stream_capturing()
     with torch.cuda.stream(stream):
         return torch.cuda.is_current_stream_capturing()
@@ -161,28 +161,37 @@ class Workspace:
     that needs it: the sparse calls keep arrival counters in it, which must
     start at zero and which every call leaves at zero.
 
-    Calls through one Workspace are ordered, whatever streams they run on:
-    after every call an event is recorded on each stream the call used (its
-    stream and, for step 1, its select stream), and the next call's stream
-    waits for those of other streams before the library touches the buffer.
-    A buffer that is replaced by a larger one goes back to the allocator only
-    after the work queued on every stream that used it (record_stream). Under
-    graph capture no event is recorded or waited for: the graph's own edges
-    order the captured calls.
+    Calls through one Workspace are ordered, whatever streams they run on: a
+    call notes the streams it used (its stream and, for step 1, its select
+    stream); when the next call runs on another stream, an event is recorded
+    on each of those streams (after everything queued there, the previous call
+    included) and the new call's stream waits for it. A buffer that is
+    replaced by a larger one goes back to the allocator only after the work
+    queued on every stream that used it (record_stream). Under graph capture
+    nothing is recorded or waited for: the graph's own edges order the
+    captured calls.
     """
 
     def __init__(self, device=None):
         self.device = torch.device(device or "cuda")
         self.buf = None
-        self.pending = []          # [(stream, event)] of the previous call
+        self.pending = []          # streams the previous call used
         self._users = set()        # streams (handles) the current buffer was used on
+        self._events = {}          # one reusable event per stream handle
+
+    def _order_after_pending(self, st):
+        for s in self.pending or []:
+            if s.cuda_stream != st.cuda_stream:
+                ev = self._events.get(s.cuda_stream)
+                if ev is None:
+                    ev = self._events[s.cuda_stream] = torch.cuda.Event()
+                ev.record(s)
+                st.wait_event(ev)
 
     def get(self, nbytes: int, stream=None) -> torch.Tensor:
         st = stream if stream is not None else torch.cuda.current_stream(self.device)
         if not _capturing(st):
-            for s, ev in self.pending or []:
-                if s.cuda_stream != st.cuda_stream:
-                    st.wait_event(ev)
+            self._order_after_pending(st)
             self.pending = []
         if self.buf is None or self.buf.numel() < nbytes:
             with torch.cuda.stream(st):
@@ -193,20 +202,17 @@ class Workspace:
         return self.buf
 
     def done(self, stream=None, *others):
-        """Record that the call just issued used this workspace on `stream`
+        """Note that the call just issued used this workspace on `stream`
         (None = the current stream) and on `others` (None entries ignored)."""
         first = stream if stream is not None else torch.cuda.current_stream(self.device)
         sts = [first] + [s for s in others if s is not None]
-        if any(_capturing(s) for s in sts):
+        if _capturing(first):
             return
-        out, seen = [], set()
+        out = []
         for s in sts:
-            if s.cuda_stream in seen:
+            if any(s.cuda_stream == x.cuda_stream for x in out):
                 continue
-            seen.add(s.cuda_stream)
-            ev = torch.cuda.Event()
-            ev.record(s)
-            out.append((s, ev))
+            out.append(s)
             if s.cuda_stream not in self._users:
                 self.buf.record_stream(s)
                 self._users.add(s.cuda_stream)
@@ -222,9 +228,7 @@ class Workspace:
         st = stream if stream is not None else torch.cuda.current_stream(self.device)
         if self.buf is None:
             return 0
-        for s, ev in self.pending or []:
-            if s.cuda_stream != st.cuda_stream:
-                st.wait_event(ev)
+        self._order_after_pending(st)
         out = torch.empty(1, dtype=torch.int32, device=self.device)
         _check(lib().mage_workspace_check(_ptr(self.buf), self.buf.numel(), _ptr(out), _stream(st)),
                "mage_workspace_check")

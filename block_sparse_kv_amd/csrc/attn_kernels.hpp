@@ -76,12 +76,8 @@ __device__ __forceinline__ int64_t part_o_index(int64_t slot, int w, int db, int
   return ((((slot * 4 + w) * (D / 32) + db) * 4 + i4) * kWave + lane);
 }
 
-// Partials handed from work-group to work-group inside one launch use
-// device-scope accesses (cache-policy bit sc1): a store with it is complete at
-// device scope, in every XCD's view, once the wave's vmcnt has drained, and a
-// load with it reads device-coherent data. Ordering the stores before an
-// arrival count then needs only that drain, not a release fence (which on
-// gfx950 writes back the XCD's whole L2).
+// Partials handed from work-group to work-group inside one launch are stored
+// and read with the agent-scope cache bit (sc1) and ordered by count_in.
 constexpr int kScopeDevice = 16;   // sc1
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* base, uint32_t bytes) {
@@ -1039,19 +1035,11 @@ __global__ __launch_bounds__(kSparseThreads) void sparse_attn_kernel(AttnParams 
   }
   MAGE_TRACE_POINT(5);
   if (!handoff) return;
-  // every wave's partial stores are complete at device scope before the count
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  int32_t* s_last = &s_tab[0][0];   // the row tables are free once every wave has left its tiles
-  if (tid == 0) {
-    uint32_t* arrived = p.arrivals + static_cast<int64_t>(u) * (kMaxRows / 32) + rb;
-    const uint32_t before = __hip_atomic_fetch_add(arrived, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const bool last = before == static_cast<uint32_t>(p.nchunk - 1);
-    if (last) __hip_atomic_store(arrived, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // ready for the next launch
-    *s_last = last;
-  }
-  __syncthreads();
-  if (!*s_last) return;
+  // the row tables are free once every wave has left its tiles; the counter is
+  // left at zero for the next launch
+  if (!count_in(p.arrivals + static_cast<int64_t>(u) * (kMaxRows / 32) + rb, static_cast<uint32_t>(p.nchunk),
+                true, &s_tab[0][0]))
+    return;
   MAGE_TRACE_POINT(7);
   // the last arriver: wave w merges kTasks consecutive (d block, register
   // group) pairs of the 4 * kNdb, all chunks' loads of a batch in flight at once

@@ -643,6 +643,7 @@ mage_status launch_sparse(const Dims& d, const uint16_t* q, const KvArgs& kv, co
     seq_slots = slots_for(chunk);
   }
   const int nch = static_cast<int>(cdiv(k, chunk));   // block rows, if any, ride in the last chunk
+  if (!counts && nch > 1 && U * nch > L.slots) return fail(MAGE_ERR_UNSUPPORTED, "workspace plan too small for the split");
   AttnParams ap{};
   ap.q = q;
   ap.kv = kv.src;

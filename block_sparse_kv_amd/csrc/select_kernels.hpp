@@ -11,17 +11,16 @@
 //
 // Top-k: the k_eff largest scores, ties to the lower position, ascending
 // output. Scores are >= +0, so their fp32 bit patterns order like the values
-// and the selection is integer work on those bits: an MSB-first radix select
-// (8-bit digits, per-wave LDS histograms, a sampled first digit that narrows
-// the search to a small candidate window) finds the k-th largest bit pattern T
-// and how many entries equal to T to keep; an index-ordered compaction (each
-// thread owns a contiguous run, block prefix sums give the output offsets)
-// then keeps every entry > T and the lowest-positioned entries == T. A first
-// kernel does this per 16384-position chunk held in LDS;
-// a second kernel runs the same selection over the concatenated per-chunk
-// winners, which are in position order, so its output is already ascending.
-// The two kernels replace an in-kernel last-arriver handoff: on gfx950 a
-// device-scope fence writes back the XCD's whole L2, which costs microseconds.
+// and the selection is integer work on those bits. The score sweep adds every
+// score to a 1024-bin histogram of its row (top bits of the pattern); the
+// top-k launch then finds the bin holding the row's k-th largest score, has
+// each work-group compact its chunk's scores in that bin and above (in
+// position order) to a candidate slice, and the row's last work-group runs an
+// MSB-first radix select (8-bit digits, LDS histograms) over the candidates
+// for the k-th largest pattern T and how many entries equal to T to keep; an
+// index-ordered compaction (each thread owns a contiguous run, block prefix
+// sums give the output offsets) keeps every entry > T and the
+// lowest-positioned entries == T, so the output is already ascending.
 #pragma once
 
 #include "attn_kernels.hpp"
@@ -796,9 +795,8 @@ __global__ __launch_bounds__(kHistThreads) void topk_hist_kernel(TopkParams p) {
   publish_hist<kHistThreads>(s_hist, p.hist + static_cast<int64_t>(u) * kHistBins);
 }
 
-// Device-scope (cache bit sc1) accesses for what one work-group of a launch
-// hands to another: complete in every XCD's view once the writer's vmcnt has
-// drained, read from the coherent level rather than from a stale L2 line.
+// Agent-scope (cache bit sc1) accesses for what one work-group of a launch
+// hands to another (relaxed agent-scope atomics); count_in orders them.
 __device__ __forceinline__ void st_dev(uint32_t* p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -871,8 +869,8 @@ __device__ void wave_select_in_bin(const uint32_t* cand, int m, int rem, uint32_
 //      score: every score in a higher bin is in the top k, none in a lower one.
 //   2. The chunk's scores in bins >= b*, in position order, go to the chunk's
 //      candidate slice (device-scope stores), and their number to cand_count.
-//   3. The work-group counts itself in on the row's arrival counter (after its
-//      stores have drained); the last of the row's work-groups selects among
+//   3. The work-group counts itself in on the row's arrival counter (count_in:
+//      after its stores have drained); the last of the row's work-groups selects among
 //      the row's candidates: the chunks' slices taken in chunk order are in
 //      position order, the kk-th largest among them is the row's kk-th largest
 //      (every larger score is a candidate), and the ordered compaction keeps
@@ -947,16 +945,10 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(TopkParams p)
       }
     if (tid == 0) st_dev(p.cand_count + static_cast<int64_t>(u) * p.nchunk + c, kept);
   }
-  // ---- 3. count in; the row's last work-group selects
-  __builtin_amdgcn_s_waitcnt(0);   // this thread's candidate stores are complete at device scope
-  __syncthreads();
+  // ---- 3. count in; the row's last work-group selects (the counter is zeroed
+  // by the next exact pass)
   const int nch = (n + kLocalChunk - 1) / kLocalChunk;
-  if (tid == 0) {
-    const uint32_t before = __hip_atomic_fetch_add(p.arrivals + u, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_sel[2] = before == static_cast<uint32_t>(nch - 1);
-  }
-  __syncthreads();
-  if (!s_sel[2]) return;
+  if (!count_in(p.arrivals + u, static_cast<uint32_t>(nch), false, &s_sel[2])) return;
   MAGE_TRACE_POINT(2);
   const int32_t* cnt = p.cand_count + static_cast<int64_t>(u) * p.nchunk;
   // s_off[c] = candidates before chunk c (thread t sums a contiguous run of chunks)

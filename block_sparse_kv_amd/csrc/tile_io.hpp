@@ -47,6 +47,32 @@ __device__ __forceinline__ void wg_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Hand-off between the work-groups of one launch through a counter. What is
+// handed over is stored and read only with agent-scope cache bits (sc1): the
+// instructions the compiler emits for relaxed agent-scope atomic stores and
+// loads, which its gfx942/gfx950 memory model makes coherent across the XCDs'
+// L2s by the scope bits alone. Its agent-scope release adds a write-back of
+// the XCD's L2 (buffer_wbl2) before the wait for completion, for plain stores
+// that may sit dirty there; with no plain stores to publish, the wait alone
+// orders the handed-over stores before the count: every thread's stores
+// drain (vmcnt 0: performed at agent scope), the work-group meets, one lane
+// counts in. The work-group that brings the count to n (zeroing the counter
+// when `reset`) gets true in every thread and reads the data with sc1 loads,
+// issued after the count's result returned. With the compiler's release and
+// acquire fences instead, the later step takes 1.2 us longer at 128K context.
+__device__ __forceinline__ bool count_in(uint32_t* counter, uint32_t n, bool reset, int32_t* s_flag) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t before = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = before == n - 1;
+    if (last && reset) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *s_flag = last;
+  }
+  __syncthreads();
+  return *s_flag != 0;
+}
+
 // Wait until at most `pending` tiles (of kPerTile DMA instructions each) are
 // still in flight for this wave; pending <= kStages - 1.
 template <int kPerTile, int P>
@@ -137,6 +163,7 @@ __device__ __forceinline__ void dma16(const void* b, uint32_t o, uint32_t l) {
 // memory; the wait frees the address registers before the block ends).
 template <bool kNt = false>
 __device__ __forceinline__ void dma16_sync(const void* addr, uint32_t lds) {
+  lds = __builtin_amdgcn_readfirstlane(lds);
   if constexpr (kNt) {
     asm volatile(
         "s_mov_b32 m0, %1\n\t"
