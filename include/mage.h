@@ -133,10 +133,11 @@ mage_status mage_workspace_check(const void* workspace, size_t workspace_bytes, 
  *
  * Exact pass (split over N, MFMA, online softmax) then the split merge run on
  * attn_stream; O and lse are final when attn_stream reaches that point. The
- * score sweep and top-k run on select_stream (after waiting for the merge);
- * idx and scores are final when select_stream completes, and idx_ready (if
- * non-null) is recorded there. select_stream may be null (= attn_stream).
- * lse and scores may be null.
+ * score sweep (which merges the row statistics it needs from the exact pass's
+ * partials itself) and top-k run on select_stream after waiting for the exact
+ * pass, beside the merge; idx and scores are final when select_stream
+ * completes, and idx_ready (if non-null) is recorded there. select_stream may
+ * be null (= attn_stream). lse and scores may be null.
  */
 mage_status mage_select_exact(const mage_dims* dims, const uint16_t* q,
                               const uint16_t* k_cache, const uint16_t* v_cache,
