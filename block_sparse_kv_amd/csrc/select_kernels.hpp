@@ -951,12 +951,43 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(TopkParams p)
   if (!count_in(p.arrivals + u, static_cast<uint32_t>(nch), false, &s_sel[2])) return;
   MAGE_TRACE_POINT(2);
   const int32_t* cnt = p.cand_count + static_cast<int64_t>(u) * p.nchunk;
+  const uint32_t* bits = p.cand_bits + static_cast<int64_t>(u) * p.cand_stride;
+  const int32_t* pos = p.cand_pos + static_cast<int64_t>(u) * p.cand_stride;
+  // The first spec_per slots of every chunk's slice, loaded in the same round
+  // trip as the counts: when no chunk kept more, they hold every candidate
+  // and the second round trip of loads through the offsets is skipped. A
+  // chunk keeps about 1.1-1.2 kk / nch candidates, so the window is twice
+  // that (at least 64 slots, at most 4096 slots in all: four per thread).
+  // Slots past a chunk's count hold stale values and are dropped once the
+  // counts are known.
+  constexpr int kSpecLoads = 4, kSpecMinShift = 6;
+  const bool spec = (nch << kSpecMinShift) <= kSpecLoads * kTopkThreads;
+  int spec_shift = kSpecMinShift;   // window 2^spec_shift slots per chunk
+  while ((nch << spec_shift) < 2 * kk && (nch << (spec_shift + 1)) <= kSpecLoads * kTopkThreads) ++spec_shift;
+  const int spec_per = 1 << spec_shift;
+  uint32_t sb[kSpecLoads];
+  int32_t sp[kSpecLoads];
+  if (spec) {
+#pragma unroll
+    for (int j = 0; j < kSpecLoads; ++j) {
+      // clamped: the slots past the window repeat its last one
+      const int i = min(tid + j * kTopkThreads, (nch << spec_shift) - 1);
+      const int64_t sl = static_cast<int64_t>(i >> spec_shift) * kLocalChunk + (i & (spec_per - 1));
+      sb[j] = ld_dev(bits + sl);
+      sp[j] = ld_dev(pos + sl);
+    }
+  }
   // s_off[c] = candidates before chunk c (thread t sums a contiguous run of chunks)
+  bool over = false;
   {
     const int per = (nch + kTopkThreads - 1) / kTopkThreads;
     const int c0 = min(tid * per, nch), c1 = min(c0 + per, nch);
     int mine = 0;
-    for (int cc = c0; cc < c1; ++cc) mine += ld_dev(cnt + cc);
+    for (int cc = c0; cc < c1; ++cc) {
+      const int k1 = ld_dev(cnt + cc);
+      mine += k1;
+      over |= k1 > spec_per;
+    }
     int total;
     int oo = block_inclusive_scan(mine, sh.wsum, total) - mine;
     for (int cc = c0; cc < c1; ++cc) {
@@ -965,10 +996,11 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(TopkParams p)
     }
     if (tid == 0) s_off[nch] = total;
   }
-  __syncthreads();
+  // (the barrier runs in every case: it also orders the s_off writes above
+  // before the reads below)
+  const bool any_over = __syncthreads_or(over) != 0;
+  const bool spec_all = spec && !any_over;
   const int total = s_off[nch];
-  const uint32_t* bits = p.cand_bits + static_cast<int64_t>(u) * p.cand_stride;
-  const int32_t* pos = p.cand_pos + static_cast<int64_t>(u) * p.cand_stride;
   // candidate i -> its index in the chunk slices (binary search over s_off)
   auto slot_of = [&](int i) -> int64_t {
     int a = 0, b = nch - 1;
@@ -982,7 +1014,19 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(TopkParams p)
   int need;
   if (total <= kMax) {
     constexpr int kPer = kMax / kTopkThreads;
-    {
+    if (spec_all) {
+      // every candidate is among the speculative loads: place them in order
+      // (entries past total are never read)
+#pragma unroll
+      for (int j = 0; j < kSpecLoads; ++j) {
+        const int i = tid + j * kTopkThreads;
+        const int cc = i >> spec_shift, o = i & (spec_per - 1);
+        if (i < (nch << spec_shift) && o < s_off[cc + 1] - s_off[cc]) {
+          s_data[s_off[cc] + o] = sb[j];
+          s_data[kMax + s_off[cc] + o] = static_cast<uint32_t>(sp[j]);
+        }
+      }
+    } else {
       uint32_t vb[kPer];
       int32_t vp[kPer];
 #pragma unroll
