@@ -274,41 +274,14 @@ __device__ __forceinline__ void k_frags_lds(uint32_t base, const uint32_t (&ofs)
   for (int ks = 0; ks < D / 16; ++ks) f[ks] = __builtin_bit_cast(bf16x8, *lds_ptr<const u32x4>(base + ofs[ks]));
 }
 
-// Per-lane byte offset of the V^T fragment reads (inside a V tile).
+// Per-lane byte offset of the V^T fragment reads (inside a V tile). Each
+// fragment takes two ds_read_b64_tr_b16: within each 16-lane group the
+// hardware hands lane i element i%4 of the 8 bytes loaded by lanes i/4 + 4j,
+// so lane l ends up with 8 keys of one d column (the A operand of
+// v_mfma_f32_32x32x16_bf16 for V^T).
 __device__ __forceinline__ uint32_t vt_lane_offset(int lane) {
   const int q = lane >> 4, sg = lane & 15;
   return ((8 * (q >> 1) + (sg >> 2)) << 6) + ((q & 1) << 5) + ((sg & 3) << 3);
-}
-
-// V^T fragments for the A operand of v_mfma_f32_32x32x16_bf16, d block kDb,
-// the four 16-key slices of the tile: frag[f] holds in lane l the values
-// V[16f + 8*(l/32) + j][32*kDb + (l%32)], j = 0..7. Each fragment takes two
-// ds_read_b64_tr_b16 (within each 16-lane group the hardware hands lane i
-// element i%4 of the 8 bytes loaded by lanes i/4 + 4j); all eight reads use
-// the lane's base address and immediate offsets. Same asm pattern as k_frags.
-template <int kDb>
-__device__ __forceinline__ void vt_frags(uint32_t vaddr, bf16x8 (&frag)[4]) {
-  typedef short s4 __attribute__((ext_vector_type(4)));
-  constexpr int kB = kDb * kTileKeys * 64;
-  s4 r0, r1, r2, r3, r4, r5, r6, r7;
-  asm volatile(
-      "ds_read_b64_tr_b16 %0, %8 offset:%9\n\t"
-      "ds_read_b64_tr_b16 %1, %8 offset:%10\n\t"
-      "ds_read_b64_tr_b16 %2, %8 offset:%11\n\t"
-      "ds_read_b64_tr_b16 %3, %8 offset:%12\n\t"
-      "ds_read_b64_tr_b16 %4, %8 offset:%13\n\t"
-      "ds_read_b64_tr_b16 %5, %8 offset:%14\n\t"
-      "ds_read_b64_tr_b16 %6, %8 offset:%15\n\t"
-      "ds_read_b64_tr_b16 %7, %8 offset:%16\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6), "=&v"(r7)
-      : "v"(vaddr), "i"(kB), "i"(kB + 256), "i"(kB + 1024), "i"(kB + 1280), "i"(kB + 2048),
-        "i"(kB + 2304), "i"(kB + 3072), "i"(kB + 3328));
-  typedef short s8 __attribute__((ext_vector_type(8)));
-  frag[0] = __builtin_bit_cast(bf16x8, s8{r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]});
-  frag[1] = __builtin_bit_cast(bf16x8, s8{r2[0], r2[1], r2[2], r2[3], r3[0], r3[1], r3[2], r3[3]});
-  frag[2] = __builtin_bit_cast(bf16x8, s8{r4[0], r4[1], r4[2], r4[3], r5[0], r5[1], r5[2], r5[3]});
-  frag[3] = __builtin_bit_cast(bf16x8, s8{r6[0], r6[1], r6[2], r6[3], r7[0], r7[1], r7[2], r7[3]});
 }
 
 // All V^T fragments of one 32-key half tile: frag[db][s] holds in lane l the
