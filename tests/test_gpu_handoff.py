@@ -113,3 +113,26 @@ def test_handoff_under_graph_replay_with_new_indices():
         assert np.abs(got_o - Or).max() <= TOL, rep
         assert np.abs(got_l - lr).max() <= TOL, rep
     assert int(ws.buf[:ARRIVAL_BYTES].view(torch.int32).count_nonzero()) == 0
+
+
+def test_one_launch_merge_equals_the_merge_launch():
+    # the same split (8 chunks of 128 entries per KV head) merged inside the
+    # launch (uniform index lists) and by the merge kernel (per-head counts,
+    # here all equal to the row length): the merge arithmetic is shared, so
+    # O and lse must agree bit for bit
+    w, inp, idx = _case((4000,), 8, 2, 128, 32, 1024, False, seed=91)
+    q, k, v = inp.q_steps[0].to(DEV), inp.k.to(DEV), inp.v.to(DEV)
+    ix = idx.to(DEV)
+    mage.last_launches()
+    o1, l1 = mage.sparse_attn(q, k, v, ix, w.scale)
+    names1 = mage.last_launches()
+    counts = torch.full((1, 2), 1024, dtype=torch.int32, device=DEV)
+    o2, l2 = mage.sparse_attn_counts(q, k, v, ix, counts, 2048, w.scale)
+    names2 = mage.last_launches()
+    torch.cuda.synchronize()
+    assert names1 == ["sparse_attn_kernel"], names1
+    assert names2 == ["sparse_attn_kernel", "exact_merge_kernel[sparse]"], names2
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    Or, lr = _oracle(w, inp, idx)
+    assert np.abs(o1.cpu().double().numpy() - Or).max() <= TOL
+    assert np.abs(l1.cpu().double().numpy() - lr).max() <= TOL
