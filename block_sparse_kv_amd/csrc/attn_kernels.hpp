@@ -345,7 +345,7 @@ template <int D, int kStages, bool kSplitIssue = true>
 __global__ __launch_bounds__(kAttnThreads) void exact_chunk_kernel(AttnParams p) {
   using G = TileGeom<D, kAttnThreads>;
   constexpr int kNdb = D / 32, kNks = D / 16;
-  static_assert(kStages == 4, "K(t+1)..K(t+4) and V(t-1)..V(t+2) are resident or in flight");
+  static_assert(kStages == 3 || kStages == 4, "K(t+1)..K(t+kStages) and V(t-1)..V(t+kStages-2) are resident or in flight");
   static_assert(2 * kStages * G::kBytes >= 4 * kWave * (2 + 16 * kNdb) * 4, "pair-merge area");
   // K ring (kStages tiles) followed by the V ring (kStages tiles)
   __shared__ __attribute__((aligned(1024))) uint8_t s_ring[2 * kStages * G::kBytes];

@@ -199,10 +199,15 @@ int sparse_chunk(int64_t units, int nrb, int k) {
   return std::min(kSparseMaxChunk, std::max(min_chunk, c));
 }
 
-// LDS ring depth: 4 x 32 KiB of K+V tiles at d = 128, 4 x 16 KiB at d = 64;
-// the score sweep streams K only: 4 x 16 KiB / 4 x 8 KiB (two work-groups per CU).
-template <int D>
-constexpr int kStagesFor = 4;
+// LDS ring depth of the exact pass: 3 stages of K+V tiles (3 x 32 KiB at
+// d = 128) when half the waves issue the loads (contiguous caches), 4 when
+// every wave does (paged caches). In interleaved A/Bs 3 stages took 116.4
+// against 118.4 us at head128k (98.6 / 100.7 at mha64k, 37.4 / 39.1 at
+// gqa32k): the issuing waves block less on a fuller load queue. On the paged
+// ragged batch 3 stages took 451 against 424 us. The score sweep streams K
+// only: 4 x 16 KiB / 4 x 8 KiB (two work-groups per CU).
+constexpr int kExactStagesSplit = 3;
+constexpr int kExactStagesAll = 4;
 template <int D>
 constexpr int kScoreStagesFor = 4;
 constexpr int kSparseStages = 2;
@@ -461,8 +466,8 @@ mage_status launch_select(const Dims& d, const uint16_t* q, const KvArgs& kv, in
   ap.zero_hist = main_topk ? at<uint32_t>(ws, L.hist) : nullptr;
   ap.zero_count = main_topk ? at<uint32_t>(ws, L.topk_arrivals) : nullptr;
   // contiguous caches: tile loads issued by half the waves; paged: by all
-  const void* exact_fn = kv.src.page_table ? kfn(exact_chunk_kernel<D, kStagesFor<D>, false>)
-                                           : kfn(exact_chunk_kernel<D, kStagesFor<D>, true>);
+  const void* exact_fn = kv.src.page_table ? kfn(exact_chunk_kernel<D, kExactStagesAll, false>)
+                                           : kfn(exact_chunk_kernel<D, kExactStagesSplit, true>);
   if (mage_status st = launch(exact_fn, "exact_chunk_kernel", exact_grid, kAttnThreads, attn, ap); st != MAGE_OK)
     return st;
 

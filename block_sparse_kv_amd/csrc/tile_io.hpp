@@ -111,6 +111,8 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 template <bool kNt1 = false>
 __device__ __forceinline__ void dma16x2(const void* b0, uint32_t o0, uint32_t l0, const void* b1, uint32_t o1,
                                         uint32_t l1) {
+  l0 = __builtin_amdgcn_readfirstlane(l0);   // wave-uniform; kept in SGPRs for M0
+  l1 = __builtin_amdgcn_readfirstlane(l1);
   if constexpr (kNt1) {
     asm volatile(
         "s_mov_b32 m0, %4\n\t"
@@ -139,6 +141,7 @@ __device__ __forceinline__ void dma16x2(const void* b0, uint32_t o0, uint32_t l0
 // A single load of the dma16x2 form (kNt: non-temporal).
 template <bool kNt = false>
 __device__ __forceinline__ void dma16(const void* b, uint32_t o, uint32_t l) {
+  l = __builtin_amdgcn_readfirstlane(l);
   if constexpr (kNt) {
     asm volatile(
         "s_mov_b32 m0, %2\n\t"
