@@ -205,11 +205,15 @@ int sparse_chunk(int64_t units, int nrb, int k) {
 // against 118.4 us at head128k (98.6 / 100.7 at mha64k, 37.4 / 39.1 at
 // gqa32k): the issuing waves block less on a fuller load queue. On the paged
 // ragged batch 3 stages took 451 against 424 us. The score sweep streams K
-// only: 4 x 16 KiB / 4 x 8 KiB (two work-groups per CU).
+// only, through 2 stages (2 x 16 KiB at d = 128): with 48 KiB of LDS per
+// work-group three fit on a CU instead of two, which took the sweep from 57.1
+// to 54.8 us at head128k, 23.2 to 21.3 at gqa32k and 218.6 to 188.1 us on the
+// ragged batch (interleaved A/B; 3 stages: 56.0, 22.1, 217.8).
+constexpr int kScoreRounds = 2;
 constexpr int kExactStagesSplit = 3;
 constexpr int kExactStagesAll = 4;
 template <int D>
-constexpr int kScoreStagesFor = 4;
+constexpr int kScoreStagesFor = 2;
 constexpr int kSparseStages = 2;
 
 // ---- workspace layout ------------------------------------------------------
@@ -512,11 +516,12 @@ mage_status launch_select(const Dims& d, const uint16_t* q, const KvArgs& kv, in
   sp.stride = scores ? score_stride : kv.max_n;
   sp.S = d.S; sp.B = d.B; sp.Hq = d.Hq; sp.Hkv = d.Hkv; sp.G = d.G; sp.R = d.R;
   // positions per work-group: halved from kScoreChunk (down to kScoreChunkMin)
-  // until the sweep has two rounds of work-groups (two fit on a CU)
+  // until the sweep has kScoreRounds work-groups per CU
   sp.chunk = kScoreChunk;
+  const int score_rounds = env_int("MAGE_SCORE_ROUNDS", kScoreRounds);
   for (int64_t g = 0; sp.chunk > kScoreChunkMin; sp.chunk /= 2) {
     chunk_map(kv, d, sp.chunk, g);
-    if (g >= 2 * kCus) break;
+    if (g >= score_rounds * kCus) break;
   }
   sp.nchunk = static_cast<int>(cdiv(kv.max_n, sp.chunk));
   sp.reverse = env_int("MAGE_SCORE_REVERSE", 1);
