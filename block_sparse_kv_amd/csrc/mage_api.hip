@@ -529,8 +529,8 @@ mage_status launch_select(const Dims& d, const uint16_t* q, const KvArgs& kv, in
   sp.lens = kv.lens;
   int64_t score_grid = 0;
   sp.map = chunk_map(kv, d, sp.chunk, score_grid);
-  const void* score_fn = env_int("MAGE_SCORE_NT", 1) ? kfn(score_kernel<D, kScoreStagesFor<D>, true>)
-                                                      : kfn(score_kernel<D, kScoreStagesFor<D>, false>);
+  const void* score_fn = kv.src.page_table ? kfn(score_kernel<D, kScoreStagesFor<D>, true>)
+                                            : kfn(score_kernel<D, kScoreStagesFor<D>, false>);
   if (mage_status st = launch(score_fn, "score_kernel", score_grid, kThreads, sel, sp); st != MAGE_OK)
     return st;
   if (main_topk) {

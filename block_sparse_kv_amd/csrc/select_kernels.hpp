@@ -134,14 +134,16 @@ constexpr int kScoreChunk = 2048;      // positions per work-group (largest)
 constexpr int kScoreChunkMin = 512;    // smallest, for short prefixes
 constexpr int kStatBatch = 16;         // chunk statistics merged per batch (as the step-1 merge)
 
-// kNt: the K tiles are loaded non-temporally (this sweep is their last use in
-// the step).
-template <int D, int kStages, bool kNt>
+// The K tiles are loaded non-temporally (this sweep is their last use in the
+// step). kPaged: the chunk's page ids are staged in LDS; the contiguous form
+// leaves that table out, which lets four work-groups share a CU.
+template <int D, int kStages, bool kPaged>
 __global__ __launch_bounds__(kThreads) void score_kernel(ScoreParams p) {
   using G = TileGeom<D>;
   constexpr int kNks = D / 16;
+  constexpr bool kNt = true;
   __shared__ __attribute__((aligned(1024))) uint8_t s_ring[kStages * G::kBytes];
-  __shared__ int32_t s_pages[kScoreChunk + 1];
+  __shared__ int32_t s_pages[kPaged ? kScoreChunk + 1 : 1];
   __shared__ float s_col[2][4][kTileKeys];
   __shared__ uint32_t s_hist[kHistBins];
   __shared__ float s_crow[kMaxRows];
@@ -157,7 +159,7 @@ __global__ __launch_bounds__(kThreads) void score_kernel(ScoreParams p) {
   if (e0 >= e1) return;
   const int nrb = (p.R + 31) >> 5;
   const bool computes = w < nrb;
-  const bool paged = p.kv.page_table != nullptr;
+  constexpr bool paged = kPaged;   // the host picks the form by the cache's layout
   const int pshift = p.kv.page_shift, pmask = (1 << p.kv.page_shift) - 1;
   const int64_t seq_base = paged ? 0 : (static_cast<int64_t>(s) * p.Hkv + h) * p.kv.n_uniform;
   const int page0 = e0 >> pshift;
