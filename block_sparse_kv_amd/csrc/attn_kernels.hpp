@@ -410,7 +410,7 @@ __global__ __launch_bounds__(kAttnThreads) void exact_chunk_kernel(AttnParams p)
   MAGE_TRACE_CLK(1);
 
   // element offset of the K/V row of prefix position e (clamped into the chunk)
-  auto row_of = [&](int e) -> int64_t {
+  auto row_of = [&](int e) __attribute__((always_inline)) -> int64_t {
     const int pos = min(e, e1 - 1);
     if (paged) {
       const int64_t page = s_pages[(pos >> pshift) - page0];
@@ -426,11 +426,11 @@ __global__ __launch_bounds__(kAttnThreads) void exact_chunk_kernel(AttnParams p)
   const int last_t = (cnt - 1) / kTileKeys;
   const int tail = cnt - last_t * kTileKeys;            // keys in the last tile, 1..64
   const bool shift_last = tail < kTileKeys && e1 >= kTileKeys;
-  auto tile_base = [&](int t) -> int {
+  auto tile_base = [&](int t) __attribute__((always_inline)) -> int {
     return (t == last_t && shift_last) ? e1 - kTileKeys : e0 + t * kTileKeys;
   };
   // validity bits of this wave's key half of tile t
-  auto half_mask = [&](int t) -> uint32_t {
+  auto half_mask = [&](int t) __attribute__((always_inline)) -> uint32_t {
     if (t == last_t && tail < kTileKeys) {
       if (shift_last) {
         const int lo = kTileKeys - tail - 32 * kh;     // first valid key of the half
@@ -453,8 +453,10 @@ __global__ __launch_bounds__(kAttnThreads) void exact_chunk_kernel(AttnParams p)
   const uint32_t ring_base = lds_addr(s_ring);
   const uint32_t k_half = kh * 32 * G::kRowBytes;
   const uint32_t v_lane = kh * 2048 + vt_lane_offset(lane);
-  auto k_slot = [&](int tile) -> uint32_t { return ring_base + (tile % kStages) * G::kBytes; };
-  auto v_slot = [&](int tile) -> uint32_t { return ring_base + (kStages + tile % kStages) * G::kBytes; };
+  auto k_slot_m = [&](int m) __attribute__((always_inline)) -> uint32_t { return ring_base + m * G::kBytes; };   // m = tile mod kStages
+  auto v_slot_m = [&](int m) __attribute__((always_inline)) -> uint32_t { return ring_base + (kStages + m) * G::kBytes; };
+  auto k_slot = [&](int tile) __attribute__((always_inline)) -> uint32_t { return k_slot_m(tile % kStages); };
+  auto v_slot = [&](int tile) __attribute__((always_inline)) -> uint32_t { return v_slot_m(tile % kStages); };
 
   const int ntiles = (cnt + kTileKeys - 1) / kTileKeys;
   // Full tiles: each DMA instruction covers 4 (K) or 16 (V) consecutive rows,
@@ -486,7 +488,7 @@ __global__ __launch_bounds__(kAttnThreads) void exact_chunk_kernel(AttnParams p)
   }
   const bool fast_rows = !paged || pshift >= 4;
   // byte address of the K row of prefix position pos (wave-uniform pos)
-  auto row_bytes = [&](int pos) -> int64_t {
+  auto row_bytes = [&](int pos) __attribute__((always_inline)) -> int64_t {
     if (paged) {
       const int64_t page = __builtin_amdgcn_readfirstlane(s_pages[(pos >> pshift) - page0]);
       return ((((page * p.Hkv + h) << pshift) + (pos & pmask)) * D) * 2;
@@ -494,7 +496,7 @@ __global__ __launch_bounds__(kAttnThreads) void exact_chunk_kernel(AttnParams p)
     return ((seq_base + pos) * D) * 2;
   };
   // a shifted tile of a paged cache need not start on a 16-row page boundary
-  auto fast_tile = [&](int tile) -> bool {
+  auto fast_tile = [&](int tile) __attribute__((always_inline)) -> bool {
     const int base = tile_base(tile);
     return fast_rows && base + kTileKeys <= e1 && (!paged || (base & 15) == 0);
   };
@@ -503,7 +505,7 @@ __global__ __launch_bounds__(kAttnThreads) void exact_chunk_kernel(AttnParams p)
   // (either may be -1: none) go to their ring slots.
   const char* kbytes = reinterpret_cast<const char*>(p.kv.k);
   const char* vbytes = reinterpret_cast<const char*>(p.kv.v);
-  auto issue_slices = [&](int tk, int tv, int ws) {   // the slices of wave ws of the 8-wave layout
+  auto issue_slices = [&](int tk, int tv, int ws) __attribute__((always_inline)) {   // the slices of wave ws of the 8-wave layout
     const bool fk = tk >= 0 && fast_tile(tk), fv = tv >= 0 && fast_tile(tv);
     const int bk = tk >= 0 ? tile_base(tk) : 0, bv = tv >= 0 ? tile_base(tv) : 0;
     const uint32_t lk = tk >= 0 ? k_slot(tk) : 0u, lv = tv >= 0 ? v_slot(tv) : 0u;
@@ -536,7 +538,7 @@ __global__ __launch_bounds__(kAttnThreads) void exact_chunk_kernel(AttnParams p)
       }
     }
   };
-  auto issue = [&](int tk, int tv) {
+  auto issue = [&](int tk, int tv) __attribute__((always_inline)) {
     if constexpr (split_issue) {
       if (!issuer) return;
 #pragma unroll 1
@@ -545,6 +547,36 @@ __global__ __launch_bounds__(kAttnThreads) void exact_chunk_kernel(AttnParams p)
       issue_slices(tk, tv, w);
     }
   };
+  // Steady state (contiguous rows, full tiles before the last): a tile's K
+  // (V) rows are one 16 KiB run at k_run (v_run) + tile * kBytes, so each of
+  // an issuing wave's slices is that base plus a per-lane offset and an LDS
+  // offset fixed for the whole loop. A wave issues about one instruction
+  // every four cycles, and the general path's per-slice address and branch
+  // work (about 150 instructions a tile) kept the issuing waves out of their
+  // MFMA region for most of a tile.
+  constexpr int kSlices = (split_issue ? 2 : 1) * G::kInstr;   // slices per issuing wave and tile
+  uint32_t k_lane[kSlices], v_lane_dma[kSlices], lds_slice[kSlices];
+#pragma unroll
+  for (int i = 0; i < kSlices; ++i) {
+    const int pass = i / G::kInstr, j = i % G::kInstr;
+    const int ws = split_issue ? (w & 3) + 4 * pass : w;
+    const int slot = ws * G::kInstr + j;
+    k_lane[i] = koff[j] + static_cast<uint32_t>(slot * kKRowsPerInstr * G::kRowBytes);
+    v_lane_dma[i] = voff[j] + (ws >= 4 ? static_cast<uint32_t>(G::kInstr * 32 * 2) : 0u) +
+                    static_cast<uint32_t>(((slot & 3) << 4) * G::kRowBytes);
+    lds_slice[i] = static_cast<uint32_t>(slot * 1024);
+  }
+  const char* k_run = kbytes + (seq_base + e0) * G::kRowBytes;
+  const char* v_run = vbytes + (seq_base + e0) * G::kRowBytes;
+  // K rows of tile tk into LDS lk, V rows of tile tk - 2 into lv; tk < last_t
+  auto issue_steady = [&](int tk, uint32_t lk, uint32_t lv) __attribute__((always_inline)) {
+    if (!issuer) return;
+    const char* kt = k_run + static_cast<int64_t>(tk) * G::kBytes;
+    const char* vt = v_run + static_cast<int64_t>(tk - 2) * G::kBytes;
+#pragma unroll
+    for (int i = 0; i < kSlices; ++i)
+      dma16x2<true>(kt, k_lane[i], lk + lds_slice[i], vt, v_lane_dma[i], lv + lds_slice[i]);
+  };
   // Load group g = what iteration g reads: K rows of tile g+1 and V rows of
   // tile g-1. Iteration t waits for group t, with the kStages - 2 groups after
   // it still allowed in flight, and issues group t + kStages - 1 into the
@@ -552,10 +584,10 @@ __global__ __launch_bounds__(kAttnThreads) void exact_chunk_kernel(AttnParams p)
   // has passed the barrier of iteration t (K(t) was read by the QK product and
   // V(t-2) by the PV product of iteration t-1).
   constexpr int kPerTile = (split_issue ? 2 : 1) * G::kInstr;   // issuers: two slices per tile
-  auto group_k = [&](int g) { return g + 1 < ntiles ? g + 1 : -1; };
-  auto group_v = [&](int g) { return g >= 1 && g - 1 < ntiles ? g - 1 : -1; };
-  auto group_tiles = [&](int g) { return (group_k(g) >= 0) + (group_v(g) >= 0); };
-  auto wait_group = [&](int g) {
+  auto group_k = [&](int g) __attribute__((always_inline)) { return g + 1 < ntiles ? g + 1 : -1; };
+  auto group_v = [&](int g) __attribute__((always_inline)) { return g >= 1 && g - 1 < ntiles ? g - 1 : -1; };
+  auto group_tiles = [&](int g) __attribute__((always_inline)) { return (group_k(g) >= 0) + (group_v(g) >= 0); };
+  auto wait_group = [&](int g) __attribute__((always_inline)) {
     // the others have none in flight
     int pending = 0;
 #pragma unroll
@@ -589,7 +621,7 @@ __global__ __launch_bounds__(kAttnThreads) void exact_chunk_kernel(AttnParams p)
   const bool partial = cnt % kTileKeys != 0;
   [[maybe_unused]] uint64_t trace_acc[4] = {0, 0, 0, 0};
   // t = 0: softmax of tile 0 and QK of tile 1
-  auto first = [&](auto masked) {
+  auto first = [&](auto masked) __attribute__((always_inline)) {
     wait_group(0);
     issue(group_k(kStages - 1), group_v(kStages - 1));
     if (computes) {
@@ -600,17 +632,34 @@ __global__ __launch_bounds__(kAttnThreads) void exact_chunk_kernel(AttnParams p)
       if (ntiles > 1) s_cur = qk_half<D>(k_slot(1) + k_half, kofs, qf);
     }
   };
-  auto middle = [&](int t, auto masked) {
+  // phase: t mod kStages as a compile-time constant (then every ring slot of
+  // the iteration is a constant and the LDS addresses are loop-invariant
+  // bases plus immediate offsets), or -1
+  auto middle = [&](int t, auto masked, auto steady, auto phase) __attribute__((always_inline)) {
+    constexpr int kPh = decltype(phase)::value;
     [[maybe_unused]] const uint64_t tr0 = MAGE_TRACE_NOW();
     wait_group(t);
     [[maybe_unused]] const uint64_t tr1 = MAGE_TRACE_NOW();
-    issue(group_k(t + kStages - 1), group_v(t + kStages - 1));
+    if constexpr (decltype(steady)::value) {
+      const int m0 = kPh >= 0 ? kPh : t % kStages;   // tile t + kStages
+      issue_steady(t + kStages, k_slot_m(m0), v_slot_m(m0 == kStages - 1 ? 0 : m0 + 1));
+    } else {
+      issue(group_k(t + kStages - 1), group_v(t + kStages - 1));
+    }
     if (computes) {
       const uint32_t okm = half_mask(t);
-      const uint32_t kb = k_slot(t + 1 < ntiles ? t + 1 : t) + k_half;
+      const int mk = kPh >= 0 ? (kPh + 1) % kStages : (t + 1 < ntiles ? t + 1 : t) % kStages;
+      const int mv = kPh >= 0 ? (kPh + kStages - 1) % kStages : (t - 1) % kStages;
+      const uint32_t kb = k_slot_m(mk) + k_half;
       [[maybe_unused]] const uint64_t tr2 = MAGE_TRACE_NOW();
       bf16x8 vf[kNdb][2], kf[kNks];
-      vt_frags_half_lds<D>(v_slot(t - 1) + v_lane, vf);
+      // the V fragments are read at this base plus immediate offsets; with a
+      // run-time slot the base is hidden from loop strength reduction, which
+      // would otherwise keep one address register per fragment and update all
+      // of them every iteration
+      uint32_t va = v_slot_m(mv) + v_lane;
+      if constexpr (kPh < 0) asm volatile("" : "+v"(va));
+      vt_frags_half_lds<D>(va, vf);
       k_frags_lds<D>(kb, kofs, kf);
 #pragma unroll
       for (int db = 0; db < kNdb; ++db)
@@ -673,12 +722,26 @@ __global__ __launch_bounds__(kAttnThreads) void exact_chunk_kernel(AttnParams p)
     first(std::true_type{});
   else
     first(std::false_type{});
-  for (int t = 1; t + 1 < ntiles; ++t) middle(t, std::false_type{});
+  using dyn = std::integral_constant<int, -1>;
+  int t = 1;
+  // iterations whose load group (K rows of tile t + kStages, V rows of tile
+  // t + kStages - 2) holds full tiles before the last take the steady issue,
+  // unrolled by kStages from t = 1 so that each copy knows t mod kStages
+  if (!paged) {
+    for (; t + 2 * kStages - 1 < last_t; t += kStages) {
+      middle(t, std::false_type{}, std::true_type{}, std::integral_constant<int, 1 % kStages>{});
+      middle(t + 1, std::false_type{}, std::true_type{}, std::integral_constant<int, 2 % kStages>{});
+      middle(t + 2, std::false_type{}, std::true_type{}, std::integral_constant<int, 3 % kStages>{});
+      if constexpr (kStages == 4) middle(t + 3, std::false_type{}, std::true_type{}, std::integral_constant<int, 0>{});
+    }
+    for (; t + kStages < last_t; ++t) middle(t, std::false_type{}, std::true_type{}, dyn{});
+  }
+  for (; t + 1 < ntiles; ++t) middle(t, std::false_type{}, std::false_type{}, dyn{});
   if (ntiles > 1) {
     if (partial)
-      middle(ntiles - 1, std::true_type{});
+      middle(ntiles - 1, std::true_type{}, std::false_type{}, dyn{});
     else
-      middle(ntiles - 1, std::false_type{});
+      middle(ntiles - 1, std::false_type{}, std::false_type{}, dyn{});
   }
   // t = ntiles: PV of the last tile
   wait_group(ntiles);

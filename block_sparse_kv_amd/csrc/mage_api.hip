@@ -472,6 +472,16 @@ mage_status launch_select(const Dims& d, const uint16_t* q, const KvArgs& kv, in
   // contiguous caches: tile loads issued by half the waves; paged: by all
   const void* exact_fn = kv.src.page_table ? kfn(exact_chunk_kernel<D, kExactStagesAll, false>)
                                            : kfn(exact_chunk_kernel<D, kExactStagesSplit, true>);
+#ifdef MAGE_TUNING
+  if (!kv.src.page_table) {
+    switch (env_int("MAGE_EXACT_MODE", 0)) {
+      case 1: exact_fn = kfn(exact_chunk_kernel<D, 3, false>); break;
+      case 2: exact_fn = kfn(exact_chunk_kernel<D, 4, false>); break;
+      case 3: exact_fn = kfn(exact_chunk_kernel<D, 4, true>); break;
+      default: break;
+    }
+  }
+#endif
   if (mage_status st = launch(exact_fn, "exact_chunk_kernel", exact_grid, kAttnThreads, attn, ap); st != MAGE_OK)
     return st;
 
