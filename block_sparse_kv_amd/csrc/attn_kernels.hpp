@@ -577,6 +577,33 @@ __global__ __launch_bounds__(kAttnThreads) void exact_chunk_kernel(AttnParams p)
     for (int i = 0; i < kSlices; ++i)
       dma16x2<true>(kt, k_lane[i], lk + lds_slice[i], vt, v_lane_dma[i], lv + lds_slice[i]);
   };
+  // Steady state of the paged form (every wave issues its own slices; pages
+  // of >= 16 rows and a chunk that starts on a 64-row boundary, so each
+  // slice's rows lie in one page): the page ids of the wave's slices are read
+  // from the chunk's page list in one batch, behind one wait, and each
+  // slice's address is then scalar arithmetic. The general path waits for one
+  // page-list read per slice, each queued behind the other waves' fragment
+  // reads.
+  auto issue_steady_paged = [&](int tk, uint32_t lk, uint32_t lv) __attribute__((always_inline)) {
+    const int bk = e0 + tk * kTileKeys, bv = bk - 2 * kTileKeys;   // rows of tiles tk and tk - 2
+    int pk[G::kInstr], pv[G::kInstr];
+#pragma unroll
+    for (int j = 0; j < G::kInstr; ++j) {
+      const int slot = w * G::kInstr + j;
+      pk[j] = s_pages[((bk + slot * kKRowsPerInstr) >> pshift) - page0];
+      pv[j] = s_pages[((bv + ((slot & 3) << 4)) >> pshift) - page0];
+    }
+    const uint32_t vadd = w >= 4 ? static_cast<uint32_t>(G::kInstr * 32 * 2) : 0u;
+#pragma unroll
+    for (int j = 0; j < G::kInstr; ++j) {
+      const int slot = w * G::kInstr + j;
+      const int rk = bk + slot * kKRowsPerInstr, rv = bv + ((slot & 3) << 4);
+      const int64_t pgk = __builtin_amdgcn_readfirstlane(pk[j]), pgv = __builtin_amdgcn_readfirstlane(pv[j]);
+      const int64_t ka = (((pgk * p.Hkv + h) << pshift) + (rk & pmask)) * G::kRowBytes;
+      const int64_t va = (((pgv * p.Hkv + h) << pshift) + (rv & pmask)) * G::kRowBytes;
+      dma16x2<true>(kbytes + ka, koff[j], lk + slot * 1024, vbytes + va, voff[j] + vadd, lv + slot * 1024);
+    }
+  };
   // Load group g = what iteration g reads: K rows of tile g+1 and V rows of
   // tile g-1. Iteration t waits for group t, with the kStages - 2 groups after
   // it still allowed in flight, and issues group t + kStages - 1 into the
@@ -641,8 +668,12 @@ __global__ __launch_bounds__(kAttnThreads) void exact_chunk_kernel(AttnParams p)
     wait_group(t);
     [[maybe_unused]] const uint64_t tr1 = MAGE_TRACE_NOW();
     if constexpr (decltype(steady)::value) {
-      const int m0 = kPh >= 0 ? kPh : t % kStages;   // tile t + kStages
-      issue_steady(t + kStages, k_slot_m(m0), v_slot_m(m0 == kStages - 1 ? 0 : m0 + 1));
+      const int m0 = kPh >= 0 ? kPh : t % kStages;   // K tile t + kStages; V tile t + kStages - 2
+      const uint32_t lk = k_slot_m(m0), lv = v_slot_m((m0 + kStages - 2) % kStages);
+      if constexpr (split_issue)
+        issue_steady(t + kStages, lk, lv);
+      else
+        issue_steady_paged(t + kStages, lk, lv);
     } else {
       issue(group_k(t + kStages - 1), group_v(t + kStages - 1));
     }
@@ -727,7 +758,9 @@ __global__ __launch_bounds__(kAttnThreads) void exact_chunk_kernel(AttnParams p)
   // iterations whose load group (K rows of tile t + kStages, V rows of tile
   // t + kStages - 2) holds full tiles before the last take the steady issue,
   // unrolled by kStages from t = 1 so that each copy knows t mod kStages
-  if (!paged) {
+  // (split issue: contiguous rows; every wave issuing: the paged form)
+  const bool steady_ok = split_issue || (paged && pshift >= 4 && (e0 & (kTileKeys - 1)) == 0);
+  if (steady_ok) {
     for (; t + 2 * kStages - 1 < last_t; t += kStages) {
       middle(t, std::false_type{}, std::true_type{}, std::integral_constant<int, 1 % kStages>{});
       middle(t + 1, std::false_type{}, std::true_type{}, std::integral_constant<int, 2 % kStages>{});

@@ -202,6 +202,28 @@ def test_paged_equals_contiguous_bit_exact():
         assert torch.equal(x, y)
 
 
+@pytest.mark.parametrize("d", [128, 64])
+def test_paged_equals_contiguous_long_chunks(d):
+    # about 800 keys per exact-pass chunk: the steady loop of both forms (full
+    # tiles before the last, issued from per-lane offsets or from one batch of
+    # page ids) runs for several unrolled rounds; each unit's last chunk ends
+    # mid-tile
+    w = workloads.custom((50700, 50700), 8, 2, d, 32, 300, name=f"pcl{d}")
+    print(f"[case] paged vs contiguous, long chunks, d={d}", flush=True)
+    inp = workloads.make_inputs(w, steps=2)
+    kp, vp, table, lens = workloads.to_paged(inp.k, inp.v, 16, seed=12)
+    q, kc, vc = inp.q1.to(DEV), inp.k.to(DEV), inp.v.to(DEV)
+    kp, vp, table = kp.to(DEV), vp.to(DEV), table.to(DEV)
+    a = mage.select_exact(q, kc, vc, w.k, w.scale)
+    b = mage.select_exact_paged(q, kp, vp, table, lens, w.k, w.scale)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+    ea = mage.exact_attn(q, kc, vc, w.scale)
+    eb = mage.exact_attn_paged(q, kp, vp, table, lens, w.scale)
+    for x, y in zip(ea, eb):
+        assert torch.equal(x, y)
+
+
 def test_runs_are_bit_identical():
     w = workloads.custom((5000,), 32, 8, 128, 32, 512, name="det")
     inp = workloads.make_inputs(w)
