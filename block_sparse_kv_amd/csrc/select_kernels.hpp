@@ -224,33 +224,42 @@ __global__ __launch_bounds__(kThreads) void score_kernel(ScoreParams p) {
     }
     return ((seq_base + pos) * D) * 2;
   };
+  // A wave's slices cover tile rows wrow .. wrow + 15, contiguous in memory
+  // (one page of >= 16 rows when paged), so a full tile takes one row address
+  // per wave (one page-list read) plus per-lane offsets fixed for the loop.
+  constexpr int kWaveRows = G::kInstr * kKRowsPerInstr;
+  static_assert(kWaveRows == 16, "a wave's slices span 16 tile rows");
+  const int wrow = w * kWaveRows;
+  uint32_t k_lane[G::kInstr];
+#pragma unroll
+  for (int j = 0; j < G::kInstr; ++j) k_lane[j] = koff[j] + static_cast<uint32_t>(j * kKRowsPerInstr * G::kRowBytes);
   auto issue = [&](int t) {
     const int base = e0 + tile_of(t) * kTileKeys;
-    const uint32_t st = ring_base + (t % kStages) * G::kBytes;
+    const uint32_t st = ring_base + (t % kStages) * G::kBytes + static_cast<uint32_t>(w * G::kInstr * 1024);
     if (fast_rows && base + kTileKeys <= e1 && (!paged || (base & 15) == 0)) {
+      const char* rows = kbytes + row_bytes(base + wrow);
 #pragma unroll
-      for (int j = 0; j < G::kInstr; ++j) {
-        const int slot = w * G::kInstr + j;
-        dma16<kNt>(kbytes + row_bytes(base + slot * kKRowsPerInstr), koff[j], st + slot * 1024);
-      }
+      for (int j = 0; j < G::kInstr; ++j) dma16<kNt>(rows, k_lane[j], st + j * 1024);
     } else {
 #pragma unroll
       for (int j = 0; j < G::kInstr; ++j) {
         const int slot = w * G::kInstr + j;
         const int unit = slot * kWave + lane;
         const int r = unit / G::kUnits, uk = (unit % G::kUnits) ^ (r & (G::kUnits - 1));
-        dma16_sync<kNt>(p.kv.k + row_off(base + r) + uk * 8, st + slot * 1024);
+        dma16_sync<kNt>(p.kv.k + row_off(base + r) + uk * 8, st + j * 1024);
       }
     }
   };
-  // column sums of tile t live in s_col[t & 1]; wave 0 reduces them over the
-  // row blocks one iteration later (one barrier per tile)
-  auto reduce_store = [&](int t) {
-    const int e = e0 + tile_of(t) * kTileKeys + tid;
+  // column sums of tile t live in s_col[t & 1]; one iteration later (one
+  // barrier per tile) each wave reduces 16 of the columns over the row blocks
+  // column col of tile t: the sum over the row blocks, scaled, stored and
+  // counted in the histogram
+  auto reduce_store = [&](int t, int col) {
+    const int e = e0 + tile_of(t) * kTileKeys + col;
     float sc = 0.f;
     if (e < e1) {
       float sum = 0.f;
-      for (int ww = 0; ww < nrb; ++ww) sum += s_col[t & 1][ww][tid];
+      for (int ww = 0; ww < nrb; ++ww) sum += s_col[t & 1][ww][col];
       sc = sum * inv_r;
       p.scores[static_cast<int64_t>(u) * p.stride + e] = sc;
     }
@@ -282,7 +291,8 @@ __global__ __launch_bounds__(kThreads) void score_kernel(ScoreParams p) {
     wait_tiles<G::kInstr, kStages - 1>(min(kStages - 2, ntiles - 1 - t));
     wg_barrier();
     if (t + kStages - 1 < ntiles) issue(t + kStages - 1);
-    if (t > 0 && tid < kTileKeys) reduce_store(t - 1);
+    // each wave reduces 16 of the previous tile's columns (lanes 0-15)
+    if (t > 0 && lane < kTileKeys / 4) reduce_store(t - 1, 16 * w + lane);
     const uint32_t k_base = ring_base + (t % kStages) * G::kBytes;
     if (computes) {
       f32x16 acc[2];
@@ -312,7 +322,7 @@ __global__ __launch_bounds__(kThreads) void score_kernel(ScoreParams p) {
     wait_lgkmcnt0();
   }
   __syncthreads();
-  if (tid < kTileKeys) reduce_store(ntiles - 1);
+  if (lane < kTileKeys / 4) reduce_store(ntiles - 1, 16 * w + lane);
   if (p.hist == nullptr || min(p.k, ns) == ns) return;   // every position is selected: no histogram
   __syncthreads();
   publish_hist<kThreads>(s_hist, p.hist + static_cast<int64_t>(u) * kHistBins);
