@@ -209,7 +209,12 @@ int sparse_chunk(int64_t units, int nrb, int k) {
 // work-group three fit on a CU instead of two, which took the sweep from 57.1
 // to 54.8 us at head128k, 23.2 to 21.3 at gqa32k and 218.6 to 188.1 us on the
 // ragged batch (interleaved A/B; 3 stages: 56.0, 22.1, 217.8).
-constexpr int kScoreRounds = 2;
+// Score work-groups per CU: the sweep holds 160 VGPRs (three waves per SIMD)
+// and 39 KiB of LDS (46 KiB paged), so three fit. Filling all three with a
+// chunk that is any multiple of 64 took the sweep from 58.4 to 56.4 us at
+// head128k and 48.4 to 45.9 us at mha64k against power-of-two chunks at two
+// per CU (interleaved A/B, bit-identical).
+constexpr int kScoreWgsPerCu = 3;
 constexpr int kExactStagesSplit = 3;
 constexpr int kExactStagesAll = 4;
 template <int D>
@@ -525,13 +530,24 @@ mage_status launch_select(const Dims& d, const uint16_t* q, const KvArgs& kv, in
   sp.scores = scores ? scores : at<float>(ws, L.scores);
   sp.stride = scores ? score_stride : kv.max_n;
   sp.S = d.S; sp.B = d.B; sp.Hq = d.Hq; sp.Hkv = d.Hkv; sp.G = d.G; sp.R = d.R;
-  // positions per work-group: halved from kScoreChunk (down to kScoreChunkMin)
-  // until the sweep has kScoreRounds work-groups per CU
-  sp.chunk = kScoreChunk;
-  const int score_rounds = env_int("MAGE_SCORE_ROUNDS", kScoreRounds);
-  for (int64_t g = 0; sp.chunk > kScoreChunkMin; sp.chunk /= 2) {
-    chunk_map(kv, d, sp.chunk, g);
-    if (g >= score_rounds * kCus) break;
+  // positions per work-group: the smallest multiple of 64 in [kScoreChunkMin,
+  // kScoreChunk] whose grid fits kScoreWgsPerCu work-groups per CU, so the
+  // sweep runs as one round with every CU holding as many as fit
+  {
+    int lo = kScoreChunkMin, hi = kScoreChunk;
+    const int64_t target = static_cast<int64_t>(env_int("MAGE_SCORE_PER_CU", kScoreWgsPerCu)) * kCus;
+    int64_t g = 0;
+    chunk_map(kv, d, lo, g);
+    if (g <= target) {
+      hi = lo;
+    } else {
+      while (hi - lo > 64) {   // g(lo) > target
+        const int mid = (lo + hi) / 2 / 64 * 64;
+        chunk_map(kv, d, mid, g);
+        (g > target ? lo : hi) = mid;
+      }
+    }
+    sp.chunk = hi;
   }
   sp.nchunk = static_cast<int>(cdiv(kv.max_n, sp.chunk));
   sp.reverse = env_int("MAGE_SCORE_REVERSE", 1);
@@ -541,6 +557,11 @@ mage_status launch_select(const Dims& d, const uint16_t* q, const KvArgs& kv, in
   sp.map = chunk_map(kv, d, sp.chunk, score_grid);
   const void* score_fn = kv.src.page_table ? kfn(score_kernel<D, kScoreStagesFor<D>, true>)
                                             : kfn(score_kernel<D, kScoreStagesFor<D>, false>);
+#ifdef MAGE_TUNING
+  if (env_int("MAGE_SCORE_LEAN", 0))
+    score_fn = kv.src.page_table ? kfn(score_kernel<D, kScoreStagesFor<D>, true, true>)
+                                 : kfn(score_kernel<D, kScoreStagesFor<D>, false, true>);
+#endif
   if (mage_status st = launch(score_fn, "score_kernel", score_grid, kThreads, sel, sp); st != MAGE_OK)
     return st;
   if (main_topk) {
