@@ -339,9 +339,10 @@ __device__ __forceinline__ void attend_half(uint32_t k_base, uint32_t v_addr,
 // barrier per tile. The loop is software-pipelined: in iteration t a wave
 // issues the QK product of tile t+1 and then runs the softmax and PV of tile
 // t, so the MFMAs of one tile run under the vector work of the other.
-// kSplitIssue (contiguous caches only): the tile loads are issued by the four
-// key-half-1 waves; else (paged caches) every wave issues its own slices.
-template <int D, int kStages, bool kSplitIssue = true>
+// kSplitIssue: the tile loads are issued by the four key-half-1 waves; else
+// every wave issues its own slices (kept for measurements). kPagedForm: the
+// kernel reads paged caches (the chunk's page list is staged in LDS).
+template <int D, int kStages, bool kSplitIssue, bool kPagedForm>
 __global__ __launch_bounds__(kAttnThreads) void exact_chunk_kernel(AttnParams p) {
   using G = TileGeom<D, kAttnThreads>;
   constexpr int kNdb = D / 32, kNks = D / 16;
@@ -349,7 +350,7 @@ __global__ __launch_bounds__(kAttnThreads) void exact_chunk_kernel(AttnParams p)
   static_assert(2 * kStages * G::kBytes >= 4 * kWave * (2 + 16 * kNdb) * 4, "pair-merge area");
   // K ring (kStages tiles) followed by the V ring (kStages tiles)
   __shared__ __attribute__((aligned(1024))) uint8_t s_ring[2 * kStages * G::kBytes];
-  __shared__ int32_t s_pages[kSplitIssue ? 1 : kMaxChunkPages];   // paged layout: page ids of the chunk
+  __shared__ int32_t s_pages[kPagedForm ? kMaxChunkPages : 1];   // paged layout: page ids of the chunk
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -367,7 +368,7 @@ __global__ __launch_bounds__(kAttnThreads) void exact_chunk_kernel(AttnParams p)
   if (e0 >= e1) return;  // chunk past this sequence's end
   const int nrb = (p.R + 31) >> 5;
   const bool computes = rb < nrb;
-  const bool paged = !kSplitIssue && p.kv.page_table != nullptr;   // the split-issue form is contiguous only
+  const bool paged = kPagedForm && p.kv.page_table != nullptr;
   const int pshift = p.kv.page_shift, pmask = (1 << p.kv.page_shift) - 1;
   const int64_t seq_base = paged ? 0 : (static_cast<int64_t>(s) * p.Hkv + h) * p.kv.n_uniform;
   const int32_t* ptab = paged ? p.kv.page_table + static_cast<int64_t>(s) * p.kv.max_pages : nullptr;
@@ -471,9 +472,7 @@ __global__ __launch_bounds__(kAttnThreads) void exact_chunk_kernel(AttnParams p)
   // wave of each key half, so while one issues the next tiles the other is
   // already in its MFMA region. The per-lane offsets of the slices of waves
   // w - 4 and w are equal for K and kInstr d blocks apart for V.
-  // (kSplitIssue false, used for paged caches: every wave issues its own
-  // slices, since each slice's base needs a page-table lookup and one wave
-  // doing twice as many serializes them)
+  // (kSplitIssue false: every wave issues its own slices)
   constexpr bool split_issue = kSplitIssue;
   const bool issuer = !split_issue || w >= 4;
   uint32_t koff[G::kInstr], voff[G::kInstr];
@@ -577,28 +576,30 @@ __global__ __launch_bounds__(kAttnThreads) void exact_chunk_kernel(AttnParams p)
     for (int i = 0; i < kSlices; ++i)
       dma16x2<true>(kt, k_lane[i], lk + lds_slice[i], vt, v_lane_dma[i], lv + lds_slice[i]);
   };
-  // Steady state of the paged form (every wave issues its own slices; pages
-  // of >= 16 rows and a chunk that starts on a 64-row boundary, so each
-  // slice's rows lie in one page): the page ids of the wave's slices are read
-  // from the chunk's page list in one batch, behind one wait, and each
-  // slice's address is then scalar arithmetic. The general path waits for one
-  // page-list read per slice, each queued behind the other waves' fragment
-  // reads.
+  // Steady state of the paged form (pages of >= 16 rows and a chunk that
+  // starts on a 64-row boundary, so each slice's rows lie in one page): the
+  // page ids of an issuing wave's slices are read from the chunk's page list
+  // in one batch, behind one wait, and each slice's address is then scalar
+  // arithmetic. The general path waits for one page-list read per slice, each
+  // queued behind the other waves' fragment reads.
   auto issue_steady_paged = [&](int tk, uint32_t lk, uint32_t lv) __attribute__((always_inline)) {
+    if (!issuer) return;
     const int bk = e0 + tk * kTileKeys, bv = bk - 2 * kTileKeys;   // rows of tiles tk and tk - 2
-    int pk[G::kInstr], pv[G::kInstr];
+    int pk[kSlices], pv[kSlices];
 #pragma unroll
-    for (int j = 0; j < G::kInstr; ++j) {
-      const int slot = w * G::kInstr + j;
-      pk[j] = s_pages[((bk + slot * kKRowsPerInstr) >> pshift) - page0];
-      pv[j] = s_pages[((bv + ((slot & 3) << 4)) >> pshift) - page0];
+    for (int i = 0; i < kSlices; ++i) {
+      const int ws = split_issue ? (w & 3) + 4 * (i / G::kInstr) : w;
+      const int slot = ws * G::kInstr + i % G::kInstr;
+      pk[i] = s_pages[((bk + slot * kKRowsPerInstr) >> pshift) - page0];
+      pv[i] = s_pages[((bv + ((slot & 3) << 4)) >> pshift) - page0];
     }
-    const uint32_t vadd = w >= 4 ? static_cast<uint32_t>(G::kInstr * 32 * 2) : 0u;
 #pragma unroll
-    for (int j = 0; j < G::kInstr; ++j) {
-      const int slot = w * G::kInstr + j;
+    for (int i = 0; i < kSlices; ++i) {
+      const int ws = split_issue ? (w & 3) + 4 * (i / G::kInstr) : w;
+      const int j = i % G::kInstr, slot = ws * G::kInstr + j;
+      const uint32_t vadd = ws >= 4 ? static_cast<uint32_t>(G::kInstr * 32 * 2) : 0u;
       const int rk = bk + slot * kKRowsPerInstr, rv = bv + ((slot & 3) << 4);
-      const int64_t pgk = __builtin_amdgcn_readfirstlane(pk[j]), pgv = __builtin_amdgcn_readfirstlane(pv[j]);
+      const int64_t pgk = __builtin_amdgcn_readfirstlane(pk[i]), pgv = __builtin_amdgcn_readfirstlane(pv[i]);
       const int64_t ka = (((pgk * p.Hkv + h) << pshift) + (rk & pmask)) * G::kRowBytes;
       const int64_t va = (((pgv * p.Hkv + h) << pshift) + (rv & pmask)) * G::kRowBytes;
       dma16x2<true>(kbytes + ka, koff[j], lk + slot * 1024, vbytes + va, voff[j] + vadd, lv + slot * 1024);
@@ -670,10 +671,10 @@ __global__ __launch_bounds__(kAttnThreads) void exact_chunk_kernel(AttnParams p)
     if constexpr (decltype(steady)::value) {
       const int m0 = kPh >= 0 ? kPh : t % kStages;   // K tile t + kStages; V tile t + kStages - 2
       const uint32_t lk = k_slot_m(m0), lv = v_slot_m((m0 + kStages - 2) % kStages);
-      if constexpr (split_issue)
-        issue_steady(t + kStages, lk, lv);
-      else
+      if (paged)
         issue_steady_paged(t + kStages, lk, lv);
+      else
+        issue_steady(t + kStages, lk, lv);
     } else {
       issue(group_k(t + kStages - 1), group_v(t + kStages - 1));
     }
@@ -759,7 +760,7 @@ __global__ __launch_bounds__(kAttnThreads) void exact_chunk_kernel(AttnParams p)
   // t + kStages - 2) holds full tiles before the last take the steady issue,
   // unrolled by kStages from t = 1 so that each copy knows t mod kStages
   // (split issue: contiguous rows; every wave issuing: the paged form)
-  const bool steady_ok = split_issue || (paged && pshift >= 4 && (e0 & (kTileKeys - 1)) == 0);
+  const bool steady_ok = paged ? pshift >= 4 && (e0 & (kTileKeys - 1)) == 0 : split_issue;
   if (steady_ok) {
     for (; t + 2 * kStages - 1 < last_t; t += kStages) {
       middle(t, std::false_type{}, std::true_type{}, std::integral_constant<int, 1 % kStages>{});

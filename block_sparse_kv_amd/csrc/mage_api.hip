@@ -200,12 +200,14 @@ int sparse_chunk(int64_t units, int nrb, int k) {
 }
 
 // LDS ring depth of the exact pass: 3 stages of K+V tiles (3 x 32 KiB at
-// d = 128) when half the waves issue the loads (contiguous caches), 4 when
-// every wave does (paged caches). In interleaved A/Bs 3 stages took 116.4
-// against 118.4 us at head128k (98.6 / 100.7 at mha64k, 37.4 / 39.1 at
-// gqa32k): the issuing waves block less on a fuller load queue. On the paged
-// ragged batch 3 stages took 451 against 424 us. The score sweep streams K
-// only, through 2 stages (2 x 16 KiB at d = 128): with 48 KiB of LDS per
+// d = 128), with the tile loads issued by half the waves, for contiguous and
+// paged caches alike. Once the steady loop issued full tiles from fixed
+// per-lane offsets (contiguous) or one batch of page-list reads (paged), this
+// took the paged ragged batch to 350.7 us, against 361.4 us with every wave
+// issuing through a 4-stage ring (359.9 split with 4 stages, 352.2 every wave
+// with 3; interleaved A/B, bit-identical); contiguous caches had measured
+// 116.4 against 118.4 us at head128k for 3 against 4 stages. The score
+// sweep streams K only, through 2 stages (2 x 16 KiB at d = 128): with 48 KiB of LDS per
 // work-group three fit on a CU instead of two, which took the sweep from 57.1
 // to 54.8 us at head128k, 23.2 to 21.3 at gqa32k and 218.6 to 188.1 us on the
 // ragged batch (interleaved A/B; 3 stages: 56.0, 22.1, 217.8).
@@ -215,8 +217,7 @@ int sparse_chunk(int64_t units, int nrb, int k) {
 // head128k and 48.4 to 45.9 us at mha64k against power-of-two chunks at two
 // per CU (interleaved A/B, bit-identical).
 constexpr int kScoreWgsPerCu = 3;
-constexpr int kExactStagesSplit = 3;
-constexpr int kExactStagesAll = 4;
+constexpr int kExactStages = 3;
 template <int D>
 constexpr int kScoreStagesFor = 2;
 constexpr int kSparseStages = 2;
@@ -475,16 +476,15 @@ mage_status launch_select(const Dims& d, const uint16_t* q, const KvArgs& kv, in
   ap.zero_hist = main_topk ? at<uint32_t>(ws, L.hist) : nullptr;
   ap.zero_count = main_topk ? at<uint32_t>(ws, L.topk_arrivals) : nullptr;
   // contiguous caches: tile loads issued by half the waves; paged: by all
-  const void* exact_fn = kv.src.page_table ? kfn(exact_chunk_kernel<D, kExactStagesAll, false>)
-                                           : kfn(exact_chunk_kernel<D, kExactStagesSplit, true>);
+  const void* exact_fn = kv.src.page_table ? kfn(exact_chunk_kernel<D, kExactStages, true, true>)
+                                           : kfn(exact_chunk_kernel<D, kExactStages, true, false>);
 #ifdef MAGE_TUNING
-  if (!kv.src.page_table) {
-    switch (env_int("MAGE_EXACT_MODE", 0)) {
-      case 1: exact_fn = kfn(exact_chunk_kernel<D, 3, false>); break;
-      case 2: exact_fn = kfn(exact_chunk_kernel<D, 4, false>); break;
-      case 3: exact_fn = kfn(exact_chunk_kernel<D, 4, true>); break;
-      default: break;
-    }
+  switch (env_int("MAGE_EXACT_MODE", 0)) {   // every wave issues its own slices (4 or 3 stages)
+    case 1: exact_fn = kv.src.page_table ? kfn(exact_chunk_kernel<D, 4, false, true>)
+                                         : kfn(exact_chunk_kernel<D, 4, false, false>); break;
+    case 2: exact_fn = kv.src.page_table ? kfn(exact_chunk_kernel<D, 3, false, true>)
+                                         : kfn(exact_chunk_kernel<D, 3, false, false>); break;
+    default: break;
   }
 #endif
   if (mage_status st = launch(exact_fn, "exact_chunk_kernel", exact_grid, kAttnThreads, attn, ap); st != MAGE_OK)
