@@ -276,7 +276,10 @@ __device__ __forceinline__ void softmax_half(f32x16 sacc, uint32_t okm, float sc
       bf2 h;
       h.x = static_cast<__bf16>(x0);
       h.y = static_cast<__bf16>(x1);
-      const uint32_t hb = __builtin_bit_cast(uint32_t, h);
+      uint32_t hb = __builtin_bit_cast(uint32_t, h);
+      // hidden from the compiler, which otherwise converts x0 a second time to
+      // form the first term's fp32 value instead of shifting the packed word
+      asm volatile("" : "+v"(hb));
       bf2 l;
       l.x = static_cast<__bf16>(x0 - __uint_as_float(hb << 16));
       l.y = static_cast<__bf16>(x1 - __uint_as_float(hb & 0xffff0000u));
