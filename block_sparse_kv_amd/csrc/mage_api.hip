@@ -557,11 +557,6 @@ mage_status launch_select(const Dims& d, const uint16_t* q, const KvArgs& kv, in
   sp.map = chunk_map(kv, d, sp.chunk, score_grid);
   const void* score_fn = kv.src.page_table ? kfn(score_kernel<D, kScoreStagesFor<D>, true>)
                                             : kfn(score_kernel<D, kScoreStagesFor<D>, false>);
-#ifdef MAGE_TUNING
-  if (env_int("MAGE_SCORE_LEAN", 0))
-    score_fn = kv.src.page_table ? kfn(score_kernel<D, kScoreStagesFor<D>, true, true>)
-                                 : kfn(score_kernel<D, kScoreStagesFor<D>, false, true>);
-#endif
   if (mage_status st = launch(score_fn, "score_kernel", score_grid, kThreads, sel, sp); st != MAGE_OK)
     return st;
   if (main_topk) {

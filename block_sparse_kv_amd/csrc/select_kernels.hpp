@@ -137,11 +137,8 @@ constexpr int kStatBatch = 16;         // chunk statistics merged per batch (as 
 // The K tiles are loaded non-temporally (this sweep is their last use in the
 // step). kPaged: the chunk's page ids are staged in LDS; the contiguous form
 // leaves that table out, which lets four work-groups share a CU.
-// kLean: the two 32-key halves of a tile are read and multiplied one after
-// the other (half the K fragment registers), which fits the kernel in 128
-// VGPRs and four work-groups (16 waves) on a CU.
-template <int D, int kStages, bool kPaged, bool kLean = false>
-__global__ __launch_bounds__(kThreads, kLean ? 4 : 1) void score_kernel(ScoreParams p) {
+template <int D, int kStages, bool kPaged>
+__global__ __launch_bounds__(kThreads) void score_kernel(ScoreParams p) {
   using G = TileGeom<D>;
   constexpr int kNks = D / 16;
   constexpr bool kNt = true;
@@ -299,31 +296,18 @@ __global__ __launch_bounds__(kThreads, kLean ? 4 : 1) void score_kernel(ScorePar
     const uint32_t k_base = ring_base + (t % kStages) * G::kBytes;
     if (computes) {
       f32x16 acc[2];
-      if constexpr (kLean) {
+      bf16x8 kf[2][kNks];
+      // both halves' fragment reads go out together; each product starts
+      // when its own fragments have landed
+      k_frags_lds<D>(k_base, kofs, kf[0]);
+      k_frags_lds<D>(k_base + 32 * G::kRowBytes, kofs, kf[1]);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          bf16x8 kf[kNks];
-          k_frags_lds<D>(k_base + kb * 32 * G::kRowBytes, kofs, kf);
+      for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-          for (int i = 0; i < 16; ++i) acc[kb][i] = 0.f;
+        for (int i = 0; i < 16; ++i) acc[kb][i] = 0.f;
 #pragma unroll
-          for (int ks = 0; ks < kNks; ++ks)
-            acc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[ks], kf[ks], acc[kb], 0, 0, 0);
-        }
-      } else {
-        bf16x8 kf[2][kNks];
-        // both halves' fragment reads go out together; each product starts
-        // when its own fragments have landed
-        k_frags_lds<D>(k_base, kofs, kf[0]);
-        k_frags_lds<D>(k_base + 32 * G::kRowBytes, kofs, kf[1]);
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) acc[kb][i] = 0.f;
-#pragma unroll
-          for (int ks = 0; ks < kNks; ++ks)
-            acc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[ks], kf[kb][ks], acc[kb], 0, 0, 0);
-        }
+        for (int ks = 0; ks < kNks; ++ks)
+          acc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[ks], kf[kb][ks], acc[kb], 0, 0, 0);
       }
       // S[row][key 32kb + n]; sum the probabilities of this wave's 32 rows
 #pragma unroll
