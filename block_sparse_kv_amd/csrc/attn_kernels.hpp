@@ -34,6 +34,7 @@ struct AttnParams {
   float* part_o;            // partial O, MFMA accumulator order, per (unit, chunk)
   float* part_ml;           // partial (max, sum) per (unit, chunk, row)
   int32_t S, B, Hq, Hkv, G, R;
+  int32_t gs, g0;           // query-head stride and sub-group offset (q_head); 0, 0 when unsplit
   int32_t chunk;            // keys (exact) or idx entries (sparse) per work-group
   int32_t nchunk;           // chunks per unit in the grid
   float scale_log2;         // scale * log2(e)
@@ -57,6 +58,7 @@ struct MergeParams {
   float* o;
   float* lse;               // nullable
   int32_t S, B, Hq, Hkv, G, R, nrb;
+  int32_t gs, g0;           // query-head stride and sub-group offset (q_head)
   int32_t chunk, nchunk;
   int32_t n_uniform;        // >= 0: entries per unit (prefix length or idx count); < 0: lens
   SeqLens lens;
@@ -397,7 +399,7 @@ __global__ __launch_bounds__(kAttnThreads) void exact_chunk_kernel(AttnParams p)
     const int r = 32 * rb + n;
     if (computes && r < p.R) {
       const int b = r / p.G, g = r - b * p.G;
-      const uint16_t* qrow = p.q + ((static_cast<int64_t>(s) * p.B + b) * p.Hq + h * p.G + g) * D;
+      const uint16_t* qrow = p.q + ((static_cast<int64_t>(s) * p.B + b) * p.Hq + q_head(h, g, p.G, p.gs, p.g0)) * D;
 #pragma unroll
       for (int ks = 0; ks < kNks; ++ks)
         qf[ks] = __builtin_bit_cast(bf16x8, load16(qrow + 16 * ks + 8 * hh));
@@ -971,7 +973,7 @@ __global__ __launch_bounds__(kSparseThreads) void sparse_attn_kernel(AttnParams 
     const int r = 32 * rb + n;
     if (r < p.R) {
       const int b = r / p.G, gg = r - b * p.G;
-      const uint16_t* qrow = p.q + ((static_cast<int64_t>(s) * p.B + b) * p.Hq + h * p.G + gg) * D;
+      const uint16_t* qrow = p.q + ((static_cast<int64_t>(s) * p.B + b) * p.Hq + q_head(h, gg, p.G, p.gs, p.g0)) * D;
 #pragma unroll
       for (int ks = 0; ks < kNks; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, load16(qrow + 16 * ks + 8 * hh));
     } else {
@@ -1096,7 +1098,7 @@ __global__ __launch_bounds__(kSparseThreads) void sparse_attn_kernel(AttnParams 
     }
     if (direct) {
       if (r >= p.R) return;
-      const int b = r / p.G, gg = r - b * p.G, j = h * p.G + gg;
+      const int b = r / p.G, gg = r - b * p.G, j = q_head(h, gg, p.G, p.gs, p.g0);
       const int64_t row = (static_cast<int64_t>(s) * p.B + b) * p.Hq + j;
       const float inv = L > 0.f ? 1.f / L : 0.f;
       float* orow = p.o + row * D + 32 * db + 4 * hh;
@@ -1151,7 +1153,7 @@ __global__ __launch_bounds__(kSparseThreads) void sparse_attn_kernel(AttnParams 
                                                rb, db, i40, lane, r, M, L, acc);
   if (r < p.R) {
     const int b = r / p.G, gg = r - b * p.G;
-    const int64_t row = (static_cast<int64_t>(s) * p.B + b) * p.Hq + h * p.G + gg;
+    const int64_t row = (static_cast<int64_t>(s) * p.B + b) * p.Hq + q_head(h, gg, p.G, p.gs, p.g0);
     const float inv = L > 0.f ? 1.f / L : 0.f;
 #pragma unroll
     for (int q = 0; q < kTasks; ++q)
@@ -1199,7 +1201,7 @@ __global__ __launch_bounds__(kThreads) void exact_merge_kernel(MergeParams p) {
   merge_chunks<D, kBatch, 1, false>(p.part_o, p.part_ml, slot0, nch, w, db, i4, lane, r, M, L, accs);
   const f32x4 acc = accs[0];
   if (r >= p.R) return;
-  const int b = r / p.G, g = r - b * p.G, j = h * p.G + g;
+  const int b = r / p.G, g = r - b * p.G, j = q_head(h, g, p.G, p.gs, p.g0);
   const int64_t row = (static_cast<int64_t>(s) * p.B + b) * p.Hq + j;
   const float inv = L > 0.f ? 1.f / L : 0.f;
   f32x4 v{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};

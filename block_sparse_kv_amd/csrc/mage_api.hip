@@ -78,7 +78,29 @@ const void* kfn(K* kernel) {
 struct Dims {
   int S, B, Hq, Hkv, G, R, D, nrb, units;
   float scale;
+  int ng;        // sub-groups the head group runs in (1: not split)
+  int gs, g0;    // query-head stride and first head of a sub-group (q_head); 0, 0 when unsplit
+  int r_total;   // rows of the whole head group (the score's average)
 };
+
+// Sub-group grp of a split head group: G / ng query heads per KV head, at
+// most kMaxRows rows, run like an unsplit call.
+Dims group_dims(const Dims& d, int grp) {
+  Dims g = d;
+  g.G = d.G / d.ng;
+  g.R = d.B * g.G;
+  g.nrb = (g.R + 31) / 32;
+  g.ng = 1;
+  g.gs = d.G;
+  g.g0 = grp * g.G;
+  g.r_total = d.R;
+  return g;
+}
+
+mage_status one_group(const Dims& d) {
+  return d.ng == 1 ? MAGE_OK
+                   : fail(MAGE_ERR_UNSUPPORTED, "block * (num_q_heads / num_kv_heads) must be <= 128 for this call");
+}
 
 mage_status check_dims(const mage_dims* d, Dims& o) {
   if (!d) return fail(MAGE_ERR_INVALID_ARG, "dims is null");
@@ -95,8 +117,11 @@ mage_status check_dims(const mage_dims* d, Dims& o) {
   o.Hq = d->num_q_heads;
   o.Hkv = d->num_kv_heads;
   o.G = o.Hq / o.Hkv;
-  if (static_cast<int64_t>(o.B) * o.G > MAGE_MAX_ROWS)
-    return fail(MAGE_ERR_UNSUPPORTED, "block * (num_q_heads / num_kv_heads) must be <= 128");
+  if (o.B > MAGE_MAX_ROWS) return fail(MAGE_ERR_UNSUPPORTED, "block must be <= 128");
+  // more than MAGE_MAX_ROWS rows per KV head: the fewest equal sub-groups of
+  // heads that fit (ng = G always does)
+  o.ng = 1;
+  while (o.G % o.ng != 0 || static_cast<int64_t>(o.B) * (o.G / o.ng) > MAGE_MAX_ROWS) ++o.ng;
   if (static_cast<int64_t>(o.S) * o.Hkv > (1 << 20))
     return fail(MAGE_ERR_UNSUPPORTED, "num_seqs * num_kv_heads must be <= 2^20");
   o.R = o.B * o.G;
@@ -104,6 +129,9 @@ mage_status check_dims(const mage_dims* d, Dims& o) {
   o.nrb = (o.R + 31) / 32;
   o.units = o.S * o.Hkv;
   o.scale = d->scale;
+  o.gs = 0;
+  o.g0 = 0;
+  o.r_total = o.R;
   return MAGE_OK;
 }
 
@@ -445,7 +473,40 @@ template <int D>
 mage_status launch_select(const Dims& d, const uint16_t* q, const KvArgs& kv, int32_t k, float* o,
                           float* lse, int32_t* idx, float* scores, int64_t score_stride, void* ws,
                           const Layout& L, hipStream_t attn, hipStream_t sel, hipEvent_t idx_ready,
-                          const PagePlan* pages = nullptr, const BudgetPlan* budget = nullptr) {
+                          const PagePlan* pages = nullptr, const BudgetPlan* budget = nullptr,
+                          int group_pass = 0) {
+  if (d.ng > 1) {
+    // A head group of more than kMaxRows rows runs as sub-groups, one after
+    // another on attn (each reuses the workspace's partials): every sub-group's
+    // exact pass, merge and score sweep, the sweeps adding into one score row
+    // per unit; the last one builds the histogram and runs the top-k.
+    if (pages || budget) return one_group(d);
+    for (int grp = 0; grp < d.ng; ++grp) {
+      const int pass = (grp > 0 ? 1 : 0) | (grp == d.ng - 1 ? 2 : 0);
+      if (mage_status st = launch_select<D>(group_dims(d, grp), q, kv, k, o, lse, idx, scores, score_stride, ws, L,
+                                            attn, attn, nullptr, nullptr, nullptr, pass);
+          st != MAGE_OK)
+        return st;
+    }
+    if (k > 0 && sel && sel != attn) {
+      hipEvent_t ev = internal_event();
+      if (!ev) return fail(MAGE_ERR_HIP, "could not create the stream-ordering event");
+      if (hipError_t e = hipEventRecord(ev, attn); e != hipSuccess) return hip_fail(e, "hipEventRecord");
+      if (hipError_t e = hipStreamWaitEvent(sel, ev, 0); e != hipSuccess)
+        return hip_fail(e, "hipStreamWaitEvent");
+    } else {
+      sel = attn;
+    }
+    if (k > 0 && idx_ready) {
+      if (hipError_t e = hipEventRecord(idx_ready, sel); e != hipSuccess)
+        return hip_fail(e, "hipEventRecord(idx_ready)");
+    }
+    return MAGE_OK;
+  }
+  // group_pass (sub-groups of a split head group): bit 0 = add to the stored
+  // scores, bit 1 = the last sub-group (histogram and top-k); 0 = unsplit
+  const bool add_scores = (group_pass & 1) != 0;
+  const bool last_group = group_pass == 0 || (group_pass & 2) != 0;
   const int64_t U = d.units;
   const int chunk = exact_chunk(U, kv.max_n, kv.total_keys, kv.src.page_table ? (1 << kv.src.page_shift) : 0,
                                 kv.src.page_table ? kv.lens.n : nullptr, d.S, d.Hkv);
@@ -464,6 +525,7 @@ mage_status launch_select(const Dims& d, const uint16_t* q, const KvArgs& kv, in
   ap.part_o = at<float>(ws, L.part_o);
   ap.part_ml = at<float>(ws, L.part_ml);
   ap.S = d.S; ap.B = d.B; ap.Hq = d.Hq; ap.Hkv = d.Hkv; ap.G = d.G; ap.R = d.R;
+  ap.gs = d.gs; ap.g0 = d.g0;
   ap.chunk = chunk;
   ap.nchunk = nch;
   ap.scale_log2 = scale_log2;
@@ -509,6 +571,7 @@ mage_status launch_select(const Dims& d, const uint16_t* q, const KvArgs& kv, in
   mp.o = o;
   mp.lse = lse;
   mp.S = d.S; mp.B = d.B; mp.Hq = d.Hq; mp.Hkv = d.Hkv; mp.G = d.G; mp.R = d.R; mp.nrb = d.nrb;
+  mp.gs = d.gs; mp.g0 = d.g0;
   mp.chunk = chunk;
   mp.nchunk = nch;
   mp.n_uniform = kv.src.page_table ? -1 : kv.src.n_uniform;
@@ -525,11 +588,14 @@ mage_status launch_select(const Dims& d, const uint16_t* q, const KvArgs& kv, in
   sp.part_ml = ap.part_ml;
   sp.exact_chunk = chunk;
   sp.exact_nchunk = nch;
-  sp.hist = main_topk ? at<uint32_t>(ws, L.hist) : nullptr;
+  sp.hist = main_topk && last_group ? at<uint32_t>(ws, L.hist) : nullptr;
   sp.k = k;
   sp.scores = scores ? scores : at<float>(ws, L.scores);
   sp.stride = scores ? score_stride : kv.max_n;
   sp.S = d.S; sp.B = d.B; sp.Hq = d.Hq; sp.Hkv = d.Hkv; sp.G = d.G; sp.R = d.R;
+  sp.gs = d.gs; sp.g0 = d.g0;
+  sp.r_total = d.r_total;
+  sp.accumulate = add_scores ? 1 : 0;
   // positions per work-group: the smallest multiple of 64 in [kScoreChunkMin,
   // kScoreChunk] whose grid fits kScoreWgsPerCu work-groups per CU, so the
   // sweep runs as one round with every CU holding as many as fit
@@ -559,6 +625,7 @@ mage_status launch_select(const Dims& d, const uint16_t* q, const KvArgs& kv, in
                                             : kfn(score_kernel<D, kScoreStagesFor<D>, false>);
   if (mage_status st = launch(score_fn, "score_kernel", score_grid, kThreads, sel, sp); st != MAGE_OK)
     return st;
+  if (!last_group) return MAGE_OK;
   if (main_topk) {
     const TopkParams tp = topk_params(ws, L, sp.scores, sp.stride, idx, k, static_cast<int32_t>(U), d.Hkv,
                                       kv.src.page_table ? -1 : kv.src.n_uniform, kv.max_n, kv.lens, d.S);
@@ -660,6 +727,15 @@ mage_status launch_sparse(const Dims& d, const uint16_t* q, const KvArgs& kv, co
                           int32_t k, float* o, float* lse, void* ws, const Layout& L,
                           hipStream_t stream, const uint16_t* k_blk = nullptr,
                           const uint16_t* v_blk = nullptr, const int32_t* counts = nullptr, int32_t k_seq = 0) {
+  if (d.ng > 1) {
+    // a head group of more than kMaxRows rows: one launch per sub-group (in
+    // stream order, each reusing the workspace); the plain later step only
+    if (k_blk || counts) return one_group(d);
+    for (int grp = 0; grp < d.ng; ++grp)
+      if (mage_status st = launch_sparse<D>(group_dims(d, grp), q, kv, idx, k, o, lse, ws, L, stream); st != MAGE_OK)
+        return st;
+    return MAGE_OK;
+  }
   const int64_t U = d.units;
   int chunk = sparse_chunk(U, d.nrb, counts ? std::max(1, k_seq / d.Hkv) : k);
   int64_t seq_slots = 0;
@@ -690,6 +766,7 @@ mage_status launch_sparse(const Dims& d, const uint16_t* q, const KvArgs& kv, co
   ap.part_o = at<float>(ws, L.part_o);
   ap.part_ml = at<float>(ws, L.part_ml);
   ap.S = d.S; ap.B = d.B; ap.Hq = d.Hq; ap.Hkv = d.Hkv; ap.G = d.G; ap.R = d.R;
+  ap.gs = d.gs; ap.g0 = d.g0;
   ap.chunk = chunk;
   ap.nchunk = nch;
   ap.scale_log2 = d.scale * kLog2e;
@@ -715,6 +792,7 @@ mage_status launch_sparse(const Dims& d, const uint16_t* q, const KvArgs& kv, co
   mp.o = o;
   mp.lse = lse;
   mp.S = d.S; mp.B = d.B; mp.Hq = d.Hq; mp.Hkv = d.Hkv; mp.G = d.G; mp.R = d.R; mp.nrb = d.nrb;
+  mp.gs = d.gs; mp.g0 = d.g0;
   mp.chunk = chunk;
   mp.nchunk = nch;
   mp.n_uniform = k;  // every unit has k index entries (per-unit counts: at most k)
@@ -747,6 +825,7 @@ mage_status launch_mean_query_select(const Dims& d, const uint16_t* q, const KvA
   d1.G = 1;
   d1.R = 1;
   d1.nrb = 1;
+  d1.r_total = 1;
   return launch_select<D>(d1, mq.qbar, kv, k, at<float>(ws, L.qbar_o), nullptr, idx, scores, score_stride,
                           ws, L, stream, nullptr, nullptr);
 }
@@ -958,6 +1037,7 @@ mage_status mage_select_mean_query(const mage_dims* dims, const uint16_t* q, con
   CallScope scope;
   Dims d;
   if (mage_status st = check_dims(dims, d); st != MAGE_OK) return st;
+  if (mage_status st = one_group(d); st != MAGE_OK) return st;
   if (mage_status st = mean_query_checks(q, k, idx, scores); st != MAGE_OK) return st;
   KvArgs kv;
   if (mage_status st = contiguous_kv(d, k_cache, v_cache, seq_len, kv); st != MAGE_OK) return st;
@@ -973,6 +1053,7 @@ mage_status mage_select_mean_query_paged(const mage_dims* dims, const uint16_t* 
   CallScope scope;
   Dims d;
   if (mage_status st = check_dims(dims, d); st != MAGE_OK) return st;
+  if (mage_status st = one_group(d); st != MAGE_OK) return st;
   if (mage_status st = mean_query_checks(q, k, idx, scores); st != MAGE_OK) return st;
   KvArgs kv;
   if (mage_status st = paged_kv(d, kvp, kv); st != MAGE_OK) return st;
@@ -1000,6 +1081,7 @@ mage_status mage_select_pages(const mage_dims* dims, const uint16_t* q, const ui
   CallScope scope;
   Dims d;
   if (mage_status st = check_dims(dims, d); st != MAGE_OK) return st;
+  if (mage_status st = one_group(d); st != MAGE_OK) return st;
   if (mage_status st = page_checks(q, page_tokens, k_pages, o, lse, idx, page_idx, scores); st != MAGE_OK)
     return st;
   KvArgs kv;
@@ -1021,6 +1103,7 @@ mage_status mage_select_pages_paged(const mage_dims* dims, const uint16_t* q, co
   CallScope scope;
   Dims d;
   if (mage_status st = check_dims(dims, d); st != MAGE_OK) return st;
+  if (mage_status st = one_group(d); st != MAGE_OK) return st;
   if (mage_status st = page_checks(q, page_tokens, k_pages, o, lse, idx, page_idx, scores); st != MAGE_OK)
     return st;
   KvArgs kv;
@@ -1042,6 +1125,7 @@ mage_status mage_select_adaptive(const mage_dims* dims, const uint16_t* q, const
   CallScope scope;
   Dims d;
   if (mage_status st = check_dims(dims, d); st != MAGE_OK) return st;
+  if (mage_status st = one_group(d); st != MAGE_OK) return st;
   if (mage_status st = common_select_checks(q, k, o, lse, idx, nullptr); st != MAGE_OK) return st;
   if (!counts || !aligned(counts, 4)) return fail(MAGE_ERR_INVALID_ARG, "counts must be non-null and 4-byte aligned");
   if (static_cast<int64_t>(k) * d.Hkv > MAGE_MAX_SPARSE_K)
@@ -1065,6 +1149,7 @@ mage_status mage_select_adaptive_paged(const mage_dims* dims, const uint16_t* q,
   CallScope scope;
   Dims d;
   if (mage_status st = check_dims(dims, d); st != MAGE_OK) return st;
+  if (mage_status st = one_group(d); st != MAGE_OK) return st;
   if (mage_status st = common_select_checks(q, k, o, lse, idx, nullptr); st != MAGE_OK) return st;
   if (!counts || !aligned(counts, 4)) return fail(MAGE_ERR_INVALID_ARG, "counts must be non-null and 4-byte aligned");
   if (static_cast<int64_t>(k) * d.Hkv > MAGE_MAX_SPARSE_K)
@@ -1085,6 +1170,7 @@ mage_status mage_mean_query(const mage_dims* dims, const uint16_t* q, uint16_t* 
   CallScope scope;
   Dims d;
   if (mage_status st = check_dims(dims, d); st != MAGE_OK) return st;
+  if (mage_status st = one_group(d); st != MAGE_OK) return st;
   if (!q || !qbar) return fail(MAGE_ERR_INVALID_ARG, "q and qbar must not be null");
   if (!aligned(q, 2) || !aligned(qbar, 2)) return fail(MAGE_ERR_INVALID_ARG, "q and qbar must be 2-byte aligned");
   MeanQueryParams mq{};
@@ -1142,6 +1228,7 @@ mage_status mage_sparse_attn_noalloc(const mage_dims* dims, const uint16_t* q, c
   CallScope scope;
   Dims d;
   if (mage_status st = sparse_common(dims, q, idx, k, o, lse, d); st != MAGE_OK) return st;
+  if (mage_status st = one_group(d); st != MAGE_OK) return st;
   KvArgs kv;
   if (mage_status st = contiguous_kv(d, k_cache, v_cache, seq_len, kv); st != MAGE_OK) return st;
   // the later step's part of the workspace layout, sized for this call's plan
@@ -1188,6 +1275,7 @@ mage_status mage_sparse_block_attn(const mage_dims* dims, const uint16_t* q, con
   CallScope scope;
   Dims d;
   if (mage_status st = sparse_common(dims, q, idx, k, o, lse, d); st != MAGE_OK) return st;
+  if (mage_status st = one_group(d); st != MAGE_OK) return st;
   if (mage_status st = block_rows_checks(k_blk, v_blk); st != MAGE_OK) return st;
   KvArgs kv;
   if (mage_status st = contiguous_kv(d, k_cache, v_cache, seq_len, kv); st != MAGE_OK) return st;
@@ -1204,6 +1292,7 @@ mage_status mage_sparse_block_attn_paged(const mage_dims* dims, const uint16_t* 
   CallScope scope;
   Dims d;
   if (mage_status st = sparse_common(dims, q, idx, k, o, lse, d); st != MAGE_OK) return st;
+  if (mage_status st = one_group(d); st != MAGE_OK) return st;
   if (mage_status st = block_rows_checks(k_blk, v_blk); st != MAGE_OK) return st;
   KvArgs kv;
   if (mage_status st = paged_kv(d, kvp, kv); st != MAGE_OK) return st;
@@ -1226,6 +1315,7 @@ mage_status mage_sparse_attn_counts(const mage_dims* dims, const uint16_t* q, co
   CallScope scope;
   Dims d;
   if (mage_status st = sparse_common(dims, q, idx, k_row, o, lse, d); st != MAGE_OK) return st;
+  if (mage_status st = one_group(d); st != MAGE_OK) return st;
   if (mage_status st = counts_checks(counts, k_seq); st != MAGE_OK) return st;
   KvArgs kv;
   if (mage_status st = contiguous_kv(d, k_cache, v_cache, seq_len, kv); st != MAGE_OK) return st;
@@ -1243,6 +1333,7 @@ mage_status mage_sparse_attn_counts_paged(const mage_dims* dims, const uint16_t*
   CallScope scope;
   Dims d;
   if (mage_status st = sparse_common(dims, q, idx, k_row, o, lse, d); st != MAGE_OK) return st;
+  if (mage_status st = one_group(d); st != MAGE_OK) return st;
   if (mage_status st = counts_checks(counts, k_seq); st != MAGE_OK) return st;
   KvArgs kv;
   if (mage_status st = paged_kv(d, kvp, kv); st != MAGE_OK) return st;
@@ -1259,6 +1350,7 @@ mage_status mage_block_attn(const mage_dims* dims, const uint16_t* q, const uint
   CallScope scope;
   Dims d;
   if (mage_status st = check_dims(dims, d); st != MAGE_OK) return st;
+  if (mage_status st = one_group(d); st != MAGE_OK) return st;
   if (!q || !k_blk || !v_blk || !o_prefix || !lse_prefix || !o)
     return fail(MAGE_ERR_INVALID_ARG, "q, k_blk, v_blk, o_prefix, lse_prefix and o must not be null");
   if (!aligned(q, 16) || !aligned(k_blk, 16) || !aligned(v_blk, 16) || !aligned(o_prefix, 16) || !aligned(o, 16))
@@ -1303,6 +1395,7 @@ mage_status mage_topk(int32_t rows, const float* scores, int64_t row_stride, con
   // workspace: the full layout for one KV head per row
   Dims d{};
   d.S = rows; d.B = 1; d.Hq = 1; d.Hkv = 1; d.G = 1; d.R = 1; d.D = 64; d.nrb = 1; d.units = rows;
+  d.ng = 1; d.gs = 0; d.g0 = 0; d.r_total = 1;
   d.scale = 1.f;
   const Layout L = make_layout(d, n, k);
   if (mage_status st = check_ws(workspace, workspace_bytes, L); st != MAGE_OK) return st;

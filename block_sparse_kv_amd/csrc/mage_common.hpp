@@ -22,6 +22,14 @@ constexpr int kMaxSeqs = 256;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// Query head of row (b, g) of KV head h: h * gs + g0 + g. A call whose head
+// group holds more than kMaxRows rows (block * group) runs in sub-groups of
+// G <= kMaxRows / block heads; gs is then the full group size and g0 the
+// sub-group's first head (gs = 0: the group is not split).
+__host__ __device__ __forceinline__ int q_head(int h, int g, int G, int gs, int g0) {
+  return h * (gs ? gs : G) + g0 + g;
+}
+
 // Host-side sequence table carried in kernel arguments (ragged paged batches).
 struct SeqLens {
   int32_t n[kMaxSeqs];

@@ -121,6 +121,9 @@ struct ScoreParams {
   uint32_t* hist;           // [S * Hkv][kHistBins], zero on entry: each row's score histogram (or null)
   int32_t k;                // rows with min(k, N_s) == N_s take no histogram
   int32_t S, B, Hq, Hkv, G, R;
+  int32_t gs, g0;           // query-head stride and sub-group offset (q_head)
+  int32_t r_total;          // rows the score averages over (R, or the whole group's when split)
+  int32_t accumulate;       // add to the scores already stored (later sub-groups of a split group)
   int32_t chunk, nchunk;
   int32_t reverse;          // sweep tiles last-to-first
   float scale_log2;
@@ -175,7 +178,7 @@ __global__ __launch_bounds__(kThreads) void score_kernel(ScoreParams p) {
     const int r = 32 * w + n;
     if (computes && r < p.R) {
       const int b = r / p.G, g = r - b * p.G;
-      const uint16_t* qrow = p.q + ((static_cast<int64_t>(s) * p.B + b) * p.Hq + h * p.G + g) * D;
+      const uint16_t* qrow = p.q + ((static_cast<int64_t>(s) * p.B + b) * p.Hq + q_head(h, g, p.G, p.gs, p.g0)) * D;
 #pragma unroll
       for (int ks = 0; ks < kNks; ++ks)
         qf[ks] = __builtin_bit_cast(bf16x8, load16(qrow + 16 * ks + 8 * hh));
@@ -187,7 +190,7 @@ __global__ __launch_bounds__(kThreads) void score_kernel(ScoreParams p) {
   uint32_t kofs[kNks];
   k_frag_offsets<D>(n, hh, kofs);
   const uint32_t ring_base = lds_addr(s_ring);
-  const float inv_r = 1.f / static_cast<float>(p.R);
+  const float inv_r = 1.f / static_cast<float>(p.r_total);
   for (int b = tid; b < kHistBins; b += kThreads) s_hist[b] = 0u;
   __syncthreads();
 
@@ -260,8 +263,10 @@ __global__ __launch_bounds__(kThreads) void score_kernel(ScoreParams p) {
     if (e < e1) {
       float sum = 0.f;
       for (int ww = 0; ww < nrb; ++ww) sum += s_col[t & 1][ww][col];
+      float* dst = p.scores + static_cast<int64_t>(u) * p.stride + e;
       sc = sum * inv_r;
-      p.scores[static_cast<int64_t>(u) * p.stride + e] = sc;
+      if (p.accumulate) sc = *dst + sc;
+      *dst = sc;
     }
     wave_hist_add(s_hist, hist_bin(__float_as_uint(sc)), e < e1);
   };

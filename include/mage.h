@@ -74,7 +74,8 @@ extern "C" {
 typedef enum mage_status {
   MAGE_OK = 0,
   MAGE_ERR_INVALID_ARG = 1,          /* null pointer, bad size, Hq % Hkv != 0 */
-  MAGE_ERR_UNSUPPORTED = 2,          /* d not in {64, 128}, R > 128, S > MAGE_MAX_SEQS (paged) */
+  MAGE_ERR_UNSUPPORTED = 2,          /* d not in {64, 128}, B > 128, R > 128 where a call
+                                        takes no split group, S > MAGE_MAX_SEQS (paged) */
   MAGE_ERR_WORKSPACE_TOO_SMALL = 3,
   MAGE_ERR_HIP = 4                   /* launch or runtime failure; see mage_last_error() */
 } mage_status;
@@ -82,14 +83,21 @@ typedef enum mage_status {
 /* Largest number of sequences one paged call takes (their lengths travel in
  * the kernel arguments). */
 #define MAGE_MAX_SEQS 256
-/* Largest R = B * G rows per KV head. */
+/* Largest R = B * G rows per KV head that one pass of the kernels takes.
+ * mage_select_exact, mage_exact_attn and mage_sparse_attn (and their _paged
+ * forms) take larger head groups: they run the G query heads of each KV head
+ * in the fewest equal sub-groups of at most MAGE_MAX_ROWS rows, one after
+ * another on the call's stream (every kernel of the call on `stream`; the
+ * select stream, when given, waits for the end), with the score averaged
+ * over all R rows before the top-k. Every other call returns
+ * MAGE_ERR_UNSUPPORTED for R > MAGE_MAX_ROWS. B <= MAGE_MAX_ROWS always. */
 #define MAGE_MAX_ROWS 128
 
 typedef struct mage_dims {
   int32_t num_seqs;      /* S >= 1 */
   int32_t block;         /* B >= 1, query tokens per block */
   int32_t num_q_heads;   /* Hq >= 1 */
-  int32_t num_kv_heads;  /* Hkv >= 1, Hq % Hkv == 0, B * Hq / Hkv <= 128 */
+  int32_t num_kv_heads;  /* Hkv >= 1, Hq % Hkv == 0 (R = B * Hq / Hkv: see MAGE_MAX_ROWS) */
   int32_t head_dim;      /* d in {64, 128} */
   float scale;           /* softmax scale applied to q.k (finite, > 0) */
 } mage_dims;

@@ -50,6 +50,9 @@ def test_workspace_bytes():
     assert mage.workspace_bytes(dims(head_dim=96), 1024, 64) == 0
     assert mage.workspace_bytes(dims(num_q_heads=30), 1024, 64) == 0
     assert mage.workspace_bytes(dims(), 0, 64) == 0
+    # R = 64 * 4 = 256 rows per KV head runs in two sub-groups on the same layout
+    assert mage.workspace_bytes(dims(block=64), 131072, 1024) == big
+    assert mage.workspace_bytes(dims(block=200), 1024, 64) == 0
     # every layout starts with the fixed 256 KiB arrival-counter region of the later steps
     tiny = mage.workspace_bytes(dims(block=1, num_q_heads=1, num_kv_heads=1, head_dim=64), 1, 1)
     assert tiny >= 16384 * 4 * 4
@@ -67,7 +70,7 @@ def call_select(d, n=1024, k=64, ws_bytes=1 << 40, q=FAKE, o=FAKE, idx=FAKE):
 @pytest.mark.parametrize("kw,status", [
     (dict(head_dim=96), mage.ERR_UNSUPPORTED),
     (dict(num_q_heads=30), mage.ERR_INVALID_ARG),
-    (dict(block=64), mage.ERR_UNSUPPORTED),           # R = 64 * 4 > 128
+    (dict(block=200), mage.ERR_UNSUPPORTED),          # B > 128 (R > 128 alone runs in sub-groups)
     (dict(num_seqs=0), mage.ERR_INVALID_ARG),
     (dict(scale=float("nan")), mage.ERR_INVALID_ARG),
     (dict(scale=-1.0), mage.ERR_INVALID_ARG),

@@ -107,6 +107,10 @@ SMALL = [
     workloads.custom((63, 64, 65, 129, 577), 8, 2, 128, 16, 64, paged=True, name="paged_edges"),
     workloads.custom((100, 1000), 8, 2, 128, 16, 64, paged=True, page_size=4, name="paged_p4"),
     workloads.custom((100, 3000), 8, 2, 128, 16, 64, paged=True, page_size=256, name="paged_p256"),
+    # head groups of more than 128 rows (B * G): run as sub-groups of query heads
+    workloads.custom((3000,), 16, 2, 128, 32, 300, name="r256_two_groups"),
+    workloads.custom((900, 2500), 24, 2, 64, 16, 128, paged=True, name="paged_r192_two_groups"),
+    workloads.custom((700,), 6, 2, 64, 100, 64, name="r300_three_groups"),
 ]
 
 
