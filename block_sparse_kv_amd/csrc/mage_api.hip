@@ -537,7 +537,7 @@ mage_status launch_select(const Dims& d, const uint16_t* q, const KvArgs& kv, in
   const bool main_topk = k > 0 && !pages && !budget;
   ap.zero_hist = main_topk ? at<uint32_t>(ws, L.hist) : nullptr;
   ap.zero_count = main_topk ? at<uint32_t>(ws, L.topk_arrivals) : nullptr;
-  // contiguous caches: tile loads issued by half the waves; paged: by all
+  // tile loads issued by half the waves through a 3-stage ring, contiguous and paged alike
   const void* exact_fn = kv.src.page_table ? kfn(exact_chunk_kernel<D, kExactStages, true, true>)
                                            : kfn(exact_chunk_kernel<D, kExactStages, true, false>);
 #ifdef MAGE_TUNING
