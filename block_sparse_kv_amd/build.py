@@ -19,6 +19,10 @@ FLAGS = [
     # keep packed-fp32 VALU instructions (v_pk_fma_f32 and kin) out of the code
     # object: the kernels are written and checked for scalar fp32 arithmetic
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in architectural VGPRs: the later step, score sweep and block
+    # attention otherwise keep their accumulators in AGPRs and copy them to VGPRs
+    # for every rescale and read (272 copies in the later step's loop at d=128)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", os.path.join(ROOT, "include"),
 ]
 
