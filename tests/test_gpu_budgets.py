@@ -46,6 +46,7 @@ CASES = [
     workloads.custom((150,), 8, 4, 128, 8, 64, name="budget_over_one_head"),
     workloads.custom((53, 200, 1000), 8, 2, 64, 4, 64, paged=True, name="paged_ragged"),
     workloads.custom((17, 4096, 900), 32, 8, 128, 32, 256, paged=True, name="paged_r128"),
+    workloads.custom((3000, 3000), 32, 8, 128, 32, 2000, name="wide_counts"),   # 1024-entry chunks
 ]
 
 

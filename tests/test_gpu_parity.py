@@ -111,6 +111,11 @@ SMALL = [
     workloads.custom((3000,), 16, 2, 128, 32, 300, name="r256_two_groups"),
     workloads.custom((900, 2500), 24, 2, 64, 16, 128, paged=True, name="paged_r192_two_groups"),
     workloads.custom((700,), 6, 2, 64, 100, 64, name="r300_three_groups"),
+    # long later-step chunks: four 512-entry chunks merged in the launch, the
+    # last one ragged (464 entries); and one unsplit 640-entry chunk per (unit,
+    # row block), 160 entries per wave, paged
+    workloads.custom((2500, 2500), 32, 8, 128, 32, 2000, name="wide_split"),
+    workloads.custom((700, 1000, 650, 2000), 32, 16, 64, 64, 600, paged=True, name="wide_paged_d64"),
 ]
 
 
@@ -189,8 +194,9 @@ def test_sparse_idx_order_padding_and_out_of_range():
     assert (o3 == 0).all() and torch.isneginf(l3).all()
 
 
-def test_paged_equals_contiguous_bit_exact():
-    w = workloads.custom((3000, 3000), 32, 8, 128, 32, 300, name="pc")
+@pytest.mark.parametrize("k", [300, 2000])   # 2000: 512-entry later-step chunks
+def test_paged_equals_contiguous_bit_exact(k):
+    w = workloads.custom((3000, 3000), 32, 8, 128, 32, k, name="pc")
     inp = workloads.make_inputs(w)
     kp, vp, table, lens = workloads.to_paged(inp.k, inp.v, 16, seed=11)
     q, kc, vc = inp.q1.to(DEV), inp.k.to(DEV), inp.v.to(DEV)
@@ -377,6 +383,8 @@ def test_block_attn_after_the_gpu_prefix_pass():
     (1, 128, 8, 8, 64, 500, 64),       # B = 128: 32 block rows per wave, four row blocks
     (1, 33, 2, 1, 128, 90, 90),        # B = 33: waves with 9, 9, 9 and 6 block rows
     (1, 2, 4, 1, 128, 300, 40),        # B = 2: two waves without block rows
+    (2, 32, 32, 8, 128, 2500, 2000),   # 4 index chunks of 512, block rows in the last
+    (4, 64, 32, 16, 64, 1000, 600),    # one 640-entry chunk (256 row-block pairs), 16 block rows per wave
 ])
 def test_sparse_block_attn_matches_oracle(S, B, Hq, Hkv, d, N, k):
     scale = 1.0
