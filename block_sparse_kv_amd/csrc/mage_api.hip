@@ -386,6 +386,61 @@ mage_status paged_kv(const Dims& d, const mage_paged_kv* kv, KvArgs& a) {
   return MAGE_OK;
 }
 
+// Sequences [s0, s0 + MAGE_MAX_SEQS) of a call (fewer for the last group).
+Dims seq_group(const Dims& d, int s0) {
+  Dims g = d;
+  g.S = std::min(MAGE_MAX_SEQS, d.S - s0);
+  g.units = g.S * d.Hkv;
+  return g;
+}
+
+// A paged call's per-sequence lengths and chunk numbering travel in the
+// kernel arguments, for at most MAGE_MAX_SEQS sequences, so a call over more
+// sequences runs as consecutive groups of at most MAGE_MAX_SEQS, in stream
+// order on one stream and with the same workspace, each with every
+// per-sequence array offset to the group's first sequence s0. Every group is
+// checked (check(g, kv)) before the first is launched (run(g, kv, s0)).
+template <class Check, class Run>
+mage_status paged_groups(const Dims& d, const mage_paged_kv* kvp, Check&& check, Run&& run) {
+  if (!kvp) return fail(MAGE_ERR_INVALID_ARG, "kv is null");
+  for (int pass = 0; pass < 2; ++pass)
+    for (int s0 = 0; s0 < d.S; s0 += MAGE_MAX_SEQS) {
+      const Dims g = seq_group(d, s0);
+      mage_paged_kv gk = *kvp;
+      if (gk.page_table) gk.page_table += static_cast<int64_t>(s0) * kvp->max_pages;
+      if (gk.seq_lens) gk.seq_lens += s0;
+      KvArgs kv;
+      if (mage_status st = paged_kv(g, &gk, kv); st != MAGE_OK) return st;
+      if (mage_status st = pass == 0 ? check(g, kv) : run(g, kv, s0); st != MAGE_OK) return st;
+    }
+  return MAGE_OK;
+}
+
+// The longest prefix of a paged call (the row length of its score output);
+// only after paged_groups has checked the lengths.
+int64_t paged_max_n(const Dims& d, const mage_paged_kv* kvp) {
+  int64_t m = 0;
+  for (int s = 0; s < d.S; ++s) m = std::max<int64_t>(m, kvp->seq_lens[s]);
+  return m;
+}
+
+// A selection that ran entirely on attn: the select stream waits for it and
+// idx_ready is recorded there, as when the selection runs on that stream.
+mage_status join_select(hipStream_t attn, hipStream_t sel, hipEvent_t idx_ready) {
+  if (sel && sel != attn) {
+    hipEvent_t ev = internal_event();
+    if (!ev) return fail(MAGE_ERR_HIP, "could not create the stream-ordering event");
+    if (hipError_t e = hipEventRecord(ev, attn); e != hipSuccess) return hip_fail(e, "hipEventRecord");
+    if (hipError_t e = hipStreamWaitEvent(sel, ev, 0); e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+  } else {
+    sel = attn;
+  }
+  if (idx_ready) {
+    if (hipError_t e = hipEventRecord(idx_ready, sel); e != hipSuccess) return hip_fail(e, "hipEventRecord(idx_ready)");
+  }
+  return MAGE_OK;
+}
+
 // Dense (row, chunk) numbering of the candidate pass when row lengths differ
 // (tp.n_uniform < 0): seqs groups of tp.rows_per_seq rows.
 ChunkMap topk_map(const TopkParams& tp, int seqs) {
@@ -488,20 +543,7 @@ mage_status launch_select(const Dims& d, const uint16_t* q, const KvArgs& kv, in
           st != MAGE_OK)
         return st;
     }
-    if (k > 0 && sel && sel != attn) {
-      hipEvent_t ev = internal_event();
-      if (!ev) return fail(MAGE_ERR_HIP, "could not create the stream-ordering event");
-      if (hipError_t e = hipEventRecord(ev, attn); e != hipSuccess) return hip_fail(e, "hipEventRecord");
-      if (hipError_t e = hipStreamWaitEvent(sel, ev, 0); e != hipSuccess)
-        return hip_fail(e, "hipStreamWaitEvent");
-    } else {
-      sel = attn;
-    }
-    if (k > 0 && idx_ready) {
-      if (hipError_t e = hipEventRecord(idx_ready, sel); e != hipSuccess)
-        return hip_fail(e, "hipEventRecord(idx_ready)");
-    }
-    return MAGE_OK;
+    return k > 0 ? join_select(attn, sel, idx_ready) : MAGE_OK;
   }
   // group_pass (sub-groups of a split head group): bit 0 = add to the stored
   // scores, bit 1 = the last sub-group (histogram and top-k); 0 = unsplit
@@ -914,6 +956,16 @@ mage_status scratch_on_device(hipStream_t stream, void** out) {
   return MAGE_OK;
 }
 
+// head-dimension dispatch of the launch plans
+template <class... A>
+mage_status select_d(const Dims& d, A&&... a) {
+  return d.D == 128 ? launch_select<128>(d, a...) : launch_select<64>(d, a...);
+}
+template <class... A>
+mage_status sparse_d(const Dims& d, A&&... a) {
+  return d.D == 128 ? launch_sparse<128>(d, a...) : launch_sparse<64>(d, a...);
+}
+
 }  // namespace
 
 extern "C" {
@@ -921,7 +973,10 @@ extern "C" {
 size_t mage_workspace_bytes(const mage_dims* dims, int32_t max_seq_len, int32_t k) {
   Dims d;
   if (check_dims(dims, d) != MAGE_OK || max_seq_len < 1 || k < 1) return 0;
-  return make_layout(d, max_seq_len, k).total;
+  // also enough for a paged call's groups of MAGE_MAX_SEQS sequences
+  size_t t = make_layout(d, max_seq_len, k).total;
+  for (int s0 = 0; s0 < d.S; s0 += MAGE_MAX_SEQS) t = std::max(t, make_layout(seq_group(d, s0), max_seq_len, k).total);
+  return t;
 }
 
 mage_status mage_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream) {
@@ -976,14 +1031,20 @@ mage_status mage_select_exact_paged(const mage_dims* dims, const uint16_t* q, co
   Dims d;
   if (mage_status st = check_dims(dims, d); st != MAGE_OK) return st;
   if (mage_status st = common_select_checks(q, k, o, lse, idx, scores); st != MAGE_OK) return st;
-  KvArgs kv;
-  if (mage_status st = paged_kv(d, kvp, kv); st != MAGE_OK) return st;
-  const Layout L = make_layout(d, kv.max_n, k);
-  if (mage_status st = check_ws(workspace, workspace_bytes, L); st != MAGE_OK) return st;
-  return d.D == 128 ? launch_select<128>(d, q, kv, k, o, lse, idx, scores, kv.max_n, workspace, L,
-                                         attn_stream, select_stream, idx_ready)
-                    : launch_select<64>(d, q, kv, k, o, lse, idx, scores, kv.max_n, workspace, L,
-                                        attn_stream, select_stream, idx_ready);
+  const bool grouped = d.S > MAGE_MAX_SEQS;
+  int64_t stride = 0;
+  mage_status st = paged_groups(
+      d, kvp,
+      [&](const Dims& g, const KvArgs& kv) { return check_ws(workspace, workspace_bytes, make_layout(g, kv.max_n, k)); },
+      [&](const Dims& g, const KvArgs& kv, int s0) {
+        if (stride == 0) stride = paged_max_n(d, kvp);
+        const int64_t sq = static_cast<int64_t>(s0) * d.B * d.Hq, su = static_cast<int64_t>(s0) * d.Hkv;
+        return select_d(g, q + sq * d.D, kv, k, o + sq * d.D, lse ? lse + sq : nullptr, idx + su * k,
+                        scores ? scores + su * stride : nullptr, stride, workspace, make_layout(g, kv.max_n, k),
+                        attn_stream, grouped ? attn_stream : select_stream, grouped ? nullptr : idx_ready);
+      });
+  if (st != MAGE_OK || !grouped) return st;
+  return join_select(attn_stream, select_stream, idx_ready);
 }
 
 mage_status mage_exact_attn(const mage_dims* dims, const uint16_t* q, const uint16_t* k_cache,
@@ -1012,14 +1073,14 @@ mage_status mage_exact_attn_paged(const mage_dims* dims, const uint16_t* q, cons
   if (mage_status st = check_dims(dims, d); st != MAGE_OK) return st;
   int32_t dummy_idx = 0;
   if (mage_status st = common_select_checks(q, 1, o, lse, &dummy_idx, nullptr); st != MAGE_OK) return st;
-  KvArgs kv;
-  if (mage_status st = paged_kv(d, kvp, kv); st != MAGE_OK) return st;
-  const Layout L = make_layout(d, kv.max_n, 1);
-  if (mage_status st = check_ws(workspace, workspace_bytes, L); st != MAGE_OK) return st;
-  return d.D == 128 ? launch_select<128>(d, q, kv, 0, o, lse, nullptr, nullptr, 0, workspace, L,
-                                         stream, nullptr, nullptr)
-                    : launch_select<64>(d, q, kv, 0, o, lse, nullptr, nullptr, 0, workspace, L,
-                                        stream, nullptr, nullptr);
+  return paged_groups(
+      d, kvp,
+      [&](const Dims& g, const KvArgs& kv) { return check_ws(workspace, workspace_bytes, make_layout(g, kv.max_n, 1)); },
+      [&](const Dims& g, const KvArgs& kv, int s0) {
+        const int64_t sq = static_cast<int64_t>(s0) * d.B * d.Hq;
+        return select_d(g, q + sq * d.D, kv, 0, o + sq * d.D, lse ? lse + sq : nullptr, nullptr, nullptr, 0,
+                        workspace, make_layout(g, kv.max_n, 1), stream, nullptr, nullptr);
+      });
 }
 
 static mage_status mean_query_checks(const uint16_t* q, int32_t k, int32_t* idx, float* scores) {
@@ -1055,12 +1116,19 @@ mage_status mage_select_mean_query_paged(const mage_dims* dims, const uint16_t* 
   if (mage_status st = check_dims(dims, d); st != MAGE_OK) return st;
   if (mage_status st = one_group(d); st != MAGE_OK) return st;
   if (mage_status st = mean_query_checks(q, k, idx, scores); st != MAGE_OK) return st;
-  KvArgs kv;
-  if (mage_status st = paged_kv(d, kvp, kv); st != MAGE_OK) return st;
-  const Layout L = make_layout(d, kv.max_n, k);
-  if (mage_status st = check_ws(workspace, workspace_bytes, L); st != MAGE_OK) return st;
-  return d.D == 128 ? launch_mean_query_select<128>(d, q, kv, k, idx, scores, kv.max_n, workspace, L, stream)
-                    : launch_mean_query_select<64>(d, q, kv, k, idx, scores, kv.max_n, workspace, L, stream);
+  int64_t stride = 0;
+  return paged_groups(
+      d, kvp,
+      [&](const Dims& g, const KvArgs& kv) { return check_ws(workspace, workspace_bytes, make_layout(g, kv.max_n, k)); },
+      [&](const Dims& g, const KvArgs& kv, int s0) {
+        if (stride == 0) stride = paged_max_n(d, kvp);
+        const int64_t sq = static_cast<int64_t>(s0) * d.B * d.Hq, su = static_cast<int64_t>(s0) * d.Hkv;
+        const Layout L = make_layout(g, kv.max_n, k);
+        float* sc = scores ? scores + su * stride : nullptr;
+        return d.D == 128
+                   ? launch_mean_query_select<128>(g, q + sq * d.D, kv, k, idx + su * k, sc, stride, workspace, L, stream)
+                   : launch_mean_query_select<64>(g, q + sq * d.D, kv, k, idx + su * k, sc, stride, workspace, L, stream);
+      });
 }
 
 static mage_status page_checks(const uint16_t* q, int32_t page_tokens, int32_t k_pages, float* o, float* lse,
@@ -1106,16 +1174,22 @@ mage_status mage_select_pages_paged(const mage_dims* dims, const uint16_t* q, co
   if (mage_status st = one_group(d); st != MAGE_OK) return st;
   if (mage_status st = page_checks(q, page_tokens, k_pages, o, lse, idx, page_idx, scores); st != MAGE_OK)
     return st;
-  KvArgs kv;
-  if (mage_status st = paged_kv(d, kvp, kv); st != MAGE_OK) return st;
   const int32_t k = k_pages * page_tokens;
-  const Layout L = make_layout(d, kv.max_n, k);
-  if (mage_status st = check_ws(workspace, workspace_bytes, L); st != MAGE_OK) return st;
-  const PagePlan pp{page_tokens, k_pages, page_idx};
-  return d.D == 128 ? launch_select<128>(d, q, kv, k, o, lse, idx, scores, kv.max_n, workspace, L, attn_stream,
-                                         select_stream, idx_ready, &pp)
-                    : launch_select<64>(d, q, kv, k, o, lse, idx, scores, kv.max_n, workspace, L, attn_stream,
-                                        select_stream, idx_ready, &pp);
+  const bool grouped = d.S > MAGE_MAX_SEQS;
+  int64_t stride = 0;
+  mage_status st = paged_groups(
+      d, kvp,
+      [&](const Dims& g, const KvArgs& kv) { return check_ws(workspace, workspace_bytes, make_layout(g, kv.max_n, k)); },
+      [&](const Dims& g, const KvArgs& kv, int s0) {
+        if (stride == 0) stride = paged_max_n(d, kvp);
+        const int64_t sq = static_cast<int64_t>(s0) * d.B * d.Hq, su = static_cast<int64_t>(s0) * d.Hkv;
+        const PagePlan pp{page_tokens, k_pages, page_idx ? page_idx + su * k_pages : nullptr};
+        return select_d(g, q + sq * d.D, kv, k, o + sq * d.D, lse ? lse + sq : nullptr, idx + su * k,
+                        scores ? scores + su * stride : nullptr, stride, workspace, make_layout(g, kv.max_n, k),
+                        attn_stream, grouped ? attn_stream : select_stream, grouped ? nullptr : idx_ready, &pp);
+      });
+  if (st != MAGE_OK || !grouped) return st;
+  return join_select(attn_stream, select_stream, idx_ready);
 }
 
 mage_status mage_select_adaptive(const mage_dims* dims, const uint16_t* q, const uint16_t* k_cache,
@@ -1154,16 +1228,20 @@ mage_status mage_select_adaptive_paged(const mage_dims* dims, const uint16_t* q,
   if (!counts || !aligned(counts, 4)) return fail(MAGE_ERR_INVALID_ARG, "counts must be non-null and 4-byte aligned");
   if (static_cast<int64_t>(k) * d.Hkv > MAGE_MAX_SPARSE_K)
     return fail(MAGE_ERR_UNSUPPORTED, "k * num_kv_heads must be <= MAGE_MAX_SPARSE_K");
-  KvArgs kv;
-  if (mage_status st = paged_kv(d, kvp, kv); st != MAGE_OK) return st;
   const int32_t K = k * d.Hkv;
-  const Layout L = make_layout(d, kv.max_n, K);
-  if (mage_status st = check_ws(workspace, workspace_bytes, L); st != MAGE_OK) return st;
-  const BudgetPlan bp{k, counts};
-  return d.D == 128 ? launch_select<128>(d, q, kv, K, o, lse, idx, nullptr, 0, workspace, L, attn_stream,
-                                         select_stream, idx_ready, nullptr, &bp)
-                    : launch_select<64>(d, q, kv, K, o, lse, idx, nullptr, 0, workspace, L, attn_stream,
-                                        select_stream, idx_ready, nullptr, &bp);
+  const bool grouped = d.S > MAGE_MAX_SEQS;
+  mage_status st = paged_groups(
+      d, kvp,
+      [&](const Dims& g, const KvArgs& kv) { return check_ws(workspace, workspace_bytes, make_layout(g, kv.max_n, K)); },
+      [&](const Dims& g, const KvArgs& kv, int s0) {
+        const int64_t sq = static_cast<int64_t>(s0) * d.B * d.Hq, su = static_cast<int64_t>(s0) * d.Hkv;
+        const BudgetPlan bp{k, counts + su};
+        return select_d(g, q + sq * d.D, kv, K, o + sq * d.D, lse ? lse + sq : nullptr, idx + su * K, nullptr, 0,
+                        workspace, make_layout(g, kv.max_n, K), attn_stream,
+                        grouped ? attn_stream : select_stream, grouped ? nullptr : idx_ready, nullptr, &bp);
+      });
+  if (st != MAGE_OK || !grouped) return st;
+  return join_select(attn_stream, select_stream, idx_ready);
 }
 
 mage_status mage_mean_query(const mage_dims* dims, const uint16_t* q, uint16_t* qbar, hipStream_t stream) {
@@ -1253,12 +1331,14 @@ mage_status mage_sparse_attn_paged(const mage_dims* dims, const uint16_t* q, con
   CallScope scope;
   Dims d;
   if (mage_status st = sparse_common(dims, q, idx, k, o, lse, d); st != MAGE_OK) return st;
-  KvArgs kv;
-  if (mage_status st = paged_kv(d, kvp, kv); st != MAGE_OK) return st;
-  const Layout L = make_layout(d, kv.max_n, k);
-  if (mage_status st = check_ws(workspace, workspace_bytes, L); st != MAGE_OK) return st;
-  return d.D == 128 ? launch_sparse<128>(d, q, kv, idx, k, o, lse, workspace, L, stream)
-                    : launch_sparse<64>(d, q, kv, idx, k, o, lse, workspace, L, stream);
+  return paged_groups(
+      d, kvp,
+      [&](const Dims& g, const KvArgs& kv) { return check_ws(workspace, workspace_bytes, make_layout(g, kv.max_n, k)); },
+      [&](const Dims& g, const KvArgs& kv, int s0) {
+        const int64_t sq = static_cast<int64_t>(s0) * d.B * d.Hq, su = static_cast<int64_t>(s0) * d.Hkv;
+        return sparse_d(g, q + sq * d.D, kv, idx + su * k, k, o + sq * d.D, lse ? lse + sq : nullptr, workspace,
+                        make_layout(g, kv.max_n, k), stream);
+      });
 }
 
 static mage_status block_rows_checks(const uint16_t* k_blk, const uint16_t* v_blk) {
@@ -1294,12 +1374,15 @@ mage_status mage_sparse_block_attn_paged(const mage_dims* dims, const uint16_t* 
   if (mage_status st = sparse_common(dims, q, idx, k, o, lse, d); st != MAGE_OK) return st;
   if (mage_status st = one_group(d); st != MAGE_OK) return st;
   if (mage_status st = block_rows_checks(k_blk, v_blk); st != MAGE_OK) return st;
-  KvArgs kv;
-  if (mage_status st = paged_kv(d, kvp, kv); st != MAGE_OK) return st;
-  const Layout L = make_layout(d, kv.max_n, k);
-  if (mage_status st = check_ws(workspace, workspace_bytes, L); st != MAGE_OK) return st;
-  return d.D == 128 ? launch_sparse<128>(d, q, kv, idx, k, o, lse, workspace, L, stream, k_blk, v_blk)
-                    : launch_sparse<64>(d, q, kv, idx, k, o, lse, workspace, L, stream, k_blk, v_blk);
+  return paged_groups(
+      d, kvp,
+      [&](const Dims& g, const KvArgs& kv) { return check_ws(workspace, workspace_bytes, make_layout(g, kv.max_n, k)); },
+      [&](const Dims& g, const KvArgs& kv, int s0) {
+        const int64_t sq = static_cast<int64_t>(s0) * d.B * d.Hq, su = static_cast<int64_t>(s0) * d.Hkv;
+        const int64_t sb = su * d.B * d.D;   // block rows before the group
+        return sparse_d(g, q + sq * d.D, kv, idx + su * k, k, o + sq * d.D, lse ? lse + sq : nullptr, workspace,
+                        make_layout(g, kv.max_n, k), stream, k_blk + sb, v_blk + sb);
+      });
 }
 
 static mage_status counts_checks(const int32_t* counts, int32_t k_seq) {
@@ -1335,13 +1418,14 @@ mage_status mage_sparse_attn_counts_paged(const mage_dims* dims, const uint16_t*
   if (mage_status st = sparse_common(dims, q, idx, k_row, o, lse, d); st != MAGE_OK) return st;
   if (mage_status st = one_group(d); st != MAGE_OK) return st;
   if (mage_status st = counts_checks(counts, k_seq); st != MAGE_OK) return st;
-  KvArgs kv;
-  if (mage_status st = paged_kv(d, kvp, kv); st != MAGE_OK) return st;
-  const Layout L = make_layout(d, kv.max_n, k_row);
-  if (mage_status st = check_ws(workspace, workspace_bytes, L); st != MAGE_OK) return st;
-  return d.D == 128
-             ? launch_sparse<128>(d, q, kv, idx, k_row, o, lse, workspace, L, stream, nullptr, nullptr, counts, k_seq)
-             : launch_sparse<64>(d, q, kv, idx, k_row, o, lse, workspace, L, stream, nullptr, nullptr, counts, k_seq);
+  return paged_groups(
+      d, kvp,
+      [&](const Dims& g, const KvArgs& kv) { return check_ws(workspace, workspace_bytes, make_layout(g, kv.max_n, k_row)); },
+      [&](const Dims& g, const KvArgs& kv, int s0) {
+        const int64_t sq = static_cast<int64_t>(s0) * d.B * d.Hq, su = static_cast<int64_t>(s0) * d.Hkv;
+        return sparse_d(g, q + sq * d.D, kv, idx + su * k_row, k_row, o + sq * d.D, lse ? lse + sq : nullptr,
+                        workspace, make_layout(g, kv.max_n, k_row), stream, nullptr, nullptr, counts + su, k_seq);
+      });
 }
 
 mage_status mage_block_attn(const mage_dims* dims, const uint16_t* q, const uint16_t* k_blk,
@@ -1380,27 +1464,37 @@ mage_status mage_topk(int32_t rows, const float* scores, int64_t row_stride, con
   if (!scores || !idx) return fail(MAGE_ERR_INVALID_ARG, "scores and idx must not be null");
   if (!aligned(scores, 4) || !aligned(idx, 4)) return fail(MAGE_ERR_INVALID_ARG, "scores and idx must be 4-byte aligned");
   if (row_stride < n) return fail(MAGE_ERR_INVALID_ARG, "row_stride must be >= n");
-  if (lens && rows > MAGE_MAX_SEQS)
-    return fail(MAGE_ERR_UNSUPPORTED, "per-row lengths need rows <= MAGE_MAX_SEQS");
-  SeqLens sl;
-  std::memset(&sl, 0, sizeof sl);
   if (lens) {
-    for (int r = 0; r < rows; ++r) {
+    for (int r = 0; r < rows; ++r)
       if (lens[r] < 1 || lens[r] > n) return fail(MAGE_ERR_INVALID_ARG, "lens[r] must be in [1, n]");
-      sl.n[r] = lens[r];
-    }
   }
   if (rows > (1 << 20)) return fail(MAGE_ERR_UNSUPPORTED, "rows must be <= 2^20");
   if (n > kMaxTopkLen) return fail(MAGE_ERR_UNSUPPORTED, "rows longer than 2^25 entries");
-  // workspace: the full layout for one KV head per row
+  // workspace: the full layout for one KV head per row. Per-row lengths travel
+  // in the kernel arguments, so with lens the rows run in stream-ordered
+  // groups of at most MAGE_MAX_SEQS.
   Dims d{};
   d.S = rows; d.B = 1; d.Hq = 1; d.Hkv = 1; d.G = 1; d.R = 1; d.D = 64; d.nrb = 1; d.units = rows;
   d.ng = 1; d.gs = 0; d.g0 = 0; d.r_total = 1;
   d.scale = 1.f;
-  const Layout L = make_layout(d, n, k);
-  if (mage_status st = check_ws(workspace, workspace_bytes, L); st != MAGE_OK) return st;
-  const TopkParams tp = topk_params(workspace, L, scores, row_stride, idx, k, rows, 1, lens ? -1 : n, n, sl, rows);
-  return launch_topk(tp, stream, true);
+  const int group = lens ? MAGE_MAX_SEQS : rows;
+  for (int pass = 0; pass < 2; ++pass)
+    for (int r0 = 0; r0 < rows; r0 += group) {
+      const Dims g = lens ? seq_group(d, r0) : d;
+      const Layout L = make_layout(g, n, k);
+      if (pass == 0) {
+        if (mage_status st = check_ws(workspace, workspace_bytes, L); st != MAGE_OK) return st;
+        continue;
+      }
+      SeqLens sl;
+      std::memset(&sl, 0, sizeof sl);
+      if (lens)
+        for (int r = 0; r < g.S; ++r) sl.n[r] = lens[r0 + r];
+      const TopkParams tp = topk_params(workspace, L, scores + r0 * row_stride, row_stride, idx + static_cast<int64_t>(r0) * k,
+                                        k, g.S, 1, lens ? -1 : n, n, sl, g.S);
+      if (mage_status st = launch_topk(tp, stream, true); st != MAGE_OK) return st;
+    }
+  return MAGE_OK;
 }
 
 const char* mage_status_string(mage_status status) {

@@ -75,13 +75,19 @@ typedef enum mage_status {
   MAGE_OK = 0,
   MAGE_ERR_INVALID_ARG = 1,          /* null pointer, bad size, Hq % Hkv != 0 */
   MAGE_ERR_UNSUPPORTED = 2,          /* d not in {64, 128}, B > 128, R > 128 where a call
-                                        takes no split group, S > MAGE_MAX_SEQS (paged) */
+                                        takes no split group */
   MAGE_ERR_WORKSPACE_TOO_SMALL = 3,
   MAGE_ERR_HIP = 4                   /* launch or runtime failure; see mage_last_error() */
 } mage_status;
 
-/* Largest number of sequences one paged call takes (their lengths travel in
- * the kernel arguments). */
+/* Sequences per launch of a paged call (their lengths and chunk numbering
+ * travel in the kernel arguments). A paged call over more sequences runs as
+ * consecutive groups of at most MAGE_MAX_SEQS sequences, in stream order on
+ * the call's stream with the same workspace; its results are those of one
+ * call per group. Every group's arguments are checked before the first
+ * launch. A grouped step-1 call runs its selection on attn_stream too; the
+ * select stream, when given, waits for the end and records idx_ready there.
+ * The standalone top-k runs rows with per-row lengths the same way. */
 #define MAGE_MAX_SEQS 256
 /* Largest R = B * G rows per KV head that one pass of the kernels takes.
  * mage_select_exact, mage_exact_attn and mage_sparse_attn (and their _paged
@@ -113,7 +119,8 @@ typedef struct mage_paged_kv {
 } mage_paged_kv;
 
 /* Bytes of workspace that every entry point below needs for these dims, any
- * prefix length <= max_seq_len and any top-k budget <= k. */
+ * prefix length <= max_seq_len and any top-k budget <= k (including a paged
+ * call's groups of MAGE_MAX_SEQS sequences). */
 size_t mage_workspace_bytes(const mage_dims* dims, int32_t max_seq_len, int32_t k);
 
 /* Zero-fill a workspace on `stream` with a fill kernel (no memset node).

@@ -53,6 +53,10 @@ def test_workspace_bytes():
     # R = 64 * 4 = 256 rows per KV head runs in two sub-groups on the same layout
     assert mage.workspace_bytes(dims(block=64), 131072, 1024) == big
     assert mage.workspace_bytes(dims(block=200), 1024, 64) == 0
+    # a paged call over more than MAGE_MAX_SEQS sequences runs in groups of 256: the
+    # size covers the whole shape and every group's
+    many = mage.workspace_bytes(dims(num_seqs=300), 4096, 256)
+    assert many >= mage.workspace_bytes(dims(num_seqs=256), 4096, 256) > mage.workspace_bytes(dims(num_seqs=44), 4096, 256)
     # every layout starts with the fixed 256 KiB arrival-counter region of the later steps
     tiny = mage.workspace_bytes(dims(block=1, num_q_heads=1, num_kv_heads=1, head_dim=64), 1, 1)
     assert tiny >= 16384 * 4 * 4
@@ -137,10 +141,18 @@ def test_paged_rejects_bad_arguments():
     assert sel(kv(table=None)) == mage.ERR_INVALID_ARG
     lens[1] = 0
     assert sel(kv()) == mage.ERR_INVALID_ARG
+    # 300 sequences run as groups of 256 and 44; a bad length in the second group
+    # is found before the first group is launched (a launch here, with no GPU,
+    # would return ERR_HIP)
     big = dims(num_seqs=300, num_kv_heads=8)
-    k = kv()
+    lens300 = (ctypes.c_int32 * 300)(*([64] * 300))
+    lens300[280] = 0
+    k = mage.PagedKv(FAKE.value, FAKE.value, FAKE.value, 8, 16, ctypes.cast(lens300, ctypes.POINTER(ctypes.c_int32)))
     assert lib.mage_sparse_attn_paged(ctypes.byref(big), FAKE, ctypes.byref(k), FAKE, 64, FAKE, None,
-                                      FAKE, 1 << 40, None) == mage.ERR_UNSUPPORTED
+                                      FAKE, 1 << 40, None) == mage.ERR_INVALID_ARG
+    assert lib.mage_select_exact_paged(ctypes.byref(big), FAKE, ctypes.byref(k), 64, FAKE, None, FAKE, None,
+                                       FAKE, 1 << 40, None, None, None) == mage.ERR_INVALID_ARG
+    assert b"seq_lens" in lib.mage_last_error()
 
 
 def test_topk_rejects_bad_arguments():
