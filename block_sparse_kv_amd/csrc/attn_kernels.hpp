@@ -1230,6 +1230,7 @@ struct BlockParams {
   float* o;                 // fp32 [S][B][Hq][d]; may be o_pre
   float* lse;               // fp32 [S][B][Hq] or null; may be lse_pre
   int32_t S, B, Hq, Hkv, G, R;
+  int32_t gs, g0;           // a sub-group of query heads: head stride, first head (0, 0: the whole group)
   float scale_log2;         // scale * log2(e)
 };
 
@@ -1250,7 +1251,7 @@ __global__ __launch_bounds__(kWave) void block_attn_kernel(BlockParams p) {
   {
     if (r < p.R) {
       const int b = r / p.G, gg = r - b * p.G;
-      const uint16_t* qrow = p.q + ((static_cast<int64_t>(s) * p.B + b) * p.Hq + h * p.G + gg) * D;
+      const uint16_t* qrow = p.q + ((static_cast<int64_t>(s) * p.B + b) * p.Hq + q_head(h, gg, p.G, p.gs, p.g0)) * D;
 #pragma unroll
       for (int ks = 0; ks < kNks; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, load16(qrow + 16 * ks + 8 * hh));
     } else {
@@ -1294,7 +1295,7 @@ __global__ __launch_bounds__(kWave) void block_attn_kernel(BlockParams p) {
   l_run = wave_sum_pair(l_run);
   if (r >= p.R) return;
   const int b = r / p.G, gg = r - b * p.G;
-  const int64_t row = (static_cast<int64_t>(s) * p.B + b) * p.Hq + h * p.G + gg;
+  const int64_t row = (static_cast<int64_t>(s) * p.B + b) * p.Hq + q_head(h, gg, p.G, p.gs, p.g0);
   // log2 units: the block part's log-sum-exp is m + log2(l) (l >= 1)
   const float lb = m_run + __log2f(l_run);
   const float lp = p.lse_pre[row] * kLog2e;

@@ -97,11 +97,6 @@ Dims group_dims(const Dims& d, int grp) {
   return g;
 }
 
-mage_status one_group(const Dims& d) {
-  return d.ng == 1 ? MAGE_OK
-                   : fail(MAGE_ERR_UNSUPPORTED, "block * (num_q_heads / num_kv_heads) must be <= 128 for this call");
-}
-
 mage_status check_dims(const mage_dims* d, Dims& o) {
   if (!d) return fail(MAGE_ERR_INVALID_ARG, "dims is null");
   if (d->num_seqs < 1 || d->block < 1 || d->num_q_heads < 1 || d->num_kv_heads < 1)
@@ -534,12 +529,11 @@ mage_status launch_select(const Dims& d, const uint16_t* q, const KvArgs& kv, in
     // A head group of more than kMaxRows rows runs as sub-groups, one after
     // another on attn (each reuses the workspace's partials): every sub-group's
     // exact pass, merge and score sweep, the sweeps adding into one score row
-    // per unit; the last one builds the histogram and runs the top-k.
-    if (pages || budget) return one_group(d);
+    // per unit; the last one runs the top-k (positions, pages or budgets).
     for (int grp = 0; grp < d.ng; ++grp) {
       const int pass = (grp > 0 ? 1 : 0) | (grp == d.ng - 1 ? 2 : 0);
       if (mage_status st = launch_select<D>(group_dims(d, grp), q, kv, k, o, lse, idx, scores, score_stride, ws, L,
-                                            attn, attn, nullptr, nullptr, nullptr, pass);
+                                            attn, attn, nullptr, pages, budget, pass);
           st != MAGE_OK)
         return st;
     }
@@ -771,10 +765,12 @@ mage_status launch_sparse(const Dims& d, const uint16_t* q, const KvArgs& kv, co
                           const uint16_t* v_blk = nullptr, const int32_t* counts = nullptr, int32_t k_seq = 0) {
   if (d.ng > 1) {
     // a head group of more than kMaxRows rows: one launch per sub-group (in
-    // stream order, each reusing the workspace); the plain later step only
-    if (k_blk || counts) return one_group(d);
+    // stream order, each reusing the workspace), each with the KV head's
+    // block rows and counts
     for (int grp = 0; grp < d.ng; ++grp)
-      if (mage_status st = launch_sparse<D>(group_dims(d, grp), q, kv, idx, k, o, lse, ws, L, stream); st != MAGE_OK)
+      if (mage_status st = launch_sparse<D>(group_dims(d, grp), q, kv, idx, k, o, lse, ws, L, stream, k_blk, v_blk,
+                                            counts, k_seq);
+          st != MAGE_OK)
         return st;
     return MAGE_OK;
   }
@@ -868,6 +864,9 @@ mage_status launch_mean_query_select(const Dims& d, const uint16_t* q, const KvA
   d1.R = 1;
   d1.nrb = 1;
   d1.r_total = 1;
+  d1.ng = 1;   // one row per KV head, whatever the block's head group
+  d1.gs = 0;
+  d1.g0 = 0;
   return launch_select<D>(d1, mq.qbar, kv, k, at<float>(ws, L.qbar_o), nullptr, idx, scores, score_stride,
                           ws, L, stream, nullptr, nullptr);
 }
@@ -1098,7 +1097,6 @@ mage_status mage_select_mean_query(const mage_dims* dims, const uint16_t* q, con
   CallScope scope;
   Dims d;
   if (mage_status st = check_dims(dims, d); st != MAGE_OK) return st;
-  if (mage_status st = one_group(d); st != MAGE_OK) return st;
   if (mage_status st = mean_query_checks(q, k, idx, scores); st != MAGE_OK) return st;
   KvArgs kv;
   if (mage_status st = contiguous_kv(d, k_cache, v_cache, seq_len, kv); st != MAGE_OK) return st;
@@ -1114,7 +1112,6 @@ mage_status mage_select_mean_query_paged(const mage_dims* dims, const uint16_t* 
   CallScope scope;
   Dims d;
   if (mage_status st = check_dims(dims, d); st != MAGE_OK) return st;
-  if (mage_status st = one_group(d); st != MAGE_OK) return st;
   if (mage_status st = mean_query_checks(q, k, idx, scores); st != MAGE_OK) return st;
   int64_t stride = 0;
   return paged_groups(
@@ -1149,7 +1146,6 @@ mage_status mage_select_pages(const mage_dims* dims, const uint16_t* q, const ui
   CallScope scope;
   Dims d;
   if (mage_status st = check_dims(dims, d); st != MAGE_OK) return st;
-  if (mage_status st = one_group(d); st != MAGE_OK) return st;
   if (mage_status st = page_checks(q, page_tokens, k_pages, o, lse, idx, page_idx, scores); st != MAGE_OK)
     return st;
   KvArgs kv;
@@ -1171,7 +1167,6 @@ mage_status mage_select_pages_paged(const mage_dims* dims, const uint16_t* q, co
   CallScope scope;
   Dims d;
   if (mage_status st = check_dims(dims, d); st != MAGE_OK) return st;
-  if (mage_status st = one_group(d); st != MAGE_OK) return st;
   if (mage_status st = page_checks(q, page_tokens, k_pages, o, lse, idx, page_idx, scores); st != MAGE_OK)
     return st;
   const int32_t k = k_pages * page_tokens;
@@ -1199,7 +1194,6 @@ mage_status mage_select_adaptive(const mage_dims* dims, const uint16_t* q, const
   CallScope scope;
   Dims d;
   if (mage_status st = check_dims(dims, d); st != MAGE_OK) return st;
-  if (mage_status st = one_group(d); st != MAGE_OK) return st;
   if (mage_status st = common_select_checks(q, k, o, lse, idx, nullptr); st != MAGE_OK) return st;
   if (!counts || !aligned(counts, 4)) return fail(MAGE_ERR_INVALID_ARG, "counts must be non-null and 4-byte aligned");
   if (static_cast<int64_t>(k) * d.Hkv > MAGE_MAX_SPARSE_K)
@@ -1223,7 +1217,6 @@ mage_status mage_select_adaptive_paged(const mage_dims* dims, const uint16_t* q,
   CallScope scope;
   Dims d;
   if (mage_status st = check_dims(dims, d); st != MAGE_OK) return st;
-  if (mage_status st = one_group(d); st != MAGE_OK) return st;
   if (mage_status st = common_select_checks(q, k, o, lse, idx, nullptr); st != MAGE_OK) return st;
   if (!counts || !aligned(counts, 4)) return fail(MAGE_ERR_INVALID_ARG, "counts must be non-null and 4-byte aligned");
   if (static_cast<int64_t>(k) * d.Hkv > MAGE_MAX_SPARSE_K)
@@ -1248,7 +1241,6 @@ mage_status mage_mean_query(const mage_dims* dims, const uint16_t* q, uint16_t* 
   CallScope scope;
   Dims d;
   if (mage_status st = check_dims(dims, d); st != MAGE_OK) return st;
-  if (mage_status st = one_group(d); st != MAGE_OK) return st;
   if (!q || !qbar) return fail(MAGE_ERR_INVALID_ARG, "q and qbar must not be null");
   if (!aligned(q, 2) || !aligned(qbar, 2)) return fail(MAGE_ERR_INVALID_ARG, "q and qbar must be 2-byte aligned");
   MeanQueryParams mq{};
@@ -1306,11 +1298,12 @@ mage_status mage_sparse_attn_noalloc(const mage_dims* dims, const uint16_t* q, c
   CallScope scope;
   Dims d;
   if (mage_status st = sparse_common(dims, q, idx, k, o, lse, d); st != MAGE_OK) return st;
-  if (mage_status st = one_group(d); st != MAGE_OK) return st;
   KvArgs kv;
   if (mage_status st = contiguous_kv(d, k_cache, v_cache, seq_len, kv); st != MAGE_OK) return st;
   // the later step's part of the workspace layout, sized for this call's plan
-  const int64_t nch = cdiv(k, sparse_chunk(d.units, d.nrb, k));
+  // (that of each sub-group when the head group is split)
+  const Dims g0 = d.ng > 1 ? group_dims(d, 0) : d;
+  const int64_t nch = cdiv(k, sparse_chunk(g0.units, g0.nrb, k));
   Layout L{};
   L.slots = nch > 1 ? d.units * nch : 0;
   L.arrivals = 0;
@@ -1355,7 +1348,6 @@ mage_status mage_sparse_block_attn(const mage_dims* dims, const uint16_t* q, con
   CallScope scope;
   Dims d;
   if (mage_status st = sparse_common(dims, q, idx, k, o, lse, d); st != MAGE_OK) return st;
-  if (mage_status st = one_group(d); st != MAGE_OK) return st;
   if (mage_status st = block_rows_checks(k_blk, v_blk); st != MAGE_OK) return st;
   KvArgs kv;
   if (mage_status st = contiguous_kv(d, k_cache, v_cache, seq_len, kv); st != MAGE_OK) return st;
@@ -1372,7 +1364,6 @@ mage_status mage_sparse_block_attn_paged(const mage_dims* dims, const uint16_t* 
   CallScope scope;
   Dims d;
   if (mage_status st = sparse_common(dims, q, idx, k, o, lse, d); st != MAGE_OK) return st;
-  if (mage_status st = one_group(d); st != MAGE_OK) return st;
   if (mage_status st = block_rows_checks(k_blk, v_blk); st != MAGE_OK) return st;
   return paged_groups(
       d, kvp,
@@ -1398,7 +1389,6 @@ mage_status mage_sparse_attn_counts(const mage_dims* dims, const uint16_t* q, co
   CallScope scope;
   Dims d;
   if (mage_status st = sparse_common(dims, q, idx, k_row, o, lse, d); st != MAGE_OK) return st;
-  if (mage_status st = one_group(d); st != MAGE_OK) return st;
   if (mage_status st = counts_checks(counts, k_seq); st != MAGE_OK) return st;
   KvArgs kv;
   if (mage_status st = contiguous_kv(d, k_cache, v_cache, seq_len, kv); st != MAGE_OK) return st;
@@ -1416,7 +1406,6 @@ mage_status mage_sparse_attn_counts_paged(const mage_dims* dims, const uint16_t*
   CallScope scope;
   Dims d;
   if (mage_status st = sparse_common(dims, q, idx, k_row, o, lse, d); st != MAGE_OK) return st;
-  if (mage_status st = one_group(d); st != MAGE_OK) return st;
   if (mage_status st = counts_checks(counts, k_seq); st != MAGE_OK) return st;
   return paged_groups(
       d, kvp,
@@ -1434,7 +1423,6 @@ mage_status mage_block_attn(const mage_dims* dims, const uint16_t* q, const uint
   CallScope scope;
   Dims d;
   if (mage_status st = check_dims(dims, d); st != MAGE_OK) return st;
-  if (mage_status st = one_group(d); st != MAGE_OK) return st;
   if (!q || !k_blk || !v_blk || !o_prefix || !lse_prefix || !o)
     return fail(MAGE_ERR_INVALID_ARG, "q, k_blk, v_blk, o_prefix, lse_prefix and o must not be null");
   if (!aligned(q, 16) || !aligned(k_blk, 16) || !aligned(v_blk, 16) || !aligned(o_prefix, 16) || !aligned(o, 16))
@@ -1449,11 +1437,19 @@ mage_status mage_block_attn(const mage_dims* dims, const uint16_t* q, const uint
   bp.lse_pre = lse_prefix;
   bp.o = o;
   bp.lse = lse;
-  bp.S = d.S; bp.B = d.B; bp.Hq = d.Hq; bp.Hkv = d.Hkv; bp.G = d.G; bp.R = d.R;
+  bp.S = d.S; bp.B = d.B; bp.Hq = d.Hq; bp.Hkv = d.Hkv;
   bp.scale_log2 = d.scale * kLog2e;
-  const int64_t grid = d.units * d.nrb;
-  return d.D == 128 ? launch(kfn(block_attn_kernel<128>), "block_attn_kernel", grid, kWave, stream, bp)
-                    : launch(kfn(block_attn_kernel<64>), "block_attn_kernel", grid, kWave, stream, bp);
+  // more than MAGE_MAX_ROWS rows per KV head: one launch per sub-group of heads
+  for (int grp = 0; grp < d.ng; ++grp) {
+    const Dims g = d.ng > 1 ? group_dims(d, grp) : d;
+    bp.G = g.G; bp.R = g.R; bp.gs = g.gs; bp.g0 = g.g0;
+    const int64_t grid = g.units * g.nrb;
+    if (mage_status st = d.D == 128 ? launch(kfn(block_attn_kernel<128>), "block_attn_kernel", grid, kWave, stream, bp)
+                                    : launch(kfn(block_attn_kernel<64>), "block_attn_kernel", grid, kWave, stream, bp);
+        st != MAGE_OK)
+      return st;
+  }
+  return MAGE_OK;
 }
 
 mage_status mage_topk(int32_t rows, const float* scores, int64_t row_stride, const int32_t* lens,

@@ -90,13 +90,12 @@ typedef enum mage_status {
  * The standalone top-k runs rows with per-row lengths the same way. */
 #define MAGE_MAX_SEQS 256
 /* Largest R = B * G rows per KV head that one pass of the kernels takes.
- * mage_select_exact, mage_exact_attn and mage_sparse_attn (and their _paged
- * forms) take larger head groups: they run the G query heads of each KV head
- * in the fewest equal sub-groups of at most MAGE_MAX_ROWS rows, one after
- * another on the call's stream (every kernel of the call on `stream`; the
- * select stream, when given, waits for the end), with the score averaged
- * over all R rows before the top-k. Every other call returns
- * MAGE_ERR_UNSUPPORTED for R > MAGE_MAX_ROWS. B <= MAGE_MAX_ROWS always. */
+ * Every call takes larger head groups: it runs the G query heads of each KV
+ * head in the fewest equal sub-groups of at most MAGE_MAX_ROWS rows, one
+ * after another on the call's stream (every kernel of the call on that
+ * stream; the select stream, when given, waits for the end), with the score
+ * averaged over all R rows before the top-k (positions, pages or budgets).
+ * The mean query averages all R rows in one pass. B <= MAGE_MAX_ROWS always. */
 #define MAGE_MAX_ROWS 128
 
 typedef struct mage_dims {

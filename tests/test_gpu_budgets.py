@@ -47,6 +47,9 @@ CASES = [
     workloads.custom((53, 200, 1000), 8, 2, 64, 4, 64, paged=True, name="paged_ragged"),
     workloads.custom((17, 4096, 900), 32, 8, 128, 32, 256, paged=True, name="paged_r128"),
     workloads.custom((3000, 3000), 32, 8, 128, 32, 2000, name="wide_counts"),   # 1024-entry chunks
+    # R > 128 rows per KV head: two sub-groups (scores summed over all rows), paged R = 192
+    workloads.custom((3000,), 16, 2, 128, 32, 300, name="r256_budgets"),
+    workloads.custom((900, 2500), 24, 2, 64, 16, 128, paged=True, name="paged_r192_budgets"),
 ]
 
 

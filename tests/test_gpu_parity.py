@@ -336,6 +336,8 @@ def _block_inputs(S, B, Hq, Hkv, d, N, k, seed):
     (1, 64, 16, 16, 128, 2048, 300),   # MHA, B = 64: two 32-key tiles
     (1, 128, 8, 8, 64, 500, 64),       # B = 128: four 32-key tiles, four row blocks
     (1, 33, 2, 1, 128, 90, 90),        # B = 33: a second tile with one key
+    (1, 32, 16, 2, 128, 700, 100),     # R = 256: two sub-groups of query heads
+    (2, 100, 6, 2, 64, 700, 64),       # R = 300: three sub-groups of 100 rows
 ])
 def test_block_attn_matches_oracle(S, B, Hq, Hkv, d, N, k):
     scale = 1.0
@@ -385,6 +387,8 @@ def test_block_attn_after_the_gpu_prefix_pass():
     (1, 2, 4, 1, 128, 300, 40),        # B = 2: two waves without block rows
     (2, 32, 32, 8, 128, 2500, 2000),   # 4 index chunks of 512, block rows in the last
     (4, 64, 32, 16, 64, 1000, 600),    # one 640-entry chunk (256 row-block pairs), 16 block rows per wave
+    (1, 32, 16, 2, 128, 2000, 300),    # R = 256: two sub-groups, each with the block rows
+    (2, 100, 6, 2, 64, 700, 64),       # R = 300: three sub-groups of 100 rows
 ])
 def test_sparse_block_attn_matches_oracle(S, B, Hq, Hkv, d, N, k):
     scale = 1.0

@@ -1,6 +1,7 @@
 """mage_sparse_attn_noalloc (the later step with the library's fixed scratch
-instead of a workspace) against mage_sparse_attn on the same inputs: two
-different calls in a row, the second smaller, each repeated, every result
+instead of a workspace) against mage_sparse_attn on the same inputs: calls
+of different shapes in a row (a smaller one after a larger one and the
+reverse, one with its head group run as two sub-groups), each repeated, every result
 bit-identical to the workspace call (same kernels and plan) and within the
 2e-3 bar of the fp64 oracle. Both calls split their index lists, so the
 arrival counters in the scratch are exercised and must be left at zero."""
@@ -19,7 +20,8 @@ DEV = "cuda:0"
 
 @pytest.mark.parametrize("first", [True, False])
 def test_noalloc_matches_the_workspace_call(first):
-    cases = [(20000, 32, 8, 128, 32, 1024, 71), (3000, 16, 4, 64, 16, 512, 72)]
+    # the third: R = 16 * 16 = 256 rows per KV head, two sub-groups in turn on the scratch
+    cases = [(20000, 32, 8, 128, 32, 1024, 71), (3000, 16, 4, 64, 16, 512, 72), (3000, 32, 2, 128, 16, 1024, 73)]
     if not first:
         cases = cases[::-1]
     for n, Hq, Hkv, d, B, k, seed in cases:
