@@ -90,7 +90,7 @@ def ora_sparse(inp, q, idx):
 
 
 SMALL = [
-    workloads.CONFIGS[0],                                              # tiny, R = 16, d = 64
+    workloads.CONFIG_BY_NAME["tiny"],                                  # R = 16, d = 64
     workloads.custom((300,), 4, 1, 64, 3, 40, name="r12"),             # R = 12, ragged tile
     workloads.custom((1000,), 8, 2, 128, 16, 100, name="r64"),         # R = 64
     workloads.custom((777,), 32, 8, 128, 32, 129, name="r128"),        # R = 128, ragged k and N
