@@ -123,3 +123,30 @@ def test_topk_with_lengths_over_more_than_256_rows():
     got = idx.cpu().numpy()
     for r, m in enumerate(lens):
         assert np.array_equal(got[r], oracle.topk(sc[r, :m].numpy().astype(np.float64), k)[0]), r
+
+
+def test_sequence_groups_with_split_head_groups():
+    # 260 sequences (groups of 256 and 4) whose head groups hold R = 16 * 16 = 256 rows
+    # per KV head (two sub-groups each): step 1 and the later step, grouped == split,
+    # and the later step == the oracle
+    rng = np.random.default_rng(310)
+    lens = [int(x) for x in rng.integers(20, 90, 260)]
+    w = workloads.custom(tuple(lens), 16, 1, 64, 16, 12, paged=True, steps=2, seed=310, name="s260_r256")
+    inp = workloads.make_inputs(w, steps=2)
+    print(f"[case] 260 paged sequences, R = {w.block * w.num_q_heads // w.num_kv_heads}", flush=True)
+    q1, q2 = inp.q1.to(DEV), inp.q_steps[0].to(DEV)
+    kp, vp, tab = inp.k_pool.to(DEV), inp.v_pool.to(DEV), inp.page_table.to(DEV)
+    parts = _parts(len(lens))
+    full = mage.select_exact_paged(q1, kp, vp, tab, lens, w.k, w.scale)
+    split = [mage.select_exact_paged(q1[s], kp, vp, tab[s], lens[s], w.k, w.scale) for s in parts]
+    torch.cuda.synchronize()
+    _equal(full, split, lens, score_at=3)
+    idx = full[2]
+    o, lse = mage.sparse_attn_paged(q2, kp, vp, tab, lens, idx, w.scale)
+    split = [mage.sparse_attn_paged(q2[s], kp, vp, tab[s], lens[s], idx[s], w.scale) for s in parts]
+    torch.cuda.synchronize()
+    _equal((o, lse), split)
+    O2, L2 = oracle.sparse_paged(inp.q_steps[0], inp.k_pool, inp.v_pool, inp.page_table, inp.seq_lens,
+                                 idx.cpu().numpy(), w.scale)
+    assert np.abs(o.cpu().double().numpy() - O2).max() <= TOL
+    assert np.abs(lse.cpu().double().numpy() - L2).max() <= TOL
