@@ -38,6 +38,7 @@ CASES = [
     (workloads.custom((5000,), 32, 8, 128, 32, 64, name="p64"), 64, 4),
     (workloads.custom((100,), 4, 1, 64, 8, 8, name="more_pages_than_exist"), 16, 9),
     (workloads.custom((3000,), 16, 2, 128, 32, 64, name="r256_pages"), 16, 8),   # R = 256: two sub-groups
+    (workloads.custom((700, 1800), 24, 2, 64, 16, 64, paged=True, name="paged_r192_pages"), 16, 6),   # R = 192
     (workloads.custom((53, 200, 1000), 8, 2, 64, 4, 64, paged=True, name="paged_ragged"), 16, 4),
     (workloads.custom((17, 4096, 900), 32, 8, 128, 32, 512, paged=True, name="paged_p4"), 4, 100),
 ]

@@ -401,17 +401,20 @@ def test_sparse_block_attn_matches_oracle(S, B, Hq, Hkv, d, N, k):
     assert np.abs(lse.cpu().numpy() - l_ref).max() <= 2e-3
 
 
-@pytest.mark.parametrize("k", [64, 700])   # 700: six index chunks merged in the launch, some only padding
-def test_sparse_block_attn_paged_matches_oracle(k):
+@pytest.mark.parametrize("k,Hq,B", [
+    (64, 8, 4), (700, 8, 4),   # 700: six index chunks merged in the launch, some only padding
+    (100, 32, 16),             # R = 16 * 16 = 256 rows per KV head: two sub-groups, each with the block rows
+])
+def test_sparse_block_attn_paged_matches_oracle(k, Hq, B):
     # ragged paged prefix, shuffled 16-token pages; the oracle's own index set
-    w = workloads.custom((53, 200, 1000), 8, 2, 64, 4, k, paged=True, steps=2, name="paged_ragged", seed=31)
+    w = workloads.custom((53, 200, 1000), Hq, 2, 64, B, k, paged=True, steps=2, name="paged_ragged", seed=31)
     inp = workloads.make_inputs(w, steps=2)
     d = dev_inputs(inp)
     idx = np.ascontiguousarray(ora_select(inp)[3])
     g = torch.Generator().manual_seed(9)
     S = len(w.seq_lens)
-    kb = torch.randn(S, 2, 4, 64, generator=g).to(torch.bfloat16)
-    vb = torch.randn(S, 2, 4, 64, generator=g).to(torch.bfloat16)
+    kb = torch.randn(S, 2, B, 64, generator=g).to(torch.bfloat16)
+    vb = torch.randn(S, 2, B, 64, generator=g).to(torch.bfloat16)
     qt = d["q"][0]
     o, lse = mage.sparse_block_attn_paged(qt, d["k_pool"], d["v_pool"], d["table"], d["lens"],
                                           torch.from_numpy(idx).to(DEV), kb.to(DEV), vb.to(DEV), w.scale)
