@@ -74,8 +74,8 @@ extern "C" {
 typedef enum mage_status {
   MAGE_OK = 0,
   MAGE_ERR_INVALID_ARG = 1,          /* null pointer, bad size, Hq % Hkv != 0 */
-  MAGE_ERR_UNSUPPORTED = 2,          /* d not in {64, 128}, B > 128, R > 128 where a call
-                                        takes no split group */
+  MAGE_ERR_UNSUPPORTED = 2,          /* d not in {64, 128}, B > 128, sizes beyond a
+                                        stated maximum (MAGE_MAX_SPARSE_K, ...) */
   MAGE_ERR_WORKSPACE_TOO_SMALL = 3,
   MAGE_ERR_HIP = 4                   /* launch or runtime failure; see mage_last_error() */
 } mage_status;
