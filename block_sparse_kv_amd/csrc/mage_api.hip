@@ -268,7 +268,7 @@ Layout make_layout(const Dims& d, int64_t max_n, int64_t k) {
   const int64_t sparse_slots = U * (std::min<int64_t>(kSparseMaxChunks, cdiv(k, kSparseChunkUnit)) + 1);
   L.slots = std::max(exact_slots, sparse_slots);
   const int64_t nchunk = cdiv(max_n, kLocalChunk);
-  L.cand_stride = nchunk * kLocalChunk;
+  L.cand_stride = round_up(max_n, kWideChunk);   // room for either candidate chunk
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t at = off;
@@ -446,7 +446,7 @@ ChunkMap topk_map(const TopkParams& tp, int seqs) {
   int64_t acc = 0;
   for (int s = 0; s < seqs; ++s) {
     m.first[s] = static_cast<int32_t>(acc);
-    acc += cdiv(tp.lens.n[s], kLocalChunk) * tp.rows_per_seq;
+    acc += cdiv(tp.lens.n[s], tp.chunk) * tp.rows_per_seq;
   }
   m.first[seqs] = static_cast<int32_t>(acc);
   return m;
@@ -460,18 +460,25 @@ constexpr int64_t kMaxTopkLen = static_cast<int64_t>(kMaxLocalChunks) * kLocalCh
 // else the score sweep has built them after the exact pass zeroed them.
 mage_status launch_topk(const TopkParams& tp, hipStream_t stream, bool build_hist) {
   const int64_t wgs = tp.map.on ? tp.map.first[tp.rows / tp.rows_per_seq] : static_cast<int64_t>(tp.rows) * tp.nchunk;
+  const bool wide_chunk = tp.chunk == kWideChunk;
   if (build_hist) {
     if (mage_status st = launch(kfn(topk_prep_kernel), "topk_prep_kernel", tp.rows, kHistThreads, stream, tp);
         st != MAGE_OK)
       return st;
-    if (mage_status st = launch(kfn(topk_hist_kernel), "topk_hist_kernel", wgs, kHistThreads, stream, tp);
+    if (mage_status st = wide_chunk ? launch(kfn(topk_hist_kernel<kWideChunk>), "topk_hist_kernel", wgs,
+                                             kHistThreads, stream, tp)
+                                    : launch(kfn(topk_hist_kernel<kLocalChunk>), "topk_hist_kernel", wgs,
+                                             kHistThreads, stream, tp);
         st != MAGE_OK)
       return st;
   }
   // the wide final pass for large k: more candidates stay on the register path
-  if (tp.k > kFinalMax / 2)
-    return launch(kfn(topk_select_kernel<kFinalMaxWide>), "topk_select_kernel", wgs, kTopkThreads, stream, tp);
-  return launch(kfn(topk_select_kernel<kFinalMax>), "topk_select_kernel", wgs, kTopkThreads, stream, tp);
+  const void* fn = tp.k > kFinalMax / 2
+                       ? (wide_chunk ? kfn(topk_select_kernel<kFinalMaxWide, kWideChunk>)
+                                     : kfn(topk_select_kernel<kFinalMaxWide, kLocalChunk>))
+                       : (wide_chunk ? kfn(topk_select_kernel<kFinalMax, kWideChunk>)
+                                     : kfn(topk_select_kernel<kFinalMax, kLocalChunk>));
+  return launch(fn, "topk_select_kernel", wgs, kTopkThreads, stream, tp);
 }
 
 // The shared fields of a top-k over `rows` rows of the workspace's buffers.
@@ -486,8 +493,18 @@ TopkParams topk_params(void* ws, const Layout& L, const float* scores, int64_t s
   tp.hist = at<uint32_t>(ws, L.hist);
   tp.cand_bits = at<uint32_t>(ws, L.cand_bits);
   tp.cand_pos = at<int32_t>(ws, L.cand_pos);
-  tp.nchunk = static_cast<int>(cdiv(row_len_max, kLocalChunk));
-  tp.cand_stride = static_cast<int64_t>(tp.nchunk) * kLocalChunk;
+  // candidate chunks of kLocalChunk positions, or of kWideChunk when those
+  // would take more than one round of the CUs (ragged batch: 39.7 -> 29.1 us;
+  // at one round the wider chunk was 2.5-3 us slower; interleaved, bit-identical)
+  auto chunks = [&](int ch) {
+    if (n_uniform >= 0) return static_cast<int64_t>(rows) * cdiv(row_len_max, ch);
+    int64_t w = 0;
+    for (int s = 0; s < seqs; ++s) w += cdiv(lens.n[s], ch) * rows_per_seq;
+    return w;
+  };
+  tp.chunk = chunks(kLocalChunk) > kCus ? kWideChunk : kLocalChunk;
+  tp.nchunk = static_cast<int>(cdiv(row_len_max, tp.chunk));
+  tp.cand_stride = static_cast<int64_t>(tp.nchunk) * tp.chunk;
   tp.cand_count = at<int32_t>(ws, L.cand_count);
   tp.arrivals = at<uint32_t>(ws, L.topk_arrivals);
   tp.rows = rows;

@@ -337,7 +337,7 @@ __global__ __launch_bounds__(kThreads) void score_kernel(ScoreParams p) {
 // top-k
 
 // Top-k work-group: 1024 threads. In its candidate phase it takes
-// kLocalChunk positions of one row (kLocalPer per thread); the last of a
+// a chunk of one row (kLocalChunk or kWideChunk positions); the last of a
 // row's work-groups then selects among the row's candidates on its register
 // path, which holds up to kFinalMax entries (8 per thread), or kFinalMaxWide
 // (12 per thread, for large k) in the wide variant.
@@ -346,7 +346,10 @@ constexpr int kTopkWaves = kTopkThreads / kWave;
 constexpr int kFinalMax = 8192;
 constexpr int kFinalMaxWide = 12288;
 constexpr int kLocalChunk = 4096;
-constexpr int kLocalPer = kLocalChunk / kTopkThreads;
+// candidate chunk of rows whose 4096-position chunks would take more than one
+// round of the CUs (many or long rows): half the work-groups, each with twice
+// the positions
+constexpr int kWideChunk = 8192;
 // histogram pass of the standalone top-k: one 256-thread work-group per chunk
 constexpr int kHistThreads = 256;
 // chunks per row the final pass can index (rows up to 2^25 positions)
@@ -359,9 +362,9 @@ struct TopkParams {
   int32_t k;
   uint32_t* hist;           // [rows][kHistBins]: the row's score histogram (complete before the
                             //   top-k launch: built by the score sweep or topk_hist_kernel)
-  uint32_t* cand_bits;      // per row: chunk c's candidates at c * kLocalChunk
+  uint32_t* cand_bits;      // per row: chunk c's candidates at c * chunk
   int32_t* cand_pos;
-  int64_t cand_stride;      // nchunk * kLocalChunk
+  int64_t cand_stride;      // nchunk * chunk
   int32_t* cand_count;      // [rows][nchunk]
   uint32_t* arrivals;       // [rows]: work-groups of the row done with their candidates; zero on entry
   int32_t rows;
@@ -369,7 +372,8 @@ struct TopkParams {
   int32_t n_uniform;        // >= 0: every row has this many entries; else lens
   int32_t nchunk;
   SeqLens lens;
-  ChunkMap map;             // work-group -> (row, chunk of kLocalChunk positions)
+  ChunkMap map;             // work-group -> (row, chunk of `chunk` positions)
+  int32_t chunk;            // positions per candidate chunk: kLocalChunk or kWideChunk
 };
 
 struct TopkShared {
@@ -789,17 +793,18 @@ __global__ __launch_bounds__(kHistThreads) void topk_prep_kernel(TopkParams p) {
 // Histograms of user-supplied rows (the standalone top-k entry point; the
 // selection path builds them in the score sweep). One work-group per (row,
 // chunk) adds its chunk's histogram into the row's.
+template <int kChunk>
 __global__ __launch_bounds__(kHistThreads) void topk_hist_kernel(TopkParams p) {
-  constexpr int kPer = kLocalChunk / kHistThreads;
+  constexpr int kPer = kChunk / kHistThreads;
   __shared__ uint32_t s_hist[kHistBins];
   const int tid = threadIdx.x;
   int u, c;
-  map_chunk(p.map, p.lens, p.rows / p.rows_per_seq, p.rows_per_seq, kLocalChunk, p.nchunk, blockIdx.x, u, c);
+  map_chunk(p.map, p.lens, p.rows / p.rows_per_seq, p.rows_per_seq, kChunk, p.nchunk, blockIdx.x, u, c);
   if (u >= p.rows) return;
   const int n = topk_row_len(p, u);
-  const int start = c * kLocalChunk;
+  const int start = c * kChunk;
   if (min(p.k, n) == n || start >= n) return;   // such rows need no histogram
-  const int len = min(kLocalChunk, n - start);
+  const int len = min(kChunk, n - start);
   for (int b = tid; b < kHistBins; b += kHistThreads) s_hist[b] = 0u;
   __syncthreads();
   const float* src = p.scores + static_cast<int64_t>(u) * p.stride + start;
@@ -880,7 +885,7 @@ __device__ void wave_select_in_bin(const uint32_t* cand, int m, int rem, uint32_
   eq = cnt;
 }
 
-// Top-k of every row, one launch. Work-group (row u, chunk c of kLocalChunk
+// Top-k of every row, one launch. Work-group (row u, chunk c of kChunk
 // positions):
 //   1. From the row's histogram, the bin b* that holds the row's k-th largest
 //      score: every score in a higher bin is in the top k, none in a lower one.
@@ -893,21 +898,22 @@ __device__ void wave_select_in_bin(const uint32_t* cand, int m, int rem, uint32_
 //      (every larger score is a candidate), and the ordered compaction keeps
 //      ties at the lowest positions, so the output is ascending.
 // Rows whose every position is selected are written in step 1's place.
-template <int kMax>
+template <int kMax, int kChunk>
 __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(TopkParams p) {
+  constexpr int kLocalPer = kChunk / kTopkThreads;   // positions per thread in the candidate phase
   __shared__ uint32_t s_data[2 * kMax];   // bits, then positions (final pass)
   __shared__ int32_t s_off[kMaxLocalChunks + 1];
   __shared__ TopkShared sh;
   __shared__ int32_t s_sel[3];           // b*, scores in bins above b*, last arriver
   const int tid = threadIdx.x;
   int u, c;
-  map_chunk(p.map, p.lens, p.rows / p.rows_per_seq, p.rows_per_seq, kLocalChunk, p.nchunk, blockIdx.x, u, c);
+  map_chunk(p.map, p.lens, p.rows / p.rows_per_seq, p.rows_per_seq, kChunk, p.nchunk, blockIdx.x, u, c);
   if (u >= p.rows) return;
   const int n = topk_row_len(p, u);
   const int kk = min(p.k, n);
-  const int start = c * kLocalChunk;
+  const int start = c * kChunk;
   if (start >= n) return;
-  const int len = min(kLocalChunk, n - start);
+  const int len = min(kChunk, n - start);
   int32_t* out = p.idx + static_cast<int64_t>(u) * p.k;
   MAGE_TRACE_POINT(0);
   if (kk == n) {  // every position is selected
@@ -964,7 +970,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(TopkParams p)
   }
   // ---- 3. count in; the row's last work-group selects (the counter is zeroed
   // by the next exact pass)
-  const int nch = (n + kLocalChunk - 1) / kLocalChunk;
+  const int nch = (n + kChunk - 1) / kChunk;
   if (!count_in(p.arrivals + u, static_cast<uint32_t>(nch), false, &s_sel[2])) return;
   MAGE_TRACE_POINT(2);
   const int32_t* cnt = p.cand_count + static_cast<int64_t>(u) * p.nchunk;
@@ -989,7 +995,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(TopkParams p)
     for (int j = 0; j < kSpecLoads; ++j) {
       // clamped: the slots past the window repeat its last one
       const int i = min(tid + j * kTopkThreads, (nch << spec_shift) - 1);
-      const int64_t sl = static_cast<int64_t>(i >> spec_shift) * kLocalChunk + (i & (spec_per - 1));
+      const int64_t sl = static_cast<int64_t>(i >> spec_shift) * kChunk + (i & (spec_per - 1));
       sb[j] = ld_dev(bits + sl);
       sp[j] = ld_dev(pos + sl);
     }
@@ -1025,7 +1031,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(TopkParams p)
       const int mid = (a + b + 1) >> 1;
       if (s_off[mid] <= i) a = mid; else b = mid - 1;
     }
-    return static_cast<int64_t>(a) * kLocalChunk + (i - s_off[a]);
+    return static_cast<int64_t>(a) * kChunk + (i - s_off[a]);
   };
   uint32_t T;
   int need;
