@@ -753,6 +753,7 @@ mage_status launch_page_topk(const Dims& d, const KvArgs& kv, const float* score
   ps.n_uniform = ragged ? -1 : kv.src.n_uniform;
   ps.page_tokens = P;
   ps.pages_max = static_cast<int32_t>(pages_max);
+  ps.vec4 = P % 4 == 0 && stride % 4 == 0 && aligned(scores, 16);
   ps.lens = kv.lens;
   if (mage_status st = launch(kfn(page_sum_kernel), "page_sum_kernel", cdiv(d.units * pages_max, 256), 256,
                               stream, ps);
