@@ -345,6 +345,9 @@ constexpr int kTopkThreads = 1024;
 constexpr int kTopkWaves = kTopkThreads / kWave;
 constexpr int kFinalMax = 8192;
 constexpr int kFinalMaxWide = 12288;
+// candidates per thread that the final pass holds in registers when more
+// than the LDS takes (rows with many scores in the k-th score's bin)
+constexpr int kOverflowPer = 24;
 constexpr int kLocalChunk = 4096;
 // candidate chunk of rows whose 4096-position chunks would take more than one
 // round of the CUs (many or long rows): half the work-groups, each with twice
@@ -1106,6 +1109,18 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(TopkParams p)
     MAGE_TRACE_POINT(4);
     ordered_compact_regs<kPer>(w, total, T, need, [&](int j) { return static_cast<int32_t>(wpos[j]); }, nullptr,
                                out, sh, eq_total, kk);
+  } else if (total <= kOverflowPer * kTopkThreads) {
+    // more candidates than the LDS holds: each thread's contiguous run of their
+    // scores in registers, its loads all in flight at once; positions are
+    // loaded for the kept entries only
+    uint32_t w[kOverflowPer];
+#pragma unroll
+    for (int j = 0; j < kOverflowPer; ++j) w[j] = ld_dev(bits + slot_of(min(tid * kOverflowPer + j, total - 1)));
+    int eq_total;
+    radix_select_regs<kOverflowPer>(w, total, kk, sh, T, need, &eq_total);
+    ordered_compact_regs<kOverflowPer>(
+        w, total, T, need, [&](int j) { return ld_dev(pos + slot_of(tid * kOverflowPer + j)); }, nullptr, out, sh,
+        eq_total, kk);
   } else {
     auto get = [&](int i) { return ld_dev(bits + slot_of(i)); };
     radix_select(get, total, kk, sh, T, need);

@@ -263,7 +263,8 @@ def test_equal_keys_pick_lowest_positions_and_constant_v():
 @pytest.mark.parametrize("ties", ["none", "many", "all", "zeros"])
 @pytest.mark.parametrize("n,k", [(1, 1), (5, 3), (100, 100), (1000, 17), (16384, 1024),
                                  (16385, 1024), (40000, 2048), (50000, 20000), (9, 30), (200000, 6000),
-                                 (1 << 20, 8192)])
+                                 (1 << 20, 8192),
+                                 (24576, 100), (24577, 100)])   # register capacity of the final pass's overflow tier
 def test_topk_bit_exact(ties, n, k):
     sc = workloads.random_scores(3, n, seed=n * 7 + k, ties=ties)
     idx = mage.topk(sc.to(DEV), k)
