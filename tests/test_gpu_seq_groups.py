@@ -150,3 +150,27 @@ def test_sequence_groups_with_split_head_groups():
                                  idx.cpu().numpy(), w.scale)
     assert np.abs(o.cpu().double().numpy() - O2).max() <= TOL
     assert np.abs(lse.cpu().double().numpy() - L2).max() <= TOL
+
+
+def test_grouped_selection_with_a_select_stream():
+    # a grouped step-1 call with a select stream: idx_ready (recorded on the select
+    # stream after every group) is all a consumer waits for; the results equal the
+    # same call on one stream bit for bit
+    w, inp = _inputs()
+    lens = list(w.seq_lens)
+    q1 = inp.q1.to(DEV)
+    kp, vp, tab = inp.k_pool.to(DEV), inp.v_pool.to(DEV), inp.page_table.to(DEV)
+    ref = mage.select_exact_paged(q1, kp, vp, tab, lens, w.k, w.scale)
+    torch.cuda.synchronize()
+    side, consumer = torch.cuda.Stream(device=DEV), torch.cuda.Stream(device=DEV)
+    ready = torch.cuda.Event()
+    o, lse, idx, sc = mage.select_exact_paged(q1, kp, vp, tab, lens, w.k, w.scale, select_stream=side,
+                                              idx_ready=ready)
+    consumer.wait_event(ready)
+    with torch.cuda.stream(consumer):
+        idx_copy = idx.clone()
+        sc_copy = sc.clone()
+    torch.cuda.synchronize()
+    assert torch.equal(idx_copy, ref[2])
+    _equal((sc_copy,), [(ref[3],)], lens, score_at=0)
+    assert torch.equal(o, ref[0]) and torch.equal(lse, ref[1])
